@@ -1,0 +1,347 @@
+"""Pins of the fp64 oracle against what the pages and the mathematics fix.
+
+Every check here compares the oracle with something that is not the oracle:
+printed worked examples (tests/golden/), closed forms, limiting cases written
+out independently from the pages' own equations for DeltaNet, Gated DeltaNet
+and linear attention, the expanded DPLR transition form, brute-force products
+of dense transition matrices, invariants (read-back, locality, contraction),
+and the independent chunkwise formulation.  Each test is chosen so that a
+plausible slip in the loop (read before write, decay on the wrong side, a sign,
+a dropped beta or scale, exp2 instead of exp, state leaking between packed
+sequences) fails at least one of them.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import chunk_form
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def run1(q, k, v, g, beta, S0=None, scale=1.0, delta_rule=True):
+    """One chain [T, d] through the oracle (B = H = 1).  Returns (o [T, dv], S_T)."""
+    q = np.asarray(q, np.float32)[None, :, None, :]
+    k = np.asarray(k, np.float32)[None, :, None, :]
+    v = np.asarray(v, np.float32)[None, :, None, :]
+    g = np.asarray(g, np.float32)[None, :, None, :]
+    beta = np.asarray(beta, np.float32)[None, :, None]
+    s0 = None if S0 is None else np.asarray(S0, np.float64)[None, None]
+    outs, Sf = oracle.forward(q, k, v, g, beta, S0=s0, scale=scale, delta_rule=delta_rule,
+                              threads=1)
+    return outs[0], Sf[0]
+
+
+def rand_chain(rng, T, dk, dv, unit_keys=True, f32_exact=True):
+    """Random fp32-representable chain (so fp64 references see the same values)."""
+    q = rng.standard_normal((T, dk)).astype(np.float32)
+    k = rng.standard_normal((T, dk)).astype(np.float32)
+    if unit_keys:
+        q /= np.linalg.norm(q, axis=1, keepdims=True)
+        k /= np.linalg.norm(k, axis=1, keepdims=True)
+    v = rng.standard_normal((T, dv)).astype(np.float32)
+    g = (-np.exp(rng.standard_normal((T, dk)) - 2.0)).astype(np.float32)
+    beta = (1 / (1 + np.exp(-rng.standard_normal(T)))).astype(np.float32)
+    return q, k, v, g, beta
+
+
+def f64(*xs):
+    return [np.asarray(x, np.float64) for x in xs]
+
+
+# ---------------------------------------------------------------- worked examples
+
+def test_noncommuting_example_fixes_forget_before_write():
+    gd = golden("noncommuting_2x2.json")
+    k = np.array([gd["k"]], np.float32)
+    g = np.log(np.array([gd["alpha"]], np.float64)).astype(np.float32)
+    _, S1 = run1(np.zeros((1, 2)), k, np.zeros((1, 2)), g, [gd["beta"]], S0=np.eye(2))
+    # fp32 k = 1/sqrt(2) rounded: k k^T = 0.5 within 1e-7
+    np.testing.assert_allclose(S1, gd["forget_then_write"], atol=2e-7)
+    assert np.abs(S1 - np.array(gd["write_then_forget"])).max() > 0.2
+
+
+def test_channelwise_decay_readout():
+    gd = golden("decay_readout_2x2.json")
+    g = np.log(np.array([gd["alpha"], [1.0, 1.0]])).astype(np.float32)   # decay, then hold
+    q = np.array([[1.0, 0.0], [0.0, 1.0]], np.float32)
+    o, S = run1(q, np.zeros((2, 2)), np.zeros((2, 2)), g, [0.0, 0.0], S0=gd["S0"])
+    np.testing.assert_allclose(o[0], gd["read_e1"], atol=1e-15)
+    np.testing.assert_allclose(o[1], gd["read_e2"], atol=1e-15)
+    np.testing.assert_allclose(S, np.diag(gd["alpha"]), atol=1e-15)
+
+
+@pytest.mark.parametrize("beta", [1.0, 0.25, 0.5, 0.875])
+def test_delta_overwrite_and_interpolation(beta):
+    gd = golden("delta_overwrite.json")
+    other = [0.625, -1.5]
+    S0 = np.array([gd["old_value"], other])              # row i = what key e_i reads
+    k = np.array([gd["k"]], np.float32)
+    o, S1 = run1(k, k, np.array([gd["new_value"]], np.float32), np.zeros((1, 2)), [beta], S0=S0)
+    want = (1 - beta) * np.array(gd["old_value"]) + beta * np.array(gd["new_value"])
+    np.testing.assert_allclose(o[0], want, atol=1e-15)    # read after the write, same key
+    np.testing.assert_allclose(S1[1], other, atol=0)      # orthogonal key row untouched
+
+
+def test_half_life_fixes_natural_log():
+    gd = golden("half_life.json")
+    n = gd["tokens"]
+    g = np.full((n, 1), np.log(gd["alpha"]), np.float32)
+    _, S = run1(np.zeros((n, 1)), np.zeros((n, 1)), np.zeros((n, 1)), g, np.zeros(n),
+                S0=[[1.0]])
+    assert abs(S[0, 0] - gd["remaining_fraction_approx"]) < gd["tolerance"]
+    np.testing.assert_allclose(S[0, 0], np.exp(n * np.float64(np.float32(np.log(0.99)))),
+                               rtol=1e-13)
+
+
+# ---------------------------------------------------------------- limiting cases
+
+def deltanet_loop(q, k, v, beta, S0, scale):
+    """DeltaNet from the reconstruction-loss step ("Kimi Unveils ...", 2.2):
+    S <- S - beta * grad(1/2 |S^T k - v|^2) in the key-by-value orientation."""
+    S = np.array(S0, np.float64)
+    outs = []
+    for t in range(q.shape[0]):
+        grad = np.outer(k[t], S.T @ k[t] - v[t])
+        S = S - beta[t] * grad
+        outs.append(S.T @ (scale * q[t]))
+    return np.array(outs), S
+
+
+def gated_deltanet_loop(q, k, v, alpha, beta, S0, scale):
+    """Gated DeltaNet ("Kimi Unveils ...", 3): forget (scalar), predict, correct, write."""
+    S = np.array(S0, np.float64)
+    outs = []
+    for t in range(q.shape[0]):
+        St = alpha[t] * S
+        vhat = St.T @ k[t]
+        e = beta[t] * (v[t] - vhat)
+        S = St + np.outer(k[t], e)
+        outs.append(S.T @ (scale * q[t]))
+    return np.array(outs), S
+
+
+def test_alpha_one_is_deltanet():
+    rng = np.random.default_rng(1)
+    q, k, v, _, beta = rand_chain(rng, 40, 8, 6)
+    S0 = 0.3 * rng.standard_normal((8, 6))
+    o, S = run1(q, k, v, np.zeros((40, 8)), beta, S0=S0, scale=0.7)
+    o2, S2 = deltanet_loop(*f64(q, k, v, beta), S0, 0.7)
+    np.testing.assert_allclose(o, o2, atol=1e-12)
+    np.testing.assert_allclose(S, S2, atol=1e-12)
+
+
+def test_scalar_alpha_is_gated_deltanet():
+    rng = np.random.default_rng(2)
+    q, k, v, _, beta = rand_chain(rng, 40, 8, 6)
+    gs = (-np.exp(rng.standard_normal(40) - 2)).astype(np.float32)
+    g = np.repeat(gs[:, None], 8, axis=1)
+    S0 = 0.3 * rng.standard_normal((8, 6))
+    o, S = run1(q, k, v, g, beta, S0=S0, scale=0.5)
+    o2, S2 = gated_deltanet_loop(*f64(q, k, v), np.exp(gs.astype(np.float64)),
+                                 beta.astype(np.float64), S0, 0.5)
+    np.testing.assert_allclose(o, o2, atol=1e-12)
+    np.testing.assert_allclose(S, S2, atol=1e-12)
+
+
+def test_no_delta_alpha_one_is_linear_attention():
+    """o_t = s * sum_{i<=t} <k_i, q_t> v_i  ("Kimi Unveils ...", 1.1)."""
+    rng = np.random.default_rng(3)
+    T, dk, dv = 30, 5, 4
+    q = rng.standard_normal((T, dk)).astype(np.float32)
+    k = rng.standard_normal((T, dk)).astype(np.float32)
+    v = rng.standard_normal((T, dv)).astype(np.float32)
+    s = 0.3
+    o, S = run1(q, k, v, np.zeros((T, dk)), np.ones(T), scale=s, delta_rule=False)
+    q64, k64, v64 = f64(q, k, v)
+    want = np.array([s * sum(np.dot(k64[i], q64[t]) * v64[i] for i in range(t + 1))
+                     for t in range(T)])
+    np.testing.assert_allclose(o, want, atol=1e-12)
+    np.testing.assert_allclose(S, k64.T @ v64, atol=1e-12)
+
+
+def test_beta_zero_only_decays():
+    rng = np.random.default_rng(4)
+    T, dk, dv = 25, 6, 3
+    q, k, v, g, _ = rand_chain(rng, T, dk, dv)
+    S0 = rng.standard_normal((dk, dv))
+    s = 0.4
+    o, S = run1(q, k, v, g, np.zeros(T), S0=S0, scale=s)
+    G = np.cumsum(g.astype(np.float64), axis=0)
+    np.testing.assert_allclose(S, np.exp(G[-1])[:, None] * S0, atol=1e-13)
+    want = np.array([(np.exp(G[t])[:, None] * S0).T @ (s * q[t].astype(np.float64))
+                     for t in range(T)])
+    np.testing.assert_allclose(o, want, atol=1e-13)
+
+
+# ---------------------------------------------------------------- other forms
+
+def test_expanded_form_equals_update_form():
+    """S_t = A_t S_{t-1} + B_t, A_t = (I - beta k k^T) D_t, B_t = beta k v^T
+    ("Kimi Delta Attention: Channel-Wise Memory Control", DPLR section)."""
+    rng = np.random.default_rng(5)
+    for trial in range(12):
+        dk = int(rng.integers(2, 17)); dv = int(rng.integers(2, 17)); T = int(rng.integers(1, 33))
+        q, k, v, g, beta = rand_chain(rng, T, dk, dv, unit_keys=bool(trial % 2))
+        S0 = rng.standard_normal((dk, dv))
+        s = float(rng.uniform(0.1, 1.0))
+        o, S = run1(q, k, v, g, beta, S0=S0, scale=s)
+        q64, k64, v64, g64, b64 = f64(q, k, v, g, beta)
+        St = S0.copy()
+        for t in range(T):
+            A = (np.eye(dk) - b64[t] * np.outer(k64[t], k64[t])) @ np.diag(np.exp(g64[t]))
+            St = A @ St + b64[t] * np.outer(k64[t], v64[t])
+            np.testing.assert_allclose(o[t], St.T @ (s * q64[t]), atol=1e-12)
+        np.testing.assert_allclose(S, St, atol=1e-12)
+
+
+def test_brute_force_transition_products():
+    """Tiny cases: S_T = (A_T ... A_1) S0 + sum_t (A_T ... A_{t+1}) B_t."""
+    rng = np.random.default_rng(6)
+    for _ in range(10):
+        T = int(rng.integers(1, 13)); dk = int(rng.integers(1, 5)); dv = int(rng.integers(1, 5))
+        q, k, v, g, beta = rand_chain(rng, T, dk, dv, unit_keys=False)
+        S0 = rng.standard_normal((dk, dv))
+        _, S = run1(q, k, v, g, beta, S0=S0)
+        q64, k64, v64, g64, b64 = f64(q, k, v, g, beta)
+        A = [(np.eye(dk) - b64[t] * np.outer(k64[t], k64[t])) @ np.diag(np.exp(g64[t]))
+             for t in range(T)]
+        Bm = [b64[t] * np.outer(k64[t], v64[t]) for t in range(T)]
+
+        def prod(lo, hi):  # A_{hi-1} ... A_lo
+            P = np.eye(dk)
+            for t in range(lo, hi):
+                P = A[t] @ P
+            return P
+        want = prod(0, T) @ S0 + sum(prod(t + 1, T) @ Bm[t] for t in range(T))
+        np.testing.assert_allclose(S, want, atol=1e-12)
+
+
+def test_readback_and_locality_identities():
+    """Unit k: S_t^T k = (1 - beta) Sbar^T k + beta v; x orthogonal to k is
+    unaffected by the write ("Kimi Unveils ...", 2.1)."""
+    rng = np.random.default_rng(7)
+    dk, dv = 9, 5
+    for _ in range(8):
+        q, k, v, g, beta = rand_chain(rng, 1, dk, dv)
+        S0 = rng.standard_normal((dk, dv))
+        _, S1 = run1(q, k, v, g, beta, S0=S0)
+        k64, v64, g64 = f64(k[0], v[0], g[0])
+        b = float(beta[0])
+        Sbar = np.exp(g64)[:, None] * S0
+        n = k64 @ k64                                     # 1 for a unit key (up to fp32)
+        np.testing.assert_allclose(S1.T @ k64, (1 - b * n) * (Sbar.T @ k64) + b * n * v64,
+                                   atol=1e-12)
+        x = rng.standard_normal(dk)
+        x -= (x @ k64) / (k64 @ k64) * k64
+        np.testing.assert_allclose((S1 - Sbar).T @ x, 0, atol=1e-12)
+
+
+def test_contraction_with_zero_values():
+    """Unit keys, beta in [0,1], g <= 0, v = 0: every transition has eigenvalues
+    in [0, 1] ("Kimi Unveils ...", 2.3) so |S|_F never grows."""
+    rng = np.random.default_rng(8)
+    dk, dv = 6, 4
+    q, k, _, g, beta = rand_chain(rng, 1000, dk, dv)
+    beta[::7] = 1.0
+    beta[3::11] = 0.0
+    S = rng.standard_normal((dk, dv))
+    prev = np.linalg.norm(S)
+    for t in range(1000):
+        _, S = run1(q[t:t + 1], k[t:t + 1], np.zeros((1, dv)), g[t:t + 1], beta[t:t + 1], S0=S)
+        cur = np.linalg.norm(S)
+        assert cur <= prev * (1 + 1e-14)
+        prev = cur
+
+
+@pytest.mark.parametrize("chunk", [1, 4, 16, 64, 200, 256])
+def test_chunkwise_algebra_matches(chunk):
+    """The section-6 chunkwise form gives the same states and outputs."""
+    rng = np.random.default_rng(9)
+    T, dk, dv = 200, 16, 12
+    q, k, v, g, beta = rand_chain(rng, T, dk, dv)
+    S0 = 0.5 * rng.standard_normal((dk, dv))
+    s = dk ** -0.5
+    o, S = run1(q, k, v, g, beta, S0=S0, scale=s)
+    o2, S2 = chunk_form.chain_forward(*f64(q, k, v, g, beta), S0, s, chunk)
+    np.testing.assert_allclose(o, o2, atol=1e-12)
+    np.testing.assert_allclose(S, S2, atol=1e-12)
+
+
+# ---------------------------------------------------------------- layout handling
+
+def test_batched_heads_are_independent_chains():
+    rng = np.random.default_rng(10)
+    B, T, H, dk, dv = 2, 17, 3, 4, 5
+    q = rng.standard_normal((B, T, H, dk)).astype(np.float32)
+    k = rng.standard_normal((B, T, H, dk)).astype(np.float32)
+    v = rng.standard_normal((B, T, H, dv)).astype(np.float32)
+    g = (-np.exp(rng.standard_normal((B, T, H, dk)) - 2)).astype(np.float32)
+    beta = rng.uniform(0, 1, (B, T, H)).astype(np.float32)
+    S0 = rng.standard_normal((B, H, dk, dv))
+    out, Sf = oracle.forward_dense(q, k, v, g, beta, S0=S0, scale=0.5, threads=3)
+    for b in range(B):
+        for h in range(H):
+            o1, s1 = run1(q[b, :, h], k[b, :, h], v[b, :, h], g[b, :, h], beta[b, :, h],
+                          S0=S0[b, h], scale=0.5)
+            np.testing.assert_array_equal(out[b, :, h], o1)
+            np.testing.assert_array_equal(Sf[b, h], s1)
+    # chain subsets in any order give the same numbers
+    outs, Ssub = oracle.forward(q, k, v, g, beta, S0=S0, scale=0.5, chains=[(1, 2), (0, 1)])
+    np.testing.assert_array_equal(outs[0], out[1, :, 2])
+    np.testing.assert_array_equal(Ssub[1], Sf[0, 1])
+
+
+def test_varlen_state_does_not_cross_sequences():
+    rng = np.random.default_rng(11)
+    lens = [3, 5, 0, 2, 7]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    Tt, H, dk, dv = int(cu[-1]), 2, 4, 3
+    q = rng.standard_normal((Tt, H, dk)).astype(np.float32)
+    k = rng.standard_normal((Tt, H, dk)).astype(np.float32)
+    v = rng.standard_normal((Tt, H, dv)).astype(np.float32)
+    g = (-np.exp(rng.standard_normal((Tt, H, dk)) - 2)).astype(np.float32)
+    beta = rng.uniform(0, 1, (Tt, H)).astype(np.float32)
+    S0 = rng.standard_normal((len(lens), H, dk, dv))
+    out, Sf = oracle.forward_dense(q, k, v, g, beta, S0=S0, cu_seqlens=cu, scale=1.0)
+    for n in range(len(lens)):
+        a, b = cu[n], cu[n + 1]
+        for h in range(H):
+            o1, s1 = run1(q[a:b, h], k[a:b, h], v[a:b, h], g[a:b, h], beta[a:b, h],
+                          S0=S0[n, h], scale=1.0)
+            np.testing.assert_array_equal(out[a:b, h], o1)
+            np.testing.assert_array_equal(Sf[n, h], s1)
+    np.testing.assert_array_equal(Sf[2], S0[2])       # empty sequence keeps its state
+
+
+def test_bf16_bits_are_read_exactly():
+    from gated_delta_rule_06_amd.inputs import bf16_bits_from_f32
+    rng = np.random.default_rng(12)
+    T, dk, dv = 9, 8, 8
+    q, k, v, g, beta = rand_chain(rng, T, dk, dv)
+    qb, kb, vb = (bf16_bits_from_f32(x) for x in (q, k, v))
+    # the float32 values of those bit patterns
+    up = [(x.astype(np.uint32) << 16).view(np.float32) for x in (qb, kb, vb)]
+    o1, S1 = oracle.forward(qb[None, :, None], kb[None, :, None], vb[None, :, None],
+                            g[None, :, None], beta[None, :, None])
+    o2, S2 = oracle.forward(up[0][None, :, None], up[1][None, :, None], up[2][None, :, None],
+                            g[None, :, None], beta[None, :, None])
+    np.testing.assert_array_equal(o1[0], o2[0])
+    np.testing.assert_array_equal(S1, S2)
+
+
+def test_bf16_rounding_is_nearest_even():
+    from gated_delta_rule_06_amd.inputs import bf16_bits_from_f32
+    # 1 + 2^-8 is a tie between 1 and 1 + 2^-7: rounds to even (1.0)
+    x = np.array([1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -2.5, 1.0 + 2 ** -9], np.float32)
+    bits = bf16_bits_from_f32(x)
+    back = (bits.astype(np.uint32) << 16).view(np.float32)
+    np.testing.assert_array_equal(back, [1.0, 1.0 + 2 ** -6, -2.5, 1.0])
