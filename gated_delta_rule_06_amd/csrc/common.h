@@ -1,0 +1,78 @@
+// common.h -- small device helpers shared by the KDA kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------- bf16 <-> f32
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) {
+  return __uint_as_float(h << 16);
+}
+
+// Round to nearest even (the hardware conversion on gfx950).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  __bf16 b = (__bf16)f;
+  return __builtin_bit_cast(uint16_t, b);
+}
+
+// Two floats -> one dword holding two bf16 (lo = a, hi = b).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return (uint32_t)f32_to_bf16_bits(a) | ((uint32_t)f32_to_bf16_bits(b) << 16);
+}
+
+// Element access for the two I/O types.  IoBf16 stores raw bf16 bit patterns.
+struct IoF32 {
+  typedef float storage;
+  static constexpr bool is_bf16 = false;
+  __device__ static __forceinline__ float load(const void* p, size_t i) {
+    return reinterpret_cast<const float*>(p)[i];
+  }
+  // four consecutive elements starting at i (i % 4 == 0)
+  __device__ static __forceinline__ f32x4 load4(const void* p, size_t i) {
+    return *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(p) + i);
+  }
+  __device__ static __forceinline__ void store(void* p, size_t i, float x) {
+    reinterpret_cast<float*>(p)[i] = x;
+  }
+  __device__ static __forceinline__ void store4(void* p, size_t i, f32x4 x) {
+    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p) + i) = x;
+  }
+};
+
+struct IoBf16 {
+  typedef uint16_t storage;
+  static constexpr bool is_bf16 = true;
+  __device__ static __forceinline__ float load(const void* p, size_t i) {
+    return bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(p)[i]);
+  }
+  __device__ static __forceinline__ f32x4 load4(const void* p, size_t i) {
+    u32x2 w = *reinterpret_cast<const u32x2*>(reinterpret_cast<const uint16_t*>(p) + i);
+    f32x4 r;
+    r[0] = __uint_as_float(w[0] << 16);
+    r[1] = __uint_as_float(w[0] & 0xffff0000u);
+    r[2] = __uint_as_float(w[1] << 16);
+    r[3] = __uint_as_float(w[1] & 0xffff0000u);
+    return r;
+  }
+  __device__ static __forceinline__ void store(void* p, size_t i, float x) {
+    reinterpret_cast<uint16_t*>(p)[i] = f32_to_bf16_bits(x);
+  }
+  __device__ static __forceinline__ void store4(void* p, size_t i, f32x4 x) {
+    u32x2 w;
+    w[0] = pack_bf16x2(x[0], x[1]);
+    w[1] = pack_bf16x2(x[2], x[3]);
+    *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(p) + i) = w;
+  }
+};
+
+}  // namespace kda

@@ -1,0 +1,161 @@
+// kda_api.hip -- the C ABI declared in include/kda.h: validation, then launch.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kda.h"
+
+namespace kda {
+hipError_t launch_decode(const void* q, const void* k, const void* v, const float* g,
+                         const float* beta, float* S, void* out, int NH, int dk, int dv,
+                         float scale, bool bf16, hipStream_t stream);
+hipError_t launch_chunk(const void* q, const void* k, const void* v, const float* g,
+                        const float* beta, const float* S0, void* out, float* S_final,
+                        const int32_t* cu_seqlens, int n_seq, int T, int H, int dk, int dv,
+                        float scale, bool bf16, hipStream_t stream);
+bool chunk_supported(int dk, int dv, bool bf16);
+}  // namespace kda
+
+namespace {
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+Range span(const void* p, size_t bytes) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  return Range{a, a + bytes};
+}
+
+bool overlap(Range a, Range b) {
+  return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi;
+}
+
+bool io_ok(int io) { return io == KDA_IO_F32 || io == KDA_IO_BF16; }
+size_t io_bytes(int io) { return io == KDA_IO_BF16 ? 2 : 4; }
+
+// Copy S0 (or zeros) into S_final for sequences with no tokens: done by a
+// tiny kernel rather than a memset so that the call can sit in a HIP graph.
+__global__ void copy_state_kernel(const float* __restrict__ S0, float* __restrict__ Sf, size_t n) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x)
+    Sf[i] = S0 ? S0[i] : 0.f;
+}
+
+int launch_status(hipError_t e) { return e == hipSuccess ? KDA_OK : KDA_ERR_HIP; }
+
+// Shared validation of the prefill entry points.  `rows` is the number of
+// token rows (B*T or T_total), `n_seq` the number of state slots.
+int check_prefill(const void* q, const void* k, const void* v, const float* log_alpha,
+                  const float* beta, const float* S0, void* out, float* S_final,
+                  const int32_t* cu, size_t rows, int n_seq, int H, int d_k, int d_v, int chunk,
+                  int io_dtype) {
+  if (!io_ok(io_dtype)) return KDA_ERR_UNSUPPORTED;
+  if (chunk != 64) return KDA_ERR_UNSUPPORTED;
+  if (!kda::chunk_supported(d_k, d_v, io_dtype == KDA_IO_BF16)) return KDA_ERR_UNSUPPORTED;
+  if (rows > 0 && (!q || !k || !v || !log_alpha || !beta || !out)) return KDA_ERR_NULL;
+  const size_t e = io_bytes(io_dtype);
+  const size_t state = (size_t)n_seq * H * d_k * d_v * sizeof(float);
+  const Range in[] = {span(q, rows * H * d_k * e), span(k, rows * H * d_k * e),
+                      span(v, rows * H * d_v * e), span(log_alpha, rows * H * d_k * 4),
+                      span(beta, rows * H * 4),    span(cu, cu ? (size_t)(n_seq + 1) * 4 : 0)};
+  const Range ro = span(out, rows * H * d_v * e);
+  const Range rs = span(S_final, S_final ? state : 0);
+  const Range r0 = span(S0, S0 ? state : 0);
+  for (const Range& r : in) {
+    if (overlap(ro, r) || overlap(rs, r)) return KDA_ERR_ALIAS;
+  }
+  if (overlap(ro, rs) || overlap(ro, r0)) return KDA_ERR_ALIAS;
+  if (S_final && S0 && S0 != S_final && overlap(rs, r0)) return KDA_ERR_ALIAS;
+  return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kda_version(void) { return 100; }
+
+const char* kda_status_string(int status) {
+  switch (status) {
+    case KDA_OK: return "KDA_OK";
+    case KDA_ERR_NULL: return "KDA_ERR_NULL: a required pointer is NULL";
+    case KDA_ERR_DIM: return "KDA_ERR_DIM: a size is negative or inconsistent";
+    case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED: d_k, d_v, chunk or io_dtype not supported";
+    case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE: workspace missing or too small";
+    case KDA_ERR_HIP: return "KDA_ERR_HIP: a HIP launch failed";
+    case KDA_ERR_ALIAS: return "KDA_ERR_ALIAS: an output overlaps an input";
+    default: return "unknown KDA status";
+  }
+}
+
+size_t kda_chunk_fwd_workspace_size(int, int, int, int, int, int, int) { return 0; }
+
+size_t kda_chunk_fwd_varlen_workspace_size(int, int, int, int, int, int, int) { return 0; }
+
+int kda_chunk_fwd(const void* q, const void* k, const void* v, const float* log_alpha,
+                  const float* beta, const float* S0, void* out, float* S_final, int B, int T,
+                  int H, int d_k, int d_v, float scale, int chunk, int io_dtype, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  if (B < 0 || T < 0 || H <= 0) return KDA_ERR_DIM;
+  const size_t rows = (size_t)B * T;
+  int st = check_prefill(q, k, v, log_alpha, beta, S0, out, S_final, nullptr, rows, B, H, d_k,
+                         d_v, chunk, io_dtype);
+  if (st != KDA_OK) return st;
+  if (B == 0) return KDA_OK;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (T == 0) {
+    if (!S_final || S0 == S_final) return KDA_OK;
+    const size_t n = (size_t)B * H * d_k * d_v;
+    hipLaunchKernelGGL(copy_state_kernel, dim3(1024), dim3(256), 0, s, S0, S_final, n);
+    return launch_status(hipGetLastError());
+  }
+  return launch_status(kda::launch_chunk(q, k, v, log_alpha, beta, S0, out, S_final, nullptr, B,
+                                         T, H, d_k, d_v, scale, io_dtype == KDA_IO_BF16, s));
+}
+
+int kda_chunk_fwd_varlen(const void* q, const void* k, const void* v, const float* log_alpha,
+                         const float* beta, const float* S0, void* out, float* S_final,
+                         const int32_t* cu_seqlens, int N, int T_total, int H, int d_k, int d_v,
+                         float scale, int chunk, int io_dtype, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  if (N < 0 || T_total < 0 || H <= 0) return KDA_ERR_DIM;
+  if (!cu_seqlens) return KDA_ERR_NULL;
+  const size_t rows = (size_t)T_total;
+  int st = check_prefill(q, k, v, log_alpha, beta, S0, out, S_final, cu_seqlens, rows, N, H, d_k,
+                         d_v, chunk, io_dtype);
+  if (st != KDA_OK) return st;
+  if (N == 0) return KDA_OK;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  return launch_status(kda::launch_chunk(q, k, v, log_alpha, beta, S0, out, S_final, cu_seqlens,
+                                         N, T_total, H, d_k, d_v, scale,
+                                         io_dtype == KDA_IO_BF16, s));
+}
+
+int kda_decode_step(const void* q, const void* k, const void* v, const float* log_alpha,
+                    const float* beta, float* S_inout, void* out, int N, int H, int d_k, int d_v,
+                    float scale, int io_dtype, void* stream) {
+  if (N < 0 || H <= 0) return KDA_ERR_DIM;
+  if (!io_ok(io_dtype)) return KDA_ERR_UNSUPPORTED;
+  if (!((d_k == 64 || d_k == 128) && (d_v == 64 || d_v == 128))) return KDA_ERR_UNSUPPORTED;
+  if (N == 0) return KDA_OK;
+  if (!q || !k || !v || !log_alpha || !beta || !S_inout || !out) return KDA_ERR_NULL;
+  const size_t e = io_bytes(io_dtype);
+  const size_t heads = (size_t)N * H;
+  const Range in[] = {span(q, heads * d_k * e), span(k, heads * d_k * e), span(v, heads * d_v * e),
+                      span(log_alpha, heads * d_k * 4), span(beta, heads * 4)};
+  const Range ro = span(out, heads * d_v * e);
+  const Range rs = span(S_inout, heads * d_k * d_v * 4);
+  for (const Range& r : in) {
+    if (overlap(ro, r) || overlap(rs, r)) return KDA_ERR_ALIAS;
+  }
+  if (overlap(ro, rs)) return KDA_ERR_ALIAS;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  return launch_status(kda::launch_decode(q, k, v, log_alpha, beta, S_inout, out, (int)heads, d_k,
+                                          d_v, scale, io_dtype == KDA_IO_BF16, s));
+}
+
+}  // extern "C"

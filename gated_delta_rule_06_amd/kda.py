@@ -1,0 +1,183 @@
+"""Python binding of the KDA C ABI (include/kda.h): argument marshalling only.
+
+Every step of the forward runs in ``libkda.so``'s HIP kernels; this module
+checks tensor shapes/dtypes, passes raw device pointers and the current HIP
+stream, and turns status codes into exceptions.  PyTorch only provides device
+memory and streams.  There is no fallback: if the library is missing, importing
+this module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libkda.so")
+
+KDA_IO_F32 = 0
+KDA_IO_BF16 = 1
+CHUNK = 64
+
+
+class KdaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__("%s: %s (status %d)" % (where, status_string(status), status))
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libkda.so is not built (%s); run `python -m gated_delta_rule_06_amd.build`"
+                          % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, fp, i, sz, f = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_float
+    lib.kda_chunk_fwd.restype = i
+    lib.kda_chunk_fwd.argtypes = [vp, vp, vp, fp, fp, fp, vp, fp, i, i, i, i, i, f, i, i, vp, sz, vp]
+    lib.kda_chunk_fwd_varlen.restype = i
+    lib.kda_chunk_fwd_varlen.argtypes = [vp, vp, vp, fp, fp, fp, vp, fp, vp, i, i, i, i, i, f, i, i,
+                                         vp, sz, vp]
+    lib.kda_decode_step.restype = i
+    lib.kda_decode_step.argtypes = [vp, vp, vp, fp, fp, fp, vp, i, i, i, i, f, i, vp]
+    lib.kda_chunk_fwd_workspace_size.restype = sz
+    lib.kda_chunk_fwd_workspace_size.argtypes = [i] * 7
+    lib.kda_chunk_fwd_varlen_workspace_size.restype = sz
+    lib.kda_chunk_fwd_varlen_workspace_size.argtypes = [i] * 7
+    lib.kda_status_string.restype = ctypes.c_char_p
+    lib.kda_status_string.argtypes = [i]
+    lib.kda_version.restype = i
+    lib.kda_version.argtypes = []
+    return lib
+
+
+lib = _load()
+
+
+def status_string(status: int) -> str:
+    return lib.kda_status_string(int(status)).decode()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _io_code(dtype):
+    if dtype == torch.bfloat16:
+        return KDA_IO_BF16
+    if dtype == torch.float32:
+        return KDA_IO_F32
+    raise TypeError("q/k/v must be bfloat16 or float32, got %s" % dtype)
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check(t, name, shape, dtype, device):
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if t.dtype != dtype:
+        raise TypeError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
+    if t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _workspace(nbytes, device):
+    if nbytes == 0:
+        return None, 0
+    return torch.empty(nbytes, dtype=torch.uint8, device=device), nbytes
+
+
+def chunk_fwd(q, k, v, log_alpha, beta, S0=None, scale=None, chunk=CHUNK, out=None,
+              S_final=None, output_final_state=True):
+    """Chunkwise KDA prefill.  q, k, log_alpha: [B, T, H, d_k]; v: [B, T, H, d_v];
+    beta: [B, T, H]; S0: [B, H, d_k, d_v] fp32 or None.  Returns (o, S_final)."""
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    if scale is None:
+        scale = dk ** -0.5
+    for name, t, shp, dt in (("q", q, (B, T, H, dk), q.dtype), ("k", k, (B, T, H, dk), q.dtype),
+                             ("v", v, (B, T, H, dv), q.dtype),
+                             ("log_alpha", log_alpha, (B, T, H, dk), torch.float32),
+                             ("beta", beta, (B, T, H), torch.float32),
+                             ("S0", S0, (B, H, dk, dv), torch.float32)):
+        _check(t, name, shp, dt, dev)
+    io = _io_code(q.dtype)
+    if out is None:
+        out = torch.empty((B, T, H, dv), dtype=q.dtype, device=dev)
+    _check(out, "out", (B, T, H, dv), q.dtype, dev)
+    if S_final is None and output_final_state:
+        S_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    _check(S_final, "S_final", (B, H, dk, dv), torch.float32, dev)
+    ws, wsb = _workspace(lib.kda_chunk_fwd_workspace_size(B, T, H, dk, dv, chunk, io), dev)
+    st = lib.kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S0),
+                           _ptr(out), _ptr(S_final), B, T, H, dk, dv, float(scale), int(chunk), io,
+                           _ptr(ws), wsb, _stream(dev))
+    if st != 0:
+        raise KdaError(st, "kda_chunk_fwd")
+    return out, S_final
+
+
+def chunk_fwd_varlen(q, k, v, log_alpha, beta, cu_seqlens, S0=None, scale=None, chunk=CHUNK,
+                     out=None, S_final=None, output_final_state=True):
+    """Packed variable-length prefill.  q, k, log_alpha: [T_total, H, d_k];
+    v: [T_total, H, d_v]; beta: [T_total, H]; cu_seqlens: int32 [N+1] on the
+    device; S0: [N, H, d_k, d_v] fp32 or None.  Returns (o, S_final)."""
+    Tt, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    N = cu_seqlens.shape[0] - 1
+    if scale is None:
+        scale = dk ** -0.5
+    for name, t, shp, dt in (("q", q, (Tt, H, dk), q.dtype), ("k", k, (Tt, H, dk), q.dtype),
+                             ("v", v, (Tt, H, dv), q.dtype),
+                             ("log_alpha", log_alpha, (Tt, H, dk), torch.float32),
+                             ("beta", beta, (Tt, H), torch.float32),
+                             ("cu_seqlens", cu_seqlens, (N + 1,), torch.int32),
+                             ("S0", S0, (N, H, dk, dv), torch.float32)):
+        _check(t, name, shp, dt, dev)
+    io = _io_code(q.dtype)
+    if out is None:
+        out = torch.empty((Tt, H, dv), dtype=q.dtype, device=dev)
+    _check(out, "out", (Tt, H, dv), q.dtype, dev)
+    if S_final is None and output_final_state:
+        S_final = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    _check(S_final, "S_final", (N, H, dk, dv), torch.float32, dev)
+    ws, wsb = _workspace(lib.kda_chunk_fwd_varlen_workspace_size(N, Tt, H, dk, dv, chunk, io), dev)
+    st = lib.kda_chunk_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                                  _ptr(S0), _ptr(out), _ptr(S_final), _ptr(cu_seqlens), N, Tt, H,
+                                  dk, dv, float(scale), int(chunk), io, _ptr(ws), wsb, _stream(dev))
+    if st != 0:
+        raise KdaError(st, "kda_chunk_fwd_varlen")
+    return out, S_final
+
+
+def decode_step(q, k, v, log_alpha, beta, S_inout, scale=None, out=None):
+    """One fused recurrent step.  q, k, log_alpha: [N, H, d_k]; v: [N, H, d_v];
+    beta: [N, H]; S_inout: [N, H, d_k, d_v] fp32, updated in place.  Returns o."""
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    if scale is None:
+        scale = dk ** -0.5
+    for name, t, shp, dt in (("q", q, (N, H, dk), q.dtype), ("k", k, (N, H, dk), q.dtype),
+                             ("v", v, (N, H, dv), q.dtype),
+                             ("log_alpha", log_alpha, (N, H, dk), torch.float32),
+                             ("beta", beta, (N, H), torch.float32),
+                             ("S_inout", S_inout, (N, H, dk, dv), torch.float32)):
+        _check(t, name, shp, dt, dev)
+    io = _io_code(q.dtype)
+    if out is None:
+        out = torch.empty((N, H, dv), dtype=q.dtype, device=dev)
+    _check(out, "out", (N, H, dv), q.dtype, dev)
+    st = lib.kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                             _ptr(S_inout), _ptr(out), N, H, dk, dv, float(scale), io, _stream(dev))
+    if st != 0:
+        raise KdaError(st, "kda_decode_step")
+    return out

@@ -1,0 +1,153 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) Kimi Delta Attention forward library.
+ *
+ * The operation (one head; S is d_k x d_v, row = key channel, column = value
+ * channel; g = log alpha with natural log, g <= 0):
+ *
+ *   Sbar_t = Diag(exp(g_t)) S_{t-1}
+ *   S_t    = Sbar_t + beta_t k_t (v_t - Sbar_t^T k_t)^T
+ *   o_t    = S_t^T (scale * q_t)
+ *
+ * Definition: "Kimi Unveils Delta Attention and K3 Architecture Updates",
+ * section 4 (Kimi Delta Attention: forget each key channel, predict, correct,
+ * write, read) with its key-by-value reference layout, and "Kimi Delta
+ * Attention: Channel-Wise Memory Control", section "Change one piece of Gated
+ * DeltaNet" (S in R^{d_k x d_v}, decay by left multiplication).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every pointer is a DEVICE pointer on the current HIP device, unless stated.
+ *  - All arrays are dense, row-major, contiguous, with no padding.
+ *  - q, k, v, out use io_dtype (KDA_IO_F32 = float, KDA_IO_BF16 = bfloat16
+ *    bit patterns); log_alpha, beta and every state are float (fp32).
+ *  - The state is always fp32 and is kept fp32 on chip across a whole call.
+ *  - Ownership: the caller allocates and frees every buffer, including the
+ *    workspace.  The library allocates nothing, never frees, never
+ *    synchronises the device and keeps no state between calls; work is
+ *    enqueued on `stream` (a hipStream_t cast to void*, NULL = the default
+ *    stream) and results are valid once that stream has reached them.
+ *  - Aliasing: S0 == S_final is allowed (in-place state update); any other
+ *    overlap between an output and another argument is not.
+ *  - Supported sizes: d_k and d_v in {64, 128}; chunk == 64.
+ *  - Errors: every argument is validated before any work is enqueued; on a
+ *    validation error nothing is enqueued and a negative KDA_ERR_* code is
+ *    returned.  KDA_ERR_HIP reports a launch failure (hipGetLastError).
+ *    Values are not checked: NaN/Inf propagate; beta outside [0, 1], g > 0 or
+ *    non-normalised keys give the recurrence's (possibly unstable) result.
+ *  - T == 0 (or an empty packed sequence) copies S0 to S_final (zeros if S0 is
+ *    NULL) and writes no output row.
+ *  - Thread safety: calls are re-entrant; calls on different streams may run
+ *    concurrently as long as their buffers do not overlap.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum kda_io_dtype { KDA_IO_F32 = 0, KDA_IO_BF16 = 1 };
+
+enum kda_status {
+  KDA_OK = 0,
+  KDA_ERR_NULL = -1,        /* a required pointer is NULL */
+  KDA_ERR_DIM = -2,         /* a size is negative or inconsistent */
+  KDA_ERR_UNSUPPORTED = -3, /* d_k, d_v, chunk or io_dtype not supported */
+  KDA_ERR_WORKSPACE = -4,   /* workspace missing or smaller than required */
+  KDA_ERR_HIP = -5,         /* a HIP launch failed */
+  KDA_ERR_ALIAS = -6        /* an output overlaps an input (other than S0 == S_final) */
+};
+
+/*
+ * kda_chunk_fwd -- chunkwise prefill over a batch of equal-length sequences.
+ *
+ * Computes exactly the recurrence above for every (b, h), scheduled chunk by
+ * chunk as in "Kimi Unveils Delta Attention and K3 Architecture Updates",
+ * section 6 (Chunkwise KDA): chunk-local cumulative decay, the causal
+ * key-key system resolved by a unit-lower-triangular inverse, the
+ * fast-forwarded state and the causal outputs.  A last partial chunk behaves
+ * as if padded with tokens that leave the state unchanged.
+ *
+ *  q, k       [B, T, H, d_k]  io_dtype
+ *  v          [B, T, H, d_v]  io_dtype
+ *  log_alpha  [B, T, H, d_k]  fp32, g = log alpha (natural log)
+ *  beta       [B, T, H]       fp32
+ *  S0         [B, H, d_k, d_v] fp32, or NULL for a zero initial state
+ *  out        [B, T, H, d_v]  io_dtype (bf16 results are rounded to nearest even)
+ *  S_final    [B, H, d_k, d_v] fp32, or NULL to skip
+ *  scale      multiplies q (the pages' default is d_k^-1/2)
+ *  chunk      tokens per chunk; must be 64
+ *  workspace  device scratch of at least kda_chunk_fwd_workspace_size(...)
+ *             bytes (may be NULL when that size is 0)
+ * Returns KDA_OK or a KDA_ERR_* code.
+ */
+int kda_chunk_fwd(const void* q, const void* k, const void* v, const float* log_alpha,
+                  const float* beta, const float* S0, void* out, float* S_final, int B, int T,
+                  int H, int d_k, int d_v, float scale, int chunk, int io_dtype, void* workspace,
+                  size_t workspace_bytes, void* stream);
+
+/*
+ * kda_chunk_fwd_varlen -- chunkwise prefill over N packed variable-length
+ * sequences.  Sequence n owns tokens [cu_seqlens[n], cu_seqlens[n+1]) of the
+ * packed token axis; its state starts from S0[n] and never crosses into
+ * another sequence ("Linear Attention, From Scratch to Kimi 3", section 9,
+ * cu_seqlens).  Chunks never straddle two sequences.
+ *
+ *  q, k       [T_total, H, d_k]  io_dtype
+ *  v, out     [T_total, H, d_v]  io_dtype
+ *  log_alpha  [T_total, H, d_k]  fp32
+ *  beta       [T_total, H]       fp32
+ *  S0         [N, H, d_k, d_v]   fp32 or NULL (zeros)
+ *  S_final    [N, H, d_k, d_v]   fp32 or NULL
+ *  cu_seqlens [N + 1] int32, DEVICE memory: cu_seqlens[0] == 0,
+ *             non-decreasing, cu_seqlens[N] == T_total.  These preconditions
+ *             are not checked on the device (the values are never read on the
+ *             host); a violation gives undefined results.
+ * Returns KDA_OK or a KDA_ERR_* code.
+ */
+int kda_chunk_fwd_varlen(const void* q, const void* k, const void* v, const float* log_alpha,
+                         const float* beta, const float* S0, void* out, float* S_final,
+                         const int32_t* cu_seqlens, int N, int T_total, int H, int d_k, int d_v,
+                         float scale, int chunk, int io_dtype, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/*
+ * kda_decode_step -- one token for each of N sequences: the fused recurrent
+ * step ("Kimi Unveils Delta Attention and K3 Architecture Updates", section 5:
+ * decay, prediction reduction, outer-product write, read reduction).  Each
+ * head's fp32 state is read once and written once.
+ *
+ *  q, k       [N, H, d_k]  io_dtype
+ *  v, out     [N, H, d_v]  io_dtype
+ *  log_alpha  [N, H, d_k]  fp32
+ *  beta       [N, H]       fp32
+ *  S_inout    [N, H, d_k, d_v] fp32, updated in place
+ * Returns KDA_OK or a KDA_ERR_* code.
+ */
+int kda_decode_step(const void* q, const void* k, const void* v, const float* log_alpha,
+                    const float* beta, float* S_inout, void* out, int N, int H, int d_k, int d_v,
+                    float scale, int io_dtype, void* stream);
+
+/* Workspace bytes kda_chunk_fwd needs for these sizes (0 if none; the
+ * arguments are not validated here: unsupported sizes give 0). */
+size_t kda_chunk_fwd_workspace_size(int B, int T, int H, int d_k, int d_v, int chunk,
+                                    int io_dtype);
+
+/* Workspace bytes kda_chunk_fwd_varlen needs for these sizes. */
+size_t kda_chunk_fwd_varlen_workspace_size(int N, int T_total, int H, int d_k, int d_v,
+                                           int chunk, int io_dtype);
+
+/* A static, human-readable name for a status code. */
+const char* kda_status_string(int status);
+
+/* Library ABI version (major * 10000 + minor * 100 + patch). */
+int kda_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

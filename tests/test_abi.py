@@ -1,0 +1,115 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+include/kda.h declares, and rejects bad arguments before enqueuing any work
+(every call here returns from validation, so no HIP call is made)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from gated_delta_rule_06_amd import build as b
+    if not os.path.exists(b.LIB):
+        b.build()
+    from gated_delta_rule_06_amd import kda
+    return kda.lib
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for want in ("kda_chunk_fwd", "kda_chunk_fwd_varlen", "kda_decode_step",
+                 "kda_chunk_fwd_workspace_size", "kda_chunk_fwd_varlen_workspace_size",
+                 "kda_status_string", "kda_version"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), "libkda.so does not export %s" % name
+
+
+def test_status_strings_and_version(lib):
+    from gated_delta_rule_06_amd import kda
+    assert kda.status_string(0) == "KDA_OK"
+    for code in range(-1, -7, -1):
+        assert kda.status_string(code).startswith("KDA_ERR_")
+    assert "unknown" in kda.status_string(-99)
+    assert lib.kda_version() >= 100
+
+
+def test_workspace_is_zero(lib):
+    assert lib.kda_chunk_fwd_workspace_size(8, 8192, 32, 128, 128, 64, 1) == 0
+    assert lib.kda_chunk_fwd_varlen_workspace_size(16, 537014, 32, 128, 128, 64, 1) == 0
+
+
+P = [ctypes.c_void_p(0x10000000 + 0x1000000 * i) for i in range(12)]   # never dereferenced
+
+
+def chunk(lib, q=P[0], k=P[1], v=P[2], g=P[3], beta=P[4], S0=None, out=P[5], Sf=P[6], B=1, T=64,
+          H=2, dk=128, dv=128, chunk=64, io=1):
+    return lib.kda_chunk_fwd(q, k, v, g, beta, S0, out, Sf, B, T, H, dk, dv, 0.1, chunk, io, None,
+                             0, None)
+
+
+def test_chunk_fwd_validation(lib):
+    from gated_delta_rule_06_amd import kda
+    assert chunk(lib, q=None) == -1                       # KDA_ERR_NULL
+    assert chunk(lib, beta=None) == -1
+    assert chunk(lib, B=-1) == -2                         # KDA_ERR_DIM
+    assert chunk(lib, T=-5) == -2
+    assert chunk(lib, H=0) == -2
+    assert chunk(lib, chunk=32) == -3                     # KDA_ERR_UNSUPPORTED
+    assert chunk(lib, dk=96) == -3
+    assert chunk(lib, dv=256) == -3
+    assert chunk(lib, io=7) == -3
+    assert chunk(lib, io=0) == -3                         # fp32 I/O only for d_k = d_v = 64
+    assert chunk(lib, out=P[0]) == -6                     # KDA_ERR_ALIAS: out == q
+    assert chunk(lib, Sf=P[5]) == -6                      # S_final == out
+    assert chunk(lib, B=0) == 0                           # nothing to do, nothing enqueued
+    assert kda.status_string(chunk(lib, q=None)).startswith("KDA_ERR_NULL")
+
+
+def test_varlen_validation(lib):
+    f = lib.kda_chunk_fwd_varlen
+    args = lambda **kw: (kw.get("q", P[0]), P[1], P[2], P[3], P[4], None, kw.get("out", P[5]),
+                         P[6], kw.get("cu", P[7]), kw.get("N", 3), kw.get("Tt", 100), 2,
+                         kw.get("dk", 128), 128, 0.1, kw.get("chunk", 64), 1, None, 0, None)
+    assert f(*args(cu=None)) == -1
+    assert f(*args(N=-1)) == -2
+    assert f(*args(Tt=-1)) == -2
+    assert f(*args(dk=32)) == -3
+    assert f(*args(chunk=16)) == -3
+    assert f(*args(out=P[1])) == -6
+    assert f(*args(N=0)) == 0
+
+
+def test_decode_validation(lib):
+    f = lib.kda_decode_step
+    args = lambda **kw: (kw.get("q", P[0]), P[1], P[2], P[3], P[4], kw.get("S", P[5]),
+                         kw.get("out", P[6]), kw.get("N", 4), 2, kw.get("dk", 128), 128, 0.1,
+                         kw.get("io", 1), None)
+    assert f(*args(q=None)) == -1
+    assert f(*args(S=None)) == -1
+    assert f(*args(N=-3)) == -2
+    assert f(*args(dk=100)) == -3
+    assert f(*args(io=3)) == -3
+    assert f(*args(out=P[5])) == -6                       # out overlaps the state
+    assert f(*args(N=0)) == 0
+
+
+def test_product_path_has_no_oracle_or_cpu_fallback():
+    """The library binding must not import the oracle or compute on the CPU."""
+    src = open(os.path.join(ROOT, "gated_delta_rule_06_amd", "kda.py")).read()
+    assert "oracle" not in src
+    assert "numpy" not in src

@@ -1,0 +1,181 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on the
+same seeded inputs.  Bars: rel-L2 <= 1e-4 for fp32 I/O and <= 2e-2 for bf16
+I/O with fp32 state, on both the outputs o and the final state S_T."""
+import numpy as np
+import pytest
+import torch
+
+from gated_delta_rule_06_amd import inputs
+from parity_util import (assert_close, gpu_chains_batched, gpu_chains_varlen, oracle_batched,
+                         oracle_varlen, rel_l2, tol_for)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def kda():
+    from gated_delta_rule_06_amd import kda as k
+    return k
+
+
+def note(msg):
+    print(msg, flush=True)
+
+
+# ------------------------------------------------------------------ prefill
+
+PREFILL_CASES = [
+    # (B, T, H, dk, dv, io, with_S0)
+    (1, 256, 1, 64, 64, "f32", False),      # the single-head fp32 workload
+    (1, 64, 2, 64, 64, "f32", True),
+    (1, 1, 1, 64, 64, "f32", True),
+    (2, 300, 3, 128, 128, "bf16", True),    # several chunks + ragged tail
+    (1, 65, 2, 128, 128, "bf16", False),
+    (1, 63, 2, 128, 128, "bf16", True),
+    (3, 130, 2, 64, 128, "bf16", True),
+    (2, 200, 2, 128, 64, "bf16", True),
+    (1, 129, 4, 64, 64, "bf16", False),
+]
+
+
+@pytest.mark.parametrize("B,T,H,dk,dv,io,with_S0", PREFILL_CASES)
+def test_chunk_fwd_matches_oracle(B, T, H, dk, dv, io, with_S0):
+    note("chunk_fwd B=%d T=%d H=%d dk=%d dv=%d io=%s S0=%s" % (B, T, H, dk, dv, io, with_S0))
+    d = inputs.prefill_inputs(B, T, H, dk, dv, io=io, seed=B * 1000 + T, with_S0=with_S0,
+                              device=DEV)
+    o, S = kda().chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], S0=d["S0"])
+    torch.cuda.synchronize()
+    chains = [(b, h) for b in range(B) for h in range(H)]
+    ro, rs = oracle_batched(d, chains)
+    go, gs = gpu_chains_batched(o, S, chains)
+    assert_close(go, gs, ro, rs, tol_for(io), "chunk")
+
+
+def test_prefill_h16_t4096_with_S0():
+    """The B=1, H=16, T=4096, d=128 bf16 workload with a random fp32 S0."""
+    cfg = inputs.CONFIGS["prefill_h16_s0"]
+    note("prefill_h16_s0 full")
+    d = inputs.prefill_inputs(cfg["B"], cfg["T"], cfg["H"], cfg["dk"], cfg["dv"], io=cfg["io"],
+                              seed=0, with_S0=True, device=DEV)
+    o, S = kda().chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], S0=d["S0"])
+    torch.cuda.synchronize()
+    chains = [(0, h) for h in range(cfg["H"])]
+    ro, rs = oracle_batched(d, chains)
+    go, gs = gpu_chains_batched(o, S, chains)
+    assert_close(go, gs, ro, rs, tol_for("bf16"), "prefill_h16_s0")
+
+
+def test_headline_prefill_sampled_chains():
+    """B=8, H=32, T=8192, d=128 bf16 at full size in the benchmark's launch;
+    the oracle recomputes a sample of chains one by one."""
+    cfg = inputs.CONFIGS["prefill_b8_h32_t8192"]
+    note("prefill_b8_h32_t8192 full, sampled chains")
+    d = inputs.prefill_inputs(cfg["B"], cfg["T"], cfg["H"], cfg["dk"], cfg["dv"], io=cfg["io"],
+                              seed=0, with_S0=False, device=DEV)
+    o, S = kda().chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"])
+    torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all() and torch.isfinite(S).all()
+    chains = [(0, 0), (3, 17), (7, 31)]
+    ro, rs = oracle_batched(d, chains)
+    go, gs = gpu_chains_batched(o, S, chains)
+    assert_close(go, gs, ro, rs, tol_for("bf16"), "headline sampled")
+
+
+# ------------------------------------------------------------------ varlen
+
+VARLEN_CASES = [
+    ([1, 63, 64, 65, 130, 0, 200], 2, 128, 128, "bf16", True),
+    ([256, 3, 77], 1, 64, 64, "f32", True),
+    ([0], 2, 128, 128, "bf16", True),
+    ([5, 0, 0, 9], 3, 64, 128, "bf16", False),
+]
+
+
+@pytest.mark.parametrize("lens,H,dk,dv,io,with_S0", VARLEN_CASES)
+def test_varlen_matches_oracle(lens, H, dk, dv, io, with_S0):
+    note("varlen lens=%s H=%d dk=%d dv=%d io=%s" % (lens, H, dk, dv, io))
+    d = inputs.varlen_inputs(lens, H, dk, dv, io=io, seed=len(lens), with_S0=with_S0,
+                             long_channels=min(8, dk // 4), device=DEV)
+    o, S = kda().chunk_fwd_varlen(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"],
+                                  S0=d["S0"])
+    torch.cuda.synchronize()
+    chains = [(n, h) for n in range(d["N"]) for h in range(H)]
+    ro, rs = oracle_varlen(d, chains)
+    go, gs = gpu_chains_varlen(o, S, d["cu_seqlens"], chains)
+    if sum(lens) == 0:
+        np.testing.assert_array_equal(gs, rs)   # state copied through untouched
+    else:
+        assert_close(go, gs, ro, rs, tol_for(io), "varlen")
+
+
+def test_varlen_16seq_sampled_chains():
+    """16 packed sequences of U{1024..65536} tokens (seed 0), H=32, with 8
+    long-horizon key channels per head; the oracle checks the shortest and the
+    longest sequence at two heads."""
+    cfg = inputs.CONFIGS["varlen_16seq_h32"]
+    lens = inputs.varlen_lengths(cfg["n_seq"], cfg["lo"], cfg["hi"], seed=0)
+    note("varlen_16seq_h32 total=%d" % int(lens.sum()))
+    d = inputs.varlen_inputs(lens, cfg["H"], cfg["dk"], cfg["dv"], io=cfg["io"], seed=0,
+                             long_channels=cfg["long_channels"], device=DEV)
+    o, S = kda().chunk_fwd_varlen(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"])
+    torch.cuda.synchronize()
+    assert torch.isfinite(S).all()
+    chains = [(int(np.argmin(lens)), 0), (int(np.argmax(lens)), 5)]
+    ro, rs = oracle_varlen(d, chains)
+    go, gs = gpu_chains_varlen(o, S, d["cu_seqlens"], chains)
+    assert_close(go, gs, ro, rs, tol_for("bf16"), "varlen sampled")
+
+
+# ------------------------------------------------------------------ decode
+
+@pytest.mark.parametrize("N,H,dk,dv,io", [(4, 3, 128, 128, "bf16"), (3, 2, 64, 64, "f32"),
+                                          (2, 2, 64, 128, "bf16"), (2, 3, 128, 64, "f32")])
+def test_decode_steps_match_oracle(N, H, dk, dv, io):
+    steps = 12
+    note("decode N=%d H=%d dk=%d dv=%d io=%s" % (N, H, dk, dv, io))
+    d = inputs.decode_inputs(N, H, dk, dv, steps, io=io, seed=7, device=DEV)
+    S = d["S"].clone()
+    outs = []
+    for t in range(steps):
+        outs.append(kda().decode_step(d["q"][t], d["k"][t], d["v"][t], d["g"][t], d["beta"][t], S))
+    torch.cuda.synchronize()
+    # oracle: the same steps as one sequence per (n, h) in the packed layout
+    import oracle
+    from gated_delta_rule_06_amd.inputs import to_host
+    q = to_host(d["q"].transpose(0, 1).contiguous())        # [N, steps, H, dk]
+    k = to_host(d["k"].transpose(0, 1).contiguous())
+    v = to_host(d["v"].transpose(0, 1).contiguous())
+    g = to_host(d["g"].transpose(0, 1).contiguous())
+    b = to_host(d["beta"].transpose(0, 1).contiguous())
+    ro, rs = oracle.forward_dense(q, k, v, g, b, S0=to_host(d["S"]))
+    go = torch.stack(outs, 1).float().cpu().numpy()         # [N, steps, H, dv]
+    tol = tol_for(io) if io == "bf16" else 1e-5
+    eo, es = rel_l2(go, ro), rel_l2(S.cpu().numpy(), rs)
+    note("decode rel-L2 o=%.3e S=%.3e" % (eo, es))
+    assert eo <= tol and es <= tol
+
+
+def test_decode_full_size_128_steps_sampled():
+    """256 sequences x 32 heads, fp32 state (512 MiB), 128 chained steps in the
+    benchmark's launch; the oracle carries its own fp64 state for sampled heads."""
+    cfg = inputs.CONFIGS["decode_n256_h32"]
+    N, H, dk, dv, steps = cfg["N"], cfg["H"], cfg["dk"], cfg["dv"], cfg["steps"]
+    note("decode_n256_h32 full, %d steps" % steps)
+    d = inputs.decode_inputs(N, H, dk, dv, steps, io=cfg["io"], seed=0, device=DEV)
+    S = d["S"].clone()
+    S_init = d["S"][[0, 100, 255]].clone()
+    out_keep = []
+    for t in range(steps):
+        o = kda().decode_step(d["q"][t], d["k"][t], d["v"][t], d["g"][t], d["beta"][t], S)
+        out_keep.append(o[[0, 100, 255]].clone())
+    torch.cuda.synchronize()
+    import oracle
+    from gated_delta_rule_06_amd.inputs import to_host
+    sel = [0, 100, 255]
+    pick = lambda t: to_host(t[:, sel].transpose(0, 1).contiguous())
+    ro, rs = oracle.forward_dense(pick(d["q"]), pick(d["k"]), pick(d["v"]), pick(d["g"]),
+                                  pick(d["beta"]), S0=to_host(S_init))
+    go = torch.stack(out_keep, 1).float().cpu().numpy()
+    eo, es = rel_l2(go, ro), rel_l2(S[sel].cpu().numpy(), rs)
+    note("decode full rel-L2 o=%.3e S=%.3e" % (eo, es))
+    assert eo <= 2e-2 and es <= 2e-2
