@@ -1,0 +1,244 @@
+#!/usr/bin/env python3
+"""Benchmark of the KDA forward on one MI355X.
+
+A step is one chunkwise prefill (kda_chunk_fwd) of the headline workload
+B=8, H=32, T=8192, d_k=d_v=128, bf16 q/k/v/o, fp32 gates and state, chunk 64,
+S0 = NULL (65,536 tokens), with inputs already resident in HBM.  `value` is
+prefill tokens/s (B*T per step).  The same run also measures the decode
+workload (256 sequences x 32 heads, fp32 state of 512 MiB, 128 chained
+kda_decode_step calls) and reports its steps/s.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA, published
+
+PREFILL = dict(B=8, T=8192, H=32, dk=128, dv=128, io="bf16", chunk=64)
+DECODE = dict(N=256, H=32, dk=128, dv=128, io="bf16", steps=128)
+
+
+def prefill_alg_bytes(B, T, H, dk, dv, io, with_S0=False, with_S_final=True):
+    """Inputs read once and outputs written once: q, k (dk), v, o (dv) in the
+    I/O type, log_alpha (dk) and beta in fp32, plus the fp32 states."""
+    e = 2 if io == "bf16" else 4
+    per_ht = e * (2 * dk + 2 * dv) + 4 * dk + 4
+    states = B * H * dk * dv * 4 * (int(with_S0) + int(with_S_final))
+    return B * T * H * per_ht + states
+
+
+def prefill_alg_flops(B, T, H, dk, dv, C=64):
+    """Chunkwise method per head-token: 6 dk dv + 2C(3dk + 2dv) + C^2/3."""
+    return B * T * H * (6 * dk * dv + 2 * C * (3 * dk + 2 * dv) + C * C / 3)
+
+
+def decode_alg_bytes(N, H, dk, dv, io):
+    e = 2 if io == "bf16" else 4
+    return N * H * (2 * dk * dv * 4 + e * (2 * dk + 2 * dv) + 4 * dk + 4)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-reps", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-chains", type=int, default=32,
+                    help="chains of the prefill workload the oracle runs for the CPU baseline")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run a plain device copy of this size (for counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        msg = ("bench.py measures one GPU only: this build runs the KDA forward on a single "
+               "MI355X (how the path would shard is described in DESIGN.md); got --gpus %d, "
+               "WORLD_SIZE %d" % (args.gpus, world))
+        print(msg, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from gated_delta_rule_06_amd import inputs, kda
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    P = PREFILL
+    log("generating prefill inputs", P)
+    d = inputs.prefill_inputs(P["B"], P["T"], P["H"], P["dk"], P["dv"], io=P["io"], seed=0,
+                              with_S0=False, device=dev)
+    out = torch.empty((P["B"], P["T"], P["H"], P["dv"]), dtype=torch.bfloat16, device=dev)
+    Sf = torch.empty((P["B"], P["H"], P["dk"], P["dv"]), dtype=torch.float32, device=dev)
+
+    def step():
+        kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], S0=None, out=out, S_final=Sf)
+
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib << 20
+        a = torch.empty(n // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        for _ in range(2):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        log("calibration copy of %d MiB done" % args.calib_copy_mib)
+        del a, b
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s, e in ev:
+        s.record(stream)
+        step()
+        e.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = [s.elapsed_time(e) for s, e in ev]
+    ms_per_step = 1e3 * wall / args.steps
+    avg_kernel_ms = float(np.mean(kern_ms))
+    tokens = P["B"] * P["T"]
+    value = tokens / (wall / args.steps)
+    alg_b = prefill_alg_bytes(P["B"], P["T"], P["H"], P["dk"], P["dv"], P["io"])
+    alg_f = prefill_alg_flops(P["B"], P["T"], P["H"], P["dk"], P["dv"])
+    achieved = alg_b / (avg_kernel_ms * 1e-3) / 1e9
+    log("prefill: %.3f ms/step (wall), kernel %.3f ms avg (min %.3f), %.3e tokens/s, %.0f GB/s"
+        % (ms_per_step, avg_kernel_ms, min(kern_ms), value, achieved))
+
+    # ---------------------------------------------------------------- decode
+    D = DECODE
+    del d
+    torch.cuda.empty_cache()
+    log("generating decode inputs", D)
+    dd = inputs.decode_inputs(D["N"], D["H"], D["dk"], D["dv"], D["steps"], io=D["io"], seed=0,
+                              device=dev)
+    S = dd["S"]
+    o_dec = torch.empty((D["N"], D["H"], D["dv"]), dtype=torch.bfloat16, device=dev)
+
+    def decode_run():
+        for t in range(D["steps"]):
+            kda.decode_step(dd["q"][t], dd["k"][t], dd["v"][t], dd["g"][t], dd["beta"][t], S,
+                            out=o_dec)
+
+    decode_run()   # warm-up run
+    torch.cuda.synchronize()
+    dk_ms = []
+    dec_walls = []
+    for _ in range(args.decode_reps):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(D["steps"])]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for t in range(D["steps"]):
+            evs[t][0].record(stream)
+            kda.decode_step(dd["q"][t], dd["k"][t], dd["v"][t], dd["g"][t], dd["beta"][t], S,
+                            out=o_dec)
+            evs[t][1].record(stream)
+        torch.cuda.synchronize()
+        dec_walls.append(time.perf_counter() - t0)
+        dk_ms += [a.elapsed_time(b) for a, b in evs]
+    dec_wall = float(np.median(dec_walls))
+    dec_steps_s = D["steps"] / dec_wall
+    dec_kernel_ms = float(np.mean(dk_ms))
+    dec_b = decode_alg_bytes(D["N"], D["H"], D["dk"], D["dv"], D["io"])
+    dec_gbs = dec_b / (dec_kernel_ms * 1e-3) / 1e9
+    log("decode: %.1f steps/s (wall), kernel %.2f us avg, %.0f GB/s"
+        % (dec_steps_s, dec_kernel_ms * 1e3, dec_gbs))
+    del dd, S
+    torch.cuda.empty_cache()
+
+    # ---------------------------------------------------------------- CPU baseline
+    cpu = None
+    parity = None
+    if not args.no_cpu_baseline:
+        import oracle
+        from gated_delta_rule_06_amd.inputs import to_host
+        d = inputs.prefill_inputs(P["B"], P["T"], P["H"], P["dk"], P["dv"], io=P["io"], seed=0,
+                                  with_S0=False, device=dev)
+        step_out, step_S = kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"])
+        torch.cuda.synchronize()
+        n = max(1, min(args.cpu_chains, P["B"] * P["H"]))
+        rng = np.random.default_rng(1)
+        ids = sorted(rng.choice(P["B"] * P["H"], size=n, replace=False).tolist())
+        # gather the sampled chains as a [n, T, 1, d] batch
+        sel = lambda t: np.stack([to_host(t[c // P["H"], :, c % P["H"]].contiguous())
+                                  for c in ids])[:, :, None]
+        q, k, v, g = sel(d["q"]), sel(d["k"]), sel(d["v"]), sel(d["g"])
+        beta = np.stack([to_host(d["beta"][c // P["H"], :, c % P["H"]].contiguous())
+                         for c in ids])[:, :, None]
+        threads = min(16, oracle.default_threads())
+        log("oracle: %d chains x %d tokens on %d threads" % (n, P["T"], threads))
+        t0 = time.perf_counter()
+        outs, Sref = oracle.forward(q, k, v, g, beta, threads=threads)
+        cpu_wall = time.perf_counter() - t0
+        head_tokens = n * P["T"]
+        cpu = {"value": head_tokens / P["H"] / cpu_wall, "unit": "tokens/s", "cores": threads,
+               "kind": "oracle",
+               "sample": "%d of the %d (sequence, head) chains of the B8 H32 T8192 d128 workload "
+                         "(%d head-tokens, fp64 sequential recurrence); tokens/s counts a token "
+                         "as all %d heads, i.e. head-tokens/s / %d; wall %.2f s"
+                         % (n, P["B"] * P["H"], head_tokens, P["H"], P["H"], cpu_wall)}
+        go = np.stack([step_out[c // P["H"], :, c % P["H"]].float().cpu().numpy() for c in ids])
+        gs = np.stack([step_S[c // P["H"], c % P["H"]].cpu().numpy() for c in ids])
+        ro = np.stack(outs)
+        rel = lambda a, b: float(np.linalg.norm((a - b).ravel()) / np.linalg.norm(b.ravel()))
+        parity = {"chains": n, "rel_l2_o": rel(go, ro), "rel_l2_S": rel(gs, Sref)}
+        log("oracle %.2f s -> %.3e tokens/s; parity %s" % (cpu_wall, cpu["value"], parity))
+
+    rec = {
+        "metric": "KDA prefill tokens/s (B8 H32 T8192 d128) + decode steps/s, % of roofline",
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded: L2-normalised Gaussian q/k, Gaussian v, "
+                "log_alpha=-exp(N(-3,1)), beta=sigmoid(N(0,1)))",
+        "config": {"workload": "prefill_b8_h32_t8192", "B": P["B"], "T": P["T"], "H": P["H"],
+                   "d_k": P["dk"], "d_v": P["dv"], "chunk": P["chunk"], "io": "bf16",
+                   "state": "fp32", "S0": None},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "chunk_fwd_kernel<128,128,bf16>",
+                     "alg_bytes_per_launch": alg_b, "avg_launch_ms": avg_kernel_ms,
+                     "alg_tflops": alg_f / (avg_kernel_ms * 1e-3) / 1e12,
+                     "mfma_frac": alg_f / (avg_kernel_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS},
+        "cpu_baseline": cpu,
+        "decode": {"workload": "decode_n256_h32", "steps_per_s": dec_steps_s,
+                   "tokens_per_s": dec_steps_s * D["N"], "ms_per_step": 1e3 / dec_steps_s,
+                   "roofline": {"bound": "hbm", "achieved": dec_gbs, "peak": HBM_PEAK_GBS,
+                                "unit": "GB/s", "frac": dec_gbs / HBM_PEAK_GBS,
+                                "alg_bytes_per_launch": dec_b,
+                                "avg_launch_ms": dec_kernel_ms}},
+        "parity_sample": parity,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

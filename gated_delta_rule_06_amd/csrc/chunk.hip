@@ -12,10 +12,10 @@
 //   BV_i = beta_i v_i
 //
 // (products per key channel).  Then (section 6.3) R = strict_tril(KG KI^T)
-// holds rho_ij = beta_i <k_j, D_{j+1:i} k_i>, (section 6.5)
-// Aqk = tril(QG KI^T) holds chi_ij, and with T = (I + R)^{-1} the WY factors
-// W = T KG and U = T BV give the resolved errors E = U - W S_c (section 6.2 +
-// 6.3: E = T (BV - KG S_c)).  Finally (6.4, 6.5)
+// holds rho_ij = beta_i <k_j, D_{j+1:i} k_i>, (section 6.5) Aqk = tril(QG KI^T)
+// holds chi_ij, the provisional errors of section 6.2 are Ebar = BV - KG S_c,
+// and the resolved errors are E = (I + R)^{-1} Ebar (the causal triangular
+// solve of section 6.3).  Finally (6.4, 6.5)
 //
 //   O_c     = QG S_c + Aqk E
 //   S_{c+1} = Diag(Gamma_L) S_c + KE^T E.
@@ -30,9 +30,11 @@
 //    every other operand is read from LDS in that same k order;
 //  * operands contracted over tokens are stored row-major and read with
 //    ds_read_b64_tr_b16 (gfx950 LDS transpose read);
-//  * T is never formed off the diagonal: the four 16x16 diagonal blocks are
-//    inverted by forward substitution, and W, U come from block forward
-//    substitution X_I = T_II (B_I - sum_{J<I} R_IJ X_J);
+//  * the triangular solve runs by 16-token blocks: the four 16x16 diagonal
+//    blocks of I + R are inverted by forward substitution (S-independent, once
+//    per chunk), then X_I = T_II (Y_I - sum_{J<I} R_IJ X_J) on MFMA;
+//  * signs are folded into the stored operands (-BV, -KE, -Aqk) so that the
+//    solve yields -E directly and no extra negation is needed;
 //  * the next chunk's inputs are loaded into registers while this chunk is
 //    computed.
 //  * Exactness guard: the single chunk-start reference of KI = k / Gamma needs
@@ -48,9 +50,67 @@ typedef short i16x8 __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
-template <class P>
-__device__ __forceinline__ __attribute__((address_space(3))) P* lds_ptr(const void* p) {
-  return (__attribute__((address_space(3))) P*)(p);
+// The lane id, re-materialised wherever it is asked for: the volatile asm keeps
+// the compiler from hoisting lane-dependent addresses and constants out of the
+// chunk loop, where they would occupy registers for the whole kernel.  Each
+// phase asks once and passes it down.
+__device__ __forceinline__ int lane_fresh() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
+// No instruction may be scheduled across this point (nothing is emitted).
+// Used to bound how far the scheduler hoists loads, which otherwise keeps far
+// more values live than there are registers.
+__device__ __forceinline__ void compiler_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+// All LDS addressing is done on address_space(3) pointers (32-bit), so that
+// constant offsets fold into the ds_* instructions' immediate field.
+#define LDS __attribute__((address_space(3)))
+
+template <class P, class Q>
+__device__ __forceinline__ LDS P* lds_ptr(LDS Q* p) {
+  return (LDS P*)(p);
+}
+
+// ------------------------------------------------------------ buffer access
+// Raw buffer loads/stores with a workgroup-uniform resource: the base lives in
+// SGPRs, each lane supplies a 32-bit byte offset, and any access at or beyond
+// num_records bytes reads as zero (loads) or is dropped (stores).  That is
+// how a chunk's padding tokens come out as zeros without branches.
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+#define KDA_BUF_FLAGS 0x00020000
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           KDA_BUF_FLAGS);
+}
+template <class V> __device__ __forceinline__ V buf_load(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff = 0);
+template <> __device__ __forceinline__ uint16_t buf_load<uint16_t>(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff) {
+  return (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, soff, 0);
+}
+template <> __device__ __forceinline__ uint32_t buf_load<uint32_t>(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, off, soff, 0);
+}
+template <> __device__ __forceinline__ float buf_load<float>(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff) {
+  return __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, soff, 0));
+}
+template <> __device__ __forceinline__ u32x2 buf_load<u32x2>(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, soff, 0));
+}
+template <> __device__ __forceinline__ f32x2 buf_load<f32x2>(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff) {
+  return __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, soff, 0));
+}
+template <> __device__ __forceinline__ f32x4 buf_load<f32x4>(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, 0));
+}
+template <> __device__ __forceinline__ u32x4 buf_load<u32x4>(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, 0));
+}
+__device__ __forceinline__ void buf_store16(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), r, off, 0, 0);
 }
 
 // bf16 operands, fp32 accumulation: v_mfma_f32_16x16x32_bf16 / 16x16x16_bf16.
@@ -88,27 +148,24 @@ struct OpBf16 {
                                                     __builtin_bit_cast(bf16x8, b8), c, 0, 0, 0);
   }
   // X row-major (ld elements per row): lane gets X[row0 + l%16][k0 + 4g + e], e < 4
-  static __device__ __forceinline__ F16 ld16_rm(const T* X, int ld, int row0, int k0) {
-    const int l = lane_id();
+  static __device__ __forceinline__ F16 ld16_rm(int l, const LDS T* X, int ld, int row0, int k0) {
     return *lds_ptr<const F16>(X + (row0 + (l & 15)) * ld + k0 + 4 * (l >> 4));
   }
   // X row-major: lane gets X[k0 + 4g + e][m0 + l%16] (transpose read)
-  static __device__ __forceinline__ F16 ld16_tr(const T* X, int ld, int k0, int m0) {
-    const int l = lane_id();
+  static __device__ __forceinline__ F16 ld16_tr(int l, const LDS T* X, int ld, int k0, int m0) {
     const int j = l & 15;
-    const T* p = X + (k0 + 4 * (l >> 4) + (j >> 2)) * ld + m0 + 4 * (j & 3);
-    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p));
+    const LDS T* p = X + (k0 + 4 * (l >> 4) + (j >> 2)) * ld + m0 + 4 * (j & 3);
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS i16x4*)(p));
   }
-  static __device__ __forceinline__ F32 ld32_rm(const T* X, int ld, int row0, int k0) {
-    return F32{ld16_rm(X, ld, row0, k0), ld16_rm(X, ld, row0, k0 + 16)};
+  static __device__ __forceinline__ F32 ld32_rm(int l, const LDS T* X, int ld, int row0, int k0) {
+    return F32{ld16_rm(l, X, ld, row0, k0), ld16_rm(l, X, ld, row0, k0 + 16)};
   }
-  static __device__ __forceinline__ F32 ld32_tr(const T* X, int ld, int k0, int m0) {
-    return F32{ld16_tr(X, ld, k0, m0), ld16_tr(X, ld, k0 + 16, m0)};
+  static __device__ __forceinline__ F32 ld32_tr(int l, const LDS T* X, int ld, int k0, int m0) {
+    return F32{ld16_tr(l, X, ld, k0, m0), ld16_tr(l, X, ld, k0 + 16, m0)};
   }
   // write accumulator tile t (rows row0 + 4g + r, column col0 + l%16) transposed:
   // Xt[col0 + l%16][row0 + 4g + r] for r = 0..3 (four contiguous elements)
-  static __device__ __forceinline__ void st_ct(T* Xt, int ld, int col0, int row0, f32x4 t) {
-    const int l = lane_id();
+  static __device__ __forceinline__ void st_ct(int l, LDS T* Xt, int ld, int col0, int row0, f32x4 t) {
     *lds_ptr<F16>(Xt + (col0 + (l & 15)) * ld + row0 + 4 * (l >> 4)) = pack(t);
   }
 };
@@ -135,13 +192,11 @@ struct OpF32 {
   static __device__ __forceinline__ f32x4 mma32(F32 a, F32 b, f32x4 c) {
     return mma16(a.hi, b.hi, mma16(a.lo, b.lo, c));
   }
-  static __device__ __forceinline__ F16 ld16_rm(const T* X, int ld, int row0, int k0) {
-    const int l = lane_id();
+  static __device__ __forceinline__ F16 ld16_rm(int l, const LDS T* X, int ld, int row0, int k0) {
     return *lds_ptr<const F16>(X + (row0 + (l & 15)) * ld + k0 + 4 * (l >> 4));
   }
-  static __device__ __forceinline__ F16 ld16_tr(const T* X, int ld, int k0, int m0) {
-    const int l = lane_id();
-    const T* p = X + (k0 + 4 * (l >> 4)) * ld + m0 + (l & 15);
+  static __device__ __forceinline__ F16 ld16_tr(int l, const LDS T* X, int ld, int k0, int m0) {
+    const LDS T* p = X + (k0 + 4 * (l >> 4)) * ld + m0 + (l & 15);
     F16 r;
     r[0] = *lds_ptr<const T>(p);
     r[1] = *lds_ptr<const T>(p + ld);
@@ -149,68 +204,57 @@ struct OpF32 {
     r[3] = *lds_ptr<const T>(p + 3 * ld);
     return r;
   }
-  static __device__ __forceinline__ F32 ld32_rm(const T* X, int ld, int row0, int k0) {
-    return F32{ld16_rm(X, ld, row0, k0), ld16_rm(X, ld, row0, k0 + 16)};
+  static __device__ __forceinline__ F32 ld32_rm(int l, const LDS T* X, int ld, int row0, int k0) {
+    return F32{ld16_rm(l, X, ld, row0, k0), ld16_rm(l, X, ld, row0, k0 + 16)};
   }
-  static __device__ __forceinline__ F32 ld32_tr(const T* X, int ld, int k0, int m0) {
-    return F32{ld16_tr(X, ld, k0, m0), ld16_tr(X, ld, k0 + 16, m0)};
+  static __device__ __forceinline__ F32 ld32_tr(int l, const LDS T* X, int ld, int k0, int m0) {
+    return F32{ld16_tr(l, X, ld, k0, m0), ld16_tr(l, X, ld, k0 + 16, m0)};
   }
-  static __device__ __forceinline__ void st_ct(T* Xt, int ld, int col0, int row0, f32x4 t) {
-    const int l = lane_id();
+  static __device__ __forceinline__ void st_ct(int l, LDS T* Xt, int ld, int col0, int row0, f32x4 t) {
     *lds_ptr<F16>(Xt + (col0 + (l & 15)) * ld + row0 + 4 * (l >> 4)) = t;
   }
 };
 
-// ============================================================ raw input vectors
-// N consecutive I/O elements kept in their storage form, so that a prefetch
-// stays in flight until the next chunk unpacks it.
-template <class Io, int N> struct RawVec;
-template <> struct RawVec<IoBf16, 4> {
-  typedef u32x2 type;
-  __device__ static type load(const void* p, size_t i) {
-    return *reinterpret_cast<const u32x2*>(reinterpret_cast<const uint16_t*>(p) + i);
+// ============================================================ raw input words
+// BYTES of consecutive input kept as raw dwords, so that a prefetch stays in
+// flight until the next chunk unpacks it.  Loaded as 16-byte pieces (plus one
+// 8-byte piece when BYTES is not a multiple of 16).
+template <int BYTES>
+struct RawWords {
+  static_assert(BYTES % 8 == 0, "raw vectors are whole 8-byte pieces");
+  static constexpr int N16 = BYTES / 16, N8 = (BYTES % 16) / 8;
+  u32x4 q[N16 > 0 ? N16 : 1];
+  u32x2 d;
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+#pragma unroll
+    for (int i = 0; i < N16; ++i) q[i] = buf_load<u32x4>(r, voff + 16 * i, soff);
+    if (N8) d = buf_load<u32x2>(r, voff + 16 * N16, soff);
   }
-  __device__ static void unpack(type w, float* o) {
-    o[0] = __uint_as_float(w[0] << 16); o[1] = __uint_as_float(w[0] & 0xffff0000u);
-    o[2] = __uint_as_float(w[1] << 16); o[3] = __uint_as_float(w[1] & 0xffff0000u);
-  }
-};
-template <> struct RawVec<IoBf16, 2> {
-  typedef uint32_t type;
-  __device__ static type load(const void* p, size_t i) {
-    return *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint16_t*>(p) + i);
-  }
-  __device__ static void unpack(type w, float* o) {
-    o[0] = __uint_as_float(w << 16); o[1] = __uint_as_float(w & 0xffff0000u);
+  __device__ __forceinline__ uint32_t word(int i) const {
+    return i < 4 * N16 ? q[i / 4][i % 4] : d[i - 4 * N16];
   }
 };
-template <> struct RawVec<IoF32, 4> {
-  typedef f32x4 type;
-  __device__ static type load(const void* p, size_t i) {
-    return *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(p) + i);
+
+// N elements of I/O type Io as floats
+template <class Io, int N>
+struct RawIo {
+  RawWords<N * (int)sizeof(typename Io::storage)> w;
+  __device__ __forceinline__ void unpack(float* o) const {
+#pragma unroll
+    for (int e = 0; e < N; ++e) {
+      if (Io::is_bf16) {
+        const uint32_t x = w.word(e / 2);
+        o[e] = __uint_as_float((e & 1) ? (x & 0xffff0000u) : (x << 16));
+      } else {
+        o[e] = __uint_as_float(w.word(e));
+      }
+    }
   }
-  __device__ static void unpack(type w, float* o) { o[0] = w[0]; o[1] = w[1]; o[2] = w[2]; o[3] = w[3]; }
-};
-template <> struct RawVec<IoF32, 2> {
-  typedef f32x2 type;
-  __device__ static type load(const void* p, size_t i) {
-    return *reinterpret_cast<const f32x2*>(reinterpret_cast<const float*>(p) + i);
-  }
-  __device__ static void unpack(type w, float* o) { o[0] = w[0]; o[1] = w[1]; }
-};
-template <int N> struct RawG;
-template <> struct RawG<4> {
-  typedef f32x4 type;
-  __device__ static type load(const float* p, size_t i) { return *reinterpret_cast<const f32x4*>(p + i); }
-  __device__ static void unpack(type w, float* o) { o[0] = w[0]; o[1] = w[1]; o[2] = w[2]; o[3] = w[3]; }
-};
-template <> struct RawG<2> {
-  typedef f32x2 type;
-  __device__ static type load(const float* p, size_t i) { return *reinterpret_cast<const f32x2*>(p + i); }
-  __device__ static void unpack(type w, float* o) { o[0] = w[0]; o[1] = w[1]; }
 };
 
 // ============================================================ configuration
+// Four waves per workgroup; wave w owns value columns [w d_v/4, (w+1) d_v/4)
+// of the state for the whole sequence.
 template <int DK_, int DV_, class Io_, class Op_>
 struct ChunkCfg {
   static constexpr int DK = DK_, DV = DV_;
@@ -220,37 +264,47 @@ struct ChunkCfg {
   static constexpr int C = 64;          // tokens per chunk
   static constexpr int NB = 4;          // 16-token blocks per chunk
   static constexpr int NW = 4;          // waves per workgroup
-  static constexpr int CPL = DK / 32;   // key channels per lane in the prep layout
-  static constexpr int VPL = DV / 32;   // value channels per lane in the prep layout
+  static constexpr int NTHREADS = 64 * NW;
   static constexpr int NKS = DK / 32;   // 32-deep steps over key channels
   static constexpr int MTK = DK / 16;   // 16-row tiles over key channels
-  static constexpr int NVT = DV / 64;   // 16-column value tiles per wave
-  static constexpr int NKT = DK / 64;   // 16-column W tiles per wave
-  static constexpr int NT = NKT + NVT;  // tiles per wave in the block substitution
+  static constexpr int VW = DV / NW;    // value columns per wave
+  static constexpr int NVT = VW / 16;   // 16-column value tiles per wave
+  static constexpr int NWT = DK / 16 / NW;   // 16-column W tiles per wave
+  // prep layout: each lane holds 8 consecutive key channels of TPL tokens
+  static constexpr int CPL = 8;
+  static constexpr int CQ = DK / NW / CPL;   // lanes across a wave's key channels
+  static constexpr int TG = 64 / CQ;         // token groups
+  static constexpr int TPL = C / TG;         // tokens per lane
+  static constexpr int VPL = VW / CQ;        // value channels per lane
+  static_assert(CQ * TG == 64 && TPL * TG == C && VPL * CQ == VW && NWT >= 1, "layout");
   // LDS leading dimensions (elements)
   static constexpr int LD_K = DK + Op::PAD_RM;   // QG, KG, KI  [C][LD_K]
   static constexpr int LD_E = DK + Op::PAD_TR;   // KE          [C][LD_E]
   static constexpr int LD_V = DV + Op::PAD_TR;   // BV          [C][LD_V]
   static constexpr int LD_64 = C + Op::PAD_64;   // RTn, AQT [C][LD_64], WTn [DK][LD_64]
-  // LDS byte offsets
   static constexpr int SZ = sizeof(T);
+  // LDS byte offsets.  The output staging tile OST (scan) overlays KI, which
+  // is dead once the key-key tiles are built.
   static constexpr int OFF_QG = 0;
   static constexpr int OFF_KG = OFF_QG + C * LD_K * SZ;
   static constexpr int OFF_KI = OFF_KG + C * LD_K * SZ;
-  static constexpr int OFF_KE = OFF_KI + C * LD_K * SZ;
+  static constexpr int OFF_RD = OFF_KI + C * LD_K * SZ;
+  static constexpr int RD_LD = 20;     // floats per column of a diagonal block (padded)
+  static constexpr int OFF_KE = OFF_RD + NB * 16 * RD_LD * 4;
   static constexpr int OFF_BV = OFF_KE + C * LD_E * SZ;
-  static constexpr int OFF_RT = OFF_BV + C * LD_V * SZ;
-  static constexpr int OFF_AQ = OFF_RT + C * LD_64 * SZ;
-  static constexpr int OFF_WT = OFF_AQ + C * LD_64 * SZ;
-  static constexpr int OFF_TD = OFF_WT + DK * LD_64 * SZ;
-  static constexpr int OFF_RD = OFF_TD + NB * 16 * 16 * SZ;
-  static constexpr int OFF_GL = OFF_RD + NB * 16 * 16 * 4;
+  static constexpr int OFF_AQ = OFF_BV + C * LD_V * SZ;
+  static constexpr int OFF_RT = OFF_AQ + C * LD_64 * SZ;
+  static constexpr int OFF_TD = OFF_RT + C * LD_64 * SZ;
+  static constexpr int OFF_GL = OFF_TD + NB * 16 * 16 * SZ;
   static constexpr int OFF_FL = OFF_GL + DK * 4;
-  static constexpr int LDS_BYTES = OFF_FL + 16;
-  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
-  static_assert(OFF_KG % 16 == 0 && OFF_KE % 16 == 0 && OFF_BV % 16 == 0 && OFF_RT % 16 == 0 &&
-                OFF_AQ % 16 == 0 && OFF_WT % 16 == 0 && OFF_TD % 16 == 0 && OFF_RD % 16 == 0,
-                "LDS alignment");
+  static constexpr int LDS_BYTES = OFF_FL + 64;
+  static constexpr int LD_OS = DV + Op::PAD_RM;  // OST [C][LD_OS]
+  static constexpr int OFF_OS = (LD_OS <= LD_K) ? OFF_KI : OFF_FL + 64;
+  static constexpr int LDS_TOTAL = (OFF_OS == OFF_KI) ? LDS_BYTES : OFF_OS + C * LD_OS * SZ;
+  static_assert(LDS_BYTES + C * (DV + Op::PAD_RM) * SZ <= 160 * 1024, "LDS budget");
+  static_assert(OFF_KG % 16 == 0 && OFF_KI % 16 == 0 && OFF_RD % 16 == 0 && OFF_KE % 16 == 0 && OFF_FL % 16 == 0 &&
+                OFF_BV % 16 == 0 && OFF_AQ % 16 == 0 && OFF_RT % 16 == 0 && OFF_TD % 16 == 0 &&
+                OFF_GL % 16 == 0 && (LD_K * SZ) % 16 == 0, "LDS alignment");
 };
 
 // Threshold below which a channel's chunk decay Gamma_L makes k / Gamma unsafe.
@@ -262,57 +316,22 @@ struct ChunkKernel {
   typedef typename Cfg::Io Io;
   typedef typename Cfg::Op Op;
   typedef typename Cfg::T T;
-  static constexpr int DK = Cfg::DK, DV = Cfg::DV, C = Cfg::C;
-  static constexpr int CPL = Cfg::CPL, VPL = Cfg::VPL;
-  static constexpr int NKS = Cfg::NKS, MTK = Cfg::MTK, NVT = Cfg::NVT, NKT = Cfg::NKT,
-                       NT = Cfg::NT;
-
-  typedef typename RawVec<Io, CPL>::type RK;
-  typedef typename RawVec<Io, VPL>::type RV;
-  typedef typename RawG<CPL>::type RG;
+  static constexpr int DK = Cfg::DK, DV = Cfg::DV, C = Cfg::C, NW = Cfg::NW;
+  static constexpr int CPL = Cfg::CPL, VPL = Cfg::VPL, CQ = Cfg::CQ, TG = Cfg::TG,
+                       TPL = Cfg::TPL, VW = Cfg::VW;
+  static constexpr int NKS = Cfg::NKS, MTK = Cfg::MTK, NWT = Cfg::NWT, NVT = Cfg::NVT;
 
   struct Raw {
-    RG g[8];
-    RK q[8], k[8];
-    RV v[8];
+    RawWords<CPL * 4> g[TPL];
+    RawIo<Io, CPL> q[TPL], k[TPL];
+    RawIo<Io, VPL> v[TPL];
     float beta;
   };
-
-  // ---------------------------------------------------------------- loads
-  // Prep layout: wave w, lane l: token group tg = l / 8 (tokens 8tg .. 8tg+7),
-  // key channels kc0 .. kc0 + CPL - 1 with kc0 = w * DK/4 + (l % 8) * CPL,
-  // value channels vc0 .. vc0 + VPL - 1 with vc0 = w * DV/4 + (l % 8) * VPL.
-  static __device__ __forceinline__ void load_raw(Raw& r, const void* q, const void* k,
-                                                  const void* v, const float* g,
-                                                  const float* beta, size_t row_base, int H,
-                                                  int h, int clen) {
-    const int w = threadIdx.x >> 6, l = lane_id();
-    const int tg = l >> 3, cq = l & 7;
-    const int kc0 = w * (DK / 4) + cq * CPL;
-    const int vc0 = w * (DV / 4) + cq * VPL;
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const int i = 8 * tg + t;
-      if (i < clen) {
-        const size_t row = (row_base + i) * H + h;
-        r.g[t] = RawG<CPL>::load(g, row * DK + kc0);
-        r.q[t] = RawVec<Io, CPL>::load(q, row * DK + kc0);
-        r.k[t] = RawVec<Io, CPL>::load(k, row * DK + kc0);
-        r.v[t] = RawVec<Io, VPL>::load(v, row * DV + vc0);
-      } else {
-        r.g[t] = RG{};
-        r.q[t] = RK{};
-        r.k[t] = RK{};
-        r.v[t] = RV{};
-      }
-    }
-    // lane l fetches beta of token l
-    r.beta = (l < clen) ? beta[(row_base + l) * H + h] : 0.f;
-  }
+  enum { LOAD_QKV = 1, LOAD_G = 2, LOAD_ALL = 3 };
 
   // N contiguous LDS elements written as one vector store
   template <int N>
-  static __device__ __forceinline__ void st_vec(T* p, const T (&x)[N]) {
+  static __device__ __forceinline__ void st_vec(LDS T* p, const T (&x)[N]) {
     typedef T vec __attribute__((ext_vector_type(N)));
     vec v;
 #pragma unroll
@@ -320,110 +339,169 @@ struct ChunkKernel {
     *lds_ptr<vec>(p) = v;
   }
 
+  // ---------------------------------------------------------------- loads
+  // Prep layout: wave w, lane l = tg * CQ + cq holds tokens TPL*tg + t
+  // (t < TPL), key channels kc0 .. kc0+7 with kc0 = w*DK/4 + 8 cq, and value
+  // channels vc0 .. vc0+VPL-1 with vc0 = w*DV/4 + VPL cq.  Offsets are
+  // relative to the chunk's first token, hence the same for every chunk.
+  struct Offsets {
+    uint32_t qk, g, v, beta;   // lane byte offsets of its first token
+    uint32_t sqk, sg, sv;      // byte strides between consecutive tokens
+  };
+  static __device__ __forceinline__ Offsets lane_offsets(int H) {
+    const int w = threadIdx.x >> 6, l = lane_fresh();
+    const int tg = l / CQ, cq = l % CQ;
+    const int kc0 = w * (DK / NW) + CPL * cq;
+    const int vc0 = w * VW + VPL * cq;
+    constexpr uint32_t E = sizeof(typename Io::storage);
+    Offsets o;
+    o.sqk = (uint32_t)H * DK * E;
+    o.sg = (uint32_t)H * DK * 4;
+    o.sv = (uint32_t)H * DV * E;
+    o.qk = (uint32_t)(TPL * tg) * o.sqk + kc0 * E;
+    o.g = (uint32_t)(TPL * tg) * o.sg + kc0 * 4;
+    o.v = (uint32_t)(TPL * tg) * o.sv + vc0 * E;
+    o.beta = (uint32_t)l * H * 4;
+    return o;
+  }
+  // Loads of one chunk (first token row0, clen valid tokens); padding tokens
+  // read as zeros through the resources' size limit.
+  template <int PART>
+  static __device__ __forceinline__ void load_raw(Raw& r, const Offsets& o, const void* q,
+                                                  const void* k, const void* v, const float* g,
+                                                  const float* beta, size_t row0, int H, int h,
+                                                  int clen) {
+    constexpr size_t E = sizeof(typename Io::storage);
+    const size_t e0 = row0 * H + h;   // element row of the chunk's first token, this head
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc((const char*)q + e0 * DK * E, clen * o.sqk);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc((const char*)k + e0 * DK * E, clen * o.sqk);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc((const char*)v + e0 * DV * E, clen * o.sv);
+    const __amdgpu_buffer_rsrc_t rg = make_rsrc((const char*)g + e0 * DK * 4, clen * o.sg);
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(beta + e0, (uint32_t)clen * H * 4);
+    // lane part in the VGPR offset, the token step in the scalar offset
+#pragma unroll
+    for (int t = 0; t < TPL; ++t) {
+      if (PART & LOAD_QKV) {
+        r.q[t].w.load(rq, o.qk, t * o.sqk);
+        r.k[t].w.load(rk, o.qk, t * o.sqk);
+        r.v[t].w.load(rv, o.v, t * o.sv);
+      }
+      if (PART & LOAD_G) r.g[t].load(rg, o.g, t * o.sg);
+    }
+    if (PART & LOAD_QKV) r.beta = buf_load<float>(rb, o.beta);   // lane l: beta of token l
+  }
+
   // ---------------------------------------------------------------- prep
   // Cumulative decay and the five gate-scaled operands; returns the chunk's
   // guard flag (1 = some channel decays below KDA_GAMMA_MIN).
-  static __device__ __forceinline__ int prep(const Raw& r, char* smem, float scale) {
-    const int w = threadIdx.x >> 6, l = lane_id();
-    const int tg = l >> 3, cq = l & 7;
-    const int kc0 = w * (DK / 4) + cq * CPL;
-    const int vc0 = w * (DV / 4) + cq * VPL;
-    T* QG = reinterpret_cast<T*>(smem + Cfg::OFF_QG);
-    T* KG = reinterpret_cast<T*>(smem + Cfg::OFF_KG);
-    T* KI = reinterpret_cast<T*>(smem + Cfg::OFF_KI);
-    T* KE = reinterpret_cast<T*>(smem + Cfg::OFF_KE);
-    T* BV = reinterpret_cast<T*>(smem + Cfg::OFF_BV);
-    float* GL = reinterpret_cast<float*>(smem + Cfg::OFF_GL);
+  static __device__ __forceinline__ int prep(const Raw& r, LDS char* smem, float scale) {
+    const int w = threadIdx.x >> 6, l = lane_fresh();
+    const int tg = l / CQ, cq = l % CQ;
+    const int kc0 = w * (DK / NW) + CPL * cq;
+    const int vc0 = w * VW + VPL * cq;
+    LDS T* QG = (LDS T*)(smem + Cfg::OFF_QG);
+    LDS T* KG = (LDS T*)(smem + Cfg::OFF_KG);
+    LDS T* KI = (LDS T*)(smem + Cfg::OFF_KI);
+    LDS T* KE = (LDS T*)(smem + Cfg::OFF_KE);
+    LDS T* BV = (LDS T*)(smem + Cfg::OFF_BV);
+    LDS float* GL = (LDS float*)(smem + Cfg::OFF_GL);
 
-    // in-lane running products of alpha over the lane's 8 tokens
-    float cp[8][CPL];
+    // in-lane running products of alpha over the lane's TPL tokens
+    float cp[TPL][CPL];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      float gv[CPL];
-      RawG<CPL>::unpack(r.g[t], gv);
+    for (int t = 0; t < TPL; ++t)
 #pragma unroll
       for (int c = 0; c < CPL; ++c) {
-        const float a = __expf(gv[c]);
+        const float a = __expf(__uint_as_float(r.g[t].word(c)));
         cp[t][c] = (t == 0) ? a : cp[t - 1][c] * a;
       }
-    }
-    // exclusive product over the 8 token groups (lanes cq + 8 tg)
+    // product over the TG token groups (lanes cq + CQ tg): inclusive scan,
+    // then shift by one group for the exclusive prefix
     float ex[CPL], tot[CPL];
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
-      float x = cp[7][c];
+      float x = cp[TPL - 1][c];
 #pragma unroll
-      for (int d = 8; d < 64; d <<= 1) {
+      for (int d = CQ; d < 64; d <<= 1) {
         const float y = __shfl_up(x, d);
         if (l >= d) x *= y;
       }
-      tot[c] = __shfl(x, 56 + cq);          // Gamma_L
-      const float y = __shfl_up(x, 8);
-      ex[c] = (l >= 8) ? y : 1.f;
+      tot[c] = __shfl(x, 64 - CQ + cq);     // Gamma_L
+      const float y = __shfl_up(x, CQ);
+      ex[c] = (l >= CQ) ? y : 1.f;
     }
     int bad = 0;
 #pragma unroll
     for (int c = 0; c < CPL; ++c) bad |= !(tot[c] >= KDA_GAMMA_MIN);
     if (tg == 0) {
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) GL[kc0 + c] = tot[c];
+      *lds_ptr<f32x4>(GL + kc0) = f32x4{tot[0], tot[1], tot[2], tot[3]};
+      *lds_ptr<f32x4>(GL + kc0 + 4) = f32x4{tot[4], tot[5], tot[6], tot[7]};
     }
-    // betas of this lane's tokens
-    float bt[8];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) bt[t] = __shfl(r.beta, 8 * tg + t);
-
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const int i = 8 * tg + t;
+    for (int t = 0; t < TPL; ++t) {
+      const int i = TPL * tg + t;
+      const float bt = __shfl(r.beta, i);
       float qv[CPL], kv[CPL];
-      RawVec<Io, CPL>::unpack(r.q[t], qv);
-      RawVec<Io, CPL>::unpack(r.k[t], kv);
+      r.q[t].unpack(qv);
+      r.k[t].unpack(kv);
       T qg[CPL], kg[CPL], ki[CPL], ke[CPL];
 #pragma unroll
       for (int c = 0; c < CPL; ++c) {
         const float gam = ex[c] * cp[t][c];
         const float inv = __builtin_amdgcn_rcpf(gam);
         qg[c] = Op::cvt(scale * qv[c] * gam);
-        kg[c] = Op::cvt(bt[t] * kv[c] * gam);
+        kg[c] = Op::cvt(bt * kv[c] * gam);
         ki[c] = Op::cvt(kv[c] * inv);
-        ke[c] = Op::cvt(kv[c] * (tot[c] * inv));
+        ke[c] = Op::cvt(-kv[c] * (tot[c] * inv));
       }
-      st_vec(QG + i * Cfg::LD_K + kc0, qg);
-      st_vec(KG + i * Cfg::LD_K + kc0, kg);
-      st_vec(KI + i * Cfg::LD_K + kc0, ki);
-      st_vec(KE + i * Cfg::LD_E + kc0, ke);
+      st_chunk(QG + i * Cfg::LD_K + kc0, qg);
+      st_chunk(KG + i * Cfg::LD_K + kc0, kg);
+      st_chunk(KI + i * Cfg::LD_K + kc0, ki);
+      st_chunk(KE + i * Cfg::LD_E + kc0, ke);
       float vv[VPL];
-      RawVec<Io, VPL>::unpack(r.v[t], vv);
+      r.v[t].unpack(vv);
       T bv[VPL];
 #pragma unroll
-      for (int c = 0; c < VPL; ++c) bv[c] = Op::cvt(bt[t] * vv[c]);
-      st_vec(BV + i * Cfg::LD_V + vc0, bv);
+      for (int c = 0; c < VPL; ++c) bv[c] = Op::cvt(-bt * vv[c]);
+      st_chunk(BV + i * Cfg::LD_V + vc0, bv);
     }
     return bad;
   }
 
+  // N elements to LDS as 16-byte (or smaller) vector stores
+  template <int N>
+  static __device__ __forceinline__ void st_chunk(LDS T* p, const T (&x)[N]) {
+    constexpr int PER = 16 / (int)sizeof(T) < N ? 16 / (int)sizeof(T) : N;
+#pragma unroll
+    for (int c0 = 0; c0 < N; c0 += PER) {
+      T part[PER];
+#pragma unroll
+      for (int c = 0; c < PER; ++c) part[c] = x[c0 + c];
+      st_vec(p + c0, part);
+    }
+  }
+
   // ---------------------------------------------------------------- phase A
   // R = strict_tril(KG KI^T) and Aqk = tril(QG KI^T) by 16x16 tiles.
-  // Off-diagonal R tiles go negated and transposed to RTn (bf16/f32), diagonal
-  // R tiles to RD (fp32, transposed) for the inverse, Aqk transposed to AQT.
-  static __device__ __forceinline__ void tile_qk(char* smem, int I, int J) {
-    const T* QG = reinterpret_cast<const T*>(smem + Cfg::OFF_QG);
-    const T* KG = reinterpret_cast<const T*>(smem + Cfg::OFF_KG);
-    const T* KI = reinterpret_cast<const T*>(smem + Cfg::OFF_KI);
-    T* RTn = reinterpret_cast<T*>(smem + Cfg::OFF_RT);
-    T* AQT = reinterpret_cast<T*>(smem + Cfg::OFF_AQ);
-    float* RD = reinterpret_cast<float*>(smem + Cfg::OFF_RD);
+  // Off-diagonal R tiles go negated and transposed to RTn, diagonal R tiles
+  // to RD (fp32, transposed) for the inverse, -Aqk transposed to AQT.
+  static __device__ __forceinline__ void tile_qk(LDS char* smem, int I, int J) {
+    const int l = lane_fresh();
+    const LDS T* QG = (const LDS T*)(smem + Cfg::OFF_QG);
+    const LDS T* KG = (const LDS T*)(smem + Cfg::OFF_KG);
+    const LDS T* KI = (const LDS T*)(smem + Cfg::OFF_KI);
+    LDS T* RTn = (LDS T*)(smem + Cfg::OFF_RT);
+    LDS T* AQT = (LDS T*)(smem + Cfg::OFF_AQ);
+    LDS float* RD = (LDS float*)(smem + Cfg::OFF_RD);
     f32x4 accR = {0.f, 0.f, 0.f, 0.f}, accA = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      const typename Op::F32 b = Op::ld32_rm(KI, Cfg::LD_K, 16 * J, 32 * ks);
-      const typename Op::F32 ak = Op::ld32_rm(KG, Cfg::LD_K, 16 * I, 32 * ks);
-      const typename Op::F32 aq = Op::ld32_rm(QG, Cfg::LD_K, 16 * I, 32 * ks);
+      const typename Op::F32 b = Op::ld32_rm(l, KI, Cfg::LD_K, 16 * J, 32 * ks);
+      const typename Op::F32 ak = Op::ld32_rm(l, KG, Cfg::LD_K, 16 * I, 32 * ks);
+      const typename Op::F32 aq = Op::ld32_rm(l, QG, Cfg::LD_K, 16 * I, 32 * ks);
       accR = Op::mma32(ak, b, accR);
       accA = Op::mma32(aq, b, accA);
     }
-    const int l = lane_id();
     const int n = l & 15, g4 = 4 * (l >> 4);
     if (I == J) {
 #pragma unroll
@@ -432,21 +510,31 @@ struct ChunkKernel {
         if (!(n <= g4 + r)) accA[r] = 0.f;   // lower with diagonal
       }
       // RD[I][m][i] = R[16I + i][16I + m]  (column m of the block, contiguous over i)
-      *lds_ptr<f32x4>(RD + I * 256 + n * 16 + g4) = accR;
+      *lds_ptr<f32x4>(RD + I * 16 * Cfg::RD_LD + n * Cfg::RD_LD + g4) = accR;
     } else {
-      Op::st_ct(RTn, Cfg::LD_64, 16 * J, 16 * I, -accR);
+      Op::st_ct(l, RTn, Cfg::LD_64, 16 * J, 16 * I, -accR);
     }
-    Op::st_ct(AQT, Cfg::LD_64, 16 * J, 16 * I, accA);
+    Op::st_ct(l, AQT, Cfg::LD_64, 16 * J, 16 * I, -accA);
+  }
+
+  // 10 tile pairs over 4 waves: 3, 3, 2, 2
+  static __device__ __forceinline__ void phase_a(LDS char* smem) {
+    switch (threadIdx.x >> 6) {
+      case 0: tile_qk(smem, 0, 0); tile_qk(smem, 1, 0); tile_qk(smem, 1, 1); break;
+      case 1: tile_qk(smem, 2, 0); tile_qk(smem, 2, 1); tile_qk(smem, 2, 2); break;
+      case 2: tile_qk(smem, 3, 0); tile_qk(smem, 3, 1); break;
+      default: tile_qk(smem, 3, 2); tile_qk(smem, 3, 3); break;
+    }
   }
 
   // ---------------------------------------------------------------- phase T
   // T_II = (I + R_II)^{-1} for block I = wave id, by column forward
   // substitution; lane l%16 = column.  Written transposed (TD[I][col][i]).
-  static __device__ __forceinline__ void invert_diag(char* smem) {
-    const int w = threadIdx.x >> 6, l = lane_id();
+  static __device__ __forceinline__ void invert_diag(LDS char* smem) {
+    const int w = threadIdx.x >> 6, l = lane_fresh();
     const int col = l & 15;
-    const float* RD = reinterpret_cast<const float*>(smem + Cfg::OFF_RD) + w * 256;
-    T* TD = reinterpret_cast<T*>(smem + Cfg::OFF_TD) + w * 256;
+    const LDS float* RD = (const LDS float*)(smem + Cfg::OFF_RD) + w * 16 * Cfg::RD_LD;
+    LDS T* TD = (LDS T*)(smem + Cfg::OFF_TD) + w * 256;
     float x[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) x[i] = (i == col) ? 1.f : 0.f;
@@ -456,7 +544,7 @@ struct ChunkKernel {
       // column m of N: N[i][m] = RD[m][i]
 #pragma unroll
       for (int i4 = (m + 1) / 4; i4 < 4; ++i4) {
-        const f32x4 nv = *lds_ptr<const f32x4>(RD + m * 16 + 4 * i4);
+        const f32x4 nv = *lds_ptr<const f32x4>(RD + m * Cfg::RD_LD + 4 * i4);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = 4 * i4 + e;
@@ -473,65 +561,27 @@ struct ChunkKernel {
     }
   }
 
-  // ---------------------------------------------------------------- phase S1
-  // Block forward substitution for this wave's W channels and U columns:
-  //   Y_I = [KG | BV]_I - sum_{J<I} R_IJ X_J,  X_I = T_II Y_I.
-  // The W part is written negated and transposed to WTn; U stays in registers.
-  static __device__ __forceinline__ void wy_factors(char* smem, f32x4 (&U)[4][NVT]) {
-    const int w = threadIdx.x >> 6;
-    const T* KG = reinterpret_cast<const T*>(smem + Cfg::OFF_KG);
-    const T* BV = reinterpret_cast<const T*>(smem + Cfg::OFF_BV);
-    const T* RTn = reinterpret_cast<const T*>(smem + Cfg::OFF_RT);
-    const T* TD = reinterpret_cast<const T*>(smem + Cfg::OFF_TD);
-    T* WTn = reinterpret_cast<T*>(smem + Cfg::OFF_WT);
-    const int cw0 = w * (DK / 4), vw0 = w * (DV / 4);
-    f32x4 X[4][NT];
-#pragma unroll
-    for (int I = 0; I < 4; ++I) {
-      f32x4 Y[NT];
-#pragma unroll
-      for (int nt = 0; nt < NKT; ++nt) Y[nt] = Op::unpack(Op::ld16_tr(KG, Cfg::LD_K, 16 * I, cw0 + 16 * nt));
-#pragma unroll
-      for (int nt = 0; nt < NVT; ++nt)
-        Y[NKT + nt] = Op::unpack(Op::ld16_tr(BV, Cfg::LD_V, 16 * I, vw0 + 16 * nt));
-#pragma unroll
-      for (int J = 0; J < I; ++J) {
-        // A[m = i][k = j] = -R[16I + m][16J + k] = RTn[16J + k][16I + m]
-        const typename Op::F16 a = Op::ld16_tr(RTn, Cfg::LD_64, 16 * J, 16 * I);
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) Y[nt] = Op::mma16(a, Op::pack(X[J][nt]), Y[nt]);
-      }
-      // A[m = i][k = i'] = T_II[m][k] = TD[I][k][m]
-      const typename Op::F16 a = Op::ld16_tr(TD + I * 256, 16, 0, 0);
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        X[I][nt] = Op::mma16(a, Op::pack(Y[nt]), z);
-      }
-    }
-#pragma unroll
-    for (int I = 0; I < 4; ++I) {
-#pragma unroll
-      for (int nt = 0; nt < NKT; ++nt) Op::st_ct(WTn, Cfg::LD_64, cw0 + 16 * nt, 16 * I, -X[I][nt]);
-#pragma unroll
-      for (int nt = 0; nt < NVT; ++nt) U[I][nt] = X[I][NKT + nt];
-    }
-  }
+  // ---------------------------------------------------------------- phase S
+  // Y = -Ebar = KG S - BV; X = (I + R)^{-1} Y = -E by block forward
+  // substitution; O^T = S^T QG^T + (-E)^T (-Aqk)^T staged through LDS and
+  // written as whole token rows; S <- Diag(Gamma_L) S + (-KE)^T (-E).
+  static __device__ __forceinline__ void scan_step(LDS char* smem, f32x4 (&S)[MTK][NVT],
+                                                   void* out, size_t row_base, int H, int h,
+                                                   int clen) {
+    const int w = threadIdx.x >> 6, l = lane_fresh();
+    const LDS T* QG = (const LDS T*)(smem + Cfg::OFF_QG);
+    const LDS T* KG = (const LDS T*)(smem + Cfg::OFF_KG);
+    const LDS T* KE = (const LDS T*)(smem + Cfg::OFF_KE);
+    const LDS T* BV = (const LDS T*)(smem + Cfg::OFF_BV);
+    const LDS T* AQT = (const LDS T*)(smem + Cfg::OFF_AQ);
+    const LDS T* RTn = (const LDS T*)(smem + Cfg::OFF_RT);
+    const LDS T* TD = (const LDS T*)(smem + Cfg::OFF_TD);
+    LDS T* OST = (LDS T*)(smem + Cfg::OFF_OS);
+    const LDS float* GL = (const LDS float*)(smem + Cfg::OFF_GL);
+    const int vw0 = w * VW;
+    const int g4 = 4 * (l >> 4);
 
-  // ---------------------------------------------------------------- phase S2
-  // E = U - W S, O = QG S + Aqk E, S <- Diag(Gamma_L) S + KE^T E.
-  static __device__ __forceinline__ void scan_step(char* smem, f32x4 (&S)[MTK][NVT],
-                                                   const f32x4 (&U)[4][NVT], void* out,
-                                                   size_t row_base, int H, int h, int clen) {
-    const int w = threadIdx.x >> 6, l = lane_id();
-    const T* QG = reinterpret_cast<const T*>(smem + Cfg::OFF_QG);
-    const T* KE = reinterpret_cast<const T*>(smem + Cfg::OFF_KE);
-    const T* AQT = reinterpret_cast<const T*>(smem + Cfg::OFF_AQ);
-    const T* WTn = reinterpret_cast<const T*>(smem + Cfg::OFF_WT);
-    const float* GL = reinterpret_cast<const float*>(smem + Cfg::OFF_GL);
-    const int vw0 = w * (DV / 4);
-
-    // S as 32-deep B operands over key channels
+    // S as 32-deep operands over key channels (lane: value column, k: channels)
     typename Op::F32 SB[NKS][NVT];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
@@ -539,62 +589,102 @@ struct ChunkKernel {
       for (int nt = 0; nt < NVT; ++nt)
         SB[ks][nt] = typename Op::F32{Op::pack(S[2 * ks][nt]), Op::pack(S[2 * ks + 1][nt])};
 
-    f32x4 E[4][NVT], O[4][NVT];
+    // (1) + (2): per 16-token block, Y_I = KG_I S - BV_I, then the solve
+    //     X_I = T_II (Y_I - sum_{J<I} R_IJ X_J); X kept as 16-deep operands.
+    typename Op::F16 XP[4][NVT];
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
+      f32x4 Y[NVT];
 #pragma unroll
-      for (int nt = 0; nt < NVT; ++nt) {
-        E[I][nt] = U[I][nt];
-        O[I][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
+      for (int nt = 0; nt < NVT; ++nt)
+        Y[nt] = Op::unpack(Op::ld16_tr(l, BV, Cfg::LD_V, 16 * I, vw0 + 16 * nt));   // -BV
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        const typename Op::F32 aw = Op::ld32_tr(WTn, Cfg::LD_64, 32 * ks, 16 * I);
-        const typename Op::F32 aq = Op::ld32_rm(QG, Cfg::LD_K, 16 * I, 32 * ks);
+        const typename Op::F32 ak = Op::ld32_rm(l, KG, Cfg::LD_K, 16 * I, 32 * ks);
 #pragma unroll
-        for (int nt = 0; nt < NVT; ++nt) {
-          E[I][nt] = Op::mma32(aw, SB[ks][nt], E[I][nt]);
-          O[I][nt] = Op::mma32(aq, SB[ks][nt], O[I][nt]);
+        for (int nt = 0; nt < NVT; ++nt) Y[nt] = Op::mma32(ak, SB[ks][nt], Y[nt]);
+      }
+      // The -R_IJ X_J terms accumulate in their own registers (16-deep
+      // products) and join Y with a vector add: an accumulator produced by
+      // one MFMA shape is never fed straight into another shape's
+      // accumulate input.  Mixed-shape accumulation chains were miscompiled
+      // for gfx950 (too few wait states after the 32-deep producer).
+      if (I > 0) {
+        f32x4 Z[NVT];
+#pragma unroll
+        for (int nt = 0; nt < NVT; ++nt) Z[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int J = 0; J < I; ++J) {
+          // A[m = i][k = j] = -R[16I + m][16J + k] = RTn[16J + k][16I + m]
+          const typename Op::F16 a = Op::ld16_tr(l, RTn, Cfg::LD_64, 16 * J, 16 * I);
+#pragma unroll
+          for (int nt = 0; nt < NVT; ++nt) Z[nt] = Op::mma16(a, XP[J][nt], Z[nt]);
         }
+#pragma unroll
+        for (int nt = 0; nt < NVT; ++nt) Y[nt] += Z[nt];
+      }
+      // A[m = i][k = i'] = T_II[m][k] = TD[I][k][m]
+      const typename Op::F16 a = Op::ld16_tr(l, TD + I * 256, 16, 0, 0);
+#pragma unroll
+      for (int nt = 0; nt < NVT; ++nt) {
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        XP[I][nt] = Op::pack(Op::mma16(a, Op::pack(Y[nt]), z));
       }
     }
-    // E as 32-deep B operands over tokens
+    // -E as 32-deep operands over tokens: two 16-deep blocks side by side
     typename Op::F32 EB[2][NVT];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int nt = 0; nt < NVT; ++nt)
-        EB[kt][nt] = typename Op::F32{Op::pack(E[2 * kt][nt]), Op::pack(E[2 * kt + 1][nt])};
-    // causal in-chunk part of the outputs
+      for (int nt = 0; nt < NVT; ++nt) EB[kt][nt] = typename Op::F32{XP[2 * kt][nt], XP[2 * kt + 1][nt]};
+
+    // (3) O_I^T = S^T QG_I^T + (-E)^T (-Aqk_I)^T: rows = value columns,
+    //     columns = tokens 16I + n; staged as OST[token][value]
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
+      f32x4 O[NVT];
+#pragma unroll
+      for (int nt = 0; nt < NVT; ++nt) O[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const typename Op::F32 bq = Op::ld32_rm(l, QG, Cfg::LD_K, 16 * I, 32 * ks);
+#pragma unroll
+        for (int nt = 0; nt < NVT; ++nt) O[nt] = Op::mma32(SB[ks][nt], bq, O[nt]);
+      }
 #pragma unroll
       for (int kt = 0; kt <= I / 2; ++kt) {
-        const typename Op::F32 a = Op::ld32_tr(AQT, Cfg::LD_64, 32 * kt, 16 * I);
+        const typename Op::F32 ba = Op::ld32_tr(l, AQT, Cfg::LD_64, 32 * kt, 16 * I);
 #pragma unroll
-        for (int nt = 0; nt < NVT; ++nt) O[I][nt] = Op::mma32(a, EB[kt][nt], O[I][nt]);
+        for (int nt = 0; nt < NVT; ++nt) O[nt] = Op::mma32(EB[kt][nt], ba, O[nt]);
+      }
+#pragma unroll
+      for (int nt = 0; nt < NVT; ++nt) Op::st_ct(l, OST, Cfg::LD_OS, 16 * I, vw0 + 16 * nt, O[nt]);
+    }
+    __syncthreads();
+    // copy the staged tile out: 16-byte pieces of whole token rows
+    {
+      constexpr int PIECE = 16 / Cfg::SZ;                 // elements per 16 bytes
+      constexpr int PER_ROW = DV / PIECE;
+      constexpr uint32_t E = sizeof(typename Io::storage);
+      const uint32_t srow = (uint32_t)H * DV * E;
+      const __amdgpu_buffer_rsrc_t ro =
+          make_rsrc((char*)out + (row_base * H + h) * DV * E, clen * srow);
+#pragma unroll
+      for (int p0 = 0; p0 < C * PER_ROW; p0 += Cfg::NTHREADS) {
+        const int p = p0 + threadIdx.x;
+        const int i = p / PER_ROW, c = (p % PER_ROW) * PIECE;
+        const u32x4 val = *lds_ptr<const u32x4>(OST + i * Cfg::LD_OS + c);
+        buf_store16(ro, i * srow + c * E, val);
       }
     }
-    // store outputs: rows i = 16I + 4g + r, column vw0 + 16nt + l%16
-    const int n = l & 15, g4 = 4 * (l >> 4);
-#pragma unroll
-    for (int I = 0; I < 4; ++I)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = 16 * I + g4 + r;
-        if (i < clen) {
-          const size_t base = ((row_base + i) * H + h) * DV + vw0 + n;
-#pragma unroll
-          for (int nt = 0; nt < NVT; ++nt) Io::store(out, base + 16 * nt, O[I][nt][r]);
-        }
-      }
-    // state update
+
+    // (4) state update with -KE and -E
 #pragma unroll
     for (int mt = 0; mt < MTK; ++mt) {
       const f32x4 gl = *lds_ptr<const f32x4>(GL + 16 * mt + g4);
       typename Op::F32 a[2];
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) a[kt] = Op::ld32_tr(KE, Cfg::LD_E, 32 * kt, 16 * mt);
+      for (int kt = 0; kt < 2; ++kt) a[kt] = Op::ld32_tr(l, KE, Cfg::LD_E, 32 * kt, 16 * mt);
 #pragma unroll
       for (int nt = 0; nt < NVT; ++nt) {
         f32x4 s = S[mt][nt] * gl;
@@ -608,30 +698,28 @@ struct ChunkKernel {
   // ---------------------------------------------------------------- guard path
   // The recurrence itself, token by token, on the on-chip state (each wave its
   // own value columns; reductions over key rows stay inside the wave).
-  static __device__ void recurrent_chunk(f32x4 (&S)[MTK][NVT], const void* q, const void* k,
-                                         const void* v, const float* g, const float* beta,
-                                         void* out, size_t row_base, int H, int h, int clen,
-                                         float scale) {
-    const int w = threadIdx.x >> 6, l = lane_id();
+  static __device__ __forceinline__ void recurrent_chunk(f32x4 (&S)[MTK][NVT], const void* q,
+                                                         const void* k, const void* v,
+                                                         const float* g, const float* beta,
+                                                         void* out, size_t row_base, int H,
+                                                         int h, int clen, float scale) {
+    const int w = threadIdx.x >> 6, l = lane_fresh();
     const int n = l & 15, g4 = 4 * (l >> 4);
-    const int vw0 = w * (DV / 4);
+    const int vw0 = w * VW;
     for (int t = 0; t < clen; ++t) {
       const size_t row = (row_base + t) * H + h;
-      float p[NVT], o[NVT];
+      // forget, then the prediction Sbar^T k
+      float p[NVT];
 #pragma unroll
       for (int nt = 0; nt < NVT; ++nt) p[nt] = 0.f;
-      float kk[MTK][4], qq[MTK][4];
 #pragma unroll
       for (int mt = 0; mt < MTK; ++mt) {
         const size_t ci = row * DK + 16 * mt + g4;
         const f32x4 gv = *reinterpret_cast<const f32x4*>(g + ci);
         const f32x4 kv = Io::load4(k, ci);
-        const f32x4 qv = Io::load4(q, ci);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const float a = __expf(gv[r]);
-          kk[mt][r] = kv[r];
-          qq[mt][r] = scale * qv[r];
 #pragma unroll
           for (int nt = 0; nt < NVT; ++nt) {
             S[mt][nt][r] *= a;
@@ -644,15 +732,27 @@ struct ChunkKernel {
       for (int nt = 0; nt < NVT; ++nt) {
         p[nt] += __shfl_xor(p[nt], 16);
         p[nt] += __shfl_xor(p[nt], 32);
-        const float e = b * (Io::load(v, row * DV + vw0 + 16 * nt + n) - p[nt]);
-        o[nt] = 0.f;
+        p[nt] = b * (Io::load(v, row * DV + vw0 + 16 * nt + n) - p[nt]);   // e
+      }
+      // write k e^T, then read with s q
+      float o[NVT];
 #pragma unroll
-        for (int mt = 0; mt < MTK; ++mt)
+      for (int nt = 0; nt < NVT; ++nt) o[nt] = 0.f;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            S[mt][nt][r] += kk[mt][r] * e;
-            o[nt] += S[mt][nt][r] * qq[mt][r];
+      for (int mt = 0; mt < MTK; ++mt) {
+        const size_t ci = row * DK + 16 * mt + g4;
+        const f32x4 kv = Io::load4(k, ci);
+        const f32x4 qv = Io::load4(q, ci);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int nt = 0; nt < NVT; ++nt) {
+            S[mt][nt][r] += kv[r] * p[nt];
+            o[nt] += S[mt][nt][r] * (scale * qv[r]);
           }
+      }
+#pragma unroll
+      for (int nt = 0; nt < NVT; ++nt) {
         o[nt] += __shfl_xor(o[nt], 16);
         o[nt] += __shfl_xor(o[nt], 32);
         if (l < 16) Io::store(out, row * DV + vw0 + 16 * nt + n, o[nt]);
@@ -661,76 +761,82 @@ struct ChunkKernel {
   }
 
   // ---------------------------------------------------------------- driver
-  static __device__ void run(const void* q, const void* k, const void* v, const float* g,
-                             const float* beta, const float* S0, void* out, float* S_final,
-                             size_t row_base, int len, int H, int h, size_t chain, float scale) {
-    extern __shared__ __attribute__((aligned(16))) char smem[];
-    const int w = threadIdx.x >> 6, l = lane_id();
-    const int n = l & 15, g4 = 4 * (l >> 4);
-    const int vw0 = w * (DV / 4);
-    int* FL = reinterpret_cast<int*>(smem + Cfg::OFF_FL);
+  static __device__ __forceinline__ void run(const void* q, const void* k, const void* v,
+                                             const float* g, const float* beta, const float* S0,
+                                             void* out, float* S_final, size_t row_base, int len,
+                                             int H, int h, size_t chain, float scale) {
+    extern __shared__ __attribute__((aligned(16))) char smem_[];
+    LDS char* smem = (LDS char*)smem_;
+    const int w = threadIdx.x >> 6;
+    const int vw0 = w * VW;
+    LDS int* FL = (LDS int*)(smem + Cfg::OFF_FL);
 
     // Aqk^T tiles above the diagonal are never written: zero the buffer once.
     {
-      T* AQT = reinterpret_cast<T*>(smem + Cfg::OFF_AQ);
-      for (int i = threadIdx.x; i < C * Cfg::LD_64; i += 256) AQT[i] = Op::cvt(0.f);
+      LDS T* AQT = (LDS T*)(smem + Cfg::OFF_AQ);
+      for (int i = threadIdx.x; i < C * Cfg::LD_64; i += Cfg::NTHREADS) AQT[i] = Op::cvt(0.f);
     }
     // state tiles: S[16mt + 4g + r][vw0 + 16nt + n]
     f32x4 S[MTK][NVT];
-#pragma unroll
-    for (int mt = 0; mt < MTK; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < NVT; ++nt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          S[mt][nt][r] = S0 ? S0[(chain * DK + 16 * mt + g4 + r) * DV + vw0 + 16 * nt + n] : 0.f;
-
-    Raw nxt;
-    if (len > 0) load_raw(nxt, q, k, v, g, beta, row_base, H, h, len < C ? len : C);
-    for (int c0 = 0; c0 < len; c0 += C) {
-      const int clen = (len - c0) < C ? (len - c0) : C;
-      Raw cur = nxt;
-      if (c0 + C < len) {
-        const int nlen = (len - c0 - C) < C ? (len - c0 - C) : C;
-        load_raw(nxt, q, k, v, g, beta, row_base + c0 + C, H, h, nlen);
-      }
-      const int bad = prep(cur, smem, scale);
-      const bool wave_bad = __any(bad);
-      if (l == 0) FL[w] = wave_bad ? 1 : 0;
-      __syncthreads();                                           // B1
-      const bool guard = (FL[0] | FL[1] | FL[2] | FL[3]) != 0;
-      if (!guard) {
-        // balanced tile lists: 3, 3, 2, 2 tile pairs per wave
-        if (w == 0) { tile_qk(smem, 0, 0); tile_qk(smem, 1, 0); tile_qk(smem, 1, 1); }
-        if (w == 1) { tile_qk(smem, 2, 0); tile_qk(smem, 2, 1); tile_qk(smem, 2, 2); }
-        if (w == 2) { tile_qk(smem, 3, 0); tile_qk(smem, 3, 1); }
-        if (w == 3) { tile_qk(smem, 3, 2); tile_qk(smem, 3, 3); }
-        __syncthreads();                                         // B2
-        invert_diag(smem);
-        __syncthreads();                                         // B3
-        f32x4 U[4][NVT];
-        wy_factors(smem, U);
-        __syncthreads();                                         // B4
-        scan_step(smem, S, U, out, row_base + c0, H, h, clen);
-      } else {
-        recurrent_chunk(S, q, k, v, g, beta, out, row_base + c0, H, h, clen, scale);
-      }
-      __syncthreads();                                           // LDS reuse
-    }
-    if (S_final) {
+    {
+      const int l = lane_fresh();
+      const int n = l & 15, g4 = 4 * (l >> 4);
 #pragma unroll
       for (int mt = 0; mt < MTK; ++mt)
 #pragma unroll
         for (int nt = 0; nt < NVT; ++nt)
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            S_final[(chain * DK + 16 * mt + g4 + r) * DV + vw0 + 16 * nt + n] = S[mt][nt][r];
+            S[mt][nt][r] = S0 ? S0[(chain * DK + 16 * mt + g4 + r) * DV + vw0 + 16 * nt + n] : 0.f;
+    }
+
+    // One register buffer of raw inputs: the prep consumes chunk c; the loads
+    // of chunk c + 1 go into the same registers once the inverse is done.
+    const Offsets offs = lane_offsets(H);
+    Raw raw;
+    if (len > 0) load_raw<LOAD_ALL>(raw, offs, q, k, v, g, beta, row_base, H, h, len < C ? len : C);
+    for (int c0 = 0; c0 < len; c0 += C) {
+      const int clen = (len - c0) < C ? (len - c0) : C;
+      const int bad = prep(raw, smem, scale);
+      if (lane_fresh() == 0) FL[w] = __any(bad) ? 1 : 0;
+      __syncthreads();                                           // B1
+      int any_bad = 0;
+#pragma unroll
+      for (int i = 0; i < NW; ++i) any_bad |= FL[i];
+      const bool more = c0 + C < len;
+      const int nlen = (len - c0 - C) < C ? (len - c0 - C) : C;
+      if (!any_bad) {
+        phase_a(smem);
+        __syncthreads();                                         // B2
+        invert_diag(smem);
+        // the next chunk's loads stay in flight through the scan (issued
+        // before the inverse they would overlap two register peaks)
+        compiler_fence();
+        if (more) load_raw<LOAD_ALL>(raw, offs, q, k, v, g, beta, row_base + c0 + C, H, h, nlen);
+        __syncthreads();                                         // B3
+        scan_step(smem, S, out, row_base + c0, H, h, clen);
+      } else {
+        recurrent_chunk(S, q, k, v, g, beta, out, row_base + c0, H, h, clen, scale);
+        if (more) load_raw<LOAD_ALL>(raw, offs, q, k, v, g, beta, row_base + c0 + C, H, h, nlen);
+      }
+      __syncthreads();                                           // LDS reuse
+    }
+    if (S_final) {
+      const int l = lane_fresh();
+      const int n = l & 15, g4 = 4 * (l >> 4);
+      float* Sf = S_final + chain * DK * DV + vw0 + n;
+#pragma unroll
+      for (int mt = 0; mt < MTK; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NVT; ++nt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) Sf[(16 * mt + g4 + r) * DV + 16 * nt] = S[mt][nt][r];
     }
   }
 };
 
 template <class Cfg>
-__global__ __launch_bounds__(256, 1) void chunk_fwd_kernel(
+__global__ __launch_bounds__(Cfg::NTHREADS, 1) void chunk_fwd_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, const float* S0, void* out,
     float* S_final, int T, int H, float scale) {
@@ -741,7 +847,7 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_kernel(
 }
 
 template <class Cfg>
-__global__ __launch_bounds__(256, 1) void chunk_fwd_varlen_kernel(
+__global__ __launch_bounds__(Cfg::NTHREADS, 1) void chunk_fwd_varlen_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, const float* S0, void* out,
     float* S_final, const int32_t* __restrict__ cu_seqlens, int H, float scale) {
@@ -757,21 +863,21 @@ static hipError_t launch_chunk_t(const void* q, const void* k, const void* v, co
                                  const float* beta, const float* S0, void* out, float* S_final,
                                  const int32_t* cu, int n_seq, int T, int H, float scale,
                                  hipStream_t stream) {
-  const int bytes = Cfg::LDS_BYTES;
+  const int bytes = Cfg::LDS_TOTAL;
   if (cu) {
     auto kern = chunk_fwd_varlen_kernel<Cfg>;
     hipError_t e = hipFuncSetAttribute((const void*)kern,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(n_seq * H), dim3(256), bytes, stream, q, k, v, g, beta, S0, out,
-                       S_final, cu, H, scale);
+    hipLaunchKernelGGL(kern, dim3(n_seq * H), dim3(Cfg::NTHREADS), bytes, stream, q, k, v, g,
+                       beta, S0, out, S_final, cu, H, scale);
   } else {
     auto kern = chunk_fwd_kernel<Cfg>;
     hipError_t e = hipFuncSetAttribute((const void*)kern,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(n_seq * H), dim3(256), bytes, stream, q, k, v, g, beta, S0, out,
-                       S_final, T, H, scale);
+    hipLaunchKernelGGL(kern, dim3(n_seq * H), dim3(Cfg::NTHREADS), bytes, stream, q, k, v, g,
+                       beta, S0, out, S_final, T, H, scale);
   }
   return hipGetLastError();
 }

@@ -25,9 +25,12 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
   return __builtin_bit_cast(uint16_t, b);
 }
 
-// Two floats -> one dword holding two bf16 (lo = a, hi = b).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two floats -> one dword holding two bf16 (lo = a, hi = b), round to nearest
+// even: one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  return (uint32_t)f32_to_bf16_bits(a) | ((uint32_t)f32_to_bf16_bits(b) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
 
 // Element access for the two I/O types.  IoBf16 stores raw bf16 bit patterns.
@@ -46,6 +49,10 @@ struct IoF32 {
   }
   __device__ static __forceinline__ void store4(void* p, size_t i, f32x4 x) {
     *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p) + i) = x;
+  }
+  // 16 bytes (four elements) starting at element i
+  __device__ static __forceinline__ void store16(void* p, size_t i, u32x4 x) {
+    *reinterpret_cast<u32x4*>(reinterpret_cast<float*>(p) + i) = x;
   }
 };
 
@@ -72,6 +79,10 @@ struct IoBf16 {
     w[0] = pack_bf16x2(x[0], x[1]);
     w[1] = pack_bf16x2(x[2], x[3]);
     *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(p) + i) = w;
+  }
+  // 16 bytes (eight elements) starting at element i
+  __device__ static __forceinline__ void store16(void* p, size_t i, u32x4 x) {
+    *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(p) + i) = x;
   }
 };
 
