@@ -48,6 +48,31 @@ def prefill_alg_flops(B, T, H, dk, dv, C=64):
     return B * T * H * (6 * dk * dv + 2 * C * (3 * dk + 2 * dv) + C * C / 3)
 
 
+HERE = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_FILE = os.path.join(HERE, "profiles", "chunk_fwd_128x128_b8_h32_t8192_traffic.md")
+CHUNK_SRC = os.path.join(HERE, "gated_delta_rule_06_amd", "csrc", "chunk.hip")
+
+
+def measured_traffic():
+    """HBM bytes per launch of the prefill kernel from the committed counter
+    summary (FETCH_SIZE + WRITE_SIZE, calibrated on a plain copy), or None when
+    the kernel source has changed since the counters were taken."""
+    import hashlib
+    try:
+        txt = open(TRAFFIC_FILE).read()
+        src = hashlib.sha256(open(CHUNK_SRC, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    fields = dict(l.split(":", 1) for l in txt.splitlines() if ":" in l and not l.startswith("#"))
+    fields = {k.strip("- `*").strip(): v.strip().strip("`") for k, v in fields.items()}
+    if fields.get("source_sha256") != src:
+        return None
+    try:
+        return float(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def decode_alg_bytes(N, H, dk, dv, io):
     e = 2 if io == "bf16" else 4
     return N * H * (2 * dk * dv * 4 + e * (2 * dk + 2 * dv) + 4 * dk + 4)
@@ -60,7 +85,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--decode-reps", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-chains", type=int, default=32,
+    ap.add_argument("--cpu-chains", type=int, default=160,
                     help="chains of the prefill workload the oracle runs for the CPU baseline")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this size (for counter calibration)")
@@ -223,7 +248,7 @@ def main():
                    "d_k": P["dk"], "d_v": P["dv"], "chunk": P["chunk"], "io": "bf16",
                    "state": "fp32", "S0": None},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(),
                      "kernel": "chunk_fwd_kernel<128,128,bf16>",
                      "alg_bytes_per_launch": alg_b, "avg_launch_ms": avg_kernel_ms,
                      "alg_tflops": alg_f / (avg_kernel_ms * 1e-3) / 1e12,

@@ -28,7 +28,10 @@
  *    stream) and results are valid once that stream has reached them.
  *  - Aliasing: S0 == S_final is allowed (in-place state update); any other
  *    overlap between an output and another argument is not.
- *  - Supported sizes: d_k and d_v in {64, 128}; chunk == 64.
+ *  - Supported sizes: d_k and d_v in {64, 128}; chunk == 64.  The two
+ *    prefill calls take KDA_IO_F32 only with d_k == d_v == 64 (their fp32
+ *    operand tiles do not fit in LDS otherwise); decode takes both types at
+ *    every supported size.  Anything else returns KDA_ERR_UNSUPPORTED.
  *  - Errors: every argument is validated before any work is enqueued; on a
  *    validation error nothing is enqueued and a negative KDA_ERR_* code is
  *    returned.  KDA_ERR_HIP reports a launch failure (hipGetLastError).
