@@ -20,10 +20,11 @@
 //   O_c     = QG S_c + Aqk E
 //   S_{c+1} = Diag(Gamma_L) S_c + KE^T E.
 //
-// Design (one workgroup of 4 waves per (sequence, head) chain, all of d_v):
-//  * the fp32 state never leaves the chip: each wave keeps its d_v/4 value
-//    columns of S in MFMA accumulator registers for the whole sequence, and
-//    only the chunk's S-independent operands are shared through LDS;
+// Design (one workgroup per (sequence, head) chain, all of d_v; 8 waves -- two
+// per SIMD -- for d_v = 128, 4 for d_v = 64):
+//  * the fp32 state never leaves the chip: each wave keeps its d_v/NW value
+//    columns of S in registers for the whole sequence, and only the chunk's
+//    S-independent operands are shared through LDS;
 //  * S and E are consumed straight from the accumulator layout: two stacked
 //    16-row accumulator tiles are one 32-deep MFMA operand once the k index is
 //    relabelled (k = 4g + e for e < 4, 16 + 4g + e - 4 for e >= 4, g = lane/16);
@@ -36,7 +37,7 @@
 //  * signs are folded into the stored operands (-BV, -KE, -Aqk) so that the
 //    solve yields -E directly and no extra negation is needed;
 //  * the next chunk's inputs are loaded into registers while this chunk is
-//    computed.
+//    computed, in three batches spread over the phases.
 //  * Exactness guard: the single chunk-start reference of KI = k / Gamma needs
 //    Gamma_L >= 2^-100 in every key channel.  A chunk that decays more than
 //    that in any channel is processed token by token (the recurrence itself)
@@ -255,7 +256,7 @@ struct RawIo {
 // ============================================================ configuration
 // Four waves per workgroup; wave w owns value columns [w d_v/4, (w+1) d_v/4)
 // of the state for the whole sequence.
-template <int DK_, int DV_, class Io_, class Op_>
+template <int DK_, int DV_, class Io_, class Op_, int NW_ = 4>
 struct ChunkCfg {
   static constexpr int DK = DK_, DV = DV_;
   typedef Io_ Io;
@@ -263,20 +264,20 @@ struct ChunkCfg {
   typedef typename Op::T T;
   static constexpr int C = 64;          // tokens per chunk
   static constexpr int NB = 4;          // 16-token blocks per chunk
-  static constexpr int NW = 4;          // waves per workgroup
+  static constexpr int NW = NW_;        // waves per workgroup (4 or 8)
   static constexpr int NTHREADS = 64 * NW;
   static constexpr int NKS = DK / 32;   // 32-deep steps over key channels
   static constexpr int MTK = DK / 16;   // 16-row tiles over key channels
   static constexpr int VW = DV / NW;    // value columns per wave
   static constexpr int NVT = VW / 16;   // 16-column value tiles per wave
-  static constexpr int NWT = DK / 16 / NW;   // 16-column W tiles per wave
   // prep layout: each lane holds 8 consecutive key channels of TPL tokens
   static constexpr int CPL = 8;
   static constexpr int CQ = DK / NW / CPL;   // lanes across a wave's key channels
   static constexpr int TG = 64 / CQ;         // token groups
   static constexpr int TPL = C / TG;         // tokens per lane
   static constexpr int VPL = VW / CQ;        // value channels per lane
-  static_assert(CQ * TG == 64 && TPL * TG == C && VPL * CQ == VW && NWT >= 1, "layout");
+  static_assert((NW == 4 || NW == 8) && CQ * TG == 64 && TPL * TG == C && VPL * CQ == VW,
+                "layout");
   // LDS leading dimensions (elements)
   static constexpr int LD_K = DK + Op::PAD_RM;   // QG, KG, KI  [C][LD_K]
   static constexpr int LD_E = DK + Op::PAD_TR;   // KE          [C][LD_E]
@@ -327,7 +328,7 @@ struct ChunkKernel {
     RawIo<Io, VPL> v[TPL];
     float beta;
   };
-  enum { LOAD_QKV = 1, LOAD_G = 2, LOAD_ALL = 3 };
+  enum { LOAD_Q = 1, LOAD_K = 2, LOAD_V = 4, LOAD_G = 8, LOAD_ALL = 15 };
 
   // N contiguous LDS elements written as one vector store
   template <int N>
@@ -381,14 +382,12 @@ struct ChunkKernel {
     // lane part in the VGPR offset, the token step in the scalar offset
 #pragma unroll
     for (int t = 0; t < TPL; ++t) {
-      if (PART & LOAD_QKV) {
-        r.q[t].w.load(rq, o.qk, t * o.sqk);
-        r.k[t].w.load(rk, o.qk, t * o.sqk);
-        r.v[t].w.load(rv, o.v, t * o.sv);
-      }
+      if (PART & LOAD_Q) r.q[t].w.load(rq, o.qk, t * o.sqk);
+      if (PART & LOAD_K) r.k[t].w.load(rk, o.qk, t * o.sqk);
+      if (PART & LOAD_V) r.v[t].w.load(rv, o.v, t * o.sv);
       if (PART & LOAD_G) r.g[t].load(rg, o.g, t * o.sg);
     }
-    if (PART & LOAD_QKV) r.beta = buf_load<float>(rb, o.beta);   // lane l: beta of token l
+    if (PART & LOAD_V) r.beta = buf_load<float>(rb, o.beta);   // lane l: beta of token l
   }
 
   // ---------------------------------------------------------------- prep
@@ -517,8 +516,21 @@ struct ChunkKernel {
     Op::st_ct(l, AQT, Cfg::LD_64, 16 * J, 16 * I, -accA);
   }
 
-  // 10 tile pairs over 4 waves: 3, 3, 2, 2
+  // The 10 tile pairs over the waves: 3, 3, 2, 2 (four waves) or 2, 2, 1 x 6.
   static __device__ __forceinline__ void phase_a(LDS char* smem) {
+    if (NW == 8) {
+      switch (threadIdx.x >> 6) {
+        case 0: tile_qk(smem, 0, 0); tile_qk(smem, 1, 1); break;
+        case 1: tile_qk(smem, 1, 0); tile_qk(smem, 2, 2); break;
+        case 2: tile_qk(smem, 2, 0); break;
+        case 3: tile_qk(smem, 2, 1); break;
+        case 4: tile_qk(smem, 3, 0); break;
+        case 5: tile_qk(smem, 3, 1); break;
+        case 6: tile_qk(smem, 3, 2); break;
+        default: tile_qk(smem, 3, 3); break;
+      }
+      return;
+    }
     switch (threadIdx.x >> 6) {
       case 0: tile_qk(smem, 0, 0); tile_qk(smem, 1, 0); tile_qk(smem, 1, 1); break;
       case 1: tile_qk(smem, 2, 0); tile_qk(smem, 2, 1); tile_qk(smem, 2, 2); break;
@@ -528,10 +540,11 @@ struct ChunkKernel {
   }
 
   // ---------------------------------------------------------------- phase T
-  // T_II = (I + R_II)^{-1} for block I = wave id, by column forward
+  // T_II = (I + R_II)^{-1} for block I = wave id (waves 0-3), by column forward
   // substitution; lane l%16 = column.  Written transposed (TD[I][col][i]).
   static __device__ __forceinline__ void invert_diag(LDS char* smem) {
     const int w = threadIdx.x >> 6, l = lane_fresh();
+    if (w >= 4) return;
     const int col = l & 15;
     const LDS float* RD = (const LDS float*)(smem + Cfg::OFF_RD) + w * 16 * Cfg::RD_LD;
     LDS T* TD = (LDS T*)(smem + Cfg::OFF_TD) + w * 256;
@@ -791,33 +804,39 @@ struct ChunkKernel {
     }
 
     // One register buffer of raw inputs: the prep consumes chunk c; the loads
-    // of chunk c + 1 go into the same registers once the inverse is done.
+    // of chunk c + 1 go into the same registers afterwards, spread over the
+    // phases (gates after the prep, q and k after the key-key tiles, v and
+    // beta after the inverse) so that the memory system sees a steady stream
+    // instead of one burst per chunk that would stall the issuing waves.
     const Offsets offs = lane_offsets(H);
     Raw raw;
     if (len > 0) load_raw<LOAD_ALL>(raw, offs, q, k, v, g, beta, row_base, H, h, len < C ? len : C);
     for (int c0 = 0; c0 < len; c0 += C) {
       const int clen = (len - c0) < C ? (len - c0) : C;
+      const bool more = c0 + C < len;
+      const int nlen = (len - c0 - C) < C ? (len - c0 - C) : C;
+      const size_t next = row_base + c0 + C;
       const int bad = prep(raw, smem, scale);
       if (lane_fresh() == 0) FL[w] = __any(bad) ? 1 : 0;
+      compiler_fence();
+      if (more) load_raw<LOAD_G>(raw, offs, q, k, v, g, beta, next, H, h, nlen);
       __syncthreads();                                           // B1
       int any_bad = 0;
 #pragma unroll
       for (int i = 0; i < NW; ++i) any_bad |= FL[i];
-      const bool more = c0 + C < len;
-      const int nlen = (len - c0 - C) < C ? (len - c0 - C) : C;
       if (!any_bad) {
         phase_a(smem);
+        compiler_fence();
+        if (more) load_raw<LOAD_Q | LOAD_K>(raw, offs, q, k, v, g, beta, next, H, h, nlen);
         __syncthreads();                                         // B2
         invert_diag(smem);
-        // the next chunk's loads stay in flight through the scan (issued
-        // before the inverse they would overlap two register peaks)
         compiler_fence();
-        if (more) load_raw<LOAD_ALL>(raw, offs, q, k, v, g, beta, row_base + c0 + C, H, h, nlen);
+        if (more) load_raw<LOAD_V>(raw, offs, q, k, v, g, beta, next, H, h, nlen);
         __syncthreads();                                         // B3
         scan_step(smem, S, out, row_base + c0, H, h, clen);
       } else {
         recurrent_chunk(S, q, k, v, g, beta, out, row_base + c0, H, h, clen, scale);
-        if (more) load_raw<LOAD_ALL>(raw, offs, q, k, v, g, beta, row_base + c0 + C, H, h, nlen);
+        if (more) load_raw<LOAD_Q | LOAD_K | LOAD_V>(raw, offs, q, k, v, g, beta, next, H, h, nlen);
       }
       __syncthreads();                                           // LDS reuse
     }
@@ -893,16 +912,18 @@ hipError_t launch_chunk(const void* q, const void* k, const void* v, const float
                         const float* beta, const float* S0, void* out, float* S_final,
                         const int32_t* cu_seqlens, int n_seq, int T, int H, int dk, int dv,
                         float scale, bool bf16, hipStream_t stream) {
-#define KDA_CH(DK, DV, IO, OP)                                                            \
-  return launch_chunk_t<ChunkCfg<DK, DV, IO, OP>>(q, k, v, g, beta, S0, out, S_final,     \
-                                                  cu_seqlens, n_seq, T, H, scale, stream);
+#define KDA_CH(DK, DV, IO, OP, NWV)                                                       \
+  return launch_chunk_t<ChunkCfg<DK, DV, IO, OP, NWV>>(q, k, v, g, beta, S0, out, S_final, \
+                                                       cu_seqlens, n_seq, T, H, scale, stream);
+  // d_v = 128 runs 8 waves (two per SIMD, 16 value columns each); d_v = 64
+  // keeps 4 (value tiles are 16 columns wide).
   if (bf16) {
-    if (dk == 128 && dv == 128) { KDA_CH(128, 128, IoBf16, OpBf16) }
-    if (dk == 128 && dv == 64) { KDA_CH(128, 64, IoBf16, OpBf16) }
-    if (dk == 64 && dv == 128) { KDA_CH(64, 128, IoBf16, OpBf16) }
-    if (dk == 64 && dv == 64) { KDA_CH(64, 64, IoBf16, OpBf16) }
+    if (dk == 128 && dv == 128) { KDA_CH(128, 128, IoBf16, OpBf16, 8) }
+    if (dk == 128 && dv == 64) { KDA_CH(128, 64, IoBf16, OpBf16, 4) }
+    if (dk == 64 && dv == 128) { KDA_CH(64, 128, IoBf16, OpBf16, 8) }
+    if (dk == 64 && dv == 64) { KDA_CH(64, 64, IoBf16, OpBf16, 4) }
   } else {
-    if (dk == 64 && dv == 64) { KDA_CH(64, 64, IoF32, OpF32) }
+    if (dk == 64 && dv == 64) { KDA_CH(64, 64, IoF32, OpF32, 4) }
   }
 #undef KDA_CH
   return hipErrorInvalidValue;
