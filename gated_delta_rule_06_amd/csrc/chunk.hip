@@ -8,8 +8,7 @@
 // sum), Gamma_L the decay over the whole chunk, and
 //
 //   QG_i = s q_i * Gamma_i          KG_i = beta_i k_i * Gamma_i
-//   KI_i = k_i / Gamma_i            KE_i = k_i * Gamma_L / Gamma_i   (K_end)
-//   BV_i = beta_i v_i
+//   KI_i = k_i / Gamma_i            BV_i = beta_i v_i
 //
 // (products per key channel).  Then (section 6.3) R = strict_tril(KG KI^T)
 // holds rho_ij = beta_i <k_j, D_{j+1:i} k_i>, (section 6.5) Aqk = tril(QG KI^T)
@@ -18,7 +17,10 @@
 // solve of section 6.3).  Finally (6.4, 6.5)
 //
 //   O_c     = QG S_c + Aqk E
-//   S_{c+1} = Diag(Gamma_L) S_c + KE^T E.
+//   S_{c+1} = Diag(Gamma_L) (S_c + KI^T E)
+//
+// (the second line is Diag(Gamma_L) S_c + K_end^T E with K_end = k Gamma_L /
+// Gamma row-wise, so K_end is never formed).
 //
 // Design (one workgroup per (sequence, head) chain, all of d_v; 8 waves -- two
 // per SIMD -- for d_v = 128, 4 for d_v = 64):
@@ -34,8 +36,8 @@
 //  * the triangular solve runs by 16-token blocks: the four 16x16 diagonal
 //    blocks of I + R are inverted by forward substitution (S-independent, once
 //    per chunk), then X_I = T_II (Y_I - sum_{J<I} R_IJ X_J) on MFMA;
-//  * signs are folded into the stored operands (-BV, -KE, -Aqk) so that the
-//    solve yields -E directly and no extra negation is needed;
+//  * signs are folded into the stored operands (-BV, -KI, hence -R and -Aqk)
+//    so that the solve yields -E directly and no extra negation is needed;
 //  * the next chunk's inputs are loaded into registers while this chunk is
 //    computed, in three batches spread over the phases.
 //  * Exactness guard: the single chunk-start reference of KI = k / Gamma needs
@@ -279,31 +281,27 @@ struct ChunkCfg {
   static_assert((NW == 4 || NW == 8) && CQ * TG == 64 && TPL * TG == C && VPL * CQ == VW,
                 "layout");
   // LDS leading dimensions (elements)
-  static constexpr int LD_K = DK + Op::PAD_RM;   // QG, KG, KI  [C][LD_K]
-  static constexpr int LD_E = DK + Op::PAD_TR;   // KE          [C][LD_E]
+  static constexpr int LD_K = DK + Op::PAD_RM;   // QG, KG, KIn [C][LD_K]
   static constexpr int LD_V = DV + Op::PAD_TR;   // BV          [C][LD_V]
   static constexpr int LD_64 = C + Op::PAD_64;   // RTn, AQT [C][LD_64], WTn [DK][LD_64]
   static constexpr int SZ = sizeof(T);
-  // LDS byte offsets.  The output staging tile OST (scan) overlays KI, which
-  // is dead once the key-key tiles are built.
+  // LDS byte offsets.
   static constexpr int OFF_QG = 0;
   static constexpr int OFF_KG = OFF_QG + C * LD_K * SZ;
   static constexpr int OFF_KI = OFF_KG + C * LD_K * SZ;
   static constexpr int OFF_RD = OFF_KI + C * LD_K * SZ;
   static constexpr int RD_LD = 20;     // floats per column of a diagonal block (padded)
-  static constexpr int OFF_KE = OFF_RD + NB * 16 * RD_LD * 4;
-  static constexpr int OFF_BV = OFF_KE + C * LD_E * SZ;
+  static constexpr int LD_OS = DV + Op::PAD_RM;  // OST [C][LD_OS]
+  static constexpr int OFF_OS = OFF_RD + NB * 16 * RD_LD * 4;
+  static constexpr int OFF_BV = OFF_OS + C * LD_OS * SZ;
   static constexpr int OFF_AQ = OFF_BV + C * LD_V * SZ;
   static constexpr int OFF_RT = OFF_AQ + C * LD_64 * SZ;
   static constexpr int OFF_TD = OFF_RT + C * LD_64 * SZ;
   static constexpr int OFF_GL = OFF_TD + NB * 16 * 16 * SZ;
   static constexpr int OFF_FL = OFF_GL + DK * 4;
-  static constexpr int LDS_BYTES = OFF_FL + 64;
-  static constexpr int LD_OS = DV + Op::PAD_RM;  // OST [C][LD_OS]
-  static constexpr int OFF_OS = (LD_OS <= LD_K) ? OFF_KI : OFF_FL + 64;
-  static constexpr int LDS_TOTAL = (OFF_OS == OFF_KI) ? LDS_BYTES : OFF_OS + C * LD_OS * SZ;
-  static_assert(LDS_BYTES + C * (DV + Op::PAD_RM) * SZ <= 160 * 1024, "LDS budget");
-  static_assert(OFF_KG % 16 == 0 && OFF_KI % 16 == 0 && OFF_RD % 16 == 0 && OFF_KE % 16 == 0 && OFF_FL % 16 == 0 &&
+  static constexpr int LDS_TOTAL = OFF_FL + 64;
+  static_assert(LDS_TOTAL <= 160 * 1024, "LDS budget");
+  static_assert(OFF_KG % 16 == 0 && OFF_KI % 16 == 0 && OFF_RD % 16 == 0 && OFF_OS % 16 == 0 && OFF_FL % 16 == 0 &&
                 OFF_BV % 16 == 0 && OFF_AQ % 16 == 0 && OFF_RT % 16 == 0 && OFF_TD % 16 == 0 &&
                 OFF_GL % 16 == 0 && (LD_K * SZ) % 16 == 0, "LDS alignment");
 };
@@ -401,7 +399,6 @@ struct ChunkKernel {
     LDS T* QG = (LDS T*)(smem + Cfg::OFF_QG);
     LDS T* KG = (LDS T*)(smem + Cfg::OFF_KG);
     LDS T* KI = (LDS T*)(smem + Cfg::OFF_KI);
-    LDS T* KE = (LDS T*)(smem + Cfg::OFF_KE);
     LDS T* BV = (LDS T*)(smem + Cfg::OFF_BV);
     LDS float* GL = (LDS float*)(smem + Cfg::OFF_GL);
 
@@ -443,20 +440,18 @@ struct ChunkKernel {
       float qv[CPL], kv[CPL];
       r.q[t].unpack(qv);
       r.k[t].unpack(kv);
-      T qg[CPL], kg[CPL], ki[CPL], ke[CPL];
+      T qg[CPL], kg[CPL], ki[CPL];
 #pragma unroll
       for (int c = 0; c < CPL; ++c) {
         const float gam = ex[c] * cp[t][c];
         const float inv = __builtin_amdgcn_rcpf(gam);
         qg[c] = Op::cvt(scale * qv[c] * gam);
         kg[c] = Op::cvt(bt * kv[c] * gam);
-        ki[c] = Op::cvt(kv[c] * inv);
-        ke[c] = Op::cvt(-kv[c] * (tot[c] * inv));
+        ki[c] = Op::cvt(-kv[c] * inv);          // -KI
       }
       st_chunk(QG + i * Cfg::LD_K + kc0, qg);
       st_chunk(KG + i * Cfg::LD_K + kc0, kg);
       st_chunk(KI + i * Cfg::LD_K + kc0, ki);
-      st_chunk(KE + i * Cfg::LD_E + kc0, ke);
       float vv[VPL];
       r.v[t].unpack(vv);
       T bv[VPL];
@@ -481,9 +476,10 @@ struct ChunkKernel {
   }
 
   // ---------------------------------------------------------------- phase A
-  // R = strict_tril(KG KI^T) and Aqk = tril(QG KI^T) by 16x16 tiles.
-  // Off-diagonal R tiles go negated and transposed to RTn, diagonal R tiles
-  // to RD (fp32, transposed) for the inverse, -Aqk transposed to AQT.
+  // R = strict_tril(KG KI^T) and Aqk = tril(QG KI^T) by 16x16 tiles, from
+  // the stored -KI (so the products come out negated).  Off-diagonal -R tiles
+  // go transposed to RTn, diagonal R tiles to RD (fp32, transposed) for the
+  // inverse, -Aqk transposed to AQT.
   static __device__ __forceinline__ void tile_qk(LDS char* smem, int I, int J) {
     const int l = lane_fresh();
     const LDS T* QG = (const LDS T*)(smem + Cfg::OFF_QG);
@@ -509,11 +505,11 @@ struct ChunkKernel {
         if (!(n <= g4 + r)) accA[r] = 0.f;   // lower with diagonal
       }
       // RD[I][m][i] = R[16I + i][16I + m]  (column m of the block, contiguous over i)
-      *lds_ptr<f32x4>(RD + I * 16 * Cfg::RD_LD + n * Cfg::RD_LD + g4) = accR;
+      *lds_ptr<f32x4>(RD + I * 16 * Cfg::RD_LD + n * Cfg::RD_LD + g4) = -accR;
     } else {
-      Op::st_ct(l, RTn, Cfg::LD_64, 16 * J, 16 * I, -accR);
+      Op::st_ct(l, RTn, Cfg::LD_64, 16 * J, 16 * I, accR);
     }
-    Op::st_ct(l, AQT, Cfg::LD_64, 16 * J, 16 * I, -accA);
+    Op::st_ct(l, AQT, Cfg::LD_64, 16 * J, 16 * I, accA);
   }
 
   // The 10 tile pairs over the waves: 3, 3, 2, 2 (four waves) or 2, 2, 1 x 6.
@@ -577,14 +573,14 @@ struct ChunkKernel {
   // ---------------------------------------------------------------- phase S
   // Y = -Ebar = KG S - BV; X = (I + R)^{-1} Y = -E by block forward
   // substitution; O^T = S^T QG^T + (-E)^T (-Aqk)^T staged through LDS and
-  // written as whole token rows; S <- Diag(Gamma_L) S + (-KE)^T (-E).
+  // written as whole token rows; S <- Diag(Gamma_L) (S + (-KI)^T (-E)).
   static __device__ __forceinline__ void scan_step(LDS char* smem, f32x4 (&S)[MTK][NVT],
                                                    void* out, size_t row_base, int H, int h,
                                                    int clen) {
     const int w = threadIdx.x >> 6, l = lane_fresh();
     const LDS T* QG = (const LDS T*)(smem + Cfg::OFF_QG);
     const LDS T* KG = (const LDS T*)(smem + Cfg::OFF_KG);
-    const LDS T* KE = (const LDS T*)(smem + Cfg::OFF_KE);
+    const LDS T* KIn = (const LDS T*)(smem + Cfg::OFF_KI);
     const LDS T* BV = (const LDS T*)(smem + Cfg::OFF_BV);
     const LDS T* AQT = (const LDS T*)(smem + Cfg::OFF_AQ);
     const LDS T* RTn = (const LDS T*)(smem + Cfg::OFF_RT);
@@ -691,19 +687,21 @@ struct ChunkKernel {
       }
     }
 
-    // (4) state update with -KE and -E
+    // (4) state update, S <- Diag(Gamma_L) (S + KI^T E), from -KI and -E.
+    //     K_end = Diag(Gamma_L) KI row-wise, so this is Diag(Gamma_L) S +
+    //     K_end^T E without forming K_end (section 6.4).
 #pragma unroll
     for (int mt = 0; mt < MTK; ++mt) {
       const f32x4 gl = *lds_ptr<const f32x4>(GL + 16 * mt + g4);
       typename Op::F32 a[2];
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) a[kt] = Op::ld32_tr(l, KE, Cfg::LD_E, 32 * kt, 16 * mt);
+      for (int kt = 0; kt < 2; ++kt) a[kt] = Op::ld32_tr(l, KIn, Cfg::LD_K, 32 * kt, 16 * mt);
 #pragma unroll
       for (int nt = 0; nt < NVT; ++nt) {
-        f32x4 s = S[mt][nt] * gl;
+        f32x4 s = S[mt][nt];
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) s = Op::mma32(a[kt], EB[kt][nt], s);
-        S[mt][nt] = s;
+        S[mt][nt] = s * gl;
       }
     }
   }
