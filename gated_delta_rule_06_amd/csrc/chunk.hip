@@ -166,6 +166,29 @@ struct OpBf16 {
   static __device__ __forceinline__ F32 ld32_tr(int l, const LDS T* X, int ld, int k0, int m0) {
     return F32{ld16_tr(l, X, ld, k0, m0), ld16_tr(l, X, ld, k0 + 16, m0)};
   }
+  // Key-channel-permuted buffers (QG, KG, -KI): inside every block of 32
+  // channels, position 8g + e holds channel 4g + e and position 8g + 4 + e
+  // holds channel 16 + 4g + e (g, e < 4) -- the k order of a 32-deep operand
+  // -- so that one 16-byte read gives a lane both halves of its fragment.
+  static constexpr bool PERMUTED = true;
+  static __device__ __forceinline__ int perm_pos(int c) {    // c % 4 == 0
+    const int r = c & 31;
+    return (c & ~31) + 8 * ((r & 15) >> 2) + ((r & 16) >> 2);
+  }
+  static __device__ __forceinline__ F32 ld32_rmp(int l, const LDS T* X, int ld, int row0, int k0) {
+    const i16x8 v = *lds_ptr<const i16x8>(X + (row0 + (l & 15)) * ld + k0 + 8 * (l >> 4));
+    return F32{__builtin_shufflevector(v, v, 0, 1, 2, 3), __builtin_shufflevector(v, v, 4, 5, 6, 7)};
+  }
+  // transpose read of a permuted buffer: lane gets X[k0 + 4g + e][channel
+  // c0 + l%16] with c0 = a multiple of 16 (position base m0 = perm_pos(c0))
+  static __device__ __forceinline__ F16 ld16_trp(int l, const LDS T* X, int ld, int k0, int m0) {
+    const int j = l & 15;
+    const LDS T* p = X + (k0 + 4 * (l >> 4) + (j >> 2)) * ld + m0 + 8 * (j & 3);
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS i16x4*)(p));
+  }
+  static __device__ __forceinline__ F32 ld32_trp(int l, const LDS T* X, int ld, int k0, int m0) {
+    return F32{ld16_trp(l, X, ld, k0, m0), ld16_trp(l, X, ld, k0 + 16, m0)};
+  }
   // write accumulator tile t (rows row0 + 4g + r, column col0 + l%16) transposed:
   // Xt[col0 + l%16][row0 + 4g + r] for r = 0..3 (four contiguous elements)
   static __device__ __forceinline__ void st_ct(int l, LDS T* Xt, int ld, int col0, int row0, f32x4 t) {
@@ -215,6 +238,15 @@ struct OpF32 {
   }
   static __device__ __forceinline__ void st_ct(int l, LDS T* Xt, int ld, int col0, int row0, f32x4 t) {
     *lds_ptr<F16>(Xt + (col0 + (l & 15)) * ld + row0 + 4 * (l >> 4)) = t;
+  }
+  // fp32 operands keep the natural channel order
+  static constexpr bool PERMUTED = false;
+  static __device__ __forceinline__ int perm_pos(int c) { return c; }
+  static __device__ __forceinline__ F32 ld32_rmp(int l, const LDS T* X, int ld, int row0, int k0) {
+    return ld32_rm(l, X, ld, row0, k0);
+  }
+  static __device__ __forceinline__ F32 ld32_trp(int l, const LDS T* X, int ld, int k0, int m0) {
+    return ld32_tr(l, X, ld, k0, m0);
   }
 };
 
@@ -449,9 +481,9 @@ struct ChunkKernel {
         kg[c] = Op::cvt(bt * kv[c] * gam);
         ki[c] = Op::cvt(-kv[c] * inv);          // -KI
       }
-      st_chunk(QG + i * Cfg::LD_K + kc0, qg);
-      st_chunk(KG + i * Cfg::LD_K + kc0, kg);
-      st_chunk(KI + i * Cfg::LD_K + kc0, ki);
+      st_perm(QG + i * Cfg::LD_K, kc0, qg);
+      st_perm(KG + i * Cfg::LD_K, kc0, kg);
+      st_perm(KI + i * Cfg::LD_K, kc0, ki);
       float vv[VPL];
       r.v[t].unpack(vv);
       T bv[VPL];
@@ -460,6 +492,15 @@ struct ChunkKernel {
       st_chunk(BV + i * Cfg::LD_V + vc0, bv);
     }
     return bad;
+  }
+
+  // 8 consecutive channels c0 .. c0+7 of one row of a channel-permuted
+  // buffer: two 4-element pieces at their permuted positions
+  static __device__ __forceinline__ void st_perm(LDS T* row, int c0, const T (&x)[8]) {
+    if (!Op::PERMUTED) { st_chunk(row + c0, x); return; }
+    const T a[4] = {x[0], x[1], x[2], x[3]}, b[4] = {x[4], x[5], x[6], x[7]};
+    st_vec(row + Op::perm_pos(c0), a);
+    st_vec(row + Op::perm_pos(c0 + 4), b);
   }
 
   // N elements to LDS as 16-byte (or smaller) vector stores
@@ -491,9 +532,9 @@ struct ChunkKernel {
     f32x4 accR = {0.f, 0.f, 0.f, 0.f}, accA = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      const typename Op::F32 b = Op::ld32_rm(l, KI, Cfg::LD_K, 16 * J, 32 * ks);
-      const typename Op::F32 ak = Op::ld32_rm(l, KG, Cfg::LD_K, 16 * I, 32 * ks);
-      const typename Op::F32 aq = Op::ld32_rm(l, QG, Cfg::LD_K, 16 * I, 32 * ks);
+      const typename Op::F32 b = Op::ld32_rmp(l, KI, Cfg::LD_K, 16 * J, 32 * ks);
+      const typename Op::F32 ak = Op::ld32_rmp(l, KG, Cfg::LD_K, 16 * I, 32 * ks);
+      const typename Op::F32 aq = Op::ld32_rmp(l, QG, Cfg::LD_K, 16 * I, 32 * ks);
       accR = Op::mma32(ak, b, accR);
       accA = Op::mma32(aq, b, accA);
     }
@@ -609,7 +650,7 @@ struct ChunkKernel {
         Y[nt] = Op::unpack(Op::ld16_tr(l, BV, Cfg::LD_V, 16 * I, vw0 + 16 * nt));   // -BV
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        const typename Op::F32 ak = Op::ld32_rm(l, KG, Cfg::LD_K, 16 * I, 32 * ks);
+        const typename Op::F32 ak = Op::ld32_rmp(l, KG, Cfg::LD_K, 16 * I, 32 * ks);
 #pragma unroll
         for (int nt = 0; nt < NVT; ++nt) Y[nt] = Op::mma32(ak, SB[ks][nt], Y[nt]);
       }
@@ -656,7 +697,7 @@ struct ChunkKernel {
       for (int nt = 0; nt < NVT; ++nt) O[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        const typename Op::F32 bq = Op::ld32_rm(l, QG, Cfg::LD_K, 16 * I, 32 * ks);
+        const typename Op::F32 bq = Op::ld32_rmp(l, QG, Cfg::LD_K, 16 * I, 32 * ks);
 #pragma unroll
         for (int nt = 0; nt < NVT; ++nt) O[nt] = Op::mma32(SB[ks][nt], bq, O[nt]);
       }
@@ -695,7 +736,8 @@ struct ChunkKernel {
       const f32x4 gl = *lds_ptr<const f32x4>(GL + 16 * mt + g4);
       typename Op::F32 a[2];
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) a[kt] = Op::ld32_tr(l, KIn, Cfg::LD_K, 32 * kt, 16 * mt);
+      for (int kt = 0; kt < 2; ++kt)
+        a[kt] = Op::ld32_trp(l, KIn, Cfg::LD_K, 32 * kt, Op::perm_pos(16 * mt));
 #pragma unroll
       for (int nt = 0; nt < NVT; ++nt) {
         f32x4 s = S[mt][nt];
