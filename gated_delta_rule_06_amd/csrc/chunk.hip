@@ -48,6 +48,43 @@
 
 namespace kda {
 
+// ============================================================ lane shifts
+// DPP moves (a lane reads a neighbour's register inside one VALU instruction,
+// with no LDS traffic); lanes without a valid source get 1.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp1(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(1.f), __float_as_int(x), CTRL,
+                                                    ROW_MASK, 0xf, false));
+}
+// x of lane l - D inside the lane's 16-lane row (1 for the first D lanes)
+template <int D>
+__device__ __forceinline__ float dpp_row_shr(float x) { return dpp1<0x110 + D, 0xf>(x); }
+// x of lane l - 1 across the whole wave (1 for lane 0)
+__device__ __forceinline__ float dpp_wave_shr1(float x) { return dpp1<0x138, 0xf>(x); }
+// x of the last lane (15) of the previous row, into rows 1 and 3 (others 1)
+__device__ __forceinline__ float dpp_bcast15(float x) { return dpp1<0x142, 0xa>(x); }
+// x of lane 31, into rows 2 and 3 (others 1)
+__device__ __forceinline__ float dpp_bcast31(float x) { return dpp1<0x143, 0xc>(x); }
+
+// Inclusive product scan over the lanes of one parity (lane = 2 t + p,
+// p = this lane's parity): in-row shifts by 2, 4, 8, then the rows' totals
+// (lanes 16r + 14 + p) carried into the later rows -- lane 14 is first moved
+// to lane 15 for the even lanes, since the row broadcasts take lane 15/31.
+__device__ __forceinline__ float scan_stride2(float x, int p) {
+  x *= dpp_row_shr<2>(x);
+  x *= dpp_row_shr<4>(x);
+  x *= dpp_row_shr<8>(x);
+  {
+    const float odd = dpp_bcast15(x), even = dpp_bcast15(dpp_row_shr<1>(x));
+    x *= p ? odd : even;
+  }
+  {
+    const float odd = dpp_bcast31(x), even = dpp_bcast31(dpp_row_shr<1>(x));
+    x *= p ? odd : even;
+  }
+  return x;
+}
+
 // ============================================================ operand policies
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 
@@ -449,14 +486,24 @@ struct ChunkKernel {
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
       float x = cp[TPL - 1][c];
+      if (CQ == 2) {
+        x = scan_stride2(x, cq);
+        // Gamma_L: the last lane of this lane's parity
+        const float t0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 62));
+        const float t1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
+        tot[c] = cq ? t1 : t0;
+        const float y = dpp_wave_shr1(dpp_wave_shr1(x));
+        ex[c] = (l >= 2) ? y : 1.f;
+      } else {
 #pragma unroll
-      for (int d = CQ; d < 64; d <<= 1) {
-        const float y = __shfl_up(x, d);
-        if (l >= d) x *= y;
+        for (int d = CQ; d < 64; d <<= 1) {
+          const float y = __shfl_up(x, d);
+          if (l >= d) x *= y;
+        }
+        tot[c] = __shfl(x, 64 - CQ + cq);     // Gamma_L
+        const float y = __shfl_up(x, CQ);
+        ex[c] = (l >= CQ) ? y : 1.f;
       }
-      tot[c] = __shfl(x, 64 - CQ + cq);     // Gamma_L
-      const float y = __shfl_up(x, CQ);
-      ex[c] = (l >= CQ) ? y : 1.f;
     }
     int bad = 0;
 #pragma unroll
