@@ -203,14 +203,15 @@ struct OpBf16 {
   static __device__ __forceinline__ F32 ld32_tr(int l, const LDS T* X, int ld, int k0, int m0) {
     return F32{ld16_tr(l, X, ld, k0, m0), ld16_tr(l, X, ld, k0 + 16, m0)};
   }
-  // Key-channel-permuted buffers (QG, KG, -KI): inside every block of 32
-  // channels, position 8g + e holds channel 4g + e and position 8g + 4 + e
-  // holds channel 16 + 4g + e (g, e < 4) -- the k order of a 32-deep operand
-  // -- so that one 16-byte read gives a lane both halves of its fragment.
+  // Permuted buffers (QG, KG, -KI over key channels, the key-major -KI over
+  // tokens): inside every block of 32 indices, position 8g + e holds index
+  // 4g + e and position 8g + 4 + e holds index 16 + 4g + e (g, e < 4) -- the
+  // k order of a 32-deep operand -- so that one 16-byte read gives a lane both
+  // halves of its fragment.
   static constexpr bool PERMUTED = true;
-  static __device__ __forceinline__ int perm_pos(int c) {    // c % 4 == 0
+  static __device__ __forceinline__ int perm_pos(int c) {
     const int r = c & 31;
-    return (c & ~31) + 8 * ((r & 15) >> 2) + ((r & 16) >> 2);
+    return (c & ~31) + 8 * ((r & 15) >> 2) + ((r & 16) >> 2) + (r & 3);
   }
   static __device__ __forceinline__ F32 ld32_rmp(int l, const LDS T* X, int ld, int row0, int k0) {
     const i16x8 v = *lds_ptr<const i16x8>(X + (row0 + (l & 15)) * ld + k0 + 8 * (l >> 4));
@@ -366,13 +367,16 @@ struct ChunkCfg {
   static constexpr int OFF_AQ = OFF_BV + C * LD_V * SZ;
   static constexpr int OFF_RT = OFF_AQ + C * LD_64 * SZ;
   static constexpr int OFF_TD = OFF_RT + C * LD_64 * SZ;
-  static constexpr int OFF_GL = OFF_TD + NB * 16 * 16 * SZ;
+  static constexpr int LD_KT = C + Op::PAD_RM;  // KIT [DK][LD_KT]
+  static constexpr int OFF_KT = OFF_TD + NB * 16 * 16 * SZ;
+  static constexpr int OFF_GL = OFF_KT + DK * LD_KT * SZ;
   static constexpr int OFF_FL = OFF_GL + DK * 4;
   static constexpr int LDS_TOTAL = OFF_FL + 64;
   static_assert(LDS_TOTAL <= 160 * 1024, "LDS budget");
   static_assert(OFF_KG % 16 == 0 && OFF_KI % 16 == 0 && OFF_RD % 16 == 0 && OFF_OS % 16 == 0 && OFF_FL % 16 == 0 &&
                 OFF_BV % 16 == 0 && OFF_AQ % 16 == 0 && OFF_RT % 16 == 0 && OFF_TD % 16 == 0 &&
-                OFF_GL % 16 == 0 && (LD_K * SZ) % 16 == 0, "LDS alignment");
+                OFF_GL % 16 == 0 && OFF_KT % 16 == 0 && (LD_K * SZ) % 16 == 0 &&
+                (LD_KT * SZ) % 16 == 0, "LDS alignment");
 };
 
 // Threshold below which a channel's chunk decay Gamma_L makes k / Gamma unsafe.
@@ -469,6 +473,7 @@ struct ChunkKernel {
     LDS T* KG = (LDS T*)(smem + Cfg::OFF_KG);
     LDS T* KI = (LDS T*)(smem + Cfg::OFF_KI);
     LDS T* BV = (LDS T*)(smem + Cfg::OFF_BV);
+    LDS T* KIT = (LDS T*)(smem + Cfg::OFF_KT);
     LDS float* GL = (LDS float*)(smem + Cfg::OFF_GL);
 
     // in-lane running products of alpha over the lane's TPL tokens
@@ -512,6 +517,7 @@ struct ChunkKernel {
       *lds_ptr<f32x4>(GL + kc0) = f32x4{tot[0], tot[1], tot[2], tot[3]};
       *lds_ptr<f32x4>(GL + kc0 + 4) = f32x4{tot[4], tot[5], tot[6], tot[7]};
     }
+    T kit[CPL][TPL];   // -KI of the lane's tokens, per key channel
 #pragma unroll
     for (int t = 0; t < TPL; ++t) {
       const int i = TPL * tg + t;
@@ -527,6 +533,7 @@ struct ChunkKernel {
         qg[c] = Op::cvt(scale * qv[c] * gam);
         kg[c] = Op::cvt(bt * kv[c] * gam);
         ki[c] = Op::cvt(-kv[c] * inv);          // -KI
+        kit[c][t] = ki[c];
       }
       st_perm(QG + i * Cfg::LD_K, kc0, qg);
       st_perm(KG + i * Cfg::LD_K, kc0, kg);
@@ -538,6 +545,10 @@ struct ChunkKernel {
       for (int c = 0; c < VPL; ++c) bv[c] = Op::cvt(-bt * vv[c]);
       st_chunk(BV + i * Cfg::LD_V + vc0, bv);
     }
+    // key-major copy KIT[channel][token]: the lane's TPL tokens are
+    // consecutive (and stay so under the token permutation)
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) st_vec(KIT + (kc0 + c) * Cfg::LD_KT + Op::perm_pos(TPL * tg), kit[c]);
     return bad;
   }
 
@@ -668,7 +679,7 @@ struct ChunkKernel {
     const int w = threadIdx.x >> 6, l = lane_fresh();
     const LDS T* QG = (const LDS T*)(smem + Cfg::OFF_QG);
     const LDS T* KG = (const LDS T*)(smem + Cfg::OFF_KG);
-    const LDS T* KIn = (const LDS T*)(smem + Cfg::OFF_KI);
+    const LDS T* KIT = (const LDS T*)(smem + Cfg::OFF_KT);
     const LDS T* BV = (const LDS T*)(smem + Cfg::OFF_BV);
     const LDS T* AQT = (const LDS T*)(smem + Cfg::OFF_AQ);
     const LDS T* RTn = (const LDS T*)(smem + Cfg::OFF_RT);
@@ -784,7 +795,7 @@ struct ChunkKernel {
       typename Op::F32 a[2];
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
-        a[kt] = Op::ld32_trp(l, KIn, Cfg::LD_K, 32 * kt, Op::perm_pos(16 * mt));
+        a[kt] = Op::ld32_rmp(l, KIT, Cfg::LD_KT, 16 * mt, 32 * kt);
 #pragma unroll
       for (int nt = 0; nt < NVT; ++nt) {
         f32x4 s = S[mt][nt];
