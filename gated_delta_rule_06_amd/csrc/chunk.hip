@@ -158,7 +158,6 @@ struct OpBf16 {
   typedef uint16_t T;
   static constexpr int PAD_RM = 8;    // row padding (elements) of buffers read row-wise
   static constexpr int PAD_TR = 16;   // row padding of buffers read with the transpose read
-  static constexpr int PAD_64 = 16;   // row padding of 64-wide buffers
   typedef i16x4 F16;                  // 16-deep operand fragment
   struct F32 { i16x4 lo, hi; };       // 32-deep operand fragment
 
@@ -239,7 +238,6 @@ struct OpF32 {
   typedef float T;
   static constexpr int PAD_RM = 4;
   static constexpr int PAD_TR = 4;
-  static constexpr int PAD_64 = 4;
   typedef f32x4 F16;
   struct F32 { f32x4 lo, hi; };
 
@@ -353,7 +351,7 @@ struct ChunkCfg {
   // LDS leading dimensions (elements)
   static constexpr int LD_K = DK + Op::PAD_RM;   // QG, KG, KIn [C][LD_K]
   static constexpr int LD_V = DV + Op::PAD_TR;   // BV          [C][LD_V]
-  static constexpr int LD_64 = C + Op::PAD_64;   // RTn, AQT [C][LD_64], WTn [DK][LD_64]
+  static constexpr int LD_64 = C + Op::PAD_RM;   // RR, AQ [C][LD_64] (row-wise reads)
   static constexpr int SZ = sizeof(T);
   // LDS byte offsets.
   static constexpr int OFF_QG = 0;
@@ -576,16 +574,19 @@ struct ChunkKernel {
 
   // ---------------------------------------------------------------- phase A
   // R = strict_tril(KG KI^T) and Aqk = tril(QG KI^T) by 16x16 tiles, from
-  // the stored -KI (so the products come out negated).  Off-diagonal -R tiles
-  // go transposed to RTn, diagonal R tiles to RD (fp32, transposed) for the
-  // inverse, -Aqk transposed to AQT.
+  // the stored -KI (so the products come out negated).  The tiles are formed
+  // as (KI QG^T)^T-style products so that a lane ends up with four
+  // consecutive columns of one row: off-diagonal -R tiles go row-major to RR,
+  // -Aqk row-major to AQ (columns permuted like the 32-deep operand that reads
+  // them), and the diagonal R tiles (in the other orientation) to RD, fp32,
+  // column-contiguous, for the inverse.
   static __device__ __forceinline__ void tile_qk(LDS char* smem, int I, int J) {
     const int l = lane_fresh();
     const LDS T* QG = (const LDS T*)(smem + Cfg::OFF_QG);
     const LDS T* KG = (const LDS T*)(smem + Cfg::OFF_KG);
     const LDS T* KI = (const LDS T*)(smem + Cfg::OFF_KI);
-    LDS T* RTn = (LDS T*)(smem + Cfg::OFF_RT);
-    LDS T* AQT = (LDS T*)(smem + Cfg::OFF_AQ);
+    LDS T* RR = (LDS T*)(smem + Cfg::OFF_RT);
+    LDS T* AQ = (LDS T*)(smem + Cfg::OFF_AQ);
     LDS float* RD = (LDS float*)(smem + Cfg::OFF_RD);
     f32x4 accR = {0.f, 0.f, 0.f, 0.f}, accA = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -593,22 +594,25 @@ struct ChunkKernel {
       const typename Op::F32 b = Op::ld32_rmp(l, KI, Cfg::LD_K, 16 * J, 32 * ks);
       const typename Op::F32 ak = Op::ld32_rmp(l, KG, Cfg::LD_K, 16 * I, 32 * ks);
       const typename Op::F32 aq = Op::ld32_rmp(l, QG, Cfg::LD_K, 16 * I, 32 * ks);
-      accR = Op::mma32(ak, b, accR);
-      accA = Op::mma32(aq, b, accA);
+      accR = (I == J) ? Op::mma32(ak, b, accR) : Op::mma32(b, ak, accR);
+      accA = Op::mma32(b, aq, accA);
     }
+    // accA[r] = -Aqk[16I + n][16J + g4 + r]; accR[r] = -R[16I + g4 + r][16I + n]
+    // on the diagonal, -R[16I + n][16J + g4 + r] off it
     const int n = l & 15, g4 = 4 * (l >> 4);
     if (I == J) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         if (!(n < g4 + r)) accR[r] = 0.f;    // strictly lower
-        if (!(n <= g4 + r)) accA[r] = 0.f;   // lower with diagonal
+        if (!(g4 + r <= n)) accA[r] = 0.f;   // lower with diagonal
       }
       // RD[I][m][i] = R[16I + i][16I + m]  (column m of the block, contiguous over i)
       *lds_ptr<f32x4>(RD + I * 16 * Cfg::RD_LD + n * Cfg::RD_LD + g4) = -accR;
     } else {
-      Op::st_ct(l, RTn, Cfg::LD_64, 16 * J, 16 * I, accR);
+      *lds_ptr<typename Op::F16>(RR + (16 * I + n) * Cfg::LD_64 + 16 * J + g4) = Op::pack(accR);
     }
-    Op::st_ct(l, AQT, Cfg::LD_64, 16 * J, 16 * I, accA);
+    *lds_ptr<typename Op::F16>(AQ + (16 * I + n) * Cfg::LD_64 + Op::perm_pos(16 * J + g4)) =
+        Op::pack(accA);
   }
 
   // The 10 tile pairs over the waves: 3, 3, 2, 2 (four waves) or 2, 2, 1 x 6.
@@ -681,8 +685,8 @@ struct ChunkKernel {
     const LDS T* KG = (const LDS T*)(smem + Cfg::OFF_KG);
     const LDS T* KIT = (const LDS T*)(smem + Cfg::OFF_KT);
     const LDS T* BV = (const LDS T*)(smem + Cfg::OFF_BV);
-    const LDS T* AQT = (const LDS T*)(smem + Cfg::OFF_AQ);
-    const LDS T* RTn = (const LDS T*)(smem + Cfg::OFF_RT);
+    const LDS T* AQ = (const LDS T*)(smem + Cfg::OFF_AQ);
+    const LDS T* RR = (const LDS T*)(smem + Cfg::OFF_RT);
     const LDS T* TD = (const LDS T*)(smem + Cfg::OFF_TD);
     LDS T* OST = (LDS T*)(smem + Cfg::OFF_OS);
     const LDS float* GL = (const LDS float*)(smem + Cfg::OFF_GL);
@@ -723,8 +727,8 @@ struct ChunkKernel {
         for (int nt = 0; nt < NVT; ++nt) Z[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int J = 0; J < I; ++J) {
-          // A[m = i][k = j] = -R[16I + m][16J + k] = RTn[16J + k][16I + m]
-          const typename Op::F16 a = Op::ld16_tr(l, RTn, Cfg::LD_64, 16 * J, 16 * I);
+          // A[m = i][k = j] = -R[16I + m][16J + k] = RR[16I + m][16J + k]
+          const typename Op::F16 a = Op::ld16_rm(l, RR, Cfg::LD_64, 16 * I, 16 * J);
 #pragma unroll
           for (int nt = 0; nt < NVT; ++nt) Z[nt] = Op::mma16(a, XP[J][nt], Z[nt]);
         }
@@ -761,7 +765,7 @@ struct ChunkKernel {
       }
 #pragma unroll
       for (int kt = 0; kt <= I / 2; ++kt) {
-        const typename Op::F32 ba = Op::ld32_tr(l, AQT, Cfg::LD_64, 32 * kt, 16 * I);
+        const typename Op::F32 ba = Op::ld32_rmp(l, AQ, Cfg::LD_64, 16 * I, 32 * kt);
 #pragma unroll
         for (int nt = 0; nt < NVT; ++nt) O[nt] = Op::mma32(EB[kt][nt], ba, O[nt]);
       }
@@ -882,10 +886,11 @@ struct ChunkKernel {
     const int vw0 = w * VW;
     LDS int* FL = (LDS int*)(smem + Cfg::OFF_FL);
 
-    // Aqk^T tiles above the diagonal are never written: zero the buffer once.
+    // -Aqk tiles above the diagonal are read (inside 32-deep operands) but never
+    // written: zero the buffer once.
     {
-      LDS T* AQT = (LDS T*)(smem + Cfg::OFF_AQ);
-      for (int i = threadIdx.x; i < C * Cfg::LD_64; i += Cfg::NTHREADS) AQT[i] = Op::cvt(0.f);
+      LDS T* AQ = (LDS T*)(smem + Cfg::OFF_AQ);
+      for (int i = threadIdx.x; i < C * Cfg::LD_64; i += Cfg::NTHREADS) AQ[i] = Op::cvt(0.f);
     }
     // state tiles: S[16mt + 4g + r][vw0 + 16nt + n]
     f32x4 S[MTK][NVT];
