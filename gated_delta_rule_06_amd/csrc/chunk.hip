@@ -367,13 +367,18 @@ struct ChunkCfg {
   static constexpr int OFF_TD = OFF_RT + C * LD_64 * SZ;
   static constexpr int LD_KT = C + Op::PAD_RM;  // KIT [DK][LD_KT]
   static constexpr int OFF_KT = OFF_TD + NB * 16 * 16 * SZ;
-  static constexpr int OFF_GL = OFF_KT + DK * LD_KT * SZ;
+  // per-wave block for the decay scan (two lanes per token group, 16 key
+  // channels per wave): 16 channel rows of 32 group totals (padded)
+  static constexpr int SC_LD = 36;
+  static constexpr int OFF_SC = OFF_KT + DK * LD_KT * SZ;
+  static constexpr int SZ_SC = (CQ == 2 && DK / NW == 16) ? NW * 16 * SC_LD * 4 : 0;
+  static constexpr int OFF_GL = OFF_SC + SZ_SC;
   static constexpr int OFF_FL = OFF_GL + DK * 4;
   static constexpr int LDS_TOTAL = OFF_FL + 64;
   static_assert(LDS_TOTAL <= 160 * 1024, "LDS budget");
   static_assert(OFF_KG % 16 == 0 && OFF_KI % 16 == 0 && OFF_RD % 16 == 0 && OFF_OS % 16 == 0 && OFF_FL % 16 == 0 &&
                 OFF_BV % 16 == 0 && OFF_AQ % 16 == 0 && OFF_RT % 16 == 0 && OFF_TD % 16 == 0 &&
-                OFF_GL % 16 == 0 && OFF_KT % 16 == 0 && (LD_K * SZ) % 16 == 0 &&
+                OFF_GL % 16 == 0 && OFF_KT % 16 == 0 && OFF_SC % 16 == 0 && (LD_K * SZ) % 16 == 0 &&
                 (LD_KT * SZ) % 16 == 0, "LDS alignment");
 };
 
@@ -483,21 +488,50 @@ struct ChunkKernel {
         const float a = __expf(__uint_as_float(r.g[t].word(c)));
         cp[t][c] = (t == 0) ? a : cp[t - 1][c] * a;
       }
-    // product over the TG token groups (lanes cq + CQ tg): inclusive scan,
-    // then shift by one group for the exclusive prefix
-    float ex[CPL], tot[CPL];
+    // product over the TG token groups: ex = exclusive prefix, Gamma_L -> GL
+    float ex[CPL];
+    int bad = 0;
+    if (Cfg::SZ_SC > 0) {
+      // Two lanes per token group (lane = 2 tg + cq, 16 channels per wave).
+      // The group totals go through a wave-private LDS block, transposed to
+      // X[channel][group]; there lane 4 ch + qq takes groups 8 qq .. 8 qq + 7
+      // of channel ch: a running product over its eight groups, then an
+      // exclusive product scan over the four lanes of the quad (DPP quad
+      // permutations; the first lane of each quad holds 1, so lanes that
+      // read it are unaffected).  A wave's LDS accesses complete in order.
+      LDS float* X = (LDS float*)(smem + Cfg::OFF_SC) + w * 16 * Cfg::SC_LD;
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-      float x = cp[TPL - 1][c];
-      if (CQ == 2) {
-        x = scan_stride2(x, cq);
-        // Gamma_L: the last lane of this lane's parity
-        const float t0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 62));
-        const float t1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
-        tot[c] = cq ? t1 : t0;
-        const float y = dpp_wave_shr1(dpp_wave_shr1(x));
-        ex[c] = (l >= 2) ? y : 1.f;
-      } else {
+      for (int c = 0; c < CPL; ++c) X[(8 * cq + c) * Cfg::SC_LD + tg] = cp[TPL - 1][c];
+      __asm__ __volatile__("" ::: "memory");
+      const int ch = l >> 2, qq = l & 3;
+      LDS float* xr = X + ch * Cfg::SC_LD + 8 * qq;
+      const f32x4 v0 = *lds_ptr<const f32x4>(xr), v1 = *lds_ptr<const f32x4>(xr + 4);
+      const float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+      float e[8];
+      e[0] = 1.f;
+#pragma unroll
+      for (int m = 1; m < 8; ++m) e[m] = e[m - 1] * v[m - 1];
+      const float tq = e[7] * v[7];                       // this quarter's product
+      float z = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(tq), 0x90, 0xf, 0xf, false));
+      z = (qq == 0) ? 1.f : z;                            // quad_perm [0,0,1,2]: the previous lane
+      z *= __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(z), 0x90, 0xf, 0xf, false));
+      z *= __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(z), 0x40, 0xf, 0xf, false));
+      *lds_ptr<f32x4>(xr) = f32x4{z * e[0], z * e[1], z * e[2], z * e[3]};
+      *lds_ptr<f32x4>(xr + 4) = f32x4{z * e[4], z * e[5], z * e[6], z * e[7]};
+      if (qq == 3) {
+        const float gl = z * tq;                          // Gamma_L of channel ch
+        GL[w * 16 + ch] = gl;
+        bad = !(gl >= KDA_GAMMA_MIN);
+      }
+      __asm__ __volatile__("" ::: "memory");
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) ex[c] = X[(8 * cq + c) * Cfg::SC_LD + tg];
+    } else {
+      // inclusive scan over the lanes cq + CQ tg, then shift by one group
+      float tot[CPL];
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        float x = cp[TPL - 1][c];
 #pragma unroll
         for (int d = CQ; d < 64; d <<= 1) {
           const float y = __shfl_up(x, d);
@@ -507,13 +541,12 @@ struct ChunkKernel {
         const float y = __shfl_up(x, CQ);
         ex[c] = (l >= CQ) ? y : 1.f;
       }
-    }
-    int bad = 0;
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) bad |= !(tot[c] >= KDA_GAMMA_MIN);
-    if (tg == 0) {
-      *lds_ptr<f32x4>(GL + kc0) = f32x4{tot[0], tot[1], tot[2], tot[3]};
-      *lds_ptr<f32x4>(GL + kc0 + 4) = f32x4{tot[4], tot[5], tot[6], tot[7]};
+      for (int c = 0; c < CPL; ++c) bad |= !(tot[c] >= KDA_GAMMA_MIN);
+      if (tg == 0) {
+        *lds_ptr<f32x4>(GL + kc0) = f32x4{tot[0], tot[1], tot[2], tot[3]};
+        *lds_ptr<f32x4>(GL + kc0 + 4) = f32x4{tot[4], tot[5], tot[6], tot[7]};
+      }
     }
     T kit[CPL][TPL];   // -KI of the lane's tokens, per key channel
 #pragma unroll
@@ -916,13 +949,16 @@ struct ChunkKernel {
     if (len > 0) load_raw<LOAD_ALL>(raw, offs, q, k, v, g, beta, row_base, H, h, len < C ? len : C);
     for (int c0 = 0; c0 < len; c0 += C) {
       const int clen = (len - c0) < C ? (len - c0) : C;
+      // the next chunk's loads are issued on every step, with an empty range
+      // after the last chunk (nothing is read), so that the wait before each
+      // use of the raw registers only covers the loads older than it
       const bool more = c0 + C < len;
-      const int nlen = (len - c0 - C) < C ? (len - c0 - C) : C;
-      const size_t next = row_base + c0 + C;
+      const int nlen = !more ? 0 : ((len - c0 - C) < C ? (len - c0 - C) : C);
+      const size_t next = more ? row_base + c0 + C : row_base;
       const int bad = prep(raw, smem, scale);
       if (lane_fresh() == 0) FL[w] = __any(bad) ? 1 : 0;
       compiler_fence();
-      if (more) load_raw<LOAD_G>(raw, offs, q, k, v, g, beta, next, H, h, nlen);
+      load_raw<LOAD_G>(raw, offs, q, k, v, g, beta, next, H, h, nlen);
       __syncthreads();                                           // B1
       int any_bad = 0;
 #pragma unroll
@@ -930,16 +966,16 @@ struct ChunkKernel {
       if (!any_bad) {
         phase_a(smem);
         compiler_fence();
-        if (more) load_raw<LOAD_Q | LOAD_K>(raw, offs, q, k, v, g, beta, next, H, h, nlen);
+        load_raw<LOAD_Q | LOAD_K>(raw, offs, q, k, v, g, beta, next, H, h, nlen);
         __syncthreads();                                         // B2
         invert_diag(smem);
         compiler_fence();
-        if (more) load_raw<LOAD_V>(raw, offs, q, k, v, g, beta, next, H, h, nlen);
+        load_raw<LOAD_V>(raw, offs, q, k, v, g, beta, next, H, h, nlen);
         __syncthreads();                                         // B3
         scan_step(smem, S, out, row_base + c0, H, h, clen);
       } else {
         recurrent_chunk(S, q, k, v, g, beta, out, row_base + c0, H, h, clen, scale);
-        if (more) load_raw<LOAD_Q | LOAD_K | LOAD_V>(raw, offs, q, k, v, g, beta, next, H, h, nlen);
+        load_raw<LOAD_Q | LOAD_K | LOAD_V>(raw, offs, q, k, v, g, beta, next, H, h, nlen);
       }
       __syncthreads();                                           // LDS reuse
     }
