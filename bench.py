@@ -82,7 +82,9 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    # untimed steps first: the prefill kernel's launch time settles only after
+    # some twenty back-to-back launches (the clock ramps under sustained load)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--decode-reps", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-chains", type=int, default=160,

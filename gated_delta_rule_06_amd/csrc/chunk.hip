@@ -672,14 +672,14 @@ struct ChunkKernel {
   }
 
   // ---------------------------------------------------------------- phase T
-  // T_II = (I + R_II)^{-1} for block I = wave id (waves 0-3), by column forward
-  // substitution; lane l%16 = column.  Written transposed (TD[I][col][i]).
+  // T_II = (I + R_II)^{-1} for the four diagonal blocks at once, by column
+  // forward substitution: lane 16 I + col holds column col of block I.
+  // Written transposed (TD[I][col][i]).
   static __device__ __forceinline__ void invert_diag(LDS char* smem) {
-    const int w = threadIdx.x >> 6, l = lane_fresh();
-    if (w >= 4) return;
-    const int col = l & 15;
-    const LDS float* RD = (const LDS float*)(smem + Cfg::OFF_RD) + w * 16 * Cfg::RD_LD;
-    LDS T* TD = (LDS T*)(smem + Cfg::OFF_TD) + w * 256;
+    const int l = lane_fresh();
+    const int col = l & 15, blk = l >> 4;
+    const LDS float* RD = (const LDS float*)(smem + Cfg::OFF_RD) + blk * 16 * Cfg::RD_LD;
+    LDS T* TD = (LDS T*)(smem + Cfg::OFF_TD) + blk * 256;
     float x[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) x[i] = (i == col) ? 1.f : 0.f;
@@ -697,12 +697,10 @@ struct ChunkKernel {
         }
       }
     }
-    if (l < 16) {
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        f32x4 t = {x[4 * i4], x[4 * i4 + 1], x[4 * i4 + 2], x[4 * i4 + 3]};
-        *lds_ptr<typename Op::F16>(TD + col * 16 + 4 * i4) = Op::pack(t);
-      }
+    for (int i4 = 0; i4 < 4; ++i4) {
+      f32x4 t = {x[4 * i4], x[4 * i4 + 1], x[4 * i4 + 2], x[4 * i4 + 3]};
+      *lds_ptr<typename Op::F16>(TD + col * 16 + 4 * i4) = Op::pack(t);
     }
   }
 
@@ -710,9 +708,38 @@ struct ChunkKernel {
   // Y = -Ebar = KG S - BV; X = (I + R)^{-1} Y = -E by block forward
   // substitution; O^T = S^T QG^T + (-E)^T (-Aqk)^T staged through LDS and
   // written as whole token rows; S <- Diag(Gamma_L) (S + (-KI)^T (-E)).
+  // Y_I = KG_I S - BV_I for the four token blocks (needs no inverse), and S
+  // as 32-deep operands over key channels (lane: value column, k: channels).
+  static __device__ __forceinline__ void scan_y(LDS char* smem, const f32x4 (&S)[MTK][NVT],
+                                                typename Op::F32 (&SB)[NKS][NVT],
+                                                f32x4 (&Y)[4][NVT]) {
+    const int w = threadIdx.x >> 6, l = lane_fresh();
+    const LDS T* KG = (const LDS T*)(smem + Cfg::OFF_KG);
+    const LDS T* BV = (const LDS T*)(smem + Cfg::OFF_BV);
+    const int vw0 = w * VW;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+      for (int nt = 0; nt < NVT; ++nt)
+        SB[ks][nt] = typename Op::F32{Op::pack(S[2 * ks][nt]), Op::pack(S[2 * ks + 1][nt])};
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+#pragma unroll
+      for (int nt = 0; nt < NVT; ++nt)
+        Y[I][nt] = Op::unpack(Op::ld16_tr(l, BV, Cfg::LD_V, 16 * I, vw0 + 16 * nt));   // -BV
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const typename Op::F32 ak = Op::ld32_rmp(l, KG, Cfg::LD_K, 16 * I, 32 * ks);
+#pragma unroll
+        for (int nt = 0; nt < NVT; ++nt) Y[I][nt] = Op::mma32(ak, SB[ks][nt], Y[I][nt]);
+      }
+    }
+  }
+
   static __device__ __forceinline__ void scan_step(LDS char* smem, f32x4 (&S)[MTK][NVT],
-                                                   void* out, size_t row_base, int H, int h,
-                                                   int clen) {
+                                                   const typename Op::F32 (&SB)[NKS][NVT],
+                                                   f32x4 (&Y)[4][NVT], void* out,
+                                                   size_t row_base, int H, int h, int clen) {
     const int w = threadIdx.x >> 6, l = lane_fresh();
     const LDS T* QG = (const LDS T*)(smem + Cfg::OFF_QG);
     const LDS T* KG = (const LDS T*)(smem + Cfg::OFF_KG);
@@ -726,29 +753,12 @@ struct ChunkKernel {
     const int vw0 = w * VW;
     const int g4 = 4 * (l >> 4);
 
-    // S as 32-deep operands over key channels (lane: value column, k: channels)
-    typename Op::F32 SB[NKS][NVT];
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
-#pragma unroll
-      for (int nt = 0; nt < NVT; ++nt)
-        SB[ks][nt] = typename Op::F32{Op::pack(S[2 * ks][nt]), Op::pack(S[2 * ks + 1][nt])};
-
-    // (1) + (2): per 16-token block, Y_I = KG_I S - BV_I, then the solve
-    //     X_I = T_II (Y_I - sum_{J<I} R_IJ X_J); X kept as 16-deep operands.
+    // (2) the solve X_I = T_II (Y_I - sum_{J<I} R_IJ X_J) by 16-token
+    //     blocks; X kept as 16-deep operands.
     typename Op::F16 XP[4][NVT];
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
-      f32x4 Y[NVT];
-#pragma unroll
-      for (int nt = 0; nt < NVT; ++nt)
-        Y[nt] = Op::unpack(Op::ld16_tr(l, BV, Cfg::LD_V, 16 * I, vw0 + 16 * nt));   // -BV
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        const typename Op::F32 ak = Op::ld32_rmp(l, KG, Cfg::LD_K, 16 * I, 32 * ks);
-#pragma unroll
-        for (int nt = 0; nt < NVT; ++nt) Y[nt] = Op::mma32(ak, SB[ks][nt], Y[nt]);
-      }
+      f32x4 (&YI)[NVT] = Y[I];
       // The -R_IJ X_J terms accumulate in their own registers (16-deep
       // products) and join Y with a vector add: an accumulator produced by
       // one MFMA shape is never fed straight into another shape's
@@ -766,14 +776,14 @@ struct ChunkKernel {
           for (int nt = 0; nt < NVT; ++nt) Z[nt] = Op::mma16(a, XP[J][nt], Z[nt]);
         }
 #pragma unroll
-        for (int nt = 0; nt < NVT; ++nt) Y[nt] += Z[nt];
+        for (int nt = 0; nt < NVT; ++nt) YI[nt] += Z[nt];
       }
       // A[m = i][k = i'] = T_II[m][k] = TD[I][k][m]
       const typename Op::F16 a = Op::ld16_tr(l, TD + I * 256, 16, 0, 0);
 #pragma unroll
       for (int nt = 0; nt < NVT; ++nt) {
         const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        XP[I][nt] = Op::pack(Op::mma16(a, Op::pack(Y[nt]), z));
+        XP[I][nt] = Op::pack(Op::mma16(a, Op::pack(YI[nt]), z));
       }
     }
     // -E as 32-deep operands over tokens: two 16-deep blocks side by side
@@ -968,11 +978,21 @@ struct ChunkKernel {
         compiler_fence();
         load_raw<LOAD_Q | LOAD_K>(raw, offs, q, k, v, g, beta, next, H, h, nlen);
         __syncthreads();                                         // B2
-        invert_diag(smem);
+        // wave 0 inverts the four diagonal blocks next to its own Y (one
+        // scheduling region, so the inverse's VALU chain can fill the MFMA
+        // gaps); the other waves only form Y before the barrier
+        typename Op::F32 SB[NKS][NVT];
+        f32x4 Y[4][NVT];
+        if (__builtin_amdgcn_readfirstlane(w) == 0) {
+          invert_diag(smem);
+          scan_y(smem, S, SB, Y);
+        } else {
+          scan_y(smem, S, SB, Y);
+        }
         compiler_fence();
         load_raw<LOAD_V>(raw, offs, q, k, v, g, beta, next, H, h, nlen);
         __syncthreads();                                         // B3
-        scan_step(smem, S, out, row_base + c0, H, h, clen);
+        scan_step(smem, S, SB, Y, out, row_base + c0, H, h, clen);
       } else {
         recurrent_chunk(S, q, k, v, g, beta, out, row_base + c0, H, h, clen, scale);
         load_raw<LOAD_Q | LOAD_K | LOAD_V>(raw, offs, q, k, v, g, beta, next, H, h, nlen);
