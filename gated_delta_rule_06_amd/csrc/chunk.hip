@@ -708,14 +708,16 @@ struct ChunkKernel {
   // Y = -Ebar = KG S - BV; X = (I + R)^{-1} Y = -E by block forward
   // substitution; O^T = S^T QG^T + (-E)^T (-Aqk)^T staged through LDS and
   // written as whole token rows; S <- Diag(Gamma_L) (S + (-KI)^T (-E)).
-  // Y_I = KG_I S - BV_I for the four token blocks (needs no inverse), and S
-  // as 32-deep operands over key channels (lane: value column, k: channels).
+  // The parts that need no inverse: Y_I = KG_I S - BV_I and the S part of
+  // the outputs, O_I^T = S^T QG_I^T, for the four token blocks, with S as
+  // 32-deep operands over key channels (lane: value column, k: channels).
   static __device__ __forceinline__ void scan_y(LDS char* smem, const f32x4 (&S)[MTK][NVT],
-                                                typename Op::F32 (&SB)[NKS][NVT],
-                                                f32x4 (&Y)[4][NVT]) {
+                                                f32x4 (&Y)[4][NVT], f32x4 (&O)[4][NVT]) {
     const int w = threadIdx.x >> 6, l = lane_fresh();
     const LDS T* KG = (const LDS T*)(smem + Cfg::OFF_KG);
+    const LDS T* QG = (const LDS T*)(smem + Cfg::OFF_QG);
     const LDS T* BV = (const LDS T*)(smem + Cfg::OFF_BV);
+    typename Op::F32 SB[NKS][NVT];
     const int vw0 = w * VW;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
@@ -733,12 +735,20 @@ struct ChunkKernel {
 #pragma unroll
         for (int nt = 0; nt < NVT; ++nt) Y[I][nt] = Op::mma32(ak, SB[ks][nt], Y[I][nt]);
       }
+#pragma unroll
+      for (int nt = 0; nt < NVT; ++nt) O[I][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const typename Op::F32 bq = Op::ld32_rmp(l, QG, Cfg::LD_K, 16 * I, 32 * ks);
+#pragma unroll
+        for (int nt = 0; nt < NVT; ++nt) O[I][nt] = Op::mma32(SB[ks][nt], bq, O[I][nt]);
+      }
     }
   }
 
   static __device__ __forceinline__ void scan_step(LDS char* smem, f32x4 (&S)[MTK][NVT],
-                                                   const typename Op::F32 (&SB)[NKS][NVT],
-                                                   f32x4 (&Y)[4][NVT], void* out,
+                                                   f32x4 (&Y)[4][NVT], f32x4 (&Ob)[4][NVT],
+                                                   void* out,
                                                    size_t row_base, int H, int h, int clen) {
     const int w = threadIdx.x >> 6, l = lane_fresh();
     const LDS T* QG = (const LDS T*)(smem + Cfg::OFF_QG);
@@ -797,15 +807,7 @@ struct ChunkKernel {
     //     columns = tokens 16I + n; staged as OST[token][value]
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
-      f32x4 O[NVT];
-#pragma unroll
-      for (int nt = 0; nt < NVT; ++nt) O[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        const typename Op::F32 bq = Op::ld32_rmp(l, QG, Cfg::LD_K, 16 * I, 32 * ks);
-#pragma unroll
-        for (int nt = 0; nt < NVT; ++nt) O[nt] = Op::mma32(SB[ks][nt], bq, O[nt]);
-      }
+      f32x4 (&O)[NVT] = Ob[I];
 #pragma unroll
       for (int kt = 0; kt <= I / 2; ++kt) {
         const typename Op::F32 ba = Op::ld32_rmp(l, AQ, Cfg::LD_64, 16 * I, 32 * kt);
@@ -981,18 +983,17 @@ struct ChunkKernel {
         // wave 0 inverts the four diagonal blocks next to its own Y (one
         // scheduling region, so the inverse's VALU chain can fill the MFMA
         // gaps); the other waves only form Y before the barrier
-        typename Op::F32 SB[NKS][NVT];
-        f32x4 Y[4][NVT];
+        f32x4 Y[4][NVT], O[4][NVT];
         if (__builtin_amdgcn_readfirstlane(w) == 0) {
           invert_diag(smem);
-          scan_y(smem, S, SB, Y);
+          scan_y(smem, S, Y, O);
         } else {
-          scan_y(smem, S, SB, Y);
+          scan_y(smem, S, Y, O);
         }
         compiler_fence();
         load_raw<LOAD_V>(raw, offs, q, k, v, g, beta, next, H, h, nlen);
         __syncthreads();                                         // B3
-        scan_step(smem, S, SB, Y, out, row_base + c0, H, h, clen);
+        scan_step(smem, S, Y, O, out, row_base + c0, H, h, clen);
       } else {
         recurrent_chunk(S, q, k, v, g, beta, out, row_base + c0, H, h, clen, scale);
         load_raw<LOAD_Q | LOAD_K | LOAD_V>(raw, offs, q, k, v, g, beta, next, H, h, nlen);
