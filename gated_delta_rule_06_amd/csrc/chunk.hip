@@ -7,14 +7,16 @@
 // section 6.1/6.6 -- kept as a running product instead of exp of a prefix
 // sum), Gamma_L the decay over the whole chunk, and
 //
-//   QG_i = s q_i * Gamma_i          KG_i = beta_i k_i * Gamma_i
-//   KI_i = k_i / Gamma_i            BV_i = beta_i v_i
+//   QG_i = s q_i * Gamma_i          KG_i = k_i * Gamma_i
+//   KI_i = k_i / Gamma_i
 //
-// (products per key channel).  Then (section 6.3) R = strict_tril(KG KI^T)
-// holds rho_ij = beta_i <k_j, D_{j+1:i} k_i>, (section 6.5) Aqk = tril(QG KI^T)
-// holds chi_ij, the provisional errors of section 6.2 are Ebar = BV - KG S_c,
-// and the resolved errors are E = (I + R)^{-1} Ebar (the causal triangular
-// solve of section 6.3).  Finally (6.4, 6.5)
+// (products per key channel).  Then (section 6.3) R = Diag(beta)
+// strict_tril(KG KI^T) holds rho_ij = beta_i <k_j, D_{j+1:i} k_i>, (section
+// 6.5) Aqk = tril(QG KI^T) holds chi_ij, the provisional errors of section 6.2
+// are Ebar = Diag(beta) (V - KG S_c), and the resolved errors are
+// E = (I + R)^{-1} Ebar (the causal triangular solve of section 6.3).  beta
+// scales whole rows, so it is applied to the R tiles and to Y rather than to
+// the stored operands.  Finally (6.4, 6.5)
 //
 //   O_c     = QG S_c + Aqk E
 //   S_{c+1} = Diag(Gamma_L) (S_c + KI^T E)
@@ -36,7 +38,7 @@
 //  * the triangular solve runs by 16-token blocks: the four 16x16 diagonal
 //    blocks of I + R are inverted by forward substitution (S-independent, once
 //    per chunk), then X_I = T_II (Y_I - sum_{J<I} R_IJ X_J) on MFMA;
-//  * signs are folded into the stored operands (-BV, -KI, hence -R and -Aqk)
+//  * signs are folded into the stored operands (-V, -KI, hence -R and -Aqk)
 //    so that the solve yields -E directly and no extra negation is needed;
 //  * the next chunk's inputs are loaded into registers while this chunk is
 //    computed, in three batches spread over the phases.
@@ -350,7 +352,7 @@ struct ChunkCfg {
                 "layout");
   // LDS leading dimensions (elements)
   static constexpr int LD_K = DK + Op::PAD_RM;   // QG, KG, KIn [C][LD_K]
-  static constexpr int LD_V = DV + Op::PAD_TR;   // BV          [C][LD_V]
+  static constexpr int LD_V = DV + Op::PAD_TR;   // -V (buffer BV) [C][LD_V]
   static constexpr int LD_64 = C + Op::PAD_RM;   // RR, AQ [C][LD_64] (row-wise reads)
   static constexpr int SZ = sizeof(T);
   // LDS byte offsets.
@@ -373,12 +375,13 @@ struct ChunkCfg {
   static constexpr int OFF_SC = OFF_KT + DK * LD_KT * SZ;
   static constexpr int SZ_SC = (CQ == 2 && DK / NW == 16) ? NW * 16 * SC_LD * 4 : 0;
   static constexpr int OFF_GL = OFF_SC + SZ_SC;
-  static constexpr int OFF_FL = OFF_GL + DK * 4;
+  static constexpr int OFF_BT = OFF_GL + DK * 4;          // beta of the chunk's tokens
+  static constexpr int OFF_FL = OFF_BT + C * 4;
   static constexpr int LDS_TOTAL = OFF_FL + 64;
   static_assert(LDS_TOTAL <= 160 * 1024, "LDS budget");
   static_assert(OFF_KG % 16 == 0 && OFF_KI % 16 == 0 && OFF_RD % 16 == 0 && OFF_OS % 16 == 0 && OFF_FL % 16 == 0 &&
                 OFF_BV % 16 == 0 && OFF_AQ % 16 == 0 && OFF_RT % 16 == 0 && OFF_TD % 16 == 0 &&
-                OFF_GL % 16 == 0 && OFF_KT % 16 == 0 && OFF_SC % 16 == 0 && (LD_K * SZ) % 16 == 0 &&
+                OFF_GL % 16 == 0 && OFF_BT % 16 == 0 && OFF_KT % 16 == 0 && OFF_SC % 16 == 0 && (LD_K * SZ) % 16 == 0 &&
                 (LD_KT * SZ) % 16 == 0, "LDS alignment");
 };
 
@@ -478,6 +481,11 @@ struct ChunkKernel {
     LDS T* BV = (LDS T*)(smem + Cfg::OFF_BV);
     LDS T* KIT = (LDS T*)(smem + Cfg::OFF_KT);
     LDS float* GL = (LDS float*)(smem + Cfg::OFF_GL);
+    LDS float* BT = (LDS float*)(smem + Cfg::OFF_BT);
+
+    // beta is applied to R and Y later, where it scales whole rows (R =
+    // Diag(beta) strict_tril((k Gamma) KI^T), Ebar = Diag(beta)(v - (k Gamma) S))
+    if (w == 0) BT[l] = r.beta;                 // lane l holds beta of token l
 
     // in-lane running products of alpha over the lane's TPL tokens
     float cp[TPL][CPL];
@@ -548,39 +556,83 @@ struct ChunkKernel {
         *lds_ptr<f32x4>(GL + kc0 + 4) = f32x4{tot[4], tot[5], tot[6], tot[7]};
       }
     }
-    T kit[CPL][TPL];   // -KI of the lane's tokens, per key channel
+    // -KI of the lane's tokens per key channel, for the key-major copy
+    constexpr bool KIT_PAIRS = Cfg::SZ == 2 && TPL == 2;
+    T kit[CPL][TPL];
+    float kif[CPL][TPL];
 #pragma unroll
     for (int t = 0; t < TPL; ++t) {
       const int i = TPL * tg + t;
-      const float bt = __shfl(r.beta, i);
       float qv[CPL], kv[CPL];
       r.q[t].unpack(qv);
       r.k[t].unpack(kv);
-      T qg[CPL], kg[CPL], ki[CPL];
+      float qg[CPL], kg[CPL];
 #pragma unroll
       for (int c = 0; c < CPL; ++c) {
         const float gam = ex[c] * cp[t][c];
         const float inv = __builtin_amdgcn_rcpf(gam);
-        qg[c] = Op::cvt(scale * qv[c] * gam);
-        kg[c] = Op::cvt(bt * kv[c] * gam);
-        ki[c] = Op::cvt(-kv[c] * inv);          // -KI
-        kit[c][t] = ki[c];
+        qg[c] = scale * qv[c] * gam;
+        kg[c] = kv[c] * gam;                    // k Gamma (beta comes later)
+        kif[c][t] = -kv[c] * inv;               // -KI
+        kit[c][t] = Op::cvt(kif[c][t]);
       }
-      st_perm(QG + i * Cfg::LD_K, kc0, qg);
-      st_perm(KG + i * Cfg::LD_K, kc0, kg);
-      st_perm(KI + i * Cfg::LD_K, kc0, ki);
-      float vv[VPL];
-      r.v[t].unpack(vv);
-      T bv[VPL];
-#pragma unroll
-      for (int c = 0; c < VPL; ++c) bv[c] = Op::cvt(-bt * vv[c]);
-      st_chunk(BV + i * Cfg::LD_V + vc0, bv);
+      st_row8(QG + i * Cfg::LD_K, kc0, qg);
+      st_row8(KG + i * Cfg::LD_K, kc0, kg);
+      st_row8(KI + i * Cfg::LD_K, kc0, kif, t);
+      st_neg(BV + i * Cfg::LD_V + vc0, r.v[t]);     // -v, exactly: the sign bits flipped
     }
     // key-major copy KIT[channel][token]: the lane's TPL tokens are
     // consecutive (and stay so under the token permutation)
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) st_vec(KIT + (kc0 + c) * Cfg::LD_KT + Op::perm_pos(TPL * tg), kit[c]);
+    for (int c = 0; c < CPL; ++c) {
+      LDS T* p = KIT + (kc0 + c) * Cfg::LD_KT + Op::perm_pos(TPL * tg);
+      if (KIT_PAIRS)
+        *lds_ptr<uint32_t>(p) = pack_bf16x2(kif[c][0], kif[c][TPL - 1]);
+      else
+        st_vec(p, kit[c]);
+    }
     return bad;
+  }
+
+  // N raw input elements to LDS with their sign bits flipped (exact negation;
+  // the I/O type equals the operand type wherever this is used)
+  template <int N>
+  static __device__ __forceinline__ void st_neg(LDS T* p, const RawIo<Io, N>& x) {
+    static_assert(sizeof(typename Io::storage) == sizeof(T), "raw words are operand words");
+    constexpr int W = N * (int)sizeof(T) / 4;
+    constexpr uint32_t SIGN = sizeof(T) == 2 ? 0x80008000u : 0x80000000u;
+#pragma unroll
+    for (int i = 0; i < W; i += 4) {
+      if (W - i >= 4) {
+        *lds_ptr<u32x4>(p + i * 4 / (int)sizeof(T)) =
+            u32x4{x.w.word(i) ^ SIGN, x.w.word(i + 1) ^ SIGN, x.w.word(i + 2) ^ SIGN, x.w.word(i + 3) ^ SIGN};
+      } else if (W - i == 2) {
+        *lds_ptr<u32x2>(p + i * 4 / (int)sizeof(T)) = u32x2{x.w.word(i) ^ SIGN, x.w.word(i + 1) ^ SIGN};
+      } else {
+        *lds_ptr<uint32_t>(p + i * 4 / (int)sizeof(T)) = x.w.word(i) ^ SIGN;
+      }
+    }
+  }
+
+  // Channels c0 .. c0+7 of one row from floats: bf16 pairs packed straight
+  // into words (round to nearest even, as Op::cvt) and stored at their
+  // permuted positions; fp32 as they are.
+  static __device__ __forceinline__ void st_row8(LDS T* row, int c0, const float (&x)[8]) {
+    if (Op::PERMUTED) {
+      *lds_ptr<u32x2>(row + Op::perm_pos(c0)) = u32x2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+      *lds_ptr<u32x2>(row + Op::perm_pos(c0 + 4)) =
+          u32x2{pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7])};
+    } else {
+      T y[8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) y[c] = Op::cvt(x[c]);
+      st_chunk(row + c0, y);
+    }
+  }
+  template <int N>
+  static __device__ __forceinline__ void st_row8(LDS T* row, int c0, const float (&x)[8][N], int t) {
+    const float y[8] = {x[0][t], x[1][t], x[2][t], x[3][t], x[4][t], x[5][t], x[6][t], x[7][t]};
+    st_row8(row, c0, y);
   }
 
   // 8 consecutive channels c0 .. c0+7 of one row of a channel-permuted
@@ -631,8 +683,14 @@ struct ChunkKernel {
       accA = Op::mma32(b, aq, accA);
     }
     // accA[r] = -Aqk[16I + n][16J + g4 + r]; accR[r] = -R[16I + g4 + r][16I + n]
-    // on the diagonal, -R[16I + n][16J + g4 + r] off it
+    // on the diagonal, -R[16I + n][16J + g4 + r] off it, once the rows are
+    // scaled by beta (KG holds k Gamma)
     const int n = l & 15, g4 = 4 * (l >> 4);
+    const LDS float* BT = (const LDS float*)(smem + Cfg::OFF_BT);
+    if (I == J)
+      accR *= *lds_ptr<const f32x4>(BT + 16 * I + g4);
+    else
+      accR *= BT[16 * I + n];
     if (I == J) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -705,10 +763,10 @@ struct ChunkKernel {
   }
 
   // ---------------------------------------------------------------- phase S
-  // Y = -Ebar = KG S - BV; X = (I + R)^{-1} Y = -E by block forward
-  // substitution; O^T = S^T QG^T + (-E)^T (-Aqk)^T staged through LDS and
-  // written as whole token rows; S <- Diag(Gamma_L) (S + (-KI)^T (-E)).
-  // The parts that need no inverse: Y_I = KG_I S - BV_I and the S part of
+  // Y = -Ebar = Diag(beta) (KG S - V); X = (I + R)^{-1} Y = -E by block
+  // forward substitution; O^T = S^T QG^T + (-E)^T (-Aqk)^T staged through LDS
+  // and written as whole token rows; S <- Diag(Gamma_L) (S + (-KI)^T (-E)).
+  // The parts that need no inverse: Y_I = Diag(beta_I) (KG_I S - V_I) and the S part of
   // the outputs, O_I^T = S^T QG_I^T, for the four token blocks, with S as
   // 32-deep operands over key channels (lane: value column, k: channels).
   static __device__ __forceinline__ void scan_y(LDS char* smem, const f32x4 (&S)[MTK][NVT],
@@ -717,6 +775,7 @@ struct ChunkKernel {
     const LDS T* KG = (const LDS T*)(smem + Cfg::OFF_KG);
     const LDS T* QG = (const LDS T*)(smem + Cfg::OFF_QG);
     const LDS T* BV = (const LDS T*)(smem + Cfg::OFF_BV);
+    const LDS float* BT = (const LDS float*)(smem + Cfg::OFF_BT);
     typename Op::F32 SB[NKS][NVT];
     const int vw0 = w * VW;
 #pragma unroll
@@ -728,13 +787,17 @@ struct ChunkKernel {
     for (int I = 0; I < 4; ++I) {
 #pragma unroll
       for (int nt = 0; nt < NVT; ++nt)
-        Y[I][nt] = Op::unpack(Op::ld16_tr(l, BV, Cfg::LD_V, 16 * I, vw0 + 16 * nt));   // -BV
+        Y[I][nt] = Op::unpack(Op::ld16_tr(l, BV, Cfg::LD_V, 16 * I, vw0 + 16 * nt));   // -V
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
         const typename Op::F32 ak = Op::ld32_rmp(l, KG, Cfg::LD_K, 16 * I, 32 * ks);
 #pragma unroll
         for (int nt = 0; nt < NVT; ++nt) Y[I][nt] = Op::mma32(ak, SB[ks][nt], Y[I][nt]);
       }
+      // rows 16I + g4 + r scaled by beta: Y = Diag(beta)((k Gamma) S - v)
+      const f32x4 b = *lds_ptr<const f32x4>(BT + 16 * I + 4 * (l >> 4));
+#pragma unroll
+      for (int nt = 0; nt < NVT; ++nt) Y[I][nt] *= b;
 #pragma unroll
       for (int nt = 0; nt < NVT; ++nt) O[I][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
