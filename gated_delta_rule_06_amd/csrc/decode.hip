@@ -7,13 +7,16 @@
 //     o = S_t^T (s q) = s (Sbar^T q + (k^T q) e),
 // so each head's fp32 state crosses HBM exactly once in and once out.
 //
-// Mapping (gfx950, wave64): one 256-thread workgroup per (sequence, head).
-// Thread t owns 4 consecutive value columns (one float4) of RPT key rows
-// spaced RG apart, so every wave-wide load or store is one contiguous 1 KiB
-// (d_v = 128) run of the row-major state: fully coalesced.  The two column
-// reductions go through LDS once.  The state stream is marked non-temporal:
-// at 512 MiB it does not fit the last-level cache and is never re-read
-// within a step.
+// Mapping (gfx950, wave64): one 256-thread workgroup per (sequence, head,
+// 64-column slice of d_v) -- value columns are independent except for the
+// scalar k^T q, which each slice forms itself.  Thread t owns 4 consecutive
+// value columns (one float4) of RPT key rows spaced RG apart, so every
+// wave-wide load or store covers whole 256-byte runs of the row-major state.
+// Splitting the columns halves the state registers per thread (more waves in
+// flight per CU; it also narrowed the spread of launch times).  The two
+// column reductions go through LDS once.  The state stream is marked
+// non-temporal: at 512 MiB it does not fit the last-level cache and is never
+// re-read within a step.
 #include "common.h"
 
 namespace kda {
@@ -23,22 +26,25 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, float* __restrict__ S,
     void* __restrict__ out, float scale) {
-  constexpr int TPR = DV / 4;     // threads per state row
+  constexpr int CW = 64;          // value columns per workgroup
+  constexpr int NSPLIT = DV / CW;
+  constexpr int TPR = CW / 4;     // threads per state row
   constexpr int RG = 256 / TPR;   // row groups
   constexpr int RPT = DK / RG;    // rows per thread
-  static_assert(RPT >= 1 && RG * RPT == DK, "shape");
+  static_assert(DV % CW == 0 && RPT >= 1 && RG * RPT == DK, "shape");
 
-  const int head = blockIdx.x;    // n * H + h
+  const int head = blockIdx.x / NSPLIT;   // n * H + h
+  const int c0 = (blockIdx.x % NSPLIT) * CW;
   const int t = threadIdx.x;
   const int cg = t % TPR;
   const int rg = t / TPR;
 
   __shared__ __attribute__((aligned(16))) float s_k[DK], s_q[DK], s_a[DK];
-  __shared__ __attribute__((aligned(16))) float s_p[RG][DV], s_r[RG][DV];
-  __shared__ __attribute__((aligned(16))) float s_e[DV];
+  __shared__ __attribute__((aligned(16))) float s_p[RG][CW], s_r[RG][CW];
+  __shared__ __attribute__((aligned(16))) float s_e[CW];
   __shared__ float s_kq[4];
 
-  float* Sh = S + (size_t)head * DK * DV;
+  float* Sh = S + (size_t)head * DK * DV + c0;
   f32x4 st[RPT];
 #pragma unroll
   for (int m = 0; m < RPT; ++m)
@@ -74,7 +80,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
   *reinterpret_cast<f32x4*>(&s_r[rg][4 * cg]) = r;
   __syncthreads();
 
-  if (t < DV) {
+  if (t < CW) {
     float pt = 0.f, rt = 0.f;
 #pragma unroll
     for (int j = 0; j < RG; ++j) {
@@ -83,9 +89,9 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
     }
     const float kq = s_kq[0] + s_kq[1] + s_kq[2] + s_kq[3];
     const float b = beta[head];
-    const float e = b * (Io::load(v, (size_t)head * DV + t) - pt);
+    const float e = b * (Io::load(v, (size_t)head * DV + c0 + t) - pt);
     s_e[t] = e;
-    Io::store(out, (size_t)head * DV + t, scale * (rt + kq * e));
+    Io::store(out, (size_t)head * DV + c0 + t, scale * (rt + kq * e));
   }
   __syncthreads();
 
@@ -103,8 +109,8 @@ template <int DK, int DV, class Io>
 static hipError_t launch_decode_t(const void* q, const void* k, const void* v, const float* g,
                                   const float* beta, float* S, void* out, int NH, float scale,
                                   hipStream_t stream) {
-  hipLaunchKernelGGL((decode_step_kernel<DK, DV, Io>), dim3(NH), dim3(256), 0, stream, q, k, v, g,
-                     beta, S, out, scale);
+  hipLaunchKernelGGL((decode_step_kernel<DK, DV, Io>), dim3(NH * (DV / 64)), dim3(256), 0, stream,
+                     q, k, v, g, beta, S, out, scale);
   return hipGetLastError();
 }
 
