@@ -880,24 +880,6 @@ struct ChunkKernel {
 #pragma unroll
       for (int nt = 0; nt < NVT; ++nt) Op::st_ct(l, OST, Cfg::LD_OS, 16 * I, vw0 + 16 * nt, O[nt]);
     }
-    __syncthreads();
-    // copy the staged tile out: 16-byte pieces of whole token rows
-    {
-      constexpr int PIECE = 16 / Cfg::SZ;                 // elements per 16 bytes
-      constexpr int PER_ROW = DV / PIECE;
-      constexpr uint32_t E = sizeof(typename Io::storage);
-      const uint32_t srow = (uint32_t)H * DV * E;
-      const __amdgpu_buffer_rsrc_t ro =
-          make_rsrc((char*)out + (row_base * H + h) * DV * E, clen * srow);
-#pragma unroll
-      for (int p0 = 0; p0 < C * PER_ROW; p0 += Cfg::NTHREADS) {
-        const int p = p0 + threadIdx.x;
-        const int i = p / PER_ROW, c = (p % PER_ROW) * PIECE;
-        const u32x4 val = *lds_ptr<const u32x4>(OST + i * Cfg::LD_OS + c);
-        buf_store16(ro, i * srow + c * E, val);
-      }
-    }
-
     // (4) state update, S <- Diag(Gamma_L) (S + KI^T E), from -KI and -E.
     //     K_end = Diag(Gamma_L) KI row-wise, so this is Diag(Gamma_L) S +
     //     K_end^T E without forming K_end (section 6.4).
@@ -916,6 +898,27 @@ struct ChunkKernel {
         S[mt][nt] = s * gl;
       }
     }
+    // Once the staged tile is complete all of the chunk's LDS reads are done:
+    // after this barrier only the copy below reads LDS, and the next chunk's
+    // prep writes nothing it reads, so no barrier separates the two.
+    __syncthreads();
+    // copy the staged tile out: 16-byte pieces of whole token rows
+    {
+      constexpr int PIECE = 16 / Cfg::SZ;                 // elements per 16 bytes
+      constexpr int PER_ROW = DV / PIECE;
+      constexpr uint32_t E = sizeof(typename Io::storage);
+      const uint32_t srow = (uint32_t)H * DV * E;
+      const __amdgpu_buffer_rsrc_t ro =
+          make_rsrc((char*)out + (row_base * H + h) * DV * E, clen * srow);
+#pragma unroll
+      for (int p0 = 0; p0 < C * PER_ROW; p0 += Cfg::NTHREADS) {
+        const int p = p0 + threadIdx.x;
+        const int i = p / PER_ROW, c = (p % PER_ROW) * PIECE;
+        const u32x4 val = *lds_ptr<const u32x4>(OST + i * Cfg::LD_OS + c);
+        buf_store16(ro, i * srow + c * E, val);
+      }
+    }
+
   }
 
   // ---------------------------------------------------------------- guard path
@@ -1060,8 +1063,8 @@ struct ChunkKernel {
       } else {
         recurrent_chunk(S, q, k, v, g, beta, out, row_base + c0, H, h, clen, scale);
         load_raw<LOAD_Q | LOAD_K | LOAD_V>(raw, offs, q, k, v, g, beta, next, H, h, nlen);
+        __syncthreads();                                         // LDS reuse
       }
-      __syncthreads();                                           // LDS reuse
     }
     if (S_final) {
       const int l = lane_fresh();
