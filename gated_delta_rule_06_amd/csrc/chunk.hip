@@ -706,36 +706,14 @@ struct ChunkKernel {
         Op::pack(accA);
   }
 
-  // The 10 tile pairs over the waves: 3, 3, 2, 2 (four waves) or 2, 2, 1 x 6.
-  static __device__ __forceinline__ void phase_a(LDS char* smem) {
-    if (NW == 8) {
-      switch (threadIdx.x >> 6) {
-        case 0: tile_qk(smem, 0, 0); tile_qk(smem, 1, 1); break;
-        case 1: tile_qk(smem, 1, 0); tile_qk(smem, 2, 2); break;
-        case 2: tile_qk(smem, 2, 0); break;
-        case 3: tile_qk(smem, 2, 1); break;
-        case 4: tile_qk(smem, 3, 0); break;
-        case 5: tile_qk(smem, 3, 1); break;
-        case 6: tile_qk(smem, 3, 2); break;
-        default: tile_qk(smem, 3, 3); break;
-      }
-      return;
-    }
-    switch (threadIdx.x >> 6) {
-      case 0: tile_qk(smem, 0, 0); tile_qk(smem, 1, 0); tile_qk(smem, 1, 1); break;
-      case 1: tile_qk(smem, 2, 0); tile_qk(smem, 2, 1); tile_qk(smem, 2, 2); break;
-      case 2: tile_qk(smem, 3, 0); tile_qk(smem, 3, 1); break;
-      default: tile_qk(smem, 3, 2); tile_qk(smem, 3, 3); break;
-    }
-  }
-
   // ---------------------------------------------------------------- phase T
-  // T_II = (I + R_II)^{-1} for the four diagonal blocks at once, by column
-  // forward substitution: lane 16 I + col holds column col of block I.
-  // Written transposed (TD[I][col][i]).
+  // T_II = (I + R_II)^{-1} for diagonal block BLK, by column forward
+  // substitution: lane col (< 16) holds column col.  Written transposed
+  // (TD[BLK][col][i]).
+  template <int BLK>
   static __device__ __forceinline__ void invert_diag(LDS char* smem) {
     const int l = lane_fresh();
-    const int col = l & 15, blk = l >> 4;
+    const int col = l & 15, blk = BLK;
     const LDS float* RD = (const LDS float*)(smem + Cfg::OFF_RD) + blk * 16 * Cfg::RD_LD;
     LDS T* TD = (LDS T*)(smem + Cfg::OFF_TD) + blk * 256;
     float x[16];
@@ -755,10 +733,12 @@ struct ChunkKernel {
         }
       }
     }
+    if (l < 16) {
 #pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      f32x4 t = {x[4 * i4], x[4 * i4 + 1], x[4 * i4 + 2], x[4 * i4 + 3]};
-      *lds_ptr<typename Op::F16>(TD + col * 16 + 4 * i4) = Op::pack(t);
+      for (int i4 = 0; i4 < 4; ++i4) {
+        f32x4 t = {x[4 * i4], x[4 * i4 + 1], x[4 * i4 + 2], x[4 * i4 + 3]};
+        *lds_ptr<typename Op::F16>(TD + col * 16 + 4 * i4) = Op::pack(t);
+      }
     }
   }
 
@@ -1042,23 +1022,40 @@ struct ChunkKernel {
 #pragma unroll
       for (int i = 0; i < NW; ++i) any_bad |= FL[i];
       if (!any_bad) {
-        phase_a(smem);
+        load_raw<LOAD_V>(raw, offs, q, k, v, g, beta, next, H, h, nlen);
+        compiler_fence();
+        // one interval for the tiles, the inverses and the products that need
+        // no inverse: wave I < 4 forms diagonal tile (I, I) and inverts it
+        // itself (one wave's LDS accesses complete in order), waves 4-7 form
+        // the six off-diagonal pairs; each wave's case is one scheduling
+        // region, so VALU (inverse) and MFMA (tiles, Y, S^T QG^T) interleave
+        f32x4 Y[4][NVT], O[4][NVT];
+        if (NW == 8) {
+          switch (__builtin_amdgcn_readfirstlane(w)) {
+            case 0: tile_qk(smem, 0, 0); invert_diag<0>(smem); scan_y(smem, S, Y, O); break;
+            case 1: tile_qk(smem, 1, 1); invert_diag<1>(smem); scan_y(smem, S, Y, O); break;
+            case 2: tile_qk(smem, 2, 2); invert_diag<2>(smem); scan_y(smem, S, Y, O); break;
+            case 3: tile_qk(smem, 3, 3); invert_diag<3>(smem); scan_y(smem, S, Y, O); break;
+            case 4: tile_qk(smem, 1, 0); tile_qk(smem, 3, 2); scan_y(smem, S, Y, O); break;
+            case 5: tile_qk(smem, 2, 0); tile_qk(smem, 2, 1); scan_y(smem, S, Y, O); break;
+            case 6: tile_qk(smem, 3, 0); scan_y(smem, S, Y, O); break;
+            default: tile_qk(smem, 3, 1); scan_y(smem, S, Y, O); break;
+          }
+        } else {
+          switch (__builtin_amdgcn_readfirstlane(w)) {
+            case 0: tile_qk(smem, 0, 0); invert_diag<0>(smem); tile_qk(smem, 1, 0);
+                    tile_qk(smem, 2, 0); scan_y(smem, S, Y, O); break;
+            case 1: tile_qk(smem, 1, 1); invert_diag<1>(smem); tile_qk(smem, 2, 1);
+                    tile_qk(smem, 3, 0); scan_y(smem, S, Y, O); break;
+            case 2: tile_qk(smem, 2, 2); invert_diag<2>(smem); tile_qk(smem, 3, 1);
+                    scan_y(smem, S, Y, O); break;
+            default: tile_qk(smem, 3, 3); invert_diag<3>(smem); tile_qk(smem, 3, 2);
+                     scan_y(smem, S, Y, O); break;
+          }
+        }
         compiler_fence();
         load_raw<LOAD_Q | LOAD_K>(raw, offs, q, k, v, g, beta, next, H, h, nlen);
         __syncthreads();                                         // B2
-        // wave 0 inverts the four diagonal blocks next to its own Y (one
-        // scheduling region, so the inverse's VALU chain can fill the MFMA
-        // gaps); the other waves only form Y before the barrier
-        f32x4 Y[4][NVT], O[4][NVT];
-        if (__builtin_amdgcn_readfirstlane(w) == 0) {
-          invert_diag(smem);
-          scan_y(smem, S, Y, O);
-        } else {
-          scan_y(smem, S, Y, O);
-        }
-        compiler_fence();
-        load_raw<LOAD_V>(raw, offs, q, k, v, g, beta, next, H, h, nlen);
-        __syncthreads();                                         // B3
         scan_step(smem, S, Y, O, out, row_base + c0, H, h, clen);
       } else {
         recurrent_chunk(S, q, k, v, g, beta, out, row_base + c0, H, h, clen, scale);
