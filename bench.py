@@ -6,7 +6,9 @@ B=8, H=32, T=8192, d_k=d_v=128, bf16 q/k/v/o, fp32 gates and state, chunk 64,
 S0 = NULL (65,536 tokens), with inputs already resident in HBM.  `value` is
 prefill tokens/s (B*T per step).  The same run also measures the decode
 workload (256 sequences x 32 heads, fp32 state of 512 MiB, 128 chained
-kda_decode_step calls) and reports its steps/s.
+kda_decode_step calls) and reports its steps/s, and the multi-token decode
+workload (the same states, 256 sequences of U{1..8} new tokens, one
+kda_recurrent_fwd_varlen call updating them in place).
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 
@@ -32,6 +34,8 @@ BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA, published
 
 PREFILL = dict(B=8, T=8192, H=32, dk=128, dv=128, io="bf16", chunk=64)
 DECODE = dict(N=256, H=32, dk=128, dv=128, io="bf16", steps=128)
+# multi-token decode: 256 sequences of U{1..8} tokens (seed 0) on resident states
+RECURRENT = dict(n_seq=256, lo=1, hi=8, H=32, dk=128, dv=128, io="bf16", calls=20)
 
 
 def prefill_alg_bytes(B, T, H, dk, dv, io, with_S0=False, with_S_final=True):
@@ -76,6 +80,13 @@ def measured_traffic():
 def decode_alg_bytes(N, H, dk, dv, io):
     e = 2 if io == "bf16" else 4
     return N * H * (2 * dk * dv * 4 + e * (2 * dk + 2 * dv) + 4 * dk + 4)
+
+
+def recurrent_alg_bytes(tokens, n_seq, H, dk, dv, io):
+    """Every state read and written once, every token's inputs read and its
+    output written once."""
+    e = 2 if io == "bf16" else 4
+    return n_seq * H * dk * dv * 4 * 2 + tokens * H * ((2 * dk + 2 * dv) * e + dk * 4 + 4)
 
 
 def main():
@@ -194,6 +205,40 @@ def main():
     del dd, S
     torch.cuda.empty_cache()
 
+    # ---------------------------------------------------------------- multi-token decode
+    R = RECURRENT
+    lens = inputs.varlen_lengths(R["n_seq"], R["lo"], R["hi"], seed=0)
+    log("generating multi-token decode inputs", R, "tokens", int(lens.sum()))
+    dr = inputs.varlen_inputs(lens, R["H"], R["dk"], R["dv"], io=R["io"], seed=0, with_S0=True,
+                              device=dev)
+    Sr = dr["S0"]
+    o_rec = torch.empty((dr["T_total"], R["H"], R["dv"]), dtype=torch.bfloat16, device=dev)
+
+    def rec_call():
+        kda.recurrent_fwd_varlen(dr["q"], dr["k"], dr["v"], dr["g"], dr["beta"], dr["cu_seqlens"],
+                                 S0=Sr, S_final=Sr, out=o_rec)
+
+    for _ in range(5):
+        rec_call()
+    torch.cuda.synchronize()
+    evr = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(R["calls"])]
+    t0 = time.perf_counter()
+    for a, b in evr:
+        a.record(stream)
+        rec_call()
+        b.record(stream)
+    torch.cuda.synchronize()
+    rec_wall = (time.perf_counter() - t0) / R["calls"]
+    rec_ms = float(np.mean([a.elapsed_time(b) for a, b in evr]))
+    rec_b = recurrent_alg_bytes(int(lens.sum()), R["n_seq"], R["H"], R["dk"], R["dv"], R["io"])
+    rec_gbs = rec_b / (rec_ms * 1e-3) / 1e9
+    log("multi-token decode: %.2f us/call (wall), kernel %.2f us avg, %.0f GB/s"
+        % (rec_wall * 1e6, rec_ms * 1e3, rec_gbs))
+    rec_tokens = int(lens.sum())
+    del dr, Sr, o_rec
+    torch.cuda.empty_cache()
+
     # ---------------------------------------------------------------- CPU baseline
     cpu = None
     parity = None
@@ -262,6 +307,13 @@ def main():
                                 "unit": "GB/s", "frac": dec_gbs / HBM_PEAK_GBS,
                                 "alg_bytes_per_launch": dec_b,
                                 "avg_launch_ms": dec_kernel_ms}},
+        "recurrent": {"workload": "multi_token_decode_n256_h32_len1to8",
+                      "tokens_per_call": rec_tokens, "calls": R["calls"],
+                      "us_per_call": rec_wall * 1e6, "tokens_per_s": rec_tokens / rec_wall,
+                      "roofline": {"bound": "hbm", "achieved": rec_gbs, "peak": HBM_PEAK_GBS,
+                                   "unit": "GB/s", "frac": rec_gbs / HBM_PEAK_GBS,
+                                   "kernel": "recurrent_fwd_kernel<128,128,bf16>",
+                                   "alg_bytes_per_launch": rec_b, "avg_launch_ms": rec_ms}},
         "parity_sample": parity,
     }
     print(json.dumps(rec), flush=True)

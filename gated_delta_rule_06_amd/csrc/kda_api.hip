@@ -13,6 +13,10 @@ hipError_t launch_chunk(const void* q, const void* k, const void* v, const float
                         const int32_t* cu_seqlens, int n_seq, int T, int H, int dk, int dv,
                         float scale, bool bf16, hipStream_t stream);
 bool chunk_supported(int dk, int dv, bool bf16);
+hipError_t launch_recurrent(const void* q, const void* k, const void* v, const float* g,
+                            const float* beta, const float* S0, void* out, float* S_final,
+                            const int32_t* cu, int n_seq, int T, int H, int dk, int dv,
+                            float scale, bool bf16, hipStream_t stream);
 }  // namespace kda
 
 namespace {
@@ -43,16 +47,34 @@ __global__ void copy_state_kernel(const float* __restrict__ S0, float* __restric
 
 int launch_status(hipError_t e) { return e == hipSuccess ? KDA_OK : KDA_ERR_HIP; }
 
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool shape_ok(int d) { return d == 64 || d == 128; }
+
+// The vector loads and stores of every kernel assume 16-byte aligned arrays
+// (beta and cu_seqlens are read as single words).
+int check_align(const void* q, const void* k, const void* v, const float* log_alpha,
+                const float* beta, const float* S0, const void* out, const float* S_final,
+                const int32_t* cu) {
+  const void* a16[] = {q, k, v, log_alpha, S0, out, S_final};
+  for (const void* p : a16)
+    if (!aligned(p, 16)) return KDA_ERR_ALIGN;
+  if (!aligned(beta, 4) || !aligned(cu, 4)) return KDA_ERR_ALIGN;
+  return KDA_OK;
+}
+
 // Shared validation of the prefill entry points.  `rows` is the number of
 // token rows (B*T or T_total), `n_seq` the number of state slots.
-int check_prefill(const void* q, const void* k, const void* v, const float* log_alpha,
-                  const float* beta, const float* S0, void* out, float* S_final,
-                  const int32_t* cu, size_t rows, int n_seq, int H, int d_k, int d_v, int chunk,
-                  int io_dtype) {
-  if (!io_ok(io_dtype)) return KDA_ERR_UNSUPPORTED;
-  if (chunk != 64) return KDA_ERR_UNSUPPORTED;
-  if (!kda::chunk_supported(d_k, d_v, io_dtype == KDA_IO_BF16)) return KDA_ERR_UNSUPPORTED;
+// Shared validation of the calls over token sequences (prefill and
+// recurrent); `supported` is the caller's verdict on d_k, d_v, chunk, io_dtype.
+int check_tokens(const void* q, const void* k, const void* v, const float* log_alpha,
+                 const float* beta, const float* S0, void* out, float* S_final,
+                 const int32_t* cu, size_t rows, int n_seq, int H, int d_k, int d_v,
+                 bool supported, int io_dtype) {
+  if (!supported) return KDA_ERR_UNSUPPORTED;
   if (rows > 0 && (!q || !k || !v || !log_alpha || !beta || !out)) return KDA_ERR_NULL;
+  const int al = check_align(q, k, v, log_alpha, beta, S0, out, S_final, cu);
+  if (al != KDA_OK) return al;
   const size_t e = io_bytes(io_dtype);
   const size_t state = (size_t)n_seq * H * d_k * d_v * sizeof(float);
   const Range in[] = {span(q, rows * H * d_k * e), span(k, rows * H * d_k * e),
@@ -67,6 +89,25 @@ int check_prefill(const void* q, const void* k, const void* v, const float* log_
   if (overlap(ro, rs) || overlap(ro, r0)) return KDA_ERR_ALIAS;
   if (S_final && S0 && S0 != S_final && overlap(rs, r0)) return KDA_ERR_ALIAS;
   return KDA_OK;
+}
+
+int check_prefill(const void* q, const void* k, const void* v, const float* log_alpha,
+                  const float* beta, const float* S0, void* out, float* S_final,
+                  const int32_t* cu, size_t rows, int n_seq, int H, int d_k, int d_v, int chunk,
+                  int io_dtype) {
+  const bool ok = io_ok(io_dtype) && chunk == 64 &&
+                  kda::chunk_supported(d_k, d_v, io_dtype == KDA_IO_BF16);
+  return check_tokens(q, k, v, log_alpha, beta, S0, out, S_final, cu, rows, n_seq, H, d_k, d_v,
+                      ok, io_dtype);
+}
+
+int check_recurrent(const void* q, const void* k, const void* v, const float* log_alpha,
+                    const float* beta, const float* S0, void* out, float* S_final,
+                    const int32_t* cu, size_t rows, int n_seq, int H, int d_k, int d_v,
+                    int io_dtype) {
+  const bool ok = io_ok(io_dtype) && shape_ok(d_k) && shape_ok(d_v);
+  return check_tokens(q, k, v, log_alpha, beta, S0, out, S_final, cu, rows, n_seq, H, d_k, d_v,
+                      ok, io_dtype);
 }
 
 }  // namespace
@@ -84,6 +125,7 @@ const char* kda_status_string(int status) {
     case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE: workspace missing or too small";
     case KDA_ERR_HIP: return "KDA_ERR_HIP: a HIP launch failed";
     case KDA_ERR_ALIAS: return "KDA_ERR_ALIAS: an output overlaps an input";
+    case KDA_ERR_ALIGN: return "KDA_ERR_ALIGN: an array is not 16-byte aligned";
     default: return "unknown KDA status";
   }
 }
@@ -140,9 +182,11 @@ int kda_decode_step(const void* q, const void* k, const void* v, const float* lo
                     float scale, int io_dtype, void* stream) {
   if (N < 0 || H <= 0) return KDA_ERR_DIM;
   if (!io_ok(io_dtype)) return KDA_ERR_UNSUPPORTED;
-  if (!((d_k == 64 || d_k == 128) && (d_v == 64 || d_v == 128))) return KDA_ERR_UNSUPPORTED;
+  if (!(shape_ok(d_k) && shape_ok(d_v))) return KDA_ERR_UNSUPPORTED;
   if (N == 0) return KDA_OK;
   if (!q || !k || !v || !log_alpha || !beta || !S_inout || !out) return KDA_ERR_NULL;
+  const int al = check_align(q, k, v, log_alpha, beta, S_inout, out, nullptr, nullptr);
+  if (al != KDA_OK) return al;
   const size_t e = io_bytes(io_dtype);
   const size_t heads = (size_t)N * H;
   const Range in[] = {span(q, heads * d_k * e), span(k, heads * d_k * e), span(v, heads * d_v * e),
@@ -156,6 +200,38 @@ int kda_decode_step(const void* q, const void* k, const void* v, const float* lo
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   return launch_status(kda::launch_decode(q, k, v, log_alpha, beta, S_inout, out, (int)heads, d_k,
                                           d_v, scale, io_dtype == KDA_IO_BF16, s));
+}
+
+int kda_recurrent_fwd(const void* q, const void* k, const void* v, const float* log_alpha,
+                      const float* beta, const float* S0, void* out, float* S_final, int B, int T,
+                      int H, int d_k, int d_v, float scale, int io_dtype, void* stream) {
+  if (B < 0 || T < 0 || H <= 0) return KDA_ERR_DIM;
+  const size_t rows = (size_t)B * T;
+  if (rows > 0x7fffffffu) return KDA_ERR_DIM;   // token indices are 32-bit in the kernel
+  int st = check_recurrent(q, k, v, log_alpha, beta, S0, out, S_final, nullptr, rows, B, H, d_k,
+                           d_v, io_dtype);
+  if (st != KDA_OK) return st;
+  if (B == 0 || (T == 0 && (!S_final || S0 == S_final))) return KDA_OK;
+  // (T == 0 with a separate S_final: the kernel copies S0, or zeros, through)
+  return launch_status(kda::launch_recurrent(q, k, v, log_alpha, beta, S0, out, S_final, nullptr,
+                                             B, T, H, d_k, d_v, scale, io_dtype == KDA_IO_BF16,
+                                             reinterpret_cast<hipStream_t>(stream)));
+}
+
+int kda_recurrent_fwd_varlen(const void* q, const void* k, const void* v, const float* log_alpha,
+                             const float* beta, const float* S0, void* out, float* S_final,
+                             const int32_t* cu_seqlens, int N, int T_total, int H, int d_k,
+                             int d_v, float scale, int io_dtype, void* stream) {
+  if (N < 0 || T_total < 0 || H <= 0) return KDA_ERR_DIM;
+  if (!cu_seqlens) return KDA_ERR_NULL;
+  int st = check_recurrent(q, k, v, log_alpha, beta, S0, out, S_final, cu_seqlens,
+                           (size_t)T_total, N, H, d_k, d_v, io_dtype);
+  if (st != KDA_OK) return st;
+  if (N == 0) return KDA_OK;
+  return launch_status(kda::launch_recurrent(q, k, v, log_alpha, beta, S0, out, S_final,
+                                             cu_seqlens, N, T_total, H, d_k, d_v, scale,
+                                             io_dtype == KDA_IO_BF16,
+                                             reinterpret_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -32,7 +32,7 @@ __all__ = ["prefill_inputs", "varlen_lengths", "varlen_inputs", "decode_inputs",
 
 _IO = {"bf16": torch.bfloat16, "f32": torch.float32}
 
-# The five workloads the path is measured and checked on.
+# The workloads the path is measured and checked on.
 CONFIGS = {
     "single_head_f32": dict(B=1, T=256, H=1, dk=64, dv=64, io="f32", S0=False, chunk=64),
     "prefill_h16_s0": dict(B=1, T=4096, H=16, dk=128, dv=128, io="bf16", S0=True, chunk=64),
@@ -40,6 +40,8 @@ CONFIGS = {
     "decode_n256_h32": dict(N=256, H=32, dk=128, dv=128, io="bf16", steps=128),
     "varlen_16seq_h32": dict(n_seq=16, lo=1024, hi=65536, H=32, dk=128, dv=128, io="bf16",
                              long_channels=8, chunk=64),
+    # multi-token decode: 256 sequences of U{1..8} new tokens on resident states
+    "recurrent_n256_h32": dict(n_seq=256, lo=1, hi=8, H=32, dk=128, dv=128, io="bf16", S0=True),
 }
 
 

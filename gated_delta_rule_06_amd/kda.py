@@ -40,6 +40,11 @@ def _load():
                                          vp, sz, vp]
     lib.kda_decode_step.restype = i
     lib.kda_decode_step.argtypes = [vp, vp, vp, fp, fp, fp, vp, i, i, i, i, f, i, vp]
+    lib.kda_recurrent_fwd.restype = i
+    lib.kda_recurrent_fwd.argtypes = [vp, vp, vp, fp, fp, fp, vp, fp, i, i, i, i, i, f, i, vp]
+    lib.kda_recurrent_fwd_varlen.restype = i
+    lib.kda_recurrent_fwd_varlen.argtypes = [vp, vp, vp, fp, fp, fp, vp, fp, vp, i, i, i, i, i, f,
+                                             i, vp]
     lib.kda_chunk_fwd_workspace_size.restype = sz
     lib.kda_chunk_fwd_workspace_size.argtypes = [i] * 7
     lib.kda_chunk_fwd_varlen_workspace_size.restype = sz
@@ -181,3 +186,67 @@ def decode_step(q, k, v, log_alpha, beta, S_inout, scale=None, out=None):
     if st != 0:
         raise KdaError(st, "kda_decode_step")
     return out
+
+
+def recurrent_fwd(q, k, v, log_alpha, beta, S0=None, scale=None, out=None, S_final=None,
+                  output_final_state=True):
+    """Token-by-token recurrence for short sequences (multi-token decode,
+    speculative verification).  Shapes as chunk_fwd.  Pass S_final=S0 to
+    update a state in place.  Returns (o, S_final)."""
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    if scale is None:
+        scale = dk ** -0.5
+    for name, t, shp, dt in (("q", q, (B, T, H, dk), q.dtype), ("k", k, (B, T, H, dk), q.dtype),
+                             ("v", v, (B, T, H, dv), q.dtype),
+                             ("log_alpha", log_alpha, (B, T, H, dk), torch.float32),
+                             ("beta", beta, (B, T, H), torch.float32),
+                             ("S0", S0, (B, H, dk, dv), torch.float32)):
+        _check(t, name, shp, dt, dev)
+    io = _io_code(q.dtype)
+    if out is None:
+        out = torch.empty((B, T, H, dv), dtype=q.dtype, device=dev)
+    _check(out, "out", (B, T, H, dv), q.dtype, dev)
+    if S_final is None and output_final_state:
+        S_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    _check(S_final, "S_final", (B, H, dk, dv), torch.float32, dev)
+    st = lib.kda_recurrent_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S0),
+                               _ptr(out), _ptr(S_final), B, T, H, dk, dv, float(scale), io,
+                               _stream(dev))
+    if st != 0:
+        raise KdaError(st, "kda_recurrent_fwd")
+    return out, S_final
+
+
+def recurrent_fwd_varlen(q, k, v, log_alpha, beta, cu_seqlens, S0=None, scale=None, out=None,
+                         S_final=None, output_final_state=True):
+    """Token-by-token recurrence over packed sequences (varlen decode).
+    Shapes as chunk_fwd_varlen; S_final=S0 updates the states in place.
+    Returns (o, S_final)."""
+    Tt, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    N = cu_seqlens.shape[0] - 1
+    if scale is None:
+        scale = dk ** -0.5
+    for name, t, shp, dt in (("q", q, (Tt, H, dk), q.dtype), ("k", k, (Tt, H, dk), q.dtype),
+                             ("v", v, (Tt, H, dv), q.dtype),
+                             ("log_alpha", log_alpha, (Tt, H, dk), torch.float32),
+                             ("beta", beta, (Tt, H), torch.float32),
+                             ("cu_seqlens", cu_seqlens, (N + 1,), torch.int32),
+                             ("S0", S0, (N, H, dk, dv), torch.float32)):
+        _check(t, name, shp, dt, dev)
+    io = _io_code(q.dtype)
+    if out is None:
+        out = torch.empty((Tt, H, dv), dtype=q.dtype, device=dev)
+    _check(out, "out", (Tt, H, dv), q.dtype, dev)
+    if S_final is None and output_final_state:
+        S_final = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    _check(S_final, "S_final", (N, H, dk, dv), torch.float32, dev)
+    st = lib.kda_recurrent_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                                      _ptr(S0), _ptr(out), _ptr(S_final), _ptr(cu_seqlens), N, Tt,
+                                      H, dk, dv, float(scale), io, _stream(dev))
+    if st != 0:
+        raise KdaError(st, "kda_recurrent_fwd_varlen")
+    return out, S_final

@@ -17,7 +17,9 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  *  - Every pointer is a DEVICE pointer on the current HIP device, unless stated.
- *  - All arrays are dense, row-major, contiguous, with no padding.
+ *  - All arrays are dense, row-major, contiguous, with no padding.  Each
+ *    array starts on a 16-byte boundary (beta and cu_seqlens: 4 bytes), as
+ *    every device allocation does; otherwise KDA_ERR_ALIGN.
  *  - q, k, v, out use io_dtype (KDA_IO_F32 = float, KDA_IO_BF16 = bfloat16
  *    bit patterns); log_alpha, beta and every state are float (fp32).
  *  - The state is always fp32 and is kept fp32 on chip across a whole call.
@@ -30,8 +32,9 @@
  *    overlap between an output and another argument is not.
  *  - Supported sizes: d_k and d_v in {64, 128}; chunk == 64.  The two
  *    prefill calls take KDA_IO_F32 only with d_k == d_v == 64 (their fp32
- *    operand tiles do not fit in LDS otherwise); decode takes both types at
- *    every supported size.  Anything else returns KDA_ERR_UNSUPPORTED.
+ *    operand tiles do not fit in LDS otherwise); decode and the recurrent
+ *    calls take both types at every supported size.  Anything else returns
+ *    KDA_ERR_UNSUPPORTED.
  *  - Errors: every argument is validated before any work is enqueued; on a
  *    validation error nothing is enqueued and a negative KDA_ERR_* code is
  *    returned.  KDA_ERR_HIP reports a launch failure (hipGetLastError).
@@ -61,7 +64,8 @@ enum kda_status {
   KDA_ERR_UNSUPPORTED = -3, /* d_k, d_v, chunk or io_dtype not supported */
   KDA_ERR_WORKSPACE = -4,   /* workspace missing or smaller than required */
   KDA_ERR_HIP = -5,         /* a HIP launch failed */
-  KDA_ERR_ALIAS = -6        /* an output overlaps an input (other than S0 == S_final) */
+  KDA_ERR_ALIAS = -6,       /* an output overlaps an input (other than S0 == S_final) */
+  KDA_ERR_ALIGN = -7        /* an array is not aligned (16 bytes; beta and cu_seqlens 4) */
 };
 
 /*
@@ -133,6 +137,42 @@ int kda_chunk_fwd_varlen(const void* q, const void* k, const void* v, const floa
 int kda_decode_step(const void* q, const void* k, const void* v, const float* log_alpha,
                     const float* beta, float* S_inout, void* out, int N, int H, int d_k, int d_v,
                     float scale, int io_dtype, void* stream);
+
+/*
+ * kda_recurrent_fwd -- the recurrence itself, token by token, for B sequences
+ * of T tokens each: multi-token decode, speculative verification, short
+ * prefill ("Kimi Unveils Delta Attention and K3 Architecture Updates",
+ * section 5, the fused recurrent kernel, which suits short sequences and
+ * stateful serving).  Each head's fp32 state is read once from S0 and written
+ * once to S_final whatever T is; the serial work grows with T, so for long
+ * sequences kda_chunk_fwd is the faster schedule of the same result.
+ *
+ *  q, k       [B, T, H, d_k]  io_dtype
+ *  v, out     [B, T, H, d_v]  io_dtype
+ *  log_alpha  [B, T, H, d_k]  fp32
+ *  beta       [B, T, H]       fp32
+ *  S0         [B, H, d_k, d_v] fp32 or NULL (zeros)
+ *  S_final    [B, H, d_k, d_v] fp32 or NULL; S_final == S0 updates the state
+ *             in place (the usual serving call)
+ *  d_k, d_v in {64, 128}; both io_dtype values for every shape.
+ * Returns KDA_OK or a KDA_ERR_* code.
+ */
+int kda_recurrent_fwd(const void* q, const void* k, const void* v, const float* log_alpha,
+                      const float* beta, const float* S0, void* out, float* S_final, int B, int T,
+                      int H, int d_k, int d_v, float scale, int io_dtype, void* stream);
+
+/*
+ * kda_recurrent_fwd_varlen -- kda_recurrent_fwd over N packed sequences of
+ * any lengths (zero included): sequence n owns tokens [cu_seqlens[n],
+ * cu_seqlens[n+1]) and state slot n ("Linear Attention, From Scratch to Kimi
+ * 3", section 9, cu_seqlens).  Layouts and cu_seqlens preconditions as for
+ * kda_chunk_fwd_varlen; S0 == S_final allowed.
+ * Returns KDA_OK or a KDA_ERR_* code.
+ */
+int kda_recurrent_fwd_varlen(const void* q, const void* k, const void* v, const float* log_alpha,
+                             const float* beta, const float* S0, void* out, float* S_final,
+                             const int32_t* cu_seqlens, int N, int T_total, int H, int d_k,
+                             int d_v, float scale, int io_dtype, void* stream);
 
 /* Workspace bytes kda_chunk_fwd needs for these sizes (0 if none; the
  * arguments are not validated here: unsupported sizes give 0). */

@@ -29,6 +29,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for want in ("kda_chunk_fwd", "kda_chunk_fwd_varlen", "kda_decode_step",
+                 "kda_recurrent_fwd", "kda_recurrent_fwd_varlen",
                  "kda_chunk_fwd_workspace_size", "kda_chunk_fwd_varlen_workspace_size",
                  "kda_status_string", "kda_version"):
         assert want in names
@@ -42,7 +43,7 @@ def test_library_exports_every_declared_symbol(lib):
 def test_status_strings_and_version(lib):
     from gated_delta_rule_06_amd import kda
     assert kda.status_string(0) == "KDA_OK"
-    for code in range(-1, -7, -1):
+    for code in range(-1, -8, -1):
         assert kda.status_string(code).startswith("KDA_ERR_")
     assert "unknown" in kda.status_string(-99)
     assert lib.kda_version() >= 100
@@ -106,6 +107,53 @@ def test_decode_validation(lib):
     assert f(*args(io=3)) == -3
     assert f(*args(out=P[5])) == -6                       # out overlaps the state
     assert f(*args(N=0)) == 0
+
+
+def test_recurrent_validation(lib):
+    f = lib.kda_recurrent_fwd
+    args = lambda **kw: (kw.get("q", P[0]), P[1], P[2], P[3], kw.get("beta", P[4]),
+                         kw.get("S0", None), kw.get("out", P[5]), kw.get("Sf", P[6]),
+                         kw.get("B", 2), kw.get("T", 4), kw.get("H", 2), kw.get("dk", 128),
+                         kw.get("dv", 128), 0.1, kw.get("io", 1), None)
+    assert f(*args(q=None)) == -1
+    assert f(*args(B=-1)) == -2
+    assert f(*args(T=-1)) == -2
+    assert f(*args(H=0)) == -2
+    assert f(*args(B=1 << 16, T=1 << 16)) == -2            # more tokens than 32-bit indices
+    assert f(*args(dk=32)) == -3
+    assert f(*args(dv=96)) == -3
+    assert f(*args(io=2)) == -3
+    assert f(*args(out=P[2])) == -6                         # out == v
+    assert f(*args(Sf=P[3])) == -6                          # S_final == log_alpha
+    assert f(*args(B=0)) == 0
+    assert f(*args(T=0, Sf=None)) == 0                      # nothing to write
+    assert f(*args(T=0, S0=P[6])) == 0                      # in place, no tokens: a no-op
+    g = lib.kda_recurrent_fwd_varlen
+    vargs = lambda **kw: (P[0], P[1], P[2], P[3], P[4], None, kw.get("out", P[5]), P[6],
+                          kw.get("cu", P[7]), kw.get("N", 3), kw.get("Tt", 10), 2, 64,
+                          kw.get("dv", 64), 0.1, 0, None)
+    assert g(*vargs(cu=None)) == -1
+    assert g(*vargs(N=-1)) == -2
+    assert g(*vargs(Tt=-2)) == -2
+    assert g(*vargs(dv=32)) == -3
+    assert g(*vargs(out=P[0])) == -6
+    assert g(*vargs(N=0)) == 0
+
+
+def test_alignment_validation(lib):
+    odd = lambda p, n: ctypes.c_void_p(p.value + n)
+    assert chunk(lib, q=odd(P[0], 2)) == -7                 # KDA_ERR_ALIGN
+    assert chunk(lib, g=odd(P[3], 8)) == -7
+    assert chunk(lib, Sf=odd(P[6], 4)) == -7
+    assert chunk(lib, beta=odd(P[4], 2)) == -7              # beta needs 4 bytes
+    f = lib.kda_decode_step
+    assert f(odd(P[0], 2), P[1], P[2], P[3], P[4], P[5], P[6], 4, 2, 128, 128, 0.1, 1, None) == -7
+    assert f(P[0], P[1], P[2], P[3], odd(P[4], 2), P[5], P[6], 4, 2, 128, 128, 0.1, 1, None) == -7
+    r = lib.kda_recurrent_fwd
+    assert r(P[0], P[1], odd(P[2], 8), P[3], P[4], None, P[5], P[6], 2, 4, 2, 128, 128, 0.1, 1,
+             None) == -7
+    from gated_delta_rule_06_amd import kda
+    assert kda.status_string(-7).startswith("KDA_ERR_ALIGN")
 
 
 def test_product_path_has_no_oracle_or_cpu_fallback():
