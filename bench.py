@@ -53,26 +53,27 @@ def prefill_alg_flops(B, T, H, dk, dv, C=64):
 
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-TRAFFIC_FILE = os.path.join(HERE, "profiles", "chunk_fwd_128x128_b8_h32_t8192_traffic.md")
-CHUNK_SRC = os.path.join(HERE, "gated_delta_rule_06_amd", "csrc", "chunk.hip")
+TRAFFIC_FILE = os.path.join(HERE, "profiles",
+                            "traffic_chunk_b8_h32_t8192_decode_n256_h32_recurrent_n256_h32.md")
+CSRC = os.path.join(HERE, "gated_delta_rule_06_amd", "csrc")
 
 
-def measured_traffic():
-    """HBM bytes per launch of the prefill kernel from the committed counter
-    summary (FETCH_SIZE + WRITE_SIZE, calibrated on a plain copy), or None when
-    the kernel source has changed since the counters were taken."""
+def measured_traffic(kernel="chunk", source="chunk.hip"):
+    """HBM bytes per launch of one kernel from the committed counter summary
+    (FETCH_SIZE + WRITE_SIZE, calibrated on a plain copy), or None when the
+    kernel's source has changed since the counters were taken."""
     import hashlib
     try:
         txt = open(TRAFFIC_FILE).read()
-        src = hashlib.sha256(open(CHUNK_SRC, "rb").read()).hexdigest()
+        src = hashlib.sha256(open(os.path.join(CSRC, source), "rb").read()).hexdigest()
     except OSError:
         return None
     fields = dict(l.split(":", 1) for l in txt.splitlines() if ":" in l and not l.startswith("#"))
     fields = {k.strip("- `*").strip(): v.strip().strip("`") for k, v in fields.items()}
-    if fields.get("source_sha256") != src:
+    if fields.get("%s_source_sha256" % kernel) != src:
         return None
     try:
-        return float(fields["traffic_bytes_per_launch"])
+        return float(fields["%s_traffic_bytes_per_launch" % kernel])
     except (KeyError, ValueError):
         return None
 
@@ -295,7 +296,7 @@ def main():
                    "d_k": P["dk"], "d_v": P["dv"], "chunk": P["chunk"], "io": "bf16",
                    "state": "fp32", "S0": None},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(),
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic("chunk", "chunk.hip"),
                      "kernel": "chunk_fwd_kernel<128,128,bf16>",
                      "alg_bytes_per_launch": alg_b, "avg_launch_ms": avg_kernel_ms,
                      "alg_tflops": alg_f / (avg_kernel_ms * 1e-3) / 1e12,
@@ -305,6 +306,7 @@ def main():
                    "tokens_per_s": dec_steps_s * D["N"], "ms_per_step": 1e3 / dec_steps_s,
                    "roofline": {"bound": "hbm", "achieved": dec_gbs, "peak": HBM_PEAK_GBS,
                                 "unit": "GB/s", "frac": dec_gbs / HBM_PEAK_GBS,
+                                "traffic": measured_traffic("decode", "decode.hip"),
                                 "alg_bytes_per_launch": dec_b,
                                 "avg_launch_ms": dec_kernel_ms}},
         "recurrent": {"workload": "multi_token_decode_n256_h32_len1to8",
@@ -312,6 +314,7 @@ def main():
                       "us_per_call": rec_wall * 1e6, "tokens_per_s": rec_tokens / rec_wall,
                       "roofline": {"bound": "hbm", "achieved": rec_gbs, "peak": HBM_PEAK_GBS,
                                    "unit": "GB/s", "frac": rec_gbs / HBM_PEAK_GBS,
+                                   "traffic": measured_traffic("recurrent", "recurrent.hip"),
                                    "kernel": "recurrent_fwd_kernel<128,128,bf16>",
                                    "alg_bytes_per_launch": rec_b, "avg_launch_ms": rec_ms}},
         "parity_sample": parity,

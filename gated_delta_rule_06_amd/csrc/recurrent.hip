@@ -2,8 +2,10 @@
 // sequence (multi-token decode, speculative verification, short prefill).
 //
 // The recurrence itself ("Kimi Unveils Delta Attention and K3 Architecture
-// Updates", section 5, the fused recurrent kernel; "Linear Attention, From
-// Scratch to Kimi 3", section 4), token by token on a state that stays in
+// Updates", section 5, the fused recurrent kernel, whose regime is decode,
+// short sequences and stateful serving; "Linear Attention, From Scratch to
+// Kimi 3", section 6 for the recurrence and section 9, where the fused kernel
+// loops over several tokens), token by token on a state that stays in
 // registers from the sequence's first token to its last:
 //     Sbar = Diag(exp(g_t)) S,  e = beta_t (v_t - Sbar^T k_t),
 //     S <- Sbar + k_t e^T,      o_t = scale (Sbar^T q_t + (k_t^T q_t) e)

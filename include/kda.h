@@ -143,7 +143,9 @@ int kda_decode_step(const void* q, const void* k, const void* v, const float* lo
  * of T tokens each: multi-token decode, speculative verification, short
  * prefill ("Kimi Unveils Delta Attention and K3 Architecture Updates",
  * section 5, the fused recurrent kernel, which suits short sequences and
- * stateful serving).  Each head's fp32 state is read once from S0 and written
+ * stateful serving; "Linear Attention, From Scratch to Kimi 3", section 9: the
+ * fused kernel can loop over several tokens).  Each head's fp32 state is read
+ * once from S0 and written
  * once to S_final whatever T is; the serial work grows with T, so for long
  * sequences kda_chunk_fwd is the faster schedule of the same result.
  *
