@@ -8,7 +8,9 @@ prefill tokens/s (B*T per step).  The same run also measures the decode
 workload (256 sequences x 32 heads, fp32 state of 512 MiB, 128 chained
 kda_decode_step calls) and reports its steps/s, and the multi-token decode
 workload (the same states, 256 sequences of U{1..8} new tokens, one
-kda_recurrent_fwd_varlen call updating them in place).
+kda_recurrent_fwd_varlen call updating them in place) and the Gated DeltaNet
+prefill (the headline shapes with one gate per token and head,
+kda_gdn_chunk_fwd).
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 
@@ -38,11 +40,12 @@ DECODE = dict(N=256, H=32, dk=128, dv=128, io="bf16", steps=128)
 RECURRENT = dict(n_seq=256, lo=1, hi=8, H=32, dk=128, dv=128, io="bf16", calls=20)
 
 
-def prefill_alg_bytes(B, T, H, dk, dv, io, with_S0=False, with_S_final=True):
+def prefill_alg_bytes(B, T, H, dk, dv, io, with_S0=False, with_S_final=True, gate_dims=None):
     """Inputs read once and outputs written once: q, k (dk), v, o (dv) in the
-    I/O type, log_alpha (dk) and beta in fp32, plus the fp32 states."""
+    I/O type, log_alpha (dk per token and head, or 1 for Gated DeltaNet) and
+    beta in fp32, plus the fp32 states."""
     e = 2 if io == "bf16" else 4
-    per_ht = e * (2 * dk + 2 * dv) + 4 * dk + 4
+    per_ht = e * (2 * dk + 2 * dv) + 4 * (dk if gate_dims is None else gate_dims) + 4
     states = B * H * dk * dv * 4 * (int(with_S0) + int(with_S_final))
     return B * T * H * per_ht + states
 
@@ -164,10 +167,38 @@ def main():
     log("prefill: %.3f ms/step (wall), kernel %.3f ms avg (min %.3f), %.3e tokens/s, %.0f GB/s"
         % (ms_per_step, avg_kernel_ms, min(kern_ms), value, achieved))
 
-    # ---------------------------------------------------------------- decode
-    D = DECODE
+    # ---------------------------------------------------------------- Gated DeltaNet prefill
     del d
     torch.cuda.empty_cache()
+    log("generating Gated DeltaNet prefill inputs (one gate per token and head)")
+    dg = inputs.prefill_inputs(P["B"], P["T"], P["H"], P["dk"], P["dv"], io=P["io"], seed=0,
+                               with_S0=False, device=dev, gate="gdn")
+
+    def gdn_step():
+        kda.chunk_fwd(dg["q"], dg["k"], dg["v"], dg["g"], dg["beta"], S0=None, out=out, S_final=Sf)
+
+    for _ in range(args.warmup):
+        gdn_step()
+    torch.cuda.synchronize()
+    evg = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for a, b in evg:
+        a.record(stream)
+        gdn_step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    gdn_wall = (time.perf_counter() - t0) / args.steps
+    gdn_ms = float(np.mean([a.elapsed_time(b) for a, b in evg]))
+    gdn_b = prefill_alg_bytes(P["B"], P["T"], P["H"], P["dk"], P["dv"], P["io"], gate_dims=1)
+    gdn_gbs = gdn_b / (gdn_ms * 1e-3) / 1e9
+    log("gdn prefill: %.3f ms/step (wall), kernel %.3f ms avg, %.3e tokens/s, %.0f GB/s"
+        % (gdn_wall * 1e3, gdn_ms, tokens / gdn_wall, gdn_gbs))
+    del dg
+    torch.cuda.empty_cache()
+
+    # ---------------------------------------------------------------- decode
+    D = DECODE
     log("generating decode inputs", D)
     dd = inputs.decode_inputs(D["N"], D["H"], D["dk"], D["dv"], D["steps"], io=D["io"], seed=0,
                               device=dev)
@@ -309,6 +340,12 @@ def main():
                                 "traffic": measured_traffic("decode", "decode.hip"),
                                 "alg_bytes_per_launch": dec_b,
                                 "avg_launch_ms": dec_kernel_ms}},
+        "gdn_prefill": {"workload": "gated_deltanet_prefill_b8_h32_t8192",
+                        "tokens_per_s": tokens / gdn_wall, "ms_per_step": gdn_wall * 1e3,
+                        "roofline": {"bound": "hbm", "achieved": gdn_gbs, "peak": HBM_PEAK_GBS,
+                                     "unit": "GB/s", "frac": gdn_gbs / HBM_PEAK_GBS,
+                                     "kernel": "chunk_fwd_kernel<128,128,bf16,scalar gate>",
+                                     "alg_bytes_per_launch": gdn_b, "avg_launch_ms": gdn_ms}},
         "recurrent": {"workload": "multi_token_decode_n256_h32_len1to8",
                       "tokens_per_call": rec_tokens, "calls": R["calls"],
                       "us_per_call": rec_wall * 1e6, "tokens_per_s": rec_tokens / rec_wall,

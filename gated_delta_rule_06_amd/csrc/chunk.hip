@@ -328,9 +328,12 @@ struct RawIo {
 // ============================================================ configuration
 // Four waves per workgroup; wave w owns value columns [w d_v/4, (w+1) d_v/4)
 // of the state for the whole sequence.
-template <int DK_, int DV_, class Io_, class Op_, int NW_ = 4>
+template <int DK_, int DV_, class Io_, class Op_, int NW_ = 4, bool SG_ = false>
 struct ChunkCfg {
   static constexpr int DK = DK_, DV = DV_;
+  // SG: one gate per (token, head) shared by every key channel (Gated
+  // DeltaNet); otherwise one per key channel (KDA)
+  static constexpr bool SG = SG_;
   typedef Io_ Io;
   typedef Op_ Op;
   typedef typename Op::T T;
@@ -400,7 +403,8 @@ struct ChunkKernel {
   static constexpr int NKS = Cfg::NKS, MTK = Cfg::MTK, NWT = Cfg::NWT, NVT = Cfg::NVT;
 
   struct Raw {
-    RawWords<CPL * 4> g[TPL];
+    RawWords<CPL * 4> g[TPL];   // per-channel gates (KDA)
+    float gs[TPL];              // the per-token gate (Gated DeltaNet)
     RawIo<Io, CPL> q[TPL], k[TPL];
     RawIo<Io, VPL> v[TPL];
     float beta;
@@ -434,10 +438,10 @@ struct ChunkKernel {
     constexpr uint32_t E = sizeof(typename Io::storage);
     Offsets o;
     o.sqk = (uint32_t)H * DK * E;
-    o.sg = (uint32_t)H * DK * 4;
+    o.sg = (uint32_t)H * (Cfg::SG ? 1 : DK) * 4;
     o.sv = (uint32_t)H * DV * E;
     o.qk = (uint32_t)(TPL * tg) * o.sqk + kc0 * E;
-    o.g = (uint32_t)(TPL * tg) * o.sg + kc0 * 4;
+    o.g = (uint32_t)(TPL * tg) * o.sg + (Cfg::SG ? 0 : kc0 * 4);
     o.v = (uint32_t)(TPL * tg) * o.sv + vc0 * E;
     o.beta = (uint32_t)l * H * 4;
     return o;
@@ -454,7 +458,8 @@ struct ChunkKernel {
     const __amdgpu_buffer_rsrc_t rq = make_rsrc((const char*)q + e0 * DK * E, clen * o.sqk);
     const __amdgpu_buffer_rsrc_t rk = make_rsrc((const char*)k + e0 * DK * E, clen * o.sqk);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc((const char*)v + e0 * DV * E, clen * o.sv);
-    const __amdgpu_buffer_rsrc_t rg = make_rsrc((const char*)g + e0 * DK * 4, clen * o.sg);
+    const __amdgpu_buffer_rsrc_t rg =
+        make_rsrc((const char*)g + e0 * (Cfg::SG ? 1 : DK) * 4, clen * o.sg);
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(beta + e0, (uint32_t)clen * H * 4);
     // lane part in the VGPR offset, the token step in the scalar offset
 #pragma unroll
@@ -462,7 +467,12 @@ struct ChunkKernel {
       if (PART & LOAD_Q) r.q[t].w.load(rq, o.qk, t * o.sqk);
       if (PART & LOAD_K) r.k[t].w.load(rk, o.qk, t * o.sqk);
       if (PART & LOAD_V) r.v[t].w.load(rv, o.v, t * o.sv);
-      if (PART & LOAD_G) r.g[t].load(rg, o.g, t * o.sg);
+      if (PART & LOAD_G) {
+        if (Cfg::SG)
+          r.gs[t] = buf_load<float>(rg, o.g, t * o.sg);
+        else
+          r.g[t].load(rg, o.g, t * o.sg);
+      }
     }
     if (PART & LOAD_V) r.beta = buf_load<float>(rb, o.beta);   // lane l: beta of token l
   }
@@ -487,73 +497,104 @@ struct ChunkKernel {
     // Diag(beta) strict_tril((k Gamma) KI^T), Ebar = Diag(beta)(v - (k Gamma) S))
     if (w == 0) BT[l] = r.beta;                 // lane l holds beta of token l
 
-    // in-lane running products of alpha over the lane's TPL tokens
-    float cp[TPL][CPL];
-#pragma unroll
-    for (int t = 0; t < TPL; ++t)
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) {
-        const float a = __expf(__uint_as_float(r.g[t].word(c)));
-        cp[t][c] = (t == 0) ? a : cp[t - 1][c] * a;
-      }
-    // product over the TG token groups: ex = exclusive prefix, Gamma_L -> GL
-    float ex[CPL];
+    float cp[TPL][CPL];   // in-lane running products of alpha over the lane's tokens
+    float ex[CPL];        // product over the earlier token groups (exclusive prefix)
     int bad = 0;
-    if (Cfg::SZ_SC > 0) {
-      // Two lanes per token group (lane = 2 tg + cq, 16 channels per wave).
-      // The group totals go through a wave-private LDS block, transposed to
-      // X[channel][group]; there lane 4 ch + qq takes groups 8 qq .. 8 qq + 7
-      // of channel ch: a running product over its eight groups, then an
-      // exclusive product scan over the four lanes of the quad (DPP quad
-      // permutations; the first lane of each quad holds 1, so lanes that
-      // read it are unaffected).  A wave's LDS accesses complete in order.
-      LDS float* X = (LDS float*)(smem + Cfg::OFF_SC) + w * 16 * Cfg::SC_LD;
+    if constexpr (Cfg::SG) {
+      // One gate per token: the same running product serves every channel.
+      // Inclusive scan of the group totals over lanes cq + CQ tg, shifted by
+      // one group; Gamma_L is the last group's inclusive product.
+      float ct[TPL];
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) X[(8 * cq + c) * Cfg::SC_LD + tg] = cp[TPL - 1][c];
-      __asm__ __volatile__("" ::: "memory");
-      const int ch = l >> 2, qq = l & 3;
-      LDS float* xr = X + ch * Cfg::SC_LD + 8 * qq;
-      const f32x4 v0 = *lds_ptr<const f32x4>(xr), v1 = *lds_ptr<const f32x4>(xr + 4);
-      const float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-      float e[8];
-      e[0] = 1.f;
-#pragma unroll
-      for (int m = 1; m < 8; ++m) e[m] = e[m - 1] * v[m - 1];
-      const float tq = e[7] * v[7];                       // this quarter's product
-      float z = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(tq), 0x90, 0xf, 0xf, false));
-      z = (qq == 0) ? 1.f : z;                            // quad_perm [0,0,1,2]: the previous lane
-      z *= __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(z), 0x90, 0xf, 0xf, false));
-      z *= __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(z), 0x40, 0xf, 0xf, false));
-      *lds_ptr<f32x4>(xr) = f32x4{z * e[0], z * e[1], z * e[2], z * e[3]};
-      *lds_ptr<f32x4>(xr + 4) = f32x4{z * e[4], z * e[5], z * e[6], z * e[7]};
-      if (qq == 3) {
-        const float gl = z * tq;                          // Gamma_L of channel ch
-        GL[w * 16 + ch] = gl;
-        bad = !(gl >= KDA_GAMMA_MIN);
+      for (int t = 0; t < TPL; ++t) {
+        const float a = __expf(r.gs[t]);
+        ct[t] = (t == 0) ? a : ct[t - 1] * a;
       }
-      __asm__ __volatile__("" ::: "memory");
+      float x = ct[TPL - 1];
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) ex[c] = X[(8 * cq + c) * Cfg::SC_LD + tg];
-    } else {
-      // inclusive scan over the lanes cq + CQ tg, then shift by one group
-      float tot[CPL];
+      for (int d = CQ; d < 64; d <<= 1) {
+        const float y = __shfl_up(x, d);
+        if (l >= d) x *= y;
+      }
+      const float gl = __shfl(x, 63);
+      const float y = __shfl_up(x, CQ);
+      const float e0 = (l >= CQ) ? y : 1.f;
+      bad = !(gl >= KDA_GAMMA_MIN);
 #pragma unroll
       for (int c = 0; c < CPL; ++c) {
-        float x = cp[TPL - 1][c];
+        ex[c] = e0;
 #pragma unroll
-        for (int d = CQ; d < 64; d <<= 1) {
-          const float y = __shfl_up(x, d);
-          if (l >= d) x *= y;
-        }
-        tot[c] = __shfl(x, 64 - CQ + cq);     // Gamma_L
-        const float y = __shfl_up(x, CQ);
-        ex[c] = (l >= CQ) ? y : 1.f;
+        for (int t = 0; t < TPL; ++t) cp[t][c] = ct[t];
       }
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) bad |= !(tot[c] >= KDA_GAMMA_MIN);
       if (tg == 0) {
-        *lds_ptr<f32x4>(GL + kc0) = f32x4{tot[0], tot[1], tot[2], tot[3]};
-        *lds_ptr<f32x4>(GL + kc0 + 4) = f32x4{tot[4], tot[5], tot[6], tot[7]};
+        *lds_ptr<f32x4>(GL + kc0) = f32x4{gl, gl, gl, gl};
+        *lds_ptr<f32x4>(GL + kc0 + 4) = f32x4{gl, gl, gl, gl};
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < TPL; ++t)
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+          const float a = __expf(__uint_as_float(r.g[t].word(c)));
+          cp[t][c] = (t == 0) ? a : cp[t - 1][c] * a;
+        }
+      // product over the TG token groups: ex = exclusive prefix, Gamma_L -> GL
+      if (Cfg::SZ_SC > 0) {
+        // Two lanes per token group (lane = 2 tg + cq, 16 channels per wave).
+        // The group totals go through a wave-private LDS block, transposed to
+        // X[channel][group]; there lane 4 ch + qq takes groups 8 qq .. 8 qq + 7
+        // of channel ch: a running product over its eight groups, then an
+        // exclusive product scan over the four lanes of the quad (DPP quad
+        // permutations; the first lane of each quad holds 1, so lanes that
+        // read it are unaffected).  A wave's LDS accesses complete in order.
+        LDS float* X = (LDS float*)(smem + Cfg::OFF_SC) + w * 16 * Cfg::SC_LD;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) X[(8 * cq + c) * Cfg::SC_LD + tg] = cp[TPL - 1][c];
+        __asm__ __volatile__("" ::: "memory");
+        const int ch = l >> 2, qq = l & 3;
+        LDS float* xr = X + ch * Cfg::SC_LD + 8 * qq;
+        const f32x4 v0 = *lds_ptr<const f32x4>(xr), v1 = *lds_ptr<const f32x4>(xr + 4);
+        const float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+        float e[8];
+        e[0] = 1.f;
+#pragma unroll
+        for (int m = 1; m < 8; ++m) e[m] = e[m - 1] * v[m - 1];
+        const float tq = e[7] * v[7];                       // this quarter's product
+        float z = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(tq), 0x90, 0xf, 0xf, false));
+        z = (qq == 0) ? 1.f : z;                            // quad_perm [0,0,1,2]: the previous lane
+        z *= __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(z), 0x90, 0xf, 0xf, false));
+        z *= __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(z), 0x40, 0xf, 0xf, false));
+        *lds_ptr<f32x4>(xr) = f32x4{z * e[0], z * e[1], z * e[2], z * e[3]};
+        *lds_ptr<f32x4>(xr + 4) = f32x4{z * e[4], z * e[5], z * e[6], z * e[7]};
+        if (qq == 3) {
+          const float gl = z * tq;                          // Gamma_L of channel ch
+          GL[w * 16 + ch] = gl;
+          bad = !(gl >= KDA_GAMMA_MIN);
+        }
+        __asm__ __volatile__("" ::: "memory");
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) ex[c] = X[(8 * cq + c) * Cfg::SC_LD + tg];
+      } else {
+        // inclusive scan over the lanes cq + CQ tg, then shift by one group
+        float tot[CPL];
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+          float x = cp[TPL - 1][c];
+#pragma unroll
+          for (int d = CQ; d < 64; d <<= 1) {
+            const float y = __shfl_up(x, d);
+            if (l >= d) x *= y;
+          }
+          tot[c] = __shfl(x, 64 - CQ + cq);     // Gamma_L
+          const float y = __shfl_up(x, CQ);
+          ex[c] = (l >= CQ) ? y : 1.f;
+        }
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) bad |= !(tot[c] >= KDA_GAMMA_MIN);
+        if (tg == 0) {
+          *lds_ptr<f32x4>(GL + kc0) = f32x4{tot[0], tot[1], tot[2], tot[3]};
+          *lds_ptr<f32x4>(GL + kc0 + 4) = f32x4{tot[4], tot[5], tot[6], tot[7]};
+        }
       }
     }
     // -KI of the lane's tokens per key channel, for the key-major copy
@@ -921,7 +962,11 @@ struct ChunkKernel {
 #pragma unroll
       for (int mt = 0; mt < MTK; ++mt) {
         const size_t ci = row * DK + 16 * mt + g4;
-        const f32x4 gv = *reinterpret_cast<const f32x4*>(g + ci);
+        f32x4 gv;
+        if constexpr (Cfg::SG)
+          gv = f32x4{g[row], g[row], g[row], g[row]};
+        else
+          gv = *reinterpret_cast<const f32x4*>(g + ci);
         const f32x4 kv = Io::load4(k, ci);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -1134,10 +1179,13 @@ bool chunk_supported(int dk, int dv, bool bf16) {
 hipError_t launch_chunk(const void* q, const void* k, const void* v, const float* g,
                         const float* beta, const float* S0, void* out, float* S_final,
                         const int32_t* cu_seqlens, int n_seq, int T, int H, int dk, int dv,
-                        float scale, bool bf16, hipStream_t stream) {
-#define KDA_CH(DK, DV, IO, OP, NWV)                                                       \
-  return launch_chunk_t<ChunkCfg<DK, DV, IO, OP, NWV>>(q, k, v, g, beta, S0, out, S_final, \
-                                                       cu_seqlens, n_seq, T, H, scale, stream);
+                        float scale, bool bf16, bool scalar_gate, hipStream_t stream) {
+#define KDA_CH(DK, DV, IO, OP, NWV)                                                          \
+  return scalar_gate                                                                        \
+             ? launch_chunk_t<ChunkCfg<DK, DV, IO, OP, NWV, true>>(                         \
+                   q, k, v, g, beta, S0, out, S_final, cu_seqlens, n_seq, T, H, scale, stream) \
+             : launch_chunk_t<ChunkCfg<DK, DV, IO, OP, NWV, false>>(                        \
+                   q, k, v, g, beta, S0, out, S_final, cu_seqlens, n_seq, T, H, scale, stream);
   // d_v = 128 runs 8 waves (two per SIMD, 16 value columns each); d_v = 64
   // keeps 4 (value tiles are 16 columns wide).
   if (bf16) {

@@ -21,7 +21,9 @@
 
 namespace kda {
 
-template <int DK, int DV, class Io>
+// SG: one gate per (sequence, head) for every key row (Gated DeltaNet: log_alpha
+// is [N, H]); otherwise one per key row (KDA: [N, H, d_k]).
+template <int DK, int DV, class Io, bool SG>
 __global__ __launch_bounds__(256) void decode_step_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, float* __restrict__ S,
@@ -58,7 +60,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
     const float kk = Io::load(k, i), qq = Io::load(q, i);
     s_k[t] = kk;
     s_q[t] = qq;
-    s_a[t] = __expf(g[i]);
+    s_a[t] = __expf(SG ? g[head] : g[i]);
     kq_part = kk * qq;
   }
 #pragma unroll
@@ -108,19 +110,25 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
 template <int DK, int DV, class Io>
 static hipError_t launch_decode_t(const void* q, const void* k, const void* v, const float* g,
                                   const float* beta, float* S, void* out, int NH, float scale,
-                                  hipStream_t stream) {
-  hipLaunchKernelGGL((decode_step_kernel<DK, DV, Io>), dim3(NH * (DV / 64)), dim3(256), 0, stream,
-                     q, k, v, g, beta, S, out, scale);
+                                  bool sg, hipStream_t stream) {
+  if (sg)
+    hipLaunchKernelGGL((decode_step_kernel<DK, DV, Io, true>), dim3(NH * (DV / 64)), dim3(256), 0,
+                       stream, q, k, v, g, beta, S, out, scale);
+  else
+    hipLaunchKernelGGL((decode_step_kernel<DK, DV, Io, false>), dim3(NH * (DV / 64)), dim3(256), 0,
+                       stream, q, k, v, g, beta, S, out, scale);
   return hipGetLastError();
 }
 
 hipError_t launch_decode(const void* q, const void* k, const void* v, const float* g,
                          const float* beta, float* S, void* out, int NH, int dk, int dv,
-                         float scale, bool bf16, hipStream_t stream) {
+                         float scale, bool bf16, bool scalar_gate, hipStream_t stream) {
 #define KDA_DEC(DK, DV)                                                                     \
   if (dk == DK && dv == DV)                                                                \
-    return bf16 ? launch_decode_t<DK, DV, IoBf16>(q, k, v, g, beta, S, out, NH, scale, stream) \
-                : launch_decode_t<DK, DV, IoF32>(q, k, v, g, beta, S, out, NH, scale, stream);
+    return bf16 ? launch_decode_t<DK, DV, IoBf16>(q, k, v, g, beta, S, out, NH, scale,        \
+                                                  scalar_gate, stream)                        \
+                : launch_decode_t<DK, DV, IoF32>(q, k, v, g, beta, S, out, NH, scale, scalar_gate, \
+                                                 stream);
   KDA_DEC(64, 64)
   KDA_DEC(64, 128)
   KDA_DEC(128, 64)

@@ -7,16 +7,16 @@
 namespace kda {
 hipError_t launch_decode(const void* q, const void* k, const void* v, const float* g,
                          const float* beta, float* S, void* out, int NH, int dk, int dv,
-                         float scale, bool bf16, hipStream_t stream);
+                         float scale, bool bf16, bool scalar_gate, hipStream_t stream);
 hipError_t launch_chunk(const void* q, const void* k, const void* v, const float* g,
                         const float* beta, const float* S0, void* out, float* S_final,
                         const int32_t* cu_seqlens, int n_seq, int T, int H, int dk, int dv,
-                        float scale, bool bf16, hipStream_t stream);
+                        float scale, bool bf16, bool scalar_gate, hipStream_t stream);
 bool chunk_supported(int dk, int dv, bool bf16);
 hipError_t launch_recurrent(const void* q, const void* k, const void* v, const float* g,
                             const float* beta, const float* S0, void* out, float* S_final,
                             const int32_t* cu, int n_seq, int T, int H, int dk, int dv,
-                            float scale, bool bf16, hipStream_t stream);
+                            float scale, bool bf16, bool scalar_gate, hipStream_t stream);
 }  // namespace kda
 
 namespace {
@@ -53,12 +53,14 @@ bool shape_ok(int d) { return d == 64 || d == 128; }
 
 // The vector loads and stores of every kernel assume 16-byte aligned arrays
 // (beta and cu_seqlens are read as single words).
+// A per-(token, head) gate (scalar_gate) is read as single words too.
 int check_align(const void* q, const void* k, const void* v, const float* log_alpha,
                 const float* beta, const float* S0, const void* out, const float* S_final,
-                const int32_t* cu) {
-  const void* a16[] = {q, k, v, log_alpha, S0, out, S_final};
+                const int32_t* cu, bool scalar_gate) {
+  const void* a16[] = {q, k, v, S0, out, S_final};
   for (const void* p : a16)
     if (!aligned(p, 16)) return KDA_ERR_ALIGN;
+  if (!aligned(log_alpha, scalar_gate ? 4 : 16)) return KDA_ERR_ALIGN;
   if (!aligned(beta, 4) || !aligned(cu, 4)) return KDA_ERR_ALIGN;
   return KDA_OK;
 }
@@ -70,15 +72,16 @@ int check_align(const void* q, const void* k, const void* v, const float* log_al
 int check_tokens(const void* q, const void* k, const void* v, const float* log_alpha,
                  const float* beta, const float* S0, void* out, float* S_final,
                  const int32_t* cu, size_t rows, int n_seq, int H, int d_k, int d_v,
-                 bool supported, int io_dtype) {
+                 bool supported, int io_dtype, bool scalar_gate) {
   if (!supported) return KDA_ERR_UNSUPPORTED;
   if (rows > 0 && (!q || !k || !v || !log_alpha || !beta || !out)) return KDA_ERR_NULL;
-  const int al = check_align(q, k, v, log_alpha, beta, S0, out, S_final, cu);
+  const int al = check_align(q, k, v, log_alpha, beta, S0, out, S_final, cu, scalar_gate);
   if (al != KDA_OK) return al;
   const size_t e = io_bytes(io_dtype);
   const size_t state = (size_t)n_seq * H * d_k * d_v * sizeof(float);
   const Range in[] = {span(q, rows * H * d_k * e), span(k, rows * H * d_k * e),
-                      span(v, rows * H * d_v * e), span(log_alpha, rows * H * d_k * 4),
+                      span(v, rows * H * d_v * e),
+                      span(log_alpha, rows * H * (scalar_gate ? 1 : d_k) * 4),
                       span(beta, rows * H * 4),    span(cu, cu ? (size_t)(n_seq + 1) * 4 : 0)};
   const Range ro = span(out, rows * H * d_v * e);
   const Range rs = span(S_final, S_final ? state : 0);
@@ -94,20 +97,119 @@ int check_tokens(const void* q, const void* k, const void* v, const float* log_a
 int check_prefill(const void* q, const void* k, const void* v, const float* log_alpha,
                   const float* beta, const float* S0, void* out, float* S_final,
                   const int32_t* cu, size_t rows, int n_seq, int H, int d_k, int d_v, int chunk,
-                  int io_dtype) {
+                  int io_dtype, bool scalar_gate) {
   const bool ok = io_ok(io_dtype) && chunk == 64 &&
                   kda::chunk_supported(d_k, d_v, io_dtype == KDA_IO_BF16);
   return check_tokens(q, k, v, log_alpha, beta, S0, out, S_final, cu, rows, n_seq, H, d_k, d_v,
-                      ok, io_dtype);
+                      ok, io_dtype, scalar_gate);
 }
 
 int check_recurrent(const void* q, const void* k, const void* v, const float* log_alpha,
                     const float* beta, const float* S0, void* out, float* S_final,
                     const int32_t* cu, size_t rows, int n_seq, int H, int d_k, int d_v,
-                    int io_dtype) {
+                    int io_dtype, bool scalar_gate) {
   const bool ok = io_ok(io_dtype) && shape_ok(d_k) && shape_ok(d_v);
   return check_tokens(q, k, v, log_alpha, beta, S0, out, S_final, cu, rows, n_seq, H, d_k, d_v,
-                      ok, io_dtype);
+                      ok, io_dtype, scalar_gate);
+}
+
+}  // namespace
+
+namespace {
+
+int chunk_fwd_impl(const void* q, const void* k, const void* v, const float* log_alpha,
+                   const float* beta, const float* S0, void* out, float* S_final, int B, int T,
+                   int H, int d_k, int d_v, float scale, int chunk, int io_dtype, bool sg,
+                   void* stream) {
+  if (B < 0 || T < 0 || H <= 0) return KDA_ERR_DIM;
+  const size_t rows = (size_t)B * T;
+  int st = check_prefill(q, k, v, log_alpha, beta, S0, out, S_final, nullptr, rows, B, H, d_k,
+                         d_v, chunk, io_dtype, sg);
+  if (st != KDA_OK) return st;
+  if (B == 0) return KDA_OK;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (T == 0) {
+    if (!S_final || S0 == S_final) return KDA_OK;
+    const size_t n = (size_t)B * H * d_k * d_v;
+    hipLaunchKernelGGL(copy_state_kernel, dim3(1024), dim3(256), 0, s, S0, S_final, n);
+    return launch_status(hipGetLastError());
+  }
+  return launch_status(kda::launch_chunk(q, k, v, log_alpha, beta, S0, out, S_final, nullptr, B,
+                                         T, H, d_k, d_v, scale, io_dtype == KDA_IO_BF16, sg, s));
+}
+
+int chunk_fwd_varlen_impl(const void* q, const void* k, const void* v, const float* log_alpha,
+                          const float* beta, const float* S0, void* out, float* S_final,
+                          const int32_t* cu_seqlens, int N, int T_total, int H, int d_k,
+                          int d_v, float scale, int chunk, int io_dtype, bool sg, void* stream) {
+  if (N < 0 || T_total < 0 || H <= 0) return KDA_ERR_DIM;
+  if (!cu_seqlens) return KDA_ERR_NULL;
+  int st = check_prefill(q, k, v, log_alpha, beta, S0, out, S_final, cu_seqlens,
+                         (size_t)T_total, N, H, d_k, d_v, chunk, io_dtype, sg);
+  if (st != KDA_OK) return st;
+  if (N == 0) return KDA_OK;
+  return launch_status(kda::launch_chunk(q, k, v, log_alpha, beta, S0, out, S_final, cu_seqlens,
+                                         N, T_total, H, d_k, d_v, scale,
+                                         io_dtype == KDA_IO_BF16, sg,
+                                         reinterpret_cast<hipStream_t>(stream)));
+}
+
+int decode_step_impl(const void* q, const void* k, const void* v, const float* log_alpha,
+                     const float* beta, float* S_inout, void* out, int N, int H, int d_k,
+                     int d_v, float scale, int io_dtype, bool sg, void* stream) {
+  if (N < 0 || H <= 0) return KDA_ERR_DIM;
+  if (!io_ok(io_dtype)) return KDA_ERR_UNSUPPORTED;
+  if (!(shape_ok(d_k) && shape_ok(d_v))) return KDA_ERR_UNSUPPORTED;
+  if (N == 0) return KDA_OK;
+  if (!q || !k || !v || !log_alpha || !beta || !S_inout || !out) return KDA_ERR_NULL;
+  const int al = check_align(q, k, v, log_alpha, beta, S_inout, out, nullptr, nullptr, sg);
+  if (al != KDA_OK) return al;
+  const size_t e = io_bytes(io_dtype);
+  const size_t heads = (size_t)N * H;
+  const Range in[] = {span(q, heads * d_k * e), span(k, heads * d_k * e), span(v, heads * d_v * e),
+                      span(log_alpha, heads * (sg ? 1 : d_k) * 4), span(beta, heads * 4)};
+  const Range ro = span(out, heads * d_v * e);
+  const Range rs = span(S_inout, heads * d_k * d_v * 4);
+  for (const Range& r : in) {
+    if (overlap(ro, r) || overlap(rs, r)) return KDA_ERR_ALIAS;
+  }
+  if (overlap(ro, rs)) return KDA_ERR_ALIAS;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  return launch_status(kda::launch_decode(q, k, v, log_alpha, beta, S_inout, out, (int)heads, d_k,
+                                          d_v, scale, io_dtype == KDA_IO_BF16, sg, s));
+}
+
+int recurrent_fwd_impl(const void* q, const void* k, const void* v, const float* log_alpha,
+                       const float* beta, const float* S0, void* out, float* S_final, int B,
+                       int T, int H, int d_k, int d_v, float scale, int io_dtype, bool sg,
+                       void* stream) {
+  if (B < 0 || T < 0 || H <= 0) return KDA_ERR_DIM;
+  const size_t rows = (size_t)B * T;
+  if (rows > 0x7fffffffu) return KDA_ERR_DIM;   // token indices are 32-bit in the kernel
+  int st = check_recurrent(q, k, v, log_alpha, beta, S0, out, S_final, nullptr, rows, B, H, d_k,
+                           d_v, io_dtype, sg);
+  if (st != KDA_OK) return st;
+  if (B == 0 || (T == 0 && (!S_final || S0 == S_final))) return KDA_OK;
+  // (T == 0 with a separate S_final: the kernel copies S0, or zeros, through)
+  return launch_status(kda::launch_recurrent(q, k, v, log_alpha, beta, S0, out, S_final, nullptr,
+                                             B, T, H, d_k, d_v, scale, io_dtype == KDA_IO_BF16,
+                                             sg, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int recurrent_fwd_varlen_impl(const void* q, const void* k, const void* v, const float* log_alpha,
+                              const float* beta, const float* S0, void* out, float* S_final,
+                              const int32_t* cu_seqlens, int N, int T_total, int H, int d_k,
+                              int d_v, float scale, int io_dtype, bool sg, void* stream) {
+  if (N < 0 || T_total < 0 || H <= 0) return KDA_ERR_DIM;
+  if (!cu_seqlens) return KDA_ERR_NULL;
+  int st = check_recurrent(q, k, v, log_alpha, beta, S0, out, S_final, cu_seqlens,
+                           (size_t)T_total, N, H, d_k, d_v, io_dtype, sg);
+  if (st != KDA_OK) return st;
+  if (N == 0) return KDA_OK;
+  return launch_status(kda::launch_recurrent(q, k, v, log_alpha, beta, S0, out, S_final,
+                                             cu_seqlens, N, T_total, H, d_k, d_v, scale,
+                                             io_dtype == KDA_IO_BF16, sg,
+                                             reinterpret_cast<hipStream_t>(stream)));
 }
 
 }  // namespace
@@ -140,21 +242,8 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const float* log_
                   size_t workspace_bytes, void* stream) {
   (void)workspace;
   (void)workspace_bytes;
-  if (B < 0 || T < 0 || H <= 0) return KDA_ERR_DIM;
-  const size_t rows = (size_t)B * T;
-  int st = check_prefill(q, k, v, log_alpha, beta, S0, out, S_final, nullptr, rows, B, H, d_k,
-                         d_v, chunk, io_dtype);
-  if (st != KDA_OK) return st;
-  if (B == 0) return KDA_OK;
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (T == 0) {
-    if (!S_final || S0 == S_final) return KDA_OK;
-    const size_t n = (size_t)B * H * d_k * d_v;
-    hipLaunchKernelGGL(copy_state_kernel, dim3(1024), dim3(256), 0, s, S0, S_final, n);
-    return launch_status(hipGetLastError());
-  }
-  return launch_status(kda::launch_chunk(q, k, v, log_alpha, beta, S0, out, S_final, nullptr, B,
-                                         T, H, d_k, d_v, scale, io_dtype == KDA_IO_BF16, s));
+  return chunk_fwd_impl(q, k, v, log_alpha, beta, S0, out, S_final, B, T, H, d_k, d_v, scale,
+                        chunk, io_dtype, false, stream);
 }
 
 int kda_chunk_fwd_varlen(const void* q, const void* k, const void* v, const float* log_alpha,
@@ -164,74 +253,75 @@ int kda_chunk_fwd_varlen(const void* q, const void* k, const void* v, const floa
                          size_t workspace_bytes, void* stream) {
   (void)workspace;
   (void)workspace_bytes;
-  if (N < 0 || T_total < 0 || H <= 0) return KDA_ERR_DIM;
-  if (!cu_seqlens) return KDA_ERR_NULL;
-  const size_t rows = (size_t)T_total;
-  int st = check_prefill(q, k, v, log_alpha, beta, S0, out, S_final, cu_seqlens, rows, N, H, d_k,
-                         d_v, chunk, io_dtype);
-  if (st != KDA_OK) return st;
-  if (N == 0) return KDA_OK;
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  return launch_status(kda::launch_chunk(q, k, v, log_alpha, beta, S0, out, S_final, cu_seqlens,
-                                         N, T_total, H, d_k, d_v, scale,
-                                         io_dtype == KDA_IO_BF16, s));
+  return chunk_fwd_varlen_impl(q, k, v, log_alpha, beta, S0, out, S_final, cu_seqlens, N,
+                               T_total, H, d_k, d_v, scale, chunk, io_dtype, false, stream);
 }
 
 int kda_decode_step(const void* q, const void* k, const void* v, const float* log_alpha,
                     const float* beta, float* S_inout, void* out, int N, int H, int d_k, int d_v,
                     float scale, int io_dtype, void* stream) {
-  if (N < 0 || H <= 0) return KDA_ERR_DIM;
-  if (!io_ok(io_dtype)) return KDA_ERR_UNSUPPORTED;
-  if (!(shape_ok(d_k) && shape_ok(d_v))) return KDA_ERR_UNSUPPORTED;
-  if (N == 0) return KDA_OK;
-  if (!q || !k || !v || !log_alpha || !beta || !S_inout || !out) return KDA_ERR_NULL;
-  const int al = check_align(q, k, v, log_alpha, beta, S_inout, out, nullptr, nullptr);
-  if (al != KDA_OK) return al;
-  const size_t e = io_bytes(io_dtype);
-  const size_t heads = (size_t)N * H;
-  const Range in[] = {span(q, heads * d_k * e), span(k, heads * d_k * e), span(v, heads * d_v * e),
-                      span(log_alpha, heads * d_k * 4), span(beta, heads * 4)};
-  const Range ro = span(out, heads * d_v * e);
-  const Range rs = span(S_inout, heads * d_k * d_v * 4);
-  for (const Range& r : in) {
-    if (overlap(ro, r) || overlap(rs, r)) return KDA_ERR_ALIAS;
-  }
-  if (overlap(ro, rs)) return KDA_ERR_ALIAS;
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  return launch_status(kda::launch_decode(q, k, v, log_alpha, beta, S_inout, out, (int)heads, d_k,
-                                          d_v, scale, io_dtype == KDA_IO_BF16, s));
+  return decode_step_impl(q, k, v, log_alpha, beta, S_inout, out, N, H, d_k, d_v, scale,
+                          io_dtype, false, stream);
 }
 
 int kda_recurrent_fwd(const void* q, const void* k, const void* v, const float* log_alpha,
                       const float* beta, const float* S0, void* out, float* S_final, int B, int T,
                       int H, int d_k, int d_v, float scale, int io_dtype, void* stream) {
-  if (B < 0 || T < 0 || H <= 0) return KDA_ERR_DIM;
-  const size_t rows = (size_t)B * T;
-  if (rows > 0x7fffffffu) return KDA_ERR_DIM;   // token indices are 32-bit in the kernel
-  int st = check_recurrent(q, k, v, log_alpha, beta, S0, out, S_final, nullptr, rows, B, H, d_k,
-                           d_v, io_dtype);
-  if (st != KDA_OK) return st;
-  if (B == 0 || (T == 0 && (!S_final || S0 == S_final))) return KDA_OK;
-  // (T == 0 with a separate S_final: the kernel copies S0, or zeros, through)
-  return launch_status(kda::launch_recurrent(q, k, v, log_alpha, beta, S0, out, S_final, nullptr,
-                                             B, T, H, d_k, d_v, scale, io_dtype == KDA_IO_BF16,
-                                             reinterpret_cast<hipStream_t>(stream)));
+  return recurrent_fwd_impl(q, k, v, log_alpha, beta, S0, out, S_final, B, T, H, d_k, d_v, scale,
+                            io_dtype, false, stream);
 }
 
 int kda_recurrent_fwd_varlen(const void* q, const void* k, const void* v, const float* log_alpha,
                              const float* beta, const float* S0, void* out, float* S_final,
                              const int32_t* cu_seqlens, int N, int T_total, int H, int d_k,
                              int d_v, float scale, int io_dtype, void* stream) {
-  if (N < 0 || T_total < 0 || H <= 0) return KDA_ERR_DIM;
-  if (!cu_seqlens) return KDA_ERR_NULL;
-  int st = check_recurrent(q, k, v, log_alpha, beta, S0, out, S_final, cu_seqlens,
-                           (size_t)T_total, N, H, d_k, d_v, io_dtype);
-  if (st != KDA_OK) return st;
-  if (N == 0) return KDA_OK;
-  return launch_status(kda::launch_recurrent(q, k, v, log_alpha, beta, S0, out, S_final,
-                                             cu_seqlens, N, T_total, H, d_k, d_v, scale,
-                                             io_dtype == KDA_IO_BF16,
-                                             reinterpret_cast<hipStream_t>(stream)));
+  return recurrent_fwd_varlen_impl(q, k, v, log_alpha, beta, S0, out, S_final, cu_seqlens, N,
+                                   T_total, H, d_k, d_v, scale, io_dtype, false, stream);
+}
+
+int kda_gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* log_alpha,
+                      const float* beta, const float* S0, void* out, float* S_final, int B, int T,
+                      int H, int d_k, int d_v, float scale, int chunk, int io_dtype,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  return chunk_fwd_impl(q, k, v, log_alpha, beta, S0, out, S_final, B, T, H, d_k, d_v, scale,
+                        chunk, io_dtype, true, stream);
+}
+
+int kda_gdn_chunk_fwd_varlen(const void* q, const void* k, const void* v, const float* log_alpha,
+                             const float* beta, const float* S0, void* out, float* S_final,
+                             const int32_t* cu_seqlens, int N, int T_total, int H, int d_k,
+                             int d_v, float scale, int chunk, int io_dtype, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  return chunk_fwd_varlen_impl(q, k, v, log_alpha, beta, S0, out, S_final, cu_seqlens, N,
+                               T_total, H, d_k, d_v, scale, chunk, io_dtype, true, stream);
+}
+
+int kda_gdn_decode_step(const void* q, const void* k, const void* v, const float* log_alpha,
+                        const float* beta, float* S_inout, void* out, int N, int H, int d_k,
+                        int d_v, float scale, int io_dtype, void* stream) {
+  return decode_step_impl(q, k, v, log_alpha, beta, S_inout, out, N, H, d_k, d_v, scale,
+                          io_dtype, true, stream);
+}
+
+int kda_gdn_recurrent_fwd(const void* q, const void* k, const void* v, const float* log_alpha,
+                          const float* beta, const float* S0, void* out, float* S_final, int B,
+                          int T, int H, int d_k, int d_v, float scale, int io_dtype,
+                          void* stream) {
+  return recurrent_fwd_impl(q, k, v, log_alpha, beta, S0, out, S_final, B, T, H, d_k, d_v, scale,
+                            io_dtype, true, stream);
+}
+
+int kda_gdn_recurrent_fwd_varlen(const void* q, const void* k, const void* v,
+                                 const float* log_alpha, const float* beta, const float* S0,
+                                 void* out, float* S_final, const int32_t* cu_seqlens, int N,
+                                 int T_total, int H, int d_k, int d_v, float scale, int io_dtype,
+                                 void* stream) {
+  return recurrent_fwd_varlen_impl(q, k, v, log_alpha, beta, S0, out, S_final, cu_seqlens, N,
+                                   T_total, H, d_k, d_v, scale, io_dtype, true, stream);
 }
 
 }  // extern "C"

@@ -67,11 +67,14 @@ __device__ __forceinline__ float row_sum16(float x) {
 
 }  // namespace
 
-template <int DK, int DV, class Io>
+// One token's inputs for one lane.  SG: one gate per (token, head) for every
+// key row (Gated DeltaNet); otherwise one per key row (KDA).
+template <int DK, int DV, class Io, bool SG>
 struct RecurrentToken {
   static constexpr int RPT = DK / 16;
   RowVec<Io, RPT> k, q;
   RowVec<IoF32, RPT> g;
+  float gs;
   RowVec<Io, 4> v;
   float beta;
   __device__ __forceinline__ void load(const void* qp, const void* kp, const void* vp,
@@ -79,15 +82,19 @@ struct RecurrentToken {
                                        int col) {
     k.load(kp, e * DK + row0);
     q.load(qp, e * DK + row0);
-    g.load(gp, e * DK + row0);
+    if constexpr (SG)
+      gs = gp[e];
+    else
+      g.load(gp, e * DK + row0);
     v.load(vp, e * DV + col);
     beta = bp[e];
   }
+  __device__ __forceinline__ float gate(int m) const { return SG ? gs : g.get(m); }
 };
 
 // S0 and S_final may be the same array (each workgroup reads its slice of the
 // state before it writes it), so neither is marked restrict.
-template <int DK, int DV, class Io>
+template <int DK, int DV, class Io, bool SG>
 __global__ __launch_bounds__(256) void recurrent_fwd_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, const float* S0,
@@ -139,7 +146,7 @@ __global__ __launch_bounds__(256) void recurrent_fwd_kernel(
   }
 
   // one token: forget, predict, correct, write, read
-  auto token = [&](const RecurrentToken<DK, DV, Io>& in, int t) {
+  auto token = [&](const RecurrentToken<DK, DV, Io, SG>& in, int t) {
     float kk[RPT], qq[RPT];
     float kq = 0.f;
 #pragma unroll
@@ -152,7 +159,7 @@ __global__ __launch_bounds__(256) void recurrent_fwd_kernel(
     f32x4 p = {0.f, 0.f, 0.f, 0.f}, r = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int m = 0; m < RPT; ++m) {
-      st[m] *= __expf(in.g.get(m));
+      st[m] *= __expf(in.gate(m));
       p += st[m] * kk[m];
       r += st[m] * qq[m];
     }
@@ -169,7 +176,7 @@ __global__ __launch_bounds__(256) void recurrent_fwd_kernel(
 #pragma unroll
     for (int m = 0; m < RPT; ++m) st[m] += kk[m] * e;
   };
-  auto fetch = [&](RecurrentToken<DK, DV, Io>& in, int t) {
+  auto fetch = [&](RecurrentToken<DK, DV, Io, SG>& in, int t) {
     in.load(q, k, v, g, beta, (size_t)t * H + h, row0, col);
   };
 
@@ -177,7 +184,7 @@ __global__ __launch_bounds__(256) void recurrent_fwd_kernel(
   // while token t is processed.  The prefetch past the end re-reads the last
   // token, so the loads need no branch.
   if (t0 < t1) {
-    RecurrentToken<DK, DV, Io> a, b;
+    RecurrentToken<DK, DV, Io, SG> a, b;
     fetch(a, t0);
     int t = t0;
     for (; t + 1 < t1; t += 2) {
@@ -209,24 +216,28 @@ template <int DK, int DV, class Io>
 static hipError_t launch_recurrent_t(const void* q, const void* k, const void* v, const float* g,
                                      const float* beta, const float* S0, void* out,
                                      float* S_final, const int32_t* cu, int n_seq, int T, int H,
-                                     float scale, hipStream_t stream) {
+                                     float scale, bool sg, hipStream_t stream) {
   const long blocks = (long)n_seq * H * (DV / 64);
   if (blocks > 0x7fffffffL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((recurrent_fwd_kernel<DK, DV, Io>), dim3((unsigned)blocks), dim3(256), 0,
-                     stream, q, k, v, g, beta, S0, out, S_final, cu, T, H, scale);
+  if (sg)
+    hipLaunchKernelGGL((recurrent_fwd_kernel<DK, DV, Io, true>), dim3((unsigned)blocks),
+                       dim3(256), 0, stream, q, k, v, g, beta, S0, out, S_final, cu, T, H, scale);
+  else
+    hipLaunchKernelGGL((recurrent_fwd_kernel<DK, DV, Io, false>), dim3((unsigned)blocks),
+                       dim3(256), 0, stream, q, k, v, g, beta, S0, out, S_final, cu, T, H, scale);
   return hipGetLastError();
 }
 
 hipError_t launch_recurrent(const void* q, const void* k, const void* v, const float* g,
                             const float* beta, const float* S0, void* out, float* S_final,
                             const int32_t* cu, int n_seq, int T, int H, int dk, int dv,
-                            float scale, bool bf16, hipStream_t stream) {
-#define KDA_REC(DK, DV)                                                                       \
-  if (dk == DK && dv == DV)                                                                  \
+                            float scale, bool bf16, bool scalar_gate, hipStream_t stream) {
+#define KDA_REC(DK, DV)                                                                    \
+  if (dk == DK && dv == DV)                                                               \
     return bf16 ? launch_recurrent_t<DK, DV, IoBf16>(q, k, v, g, beta, S0, out, S_final, cu, \
-                                                     n_seq, T, H, scale, stream)            \
+                                                     n_seq, T, H, scale, scalar_gate, stream) \
                 : launch_recurrent_t<DK, DV, IoF32>(q, k, v, g, beta, S0, out, S_final, cu,  \
-                                                    n_seq, T, H, scale, stream);
+                                                    n_seq, T, H, scale, scalar_gate, stream);
   KDA_REC(64, 64)
   KDA_REC(64, 128)
   KDA_REC(128, 64)

@@ -16,6 +16,8 @@ Recipe (the pages fix only shapes and distributions; the rest is chosen here):
   packed along the token axis with cu_seqlens; in each head a seeded choice of
   ``long_channels`` key channels draws log_alpha = -exp(N(-8, 0.5)) instead
   (a decay horizon of a few thousand tokens).
+* gate="gdn" (Gated DeltaNet) draws one log_alpha per (token, head), shape
+  [..., H], from the same -exp(N(-3, 1)); gate="kda" one per key channel.
 * Draw order: q, k, v, g, beta, S0 (lengths first for varlen).  Random numbers
   come from one ``torch.Generator`` on the target device, so a seed gives the
   same tensors on every run of one device type.
@@ -67,12 +69,16 @@ def _log_alpha(shape, gen, device, long_mask=None):
     return -torch.exp(mu + sd * z)
 
 
-def _draw(rows_shape, H, dk, dv, io, gen, device, with_S0, n_seq, s0_std, long_mask=None):
+def _draw(rows_shape, H, dk, dv, io, gen, device, with_S0, n_seq, s0_std, long_mask=None,
+          gate="kda"):
     dt = _IO[io]
     q = _unit_normal((*rows_shape, H, dk), gen, device).to(dt)
     k = _unit_normal((*rows_shape, H, dk), gen, device).to(dt)
     v = torch.randn((*rows_shape, H, dv), generator=gen, device=device, dtype=torch.float32).to(dt)
-    g = _log_alpha((*rows_shape, H, dk), gen, device, long_mask)
+    if gate == "gdn":
+        g = _log_alpha((*rows_shape, H), gen, device)
+    else:
+        g = _log_alpha((*rows_shape, H, dk), gen, device, long_mask)
     beta = torch.sigmoid(torch.randn((*rows_shape, H), generator=gen, device=device,
                                      dtype=torch.float32))
     S0 = None
@@ -83,10 +89,10 @@ def _draw(rows_shape, H, dk, dv, io, gen, device, with_S0, n_seq, s0_std, long_m
 
 
 def prefill_inputs(B, T, H, dk, dv, io="bf16", seed=0, with_S0=False, s0_std=0.02,
-                   device="cpu"):
+                   device="cpu", gate="kda"):
     """Batched prefill inputs in the [B, T, H, d] layout."""
     gen = _gen(device, seed)
-    d = _draw((B, T), H, dk, dv, io, gen, device, with_S0, B, s0_std)
+    d = _draw((B, T), H, dk, dv, io, gen, device, with_S0, B, s0_std, gate=gate)
     d.update(B=B, T=T, H=H, dk=dk, dv=dv, io=io, cu_seqlens=None)
     return d
 
@@ -98,7 +104,7 @@ def varlen_lengths(n_seq, lo, hi, seed=0):
 
 
 def varlen_inputs(lengths, H, dk, dv, io="bf16", seed=0, with_S0=False, s0_std=0.02,
-                  long_channels=0, device="cpu"):
+                  long_channels=0, device="cpu", gate="kda"):
     """Packed inputs [T_total, H, d] plus int32 cu_seqlens [N+1] (on ``device``)."""
     lengths = [int(x) for x in lengths]
     cu = np.zeros(len(lengths) + 1, dtype=np.int64)
@@ -111,14 +117,16 @@ def varlen_inputs(lengths, H, dk, dv, io="bf16", seed=0, with_S0=False, s0_std=0
         for h in range(H):
             idx = torch.randperm(dk, generator=gen, device=device)[:long_channels]
             long_mask[h, idx] = True
-    d = _draw((T_total,), H, dk, dv, io, gen, device, with_S0, len(lengths), s0_std, long_mask)
+    d = _draw((T_total,), H, dk, dv, io, gen, device, with_S0, len(lengths), s0_std, long_mask,
+              gate=gate)
     d.update(N=len(lengths), T_total=T_total, H=H, dk=dk, dv=dv, io=io,
              cu_seqlens=torch.tensor(cu, dtype=torch.int32, device=device),
              lengths=lengths, long_mask=long_mask)
     return d
 
 
-def decode_inputs(N, H, dk, dv, steps, io="bf16", seed=0, s0_std=0.02, device="cpu"):
+def decode_inputs(N, H, dk, dv, steps, io="bf16", seed=0, s0_std=0.02, device="cpu",
+                  gate="kda"):
     """State S [N, H, dk, dv] fp32 ~ N(0, s0_std^2) and ``steps`` fresh tokens.
 
     Returns dict with S (fp32), and per-step stacked q, k [steps, N, H, dk],
@@ -126,7 +134,7 @@ def decode_inputs(N, H, dk, dv, steps, io="bf16", seed=0, s0_std=0.02, device="c
     """
     gen = _gen(device, seed)
     S = s0_std * torch.randn((N, H, dk, dv), generator=gen, device=device, dtype=torch.float32)
-    d = _draw((steps, N), H, dk, dv, io, gen, device, False, N, s0_std)
+    d = _draw((steps, N), H, dk, dv, io, gen, device, False, N, s0_std, gate=gate)
     d.update(S=S, N=N, H=H, dk=dk, dv=dv, io=io, steps=steps)
     return d
 

@@ -45,6 +45,11 @@ def _load():
     lib.kda_recurrent_fwd_varlen.restype = i
     lib.kda_recurrent_fwd_varlen.argtypes = [vp, vp, vp, fp, fp, fp, vp, fp, vp, i, i, i, i, i, f,
                                              i, vp]
+    for name in ("chunk_fwd", "chunk_fwd_varlen", "decode_step", "recurrent_fwd",
+                 "recurrent_fwd_varlen"):
+        kf, gf = getattr(lib, "kda_" + name), getattr(lib, "kda_gdn_" + name)
+        gf.restype = kf.restype
+        gf.argtypes = kf.argtypes
     lib.kda_chunk_fwd_workspace_size.restype = sz
     lib.kda_chunk_fwd_workspace_size.argtypes = [i] * 7
     lib.kda_chunk_fwd_varlen_workspace_size.restype = sz
@@ -92,6 +97,14 @@ def _check(t, name, shape, dtype, device):
         raise ValueError("%s must be contiguous" % name)
 
 
+def _gate(log_alpha, rows_shape, dk):
+    """(expected log_alpha shape, entry-point prefix): KDA takes one gate per key
+    channel ([..., H, d_k]); Gated DeltaNet one per (token, head) ([..., H])."""
+    if log_alpha is not None and log_alpha.dim() == len(rows_shape):
+        return tuple(rows_shape), "kda_gdn_"
+    return tuple(rows_shape) + (dk,), "kda_"
+
+
 def _workspace(nbytes, device):
     if nbytes == 0:
         return None, 0
@@ -100,16 +113,19 @@ def _workspace(nbytes, device):
 
 def chunk_fwd(q, k, v, log_alpha, beta, S0=None, scale=None, chunk=CHUNK, out=None,
               S_final=None, output_final_state=True):
-    """Chunkwise KDA prefill.  q, k, log_alpha: [B, T, H, d_k]; v: [B, T, H, d_v];
-    beta: [B, T, H]; S0: [B, H, d_k, d_v] fp32 or None.  Returns (o, S_final)."""
+    """Chunkwise prefill.  q, k: [B, T, H, d_k]; v: [B, T, H, d_v]; beta:
+    [B, T, H]; log_alpha: [B, T, H, d_k] (KDA) or [B, T, H] (Gated DeltaNet, one
+    gate per token and head); S0: [B, H, d_k, d_v] fp32 or None.  Returns
+    (o, S_final)."""
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     dev = q.device
     if scale is None:
         scale = dk ** -0.5
+    gshape, pre = _gate(log_alpha, (B, T, H), dk)
     for name, t, shp, dt in (("q", q, (B, T, H, dk), q.dtype), ("k", k, (B, T, H, dk), q.dtype),
                              ("v", v, (B, T, H, dv), q.dtype),
-                             ("log_alpha", log_alpha, (B, T, H, dk), torch.float32),
+                             ("log_alpha", log_alpha, gshape, torch.float32),
                              ("beta", beta, (B, T, H), torch.float32),
                              ("S0", S0, (B, H, dk, dv), torch.float32)):
         _check(t, name, shp, dt, dev)
@@ -121,28 +137,31 @@ def chunk_fwd(q, k, v, log_alpha, beta, S0=None, scale=None, chunk=CHUNK, out=No
         S_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
     _check(S_final, "S_final", (B, H, dk, dv), torch.float32, dev)
     ws, wsb = _workspace(lib.kda_chunk_fwd_workspace_size(B, T, H, dk, dv, chunk, io), dev)
-    st = lib.kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S0),
-                           _ptr(out), _ptr(S_final), B, T, H, dk, dv, float(scale), int(chunk), io,
-                           _ptr(ws), wsb, _stream(dev))
+    fn = pre + "chunk_fwd"
+    st = getattr(lib, fn)(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S0),
+                          _ptr(out), _ptr(S_final), B, T, H, dk, dv, float(scale), int(chunk), io,
+                          _ptr(ws), wsb, _stream(dev))
     if st != 0:
-        raise KdaError(st, "kda_chunk_fwd")
+        raise KdaError(st, fn)
     return out, S_final
 
 
 def chunk_fwd_varlen(q, k, v, log_alpha, beta, cu_seqlens, S0=None, scale=None, chunk=CHUNK,
                      out=None, S_final=None, output_final_state=True):
-    """Packed variable-length prefill.  q, k, log_alpha: [T_total, H, d_k];
-    v: [T_total, H, d_v]; beta: [T_total, H]; cu_seqlens: int32 [N+1] on the
-    device; S0: [N, H, d_k, d_v] fp32 or None.  Returns (o, S_final)."""
+    """Packed variable-length prefill.  q, k: [T_total, H, d_k]; v: [T_total,
+    H, d_v]; beta: [T_total, H]; log_alpha: [T_total, H, d_k] (KDA) or
+    [T_total, H] (Gated DeltaNet); cu_seqlens: int32 [N+1] on the device; S0:
+    [N, H, d_k, d_v] fp32 or None.  Returns (o, S_final)."""
     Tt, H, dk = q.shape
     dv = v.shape[-1]
     dev = q.device
     N = cu_seqlens.shape[0] - 1
     if scale is None:
         scale = dk ** -0.5
+    gshape, pre = _gate(log_alpha, (Tt, H), dk)
     for name, t, shp, dt in (("q", q, (Tt, H, dk), q.dtype), ("k", k, (Tt, H, dk), q.dtype),
                              ("v", v, (Tt, H, dv), q.dtype),
-                             ("log_alpha", log_alpha, (Tt, H, dk), torch.float32),
+                             ("log_alpha", log_alpha, gshape, torch.float32),
                              ("beta", beta, (Tt, H), torch.float32),
                              ("cu_seqlens", cu_seqlens, (N + 1,), torch.int32),
                              ("S0", S0, (N, H, dk, dv), torch.float32)):
@@ -155,25 +174,28 @@ def chunk_fwd_varlen(q, k, v, log_alpha, beta, cu_seqlens, S0=None, scale=None, 
         S_final = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
     _check(S_final, "S_final", (N, H, dk, dv), torch.float32, dev)
     ws, wsb = _workspace(lib.kda_chunk_fwd_varlen_workspace_size(N, Tt, H, dk, dv, chunk, io), dev)
-    st = lib.kda_chunk_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
-                                  _ptr(S0), _ptr(out), _ptr(S_final), _ptr(cu_seqlens), N, Tt, H,
-                                  dk, dv, float(scale), int(chunk), io, _ptr(ws), wsb, _stream(dev))
+    fn = pre + "chunk_fwd_varlen"
+    st = getattr(lib, fn)(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S0),
+                          _ptr(out), _ptr(S_final), _ptr(cu_seqlens), N, Tt, H, dk, dv,
+                          float(scale), int(chunk), io, _ptr(ws), wsb, _stream(dev))
     if st != 0:
-        raise KdaError(st, "kda_chunk_fwd_varlen")
+        raise KdaError(st, fn)
     return out, S_final
 
 
 def decode_step(q, k, v, log_alpha, beta, S_inout, scale=None, out=None):
-    """One fused recurrent step.  q, k, log_alpha: [N, H, d_k]; v: [N, H, d_v];
-    beta: [N, H]; S_inout: [N, H, d_k, d_v] fp32, updated in place.  Returns o."""
+    """One fused recurrent step.  q, k: [N, H, d_k]; v: [N, H, d_v]; beta:
+    [N, H]; log_alpha: [N, H, d_k] (KDA) or [N, H] (Gated DeltaNet); S_inout:
+    [N, H, d_k, d_v] fp32, updated in place.  Returns o."""
     N, H, dk = q.shape
     dv = v.shape[-1]
     dev = q.device
     if scale is None:
         scale = dk ** -0.5
+    gshape, pre = _gate(log_alpha, (N, H), dk)
     for name, t, shp, dt in (("q", q, (N, H, dk), q.dtype), ("k", k, (N, H, dk), q.dtype),
                              ("v", v, (N, H, dv), q.dtype),
-                             ("log_alpha", log_alpha, (N, H, dk), torch.float32),
+                             ("log_alpha", log_alpha, gshape, torch.float32),
                              ("beta", beta, (N, H), torch.float32),
                              ("S_inout", S_inout, (N, H, dk, dv), torch.float32)):
         _check(t, name, shp, dt, dev)
@@ -181,26 +203,28 @@ def decode_step(q, k, v, log_alpha, beta, S_inout, scale=None, out=None):
     if out is None:
         out = torch.empty((N, H, dv), dtype=q.dtype, device=dev)
     _check(out, "out", (N, H, dv), q.dtype, dev)
-    st = lib.kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
-                             _ptr(S_inout), _ptr(out), N, H, dk, dv, float(scale), io, _stream(dev))
+    fn = pre + "decode_step"
+    st = getattr(lib, fn)(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S_inout),
+                          _ptr(out), N, H, dk, dv, float(scale), io, _stream(dev))
     if st != 0:
-        raise KdaError(st, "kda_decode_step")
+        raise KdaError(st, fn)
     return out
 
 
 def recurrent_fwd(q, k, v, log_alpha, beta, S0=None, scale=None, out=None, S_final=None,
                   output_final_state=True):
     """Token-by-token recurrence for short sequences (multi-token decode,
-    speculative verification).  Shapes as chunk_fwd.  Pass S_final=S0 to
-    update a state in place.  Returns (o, S_final)."""
+    speculative verification).  Shapes as chunk_fwd (KDA or Gated DeltaNet
+    gates).  Pass S_final=S0 to update a state in place.  Returns (o, S_final)."""
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     dev = q.device
     if scale is None:
         scale = dk ** -0.5
+    gshape, pre = _gate(log_alpha, (B, T, H), dk)
     for name, t, shp, dt in (("q", q, (B, T, H, dk), q.dtype), ("k", k, (B, T, H, dk), q.dtype),
                              ("v", v, (B, T, H, dv), q.dtype),
-                             ("log_alpha", log_alpha, (B, T, H, dk), torch.float32),
+                             ("log_alpha", log_alpha, gshape, torch.float32),
                              ("beta", beta, (B, T, H), torch.float32),
                              ("S0", S0, (B, H, dk, dv), torch.float32)):
         _check(t, name, shp, dt, dev)
@@ -211,28 +235,30 @@ def recurrent_fwd(q, k, v, log_alpha, beta, S0=None, scale=None, out=None, S_fin
     if S_final is None and output_final_state:
         S_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
     _check(S_final, "S_final", (B, H, dk, dv), torch.float32, dev)
-    st = lib.kda_recurrent_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S0),
-                               _ptr(out), _ptr(S_final), B, T, H, dk, dv, float(scale), io,
-                               _stream(dev))
+    fn = pre + "recurrent_fwd"
+    st = getattr(lib, fn)(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S0),
+                          _ptr(out), _ptr(S_final), B, T, H, dk, dv, float(scale), io,
+                          _stream(dev))
     if st != 0:
-        raise KdaError(st, "kda_recurrent_fwd")
+        raise KdaError(st, fn)
     return out, S_final
 
 
 def recurrent_fwd_varlen(q, k, v, log_alpha, beta, cu_seqlens, S0=None, scale=None, out=None,
                          S_final=None, output_final_state=True):
     """Token-by-token recurrence over packed sequences (varlen decode).
-    Shapes as chunk_fwd_varlen; S_final=S0 updates the states in place.
-    Returns (o, S_final)."""
+    Shapes as chunk_fwd_varlen (KDA or Gated DeltaNet gates); S_final=S0
+    updates the states in place.  Returns (o, S_final)."""
     Tt, H, dk = q.shape
     dv = v.shape[-1]
     dev = q.device
     N = cu_seqlens.shape[0] - 1
     if scale is None:
         scale = dk ** -0.5
+    gshape, pre = _gate(log_alpha, (Tt, H), dk)
     for name, t, shp, dt in (("q", q, (Tt, H, dk), q.dtype), ("k", k, (Tt, H, dk), q.dtype),
                              ("v", v, (Tt, H, dv), q.dtype),
-                             ("log_alpha", log_alpha, (Tt, H, dk), torch.float32),
+                             ("log_alpha", log_alpha, gshape, torch.float32),
                              ("beta", beta, (Tt, H), torch.float32),
                              ("cu_seqlens", cu_seqlens, (N + 1,), torch.int32),
                              ("S0", S0, (N, H, dk, dv), torch.float32)):
@@ -244,9 +270,10 @@ def recurrent_fwd_varlen(q, k, v, log_alpha, beta, cu_seqlens, S0=None, scale=No
     if S_final is None and output_final_state:
         S_final = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
     _check(S_final, "S_final", (N, H, dk, dv), torch.float32, dev)
-    st = lib.kda_recurrent_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
-                                      _ptr(S0), _ptr(out), _ptr(S_final), _ptr(cu_seqlens), N, Tt,
-                                      H, dk, dv, float(scale), io, _stream(dev))
+    fn = pre + "recurrent_fwd_varlen"
+    st = getattr(lib, fn)(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S0),
+                          _ptr(out), _ptr(S_final), _ptr(cu_seqlens), N, Tt, H, dk, dv,
+                          float(scale), io, _stream(dev))
     if st != 0:
-        raise KdaError(st, "kda_recurrent_fwd_varlen")
+        raise KdaError(st, fn)
     return out, S_final

@@ -176,6 +176,45 @@ int kda_recurrent_fwd_varlen(const void* q, const void* k, const void* v, const 
                              const int32_t* cu_seqlens, int N, int T_total, int H, int d_k,
                              int d_v, float scale, int io_dtype, void* stream);
 
+/*
+ * Gated DeltaNet through the same calls: one forget gate per (token, head),
+ * shared by every key channel ("Kimi Unveils Delta Attention and K3
+ * Architecture Updates", section 3; "Linear Attention, From Scratch to Kimi
+ * 3", section 5).  The recurrence above with g_t[i] = g_t for every key
+ * channel i, i.e. S_t = alpha_t (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t
+ * v_t^T.  Each kda_gdn_* call takes exactly the arguments of its kda_*
+ * counterpart, except that log_alpha has no d_k axis:
+ *
+ *  kda_gdn_chunk_fwd, kda_gdn_recurrent_fwd   log_alpha [B, T, H]      fp32
+ *  kda_gdn_chunk_fwd_varlen,
+ *  kda_gdn_recurrent_fwd_varlen                log_alpha [T_total, H]   fp32
+ *  kda_gdn_decode_step                         log_alpha [N, H]         fp32
+ *
+ * log_alpha needs 4-byte alignment only.  Same sizes, dtypes, aliasing rules
+ * and status codes as the KDA calls.
+ */
+int kda_gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* log_alpha,
+                      const float* beta, const float* S0, void* out, float* S_final, int B, int T,
+                      int H, int d_k, int d_v, float scale, int chunk, int io_dtype,
+                      void* workspace, size_t workspace_bytes, void* stream);
+int kda_gdn_chunk_fwd_varlen(const void* q, const void* k, const void* v, const float* log_alpha,
+                             const float* beta, const float* S0, void* out, float* S_final,
+                             const int32_t* cu_seqlens, int N, int T_total, int H, int d_k,
+                             int d_v, float scale, int chunk, int io_dtype, void* workspace,
+                             size_t workspace_bytes, void* stream);
+int kda_gdn_decode_step(const void* q, const void* k, const void* v, const float* log_alpha,
+                        const float* beta, float* S_inout, void* out, int N, int H, int d_k,
+                        int d_v, float scale, int io_dtype, void* stream);
+int kda_gdn_recurrent_fwd(const void* q, const void* k, const void* v, const float* log_alpha,
+                          const float* beta, const float* S0, void* out, float* S_final, int B,
+                          int T, int H, int d_k, int d_v, float scale, int io_dtype,
+                          void* stream);
+int kda_gdn_recurrent_fwd_varlen(const void* q, const void* k, const void* v,
+                                 const float* log_alpha, const float* beta, const float* S0,
+                                 void* out, float* S_final, const int32_t* cu_seqlens, int N,
+                                 int T_total, int H, int d_k, int d_v, float scale, int io_dtype,
+                                 void* stream);
+
 /* Workspace bytes kda_chunk_fwd needs for these sizes (0 if none; the
  * arguments are not validated here: unsupported sizes give 0). */
 size_t kda_chunk_fwd_workspace_size(int B, int T, int H, int d_k, int d_v, int chunk,

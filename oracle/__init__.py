@@ -88,6 +88,11 @@ def forward(q, k, v, g, beta, S0=None, scale=None, cu_seqlens=None, chains=None,
     exact values a bf16 kernel receives).  g, beta: float32.  S0: None (zeros)
     or [N, H, dk, dv] (any float dtype; upcast exactly to fp64).
 
+    Gated DeltaNet ("Kimi Unveils Delta Attention and K3 Architecture
+    Updates", section 3): g without the dk axis ([B, T, H] or [T_total, H]) is
+    one gate per (token, head), the same for every key channel; it is
+    broadcast over dk (a copy, no arithmetic) and the recurrence is unchanged.
+
     ``chains``: iterable of (n, h) pairs (or flat ids n*H+h) to compute;
     default all.  Returns (outs, S_final) where ``outs[c]`` is the fp64
     [len_c, dv] output of chain c and ``S_final`` is [n_chains, dk, dv] fp64.
@@ -98,6 +103,9 @@ def forward(q, k, v, g, beta, S0=None, scale=None, cu_seqlens=None, chains=None,
     v, dt3 = _io_array(v)
     if not (dt == dt2 == dt3):
         raise TypeError("q, k, v must share one dtype")
+    g = np.asarray(g, dtype=np.float32)
+    if g.ndim == q.ndim - 1:
+        g = np.broadcast_to(g[..., None], q.shape)
     g = np.ascontiguousarray(g, dtype=np.float32)
     beta = np.ascontiguousarray(beta, dtype=np.float32)
     if cu_seqlens is None:

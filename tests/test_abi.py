@@ -29,7 +29,9 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for want in ("kda_chunk_fwd", "kda_chunk_fwd_varlen", "kda_decode_step",
-                 "kda_recurrent_fwd", "kda_recurrent_fwd_varlen",
+                 "kda_recurrent_fwd", "kda_recurrent_fwd_varlen", "kda_gdn_chunk_fwd",
+                 "kda_gdn_chunk_fwd_varlen", "kda_gdn_decode_step", "kda_gdn_recurrent_fwd",
+                 "kda_gdn_recurrent_fwd_varlen",
                  "kda_chunk_fwd_workspace_size", "kda_chunk_fwd_varlen_workspace_size",
                  "kda_status_string", "kda_version"):
         assert want in names
@@ -138,6 +140,35 @@ def test_recurrent_validation(lib):
     assert g(*vargs(dv=32)) == -3
     assert g(*vargs(out=P[0])) == -6
     assert g(*vargs(N=0)) == 0
+
+
+def test_gdn_validation(lib):
+    """The Gated DeltaNet calls share the KDA validation; their gate array has
+    no d_k axis and needs only 4-byte alignment."""
+    f = lib.kda_gdn_chunk_fwd
+    args = lambda **kw: (P[0], P[1], P[2], kw.get("g", P[3]), P[4], None, kw.get("out", P[5]),
+                         P[6], kw.get("B", 1), 64, 2, kw.get("dk", 128), 128, 0.1,
+                         kw.get("chunk", 64), 1, None, 0, None)
+    assert f(*args(g=None)) == -1
+    assert f(*args(B=-1)) == -2
+    assert f(*args(dk=32)) == -3
+    assert f(*args(chunk=32)) == -3
+    assert f(*args(out=P[3])) == -6                         # out == log_alpha
+    assert f(*args(g=ctypes.c_void_p(P[3].value + 2))) == -7
+    assert f(*args(B=0)) == 0
+    d = lib.kda_gdn_decode_step
+    assert d(P[0], P[1], P[2], None, P[4], P[5], P[6], 4, 2, 128, 128, 0.1, 1, None) == -1
+    assert d(P[0], P[1], P[2], P[3], P[4], P[5], P[6], 4, 2, 96, 128, 0.1, 1, None) == -3
+    assert d(P[0], P[1], P[2], P[3], P[4], P[5], P[3], 4, 2, 128, 128, 0.1, 1, None) == -6
+    assert d(P[0], P[1], P[2], P[3], P[4], P[5], P[6], 0, 2, 128, 128, 0.1, 1, None) == 0
+    r = lib.kda_gdn_recurrent_fwd
+    assert r(P[0], P[1], P[2], P[3], P[4], None, P[5], P[6], 2, 4, 2, 64, 64, 0.1, 3, None) == -3
+    rv = lib.kda_gdn_recurrent_fwd_varlen
+    assert rv(P[0], P[1], P[2], P[3], P[4], None, P[5], P[6], None, 3, 10, 2, 64, 64, 0.1, 0,
+              None) == -1
+    cv = lib.kda_gdn_chunk_fwd_varlen
+    assert cv(P[0], P[1], P[2], P[3], P[4], None, P[5], P[6], P[7], -1, 10, 2, 64, 64, 0.1, 64, 0,
+              None, 0, None) == -2
 
 
 def test_alignment_validation(lib):

@@ -152,6 +152,34 @@ def test_scalar_alpha_is_gated_deltanet():
     np.testing.assert_allclose(S, S2, atol=1e-12)
 
 
+def test_head_gate_layout_is_gated_deltanet_transition():
+    """A gate per (token, head), without the d_k axis, through the oracle's
+    batched layout equals the Gated DeltaNet transition written as a matrix
+    product, S_t = alpha_t (I - beta_t k k^T) S_{t-1} + beta_t k v^T ("Kimi
+    Unveils ...", 3), for every (b, h) chain."""
+    rng = np.random.default_rng(9)
+    B, T, H, dk, dv = 2, 23, 3, 5, 4
+    q = rng.standard_normal((B, T, H, dk)).astype(np.float32)
+    k = rng.standard_normal((B, T, H, dk)).astype(np.float32)
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((B, T, H, dv)).astype(np.float32)
+    g = (-np.exp(rng.standard_normal((B, T, H)) - 2.0)).astype(np.float32)
+    beta = (1 / (1 + np.exp(-rng.standard_normal((B, T, H))))).astype(np.float32)
+    S0 = 0.2 * rng.standard_normal((B, H, dk, dv))
+    out, Sf = oracle.forward_dense(q, k, v, g, beta, S0=S0, scale=0.7, threads=2)
+    for b in range(B):
+        for h in range(H):
+            S = S0[b, h].copy()
+            for t in range(T):
+                kk = k[b, t, h].astype(np.float64)
+                a = np.exp(np.float64(g[b, t, h]))
+                bt = np.float64(beta[b, t, h])
+                S = a * (np.eye(dk) - bt * np.outer(kk, kk)) @ S + bt * np.outer(kk, v[b, t, h])
+                np.testing.assert_allclose(out[b, t, h], S.T @ (0.7 * q[b, t, h].astype(np.float64)),
+                                           atol=1e-12)
+            np.testing.assert_allclose(Sf[b, h], S, atol=1e-12)
+
+
 def test_no_delta_alpha_one_is_linear_attention():
     """o_t = s * sum_{i<=t} <k_i, q_t> v_i  ("Kimi Unveils ...", 1.1)."""
     rng = np.random.default_rng(3)
