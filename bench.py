@@ -57,7 +57,7 @@ def prefill_alg_flops(B, T, H, dk, dv, C=64):
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_FILE = os.path.join(HERE, "profiles",
-                            "traffic_chunk_b8_h32_t8192_decode_n256_h32_recurrent_n256_h32.md")
+                            "traffic_chunk_kda_gdn_b8_h32_t8192_decode_recurrent_n256_h32.md")
 CSRC = os.path.join(HERE, "gated_delta_rule_06_amd", "csrc")
 
 
@@ -344,6 +344,7 @@ def main():
                         "tokens_per_s": tokens / gdn_wall, "ms_per_step": gdn_wall * 1e3,
                         "roofline": {"bound": "hbm", "achieved": gdn_gbs, "peak": HBM_PEAK_GBS,
                                      "unit": "GB/s", "frac": gdn_gbs / HBM_PEAK_GBS,
+                                     "traffic": measured_traffic("gdn", "chunk.hip"),
                                      "kernel": "chunk_fwd_kernel<128,128,bf16,scalar gate>",
                                      "alg_bytes_per_launch": gdn_b, "avg_launch_ms": gdn_ms}},
         "recurrent": {"workload": "multi_token_decode_n256_h32_len1to8",
