@@ -26,6 +26,12 @@ _CFLAGS = ["-O2", "-ffp-contract=off", "-fno-fast-math", "-std=c99", "-D_POSIX_C
 IO_F32 = 0
 IO_BF16 = 1
 
+# input transforms (kda_ref.c): L2-normalise q and k, beta = sigmoid(beta),
+# log alpha = -5 sigmoid(exp(A_log[h]) (g + gate_bias[h, i]))
+L2NORM = 1
+BETA_SIGMOID = 2
+GATE = 4
+
 _lib = None
 
 
@@ -43,12 +49,13 @@ def _load():
     if _lib is None:
         build()
         lib = ctypes.CDLL(_LIB)
-        f = lib.kdaref_forward
+        f = lib.kdaref_forward_ex
         f.restype = ctypes.c_int
         f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                       ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                      ctypes.c_double, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
+                      ctypes.c_double, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
         _lib = lib
     return _lib
@@ -76,7 +83,7 @@ def default_threads() -> int:
 
 
 def forward(q, k, v, g, beta, S0=None, scale=None, cu_seqlens=None, chains=None,
-            delta_rule=True, threads=None):
+            delta_rule=True, threads=None, flags=0, A_log=None, gate_bias=None):
     """Run the fp64 recurrence.
 
     Batched layout (``cu_seqlens is None``): q, k, g are [B, T, H, dk]; v is
@@ -93,6 +100,10 @@ def forward(q, k, v, g, beta, S0=None, scale=None, cu_seqlens=None, chains=None,
     one gate per (token, head), the same for every key channel; it is
     broadcast over dk (a copy, no arithmetic) and the recurrence is unchanged.
 
+    ``flags`` (L2NORM | BETA_SIGMOID | GATE) applies kda_ref.c's input
+    transforms to the raw q, k, beta and g; ``A_log`` [H] and ``gate_bias``
+    ([H, dk], or [H] with a per-head gate, broadcast like g) go with GATE.
+
     ``chains``: iterable of (n, h) pairs (or flat ids n*H+h) to compute;
     default all.  Returns (outs, S_final) where ``outs[c]`` is the fp64
     [len_c, dv] output of chain c and ``S_final`` is [n_chains, dk, dv] fp64.
@@ -106,6 +117,13 @@ def forward(q, k, v, g, beta, S0=None, scale=None, cu_seqlens=None, chains=None,
     g = np.asarray(g, dtype=np.float32)
     if g.ndim == q.ndim - 1:
         g = np.broadcast_to(g[..., None], q.shape)
+    a_log = None if A_log is None else np.ascontiguousarray(A_log, dtype=np.float32)
+    gbias = None
+    if gate_bias is not None:
+        gbias = np.asarray(gate_bias, dtype=np.float32)
+        if gbias.ndim == 1:
+            gbias = np.broadcast_to(gbias[:, None], (gbias.shape[0], q.shape[-1]))
+        gbias = np.ascontiguousarray(gbias)
     g = np.ascontiguousarray(g, dtype=np.float32)
     beta = np.ascontiguousarray(beta, dtype=np.float32)
     if cu_seqlens is None:
@@ -131,10 +149,10 @@ def forward(q, k, v, g, beta, S0=None, scale=None, cu_seqlens=None, chains=None,
     total = int(sum(lens[int(c) // H] for c in ids))
     out = np.zeros((max(total, 1), dv), dtype=np.float64)
     S_final = np.zeros((len(ids), dk, dv), dtype=np.float64)
-    rc = lib.kdaref_forward(_ptr(q), _ptr(k), _ptr(v), dt, _ptr(g), _ptr(beta), _ptr(s0), _ptr(cu),
-                            B, T, H, dk, dv, float(scale), 1 if delta_rule else 0,
-                            _ptr(ids), len(ids), _ptr(out), _ptr(S_final),
-                            int(threads or default_threads()))
+    rc = lib.kdaref_forward_ex(_ptr(q), _ptr(k), _ptr(v), dt, _ptr(g), _ptr(beta), _ptr(s0),
+                               _ptr(cu), B, T, H, dk, dv, float(scale), 1 if delta_rule else 0,
+                               int(flags), _ptr(a_log), _ptr(gbias), _ptr(ids), len(ids),
+                               _ptr(out), _ptr(S_final), int(threads or default_threads()))
     if rc != 0:
         raise ValueError("kdaref_forward rejected its arguments")
     outs = []
@@ -147,13 +165,14 @@ def forward(q, k, v, g, beta, S0=None, scale=None, cu_seqlens=None, chains=None,
 
 
 def forward_dense(q, k, v, g, beta, S0=None, scale=None, cu_seqlens=None, delta_rule=True,
-                  threads=None):
+                  threads=None, flags=0, A_log=None, gate_bias=None):
     """All chains, reassembled into the input layout: returns (out, S_final)
     with out shaped like v (fp64) and S_final [N, H, dk, dv] (fp64)."""
     q_ = np.asarray(q)
     H = q_.shape[-2]
     outs, S_final = forward(q, k, v, g, beta, S0=S0, scale=scale, cu_seqlens=cu_seqlens,
-                            delta_rule=delta_rule, threads=threads)
+                            delta_rule=delta_rule, threads=threads, flags=flags, A_log=A_log,
+                            gate_bias=gate_bias)
     v_ = np.asarray(v)
     dv = v_.shape[-1]
     dk = q_.shape[-1]

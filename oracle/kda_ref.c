@@ -27,6 +27,18 @@
  *  - "Linear Attention, From Scratch to Kimi 3", section 9 (cu_seqlens): packed
  *    requests never share recurrent state.
  *
+ * Optional input transforms (kdaref_forward_ex, flags), each applied to the
+ * raw inputs of a token before the step, in fp64:
+ *  - KDAREF_L2NORM: q <- q / sqrt(sum q^2 + 1e-6), the same for k, per (token,
+ *    head) vector ("Linear Attention, From Scratch to Kimi 3", section 7: each
+ *    head's q and k are L2-normalised before the recurrence);
+ *  - KDAREF_BETA_SIGMOID: beta <- 1 / (1 + exp(-beta)) (same page, section 6:
+ *    the update strength is a sigmoid of a raw projection);
+ *  - KDAREF_GATE: g <- -5 sigmoid(exp(A_log[h]) (g + bias[h, i])) (same page,
+ *    section 6: a sigmoid scaled by -5 gives a log-retention in (-5, 0), from
+ *    the projection, a per-channel bias and one sensitivity per head; the
+ *    composition inside the sigmoid is this implementation's reading).
+ *
  * With delta_rule == 0 the correction is replaced by e = beta_t v_t, i.e. the
  * delta term is removed.  With alpha == 1 and beta == 1 that is plain causal
  * linear attention ("Kimi Unveils ...", section 1.1).  This mode exists only
@@ -44,6 +56,11 @@
 
 #define KDAREF_IO_F32 0
 #define KDAREF_IO_BF16 1
+
+#define KDAREF_L2NORM 1
+#define KDAREF_BETA_SIGMOID 2
+#define KDAREF_GATE 4
+#define KDAREF_NORM_EPS 1e-6
 
 /* Exact bf16 -> double: a bf16 value is the top 16 bits of an IEEE binary32. */
 static double bf16_bits_to_double(uint16_t h) {
@@ -67,6 +84,8 @@ typedef struct {
   int B, T, H, dk, dv;
   double scale;
   int delta_rule;
+  int flags;
+  const float *A_log, *gate_bias; /* [H], [H, dk] (NULL: zero bias) */
   const int32_t* chains;
   const int64_t* out_offset; /* first output row of each selected chain */
   int n_chains;
@@ -109,13 +128,32 @@ static void run_chain(const job_t* jb, int ci) {
     const size_t tok = (size_t)(row0 + t);
     const size_t kbase = (tok * H + h) * (size_t)dk;
     const size_t vbase = (tok * H + h) * (size_t)dv;
+    double nk = 1.0, nq = 1.0;  /* 1 / L2 norms (KDAREF_L2NORM) */
+    if (jb->flags & KDAREF_L2NORM) {
+      double sk = 0.0, sq = 0.0;
+      for (int i = 0; i < dk; ++i) {
+        const double x = load_io(jb->k, jb->dtype, kbase + i);
+        const double y = load_io(jb->q, jb->dtype, kbase + i);
+        sk += x * x;
+        sq += y * y;
+      }
+      nk = 1.0 / sqrt(sk + KDAREF_NORM_EPS);
+      nq = 1.0 / sqrt(sq + KDAREF_NORM_EPS);
+    }
     for (int i = 0; i < dk; ++i) {
-      kt[i] = load_io(jb->k, jb->dtype, kbase + i);
-      qt[i] = jb->scale * load_io(jb->q, jb->dtype, kbase + i);
-      a[i] = exp((double)jb->g[kbase + i]);
+      kt[i] = load_io(jb->k, jb->dtype, kbase + i) * nk;
+      qt[i] = jb->scale * (load_io(jb->q, jb->dtype, kbase + i) * nq);
+      double gi = (double)jb->g[kbase + i];
+      if (jb->flags & KDAREF_GATE) {
+        const double bias = jb->gate_bias ? (double)jb->gate_bias[(size_t)h * dk + i] : 0.0;
+        const double x = exp((double)jb->A_log[h]) * (gi + bias);
+        gi = -5.0 / (1.0 + exp(-x));
+      }
+      a[i] = exp(gi);
     }
     for (int j = 0; j < dv; ++j) vt[j] = load_io(jb->v, jb->dtype, vbase + j);
-    const double b = (double)jb->beta[tok * H + h];
+    double b = (double)jb->beta[tok * H + h];
+    if (jb->flags & KDAREF_BETA_SIGMOID) b = 1.0 / (1.0 + exp(-b));
 
     /* forget: Sbar = Diag(a) S (key rows) */
     for (int i = 0; i < dk; ++i)
@@ -167,14 +205,20 @@ static void* worker(void* arg) {
  *            each chain's [len, dv] outputs (fp64)
  *  S_final   [n_chains, dk, dv] fp64 or NULL
  *  threads   worker threads over independent chains (<= 0: 1)
+ *  flags     KDAREF_* input transforms (0: none); g and beta then hold the
+ *            raw projections they transform
+ *  A_log     [H] fp32, required with KDAREF_GATE
+ *  gate_bias [H, dk] fp32 or NULL (zero), with KDAREF_GATE
  * Returns 0, or -1 on bad arguments.
  */
-int kdaref_forward(const void* q, const void* k, const void* v, int dtype,
-                   const float* g, const float* beta, const double* S0,
-                   const int32_t* cu_seqlens, int B, int T, int H, int dk, int dv,
-                   double scale, int delta_rule, const int32_t* chains, int n_chains,
-                   double* out, double* S_final, int threads) {
+int kdaref_forward_ex(const void* q, const void* k, const void* v, int dtype,
+                      const float* g, const float* beta, const double* S0,
+                      const int32_t* cu_seqlens, int B, int T, int H, int dk, int dv,
+                      double scale, int delta_rule, int flags, const float* A_log,
+                      const float* gate_bias, const int32_t* chains, int n_chains, double* out,
+                      double* S_final, int threads) {
   if (!q || !k || !v || !g || !beta || !chains || !out) return -1;
+  if ((flags & KDAREF_GATE) && !A_log) return -1;
   if (B < 0 || T < 0 || H <= 0 || dk <= 0 || dv <= 0 || n_chains < 0) return -1;
   if (dtype != KDAREF_IO_F32 && dtype != KDAREF_IO_BF16) return -1;
   job_t jb;
@@ -182,6 +226,7 @@ int kdaref_forward(const void* q, const void* k, const void* v, int dtype,
   jb.q = q; jb.k = k; jb.v = v; jb.dtype = dtype; jb.g = g; jb.beta = beta; jb.S0 = S0;
   jb.cu_seqlens = cu_seqlens; jb.B = B; jb.T = T; jb.H = H; jb.dk = dk; jb.dv = dv;
   jb.scale = scale; jb.delta_rule = delta_rule; jb.chains = chains; jb.n_chains = n_chains;
+  jb.flags = flags; jb.A_log = A_log; jb.gate_bias = gate_bias;
   jb.out = out; jb.S_final = S_final;
   int64_t* off = (int64_t*)malloc(sizeof(int64_t) * (size_t)(n_chains > 0 ? n_chains : 1));
   int64_t acc = 0;
@@ -202,4 +247,14 @@ int kdaref_forward(const void* q, const void* k, const void* v, int dtype,
   pthread_mutex_destroy(&jb.lock);
   free(off);
   return 0;
+}
+
+/* kdaref_forward: kdaref_forward_ex without input transforms. */
+int kdaref_forward(const void* q, const void* k, const void* v, int dtype,
+                   const float* g, const float* beta, const double* S0,
+                   const int32_t* cu_seqlens, int B, int T, int H, int dk, int dv,
+                   double scale, int delta_rule, const int32_t* chains, int n_chains,
+                   double* out, double* S_final, int threads) {
+  return kdaref_forward_ex(q, k, v, dtype, g, beta, S0, cu_seqlens, B, T, H, dk, dv, scale,
+                           delta_rule, 0, NULL, NULL, chains, n_chains, out, S_final, threads);
 }

@@ -373,3 +373,88 @@ def test_bf16_rounding_is_nearest_even():
     bits = bf16_bits_from_f32(x)
     back = (bits.astype(np.uint32) << 16).view(np.float32)
     np.testing.assert_array_equal(back, [1.0, 1.0 + 2 ** -6, -2.5, 1.0])
+
+
+# ---------------------------------------------------------------- input transforms
+
+def run1x(q, k, v, g, beta, S0=None, scale=1.0, flags=0, A_log=None, gate_bias=None):
+    """run1 with the oracle's input transforms (one head: A_log [1], bias [1, dk])."""
+    q = np.asarray(q, np.float32)[None, :, None, :]
+    k = np.asarray(k, np.float32)[None, :, None, :]
+    v = np.asarray(v, np.float32)[None, :, None, :]
+    g = np.asarray(g, np.float32)[None, :, None, :]
+    beta = np.asarray(beta, np.float32)[None, :, None]
+    s0 = None if S0 is None else np.asarray(S0, np.float64)[None, None]
+    outs, Sf = oracle.forward(q, k, v, g, beta, S0=s0, scale=scale, threads=1, flags=flags,
+                              A_log=A_log, gate_bias=gate_bias)
+    return outs[0], Sf[0]
+
+
+def test_l2norm_leaves_unit_vectors_and_removes_per_token_scale():
+    """In-op normalisation ("Linear Attention, From Scratch to Kimi 3", 7) is
+    an L2 normalisation per (token, head) vector: unit vectors pass unchanged
+    (up to the 1e-6 guard inside the square root), and any positive per-token
+    scale of q or k is removed (scales >= 1, where the guard is below 1e-6
+    of the squared norm)."""
+    rng = np.random.default_rng(11)
+    q, k, v, g, beta = rand_chain(rng, 30, 16, 8)        # unit-norm q and k
+    S0 = 0.2 * rng.standard_normal((16, 8))
+    o_ref, S_ref = run1(q, k, v, g, beta, S0=S0, scale=0.4)
+    o1, S1 = run1x(q, k, v, g, beta, S0=S0, scale=0.4, flags=oracle.L2NORM)
+    np.testing.assert_allclose(o1, o_ref, rtol=2e-6, atol=2e-7)
+    np.testing.assert_allclose(S1, S_ref, rtol=2e-6, atol=2e-7)
+    cq = np.float32(2.0) ** rng.integers(0, 4, size=(30, 1)).astype(np.float32)  # exact scales
+    ck = np.float32(2.0) ** rng.integers(0, 4, size=(30, 1)).astype(np.float32)
+    o2, S2 = run1x(q * cq, k * ck, v, g, beta, S0=S0, scale=0.4, flags=oracle.L2NORM)
+    np.testing.assert_allclose(o2, o1, rtol=1e-5, atol=1e-7)
+    np.testing.assert_allclose(S2, S1, rtol=1e-5, atol=1e-7)
+    # without the transform the scales matter
+    o3, _ = run1(q * cq, k * ck, v, g, beta, S0=S0, scale=0.4)
+    assert np.abs(o3 - o_ref).max() > 1e-2
+
+
+def test_beta_sigmoid_special_values():
+    """beta from a raw value through a sigmoid (same page, 6): 0 gives 1/2
+    exactly, large positive values a full overwrite (beta = 1), large negative
+    values no write at all (beta = 0)."""
+    rng = np.random.default_rng(12)
+    q, k, v, g, _ = rand_chain(rng, 25, 8, 6)
+    S0 = 0.3 * rng.standard_normal((8, 6))
+    for raw, beta in ((0.0, 0.5), (60.0, 1.0), (-60.0, 0.0)):
+        o1, S1 = run1x(q, k, v, g, np.full(25, raw), S0=S0, scale=0.5, flags=oracle.BETA_SIGMOID)
+        o2, S2 = run1(q, k, v, g, np.full(25, beta), S0=S0, scale=0.5)
+        np.testing.assert_allclose(o1, o2, rtol=1e-13, atol=1e-13)
+        np.testing.assert_allclose(S1, S2, rtol=1e-13, atol=1e-13)
+
+
+def test_gate_transform_special_values_and_range():
+    """log alpha = -5 sigmoid(exp(A_log) (g + bias)) (same page, 6; the
+    composition inside the sigmoid is a reading).  Fixed points: a projection
+    equal to -bias gives -2.5 whatever A_log; A_log -> -inf gives -2.5 whatever
+    g; saturation gives -5 and 0; and with beta = 0 the per-channel decay of a
+    whole chain stays inside (e^{-5T}, 1)."""
+    rng = np.random.default_rng(13)
+    T, dk, dv = 20, 8, 5
+    q, k, v, _, beta = rand_chain(rng, T, dk, dv)
+    S0 = 0.3 * rng.standard_normal((dk, dv))
+    bias = rng.standard_normal((1, dk)).astype(np.float32)
+    gate = oracle.GATE
+
+    def same(graw, a_log, b, g_eff):
+        o1, S1 = run1x(q, k, v, graw, beta, S0=S0, scale=0.5, flags=gate,
+                       A_log=np.array([a_log], np.float32), gate_bias=b)
+        o2, S2 = run1(q, k, v, g_eff, beta, S0=S0, scale=0.5)
+        np.testing.assert_allclose(o1, o2, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(S1, S2, rtol=1e-12, atol=1e-12)
+
+    same(np.broadcast_to(-bias, (T, dk)), 1.7, bias, np.full((T, dk), -2.5))
+    same(rng.standard_normal((T, dk)), -1e4, bias, np.full((T, dk), -2.5))
+    same(np.full((T, dk), 80.0), 0.0, None, np.full((T, dk), -5.0))
+    same(np.full((T, dk), -80.0), 0.0, None, np.zeros((T, dk)))
+    # range: beta = 0 leaves only the decay, S_T = prod_t alpha_t * S0 row-wise
+    graw = 3.0 * rng.standard_normal((T, dk))
+    _, S = run1x(q, k, v, graw, np.zeros(T), S0=S0, flags=gate,
+                 A_log=np.array([0.5], np.float32), gate_bias=bias)
+    ratio = S / S0
+    assert np.all(ratio < 1.0) and np.all(ratio > np.exp(-5.0 * T))
+    np.testing.assert_allclose(ratio, ratio[:, :1] * np.ones((1, dv)), rtol=1e-12)
