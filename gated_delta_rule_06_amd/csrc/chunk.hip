@@ -328,12 +328,14 @@ struct RawIo {
 // ============================================================ configuration
 // Four waves per workgroup; wave w owns value columns [w d_v/4, (w+1) d_v/4)
 // of the state for the whole sequence.
-template <int DK_, int DV_, class Io_, class Op_, int NW_ = 4, bool SG_ = false>
+template <int DK_, int DV_, class Io_, class Op_, int NW_ = 4, bool SG_ = false, bool FU_ = false>
 struct ChunkCfg {
   static constexpr int DK = DK_, DV = DV_;
   // SG: one gate per (token, head) shared by every key channel (Gated
   // DeltaNet); otherwise one per key channel (KDA)
   static constexpr bool SG = SG_;
+  // FU: the raw inputs pass through the transforms of a Prologue (common.h)
+  static constexpr bool FU = FU_;
   typedef Io_ Io;
   typedef Op_ Op;
   typedef typename Op::T T;
@@ -380,7 +382,11 @@ struct ChunkCfg {
   static constexpr int OFF_GL = OFF_SC + SZ_SC;
   static constexpr int OFF_BT = OFF_GL + DK * 4;          // beta of the chunk's tokens
   static constexpr int OFF_FL = OFF_BT + C * 4;
-  static constexpr int LDS_TOTAL = OFF_FL + 64;
+  // FU only: per-wave partial squared norms of q and k, [C][NW] each, and the
+  // head's gate biases [DK]
+  static constexpr int OFF_NM = OFF_FL + 64;
+  static constexpr int SZ_NM = FU ? 2 * C * NW * 4 + DK * 4 : 0;
+  static constexpr int LDS_TOTAL = OFF_NM + SZ_NM;
   static_assert(LDS_TOTAL <= 160 * 1024, "LDS budget");
   static_assert(OFF_KG % 16 == 0 && OFF_KI % 16 == 0 && OFF_RD % 16 == 0 && OFF_OS % 16 == 0 && OFF_FL % 16 == 0 &&
                 OFF_BV % 16 == 0 && OFF_AQ % 16 == 0 && OFF_RT % 16 == 0 && OFF_TD % 16 == 0 &&
@@ -477,10 +483,43 @@ struct ChunkKernel {
     if (PART & LOAD_V) r.beta = buf_load<float>(rb, o.beta);   // lane l: beta of token l
   }
 
+  // ---------------------------------------------------------------- norms (FU)
+  // Per-wave partial squared norms of the chunk's raw q and k rows: the CQ
+  // lanes that share a token add their channels, then one of them stores the
+  // wave's partial to NQ / NK [token][wave].
+  static __device__ __forceinline__ void norm_partials(const Raw& r, LDS char* smem) {
+    const int w = threadIdx.x >> 6, l = lane_fresh();
+    const int tg = l / CQ, cq = l % CQ;
+    LDS float* NQ = (LDS float*)(smem + Cfg::OFF_NM);
+    LDS float* NK = NQ + C * NW;
+#pragma unroll
+    for (int t = 0; t < TPL; ++t) {
+      float qv[CPL], kv[CPL];
+      r.q[t].unpack(qv);
+      r.k[t].unpack(kv);
+      float sq = 0.f, sk = 0.f;
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        sq += qv[c] * qv[c];
+        sk += kv[c] * kv[c];
+      }
+#pragma unroll
+      for (int d = 1; d < CQ; d <<= 1) {
+        sq += __shfl_xor(sq, d);
+        sk += __shfl_xor(sk, d);
+      }
+      if (cq == 0) {
+        NQ[(TPL * tg + t) * NW + w] = sq;
+        NK[(TPL * tg + t) * NW + w] = sk;
+      }
+    }
+  }
+
   // ---------------------------------------------------------------- prep
   // Cumulative decay and the five gate-scaled operands; returns the chunk's
   // guard flag (1 = some channel decays below KDA_GAMMA_MIN).
-  static __device__ __forceinline__ int prep(const Raw& r, LDS char* smem, float scale) {
+  static __device__ __forceinline__ int prep(const Raw& r, LDS char* smem, float scale,
+                                             const Prologue& pro, float ea, int clen) {
     const int w = threadIdx.x >> 6, l = lane_fresh();
     const int tg = l / CQ, cq = l % CQ;
     const int kc0 = w * (DK / NW) + CPL * cq;
@@ -495,7 +534,20 @@ struct ChunkKernel {
 
     // beta is applied to R and Y later, where it scales whole rows (R =
     // Diag(beta) strict_tril((k Gamma) KI^T), Ebar = Diag(beta)(v - (k Gamma) S))
-    if (w == 0) BT[l] = r.beta;                 // lane l holds beta of token l
+    if (w == 0) {                               // lane l holds beta of token l
+      BT[l] = (Cfg::FU && (pro.flags & PRO_BETA_SIGMOID)) ? sigmoid_f(r.beta) : r.beta;
+    }
+    // gate transform (FU): the raw gate through -5 sigmoid(exp(A_log) (g + bias)).
+    // Rows past the chunk's end read as zeros and must stay identity tokens
+    // (alpha = 1), so the transform leaves their gate at 0.
+    const bool xg = Cfg::FU && (pro.flags & PRO_GATE);
+    float gbias[CPL];
+    if (xg) {
+      const LDS float* GB = (const LDS float*)(smem + Cfg::OFF_NM + 2 * C * NW * 4);
+      const f32x4 b0 = *lds_ptr<const f32x4>(GB + kc0), b1 = *lds_ptr<const f32x4>(GB + kc0 + 4);
+      gbias[0] = b0[0]; gbias[1] = b0[1]; gbias[2] = b0[2]; gbias[3] = b0[3];
+      gbias[4] = b1[0]; gbias[5] = b1[1]; gbias[6] = b1[2]; gbias[7] = b1[3];
+    }
 
     float cp[TPL][CPL];   // in-lane running products of alpha over the lane's tokens
     float ex[CPL];        // product over the earlier token groups (exclusive prefix)
@@ -507,7 +559,8 @@ struct ChunkKernel {
       float ct[TPL];
 #pragma unroll
       for (int t = 0; t < TPL; ++t) {
-        const float a = __expf(r.gs[t]);
+        const bool real = TPL * tg + t < clen;
+        const float a = __expf(xg ? (real ? gate_logalpha(r.gs[t], ea, gbias[0]) : 0.f) : r.gs[t]);
         ct[t] = (t == 0) ? a : ct[t - 1] * a;
       }
       float x = ct[TPL - 1];
@@ -535,7 +588,9 @@ struct ChunkKernel {
       for (int t = 0; t < TPL; ++t)
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
-          const float a = __expf(__uint_as_float(r.g[t].word(c)));
+          const float gr = __uint_as_float(r.g[t].word(c));
+          const bool real = TPL * tg + t < clen;
+          const float a = __expf(xg ? (real ? gate_logalpha(gr, ea, gbias[c]) : 0.f) : gr);
           cp[t][c] = (t == 0) ? a : cp[t - 1][c] * a;
         }
       // product over the TG token groups: ex = exclusive prefix, Gamma_L -> GL
@@ -607,6 +662,25 @@ struct ChunkKernel {
       float qv[CPL], kv[CPL];
       r.q[t].unpack(qv);
       r.k[t].unpack(kv);
+      if (Cfg::FU && (pro.flags & PRO_L2NORM)) {
+        // the token's squared norms: the sum of the waves' partials
+        const LDS float* NQ = (const LDS float*)(smem + Cfg::OFF_NM) + i * NW;
+        const LDS float* NK = NQ + C * NW;
+        float sq = 0.f, sk = 0.f;
+#pragma unroll
+        for (int j = 0; j < NW; j += 4) {
+          const f32x4 a = *lds_ptr<const f32x4>(NQ + j), b = *lds_ptr<const f32x4>(NK + j);
+          sq += (a[0] + a[1]) + (a[2] + a[3]);
+          sk += (b[0] + b[1]) + (b[2] + b[3]);
+        }
+        const float rq = __builtin_amdgcn_rsqf(sq + PRO_NORM_EPS);
+        const float rk = __builtin_amdgcn_rsqf(sk + PRO_NORM_EPS);
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+          qv[c] *= rq;
+          kv[c] *= rk;
+        }
+      }
       float qg[CPL], kg[CPL];
 #pragma unroll
       for (int c = 0; c < CPL; ++c) {
@@ -949,16 +1023,20 @@ struct ChunkKernel {
                                                          const void* k, const void* v,
                                                          const float* g, const float* beta,
                                                          void* out, size_t row_base, int H,
-                                                         int h, int clen, float scale) {
+                                                         int h, int clen, float scale,
+                                                         const Prologue& pro, float ea) {
     const int w = threadIdx.x >> 6, l = lane_fresh();
     const int n = l & 15, g4 = 4 * (l >> 4);
     const int vw0 = w * VW;
+    const bool xg = Cfg::FU && (pro.flags & PRO_GATE);
+    const bool xn = Cfg::FU && (pro.flags & PRO_L2NORM);
     for (int t = 0; t < clen; ++t) {
       const size_t row = (row_base + t) * H + h;
       // forget, then the prediction Sbar^T k
       float p[NVT];
 #pragma unroll
       for (int nt = 0; nt < NVT; ++nt) p[nt] = 0.f;
+      float k2 = 0.f;
 #pragma unroll
       for (int mt = 0; mt < MTK; ++mt) {
         const size_t ci = row * DK + 16 * mt + g4;
@@ -970,7 +1048,14 @@ struct ChunkKernel {
         const f32x4 kv = Io::load4(k, ci);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float a = __expf(gv[r]);
+          float gr = gv[r];
+          if (xg) {
+            const float bias =
+                pro.bias ? pro.bias[Cfg::SG ? h : h * DK + 16 * mt + g4 + r] : 0.f;
+            gr = gate_logalpha(gr, ea, bias);
+          }
+          const float a = __expf(gr);
+          if (Cfg::FU) k2 += kv[r] * kv[r];
 #pragma unroll
           for (int nt = 0; nt < NVT; ++nt) {
             S[mt][nt][r] *= a;
@@ -978,35 +1063,52 @@ struct ChunkKernel {
           }
         }
       }
-      const float b = beta[row];
+      float b = beta[row];
+      if (Cfg::FU && (pro.flags & PRO_BETA_SIGMOID)) b = sigmoid_f(b);
+      // L2 norm of k (FU): the sums used the raw k; scale afterwards
+      float rk = 1.f;
+      if (xn) {
+        k2 += __shfl_xor(k2, 16);
+        k2 += __shfl_xor(k2, 32);
+        rk = __builtin_amdgcn_rsqf(k2 + PRO_NORM_EPS);
+      }
 #pragma unroll
       for (int nt = 0; nt < NVT; ++nt) {
         p[nt] += __shfl_xor(p[nt], 16);
         p[nt] += __shfl_xor(p[nt], 32);
-        p[nt] = b * (Io::load(v, row * DV + vw0 + 16 * nt + n) - p[nt]);   // e
+        p[nt] = b * (Io::load(v, row * DV + vw0 + 16 * nt + n) - p[nt] * rk) * rk;  // e / |k|
       }
       // write k e^T, then read with s q
       float o[NVT];
 #pragma unroll
       for (int nt = 0; nt < NVT; ++nt) o[nt] = 0.f;
+      float q2 = 0.f;
 #pragma unroll
       for (int mt = 0; mt < MTK; ++mt) {
         const size_t ci = row * DK + 16 * mt + g4;
         const f32x4 kv = Io::load4(k, ci);
         const f32x4 qv = Io::load4(q, ci);
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
+        for (int r = 0; r < 4; ++r) {
+          if (Cfg::FU) q2 += qv[r] * qv[r];
 #pragma unroll
           for (int nt = 0; nt < NVT; ++nt) {
             S[mt][nt][r] += kv[r] * p[nt];
             o[nt] += S[mt][nt][r] * (scale * qv[r]);
           }
+        }
+      }
+      float rq = 1.f;
+      if (xn) {
+        q2 += __shfl_xor(q2, 16);
+        q2 += __shfl_xor(q2, 32);
+        rq = __builtin_amdgcn_rsqf(q2 + PRO_NORM_EPS);
       }
 #pragma unroll
       for (int nt = 0; nt < NVT; ++nt) {
         o[nt] += __shfl_xor(o[nt], 16);
         o[nt] += __shfl_xor(o[nt], 32);
-        if (l < 16) Io::store(out, row * DV + vw0 + 16 * nt + n, o[nt]);
+        if (l < 16) Io::store(out, row * DV + vw0 + 16 * nt + n, o[nt] * rq);
       }
     }
   }
@@ -1015,7 +1117,8 @@ struct ChunkKernel {
   static __device__ __forceinline__ void run(const void* q, const void* k, const void* v,
                                              const float* g, const float* beta, const float* S0,
                                              void* out, float* S_final, size_t row_base, int len,
-                                             int H, int h, size_t chain, float scale) {
+                                             int H, int h, size_t chain, float scale,
+                                             const Prologue& pro) {
     extern __shared__ __attribute__((aligned(16))) char smem_[];
     LDS char* smem = (LDS char*)smem_;
     const int w = threadIdx.x >> 6;
@@ -1027,6 +1130,15 @@ struct ChunkKernel {
     {
       LDS T* AQ = (LDS T*)(smem + Cfg::OFF_AQ);
       for (int i = threadIdx.x; i < C * Cfg::LD_64; i += Cfg::NTHREADS) AQ[i] = Op::cvt(0.f);
+    }
+    // FU: the head's exp(A_log) and gate biases (LDS, read by prep)
+    float ea = 1.f;
+    if (Cfg::FU && (pro.flags & PRO_GATE)) {
+      ea = __expf(pro.A_log[h]);
+      LDS float* GB = (LDS float*)(smem + Cfg::OFF_NM + 2 * C * NW * 4);
+      for (int i = threadIdx.x; i < DK; i += Cfg::NTHREADS)
+        GB[i] = pro.bias ? pro.bias[Cfg::SG ? h : h * DK + i] : 0.f;
+      __syncthreads();
     }
     // state tiles: S[16mt + 4g + r][vw0 + 16nt + n]
     f32x4 S[MTK][NVT];
@@ -1058,8 +1170,16 @@ struct ChunkKernel {
       const bool more = c0 + C < len;
       const int nlen = !more ? 0 : ((len - c0 - C) < C ? (len - c0 - C) : C);
       const size_t next = more ? row_base + c0 + C : row_base;
-      const int bad = prep(raw, smem, scale);
-      if (lane_fresh() == 0) FL[w] = __any(bad) ? 1 : 0;
+      if (Cfg::FU && (pro.flags & PRO_L2NORM)) {
+        // the chunk's norms need every wave's channels: one more barrier
+        norm_partials(raw, smem);
+        __syncthreads();
+      }
+      const int bad = prep(raw, smem, scale, pro, ea, clen);
+      // the vote runs in every lane: inside the lane-0 branch it would only
+      // see lane 0's flag (the scan path sets it in other lanes)
+      const int wave_bad = __any(bad);
+      if (lane_fresh() == 0) FL[w] = wave_bad ? 1 : 0;
       compiler_fence();
       load_raw<LOAD_G>(raw, offs, q, k, v, g, beta, next, H, h, nlen);
       __syncthreads();                                           // B1
@@ -1103,7 +1223,7 @@ struct ChunkKernel {
         __syncthreads();                                         // B2
         scan_step(smem, S, Y, O, out, row_base + c0, H, h, clen);
       } else {
-        recurrent_chunk(S, q, k, v, g, beta, out, row_base + c0, H, h, clen, scale);
+        recurrent_chunk(S, q, k, v, g, beta, out, row_base + c0, H, h, clen, scale, pro, ea);
         load_raw<LOAD_Q | LOAD_K | LOAD_V>(raw, offs, q, k, v, g, beta, next, H, h, nlen);
         __syncthreads();                                         // LDS reuse
       }
@@ -1126,30 +1246,30 @@ template <class Cfg>
 __global__ __launch_bounds__(Cfg::NTHREADS, 1) void chunk_fwd_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, const float* S0, void* out,
-    float* S_final, int T, int H, float scale) {
+    float* S_final, int T, int H, float scale, Prologue pro) {
   const int chain = blockIdx.x;   // b * H + h
   const int b = chain / H, h = chain % H;
   ChunkKernel<Cfg>::run(q, k, v, g, beta, S0, out, S_final, (size_t)b * T, T, H, h,
-                        (size_t)chain, scale);
+                        (size_t)chain, scale, pro);
 }
 
 template <class Cfg>
 __global__ __launch_bounds__(Cfg::NTHREADS, 1) void chunk_fwd_varlen_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, const float* S0, void* out,
-    float* S_final, const int32_t* __restrict__ cu_seqlens, int H, float scale) {
+    float* S_final, const int32_t* __restrict__ cu_seqlens, int H, float scale, Prologue pro) {
   const int chain = blockIdx.x;   // n * H + h
   const int n = chain / H, h = chain % H;
   const int b0 = cu_seqlens[n], b1 = cu_seqlens[n + 1];
   ChunkKernel<Cfg>::run(q, k, v, g, beta, S0, out, S_final, (size_t)b0, b1 - b0, H, h,
-                        (size_t)chain, scale);
+                        (size_t)chain, scale, pro);
 }
 
 template <class Cfg>
 static hipError_t launch_chunk_t(const void* q, const void* k, const void* v, const float* g,
                                  const float* beta, const float* S0, void* out, float* S_final,
                                  const int32_t* cu, int n_seq, int T, int H, float scale,
-                                 hipStream_t stream) {
+                                 const Prologue& pro, hipStream_t stream) {
   const int bytes = Cfg::LDS_TOTAL;
   if (cu) {
     auto kern = chunk_fwd_varlen_kernel<Cfg>;
@@ -1157,14 +1277,14 @@ static hipError_t launch_chunk_t(const void* q, const void* k, const void* v, co
                                        hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3(n_seq * H), dim3(Cfg::NTHREADS), bytes, stream, q, k, v, g,
-                       beta, S0, out, S_final, cu, H, scale);
+                       beta, S0, out, S_final, cu, H, scale, pro);
   } else {
     auto kern = chunk_fwd_kernel<Cfg>;
     hipError_t e = hipFuncSetAttribute((const void*)kern,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3(n_seq * H), dim3(Cfg::NTHREADS), bytes, stream, q, k, v, g,
-                       beta, S0, out, S_final, T, H, scale);
+                       beta, S0, out, S_final, T, H, scale, pro);
   }
   return hipGetLastError();
 }
@@ -1179,13 +1299,19 @@ bool chunk_supported(int dk, int dv, bool bf16) {
 hipError_t launch_chunk(const void* q, const void* k, const void* v, const float* g,
                         const float* beta, const float* S0, void* out, float* S_final,
                         const int32_t* cu_seqlens, int n_seq, int T, int H, int dk, int dv,
-                        float scale, bool bf16, bool scalar_gate, hipStream_t stream) {
-#define KDA_CH(DK, DV, IO, OP, NWV)                                                          \
-  return scalar_gate                                                                        \
-             ? launch_chunk_t<ChunkCfg<DK, DV, IO, OP, NWV, true>>(                         \
-                   q, k, v, g, beta, S0, out, S_final, cu_seqlens, n_seq, T, H, scale, stream) \
-             : launch_chunk_t<ChunkCfg<DK, DV, IO, OP, NWV, false>>(                        \
-                   q, k, v, g, beta, S0, out, S_final, cu_seqlens, n_seq, T, H, scale, stream);
+                        float scale, bool bf16, bool scalar_gate, const Prologue& pro,
+                        hipStream_t stream) {
+  const bool fu = pro.flags != 0;
+#define KDA_CH1(DK, DV, IO, OP, NWV, SG, FU)                                                 \
+  return launch_chunk_t<ChunkCfg<DK, DV, IO, OP, NWV, SG, FU>>(                              \
+      q, k, v, g, beta, S0, out, S_final, cu_seqlens, n_seq, T, H, scale, pro, stream);
+#define KDA_CH(DK, DV, IO, OP, NWV)                                       \
+  if (scalar_gate) {                                                      \
+    if (fu) { KDA_CH1(DK, DV, IO, OP, NWV, true, true) }                  \
+    KDA_CH1(DK, DV, IO, OP, NWV, true, false)                             \
+  }                                                                       \
+  if (fu) { KDA_CH1(DK, DV, IO, OP, NWV, false, true) }                   \
+  KDA_CH1(DK, DV, IO, OP, NWV, false, false)
   // d_v = 128 runs 8 waves (two per SIMD, 16 value columns each); d_v = 64
   // keeps 4 (value tiles are 16 columns wide).
   if (bf16) {
@@ -1197,6 +1323,7 @@ hipError_t launch_chunk(const void* q, const void* k, const void* v, const float
     if (dk == 64 && dv == 64) { KDA_CH(64, 64, IoF32, OpF32, 4) }
   }
 #undef KDA_CH
+#undef KDA_CH1
   return hipErrorInvalidValue;
 }
 

@@ -86,4 +86,29 @@ struct IoBf16 {
   }
 };
 
+// ---------------------------------------------------------------- input transforms
+// Optional transforms of a token's raw inputs, applied in the kernels before
+// the step ("Linear Attention, From Scratch to Kimi 3", sections 6 and 7):
+//  PRO_L2NORM:       q, k <- x / sqrt(sum x^2 + PRO_NORM_EPS) per (token, head)
+//  PRO_BETA_SIGMOID: beta <- sigmoid(beta)
+//  PRO_GATE:         g <- -5 sigmoid(exp(A_log[h]) (g + bias)), bias per key
+//                    channel [H, d_k] (per head [H] for Gated DeltaNet), or 0
+enum : uint32_t { PRO_L2NORM = 1u, PRO_BETA_SIGMOID = 2u, PRO_GATE = 4u };
+constexpr float PRO_NORM_EPS = 1e-6f;
+
+struct Prologue {
+  uint32_t flags;
+  const float* A_log;
+  const float* bias;
+};
+
+__device__ __forceinline__ float sigmoid_f(float x) {
+  return __builtin_amdgcn_rcpf(1.f + __expf(-x));
+}
+
+// log alpha from the raw gate g, the head's exp(A_log) and the channel's bias
+__device__ __forceinline__ float gate_logalpha(float g, float ea, float b) {
+  return -5.f * sigmoid_f(ea * (g + b));
+}
+
 }  // namespace kda

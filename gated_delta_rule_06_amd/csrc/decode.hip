@@ -23,11 +23,12 @@ namespace kda {
 
 // SG: one gate per (sequence, head) for every key row (Gated DeltaNet: log_alpha
 // is [N, H]); otherwise one per key row (KDA: [N, H, d_k]).
-template <int DK, int DV, class Io, bool SG>
+// FU: the raw inputs pass through the transforms of `pro` (common.h) first.
+template <int DK, int DV, class Io, bool SG, bool FU>
 __global__ __launch_bounds__(256) void decode_step_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, float* __restrict__ S,
-    void* __restrict__ out, float scale) {
+    void* __restrict__ out, float scale, Prologue pro, int H) {
   constexpr int CW = 64;          // value columns per workgroup
   constexpr int NSPLIT = DV / CW;
   constexpr int TPR = CW / 4;     // threads per state row
@@ -44,7 +45,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
   __shared__ __attribute__((aligned(16))) float s_k[DK], s_q[DK], s_a[DK];
   __shared__ __attribute__((aligned(16))) float s_p[RG][CW], s_r[RG][CW];
   __shared__ __attribute__((aligned(16))) float s_e[CW];
-  __shared__ float s_kq[4];
+  __shared__ float s_kq[4], s_k2[4], s_q2[4];
 
   float* Sh = S + (size_t)head * DK * DV + c0;
   f32x4 st[RPT];
@@ -54,19 +55,44 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
         reinterpret_cast<const f32x4*>(Sh + (size_t)(rg + RG * m) * DV) + cg);
 
   // stage this head's k, q and retention factors
-  float kq_part = 0.f;
+  float kq_part = 0.f, k2_part = 0.f, q2_part = 0.f;
   if (t < DK) {
     const size_t i = (size_t)head * DK + t;
     const float kk = Io::load(k, i), qq = Io::load(q, i);
     s_k[t] = kk;
     s_q[t] = qq;
-    s_a[t] = __expf(SG ? g[head] : g[i]);
+    float gi = SG ? g[head] : g[i];
+    if (FU && (pro.flags & PRO_GATE)) {
+      const int hh = head % H;
+      const float b = pro.bias ? (SG ? pro.bias[hh] : pro.bias[hh * DK + t]) : 0.f;
+      gi = gate_logalpha(gi, __expf(pro.A_log[hh]), b);
+    }
+    s_a[t] = __expf(gi);
     kq_part = kk * qq;
+    k2_part = kk * kk;
+    q2_part = qq * qq;
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) kq_part += __shfl_xor(kq_part, off);
   if ((t & 63) == 0) s_kq[t >> 6] = kq_part;
+  if (FU && (pro.flags & PRO_L2NORM)) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      k2_part += __shfl_xor(k2_part, off);
+      q2_part += __shfl_xor(q2_part, off);
+    }
+    if ((t & 63) == 0) {
+      s_k2[t >> 6] = k2_part;
+      s_q2[t >> 6] = q2_part;
+    }
+  }
   __syncthreads();
+  // L2 norms (FU): the reductions use the raw q and k and are scaled after
+  float rk = 1.f, rq = 1.f;
+  if (FU && (pro.flags & PRO_L2NORM)) {
+    rk = __builtin_amdgcn_rsqf(s_k2[0] + s_k2[1] + s_k2[2] + s_k2[3] + PRO_NORM_EPS);
+    rq = __builtin_amdgcn_rsqf(s_q2[0] + s_q2[1] + s_q2[2] + s_q2[3] + PRO_NORM_EPS);
+  }
 
   // forget (decay key rows), then partial prediction and read reductions
   f32x4 p = {0.f, 0.f, 0.f, 0.f}, r = {0.f, 0.f, 0.f, 0.f};
@@ -89,11 +115,12 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
       pt += s_p[j][t];
       rt += s_r[j][t];
     }
-    const float kq = s_kq[0] + s_kq[1] + s_kq[2] + s_kq[3];
-    const float b = beta[head];
-    const float e = b * (Io::load(v, (size_t)head * DV + c0 + t) - pt);
-    s_e[t] = e;
-    Io::store(out, (size_t)head * DV + c0 + t, scale * (rt + kq * e));
+    const float kq = (s_kq[0] + s_kq[1] + s_kq[2] + s_kq[3]) * (rk * rq);
+    float b = beta[head];
+    if (FU && (pro.flags & PRO_BETA_SIGMOID)) b = sigmoid_f(b);
+    const float e = b * (Io::load(v, (size_t)head * DV + c0 + t) - pt * rk);
+    s_e[t] = e * rk;                     // the write uses the raw k: k e^T / |k|
+    Io::store(out, (size_t)head * DV + c0 + t, scale * (rt * rq + kq * e));
   }
   __syncthreads();
 
@@ -107,28 +134,40 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
   }
 }
 
+template <int DK, int DV, class Io, bool SG, bool FU>
+static void launch_dec_k(const void* q, const void* k, const void* v, const float* g,
+                         const float* beta, float* S, void* out, int NH, int H, float scale,
+                         const Prologue& pro, hipStream_t stream) {
+  hipLaunchKernelGGL((decode_step_kernel<DK, DV, Io, SG, FU>), dim3(NH * (DV / 64)), dim3(256), 0,
+                     stream, q, k, v, g, beta, S, out, scale, pro, H);
+}
+
 template <int DK, int DV, class Io>
 static hipError_t launch_decode_t(const void* q, const void* k, const void* v, const float* g,
-                                  const float* beta, float* S, void* out, int NH, float scale,
-                                  bool sg, hipStream_t stream) {
-  if (sg)
-    hipLaunchKernelGGL((decode_step_kernel<DK, DV, Io, true>), dim3(NH * (DV / 64)), dim3(256), 0,
-                       stream, q, k, v, g, beta, S, out, scale);
+                                  const float* beta, float* S, void* out, int NH, int H,
+                                  float scale, bool sg, const Prologue& pro, hipStream_t stream) {
+  const bool fu = pro.flags != 0;
+  if (sg && fu)
+    launch_dec_k<DK, DV, Io, true, true>(q, k, v, g, beta, S, out, NH, H, scale, pro, stream);
+  else if (sg)
+    launch_dec_k<DK, DV, Io, true, false>(q, k, v, g, beta, S, out, NH, H, scale, pro, stream);
+  else if (fu)
+    launch_dec_k<DK, DV, Io, false, true>(q, k, v, g, beta, S, out, NH, H, scale, pro, stream);
   else
-    hipLaunchKernelGGL((decode_step_kernel<DK, DV, Io, false>), dim3(NH * (DV / 64)), dim3(256), 0,
-                       stream, q, k, v, g, beta, S, out, scale);
+    launch_dec_k<DK, DV, Io, false, false>(q, k, v, g, beta, S, out, NH, H, scale, pro, stream);
   return hipGetLastError();
 }
 
 hipError_t launch_decode(const void* q, const void* k, const void* v, const float* g,
-                         const float* beta, float* S, void* out, int NH, int dk, int dv,
-                         float scale, bool bf16, bool scalar_gate, hipStream_t stream) {
-#define KDA_DEC(DK, DV)                                                                     \
-  if (dk == DK && dv == DV)                                                                \
-    return bf16 ? launch_decode_t<DK, DV, IoBf16>(q, k, v, g, beta, S, out, NH, scale,        \
-                                                  scalar_gate, stream)                        \
-                : launch_decode_t<DK, DV, IoF32>(q, k, v, g, beta, S, out, NH, scale, scalar_gate, \
-                                                 stream);
+                         const float* beta, float* S, void* out, int NH, int H, int dk, int dv,
+                         float scale, bool bf16, bool scalar_gate, const Prologue& pro,
+                         hipStream_t stream) {
+#define KDA_DEC(DK, DV)                                                                       \
+  if (dk == DK && dv == DV)                                                                  \
+    return bf16 ? launch_decode_t<DK, DV, IoBf16>(q, k, v, g, beta, S, out, NH, H, scale,      \
+                                                  scalar_gate, pro, stream)                  \
+                : launch_decode_t<DK, DV, IoF32>(q, k, v, g, beta, S, out, NH, H, scale,       \
+                                                 scalar_gate, pro, stream);
   KDA_DEC(64, 64)
   KDA_DEC(64, 128)
   KDA_DEC(128, 64)

@@ -2,21 +2,25 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "common.h"
 #include "kda.h"
 
 namespace kda {
 hipError_t launch_decode(const void* q, const void* k, const void* v, const float* g,
-                         const float* beta, float* S, void* out, int NH, int dk, int dv,
-                         float scale, bool bf16, bool scalar_gate, hipStream_t stream);
+                         const float* beta, float* S, void* out, int NH, int H, int dk, int dv,
+                         float scale, bool bf16, bool scalar_gate, const Prologue& pro,
+                         hipStream_t stream);
 hipError_t launch_chunk(const void* q, const void* k, const void* v, const float* g,
                         const float* beta, const float* S0, void* out, float* S_final,
                         const int32_t* cu_seqlens, int n_seq, int T, int H, int dk, int dv,
-                        float scale, bool bf16, bool scalar_gate, hipStream_t stream);
+                        float scale, bool bf16, bool scalar_gate, const Prologue& pro,
+                        hipStream_t stream);
 bool chunk_supported(int dk, int dv, bool bf16);
 hipError_t launch_recurrent(const void* q, const void* k, const void* v, const float* g,
                             const float* beta, const float* S0, void* out, float* S_final,
                             const int32_t* cu, int n_seq, int T, int H, int dk, int dv,
-                            float scale, bool bf16, bool scalar_gate, hipStream_t stream);
+                            float scale, bool bf16, bool scalar_gate, const Prologue& pro,
+                            hipStream_t stream);
 }  // namespace kda
 
 namespace {
@@ -67,6 +71,32 @@ int check_align(const void* q, const void* k, const void* v, const float* log_al
 
 // Shared validation of the prefill entry points.  `rows` is the number of
 // token rows (B*T or T_total), `n_seq` the number of state slots.
+// The input transforms: known flags, A_log present with the gate transform,
+// word-aligned parameter arrays that no output overlaps.  Fills `out`.
+int check_prologue(const kda_prologue* pro, int H, int d_k, bool sg, kda::Prologue* o,
+                   Range r_out, Range r_state) {
+  *o = kda::Prologue{0u, nullptr, nullptr};
+  if (!pro) return KDA_OK;
+  const uint32_t known = KDA_PRO_QK_L2NORM | KDA_PRO_BETA_SIGMOID | KDA_PRO_GATE;
+  if (pro->flags & ~known) return KDA_ERR_UNSUPPORTED;
+  if (pro->flags & KDA_PRO_GATE) {
+    if (!pro->A_log) return KDA_ERR_NULL;
+    if (!aligned(pro->A_log, 4) || !aligned(pro->gate_bias, 4)) return KDA_ERR_ALIGN;
+    const Range ra = span(pro->A_log, (size_t)H * 4);
+    const Range rb = span(pro->gate_bias, pro->gate_bias ? (size_t)H * (sg ? 1 : d_k) * 4 : 0);
+    if (overlap(ra, r_out) || overlap(ra, r_state) || overlap(rb, r_out) || overlap(rb, r_state))
+      return KDA_ERR_ALIAS;
+  }
+  // the kernels' bit values equal the header's
+  static_assert(KDA_PRO_QK_L2NORM == kda::PRO_L2NORM && KDA_PRO_BETA_SIGMOID == kda::PRO_BETA_SIGMOID &&
+                    KDA_PRO_GATE == kda::PRO_GATE,
+                "prologue flags");
+  o->flags = pro->flags;
+  o->A_log = (pro->flags & KDA_PRO_GATE) ? pro->A_log : nullptr;
+  o->bias = (pro->flags & KDA_PRO_GATE) ? pro->gate_bias : nullptr;
+  return KDA_OK;
+}
+
 // Shared validation of the calls over token sequences (prefill and
 // recurrent); `supported` is the caller's verdict on d_k, d_v, chunk, io_dtype.
 int check_tokens(const void* q, const void* k, const void* v, const float* log_alpha,
@@ -117,46 +147,39 @@ int check_recurrent(const void* q, const void* k, const void* v, const float* lo
 
 namespace {
 
-int chunk_fwd_impl(const void* q, const void* k, const void* v, const float* log_alpha,
-                   const float* beta, const float* S0, void* out, float* S_final, int B, int T,
-                   int H, int d_k, int d_v, float scale, int chunk, int io_dtype, bool sg,
-                   void* stream) {
-  if (B < 0 || T < 0 || H <= 0) return KDA_ERR_DIM;
-  const size_t rows = (size_t)B * T;
-  int st = check_prefill(q, k, v, log_alpha, beta, S0, out, S_final, nullptr, rows, B, H, d_k,
-                         d_v, chunk, io_dtype, sg);
+// One implementation per operation; cu_seqlens NULL means the batched
+// layout (n_seq sequences of T tokens), otherwise the packed one (T = T_total).
+int chunk_impl(const void* q, const void* k, const void* v, const float* log_alpha,
+               const float* beta, const float* S0, void* out, float* S_final,
+               const int32_t* cu_seqlens, bool packed, int n_seq, int T, int H, int d_k, int d_v,
+               float scale, int chunk, int io_dtype, bool sg, const kda_prologue* pro,
+               void* stream) {
+  if (n_seq < 0 || T < 0 || H <= 0) return KDA_ERR_DIM;
+  if (packed && !cu_seqlens) return KDA_ERR_NULL;
+  const size_t rows = packed ? (size_t)T : (size_t)n_seq * T;
+  int st = check_prefill(q, k, v, log_alpha, beta, S0, out, S_final, cu_seqlens, rows, n_seq, H,
+                         d_k, d_v, chunk, io_dtype, sg);
   if (st != KDA_OK) return st;
-  if (B == 0) return KDA_OK;
+  kda::Prologue pr;
+  const size_t state = (size_t)n_seq * H * d_k * d_v * 4;
+  st = check_prologue(pro, H, d_k, sg, &pr, span(out, rows * H * d_v * io_bytes(io_dtype)),
+                      span(S_final, S_final ? state : 0));
+  if (st != KDA_OK) return st;
+  if (n_seq == 0) return KDA_OK;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (T == 0) {
+  if (!packed && T == 0) {
     if (!S_final || S0 == S_final) return KDA_OK;
-    const size_t n = (size_t)B * H * d_k * d_v;
-    hipLaunchKernelGGL(copy_state_kernel, dim3(1024), dim3(256), 0, s, S0, S_final, n);
+    hipLaunchKernelGGL(copy_state_kernel, dim3(1024), dim3(256), 0, s, S0, S_final, state / 4);
     return launch_status(hipGetLastError());
   }
-  return launch_status(kda::launch_chunk(q, k, v, log_alpha, beta, S0, out, S_final, nullptr, B,
-                                         T, H, d_k, d_v, scale, io_dtype == KDA_IO_BF16, sg, s));
+  return launch_status(kda::launch_chunk(q, k, v, log_alpha, beta, S0, out, S_final,
+                                         packed ? cu_seqlens : nullptr, n_seq, T, H, d_k, d_v,
+                                         scale, io_dtype == KDA_IO_BF16, sg, pr, s));
 }
 
-int chunk_fwd_varlen_impl(const void* q, const void* k, const void* v, const float* log_alpha,
-                          const float* beta, const float* S0, void* out, float* S_final,
-                          const int32_t* cu_seqlens, int N, int T_total, int H, int d_k,
-                          int d_v, float scale, int chunk, int io_dtype, bool sg, void* stream) {
-  if (N < 0 || T_total < 0 || H <= 0) return KDA_ERR_DIM;
-  if (!cu_seqlens) return KDA_ERR_NULL;
-  int st = check_prefill(q, k, v, log_alpha, beta, S0, out, S_final, cu_seqlens,
-                         (size_t)T_total, N, H, d_k, d_v, chunk, io_dtype, sg);
-  if (st != KDA_OK) return st;
-  if (N == 0) return KDA_OK;
-  return launch_status(kda::launch_chunk(q, k, v, log_alpha, beta, S0, out, S_final, cu_seqlens,
-                                         N, T_total, H, d_k, d_v, scale,
-                                         io_dtype == KDA_IO_BF16, sg,
-                                         reinterpret_cast<hipStream_t>(stream)));
-}
-
-int decode_step_impl(const void* q, const void* k, const void* v, const float* log_alpha,
-                     const float* beta, float* S_inout, void* out, int N, int H, int d_k,
-                     int d_v, float scale, int io_dtype, bool sg, void* stream) {
+int decode_impl(const void* q, const void* k, const void* v, const float* log_alpha,
+                const float* beta, float* S_inout, void* out, int N, int H, int d_k, int d_v,
+                float scale, int io_dtype, bool sg, const kda_prologue* pro, void* stream) {
   if (N < 0 || H <= 0) return KDA_ERR_DIM;
   if (!io_ok(io_dtype)) return KDA_ERR_UNSUPPORTED;
   if (!(shape_ok(d_k) && shape_ok(d_v))) return KDA_ERR_UNSUPPORTED;
@@ -174,41 +197,37 @@ int decode_step_impl(const void* q, const void* k, const void* v, const float* l
     if (overlap(ro, r) || overlap(rs, r)) return KDA_ERR_ALIAS;
   }
   if (overlap(ro, rs)) return KDA_ERR_ALIAS;
+  kda::Prologue pr;
+  const int sp = check_prologue(pro, H, d_k, sg, &pr, ro, rs);
+  if (sp != KDA_OK) return sp;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  return launch_status(kda::launch_decode(q, k, v, log_alpha, beta, S_inout, out, (int)heads, d_k,
-                                          d_v, scale, io_dtype == KDA_IO_BF16, sg, s));
+  return launch_status(kda::launch_decode(q, k, v, log_alpha, beta, S_inout, out, (int)heads, H,
+                                          d_k, d_v, scale, io_dtype == KDA_IO_BF16, sg, pr, s));
 }
 
-int recurrent_fwd_impl(const void* q, const void* k, const void* v, const float* log_alpha,
-                       const float* beta, const float* S0, void* out, float* S_final, int B,
-                       int T, int H, int d_k, int d_v, float scale, int io_dtype, bool sg,
-                       void* stream) {
-  if (B < 0 || T < 0 || H <= 0) return KDA_ERR_DIM;
-  const size_t rows = (size_t)B * T;
+int recurrent_impl(const void* q, const void* k, const void* v, const float* log_alpha,
+                   const float* beta, const float* S0, void* out, float* S_final,
+                   const int32_t* cu_seqlens, bool packed, int n_seq, int T, int H, int d_k,
+                   int d_v, float scale, int io_dtype, bool sg, const kda_prologue* pro,
+                   void* stream) {
+  if (n_seq < 0 || T < 0 || H <= 0) return KDA_ERR_DIM;
+  if (packed && !cu_seqlens) return KDA_ERR_NULL;
+  const size_t rows = packed ? (size_t)T : (size_t)n_seq * T;
   if (rows > 0x7fffffffu) return KDA_ERR_DIM;   // token indices are 32-bit in the kernel
-  int st = check_recurrent(q, k, v, log_alpha, beta, S0, out, S_final, nullptr, rows, B, H, d_k,
-                           d_v, io_dtype, sg);
+  int st = check_recurrent(q, k, v, log_alpha, beta, S0, out, S_final, cu_seqlens, rows, n_seq,
+                           H, d_k, d_v, io_dtype, sg);
   if (st != KDA_OK) return st;
-  if (B == 0 || (T == 0 && (!S_final || S0 == S_final))) return KDA_OK;
+  kda::Prologue pr;
+  const size_t state = (size_t)n_seq * H * d_k * d_v * 4;
+  st = check_prologue(pro, H, d_k, sg, &pr, span(out, rows * H * d_v * io_bytes(io_dtype)),
+                      span(S_final, S_final ? state : 0));
+  if (st != KDA_OK) return st;
+  if (n_seq == 0) return KDA_OK;
+  if (!packed && T == 0 && (!S_final || S0 == S_final)) return KDA_OK;
   // (T == 0 with a separate S_final: the kernel copies S0, or zeros, through)
-  return launch_status(kda::launch_recurrent(q, k, v, log_alpha, beta, S0, out, S_final, nullptr,
-                                             B, T, H, d_k, d_v, scale, io_dtype == KDA_IO_BF16,
-                                             sg, reinterpret_cast<hipStream_t>(stream)));
-}
-
-int recurrent_fwd_varlen_impl(const void* q, const void* k, const void* v, const float* log_alpha,
-                              const float* beta, const float* S0, void* out, float* S_final,
-                              const int32_t* cu_seqlens, int N, int T_total, int H, int d_k,
-                              int d_v, float scale, int io_dtype, bool sg, void* stream) {
-  if (N < 0 || T_total < 0 || H <= 0) return KDA_ERR_DIM;
-  if (!cu_seqlens) return KDA_ERR_NULL;
-  int st = check_recurrent(q, k, v, log_alpha, beta, S0, out, S_final, cu_seqlens,
-                           (size_t)T_total, N, H, d_k, d_v, io_dtype, sg);
-  if (st != KDA_OK) return st;
-  if (N == 0) return KDA_OK;
   return launch_status(kda::launch_recurrent(q, k, v, log_alpha, beta, S0, out, S_final,
-                                             cu_seqlens, N, T_total, H, d_k, d_v, scale,
-                                             io_dtype == KDA_IO_BF16, sg,
+                                             packed ? cu_seqlens : nullptr, n_seq, T, H, d_k, d_v,
+                                             scale, io_dtype == KDA_IO_BF16, sg, pr,
                                              reinterpret_cast<hipStream_t>(stream)));
 }
 
@@ -242,8 +261,8 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const float* log_
                   size_t workspace_bytes, void* stream) {
   (void)workspace;
   (void)workspace_bytes;
-  return chunk_fwd_impl(q, k, v, log_alpha, beta, S0, out, S_final, B, T, H, d_k, d_v, scale,
-                        chunk, io_dtype, false, stream);
+  return chunk_impl(q, k, v, log_alpha, beta, S0, out, S_final, nullptr, false, B, T, H, d_k, d_v,
+                    scale, chunk, io_dtype, false, nullptr, stream);
 }
 
 int kda_chunk_fwd_varlen(const void* q, const void* k, const void* v, const float* log_alpha,
@@ -253,30 +272,30 @@ int kda_chunk_fwd_varlen(const void* q, const void* k, const void* v, const floa
                          size_t workspace_bytes, void* stream) {
   (void)workspace;
   (void)workspace_bytes;
-  return chunk_fwd_varlen_impl(q, k, v, log_alpha, beta, S0, out, S_final, cu_seqlens, N,
-                               T_total, H, d_k, d_v, scale, chunk, io_dtype, false, stream);
+  return chunk_impl(q, k, v, log_alpha, beta, S0, out, S_final, cu_seqlens, true, N, T_total, H,
+                    d_k, d_v, scale, chunk, io_dtype, false, nullptr, stream);
 }
 
 int kda_decode_step(const void* q, const void* k, const void* v, const float* log_alpha,
                     const float* beta, float* S_inout, void* out, int N, int H, int d_k, int d_v,
                     float scale, int io_dtype, void* stream) {
-  return decode_step_impl(q, k, v, log_alpha, beta, S_inout, out, N, H, d_k, d_v, scale,
-                          io_dtype, false, stream);
+  return decode_impl(q, k, v, log_alpha, beta, S_inout, out, N, H, d_k, d_v, scale, io_dtype,
+                     false, nullptr, stream);
 }
 
 int kda_recurrent_fwd(const void* q, const void* k, const void* v, const float* log_alpha,
                       const float* beta, const float* S0, void* out, float* S_final, int B, int T,
                       int H, int d_k, int d_v, float scale, int io_dtype, void* stream) {
-  return recurrent_fwd_impl(q, k, v, log_alpha, beta, S0, out, S_final, B, T, H, d_k, d_v, scale,
-                            io_dtype, false, stream);
+  return recurrent_impl(q, k, v, log_alpha, beta, S0, out, S_final, nullptr, false, B, T, H, d_k,
+                        d_v, scale, io_dtype, false, nullptr, stream);
 }
 
 int kda_recurrent_fwd_varlen(const void* q, const void* k, const void* v, const float* log_alpha,
                              const float* beta, const float* S0, void* out, float* S_final,
                              const int32_t* cu_seqlens, int N, int T_total, int H, int d_k,
                              int d_v, float scale, int io_dtype, void* stream) {
-  return recurrent_fwd_varlen_impl(q, k, v, log_alpha, beta, S0, out, S_final, cu_seqlens, N,
-                                   T_total, H, d_k, d_v, scale, io_dtype, false, stream);
+  return recurrent_impl(q, k, v, log_alpha, beta, S0, out, S_final, cu_seqlens, true, N, T_total,
+                        H, d_k, d_v, scale, io_dtype, false, nullptr, stream);
 }
 
 int kda_gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* log_alpha,
@@ -285,8 +304,8 @@ int kda_gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* 
                       void* workspace, size_t workspace_bytes, void* stream) {
   (void)workspace;
   (void)workspace_bytes;
-  return chunk_fwd_impl(q, k, v, log_alpha, beta, S0, out, S_final, B, T, H, d_k, d_v, scale,
-                        chunk, io_dtype, true, stream);
+  return chunk_impl(q, k, v, log_alpha, beta, S0, out, S_final, nullptr, false, B, T, H, d_k, d_v,
+                    scale, chunk, io_dtype, true, nullptr, stream);
 }
 
 int kda_gdn_chunk_fwd_varlen(const void* q, const void* k, const void* v, const float* log_alpha,
@@ -296,23 +315,23 @@ int kda_gdn_chunk_fwd_varlen(const void* q, const void* k, const void* v, const 
                              size_t workspace_bytes, void* stream) {
   (void)workspace;
   (void)workspace_bytes;
-  return chunk_fwd_varlen_impl(q, k, v, log_alpha, beta, S0, out, S_final, cu_seqlens, N,
-                               T_total, H, d_k, d_v, scale, chunk, io_dtype, true, stream);
+  return chunk_impl(q, k, v, log_alpha, beta, S0, out, S_final, cu_seqlens, true, N, T_total, H,
+                    d_k, d_v, scale, chunk, io_dtype, true, nullptr, stream);
 }
 
 int kda_gdn_decode_step(const void* q, const void* k, const void* v, const float* log_alpha,
                         const float* beta, float* S_inout, void* out, int N, int H, int d_k,
                         int d_v, float scale, int io_dtype, void* stream) {
-  return decode_step_impl(q, k, v, log_alpha, beta, S_inout, out, N, H, d_k, d_v, scale,
-                          io_dtype, true, stream);
+  return decode_impl(q, k, v, log_alpha, beta, S_inout, out, N, H, d_k, d_v, scale, io_dtype,
+                     true, nullptr, stream);
 }
 
 int kda_gdn_recurrent_fwd(const void* q, const void* k, const void* v, const float* log_alpha,
                           const float* beta, const float* S0, void* out, float* S_final, int B,
                           int T, int H, int d_k, int d_v, float scale, int io_dtype,
                           void* stream) {
-  return recurrent_fwd_impl(q, k, v, log_alpha, beta, S0, out, S_final, B, T, H, d_k, d_v, scale,
-                            io_dtype, true, stream);
+  return recurrent_impl(q, k, v, log_alpha, beta, S0, out, S_final, nullptr, false, B, T, H, d_k,
+                        d_v, scale, io_dtype, true, nullptr, stream);
 }
 
 int kda_gdn_recurrent_fwd_varlen(const void* q, const void* k, const void* v,
@@ -320,8 +339,41 @@ int kda_gdn_recurrent_fwd_varlen(const void* q, const void* k, const void* v,
                                  void* out, float* S_final, const int32_t* cu_seqlens, int N,
                                  int T_total, int H, int d_k, int d_v, float scale, int io_dtype,
                                  void* stream) {
-  return recurrent_fwd_varlen_impl(q, k, v, log_alpha, beta, S0, out, S_final, cu_seqlens, N,
-                                   T_total, H, d_k, d_v, scale, io_dtype, true, stream);
+  return recurrent_impl(q, k, v, log_alpha, beta, S0, out, S_final, cu_seqlens, true, N, T_total,
+                        H, d_k, d_v, scale, io_dtype, true, nullptr, stream);
+}
+
+int kda_chunk_fwd_fused(const void* q, const void* k, const void* v, const float* log_alpha,
+                        const float* beta, const float* S0, void* out, float* S_final,
+                        const int32_t* cu_seqlens, int N, int T, int H, int d_k, int d_v,
+                        float scale, int chunk, int io_dtype, int per_head_gate,
+                        const kda_prologue* pro, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  if (per_head_gate != 0 && per_head_gate != 1) return KDA_ERR_UNSUPPORTED;
+  return chunk_impl(q, k, v, log_alpha, beta, S0, out, S_final, cu_seqlens, cu_seqlens != nullptr,
+                    N, T, H, d_k, d_v, scale, chunk, io_dtype, per_head_gate == 1, pro, stream);
+}
+
+int kda_recurrent_fwd_fused(const void* q, const void* k, const void* v, const float* log_alpha,
+                            const float* beta, const float* S0, void* out, float* S_final,
+                            const int32_t* cu_seqlens, int N, int T, int H, int d_k, int d_v,
+                            float scale, int io_dtype, int per_head_gate,
+                            const kda_prologue* pro, void* stream) {
+  if (per_head_gate != 0 && per_head_gate != 1) return KDA_ERR_UNSUPPORTED;
+  return recurrent_impl(q, k, v, log_alpha, beta, S0, out, S_final, cu_seqlens,
+                        cu_seqlens != nullptr, N, T, H, d_k, d_v, scale, io_dtype,
+                        per_head_gate == 1, pro, stream);
+}
+
+int kda_decode_step_fused(const void* q, const void* k, const void* v, const float* log_alpha,
+                          const float* beta, float* S_inout, void* out, int N, int H, int d_k,
+                          int d_v, float scale, int io_dtype, int per_head_gate,
+                          const kda_prologue* pro, void* stream) {
+  if (per_head_gate != 0 && per_head_gate != 1) return KDA_ERR_UNSUPPORTED;
+  return decode_impl(q, k, v, log_alpha, beta, S_inout, out, N, H, d_k, d_v, scale, io_dtype,
+                     per_head_gate == 1, pro, stream);
 }
 
 }  // extern "C"

@@ -94,12 +94,13 @@ struct RecurrentToken {
 
 // S0 and S_final may be the same array (each workgroup reads its slice of the
 // state before it writes it), so neither is marked restrict.
-template <int DK, int DV, class Io, bool SG>
+// FU: the raw inputs pass through the transforms of `pro` (common.h) first.
+template <int DK, int DV, class Io, bool SG, bool FU>
 __global__ __launch_bounds__(256) void recurrent_fwd_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, const float* S0,
     void* __restrict__ out, float* S_final, const int32_t* __restrict__ cu_seqlens, int T, int H,
-    float scale) {
+    float scale, Prologue pro) {
   constexpr int CW = 64;                 // value columns per workgroup
   constexpr int NSL = DV / CW;
   constexpr int RPT = DK / 16;           // key rows per lane
@@ -145,21 +146,39 @@ __global__ __launch_bounds__(256) void recurrent_fwd_kernel(
     for (int m = 0; m < RPT; ++m) st[m] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
+  // transform parameters of this head (FU): exp(A_log) and the lane's biases
+  float ea = 1.f, gb[RPT];
+#pragma unroll
+  for (int m = 0; m < RPT; ++m) gb[m] = 0.f;
+  if (FU && (pro.flags & PRO_GATE)) {
+    ea = __expf(pro.A_log[h]);
+    if (pro.bias) {
+#pragma unroll
+      for (int m = 0; m < RPT; ++m) gb[m] = SG ? pro.bias[h] : pro.bias[h * DK + row0 + m];
+    }
+  }
+
   // one token: forget, predict, correct, write, read
   auto token = [&](const RecurrentToken<DK, DV, Io, SG>& in, int t) {
     float kk[RPT], qq[RPT];
-    float kq = 0.f;
+    float kq = 0.f, k2 = 0.f, q2 = 0.f;
 #pragma unroll
     for (int m = 0; m < RPT; ++m) {
       kk[m] = in.k.get(m);
       qq[m] = in.q.get(m);
       kq += kk[m] * qq[m];
+      if (FU) {
+        k2 += kk[m] * kk[m];
+        q2 += qq[m] * qq[m];
+      }
     }
     // decay the key rows, then the partial prediction Sbar^T k and read Sbar^T q
     f32x4 p = {0.f, 0.f, 0.f, 0.f}, r = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int m = 0; m < RPT; ++m) {
-      st[m] *= __expf(in.gate(m));
+      float gm = in.gate(m);
+      if (FU && (pro.flags & PRO_GATE)) gm = gate_logalpha(gm, ea, gb[m]);
+      st[m] *= __expf(gm);
       p += st[m] * kk[m];
       r += st[m] * qq[m];
     }
@@ -169,12 +188,28 @@ __global__ __launch_bounds__(256) void recurrent_fwd_kernel(
       r[c] = row_sum16(r[c]);
     }
     kq = row_sum16(kq);
+    float b = in.beta;
+    // L2 norms: the sums above used the raw q and k; scale them afterwards
+    // (p by 1/|k|, r by 1/|q|, k^T q by both) and write k e^T as raw k times
+    // e/|k|
+    float rk = 1.f;
+    if (FU) {
+      if (pro.flags & PRO_L2NORM) {
+        rk = __builtin_amdgcn_rsqf(row_sum16(k2) + PRO_NORM_EPS);
+        const float rq = __builtin_amdgcn_rsqf(row_sum16(q2) + PRO_NORM_EPS);
+        p *= rk;
+        r *= rq;
+        kq *= rk * rq;
+      }
+      if (pro.flags & PRO_BETA_SIGMOID) b = sigmoid_f(b);
+    }
     const f32x4 vv = {in.v.get(0), in.v.get(1), in.v.get(2), in.v.get(3)};
-    const f32x4 e = in.beta * (vv - p);
+    const f32x4 e = b * (vv - p);
     if (rg == 0) Io::store4(out, ((size_t)t * H + h) * DV + col, scale * (r + kq * e));
     // S = Sbar + k e^T
+    const f32x4 ek = e * rk;
 #pragma unroll
-    for (int m = 0; m < RPT; ++m) st[m] += kk[m] * e;
+    for (int m = 0; m < RPT; ++m) st[m] += kk[m] * ek;
   };
   auto fetch = [&](RecurrentToken<DK, DV, Io, SG>& in, int t) {
     in.load(q, k, v, g, beta, (size_t)t * H + h, row0, col);
@@ -212,32 +247,47 @@ __global__ __launch_bounds__(256) void recurrent_fwd_kernel(
   }
 }
 
+template <int DK, int DV, class Io, bool SG, bool FU>
+static void launch_rec_k(const void* q, const void* k, const void* v, const float* g,
+                         const float* beta, const float* S0, void* out, float* S_final,
+                         const int32_t* cu, unsigned blocks, int T, int H, float scale,
+                         const Prologue& pro, hipStream_t stream) {
+  hipLaunchKernelGGL((recurrent_fwd_kernel<DK, DV, Io, SG, FU>), dim3(blocks), dim3(256), 0,
+                     stream, q, k, v, g, beta, S0, out, S_final, cu, T, H, scale, pro);
+}
+
 template <int DK, int DV, class Io>
 static hipError_t launch_recurrent_t(const void* q, const void* k, const void* v, const float* g,
                                      const float* beta, const float* S0, void* out,
                                      float* S_final, const int32_t* cu, int n_seq, int T, int H,
-                                     float scale, bool sg, hipStream_t stream) {
+                                     float scale, bool sg, const Prologue& pro,
+                                     hipStream_t stream) {
   const long blocks = (long)n_seq * H * (DV / 64);
   if (blocks > 0x7fffffffL) return hipErrorInvalidValue;
-  if (sg)
-    hipLaunchKernelGGL((recurrent_fwd_kernel<DK, DV, Io, true>), dim3((unsigned)blocks),
-                       dim3(256), 0, stream, q, k, v, g, beta, S0, out, S_final, cu, T, H, scale);
+  const unsigned nb = (unsigned)blocks;
+  const bool fu = pro.flags != 0;
+  if (sg && fu)
+    launch_rec_k<DK, DV, Io, true, true>(q, k, v, g, beta, S0, out, S_final, cu, nb, T, H, scale, pro, stream);
+  else if (sg)
+    launch_rec_k<DK, DV, Io, true, false>(q, k, v, g, beta, S0, out, S_final, cu, nb, T, H, scale, pro, stream);
+  else if (fu)
+    launch_rec_k<DK, DV, Io, false, true>(q, k, v, g, beta, S0, out, S_final, cu, nb, T, H, scale, pro, stream);
   else
-    hipLaunchKernelGGL((recurrent_fwd_kernel<DK, DV, Io, false>), dim3((unsigned)blocks),
-                       dim3(256), 0, stream, q, k, v, g, beta, S0, out, S_final, cu, T, H, scale);
+    launch_rec_k<DK, DV, Io, false, false>(q, k, v, g, beta, S0, out, S_final, cu, nb, T, H, scale, pro, stream);
   return hipGetLastError();
 }
 
 hipError_t launch_recurrent(const void* q, const void* k, const void* v, const float* g,
                             const float* beta, const float* S0, void* out, float* S_final,
                             const int32_t* cu, int n_seq, int T, int H, int dk, int dv,
-                            float scale, bool bf16, bool scalar_gate, hipStream_t stream) {
+                            float scale, bool bf16, bool scalar_gate, const Prologue& pro,
+                            hipStream_t stream) {
 #define KDA_REC(DK, DV)                                                                    \
   if (dk == DK && dv == DV)                                                               \
     return bf16 ? launch_recurrent_t<DK, DV, IoBf16>(q, k, v, g, beta, S0, out, S_final, cu, \
-                                                     n_seq, T, H, scale, scalar_gate, stream) \
+                                                     n_seq, T, H, scale, scalar_gate, pro, stream) \
                 : launch_recurrent_t<DK, DV, IoF32>(q, k, v, g, beta, S0, out, S_final, cu,  \
-                                                    n_seq, T, H, scale, scalar_gate, stream);
+                                                    n_seq, T, H, scale, scalar_gate, pro, stream);
   KDA_REC(64, 64)
   KDA_REC(64, 128)
   KDA_REC(128, 64)

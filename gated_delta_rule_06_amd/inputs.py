@@ -30,7 +30,7 @@ import numpy as np
 import torch
 
 __all__ = ["prefill_inputs", "varlen_lengths", "varlen_inputs", "decode_inputs",
-           "to_host", "bf16_bits_from_f32", "CONFIGS"]
+           "raw_layer_inputs", "to_host", "bf16_bits_from_f32", "CONFIGS"]
 
 _IO = {"bf16": torch.bfloat16, "f32": torch.float32}
 
@@ -136,6 +136,27 @@ def decode_inputs(N, H, dk, dv, steps, io="bf16", seed=0, s0_std=0.02, device="c
     S = s0_std * torch.randn((N, H, dk, dv), generator=gen, device=device, dtype=torch.float32)
     d = _draw((steps, N), H, dk, dv, io, gen, device, False, N, s0_std, gate=gate)
     d.update(S=S, N=N, H=H, dk=dk, dv=dv, io=io, steps=steps)
+    return d
+
+
+def raw_layer_inputs(d, H, dk, seed=0, gate="kda", strong_decay=False, device="cpu"):
+    """Turn an input dict into raw layer inputs for the in-kernel transforms:
+    q and k scaled per (token, head) by exp(N(0, 0.5)) (no longer unit),
+    beta replaced by logits ~ N(0, 1), log_alpha replaced by a raw gate
+    projection ~ N(-4, 1) (N(3, 1) with strong_decay), plus A_log [H] ~
+    N(0, 0.3^2) and a gate bias ~ N(0, 0.5^2) of shape [H, dk] ([H] for
+    per-head gates).  The I/O dtype of q and k is kept."""
+    gen = _gen(device, seed + 7919)
+    qk_shape = d["q"].shape
+    for name in ("q", "k"):
+        c = torch.exp(0.5 * torch.randn(qk_shape[:-1] + (1,), generator=gen, device=device))
+        d[name] = (d[name].float() * c).to(d[name].dtype)
+    d["beta"] = torch.randn(d["beta"].shape, generator=gen, device=device)
+    mu = 3.0 if strong_decay else -4.0
+    d["g"] = mu + torch.randn(d["g"].shape, generator=gen, device=device)
+    d["A_log"] = 0.3 * torch.randn((H,), generator=gen, device=device)
+    bshape = (H,) if gate == "gdn" else (H, dk)
+    d["gate_bias"] = 0.5 * torch.randn(bshape, generator=gen, device=device)
     return d
 
 

@@ -19,6 +19,14 @@ LIB_PATH = os.path.join(_PKG, "libkda.so")
 KDA_IO_F32 = 0
 KDA_IO_BF16 = 1
 CHUNK = 64
+KDA_PRO_QK_L2NORM = 1
+KDA_PRO_BETA_SIGMOID = 2
+KDA_PRO_GATE = 4
+
+
+class _Prologue(ctypes.Structure):
+    _fields_ = [("flags", ctypes.c_uint32), ("A_log", ctypes.c_void_p),
+                ("gate_bias", ctypes.c_void_p)]
 
 
 class KdaError(RuntimeError):
@@ -50,6 +58,15 @@ def _load():
         kf, gf = getattr(lib, "kda_" + name), getattr(lib, "kda_gdn_" + name)
         gf.restype = kf.restype
         gf.argtypes = kf.argtypes
+    pp = ctypes.POINTER(_Prologue)
+    lib.kda_chunk_fwd_fused.restype = i
+    lib.kda_chunk_fwd_fused.argtypes = [vp, vp, vp, fp, fp, fp, vp, fp, vp, i, i, i, i, i, f, i, i,
+                                        i, pp, vp, sz, vp]
+    lib.kda_recurrent_fwd_fused.restype = i
+    lib.kda_recurrent_fwd_fused.argtypes = [vp, vp, vp, fp, fp, fp, vp, fp, vp, i, i, i, i, i, f,
+                                            i, i, pp, vp]
+    lib.kda_decode_step_fused.restype = i
+    lib.kda_decode_step_fused.argtypes = [vp, vp, vp, fp, fp, fp, vp, i, i, i, i, f, i, i, pp, vp]
     lib.kda_chunk_fwd_workspace_size.restype = sz
     lib.kda_chunk_fwd_workspace_size.argtypes = [i] * 7
     lib.kda_chunk_fwd_varlen_workspace_size.restype = sz
@@ -105,14 +122,40 @@ def _gate(log_alpha, rows_shape, dk):
     return tuple(rows_shape) + (dk,), "kda_"
 
 
+def _prologue(H, dk, per_head, device, qk_l2norm, beta_sigmoid, A_log, gate_bias):
+    """The input transforms as a kda_prologue, or None when none is asked for.
+    A_log ([H]) switches the gate transform on; gate_bias is [H, d_k] ([H]
+    with per-head gates) or None."""
+    flags = (KDA_PRO_QK_L2NORM if qk_l2norm else 0) | (KDA_PRO_BETA_SIGMOID if beta_sigmoid else 0)
+    if gate_bias is not None and A_log is None:
+        raise ValueError("gate_bias needs A_log (the gate transform)")
+    if A_log is not None:
+        flags |= KDA_PRO_GATE
+        _check(A_log, "A_log", (H,), torch.float32, device)
+        _check(gate_bias, "gate_bias", (H,) if per_head else (H, dk), torch.float32, device)
+    if not flags:
+        return None
+    return _Prologue(flags, None if A_log is None else A_log.data_ptr(),
+                     None if gate_bias is None else gate_bias.data_ptr())
+
+
 def _workspace(nbytes, device):
     if nbytes == 0:
         return None, 0
     return torch.empty(nbytes, dtype=torch.uint8, device=device), nbytes
 
 
+_TRANSFORMS_DOC = """
+    Optional input transforms, applied inside the kernels: qk_l2norm
+    normalises q and k per (token, head); beta_sigmoid takes beta as logits;
+    A_log ([H] fp32) makes log_alpha the raw gate projection g, with log alpha
+    = -5 sigmoid(exp(A_log[h]) (g + gate_bias)), gate_bias [H, d_k] ([H] for
+    per-head gates) or None."""
+
+
 def chunk_fwd(q, k, v, log_alpha, beta, S0=None, scale=None, chunk=CHUNK, out=None,
-              S_final=None, output_final_state=True):
+              S_final=None, output_final_state=True, qk_l2norm=False, beta_sigmoid=False,
+              A_log=None, gate_bias=None):
     """Chunkwise prefill.  q, k: [B, T, H, d_k]; v: [B, T, H, d_v]; beta:
     [B, T, H]; log_alpha: [B, T, H, d_k] (KDA) or [B, T, H] (Gated DeltaNet, one
     gate per token and head); S0: [B, H, d_k, d_v] fp32 or None.  Returns
@@ -137,17 +180,26 @@ def chunk_fwd(q, k, v, log_alpha, beta, S0=None, scale=None, chunk=CHUNK, out=No
         S_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
     _check(S_final, "S_final", (B, H, dk, dv), torch.float32, dev)
     ws, wsb = _workspace(lib.kda_chunk_fwd_workspace_size(B, T, H, dk, dv, chunk, io), dev)
-    fn = pre + "chunk_fwd"
-    st = getattr(lib, fn)(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S0),
-                          _ptr(out), _ptr(S_final), B, T, H, dk, dv, float(scale), int(chunk), io,
-                          _ptr(ws), wsb, _stream(dev))
+    pro = _prologue(H, dk, pre == "kda_gdn_", dev, qk_l2norm, beta_sigmoid, A_log, gate_bias)
+    if pro is None:
+        fn = pre + "chunk_fwd"
+        st = getattr(lib, fn)(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S0),
+                              _ptr(out), _ptr(S_final), B, T, H, dk, dv, float(scale), int(chunk),
+                              io, _ptr(ws), wsb, _stream(dev))
+    else:
+        fn = "kda_chunk_fwd_fused"
+        st = lib.kda_chunk_fwd_fused(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                                     _ptr(S0), _ptr(out), _ptr(S_final), None, B, T, H, dk, dv,
+                                     float(scale), int(chunk), io, int(pre == "kda_gdn_"),
+                                     ctypes.byref(pro), _ptr(ws), wsb, _stream(dev))
     if st != 0:
         raise KdaError(st, fn)
     return out, S_final
 
 
 def chunk_fwd_varlen(q, k, v, log_alpha, beta, cu_seqlens, S0=None, scale=None, chunk=CHUNK,
-                     out=None, S_final=None, output_final_state=True):
+                     out=None, S_final=None, output_final_state=True, qk_l2norm=False,
+                     beta_sigmoid=False, A_log=None, gate_bias=None):
     """Packed variable-length prefill.  q, k: [T_total, H, d_k]; v: [T_total,
     H, d_v]; beta: [T_total, H]; log_alpha: [T_total, H, d_k] (KDA) or
     [T_total, H] (Gated DeltaNet); cu_seqlens: int32 [N+1] on the device; S0:
@@ -174,16 +226,26 @@ def chunk_fwd_varlen(q, k, v, log_alpha, beta, cu_seqlens, S0=None, scale=None, 
         S_final = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
     _check(S_final, "S_final", (N, H, dk, dv), torch.float32, dev)
     ws, wsb = _workspace(lib.kda_chunk_fwd_varlen_workspace_size(N, Tt, H, dk, dv, chunk, io), dev)
-    fn = pre + "chunk_fwd_varlen"
-    st = getattr(lib, fn)(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S0),
-                          _ptr(out), _ptr(S_final), _ptr(cu_seqlens), N, Tt, H, dk, dv,
-                          float(scale), int(chunk), io, _ptr(ws), wsb, _stream(dev))
+    pro = _prologue(H, dk, pre == "kda_gdn_", dev, qk_l2norm, beta_sigmoid, A_log, gate_bias)
+    if pro is None:
+        fn = pre + "chunk_fwd_varlen"
+        st = getattr(lib, fn)(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S0),
+                              _ptr(out), _ptr(S_final), _ptr(cu_seqlens), N, Tt, H, dk, dv,
+                              float(scale), int(chunk), io, _ptr(ws), wsb, _stream(dev))
+    else:
+        fn = "kda_chunk_fwd_fused"
+        st = lib.kda_chunk_fwd_fused(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                                     _ptr(S0), _ptr(out), _ptr(S_final), _ptr(cu_seqlens), N, Tt,
+                                     H, dk, dv, float(scale), int(chunk), io,
+                                     int(pre == "kda_gdn_"), ctypes.byref(pro), _ptr(ws), wsb,
+                                     _stream(dev))
     if st != 0:
         raise KdaError(st, fn)
     return out, S_final
 
 
-def decode_step(q, k, v, log_alpha, beta, S_inout, scale=None, out=None):
+def decode_step(q, k, v, log_alpha, beta, S_inout, scale=None, out=None, qk_l2norm=False,
+                beta_sigmoid=False, A_log=None, gate_bias=None):
     """One fused recurrent step.  q, k: [N, H, d_k]; v: [N, H, d_v]; beta:
     [N, H]; log_alpha: [N, H, d_k] (KDA) or [N, H] (Gated DeltaNet); S_inout:
     [N, H, d_k, d_v] fp32, updated in place.  Returns o."""
@@ -203,16 +265,25 @@ def decode_step(q, k, v, log_alpha, beta, S_inout, scale=None, out=None):
     if out is None:
         out = torch.empty((N, H, dv), dtype=q.dtype, device=dev)
     _check(out, "out", (N, H, dv), q.dtype, dev)
-    fn = pre + "decode_step"
-    st = getattr(lib, fn)(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S_inout),
-                          _ptr(out), N, H, dk, dv, float(scale), io, _stream(dev))
+    pro = _prologue(H, dk, pre == "kda_gdn_", dev, qk_l2norm, beta_sigmoid, A_log, gate_bias)
+    if pro is None:
+        fn = pre + "decode_step"
+        st = getattr(lib, fn)(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                              _ptr(S_inout), _ptr(out), N, H, dk, dv, float(scale), io,
+                              _stream(dev))
+    else:
+        fn = "kda_decode_step_fused"
+        st = lib.kda_decode_step_fused(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                                       _ptr(S_inout), _ptr(out), N, H, dk, dv, float(scale), io,
+                                       int(pre == "kda_gdn_"), ctypes.byref(pro), _stream(dev))
     if st != 0:
         raise KdaError(st, fn)
     return out
 
 
 def recurrent_fwd(q, k, v, log_alpha, beta, S0=None, scale=None, out=None, S_final=None,
-                  output_final_state=True):
+                  output_final_state=True, qk_l2norm=False, beta_sigmoid=False, A_log=None,
+                  gate_bias=None):
     """Token-by-token recurrence for short sequences (multi-token decode,
     speculative verification).  Shapes as chunk_fwd (KDA or Gated DeltaNet
     gates).  Pass S_final=S0 to update a state in place.  Returns (o, S_final)."""
@@ -235,17 +306,26 @@ def recurrent_fwd(q, k, v, log_alpha, beta, S0=None, scale=None, out=None, S_fin
     if S_final is None and output_final_state:
         S_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
     _check(S_final, "S_final", (B, H, dk, dv), torch.float32, dev)
-    fn = pre + "recurrent_fwd"
-    st = getattr(lib, fn)(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S0),
-                          _ptr(out), _ptr(S_final), B, T, H, dk, dv, float(scale), io,
-                          _stream(dev))
+    pro = _prologue(H, dk, pre == "kda_gdn_", dev, qk_l2norm, beta_sigmoid, A_log, gate_bias)
+    if pro is None:
+        fn = pre + "recurrent_fwd"
+        st = getattr(lib, fn)(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S0),
+                              _ptr(out), _ptr(S_final), B, T, H, dk, dv, float(scale), io,
+                              _stream(dev))
+    else:
+        fn = "kda_recurrent_fwd_fused"
+        st = lib.kda_recurrent_fwd_fused(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                                         _ptr(S0), _ptr(out), _ptr(S_final), None, B, T, H, dk,
+                                         dv, float(scale), io, int(pre == "kda_gdn_"),
+                                         ctypes.byref(pro), _stream(dev))
     if st != 0:
         raise KdaError(st, fn)
     return out, S_final
 
 
 def recurrent_fwd_varlen(q, k, v, log_alpha, beta, cu_seqlens, S0=None, scale=None, out=None,
-                         S_final=None, output_final_state=True):
+                         S_final=None, output_final_state=True, qk_l2norm=False,
+                         beta_sigmoid=False, A_log=None, gate_bias=None):
     """Token-by-token recurrence over packed sequences (varlen decode).
     Shapes as chunk_fwd_varlen (KDA or Gated DeltaNet gates); S_final=S0
     updates the states in place.  Returns (o, S_final)."""
@@ -270,10 +350,22 @@ def recurrent_fwd_varlen(q, k, v, log_alpha, beta, cu_seqlens, S0=None, scale=No
     if S_final is None and output_final_state:
         S_final = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
     _check(S_final, "S_final", (N, H, dk, dv), torch.float32, dev)
-    fn = pre + "recurrent_fwd_varlen"
-    st = getattr(lib, fn)(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S0),
-                          _ptr(out), _ptr(S_final), _ptr(cu_seqlens), N, Tt, H, dk, dv,
-                          float(scale), io, _stream(dev))
+    pro = _prologue(H, dk, pre == "kda_gdn_", dev, qk_l2norm, beta_sigmoid, A_log, gate_bias)
+    if pro is None:
+        fn = pre + "recurrent_fwd_varlen"
+        st = getattr(lib, fn)(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S0),
+                              _ptr(out), _ptr(S_final), _ptr(cu_seqlens), N, Tt, H, dk, dv,
+                              float(scale), io, _stream(dev))
+    else:
+        fn = "kda_recurrent_fwd_fused"
+        st = lib.kda_recurrent_fwd_fused(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                                         _ptr(S0), _ptr(out), _ptr(S_final), _ptr(cu_seqlens), N,
+                                         Tt, H, dk, dv, float(scale), io, int(pre == "kda_gdn_"),
+                                         ctypes.byref(pro), _stream(dev))
     if st != 0:
         raise KdaError(st, fn)
     return out, S_final
+
+
+for _f in (chunk_fwd, chunk_fwd_varlen, decode_step, recurrent_fwd, recurrent_fwd_varlen):
+    _f.__doc__ = (_f.__doc__ or "") + _TRANSFORMS_DOC

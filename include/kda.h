@@ -215,6 +215,70 @@ int kda_gdn_recurrent_fwd_varlen(const void* q, const void* k, const void* v,
                                  int T_total, int H, int d_k, int d_v, float scale, int io_dtype,
                                  void* stream);
 
+/*
+ * Input transforms applied inside the kernels to each token's raw inputs,
+ * before the step ("Linear Attention, From Scratch to Kimi 3", sections 6 and
+ * 7, the layer around the recurrence), so that no separate pass over q, k,
+ * log_alpha or beta is needed:
+ *
+ *  KDA_PRO_QK_L2NORM     q <- q / sqrt(sum q^2 + 1e-6), likewise k, per
+ *                        (token, head) vector, in fp32 (section 7: each head's
+ *                        q and k are L2-normalised)
+ *  KDA_PRO_BETA_SIGMOID  beta holds logits: beta <- 1 / (1 + exp(-beta))
+ *                        (section 6: a sigmoid applied inside the kernel)
+ *  KDA_PRO_GATE          log_alpha holds the raw gate projection g:
+ *                        log alpha = -5 sigmoid(exp(A_log[h]) (g + gate_bias))
+ *                        (section 6: -5 times a sigmoid, a log-retention in
+ *                        (-5, 0), from the projection, a learned per-channel
+ *                        bias and one learned sensitivity per head; the page's
+ *                        formula is lost, and this composition inside the
+ *                        sigmoid is this library's reading of the text)
+ *
+ * A_log is [H] fp32 (required with KDA_PRO_GATE); gate_bias is [H, d_k] fp32,
+ * or [H] with per-head gates, or NULL for zero.  Both 4-byte aligned, device
+ * memory, not overlapping any output.  Unknown flag bits return
+ * KDA_ERR_UNSUPPORTED.
+ */
+#define KDA_PRO_QK_L2NORM 1u
+#define KDA_PRO_BETA_SIGMOID 2u
+#define KDA_PRO_GATE 4u
+
+typedef struct kda_prologue {
+  uint32_t flags;          /* KDA_PRO_* bits */
+  const float* A_log;      /* [H] */
+  const float* gate_bias;  /* [H, d_k], [H] (per-head gates) or NULL */
+} kda_prologue;
+
+/*
+ * The fused forms of the three operations: every variant above through one
+ * entry point each, with optional input transforms.
+ *
+ *  cu_seqlens     NULL: N sequences of T tokens in the batched layout (as
+ *                 kda_chunk_fwd / kda_recurrent_fwd); otherwise N packed
+ *                 sequences with T = T_total (as the _varlen calls)
+ *  per_head_gate  0: KDA (log_alpha with a d_k axis); 1: Gated DeltaNet
+ *                 (log_alpha without it, as the kda_gdn_* calls)
+ *  pro            the input transforms, or NULL for none (the results are
+ *                 then those of the plain calls)
+ * Other arguments, layouts, aliasing rules and status codes as in the plain
+ * calls.
+ */
+int kda_chunk_fwd_fused(const void* q, const void* k, const void* v, const float* log_alpha,
+                        const float* beta, const float* S0, void* out, float* S_final,
+                        const int32_t* cu_seqlens, int N, int T, int H, int d_k, int d_v,
+                        float scale, int chunk, int io_dtype, int per_head_gate,
+                        const kda_prologue* pro, void* workspace, size_t workspace_bytes,
+                        void* stream);
+int kda_recurrent_fwd_fused(const void* q, const void* k, const void* v, const float* log_alpha,
+                            const float* beta, const float* S0, void* out, float* S_final,
+                            const int32_t* cu_seqlens, int N, int T, int H, int d_k, int d_v,
+                            float scale, int io_dtype, int per_head_gate,
+                            const kda_prologue* pro, void* stream);
+int kda_decode_step_fused(const void* q, const void* k, const void* v, const float* log_alpha,
+                          const float* beta, float* S_inout, void* out, int N, int H, int d_k,
+                          int d_v, float scale, int io_dtype, int per_head_gate,
+                          const kda_prologue* pro, void* stream);
+
 /* Workspace bytes kda_chunk_fwd needs for these sizes (0 if none; the
  * arguments are not validated here: unsupported sizes give 0). */
 size_t kda_chunk_fwd_workspace_size(int B, int T, int H, int d_k, int d_v, int chunk,

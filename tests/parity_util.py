@@ -23,9 +23,21 @@ def tol_for(io):
     return TOL_BF16 if io == "bf16" else TOL_F32
 
 
-def oracle_batched(d, chains=None, scale=None):
+def _pro_args(d, h, flags):
+    """Oracle keyword arguments for the input transforms of head h."""
+    if not flags:
+        return {}
+    ox = {"flags": flags}
+    if flags & oracle.GATE:
+        ox["A_log"] = to_host(d["A_log"][h:h + 1].contiguous())
+        ox["gate_bias"] = to_host(d["gate_bias"][h:h + 1].contiguous())
+    return ox
+
+
+def oracle_batched(d, chains=None, scale=None, flags=0):
     """fp64 oracle on the chains (b, h) of a batched input dict.  Returns
-    (list of [T, dv] outputs, [n, dk, dv] final states) in chain order."""
+    (list of [T, dv] outputs, [n, dk, dv] final states) in chain order.
+    ``flags``: the oracle's input transforms (A_log and gate_bias from d)."""
     B, H = d["B"], d["H"]
     if chains is None:
         chains = [(b, h) for b in range(B) for h in range(H)]
@@ -35,13 +47,13 @@ def oracle_batched(d, chains=None, scale=None):
         s0 = None if d["S0"] is None else to_host(d["S0"][b:b + 1, h:h + 1].contiguous())
         o, S = oracle.forward(sl(d["q"]), sl(d["k"]), sl(d["v"]), sl(d["g"]),
                               to_host(d["beta"][b:b + 1, :, h:h + 1].contiguous()), S0=s0,
-                              scale=scale)
+                              scale=scale, **_pro_args(d, h, flags))
         outs.append(o[0])
         states.append(S[0])
     return outs, np.stack(states) if states else np.zeros((0,))
 
 
-def oracle_varlen(d, chains=None, scale=None):
+def oracle_varlen(d, chains=None, scale=None, flags=0):
     """fp64 oracle on chains (n, h) of a packed input dict."""
     H = d["H"]
     cu = to_host(d["cu_seqlens"]).astype(np.int64)
@@ -54,7 +66,7 @@ def oracle_varlen(d, chains=None, scale=None):
         s0 = None if d["S0"] is None else to_host(d["S0"][n:n + 1, h:h + 1].contiguous())
         cu1 = np.array([0, b - a], np.int32)
         o, S = oracle.forward(sl(d["q"]), sl(d["k"]), sl(d["v"]), sl(d["g"]), sl(d["beta"]),
-                              S0=s0, scale=scale, cu_seqlens=cu1)
+                              S0=s0, scale=scale, cu_seqlens=cu1, **_pro_args(d, h, flags))
         outs.append(o[0])
         states.append(S[0])
     return outs, np.stack(states)

@@ -31,7 +31,8 @@ def test_header_declares_the_entry_points():
     for want in ("kda_chunk_fwd", "kda_chunk_fwd_varlen", "kda_decode_step",
                  "kda_recurrent_fwd", "kda_recurrent_fwd_varlen", "kda_gdn_chunk_fwd",
                  "kda_gdn_chunk_fwd_varlen", "kda_gdn_decode_step", "kda_gdn_recurrent_fwd",
-                 "kda_gdn_recurrent_fwd_varlen",
+                 "kda_gdn_recurrent_fwd_varlen", "kda_chunk_fwd_fused", "kda_recurrent_fwd_fused",
+                 "kda_decode_step_fused",
                  "kda_chunk_fwd_workspace_size", "kda_chunk_fwd_varlen_workspace_size",
                  "kda_status_string", "kda_version"):
         assert want in names
@@ -169,6 +170,31 @@ def test_gdn_validation(lib):
     cv = lib.kda_gdn_chunk_fwd_varlen
     assert cv(P[0], P[1], P[2], P[3], P[4], None, P[5], P[6], P[7], -1, 10, 2, 64, 64, 0.1, 64, 0,
               None, 0, None) == -2
+
+
+def test_fused_validation(lib):
+    """The fused calls validate the prologue before anything else happens."""
+    from gated_delta_rule_06_amd.kda import _Prologue
+    f = lib.kda_chunk_fwd_fused
+    pro = lambda flags, a=P[8], b=P[9]: ctypes.byref(_Prologue(flags, a, b))
+    args = lambda **kw: (P[0], P[1], P[2], P[3], P[4], None, kw.get("out", P[5]), P[6],
+                         kw.get("cu", None), kw.get("N", 2), 64, 2, 128, 128, 0.1, 64, 1,
+                         kw.get("ph", 0), kw.get("pro", None), None, 0, None)
+    assert f(*args(pro=pro(8))) == -3                       # unknown flag bit
+    assert f(*args(pro=pro(4, a=None))) == -1               # gate without A_log
+    assert f(*args(pro=pro(4, a=ctypes.c_void_p(P[8].value + 2)))) == -7
+    assert f(*args(pro=pro(4, b=P[5]))) == -6               # gate bias is the output
+    assert f(*args(ph=2)) == -3
+    assert f(*args(N=0, pro=pro(7))) == 0
+    assert f(*args(N=-1)) == -2
+    r = lib.kda_recurrent_fwd_fused
+    assert r(P[0], P[1], P[2], P[3], P[4], None, P[5], P[6], None, 2, 4, 2, 64, 64, 0.1, 0, 0,
+             pro(4, a=None), None) == -1
+    d = lib.kda_decode_step_fused
+    assert d(P[0], P[1], P[2], P[3], P[4], P[5], P[6], 4, 2, 128, 128, 0.1, 1, 0, pro(16),
+             None) == -3
+    assert d(P[0], P[1], P[2], P[3], P[4], P[5], P[6], 4, 2, 128, 128, 0.1, 1, 0,
+             pro(4, b=P[6]), None) == -6                    # gate bias is the output
 
 
 def test_alignment_validation(lib):

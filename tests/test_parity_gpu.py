@@ -51,6 +51,33 @@ def test_chunk_fwd_matches_oracle(B, T, H, dk, dv, io, with_S0):
     assert_close(go, gs, ro, rs, tol_for(io), "chunk")
 
 
+@pytest.mark.parametrize("dk,dv,io,strong_channels", [(128, 128, "bf16", None),
+                                                      (128, 128, "bf16", 8),
+                                                      (128, 64, "bf16", 8),
+                                                      (64, 128, "bf16", None),
+                                                      (64, 64, "f32", 4)])
+def test_strong_decay_takes_the_guard_path(dk, dv, io, strong_channels):
+    """Chunks whose decay in some key channel falls below 2^-100 (log alpha =
+    -3 per token: e^-192 over a chunk) must take the token-by-token guard
+    path, also when only a few channels decay that fast (the detection must
+    see every lane's channels); the result must match the oracle."""
+    note("strong decay dk=%d dv=%d io=%s channels=%s" % (dk, dv, io, strong_channels))
+    d = inputs.prefill_inputs(2, 150, 2, dk, dv, io=io, seed=dk + dv, with_S0=True, device=DEV)
+    if strong_channels is None:
+        d["g"] = torch.full_like(d["g"], -3.0)
+    else:
+        gen = torch.Generator(device=DEV)
+        gen.manual_seed(5)
+        idx = torch.randperm(dk, generator=gen, device=DEV)[:strong_channels]
+        d["g"][..., idx] = -3.0
+    o, S = kda().chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], S0=d["S0"])
+    torch.cuda.synchronize()
+    chains = [(b, h) for b in range(2) for h in range(2)]
+    ro, rs = oracle_batched(d, chains)
+    go, gs = gpu_chains_batched(o, S, chains)
+    assert_close(go, gs, ro, rs, tol_for(io), "strong decay")
+
+
 def test_prefill_h16_t4096_with_S0():
     """The B=1, H=16, T=4096, d=128 bf16 workload with a random fp32 S0."""
     cfg = inputs.CONFIGS["prefill_h16_s0"]
