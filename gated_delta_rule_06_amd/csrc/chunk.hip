@@ -306,6 +306,11 @@ struct RawWords {
   __device__ __forceinline__ uint32_t word(int i) const {
     return i < 4 * N16 ? q[i / 4][i % 4] : d[i - 4 * N16];
   }
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int i = 0; i < (N16 > 0 ? N16 : 1); ++i) q[i] = u32x4{0u, 0u, 0u, 0u};
+    d = u32x2{0u, 0u};
+  }
 };
 
 // N elements of I/O type Io as floats
@@ -515,11 +520,31 @@ struct ChunkKernel {
     }
   }
 
+  // ---------------------------------------------------------------- windows
+  // Zero the raw inputs of the tokens outside [lo, hi): they become identity
+  // tokens (q = k = v = 0, alpha = 1, beta = 0).
+  static __device__ __forceinline__ void mask_window(Raw& r, int lo, int hi) {
+    const int l = lane_fresh();
+    const int tg = l / CQ;
+#pragma unroll
+    for (int t = 0; t < TPL; ++t) {
+      const int i = TPL * tg + t;
+      if (i < lo || i >= hi) {
+        r.q[t].w.zero();
+        r.k[t].w.zero();
+        r.v[t].w.zero();
+        r.g[t].zero();
+        r.gs[t] = 0.f;
+      }
+    }
+    if (l < lo || l >= hi) r.beta = 0.f;   // lane l holds beta of token l
+  }
+
   // ---------------------------------------------------------------- prep
   // Cumulative decay and the five gate-scaled operands; returns the chunk's
   // guard flag (1 = some channel decays below KDA_GAMMA_MIN).
   static __device__ __forceinline__ int prep(const Raw& r, LDS char* smem, float scale,
-                                             const Prologue& pro, float ea, int clen) {
+                                             const Prologue& pro, float ea, int lo, int hi) {
     const int w = threadIdx.x >> 6, l = lane_fresh();
     const int tg = l / CQ, cq = l % CQ;
     const int kc0 = w * (DK / NW) + CPL * cq;
@@ -538,8 +563,9 @@ struct ChunkKernel {
       BT[l] = (Cfg::FU && (pro.flags & PRO_BETA_SIGMOID)) ? sigmoid_f(r.beta) : r.beta;
     }
     // gate transform (FU): the raw gate through -5 sigmoid(exp(A_log) (g + bias)).
-    // Rows past the chunk's end read as zeros and must stay identity tokens
-    // (alpha = 1), so the transform leaves their gate at 0.
+    // Rows outside [lo, hi) (past the chunk's end, or outside a window) read
+    // as zeros and must stay identity tokens (alpha = 1), so the transform
+    // leaves their gate at 0.
     const bool xg = Cfg::FU && (pro.flags & PRO_GATE);
     float gbias[CPL];
     if (xg) {
@@ -559,7 +585,7 @@ struct ChunkKernel {
       float ct[TPL];
 #pragma unroll
       for (int t = 0; t < TPL; ++t) {
-        const bool real = TPL * tg + t < clen;
+        const bool real = TPL * tg + t >= lo && TPL * tg + t < hi;
         const float a = __expf(xg ? (real ? gate_logalpha(r.gs[t], ea, gbias[0]) : 0.f) : r.gs[t]);
         ct[t] = (t == 0) ? a : ct[t - 1] * a;
       }
@@ -589,7 +615,7 @@ struct ChunkKernel {
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
           const float gr = __uint_as_float(r.g[t].word(c));
-          const bool real = TPL * tg + t < clen;
+          const bool real = TPL * tg + t >= lo && TPL * tg + t < hi;
           const float a = __expf(xg ? (real ? gate_logalpha(gr, ea, gbias[c]) : 0.f) : gr);
           cp[t][c] = (t == 0) ? a : cp[t - 1][c] * a;
         }
@@ -907,7 +933,8 @@ struct ChunkKernel {
   static __device__ __forceinline__ void scan_step(LDS char* smem, f32x4 (&S)[MTK][NVT],
                                                    f32x4 (&Y)[4][NVT], f32x4 (&Ob)[4][NVT],
                                                    void* out,
-                                                   size_t row_base, int H, int h, int clen) {
+                                                   size_t row_base, int H, int h, int clen,
+                                                   int lo = 0) {
     const int w = threadIdx.x >> 6, l = lane_fresh();
     const LDS T* QG = (const LDS T*)(smem + Cfg::OFF_QG);
     const LDS T* KG = (const LDS T*)(smem + Cfg::OFF_KG);
@@ -1010,7 +1037,7 @@ struct ChunkKernel {
         const int p = p0 + threadIdx.x;
         const int i = p / PER_ROW, c = (p % PER_ROW) * PIECE;
         const u32x4 val = *lds_ptr<const u32x4>(OST + i * Cfg::LD_OS + c);
-        buf_store16(ro, i * srow + c * E, val);
+        if (i >= lo) buf_store16(ro, i * srow + c * E, val);   // rows [lo, clen)
       }
     }
 
@@ -1113,6 +1140,40 @@ struct ChunkKernel {
     }
   }
 
+  // ---------------------------------------------------------------- middle interval
+  // One interval for the tiles, the inverses and the products that need no
+  // inverse: wave I < 4 forms diagonal tile (I, I) and inverts it itself (one
+  // wave's LDS accesses complete in order), waves 4-7 form the six
+  // off-diagonal pairs; each wave's case is one scheduling region, so VALU
+  // (inverse) and MFMA (tiles, Y, S^T QG^T) interleave.
+  static __device__ __forceinline__ void middle(LDS char* smem, f32x4 (&S)[MTK][NVT],
+                                                f32x4 (&Y)[4][NVT], f32x4 (&O)[4][NVT]) {
+    const int w = threadIdx.x >> 6;
+    if (NW == 8) {
+      switch (__builtin_amdgcn_readfirstlane(w)) {
+        case 0: tile_qk(smem, 0, 0); invert_diag<0>(smem); scan_y(smem, S, Y, O); break;
+        case 1: tile_qk(smem, 1, 1); invert_diag<1>(smem); scan_y(smem, S, Y, O); break;
+        case 2: tile_qk(smem, 2, 2); invert_diag<2>(smem); scan_y(smem, S, Y, O); break;
+        case 3: tile_qk(smem, 3, 3); invert_diag<3>(smem); scan_y(smem, S, Y, O); break;
+        case 4: tile_qk(smem, 1, 0); tile_qk(smem, 3, 2); scan_y(smem, S, Y, O); break;
+        case 5: tile_qk(smem, 2, 0); tile_qk(smem, 2, 1); scan_y(smem, S, Y, O); break;
+        case 6: tile_qk(smem, 3, 0); scan_y(smem, S, Y, O); break;
+        default: tile_qk(smem, 3, 1); scan_y(smem, S, Y, O); break;
+      }
+    } else {
+      switch (__builtin_amdgcn_readfirstlane(w)) {
+        case 0: tile_qk(smem, 0, 0); invert_diag<0>(smem); tile_qk(smem, 1, 0);
+                tile_qk(smem, 2, 0); scan_y(smem, S, Y, O); break;
+        case 1: tile_qk(smem, 1, 1); invert_diag<1>(smem); tile_qk(smem, 2, 1);
+                tile_qk(smem, 3, 0); scan_y(smem, S, Y, O); break;
+        case 2: tile_qk(smem, 2, 2); invert_diag<2>(smem); tile_qk(smem, 3, 1);
+                scan_y(smem, S, Y, O); break;
+        default: tile_qk(smem, 3, 3); invert_diag<3>(smem); tile_qk(smem, 3, 2);
+                 scan_y(smem, S, Y, O); break;
+      }
+    }
+  }
+
   // ---------------------------------------------------------------- driver
   static __device__ __forceinline__ void run(const void* q, const void* k, const void* v,
                                              const float* g, const float* beta, const float* S0,
@@ -1175,7 +1236,7 @@ struct ChunkKernel {
         norm_partials(raw, smem);
         __syncthreads();
       }
-      const int bad = prep(raw, smem, scale, pro, ea, clen);
+      const int bad = prep(raw, smem, scale, pro, ea, 0, clen);
       // the vote runs in every lane: inside the lane-0 branch it would only
       // see lane 0's flag (the scan path sets it in other lanes)
       const int wave_bad = __any(bad);
@@ -1189,41 +1250,49 @@ struct ChunkKernel {
       if (!any_bad) {
         load_raw<LOAD_V>(raw, offs, q, k, v, g, beta, next, H, h, nlen);
         compiler_fence();
-        // one interval for the tiles, the inverses and the products that need
-        // no inverse: wave I < 4 forms diagonal tile (I, I) and inverts it
-        // itself (one wave's LDS accesses complete in order), waves 4-7 form
-        // the six off-diagonal pairs; each wave's case is one scheduling
-        // region, so VALU (inverse) and MFMA (tiles, Y, S^T QG^T) interleave
         f32x4 Y[4][NVT], O[4][NVT];
-        if (NW == 8) {
-          switch (__builtin_amdgcn_readfirstlane(w)) {
-            case 0: tile_qk(smem, 0, 0); invert_diag<0>(smem); scan_y(smem, S, Y, O); break;
-            case 1: tile_qk(smem, 1, 1); invert_diag<1>(smem); scan_y(smem, S, Y, O); break;
-            case 2: tile_qk(smem, 2, 2); invert_diag<2>(smem); scan_y(smem, S, Y, O); break;
-            case 3: tile_qk(smem, 3, 3); invert_diag<3>(smem); scan_y(smem, S, Y, O); break;
-            case 4: tile_qk(smem, 1, 0); tile_qk(smem, 3, 2); scan_y(smem, S, Y, O); break;
-            case 5: tile_qk(smem, 2, 0); tile_qk(smem, 2, 1); scan_y(smem, S, Y, O); break;
-            case 6: tile_qk(smem, 3, 0); scan_y(smem, S, Y, O); break;
-            default: tile_qk(smem, 3, 1); scan_y(smem, S, Y, O); break;
-          }
-        } else {
-          switch (__builtin_amdgcn_readfirstlane(w)) {
-            case 0: tile_qk(smem, 0, 0); invert_diag<0>(smem); tile_qk(smem, 1, 0);
-                    tile_qk(smem, 2, 0); scan_y(smem, S, Y, O); break;
-            case 1: tile_qk(smem, 1, 1); invert_diag<1>(smem); tile_qk(smem, 2, 1);
-                    tile_qk(smem, 3, 0); scan_y(smem, S, Y, O); break;
-            case 2: tile_qk(smem, 2, 2); invert_diag<2>(smem); tile_qk(smem, 3, 1);
-                    scan_y(smem, S, Y, O); break;
-            default: tile_qk(smem, 3, 3); invert_diag<3>(smem); tile_qk(smem, 3, 2);
-                     scan_y(smem, S, Y, O); break;
-          }
-        }
+        middle(smem, S, Y, O);
         compiler_fence();
         load_raw<LOAD_Q | LOAD_K>(raw, offs, q, k, v, g, beta, next, H, h, nlen);
         __syncthreads();                                         // B2
         scan_step(smem, S, Y, O, out, row_base + c0, H, h, clen);
       } else {
-        recurrent_chunk(S, q, k, v, g, beta, out, row_base + c0, H, h, clen, scale, pro, ea);
+        // Some channel decays by more than 2^100 over the chunk, beyond what
+        // one reference point (the chunk start) can scale: redo the chunk as
+        // 16-token windows, each a full chunk step with the other rows as
+        // identity tokens (a window stays in range unless log alpha averages
+        // below about -4.3 over it); a window that still decays too fast runs
+        // the recurrence token by token.  The windows use their own raw
+        // registers; the next chunk's gates are already on their way, and
+        // its q, k, v follow as on the guard path before, so the loads in
+        // flight at the top of the loop are the same on both paths.
+        for (int lo = 0; lo < clen; lo += 16) {
+          const int hi = (lo + 16) < clen ? (lo + 16) : clen;
+          Raw rw;
+          load_raw<LOAD_ALL>(rw, offs, q, k, v, g, beta, row_base + c0, H, h, clen);
+          mask_window(rw, lo, hi);
+          if (Cfg::FU && (pro.flags & PRO_L2NORM)) {
+            norm_partials(rw, smem);
+            __syncthreads();
+          }
+          const int wbad = prep(rw, smem, scale, pro, ea, lo, hi);
+          const int wave_wbad = __any(wbad);
+          if (lane_fresh() == 0) FL[w] = wave_wbad ? 1 : 0;
+          __syncthreads();
+          int any_wbad = 0;
+#pragma unroll
+          for (int i = 0; i < NW; ++i) any_wbad |= FL[i];
+          if (!any_wbad) {
+            f32x4 Y[4][NVT], O[4][NVT];
+            middle(smem, S, Y, O);
+            __syncthreads();
+            scan_step(smem, S, Y, O, out, row_base + c0, H, h, hi, lo);
+          } else {
+            recurrent_chunk(S, q, k, v, g, beta, out, row_base + c0 + lo, H, h, hi - lo, scale,
+                            pro, ea);
+            __syncthreads();
+          }
+        }
         load_raw<LOAD_Q | LOAD_K | LOAD_V>(raw, offs, q, k, v, g, beta, next, H, h, nlen);
         __syncthreads();                                         // LDS reuse
       }

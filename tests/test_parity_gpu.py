@@ -51,25 +51,29 @@ def test_chunk_fwd_matches_oracle(B, T, H, dk, dv, io, with_S0):
     assert_close(go, gs, ro, rs, tol_for(io), "chunk")
 
 
-@pytest.mark.parametrize("dk,dv,io,strong_channels", [(128, 128, "bf16", None),
-                                                      (128, 128, "bf16", 8),
-                                                      (128, 64, "bf16", 8),
-                                                      (64, 128, "bf16", None),
-                                                      (64, 64, "f32", 4)])
-def test_strong_decay_takes_the_guard_path(dk, dv, io, strong_channels):
-    """Chunks whose decay in some key channel falls below 2^-100 (log alpha =
-    -3 per token: e^-192 over a chunk) must take the token-by-token guard
-    path, also when only a few channels decay that fast (the detection must
-    see every lane's channels); the result must match the oracle."""
-    note("strong decay dk=%d dv=%d io=%s channels=%s" % (dk, dv, io, strong_channels))
+@pytest.mark.parametrize("dk,dv,io,strong_channels,gval", [(128, 128, "bf16", None, -3.0),
+                                                           (128, 128, "bf16", 8, -3.0),
+                                                           (128, 64, "bf16", 8, -3.0),
+                                                           (64, 128, "bf16", None, -3.0),
+                                                           (64, 64, "f32", 4, -3.0),
+                                                           (128, 128, "bf16", 8, -5.0),
+                                                           (64, 64, "f32", None, -5.0)])
+def test_strong_decay_takes_the_guard_path(dk, dv, io, strong_channels, gval):
+    """Chunks whose decay in some key channel falls below 2^-100 must leave the
+    one-reference fast path, also when only a few channels decay that fast
+    (the detection must see every lane's channels).  At log alpha = -3 per
+    token (e^-192 over a chunk) each 16-token window fits (e^-48); at -5
+    (e^-80 per window) the windows run token by token.  Results must match
+    the oracle."""
+    note("strong decay dk=%d dv=%d io=%s channels=%s g=%.1f" % (dk, dv, io, strong_channels, gval))
     d = inputs.prefill_inputs(2, 150, 2, dk, dv, io=io, seed=dk + dv, with_S0=True, device=DEV)
     if strong_channels is None:
-        d["g"] = torch.full_like(d["g"], -3.0)
+        d["g"] = torch.full_like(d["g"], gval)
     else:
         gen = torch.Generator(device=DEV)
         gen.manual_seed(5)
         idx = torch.randperm(dk, generator=gen, device=DEV)[:strong_channels]
-        d["g"][..., idx] = -3.0
+        d["g"][..., idx] = gval
     o, S = kda().chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], S0=d["S0"])
     torch.cuda.synchronize()
     chains = [(b, h) for b in range(2) for h in range(2)]
