@@ -10,7 +10,8 @@ kda_decode_step calls) and reports its steps/s, and the multi-token decode
 workload (the same states, 256 sequences of U{1..8} new tokens, one
 kda_recurrent_fwd_varlen call updating them in place) and the Gated DeltaNet
 prefill (the headline shapes with one gate per token and head,
-kda_gdn_chunk_fwd).
+kda_gdn_chunk_fwd) and the prefill of raw layer inputs with the in-kernel
+input transforms (q/k L2 norm, beta sigmoid, the -5 sigmoid gate).
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 
@@ -197,6 +198,37 @@ def main():
     del dg
     torch.cuda.empty_cache()
 
+    # ---------------------------------------------------------------- fused input transforms
+    log("generating raw layer inputs for the in-kernel transforms")
+    dr0 = inputs.prefill_inputs(P["B"], P["T"], P["H"], P["dk"], P["dv"], io=P["io"], seed=0,
+                                with_S0=False, device=dev)
+    dr0 = inputs.raw_layer_inputs(dr0, P["H"], P["dk"], seed=0, device=dev, gate_mu=-6.0)
+
+    def fused_step():
+        kda.chunk_fwd(dr0["q"], dr0["k"], dr0["v"], dr0["g"], dr0["beta"], S0=None, out=out,
+                      S_final=Sf, qk_l2norm=True, beta_sigmoid=True, A_log=dr0["A_log"],
+                      gate_bias=dr0["gate_bias"])
+
+    for _ in range(args.warmup):
+        fused_step()
+    torch.cuda.synchronize()
+    evf = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for a, b in evf:
+        a.record(stream)
+        fused_step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    fu_wall = (time.perf_counter() - t0) / args.steps
+    fu_ms = float(np.mean([a.elapsed_time(b) for a, b in evf]))
+    fu_b = alg_b + P["H"] * 4 + P["H"] * P["dk"] * 4          # plus A_log and the gate bias
+    fu_gbs = fu_b / (fu_ms * 1e-3) / 1e9
+    log("fused prefill: %.3f ms/step (wall), kernel %.3f ms avg, %.3e tokens/s, %.0f GB/s"
+        % (fu_wall * 1e3, fu_ms, tokens / fu_wall, fu_gbs))
+    del dr0
+    torch.cuda.empty_cache()
+
     # ---------------------------------------------------------------- decode
     D = DECODE
     log("generating decode inputs", D)
@@ -347,6 +379,14 @@ def main():
                                      "traffic": measured_traffic("gdn", "chunk.hip"),
                                      "kernel": "chunk_fwd_kernel<128,128,bf16,scalar gate>",
                                      "alg_bytes_per_launch": gdn_b, "avg_launch_ms": gdn_ms}},
+        "fused_prefill": {"workload": "prefill_b8_h32_t8192_raw_inputs_in_kernel_transforms",
+                          "transforms": "q/k L2 norm, beta sigmoid, -5 sigmoid gate",
+                          "tokens_per_s": tokens / fu_wall, "ms_per_step": fu_wall * 1e3,
+                          "roofline": {"bound": "hbm", "achieved": fu_gbs, "peak": HBM_PEAK_GBS,
+                                       "unit": "GB/s", "frac": fu_gbs / HBM_PEAK_GBS,
+                                       "traffic": measured_traffic("fused", "chunk.hip"),
+                                       "kernel": "chunk_fwd_kernel<128,128,bf16,transforms>",
+                                       "alg_bytes_per_launch": fu_b, "avg_launch_ms": fu_ms}},
         "recurrent": {"workload": "multi_token_decode_n256_h32_len1to8",
                       "tokens_per_call": rec_tokens, "calls": R["calls"],
                       "us_per_call": rec_wall * 1e6, "tokens_per_s": rec_tokens / rec_wall,

@@ -139,11 +139,12 @@ def decode_inputs(N, H, dk, dv, steps, io="bf16", seed=0, s0_std=0.02, device="c
     return d
 
 
-def raw_layer_inputs(d, H, dk, seed=0, gate="kda", strong_decay=False, device="cpu"):
+def raw_layer_inputs(d, H, dk, seed=0, gate="kda", strong_decay=False, device="cpu",
+                     gate_mu=-4.0):
     """Turn an input dict into raw layer inputs for the in-kernel transforms:
     q and k scaled per (token, head) by exp(N(0, 0.5)) (no longer unit),
     beta replaced by logits ~ N(0, 1), log_alpha replaced by a raw gate
-    projection ~ N(-4, 1) (N(3, 1) with strong_decay), plus A_log [H] ~
+    projection ~ N(gate_mu, 1) (N(3, 1) with strong_decay), plus A_log [H] ~
     N(0, 0.3^2) and a gate bias ~ N(0, 0.5^2) of shape [H, dk] ([H] for
     per-head gates).  The I/O dtype of q and k is kept."""
     gen = _gen(device, seed + 7919)
@@ -152,7 +153,7 @@ def raw_layer_inputs(d, H, dk, seed=0, gate="kda", strong_decay=False, device="c
         c = torch.exp(0.5 * torch.randn(qk_shape[:-1] + (1,), generator=gen, device=device))
         d[name] = (d[name].float() * c).to(d[name].dtype)
     d["beta"] = torch.randn(d["beta"].shape, generator=gen, device=device)
-    mu = 3.0 if strong_decay else -4.0
+    mu = 3.0 if strong_decay else gate_mu
     d["g"] = mu + torch.randn(d["g"].shape, generator=gen, device=device)
     d["A_log"] = 0.3 * torch.randn((H,), generator=gen, device=device)
     bshape = (H,) if gate == "gdn" else (H, dk)
