@@ -229,6 +229,46 @@ def main():
     del dr0
     torch.cuda.empty_cache()
 
+    # ---------------------------------------------------------------- the other prefill configs
+    def timed_calls(fn, n, warm=5):
+        for _ in range(warm):
+            fn()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(n)]
+        for a, b in evs:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+    c2 = inputs.CONFIGS["prefill_h16_s0"]
+    log("generating the B1 H16 T4096 prefill with S0")
+    d2 = inputs.prefill_inputs(c2["B"], c2["T"], c2["H"], c2["dk"], c2["dv"], io=c2["io"], seed=0,
+                               with_S0=True, device=dev)
+    c2_ms = timed_calls(lambda: kda.chunk_fwd(d2["q"], d2["k"], d2["v"], d2["g"], d2["beta"],
+                                              S0=d2["S0"]), 20)
+    c2_b = prefill_alg_bytes(c2["B"], c2["T"], c2["H"], c2["dk"], c2["dv"], c2["io"], with_S0=True)
+    c2_chunks = c2["T"] // 64
+    log("prefill B1 H16 T4096 + S0: %.1f us per launch (%d chains of %d chunks on %d CUs)"
+        % (c2_ms * 1e3, c2["B"] * c2["H"], c2_chunks, 256))
+    del d2
+    c5 = inputs.CONFIGS["varlen_16seq_h32"]
+    lens5 = inputs.varlen_lengths(c5["n_seq"], c5["lo"], c5["hi"], seed=0)
+    log("generating the 16-sequence packed prefill (%d tokens)" % int(lens5.sum()))
+    d5 = inputs.varlen_inputs(lens5, c5["H"], c5["dk"], c5["dv"], io=c5["io"], seed=0,
+                              long_channels=c5["long_channels"], device=dev)
+    c5_ms = timed_calls(lambda: kda.chunk_fwd_varlen(d5["q"], d5["k"], d5["v"], d5["g"], d5["beta"],
+                                                     d5["cu_seqlens"]), 5, warm=2)
+    c5_tokens = int(lens5.sum())
+    c5_b = c5_tokens * c5["H"] * 1540 + c5["n_seq"] * c5["H"] * c5["dk"] * c5["dv"] * 4
+    c5_longest = int(-(-int(lens5.max()) // 64))
+    log("varlen 16 sequences: %.2f ms per launch, %.0f GB/s; longest chain %d chunks"
+        % (c5_ms, c5_b / (c5_ms * 1e-3) / 1e9, c5_longest))
+    del d5
+    torch.cuda.empty_cache()
+
     # ---------------------------------------------------------------- decode
     D = DECODE
     log("generating decode inputs", D)
@@ -387,6 +427,18 @@ def main():
                                        "traffic": measured_traffic("fused", "chunk.hip"),
                                        "kernel": "chunk_fwd_kernel<128,128,bf16,transforms>",
                                        "alg_bytes_per_launch": fu_b, "avg_launch_ms": fu_ms}},
+        "prefill_h16_t4096_s0": {
+            "workload": "prefill_b1_h16_t4096_with_S0", "avg_launch_ms": c2_ms,
+            "tokens_per_s": c2["B"] * c2["T"] / (c2_ms * 1e-3),
+            "achieved_gbs": c2_b / (c2_ms * 1e-3) / 1e9, "alg_bytes_per_launch": c2_b,
+            "bound": "latency: 16 chains of %d serial chunks on 256 CUs" % c2_chunks,
+            "us_per_chunk_step": c2_ms * 1e3 / c2_chunks},
+        "varlen_16seq_h32": {
+            "workload": "varlen_16_sequences_U1024_65536_h32", "tokens": c5_tokens,
+            "avg_launch_ms": c5_ms, "tokens_per_s": c5_tokens / (c5_ms * 1e-3),
+            "achieved_gbs": c5_b / (c5_ms * 1e-3) / 1e9, "alg_bytes_per_launch": c5_b,
+            "frac_hbm": c5_b / (c5_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "longest_chain_chunks": c5_longest},
         "recurrent": {"workload": "multi_token_decode_n256_h32_len1to8",
                       "tokens_per_call": rec_tokens, "calls": R["calls"],
                       "us_per_call": rec_wall * 1e6, "tokens_per_s": rec_tokens / rec_wall,

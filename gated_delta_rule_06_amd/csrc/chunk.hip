@@ -48,6 +48,9 @@
 //    on the same on-chip state instead; outputs are identical up to rounding.
 #include "common.h"
 
+// Packed sequences up to this count are started longest first.
+#define KDA_LPT_MAX 256
+
 namespace kda {
 
 // ============================================================ lane shifts
@@ -393,6 +396,7 @@ struct ChunkCfg {
   static constexpr int SZ_NM = FU ? 2 * C * NW * 4 + DK * 4 : 0;
   static constexpr int LDS_TOTAL = OFF_NM + SZ_NM;
   static_assert(LDS_TOTAL <= 160 * 1024, "LDS budget");
+  static_assert(LDS_TOTAL >= (KDA_LPT_MAX + 1) * 4, "LDS holds the length ranking");
   static_assert(OFF_KG % 16 == 0 && OFF_KI % 16 == 0 && OFF_RD % 16 == 0 && OFF_OS % 16 == 0 && OFF_FL % 16 == 0 &&
                 OFF_BV % 16 == 0 && OFF_AQ % 16 == 0 && OFF_RT % 16 == 0 && OFF_TD % 16 == 0 &&
                 OFF_GL % 16 == 0 && OFF_BT % 16 == 0 && OFF_KT % 16 == 0 && OFF_SC % 16 == 0 && (LD_K * SZ) % 16 == 0 &&
@@ -1326,9 +1330,32 @@ template <class Cfg>
 __global__ __launch_bounds__(Cfg::NTHREADS, 1) void chunk_fwd_varlen_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, const float* S0, void* out,
-    float* S_final, const int32_t* __restrict__ cu_seqlens, int H, float scale, Prologue pro) {
-  const int chain = blockIdx.x;   // n * H + h
-  const int n = chain / H, h = chain % H;
+    float* S_final, const int32_t* __restrict__ cu_seqlens, int N, int H, float scale,
+    Prologue pro) {
+  // Longest sequences first: workgroup b takes head b % H of the (b / H)-th
+  // longest sequence (ties by index), so that with skewed lengths the long
+  // chains start in the first wave of workgroups instead of setting the tail.
+  // Each workgroup ranks the lengths itself, from an LDS copy (up to
+  // KDA_LPT_MAX sequences; beyond that the order is the packed order).
+  const int r = blockIdx.x / H, h = blockIdx.x % H;
+  int n = r;
+  if (N <= KDA_LPT_MAX) {
+    extern __shared__ __attribute__((aligned(16))) char smem_[];
+    int* lens = reinterpret_cast<int*>(smem_);
+    int* sel = lens + KDA_LPT_MAX;
+    for (int m = threadIdx.x; m < N; m += Cfg::NTHREADS) lens[m] = cu_seqlens[m + 1] - cu_seqlens[m];
+    __syncthreads();
+    for (int m = threadIdx.x; m < N; m += Cfg::NTHREADS) {
+      const int lm = lens[m];
+      int rank = 0;
+      for (int j = 0; j < N; ++j) rank += (lens[j] > lm) || (lens[j] == lm && j < m);
+      if (rank == r) *sel = m;
+    }
+    __syncthreads();
+    n = *sel;
+    __syncthreads();   // the LDS is the kernel's from here on
+  }
+  const int chain = n * H + h;
   const int b0 = cu_seqlens[n], b1 = cu_seqlens[n + 1];
   ChunkKernel<Cfg>::run(q, k, v, g, beta, S0, out, S_final, (size_t)b0, b1 - b0, H, h,
                         (size_t)chain, scale, pro);
@@ -1346,7 +1373,7 @@ static hipError_t launch_chunk_t(const void* q, const void* k, const void* v, co
                                        hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3(n_seq * H), dim3(Cfg::NTHREADS), bytes, stream, q, k, v, g,
-                       beta, S0, out, S_final, cu, H, scale, pro);
+                       beta, S0, out, S_final, cu, n_seq, H, scale, pro);
   } else {
     auto kern = chunk_fwd_kernel<Cfg>;
     hipError_t e = hipFuncSetAttribute((const void*)kern,
