@@ -394,7 +394,10 @@ struct ChunkCfg {
   // head's gate biases [DK]
   static constexpr int OFF_NM = OFF_FL + 64;
   static constexpr int SZ_NM = FU ? 2 * C * NW * 4 + DK * 4 : 0;
-  static constexpr int LDS_TOTAL = OFF_NM + SZ_NM;
+  // SG only: per-token factors of the raw operands, C floats each (SV_*)
+  static constexpr int OFF_SV = OFF_NM + SZ_NM;
+  static constexpr int SZ_SV = SG ? 7 * C * 4 : 0;
+  static constexpr int LDS_TOTAL = OFF_SV + SZ_SV;
   static_assert(LDS_TOTAL <= 160 * 1024, "LDS budget");
   static_assert(LDS_TOTAL >= (KDA_LPT_MAX + 1) * 4, "LDS holds the length ranking");
   static_assert(OFF_KG % 16 == 0 && OFF_KI % 16 == 0 && OFF_RD % 16 == 0 && OFF_OS % 16 == 0 && OFF_FL % 16 == 0 &&
@@ -544,11 +547,149 @@ struct ChunkKernel {
     if (l < lo || l >= hi) r.beta = 0.f;   // lane l holds beta of token l
   }
 
+  // ---------------------------------------------------------------- raw operands (SG)
+  // 8 consecutive channels of one row straight from the raw words (the I/O
+  // type is the operand type), sign bits XOR-ed with `sign`.
+  template <int NB>
+  static __device__ __forceinline__ void st_raw8(LDS T* row, int c0, const RawWords<NB>& w,
+                                                 uint32_t sign) {
+    if constexpr (Op::PERMUTED) {
+      *lds_ptr<u32x2>(row + Op::perm_pos(c0)) = u32x2{w.word(0) ^ sign, w.word(1) ^ sign};
+      *lds_ptr<u32x2>(row + Op::perm_pos(c0 + 4)) = u32x2{w.word(2) ^ sign, w.word(3) ^ sign};
+    } else {
+      T y[8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) y[c] = __uint_as_float(w.word(c) ^ sign);
+      st_chunk(row + c0, y);
+    }
+  }
+  // Gated DeltaNet (one gate per token).  With a scalar decay the gate
+  // factors of every product are per-token scalars, so the operands stay the
+  // raw inputs: QG = q, KG = k, -KI = -k (and the key-major -k), -V, and the
+  // scalars go to LDS, C floats each, for the epilogues of the products:
+  //   SV_G   gamma_i = log2 Gamma_i (prefix sum of log2 alpha over the chunk)
+  //   SV_RQ  rq_i = scale / |q_i|      SV_RK  rk_i = 1 / |k_i|  (1 without the
+  //                                    L2-norm transform)
+  //   SV_BK  beta_i rk_i               SV_FY  beta_i Gamma_i rk_i   (Y)
+  //   SV_FO  Gamma_i rq_i   (O)        SV_FS  rk_i Gamma_L / Gamma_i (S update)
+  // Every factor is at most 1 in size (for log alpha <= 0): no decay is too
+  // strong for this form, so there is no guard.
+  enum { SV_G = 0, SV_RQ = 1, SV_RK = 2, SV_BK = 3, SV_FY = 4, SV_FO = 5, SV_FS = 6 };
+  static __device__ __forceinline__ void prep_sg(const Raw& r, LDS char* smem, float scale,
+                                                 const Prologue& pro, float ea, int lo, int hi) {
+    const int w = threadIdx.x >> 6, l = lane_fresh();
+    const int tg = l / CQ, cq = l % CQ;
+    const int kc0 = w * (DK / NW) + CPL * cq;
+    const int vc0 = w * VW + VPL * cq;
+    LDS T* QG = (LDS T*)(smem + Cfg::OFF_QG);
+    LDS T* KG = (LDS T*)(smem + Cfg::OFF_KG);
+    LDS T* KI = (LDS T*)(smem + Cfg::OFF_KI);
+    LDS T* BV = (LDS T*)(smem + Cfg::OFF_BV);
+    LDS T* KIT = (LDS T*)(smem + Cfg::OFF_KT);
+    LDS float* GL = (LDS float*)(smem + Cfg::OFF_GL);
+    LDS float* BT = (LDS float*)(smem + Cfg::OFF_BT);
+    LDS float* SV = (LDS float*)(smem + Cfg::OFF_SV);
+    constexpr uint32_t SIGN = Cfg::SZ == 2 ? 0x80008000u : 0x80000000u;
+    constexpr float LOG2E = 1.4426950408889634f;
+
+    // gamma of the lane's tokens: a running sum over its TPL tokens, an
+    // inclusive scan of the group sums over the lanes cq + CQ tg, then one
+    // group back.  Rows outside [lo, hi) keep log alpha = 0 under the gate
+    // transform (identity tokens).
+    const bool xg = Cfg::FU && (pro.flags & PRO_GATE);
+    const float gb = xg ? ((const LDS float*)(smem + Cfg::OFF_NM + 2 * C * NW * 4))[0] : 0.f;
+    float gam[TPL];
+#pragma unroll
+    for (int t = 0; t < TPL; ++t) {
+      const bool real = TPL * tg + t >= lo && TPL * tg + t < hi;
+      const float la = xg ? (real ? gate_logalpha(r.gs[t], ea, gb) : 0.f) : r.gs[t];
+      gam[t] = (t == 0 ? 0.f : gam[t - 1]) + la * LOG2E;
+    }
+    float x = gam[TPL - 1];
+#pragma unroll
+    for (int d = CQ; d < 64; d <<= 1) {
+      const float y = __shfl_up(x, d);
+      if (l >= d) x += y;
+    }
+    const float gam_l = __shfl(x, 63);
+    const float y = __shfl_up(x, CQ);
+    const float e0 = (l >= CQ) ? y : 0.f;
+#pragma unroll
+    for (int t = 0; t < TPL; ++t) gam[t] += e0;
+    if (tg == 0) {
+      const float gl = exp2f(gam_l);
+      *lds_ptr<f32x4>(GL + kc0) = f32x4{gl, gl, gl, gl};
+      *lds_ptr<f32x4>(GL + kc0 + 4) = f32x4{gl, gl, gl, gl};
+    }
+    const float beta = (Cfg::FU && (pro.flags & PRO_BETA_SIGMOID)) ? sigmoid_f(r.beta) : r.beta;
+    if (w == 0) BT[l] = beta;                   // lane l holds beta of token l
+
+#pragma unroll
+    for (int t = 0; t < TPL; ++t) {
+      const int i = TPL * tg + t;
+      st_raw8(QG + i * Cfg::LD_K, kc0, r.q[t].w, 0u);
+      st_raw8(KG + i * Cfg::LD_K, kc0, r.k[t].w, 0u);
+      st_raw8(KI + i * Cfg::LD_K, kc0, r.k[t].w, SIGN);
+      st_neg(BV + i * Cfg::LD_V + vc0, r.v[t]);
+      if (w == 0) {
+        float rq = scale, rk = 1.f;
+        if (Cfg::FU && (pro.flags & PRO_L2NORM)) {
+          // the token's squared norms: the sum of the waves' partials
+          const LDS float* NQ = (const LDS float*)(smem + Cfg::OFF_NM) + i * NW;
+          const LDS float* NK = NQ + C * NW;
+          float sq = 0.f, sk = 0.f;
+#pragma unroll
+          for (int j = 0; j < NW; j += 4) {
+            const f32x4 a = *lds_ptr<const f32x4>(NQ + j), b = *lds_ptr<const f32x4>(NK + j);
+            sq += (a[0] + a[1]) + (a[2] + a[3]);
+            sk += (b[0] + b[1]) + (b[2] + b[3]);
+          }
+          rq *= __builtin_amdgcn_rsqf(sq + PRO_NORM_EPS);
+          rk = __builtin_amdgcn_rsqf(sk + PRO_NORM_EPS);
+        }
+        const float bi = __shfl(beta, i);
+        if (cq == 0) {
+          const float G = exp2f(gam[t]);
+          SV[SV_G * C + i] = gam[t];
+          SV[SV_RQ * C + i] = rq;
+          SV[SV_RK * C + i] = rk;
+          SV[SV_BK * C + i] = bi * rk;
+          SV[SV_FY * C + i] = bi * G * rk;
+          SV[SV_FO * C + i] = G * rq;
+          SV[SV_FS * C + i] = exp2f(gam_l - gam[t]) * rk;
+        }
+      }
+    }
+    // key-major -k: KIT[channel][token], the lane's TPL consecutive tokens
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      LDS T* p = KIT + (kc0 + c) * Cfg::LD_KT + Op::perm_pos(TPL * tg);
+      if constexpr (Cfg::SZ == 2 && TPL == 2) {
+        const uint32_t a = r.k[0].w.word(c >> 1), b = r.k[1].w.word(c >> 1);
+        const uint32_t pr = (c & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
+        *lds_ptr<uint32_t>(p) = pr ^ SIGN;
+      } else {
+        T kt[TPL];
+#pragma unroll
+        for (int t = 0; t < TPL; ++t) {
+          float kv[CPL];
+          r.k[t].unpack(kv);
+          kt[t] = Op::cvt(-kv[c]);
+        }
+        st_vec(p, kt);
+      }
+    }
+  }
+
   // ---------------------------------------------------------------- prep
   // Cumulative decay and the five gate-scaled operands; returns the chunk's
   // guard flag (1 = some channel decays below KDA_GAMMA_MIN).
   static __device__ __forceinline__ int prep(const Raw& r, LDS char* smem, float scale,
                                              const Prologue& pro, float ea, int lo, int hi) {
+    if constexpr (Cfg::SG) {
+      prep_sg(r, smem, scale, pro, ea, lo, hi);
+      return 0;
+    }
     const int w = threadIdx.x >> 6, l = lane_fresh();
     const int tg = l / CQ, cq = l % CQ;
     const int kc0 = w * (DK / NW) + CPL * cq;
@@ -582,38 +723,7 @@ struct ChunkKernel {
     float cp[TPL][CPL];   // in-lane running products of alpha over the lane's tokens
     float ex[CPL];        // product over the earlier token groups (exclusive prefix)
     int bad = 0;
-    if constexpr (Cfg::SG) {
-      // One gate per token: the same running product serves every channel.
-      // Inclusive scan of the group totals over lanes cq + CQ tg, shifted by
-      // one group; Gamma_L is the last group's inclusive product.
-      float ct[TPL];
-#pragma unroll
-      for (int t = 0; t < TPL; ++t) {
-        const bool real = TPL * tg + t >= lo && TPL * tg + t < hi;
-        const float a = __expf(xg ? (real ? gate_logalpha(r.gs[t], ea, gbias[0]) : 0.f) : r.gs[t]);
-        ct[t] = (t == 0) ? a : ct[t - 1] * a;
-      }
-      float x = ct[TPL - 1];
-#pragma unroll
-      for (int d = CQ; d < 64; d <<= 1) {
-        const float y = __shfl_up(x, d);
-        if (l >= d) x *= y;
-      }
-      const float gl = __shfl(x, 63);
-      const float y = __shfl_up(x, CQ);
-      const float e0 = (l >= CQ) ? y : 1.f;
-      bad = !(gl >= KDA_GAMMA_MIN);
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) {
-        ex[c] = e0;
-#pragma unroll
-        for (int t = 0; t < TPL; ++t) cp[t][c] = ct[t];
-      }
-      if (tg == 0) {
-        *lds_ptr<f32x4>(GL + kc0) = f32x4{gl, gl, gl, gl};
-        *lds_ptr<f32x4>(GL + kc0 + 4) = f32x4{gl, gl, gl, gl};
-      }
-    } else {
+    {
 #pragma unroll
       for (int t = 0; t < TPL; ++t)
 #pragma unroll
@@ -832,16 +942,52 @@ struct ChunkKernel {
     // scaled by beta (KG holds k Gamma)
     const int n = l & 15, g4 = 4 * (l >> 4);
     const LDS float* BT = (const LDS float*)(smem + Cfg::OFF_BT);
-    if (I == J)
-      accR *= *lds_ptr<const f32x4>(BT + 16 * I + g4);
-    else
-      accR *= BT[16 * I + n];
-    if (I == J) {
+    if constexpr (Cfg::SG) {
+      // raw products: entry (i, j) of -R takes beta_i rk_i rk_j Gamma_i/Gamma_j,
+      // of -Aqk rq_i rk_j Gamma_i/Gamma_j; masked entries are selected away
+      // before the (possibly overflowing) ratio is used
+      const LDS float* SV = (const LDS float*)(smem + Cfg::OFF_SV);
+      if (I == J) {
+        // accR[r]: i = 16I + g4 + r, j = 16I + n; accA[r]: i = 16I + n, j = 16I + g4 + r
+        const f32x4 gr = *lds_ptr<const f32x4>(SV + SV_G * C + 16 * I + g4);
+        const f32x4 br = *lds_ptr<const f32x4>(SV + SV_BK * C + 16 * I + g4);
+        const f32x4 kr = *lds_ptr<const f32x4>(SV + SV_RK * C + 16 * I + g4);
+        const float gn = SV[SV_G * C + 16 * I + n], kn = SV[SV_RK * C + 16 * I + n];
+        const float qn = SV[SV_RQ * C + 16 * I + n];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        if (!(n < g4 + r)) accR[r] = 0.f;    // strictly lower
-        if (!(g4 + r <= n)) accA[r] = 0.f;   // lower with diagonal
+        for (int r = 0; r < 4; ++r) {
+          const float fr = __builtin_amdgcn_exp2f(gr[r] - gn) * br[r] * kn;
+          const float fa = __builtin_amdgcn_exp2f(gn - gr[r]) * qn * kr[r];
+          accR[r] = (n < g4 + r) ? accR[r] * fr : 0.f;    // strictly lower
+          accA[r] = (g4 + r <= n) ? accA[r] * fa : 0.f;   // lower with diagonal
+        }
+      } else {
+        // i = 16I + n, j = 16J + g4 + r for both
+        const f32x4 gj = *lds_ptr<const f32x4>(SV + SV_G * C + 16 * J + g4);
+        const f32x4 kj = *lds_ptr<const f32x4>(SV + SV_RK * C + 16 * J + g4);
+        const float gi = SV[SV_G * C + 16 * I + n], bi = SV[SV_BK * C + 16 * I + n];
+        const float qi = SV[SV_RQ * C + 16 * I + n];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float e = __builtin_amdgcn_exp2f(gi - gj[r]) * kj[r];
+          accR[r] *= e * bi;
+          accA[r] *= e * qi;
+        }
       }
+    } else {
+      if (I == J)
+        accR *= *lds_ptr<const f32x4>(BT + 16 * I + g4);
+      else
+        accR *= BT[16 * I + n];
+      if (I == J) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          if (!(n < g4 + r)) accR[r] = 0.f;    // strictly lower
+          if (!(g4 + r <= n)) accA[r] = 0.f;   // lower with diagonal
+        }
+      }
+    }
+    if (I == J) {
       // RD[I][m][i] = R[16I + i][16I + m]  (column m of the block, contiguous over i)
       *lds_ptr<f32x4>(RD + I * 16 * Cfg::RD_LD + n * Cfg::RD_LD + g4) = -accR;
     } else {
@@ -913,16 +1059,33 @@ struct ChunkKernel {
 #pragma unroll
       for (int nt = 0; nt < NVT; ++nt)
         Y[I][nt] = Op::unpack(Op::ld16_tr(l, BV, Cfg::LD_V, 16 * I, vw0 + 16 * nt));   // -V
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        const typename Op::F32 ak = Op::ld32_rmp(l, KG, Cfg::LD_K, 16 * I, 32 * ks);
-#pragma unroll
-        for (int nt = 0; nt < NVT; ++nt) Y[I][nt] = Op::mma32(ak, SB[ks][nt], Y[I][nt]);
-      }
-      // rows 16I + g4 + r scaled by beta: Y = Diag(beta)((k Gamma) S - v)
       const f32x4 b = *lds_ptr<const f32x4>(BT + 16 * I + 4 * (l >> 4));
+      if constexpr (Cfg::SG) {
+        // raw k: Y = Diag(beta) (-v) + Diag(beta Gamma rk) (k S)
+        const LDS float* SV = (const LDS float*)(smem + Cfg::OFF_SV);
+        const f32x4 fy = *lds_ptr<const f32x4>(SV + SV_FY * C + 16 * I + 4 * (l >> 4));
+        f32x4 Z[NVT];
 #pragma unroll
-      for (int nt = 0; nt < NVT; ++nt) Y[I][nt] *= b;
+        for (int nt = 0; nt < NVT; ++nt) Z[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          const typename Op::F32 ak = Op::ld32_rmp(l, KG, Cfg::LD_K, 16 * I, 32 * ks);
+#pragma unroll
+          for (int nt = 0; nt < NVT; ++nt) Z[nt] = Op::mma32(ak, SB[ks][nt], Z[nt]);
+        }
+#pragma unroll
+        for (int nt = 0; nt < NVT; ++nt) Y[I][nt] = Y[I][nt] * b + Z[nt] * fy;
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          const typename Op::F32 ak = Op::ld32_rmp(l, KG, Cfg::LD_K, 16 * I, 32 * ks);
+#pragma unroll
+          for (int nt = 0; nt < NVT; ++nt) Y[I][nt] = Op::mma32(ak, SB[ks][nt], Y[I][nt]);
+        }
+        // rows 16I + g4 + r scaled by beta: Y = Diag(beta)((k Gamma) S - v)
+#pragma unroll
+        for (int nt = 0; nt < NVT; ++nt) Y[I][nt] *= b;
+      }
 #pragma unroll
       for (int nt = 0; nt < NVT; ++nt) O[I][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -930,6 +1093,12 @@ struct ChunkKernel {
         const typename Op::F32 bq = Op::ld32_rmp(l, QG, Cfg::LD_K, 16 * I, 32 * ks);
 #pragma unroll
         for (int nt = 0; nt < NVT; ++nt) O[I][nt] = Op::mma32(SB[ks][nt], bq, O[I][nt]);
+      }
+      if constexpr (Cfg::SG) {
+        // column n = token 16I + n: raw q, so S^T q_i takes Gamma_i rq_i
+        const float fo = ((const LDS float*)(smem + Cfg::OFF_SV))[SV_FO * C + 16 * I + (l & 15)];
+#pragma unroll
+        for (int nt = 0; nt < NVT; ++nt) O[I][nt] *= fo;
       }
     }
   }
@@ -955,6 +1124,8 @@ struct ChunkKernel {
     // (2) the solve X_I = T_II (Y_I - sum_{J<I} R_IJ X_J) by 16-token
     //     blocks; X kept as 16-deep operands.
     typename Op::F16 XP[4][NVT];
+    // SG: X rows scaled by rk_j Gamma_L / Gamma_j for the update of S from the raw k
+    typename Op::F16 XS[Cfg::SG ? 4 : 1][NVT];
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
       f32x4 (&YI)[NVT] = Y[I];
@@ -982,15 +1153,25 @@ struct ChunkKernel {
 #pragma unroll
       for (int nt = 0; nt < NVT; ++nt) {
         const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        XP[I][nt] = Op::pack(Op::mma16(a, Op::pack(YI[nt]), z));
+        const f32x4 x = Op::mma16(a, Op::pack(YI[nt]), z);
+        XP[I][nt] = Op::pack(x);
+        if constexpr (Cfg::SG) {
+          const f32x4 fs = *lds_ptr<const f32x4>((const LDS float*)(smem + Cfg::OFF_SV) +
+                                                 SV_FS * C + 16 * I + g4);
+          XS[I][nt] = Op::pack(x * fs);
+        }
       }
     }
     // -E as 32-deep operands over tokens: two 16-deep blocks side by side
-    typename Op::F32 EB[2][NVT];
+    typename Op::F32 EB[2][NVT], ES[Cfg::SG ? 2 : 1][NVT];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int nt = 0; nt < NVT; ++nt) EB[kt][nt] = typename Op::F32{XP[2 * kt][nt], XP[2 * kt + 1][nt]};
+      for (int nt = 0; nt < NVT; ++nt) {
+        EB[kt][nt] = typename Op::F32{XP[2 * kt][nt], XP[2 * kt + 1][nt]};
+        if constexpr (Cfg::SG)
+          ES[kt][nt] = typename Op::F32{XS[2 * kt][nt], XS[2 * kt + 1][nt]};
+      }
 
     // (3) O_I^T = S^T QG_I^T + (-E)^T (-Aqk_I)^T: rows = value columns,
     //     columns = tokens 16I + n; staged as OST[token][value]
@@ -1018,10 +1199,18 @@ struct ChunkKernel {
         a[kt] = Op::ld32_rmp(l, KIT, Cfg::LD_KT, 16 * mt, 32 * kt);
 #pragma unroll
       for (int nt = 0; nt < NVT; ++nt) {
-        f32x4 s = S[mt][nt];
+        if constexpr (Cfg::SG) {
+          // S <- Gamma_L S + (-k)^T (-E rk Gamma_L / Gamma)
+          f32x4 s = S[mt][nt] * gl;
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) s = Op::mma32(a[kt], EB[kt][nt], s);
-        S[mt][nt] = s * gl;
+          for (int kt = 0; kt < 2; ++kt) s = Op::mma32(a[kt], ES[kt][nt], s);
+          S[mt][nt] = s;
+        } else {
+          f32x4 s = S[mt][nt];
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt) s = Op::mma32(a[kt], EB[kt][nt], s);
+          S[mt][nt] = s * gl;
+        }
       }
     }
     // Once the staged tile is complete all of the chunk's LDS reads are done:
@@ -1243,14 +1432,18 @@ struct ChunkKernel {
       const int bad = prep(raw, smem, scale, pro, ea, 0, clen);
       // the vote runs in every lane: inside the lane-0 branch it would only
       // see lane 0's flag (the scan path sets it in other lanes)
-      const int wave_bad = __any(bad);
-      if (lane_fresh() == 0) FL[w] = wave_bad ? 1 : 0;
+      if constexpr (!Cfg::SG) {   // the single-gate form has no guard
+        const int wave_bad = __any(bad);
+        if (lane_fresh() == 0) FL[w] = wave_bad ? 1 : 0;
+      }
       compiler_fence();
       load_raw<LOAD_G>(raw, offs, q, k, v, g, beta, next, H, h, nlen);
       __syncthreads();                                           // B1
       int any_bad = 0;
+      if constexpr (!Cfg::SG) {
 #pragma unroll
-      for (int i = 0; i < NW; ++i) any_bad |= FL[i];
+        for (int i = 0; i < NW; ++i) any_bad |= FL[i];
+      }
       if (!any_bad) {
         load_raw<LOAD_V>(raw, offs, q, k, v, g, beta, next, H, h, nlen);
         compiler_fence();
