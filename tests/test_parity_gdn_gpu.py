@@ -48,20 +48,26 @@ def test_gdn_chunk_fwd_matches_oracle(B, T, H, dk, dv, io, with_S0):
     assert_close(go, gs, ro, rs, tol_for(io), "gdn chunk")
 
 
-def test_gdn_chunk_strong_decay_takes_the_guard_path():
-    """log alpha = -3 for every token: a chunk's decay (e^-192) is far below
-    the 2^-100 limit of the inverse-scaled operands, so every chunk runs the
-    token-by-token guard path; results must still match."""
-    note("gdn chunk strong decay")
-    d = inputs.prefill_inputs(1, 150, 2, 128, 128, io="bf16", seed=3, with_S0=True, device=DEV,
+@pytest.mark.parametrize("gate,io", [("-3", "bf16"), ("-30", "f32"), ("uniform", "f32")])
+def test_gdn_chunk_strong_decay_matches_oracle(gate, io):
+    """Decays far beyond one chunk's range: log alpha = -3 or -30 for every token
+    (a chunk decays by e^-192 or e^-1920), or uniform in [-8, 0].  The scalar-gate
+    chunk step scales its products by per-token ratios Gamma_i / Gamma_j <= 1, so
+    it needs no guard; the results must still match."""
+    note("gdn chunk strong decay gate=%s io=%s" % (gate, io))
+    d = inputs.prefill_inputs(1, 150, 2, 128, 128, io=io, seed=3, with_S0=True, device=DEV,
                               gate="gdn")
-    d["g"] = torch.full_like(d["g"], -3.0)
+    if gate == "uniform":
+        gen = torch.Generator().manual_seed(11)
+        d["g"] = (-8.0 * torch.rand(d["g"].shape, generator=gen)).to(DEV)
+    else:
+        d["g"] = torch.full_like(d["g"], float(gate))
     o, S = kda().chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], S0=d["S0"])
     torch.cuda.synchronize()
     chains = [(0, 0), (0, 1)]
     ro, rs = oracle_batched(d, chains)
     go, gs = gpu_chains_batched(o, S, chains)
-    assert_close(go, gs, ro, rs, tol_for("bf16"), "gdn guard")
+    assert_close(go, gs, ro, rs, tol_for(io), "gdn strong decay")
 
 
 @pytest.mark.parametrize("lens,H,dk,dv,io,with_S0", [
