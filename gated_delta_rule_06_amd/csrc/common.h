@@ -86,6 +86,17 @@ struct IoBf16 {
   }
 };
 
+// ---------------------------------------------------------------- lane reductions
+// Sum over the 16 lanes of the lane's DPP row (row_ror 8, 4, 2, 1, each fused
+// into the add); every lane gets the total.
+__device__ __forceinline__ float row_sum16(float x) {
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xf, 0xf, true));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xf, 0xf, true));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x122, 0xf, 0xf, true));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x121, 0xf, 0xf, true));
+  return x;
+}
+
 // ---------------------------------------------------------------- input transforms
 // Optional transforms of a token's raw inputs, applied in the kernels before
 // the step ("Linear Attention, From Scratch to Kimi 3", sections 6 and 7):

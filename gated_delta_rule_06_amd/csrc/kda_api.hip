@@ -21,6 +21,13 @@ hipError_t launch_recurrent(const void* q, const void* k, const void* v, const f
                             const int32_t* cu, int n_seq, int T, int H, int dk, int dv,
                             float scale, bool bf16, bool scalar_gate, const Prologue& pro,
                             hipStream_t stream);
+size_t backward_workspace_bytes(int n_seq, size_t rows, int H, int dk, int dv);
+hipError_t launch_backward(const void* q, const void* k, const void* v, const float* g,
+                           const float* beta, const float* S0, const void* dout, const float* dSf,
+                           float* dq, float* dk, float* dv, float* dg, float* dbeta, float* dS0,
+                           const int32_t* cu, int n_seq, int T, int H, int d_k, int d_v,
+                           float scale, bool bf16, bool scalar_gate, float* ws,
+                           hipStream_t stream);
 }  // namespace kda
 
 namespace {
@@ -231,6 +238,54 @@ int recurrent_impl(const void* q, const void* k, const void* v, const float* log
                                              reinterpret_cast<hipStream_t>(stream)));
 }
 
+int backward_impl(const void* q, const void* k, const void* v, const float* log_alpha,
+                  const float* beta, const float* S0, const void* d_out, const float* dS_final,
+                  float* dq, float* dk, float* dv, float* dg, float* dbeta, float* dS0,
+                  const int32_t* cu_seqlens, int n_seq, int T, int H, int d_k, int d_v,
+                  float scale, int io_dtype, bool sg, void* workspace, size_t workspace_bytes,
+                  void* stream) {
+  if (n_seq < 0 || T < 0 || H <= 0) return KDA_ERR_DIM;
+  if (!io_ok(io_dtype) || !shape_ok(d_k) || !shape_ok(d_v)) return KDA_ERR_UNSUPPORTED;
+  const bool packed = cu_seqlens != nullptr;
+  const size_t rows = packed ? (size_t)T : (size_t)n_seq * T;
+  if (rows > 0x7fffffffu) return KDA_ERR_DIM;
+  if (rows > 0 && (!q || !k || !v || !log_alpha || !beta || !d_out || !dq || !dk || !dv || !dg ||
+                   !dbeta))
+    return KDA_ERR_NULL;
+  const void* a16[] = {q, k, v, S0, d_out, dS_final, dq, dk, dv, dS0, workspace};
+  for (const void* p : a16)
+    if (!aligned(p, 16)) return KDA_ERR_ALIGN;
+  const void* a4[] = {log_alpha, beta, cu_seqlens, dg, dbeta};
+  for (const void* p : a4)
+    if (!aligned(p, 4)) return KDA_ERR_ALIGN;
+  const size_t need = kda::backward_workspace_bytes(n_seq, rows, H, d_k, d_v);
+  if (n_seq > 0 && (!workspace || workspace_bytes < need)) return KDA_ERR_WORKSPACE;
+  const size_t e = io_bytes(io_dtype);
+  const size_t state = (size_t)n_seq * H * d_k * d_v * 4;
+  const size_t gk = rows * H * (sg ? 1 : d_k) * 4;
+  const Range in[] = {span(q, rows * H * d_k * e),     span(k, rows * H * d_k * e),
+                      span(v, rows * H * d_v * e),     span(log_alpha, gk),
+                      span(beta, rows * H * 4),        span(S0, S0 ? state : 0),
+                      span(d_out, rows * H * d_v * e), span(dS_final, dS_final ? state : 0),
+                      span(cu_seqlens, packed ? (size_t)(n_seq + 1) * 4 : 0)};
+  const Range outs[] = {span(dq, rows * H * d_k * 4), span(dk, rows * H * d_k * 4),
+                        span(dv, rows * H * d_v * 4), span(dg, gk),
+                        span(dbeta, rows * H * 4),    span(dS0, dS0 ? state : 0),
+                        span(workspace, n_seq > 0 ? need : 0)};
+  for (size_t i = 0; i < sizeof(outs) / sizeof(outs[0]); ++i) {
+    for (const Range& r : in)
+      if (overlap(outs[i], r)) return KDA_ERR_ALIAS;
+    for (size_t j = i + 1; j < sizeof(outs) / sizeof(outs[0]); ++j)
+      if (overlap(outs[i], outs[j])) return KDA_ERR_ALIAS;
+  }
+  if (n_seq == 0) return KDA_OK;
+  return launch_status(kda::launch_backward(q, k, v, log_alpha, beta, S0, d_out, dS_final, dq, dk,
+                                            dv, dg, dbeta, dS0, cu_seqlens, n_seq, T, H, d_k, d_v,
+                                            scale, io_dtype == KDA_IO_BF16, sg,
+                                            reinterpret_cast<float*>(workspace),
+                                            reinterpret_cast<hipStream_t>(stream)));
+}
+
 }  // namespace
 
 extern "C" {
@@ -374,6 +429,24 @@ int kda_decode_step_fused(const void* q, const void* k, const void* v, const flo
   if (per_head_gate != 0 && per_head_gate != 1) return KDA_ERR_UNSUPPORTED;
   return decode_impl(q, k, v, log_alpha, beta, S_inout, out, N, H, d_k, d_v, scale, io_dtype,
                      per_head_gate == 1, pro, stream);
+}
+
+size_t kda_backward_workspace_size(int N, int T, int H, int d_k, int d_v, int packed) {
+  if (N < 0 || T < 0 || H <= 0 || !shape_ok(d_k) || !shape_ok(d_v)) return 0;
+  const size_t rows = packed ? (size_t)T : (size_t)N * T;
+  return kda::backward_workspace_bytes(N, rows, H, d_k, d_v);
+}
+
+int kda_backward(const void* q, const void* k, const void* v, const float* log_alpha,
+                 const float* beta, const float* S0, const void* d_out, const float* dS_final,
+                 float* dq, float* dk, float* dv, float* dlog_alpha, float* dbeta, float* dS0,
+                 const int32_t* cu_seqlens, int N, int T, int H, int d_k, int d_v, float scale,
+                 int io_dtype, int per_head_gate, void* workspace, size_t workspace_bytes,
+                 void* stream) {
+  if (per_head_gate != 0 && per_head_gate != 1) return KDA_ERR_UNSUPPORTED;
+  return backward_impl(q, k, v, log_alpha, beta, S0, d_out, dS_final, dq, dk, dv, dlog_alpha,
+                       dbeta, dS0, cu_seqlens, N, T, H, d_k, d_v, scale, io_dtype,
+                       per_head_gate == 1, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

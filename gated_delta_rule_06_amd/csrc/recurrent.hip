@@ -56,15 +56,6 @@ struct RowVec {
   }
 };
 
-// Sum over the 16 lanes of the lane's DPP row; every lane gets the total.
-__device__ __forceinline__ float row_sum16(float x) {
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xf, 0xf, true));
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xf, 0xf, true));
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x122, 0xf, 0xf, true));
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x121, 0xf, 0xf, true));
-  return x;
-}
-
 }  // namespace
 
 // One token's inputs for one lane.  SG: one gate per (token, head) for every

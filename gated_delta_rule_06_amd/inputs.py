@@ -23,6 +23,8 @@ Recipe (the pages fix only shapes and distributions; the rest is chosen here):
   same tensors on every run of one device type.
 * bf16 tensors are cast from the fp32 values with round-to-nearest-even, after
   normalisation.  The oracle reads the cast values.
+* backward cotangents (grad_inputs): dL/dout ~ N(0, 1) in v's dtype, dL/dS_final
+  ~ N(0, 0.1^2) fp32, drawn after the inputs from a generator of their own.
 """
 from __future__ import annotations
 
@@ -30,7 +32,7 @@ import numpy as np
 import torch
 
 __all__ = ["prefill_inputs", "varlen_lengths", "varlen_inputs", "decode_inputs",
-           "raw_layer_inputs", "to_host", "bf16_bits_from_f32", "CONFIGS"]
+           "raw_layer_inputs", "grad_inputs", "to_host", "bf16_bits_from_f32", "CONFIGS"]
 
 _IO = {"bf16": torch.bfloat16, "f32": torch.float32}
 
@@ -158,6 +160,21 @@ def raw_layer_inputs(d, H, dk, seed=0, gate="kda", strong_decay=False, device="c
     d["A_log"] = 0.3 * torch.randn((H,), generator=gen, device=device)
     bshape = (H,) if gate == "gdn" else (H, dk)
     d["gate_bias"] = 0.5 * torch.randn(bshape, generator=gen, device=device)
+    return d
+
+
+def grad_inputs(d, seed=0, with_dS_final=True, device="cpu"):
+    """Cotangents for the backward of the forward on ``d``: d_out ~ N(0, 1)
+    shaped like v (v's dtype) and dS_final ~ N(0, 0.1^2) [N, H, dk, dv] fp32
+    (or None).  Adds them to ``d`` as "d_out" and "dS_final"."""
+    gen = _gen(device, seed + 104729)
+    n_seq = d["B"] if d.get("cu_seqlens") is None else d["N"]
+    d["d_out"] = torch.randn(d["v"].shape, generator=gen, device=device,
+                             dtype=torch.float32).to(d["v"].dtype)
+    d["dS_final"] = None
+    if with_dS_final:
+        d["dS_final"] = 0.1 * torch.randn((n_seq, d["H"], d["dk"], d["dv"]), generator=gen,
+                                          device=device, dtype=torch.float32)
     return d
 
 

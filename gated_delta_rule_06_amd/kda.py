@@ -71,6 +71,11 @@ def _load():
     lib.kda_chunk_fwd_workspace_size.argtypes = [i] * 7
     lib.kda_chunk_fwd_varlen_workspace_size.restype = sz
     lib.kda_chunk_fwd_varlen_workspace_size.argtypes = [i] * 7
+    lib.kda_backward_workspace_size.restype = sz
+    lib.kda_backward_workspace_size.argtypes = [i] * 6
+    lib.kda_backward.restype = i
+    lib.kda_backward.argtypes = [vp, vp, vp, fp, fp, fp, vp, fp, fp, fp, fp, fp, fp, fp, vp, i, i, i,
+                                 i, i, f, i, i, vp, sz, vp]
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_status_string.argtypes = [i]
     lib.kda_version.restype = i
@@ -365,6 +370,62 @@ def recurrent_fwd_varlen(q, k, v, log_alpha, beta, cu_seqlens, S0=None, scale=No
     if st != 0:
         raise KdaError(st, fn)
     return out, S_final
+
+
+def backward_workspace_size(N, T, H, dk, dv, packed=False):
+    """Bytes of workspace kda_backward needs (T = T_total when packed)."""
+    return int(lib.kda_backward_workspace_size(N, T, H, dk, dv, int(bool(packed))))
+
+
+def backward(q, k, v, log_alpha, beta, d_out, S0=None, dS_final=None, cu_seqlens=None,
+             scale=None, want_dS0=True, workspace=None):
+    """Gradients of the forward for dL/dout = ``d_out`` (shaped like out, q's
+    dtype) and dL/dS_final = ``dS_final`` ([N, H, dk, dv] fp32, or None = 0).
+    The inputs are the forward's: batched [B, T, H, .] or, with ``cu_seqlens``,
+    packed [T_total, H, .]; KDA or Gated DeltaNet gates.  ``workspace``: a
+    uint8 tensor of at least backward_workspace_size() bytes, or None (one is
+    allocated).  Returns a dict of fp32 tensors dq, dk, dv, dlog_alpha (shaped
+    like log_alpha), dbeta and dS0 (None unless ``want_dS0``)."""
+    packed = cu_seqlens is not None
+    lead = tuple(q.shape[:-2])
+    H, dk = q.shape[-2], q.shape[-1]
+    dv = v.shape[-1]
+    dev = q.device
+    if packed:
+        (Tt,) = lead
+        N, T = cu_seqlens.shape[0] - 1, Tt
+    else:
+        N, T = lead
+    if scale is None:
+        scale = dk ** -0.5
+    gshape, pre = _gate(log_alpha, lead + (H,), dk)
+    for name, t, shp, dt in (("q", q, lead + (H, dk), q.dtype), ("k", k, lead + (H, dk), q.dtype),
+                             ("v", v, lead + (H, dv), q.dtype),
+                             ("log_alpha", log_alpha, gshape, torch.float32),
+                             ("beta", beta, lead + (H,), torch.float32),
+                             ("d_out", d_out, lead + (H, dv), q.dtype),
+                             ("cu_seqlens", cu_seqlens, (N + 1,), torch.int32),
+                             ("S0", S0, (N, H, dk, dv), torch.float32),
+                             ("dS_final", dS_final, (N, H, dk, dv), torch.float32)):
+        _check(t, name, shp, dt, dev)
+    io = _io_code(q.dtype)
+    f32 = dict(dtype=torch.float32, device=dev)
+    res = {"dq": torch.empty(lead + (H, dk), **f32), "dk": torch.empty(lead + (H, dk), **f32),
+           "dv": torch.empty(lead + (H, dv), **f32), "dlog_alpha": torch.empty(gshape, **f32),
+           "dbeta": torch.empty(lead + (H,), **f32),
+           "dS0": torch.empty((N, H, dk, dv), **f32) if want_dS0 else None}
+    need = backward_workspace_size(N, T, H, dk, dv, packed)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    _check(workspace, "workspace", (workspace.numel(),), torch.uint8, dev)
+    st = lib.kda_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S0),
+                          _ptr(d_out), _ptr(dS_final), _ptr(res["dq"]), _ptr(res["dk"]),
+                          _ptr(res["dv"]), _ptr(res["dlog_alpha"]), _ptr(res["dbeta"]),
+                          _ptr(res["dS0"]), _ptr(cu_seqlens), N, T, H, dk, dv, float(scale), io,
+                          int(pre == "kda_gdn_"), _ptr(workspace), workspace.numel(), _stream(dev))
+    if st != 0:
+        raise KdaError(st, "kda_backward")
+    return res
 
 
 for _f in (chunk_fwd, chunk_fwd_varlen, decode_step, recurrent_fwd, recurrent_fwd_varlen):

@@ -279,6 +279,40 @@ int kda_decode_step_fused(const void* q, const void* k, const void* v, const flo
                           int d_v, float scale, int io_dtype, int per_head_gate,
                           const kda_prologue* pro, void* stream);
 
+/*
+ * kda_backward -- gradients of the forward (training).  The pages give no
+ * backward; chunkwise KDA is the training form ("Kimi Unveils Delta Attention
+ * and K3 Architecture Updates", section 6), so this is the reverse-mode
+ * derivative of the recurrence of section 4 (forget, predict, correct, write,
+ * read after the write) for L(out, S_final):
+ *
+ *  inputs     q, k, v, log_alpha, beta, S0, cu_seqlens, N, T, H, d_k, d_v,
+ *             scale, io_dtype, per_head_gate: exactly as given to the forward
+ *             (kda_chunk_fwd / kda_recurrent_fwd and their varlen and
+ *             Gated DeltaNet forms; cu_seqlens NULL = batched layout)
+ *  d_out      dL/dout, shaped like out, io_dtype
+ *  dS_final   dL/dS_final [N, H, d_k, d_v] fp32, or NULL (zero)
+ *  dq, dk     [rows, H, d_k] fp32                 (rows = N*T or T_total)
+ *  dv         [rows, H, d_v] fp32
+ *  dlog_alpha [rows, H, d_k] fp32 ([rows, H] with per_head_gate)
+ *  dbeta      [rows, H] fp32
+ *  dS0        dL/dS0 [N, H, d_k, d_v] fp32, or NULL (not written)
+ *  workspace  device memory of at least kda_backward_workspace_size() bytes,
+ *             16-byte aligned, overlapping nothing else; it holds the state
+ *             at the start of every 4-token block and is clobbered
+ *
+ * Every gradient is written in full (rows of empty sequences have none).  No
+ * output may overlap an input, another output or the workspace.  d_k and d_v
+ * are 64 or 128; io_dtype fp32 or bf16.  Status codes as the forward calls.
+ */
+size_t kda_backward_workspace_size(int N, int T, int H, int d_k, int d_v, int packed);
+int kda_backward(const void* q, const void* k, const void* v, const float* log_alpha,
+                 const float* beta, const float* S0, const void* d_out, const float* dS_final,
+                 float* dq, float* dk, float* dv, float* dlog_alpha, float* dbeta, float* dS0,
+                 const int32_t* cu_seqlens, int N, int T, int H, int d_k, int d_v, float scale,
+                 int io_dtype, int per_head_gate, void* workspace, size_t workspace_bytes,
+                 void* stream);
+
 /* Workspace bytes kda_chunk_fwd needs for these sizes (0 if none; the
  * arguments are not validated here: unsupported sizes give 0). */
 size_t kda_chunk_fwd_workspace_size(int B, int T, int H, int d_k, int d_v, int chunk,

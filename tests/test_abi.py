@@ -32,7 +32,7 @@ def test_header_declares_the_entry_points():
                  "kda_recurrent_fwd", "kda_recurrent_fwd_varlen", "kda_gdn_chunk_fwd",
                  "kda_gdn_chunk_fwd_varlen", "kda_gdn_decode_step", "kda_gdn_recurrent_fwd",
                  "kda_gdn_recurrent_fwd_varlen", "kda_chunk_fwd_fused", "kda_recurrent_fwd_fused",
-                 "kda_decode_step_fused",
+                 "kda_decode_step_fused", "kda_backward", "kda_backward_workspace_size",
                  "kda_chunk_fwd_workspace_size", "kda_chunk_fwd_varlen_workspace_size",
                  "kda_status_string", "kda_version"):
         assert want in names
@@ -211,6 +211,39 @@ def test_alignment_validation(lib):
              None) == -7
     from gated_delta_rule_06_amd import kda
     assert kda.status_string(-7).startswith("KDA_ERR_ALIGN")
+
+
+def test_backward_workspace_and_validation(lib):
+    """Sizes and error paths of kda_backward; every call here returns before
+    any launch (fake pointers are never dereferenced)."""
+    ws = lib.kda_backward_workspace_size
+    # one checkpoint slot (d_k x d_v fp32) per head for every 4 tokens, plus one per sequence
+    assert ws(8, 8192, 32, 128, 128, 0) == (8 + 8 * 8192 // 4) * 32 * 128 * 128 * 4
+    assert ws(3, 10, 2, 64, 64, 1) == (3 + 10 // 4) * 2 * 64 * 64 * 4
+    assert ws(1, 4, 2, 96, 64, 0) == 0
+    need = ws(2, 4, 2, 64, 64, 0)
+    f = lib.kda_backward
+
+    def call(**kw):
+        a = dict(q=P[0], k=P[1], v=P[2], g=P[3], beta=P[4], S0=None, do=P[5], dSf=None,
+                 dq=P[6], dk=P[7], dv=P[8], dg=P[9], db=P[10], dS0=None, cu=None, N=2, T=4,
+                 H=2, d_k=64, d_v=64, io=0, ph=0, ws=P[11], wsb=need)
+        a.update(kw)
+        return f(a["q"], a["k"], a["v"], a["g"], a["beta"], a["S0"], a["do"], a["dSf"], a["dq"],
+                 a["dk"], a["dv"], a["dg"], a["db"], a["dS0"], a["cu"], a["N"], a["T"], a["H"],
+                 a["d_k"], a["d_v"], 0.125, a["io"], a["ph"], a["ws"], a["wsb"], None)
+    assert call(ph=2) == -3
+    assert call(d_k=96) == -3
+    assert call(io=5) == -3
+    assert call(N=-1) == -2
+    assert call(dq=None) == -1
+    assert call(ws=None) == -4
+    assert call(wsb=need - 1) == -4
+    assert call(dv=ctypes.c_void_p(P[8].value + 4)) == -7
+    assert call(dq=P[0]) == -6                              # dq is q
+    assert call(dk=P[6]) == -6                              # two outputs in one array
+    assert call(ws=P[3]) == -6                              # workspace is log_alpha
+    assert call(N=0) == 0
 
 
 def test_product_path_has_no_oracle_or_cpu_fallback():

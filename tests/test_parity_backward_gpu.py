@@ -1,0 +1,133 @@
+"""GPU parity of kda_backward (gradients of the forward) against the oracle's
+fp64 backward (oracle/backward.py, itself pinned by finite differences of the
+forward loop), through the C ABI.
+
+The backward computes in fp32 throughout (bf16 inputs are read exactly, the
+gradients are fp32), so the bar is rel-L2 <= 1e-4 per gradient for both I/O
+types."""
+import numpy as np
+import pytest
+import torch
+
+from gated_delta_rule_06_amd import inputs
+from gated_delta_rule_06_amd.inputs import to_host
+from oracle import backward as obwd
+from parity_util import rel_l2
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+TOL = 1e-4
+NAMES = (("dq", "dq"), ("dk", "dk"), ("dv", "dv"), ("dlog_alpha", "dg"), ("dbeta", "dbeta"))
+
+
+def kda():
+    from gated_delta_rule_06_amd import kda as k
+    return k
+
+
+def note(msg):
+    print(msg, flush=True)
+
+
+def run_gpu(d, want_dS0=True):
+    res = kda().backward(d["q"], d["k"], d["v"], d["g"], d["beta"], d["d_out"], S0=d["S0"],
+                         dS_final=d["dS_final"], cu_seqlens=d["cu_seqlens"], want_dS0=want_dS0)
+    torch.cuda.synchronize()
+    return {k: (None if v is None else v.cpu().numpy()) for k, v in res.items()}
+
+
+def run_oracle(d):
+    h = lambda t: to_host(t)
+    return obwd.backward(h(d["q"]), h(d["k"]), h(d["v"]), h(d["g"]), h(d["beta"]), h(d["d_out"]),
+                         S0=h(d["S0"]), dS_final=h(d["dS_final"]),
+                         cu_seqlens=h(d["cu_seqlens"]))
+
+
+def compare(got, ref, what, tol=TOL):
+    errs = {}
+    for gname, oname in NAMES:
+        assert got[gname].shape == ref[oname].shape, (gname, got[gname].shape, ref[oname].shape)
+        assert np.isfinite(got[gname]).all(), gname
+        errs[gname] = rel_l2(got[gname], ref[oname])
+    if got["dS0"] is not None:
+        errs["dS0"] = rel_l2(got["dS0"], ref["dS0"])
+    note("%s rel-L2 %s" % (what, " ".join("%s=%.2e" % kv for kv in errs.items())))
+    for name, e in errs.items():
+        assert e <= tol, (what, name, e)
+
+
+@pytest.mark.parametrize("B,T,H,dk,dv,io,with_S0,with_dSf,gate", [
+    (2, 11, 2, 128, 128, "bf16", True, True, "kda"),
+    (1, 9, 3, 64, 64, "f32", False, False, "kda"),
+    (2, 6, 2, 128, 64, "f32", True, True, "kda"),
+    (1, 13, 2, 64, 128, "bf16", True, False, "kda"),
+    (1, 300, 2, 64, 64, "f32", True, True, "kda"),
+    (2, 10, 2, 128, 128, "bf16", True, True, "gdn"),
+    (1, 4, 1, 64, 64, "f32", False, True, "gdn"),
+    (1, 1, 2, 128, 128, "bf16", True, True, "kda"),
+])
+def test_backward_matches_oracle(B, T, H, dk, dv, io, with_S0, with_dSf, gate):
+    what = "backward B=%d T=%d H=%d dk=%d dv=%d io=%s S0=%s dSf=%s gate=%s" % (
+        B, T, H, dk, dv, io, with_S0, with_dSf, gate)
+    note(what)
+    d = inputs.prefill_inputs(B, T, H, dk, dv, io=io, seed=31 + T, with_S0=with_S0, device=DEV,
+                              gate=gate)
+    inputs.grad_inputs(d, seed=T, with_dS_final=with_dSf, device=DEV)
+    compare(run_gpu(d), run_oracle(d), what)
+
+
+@pytest.mark.parametrize("lens,io,gate", [
+    ([5, 0, 1, 13, 4], "bf16", "kda"),
+    ([7, 0, 9], "f32", "gdn"),
+])
+def test_backward_varlen_matches_oracle(lens, io, gate):
+    what = "backward varlen lens=%s io=%s gate=%s" % (lens, io, gate)
+    note(what)
+    d = inputs.varlen_inputs(lens, 2, 128, 128, io=io, seed=len(lens), with_S0=True, device=DEV,
+                             gate=gate)
+    inputs.grad_inputs(d, seed=3, device=DEV)
+    got = run_gpu(d)
+    ref = run_oracle(d)
+    compare(got, ref, what)
+    # empty sequences: dS0 = dS_final exactly
+    for n, L in enumerate(lens):
+        if L == 0:
+            np.testing.assert_array_equal(got["dS0"][n], d["dS_final"][n].cpu().numpy())
+
+
+def test_backward_without_dS0_output():
+    note("backward want_dS0=False")
+    d = inputs.prefill_inputs(1, 7, 2, 64, 64, io="f32", seed=2, with_S0=True, device=DEV)
+    inputs.grad_inputs(d, seed=2, device=DEV)
+    got = run_gpu(d, want_dS0=False)
+    assert got["dS0"] is None
+    compare(got, run_oracle(d), "backward no dS0")
+
+
+def test_backward_strong_decay():
+    """log alpha down to -20 per channel: no division by the decay anywhere,
+    so gradients stay exact where the states vanish."""
+    note("backward strong decay")
+    d = inputs.prefill_inputs(1, 40, 2, 128, 128, io="f32", seed=9, with_S0=True, device=DEV)
+    gen = torch.Generator().manual_seed(5)
+    d["g"] = (-20.0 * torch.rand(d["g"].shape, generator=gen)).to(DEV)
+    inputs.grad_inputs(d, seed=9, device=DEV)
+    compare(run_gpu(d), run_oracle(d), "backward strong decay")
+
+
+def test_backward_headline_sampled_chains():
+    """B=8, H=32, T=8192, d=128 bf16: the full launch; the oracle checks
+    sampled (sequence, head) chains."""
+    note("backward prefill_b8_h32_t8192 full")
+    d = inputs.prefill_inputs(8, 8192, 32, 128, 128, io="bf16", seed=0, device=DEV)
+    inputs.grad_inputs(d, seed=0, with_dS_final=False, device=DEV)
+    res = kda().backward(d["q"], d["k"], d["v"], d["g"], d["beta"], d["d_out"])
+    torch.cuda.synchronize()
+    for b, h in [(0, 0), (5, 21)]:
+        sl = lambda t: to_host(t[b:b + 1, :, h:h + 1].contiguous())
+        ref = obwd.backward(sl(d["q"]), sl(d["k"]), sl(d["v"]), sl(d["g"]),
+                            to_host(d["beta"][b:b + 1, :, h:h + 1].contiguous()), sl(d["d_out"]))
+        got = {k: (None if v is None else
+                   (v[b:b + 1, :, h:h + 1] if k != "dS0" else v[b:b + 1, h:h + 1]).cpu().numpy())
+               for k, v in res.items()}
+        compare(got, ref, "backward headline chain (%d, %d)" % (b, h))
