@@ -21,11 +21,13 @@
 //
 // The backward needs the forward states in reverse order.  A forward sweep
 // stores the state at the start of every block of BK tokens to the workspace
-// (each lane its own registers, so the read back needs no barrier); the
-// reverse sweep takes the blocks last to first, and for each token of a block
-// recomputes its state from the block's checkpoint (at most BK - 1 forward
-// steps) before the backward step.  The token inputs of the current block are
-// staged in LDS, two buffers, one barrier per block.
+// (each lane its own registers, so the read back needs no barrier), and v - p
+// of every token.  The reverse sweep takes the blocks last to first; the
+// states before a block's first two tokens stay in registers, the later ones
+// are recomputed from the second (one step per token on average, each a
+// decay and a rank-1 update from the stored v - p, with no reduction).  A
+// block's token inputs are staged in LDS (two buffers, one barrier per
+// block); the next block's inputs and checkpoint load while this one runs.
 #include "common.h"
 
 namespace kda {
@@ -42,10 +44,13 @@ struct BwdCfg {
   static constexpr int NW = DV / 16;          // waves
   static constexpr int NT = 64 * NW;          // threads
   static constexpr int RPT = DK / 16;         // key rows per lane
-  // staged inputs of one block (floats): q, k, g [BK][DK], v, do [BK][DV], beta [BK]
+  // staged inputs of one block (floats): q, k, g [BK][DK]; v (forward sweep)
+  // or v - p (reverse sweep), do [BK][DV]; beta [BK]
   static constexpr int IN_Q = 0, IN_K = BK * DK, IN_G = 2 * BK * DK, IN_V = 3 * BK * DK;
   static constexpr int IN_DO = IN_V + BK * DV, IN_B = IN_DO + BK * DV;
   static constexpr int IN_SZ = (IN_B + BK + 3) / 4 * 4;
+  // staging elements per thread (key-row arrays, value-column arrays)
+  static constexpr int NQ = (BK * DK + NT - 1) / NT, NV = (BK * DV + NT - 1) / NT;
   // per-wave partial sums over the wave's columns: dq, dk, dg [BK][3][NW][DK];
   // dbeta (and the Gated DeltaNet dg) [BK][2][NW]
   static constexpr int RED_SZ = BK * 3 * NW * DK;
@@ -66,31 +71,63 @@ struct Lane {
 template <class Cfg>
 struct Bwd {
   static constexpr int DK = Cfg::DK, DV = Cfg::DV, NW = Cfg::NW, NT = Cfg::NT, RPT = Cfg::RPT;
+  static constexpr int NQ = Cfg::NQ, NV = Cfg::NV;
   typedef typename Cfg::Io Io;
 
-  // The inputs of tokens [tok0, tok0 + L) of head h into one staging buffer
-  // (rows past L read as zeros).  Gated DeltaNet gates are copied to every
-  // key row.
-  static __device__ void stage(float* in, const void* q, const void* k, const void* v,
-                               const float* g, const float* beta, const void* dout,
-                               size_t tok0, int L, int H, int h) {
-    for (int i = threadIdx.x; i < BK * DK; i += NT) {
+  // One block's inputs in flight, this thread's share: loaded early into
+  // registers, written to a staging buffer once the buffer is free.  Rows
+  // past the block's length read as zeros.  Gated DeltaNet gates are copied to
+  // every key row.  REV: the reverse sweep's set (q, k, g, v - p from the
+  // workspace, do, beta); otherwise the forward sweep's (k, g, v, beta).
+  struct Stage {
+    float q[NQ], k[NQ], g[NQ], v[NV], d[NV], b;
+  };
+  template <bool REV>
+  static __device__ __forceinline__ void stage_load(Stage& st, const void* q, const void* k,
+                                                    const void* v, const float* g,
+                                                    const float* beta, const void* dout,
+                                                    const float* vp, size_t tok0, int L, int H,
+                                                    int h) {
+#pragma unroll
+    for (int s = 0; s < NQ; ++s) {
+      const int i = threadIdx.x + s * NT;
       const int j = i / DK, c = i - j * DK;
       const size_t e = ((tok0 + j) * H + h) * (size_t)DK + c;
-      const bool ok = j < L;
-      in[Cfg::IN_Q + i] = ok ? Io::load(q, e) : 0.f;
-      in[Cfg::IN_K + i] = ok ? Io::load(k, e) : 0.f;
-      in[Cfg::IN_G + i] = ok ? (Cfg::SG ? g[(tok0 + j) * H + h] : g[e]) : 0.f;
+      const bool ok = i < BK * DK && j < L;
+      st.q[s] = (REV && ok) ? Io::load(q, e) : 0.f;
+      st.k[s] = ok ? Io::load(k, e) : 0.f;
+      st.g[s] = ok ? (Cfg::SG ? g[(tok0 + j) * H + h] : g[e]) : 0.f;
     }
-    for (int i = threadIdx.x; i < BK * DV; i += NT) {
+#pragma unroll
+    for (int s = 0; s < NV; ++s) {
+      const int i = threadIdx.x + s * NT;
       const int j = i / DV, c = i - j * DV;
       const size_t e = ((tok0 + j) * H + h) * (size_t)DV + c;
-      const bool ok = j < L;
-      in[Cfg::IN_V + i] = ok ? Io::load(v, e) : 0.f;
-      in[Cfg::IN_DO + i] = ok ? Io::load(dout, e) : 0.f;
+      const bool ok = i < BK * DV && j < L;
+      st.v[s] = ok ? (REV ? vp[e] : Io::load(v, e)) : 0.f;
+      st.d[s] = (REV && ok) ? Io::load(dout, e) : 0.f;
     }
-    if (threadIdx.x < BK)
-      in[Cfg::IN_B + threadIdx.x] = (int)threadIdx.x < L ? beta[(tok0 + threadIdx.x) * H + h] : 0.f;
+    st.b = (int)threadIdx.x < L ? beta[(tok0 + threadIdx.x) * H + h] : 0.f;
+  }
+  static __device__ __forceinline__ void stage_store(const Stage& st, float* in) {
+#pragma unroll
+    for (int s = 0; s < NQ; ++s) {
+      const int i = threadIdx.x + s * NT;
+      if (i < BK * DK) {
+        in[Cfg::IN_Q + i] = st.q[s];
+        in[Cfg::IN_K + i] = st.k[s];
+        in[Cfg::IN_G + i] = st.g[s];
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < NV; ++s) {
+      const int i = threadIdx.x + s * NT;
+      if (i < BK * DV) {
+        in[Cfg::IN_V + i] = st.v[s];
+        in[Cfg::IN_DO + i] = st.d[s];
+      }
+    }
+    if (threadIdx.x < BK) in[Cfg::IN_B + threadIdx.x] = st.b;
   }
 
   // RPT consecutive staged floats (rows RPT*rg ..) into registers
@@ -102,9 +139,10 @@ struct Bwd {
     }
   }
 
-  // One forward step of token j of the staged block on S (in place).
+  // Forward sweep, token j of the staged block: the full step on S, and
+  // v - p of the lane's columns to `vp_out` (one lane per column quad).
   static __device__ __forceinline__ void fwd_step(f32x4 (&S)[RPT], const float* in, int j,
-                                                  const Lane& ln) {
+                                                  float* vp_out, const Lane& ln) {
     float kr[RPT], gr[RPT];
     rows(in + Cfg::IN_K + j * DK + RPT * ln.rg, kr);
     rows(in + Cfg::IN_G + j * DK + RPT * ln.rg, gr);
@@ -116,11 +154,25 @@ struct Bwd {
       S[r] *= __expf(gr[r]);
       p += S[r] * kr[r];
     }
-    f32x4 e;
+    f32x4 vp;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) e[c] = b * (vv[c] - row_sum16(p[c]));
+    for (int c = 0; c < 4; ++c) vp[c] = vv[c] - row_sum16(p[c]);
+    if (ln.rg == 0) *reinterpret_cast<f32x4*>(vp_out + ln.c0) = vp;
+    const f32x4 e = b * vp;
 #pragma unroll
     for (int r = 0; r < RPT; ++r) S[r] += kr[r] * e;
+  }
+
+  // Reverse sweep, recomputing: the step of token j from the stored v - p
+  // (no reduction).
+  static __device__ __forceinline__ void re_step(f32x4 (&S)[RPT], const float* in, int j,
+                                                 const Lane& ln) {
+    float kr[RPT], gr[RPT];
+    rows(in + Cfg::IN_K + j * DK + RPT * ln.rg, kr);
+    rows(in + Cfg::IN_G + j * DK + RPT * ln.rg, gr);
+    const f32x4 e = in[Cfg::IN_B + j] * *reinterpret_cast<const f32x4*>(in + Cfg::IN_V + j * DV + ln.c0);
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) S[r] = S[r] * __expf(gr[r]) + kr[r] * e;
   }
 
   // Sum over the four column quads of the wave (lanes l, l^16, l^32, l^48).
@@ -130,10 +182,9 @@ struct Bwd {
     return x;
   }
 
-  // Token j of the staged block, from its previous state Sp: the forward step
-  // it needs (Sbar, p, e, S_j), then the backward step on dS.  Per-wave
-  // partials of dq, dk, dg go to red[j], of dbeta (and the Gated DeltaNet dg)
-  // to rs[j]; dv is final and goes straight out.
+  // Token j of the staged block, from its previous state Sp: the backward
+  // step on dS.  Per-wave partials of dq, dk, dg go to red[j], of dbeta (and
+  // the Gated DeltaNet dg) to rs[j]; dv is final and goes straight out.
   static __device__ __forceinline__ void bwd_step(const f32x4 (&Sp)[RPT], f32x4 (&dS)[RPT],
                                                   const float* in, int j, float* red, float* rs,
                                                   float* dv_out, float scale, const Lane& ln) {
@@ -141,34 +192,25 @@ struct Bwd {
     rows(in + Cfg::IN_K + j * DK + RPT * ln.rg, kr);
     rows(in + Cfg::IN_G + j * DK + RPT * ln.rg, gr);
     rows(in + Cfg::IN_Q + j * DK + RPT * ln.rg, qr);
-    const f32x4 vv = *reinterpret_cast<const f32x4*>(in + Cfg::IN_V + j * DV + ln.c0);
+    const f32x4 vp = *reinterpret_cast<const f32x4*>(in + Cfg::IN_V + j * DV + ln.c0);
     const f32x4 dov = *reinterpret_cast<const f32x4*>(in + Cfg::IN_DO + j * DV + ln.c0);
     const float b = in[Cfg::IN_B + j];
-    // forward: Sbar, p, e
+    const f32x4 e = b * vp;
+    // the read o = scale S_j^T q with S_j = Sbar + k e^T: dq = scale (Sbar do +
+    // k (e . do)), and dS += scale q do^T
+    const float edo = e[0] * dov[0] + e[1] * dov[1] + e[2] * dov[2] + e[3] * dov[3];
     f32x4 Sb[RPT];
-    float a[RPT];
-    f32x4 p = {0.f, 0.f, 0.f, 0.f};
+    float a[RPT], dqp[RPT];
+    f32x4 de = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int r = 0; r < RPT; ++r) {
       a[r] = __expf(gr[r]);
       Sb[r] = Sp[r] * a[r];
-      p += Sb[r] * kr[r];
-    }
-    f32x4 e, vp;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const float pc = row_sum16(p[c]);
-      vp[c] = vv[c] - pc;
-      e[c] = b * vp[c];
-    }
-    // the read: dS += scale q do^T, dq = scale S_j do (S_j = Sbar + k e^T)
-    float dqp[RPT];
-    f32x4 de = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int r = 0; r < RPT; ++r) {
-      const f32x4 Sj = Sb[r] + kr[r] * e;
-      const f32x4 t = Sj * dov;
-      dqp[r] = scale * ((t[0] + t[1]) + (t[2] + t[3]));
+      float x = kr[r] * edo;
+      x = __builtin_fmaf(Sb[r][0], dov[0], x);
+      x = __builtin_fmaf(Sb[r][1], dov[1], x);
+      x = __builtin_fmaf(Sb[r][2], dov[2], x);
+      dqp[r] = __builtin_fmaf(Sb[r][3], dov[3], x);
       dS[r] += (scale * qr[r]) * dov;
       de += dS[r] * kr[r];
     }
@@ -176,16 +218,23 @@ struct Bwd {
     for (int c = 0; c < 4; ++c) de[c] = row_sum16(de[c]);
     const f32x4 dp = -b * de;
     // dbeta over the lane's columns (the same in the 16 lanes of a row group)
-    const f32x4 tb = de * vp;
-    float dbp = (tb[0] + tb[1]) + (tb[2] + tb[3]);
+    float dbp = de[0] * vp[0] + de[1] * vp[1] + de[2] * vp[2] + de[3] * vp[3];
     float dkp[RPT], dgp[RPT];
 #pragma unroll
     for (int r = 0; r < RPT; ++r) {
-      const f32x4 t = dS[r] * e + Sb[r] * dp;
-      dkp[r] = (t[0] + t[1]) + (t[2] + t[3]);
+      float x = dS[r][0] * e[0];
+      x = __builtin_fmaf(dS[r][1], e[1], x);
+      x = __builtin_fmaf(dS[r][2], e[2], x);
+      x = __builtin_fmaf(dS[r][3], e[3], x);
+      x = __builtin_fmaf(Sb[r][0], dp[0], x);
+      x = __builtin_fmaf(Sb[r][1], dp[1], x);
+      x = __builtin_fmaf(Sb[r][2], dp[2], x);
+      dkp[r] = __builtin_fmaf(Sb[r][3], dp[3], x);
       const f32x4 dSb = dS[r] + kr[r] * dp;
-      const f32x4 u = Sb[r] * dSb;
-      dgp[r] = (u[0] + u[1]) + (u[2] + u[3]);
+      float y = Sb[r][0] * dSb[0];
+      y = __builtin_fmaf(Sb[r][1], dSb[1], y);
+      y = __builtin_fmaf(Sb[r][2], dSb[2], y);
+      dgp[r] = __builtin_fmaf(Sb[r][3], dSb[3], y);
       dS[r] = dSb * a[r];
     }
     // dv: final, one lane per column quad
@@ -193,7 +242,7 @@ struct Bwd {
     // sums over the wave's 16 columns
 #pragma unroll
     for (int r = 0; r < RPT; ++r) {
-      dqp[r] = quad_sum(dqp[r]);
+      dqp[r] = scale * quad_sum(dqp[r]);
       dkp[r] = quad_sum(dkp[r]);
       dgp[r] = quad_sum(dgp[r]);
     }
@@ -252,7 +301,8 @@ struct Bwd {
 
 // S0, dS_final, dS0 are [n_seq, H, DK, DV].  ws holds the checkpoints: for
 // sequence n (first token t0), block m of head h is slot (n + t0/BK + m)*H + h,
-// DK*DV floats in the lanes' own order.
+// DK*DV floats in the lanes' own order; after them, vp [rows, H, DV] holds
+// v - p of every token (p = Sbar^T k, from the forward sweep).
 template <class Cfg>
 __global__ __launch_bounds__(Cfg::NT) void kda_bwd_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
@@ -260,8 +310,9 @@ __global__ __launch_bounds__(Cfg::NT) void kda_bwd_kernel(
     const void* __restrict__ dout, const float* __restrict__ dSf, float* __restrict__ dq,
     float* __restrict__ dk, float* __restrict__ dv, float* __restrict__ dg,
     float* __restrict__ dbeta, float* __restrict__ dS0, const int32_t* __restrict__ cu, int T,
-    int H, float scale, float* __restrict__ ws) {
+    int H, float scale, float* ws, float* vp) {
   typedef Bwd<Cfg> K;
+  typedef typename K::Stage Stage;
   constexpr int DK = Cfg::DK, DV = Cfg::DV, RPT = Cfg::RPT;
   extern __shared__ __attribute__((aligned(16))) float lds[];
   const int nh = blockIdx.x, n = nh / H, h = nh - n * H;
@@ -281,6 +332,7 @@ __global__ __launch_bounds__(Cfg::NT) void kda_bwd_kernel(
     len = T;
   }
   const int nb = (len + BK - 1) / BK;
+  auto blen = [&](int m) { return (len - m * BK) < BK ? (len - m * BK) : BK; };
   const size_t slot_stride = (size_t)H * DK * DV;
   float* ck = ws + ((size_t)n + t0 / BK) * slot_stride + (size_t)h * DK * DV;
   // this lane's float4 of row r inside a checkpoint slot
@@ -288,62 +340,89 @@ __global__ __launch_bounds__(Cfg::NT) void kda_bwd_kernel(
     return reinterpret_cast<f32x4*>(ck + m * slot_stride +
                                     (size_t)((ln.w * RPT + r) * 64 + ln.l) * 4);
   };
+  auto in_buf = [&](int m) { return lds + Cfg::OFF_IN + (m & 1) * Cfg::IN_SZ; };
   const size_t sbase = (size_t)nh * DK * DV + (size_t)(RPT * ln.rg) * DV + ln.c0;
+  Stage st;
 
-  // forward sweep: checkpoint at the start of every block
+  // forward sweep: checkpoint at the start of every block, v - p per token;
+  // the next block's inputs load while this one is computed
   f32x4 S[RPT];
 #pragma unroll
   for (int r = 0; r < RPT; ++r)
     S[r] = S0 ? *reinterpret_cast<const f32x4*>(S0 + sbase + (size_t)r * DV)
               : f32x4{0.f, 0.f, 0.f, 0.f};
+  if (nb > 0) {
+    K::template stage_load<false>(st, q, k, v, g, beta, dout, vp, t0, blen(0), H, h);
+    K::stage_store(st, in_buf(0));
+  }
   for (int m = 0; m < nb; ++m) {
-    const int L = (len - m * BK) < BK ? (len - m * BK) : BK;
-    float* in = lds + Cfg::OFF_IN + (m & 1) * Cfg::IN_SZ;
+    const int L = blen(m);
+    const size_t tok0 = t0 + (size_t)m * BK;
+    float* in = in_buf(m);
 #pragma unroll
     for (int r = 0; r < RPT; ++r) *ck_at(m, r) = S[r];
-    K::stage(in, q, k, v, g, beta, dout, t0 + (size_t)m * BK, L, H, h);
     __syncthreads();
-    for (int j = 0; j < L; ++j) K::fwd_step(S, in, j, ln);
+    if (m + 1 < nb)
+      K::template stage_load<false>(st, q, k, v, g, beta, dout, vp, tok0 + BK, blen(m + 1), H, h);
+    for (int j = 0; j < L; ++j)
+      K::fwd_step(S, in, j, vp + ((tok0 + j) * H + h) * (size_t)DV, ln);
+    if (m + 1 < nb) K::stage_store(st, in_buf(m + 1));
   }
-  __syncthreads();
+  __syncthreads();   // the forward sweep's staging reads and vp writes are done
 
   // reverse sweep
-  f32x4 dS[RPT];
+  f32x4 dS[RPT], Sc[RPT];
 #pragma unroll
   for (int r = 0; r < RPT; ++r)
     dS[r] = dSf ? *reinterpret_cast<const f32x4*>(dSf + sbase + (size_t)r * DV)
                 : f32x4{0.f, 0.f, 0.f, 0.f};
+  if (nb > 0) {
+    K::template stage_load<true>(st, q, k, v, g, beta, dout, vp, t0 + (size_t)(nb - 1) * BK,
+                                 blen(nb - 1), H, h);
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) Sc[r] = *ck_at(nb - 1, r);
+    K::stage_store(st, in_buf(nb - 1));
+  }
   for (int m = nb - 1; m >= 0; --m) {
     const int p = m & 1;
-    const int L = (len - m * BK) < BK ? (len - m * BK) : BK;
+    const int L = blen(m);
     const size_t tok0 = t0 + (size_t)m * BK;
-    float* in = lds + Cfg::OFF_IN + p * Cfg::IN_SZ;
+    float* in = in_buf(m);
     float* red = lds + Cfg::OFF_RED + p * Cfg::RED_SZ;
     float* rs = lds + Cfg::OFF_RS + p * Cfg::RS_SZ;
-    K::stage(in, q, k, v, g, beta, dout, tok0, L, H, h);
     __syncthreads();
-    if (m + 1 < nb) {
-      const int Ln = (len - (m + 1) * BK) < BK ? (len - (m + 1) * BK) : BK;
+    if (m + 1 < nb)
       K::write_out(lds + Cfg::OFF_RED + (p ^ 1) * Cfg::RED_SZ,
-                   lds + Cfg::OFF_RS + (p ^ 1) * Cfg::RS_SZ, tok0 + BK, Ln, H, h, dq, dk, dg,
-                   dbeta);
-    }
-    f32x4 Sc[RPT];
+                   lds + Cfg::OFF_RS + (p ^ 1) * Cfg::RS_SZ, tok0 + BK, blen(m + 1), H, h, dq, dk,
+                   dg, dbeta);
+    if (m > 0)
+      K::template stage_load<true>(st, q, k, v, g, beta, dout, vp, tok0 - BK, BK, H, h);
+    // states before tokens 0 and 1 of the block stay in registers (Sc, S1);
+    // later ones are recomputed from S1
+    f32x4 S1[RPT];
+    if (L >= 2) {
 #pragma unroll
-    for (int r = 0; r < RPT; ++r) Sc[r] = *ck_at(m, r);
-    for (int j = L - 1; j >= 0; --j) {
+      for (int r = 0; r < RPT; ++r) S1[r] = Sc[r];
+      K::re_step(S1, in, 0, ln);
+    }
+    for (int j = L - 1; j >= 2; --j) {
       f32x4 Sw[RPT];
 #pragma unroll
-      for (int r = 0; r < RPT; ++r) Sw[r] = Sc[r];
-      for (int t = 0; t < j; ++t) K::fwd_step(Sw, in, t, ln);
+      for (int r = 0; r < RPT; ++r) Sw[r] = S1[r];
+      for (int t = 1; t < j; ++t) K::re_step(Sw, in, t, ln);
       K::bwd_step(Sw, dS, in, j, red, rs, dv + ((tok0 + j) * H + h) * (size_t)DV, scale, ln);
+    }
+    if (L >= 2)
+      K::bwd_step(S1, dS, in, 1, red, rs, dv + ((tok0 + 1) * H + h) * (size_t)DV, scale, ln);
+    K::bwd_step(Sc, dS, in, 0, red, rs, dv + (tok0 * H + h) * (size_t)DV, scale, ln);
+    if (m > 0) {
+#pragma unroll
+      for (int r = 0; r < RPT; ++r) Sc[r] = *ck_at(m - 1, r);
+      K::stage_store(st, in_buf(m - 1));
     }
   }
   __syncthreads();
-  if (nb > 0) {
-    const int L0 = len < BK ? len : BK;
-    K::write_out(lds + Cfg::OFF_RED, lds + Cfg::OFF_RS, t0, L0, H, h, dq, dk, dg, dbeta);
-  }
+  if (nb > 0) K::write_out(lds + Cfg::OFF_RED, lds + Cfg::OFF_RS, t0, blen(0), H, h, dq, dk, dg, dbeta);
   if (dS0) {
 #pragma unroll
     for (int r = 0; r < RPT; ++r) *reinterpret_cast<f32x4*>(dS0 + sbase + (size_t)r * DV) = dS[r];
@@ -361,16 +440,21 @@ hipError_t launch_bwd_t(const void* q, const void* k, const void* v, const float
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      bytes);
   if (e != hipSuccess) return e;
+  // v - p follows the checkpoint slots (T is T_total when packed)
+  const size_t rows = cu ? (size_t)T : (size_t)n_seq * T;
+  float* vp = ws + ((size_t)n_seq + rows / BK) * (size_t)H * Cfg::DK * Cfg::DV;
   hipLaunchKernelGGL(kern, dim3(n_seq * H), dim3(Cfg::NT), bytes, stream, q, k, v, g, beta, S0,
-                     dout, dSf, dq, dk, dv, dg, dbeta, dS0, cu, T, H, scale, ws);
+                     dout, dSf, dq, dk, dv, dg, dbeta, dS0, cu, T, H, scale, ws, vp);
   return hipGetLastError();
 }
 
 }  // namespace
 
 // Checkpoint slots the backward needs: n_seq + rows / BK per head.
+// Checkpoint slots (n_seq + rows / BK per head), then v - p of every token.
 size_t backward_workspace_bytes(int n_seq, size_t rows, int H, int dk, int dv) {
-  return ((size_t)n_seq + rows / BK) * (size_t)H * dk * dv * sizeof(float);
+  return (((size_t)n_seq + rows / BK) * (size_t)H * dk * dv + rows * (size_t)H * dv) *
+         sizeof(float);
 }
 
 hipError_t launch_backward(const void* q, const void* k, const void* v, const float* g,
