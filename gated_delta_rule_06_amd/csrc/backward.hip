@@ -44,7 +44,7 @@ struct BwdCfg {
   static constexpr int NW = DV / 16;          // waves
   static constexpr int NT = 64 * NW;          // threads
   static constexpr int RPT = DK / 16;         // key rows per lane
-  // staged inputs of one block (floats): q, k, g [BK][DK]; v (forward sweep)
+  // staged inputs of one block (floats): q, k, alpha = exp(g) [BK][DK]; v (forward sweep)
   // or v - p (reverse sweep), do [BK][DV]; beta [BK]
   static constexpr int IN_Q = 0, IN_K = BK * DK, IN_G = 2 * BK * DK, IN_V = 3 * BK * DK;
   static constexpr int IN_DO = IN_V + BK * DV, IN_B = IN_DO + BK * DV;
@@ -116,7 +116,7 @@ struct Bwd {
       if (i < BK * DK) {
         in[Cfg::IN_Q + i] = st.q[s];
         in[Cfg::IN_K + i] = st.k[s];
-        in[Cfg::IN_G + i] = st.g[s];
+        in[Cfg::IN_G + i] = __expf(st.g[s]);   // the decay factor alpha
       }
     }
 #pragma unroll
@@ -151,7 +151,7 @@ struct Bwd {
     f32x4 p = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int r = 0; r < RPT; ++r) {
-      S[r] *= __expf(gr[r]);
+      S[r] *= gr[r];
       p += S[r] * kr[r];
     }
     f32x4 vp;
@@ -172,7 +172,7 @@ struct Bwd {
     rows(in + Cfg::IN_G + j * DK + RPT * ln.rg, gr);
     const f32x4 e = in[Cfg::IN_B + j] * *reinterpret_cast<const f32x4*>(in + Cfg::IN_V + j * DV + ln.c0);
 #pragma unroll
-    for (int r = 0; r < RPT; ++r) S[r] = S[r] * __expf(gr[r]) + kr[r] * e;
+    for (int r = 0; r < RPT; ++r) S[r] = S[r] * gr[r] + kr[r] * e;
   }
 
   // Sum over the four column quads of the wave (lanes l, l^16, l^32, l^48).
@@ -204,7 +204,7 @@ struct Bwd {
     f32x4 de = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int r = 0; r < RPT; ++r) {
-      a[r] = __expf(gr[r]);
+      a[r] = gr[r];
       Sb[r] = Sp[r] * a[r];
       float x = kr[r] * edo;
       x = __builtin_fmaf(Sb[r][0], dov[0], x);
@@ -412,12 +412,18 @@ __global__ __launch_bounds__(Cfg::NT) void kda_bwd_kernel(
       for (int t = 1; t < j; ++t) K::re_step(Sw, in, t, ln);
       K::bwd_step(Sw, dS, in, j, red, rs, dv + ((tok0 + j) * H + h) * (size_t)DV, scale, ln);
     }
+    // the previous block's checkpoint loads during the last two tokens
+    f32x4 Sn[RPT];
+    if (m > 0) {
+#pragma unroll
+      for (int r = 0; r < RPT; ++r) Sn[r] = *ck_at(m - 1, r);
+    }
     if (L >= 2)
       K::bwd_step(S1, dS, in, 1, red, rs, dv + ((tok0 + 1) * H + h) * (size_t)DV, scale, ln);
     K::bwd_step(Sc, dS, in, 0, red, rs, dv + (tok0 * H + h) * (size_t)DV, scale, ln);
     if (m > 0) {
 #pragma unroll
-      for (int r = 0; r < RPT; ++r) Sc[r] = *ck_at(m - 1, r);
+      for (int r = 0; r < RPT; ++r) Sc[r] = Sn[r];
       K::stage_store(st, in_buf(m - 1));
     }
   }
