@@ -20,21 +20,23 @@
 // one LDS slot per wave, added over the waves once per block of BK tokens.
 //
 // The backward needs the forward states in reverse order.  A forward sweep
-// stores the state at the start of every block of BK tokens to the workspace
-// (each lane its own registers, so the read back needs no barrier), and v - p
-// of every token.  The reverse sweep takes the blocks last to first; the
-// states before a block's first two tokens stay in registers, the later ones
-// are recomputed from the second (one step per token on average, each a
-// decay and a rank-1 update from the stored v - p, with no reduction).  A
-// block's token inputs are staged in LDS (two buffers, one barrier per
-// block); the next block's inputs and checkpoint load while this one runs.
+// stores the state at the start of every block of BK = 8 tokens to the
+// workspace (each lane its own registers, so the read back needs no barrier),
+// and v - p of every token.  The reverse sweep takes the blocks last to first;
+// the states before a block's tokens 0, 1 and 4 stay in registers, the others
+// are recomputed from the nearest one below (13 steps per 8 tokens, each a
+// decay and a rank-1 update from the stored v - p, with no reduction).  The
+// checkpoints are most of the kernel's memory traffic (d_k d_v fp32 per head
+// and block, written once and read once), hence the block length.  A block's
+// token inputs are staged in LDS (two buffers); the next block's inputs and
+// checkpoint load while this one runs.
 #include "common.h"
 
 namespace kda {
 
 namespace {
 
-constexpr int BK = 4;   // tokens per checkpoint block
+constexpr int BK = 8;   // tokens per checkpoint block
 
 template <int DK_, int DV_, class Io_, bool SG_>
 struct BwdCfg {
@@ -55,10 +57,10 @@ struct BwdCfg {
   // dbeta (and the Gated DeltaNet dg) [BK][2][NW]
   static constexpr int RED_SZ = BK * 3 * NW * DK;
   static constexpr int RS_SZ = (BK * 2 * NW + 3) / 4 * 4;
-  static constexpr int OFF_IN = 0;
-  static constexpr int OFF_RED = OFF_IN + 2 * IN_SZ;
-  static constexpr int OFF_RS = OFF_RED + 2 * RED_SZ;
-  static constexpr int LDS_FLOATS = OFF_RS + 2 * RS_SZ;
+  static constexpr int OFF_IN = 0;                  // two staging buffers
+  static constexpr int OFF_RED = OFF_IN + 2 * IN_SZ;  // one block of partials
+  static constexpr int OFF_RS = OFF_RED + RED_SZ;
+  static constexpr int LDS_FLOATS = OFF_RS + RS_SZ;
   static_assert(LDS_FLOATS * 4 <= 160 * 1024, "LDS budget");
 };
 
@@ -199,18 +201,18 @@ struct Bwd {
     // the read o = scale S_j^T q with S_j = Sbar + k e^T: dq = scale (Sbar do +
     // k (e . do)), and dS += scale q do^T
     const float edo = e[0] * dov[0] + e[1] * dov[1] + e[2] * dov[2] + e[3] * dov[3];
-    f32x4 Sb[RPT];
-    float a[RPT], dqp[RPT];
+    // Sbar = Diag(alpha) Sp is formed where it is used (registers are short)
+    const float (&a)[RPT] = gr;
+    float dqp[RPT];
     f32x4 de = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int r = 0; r < RPT; ++r) {
-      a[r] = gr[r];
-      Sb[r] = Sp[r] * a[r];
+      const f32x4 Sb = Sp[r] * a[r];
       float x = kr[r] * edo;
-      x = __builtin_fmaf(Sb[r][0], dov[0], x);
-      x = __builtin_fmaf(Sb[r][1], dov[1], x);
-      x = __builtin_fmaf(Sb[r][2], dov[2], x);
-      dqp[r] = __builtin_fmaf(Sb[r][3], dov[3], x);
+      x = __builtin_fmaf(Sb[0], dov[0], x);
+      x = __builtin_fmaf(Sb[1], dov[1], x);
+      x = __builtin_fmaf(Sb[2], dov[2], x);
+      dqp[r] = __builtin_fmaf(Sb[3], dov[3], x);
       dS[r] += (scale * qr[r]) * dov;
       de += dS[r] * kr[r];
     }
@@ -222,19 +224,20 @@ struct Bwd {
     float dkp[RPT], dgp[RPT];
 #pragma unroll
     for (int r = 0; r < RPT; ++r) {
+      const f32x4 Sb = Sp[r] * a[r];
       float x = dS[r][0] * e[0];
       x = __builtin_fmaf(dS[r][1], e[1], x);
       x = __builtin_fmaf(dS[r][2], e[2], x);
       x = __builtin_fmaf(dS[r][3], e[3], x);
-      x = __builtin_fmaf(Sb[r][0], dp[0], x);
-      x = __builtin_fmaf(Sb[r][1], dp[1], x);
-      x = __builtin_fmaf(Sb[r][2], dp[2], x);
-      dkp[r] = __builtin_fmaf(Sb[r][3], dp[3], x);
+      x = __builtin_fmaf(Sb[0], dp[0], x);
+      x = __builtin_fmaf(Sb[1], dp[1], x);
+      x = __builtin_fmaf(Sb[2], dp[2], x);
+      dkp[r] = __builtin_fmaf(Sb[3], dp[3], x);
       const f32x4 dSb = dS[r] + kr[r] * dp;
-      float y = Sb[r][0] * dSb[0];
-      y = __builtin_fmaf(Sb[r][1], dSb[1], y);
-      y = __builtin_fmaf(Sb[r][2], dSb[2], y);
-      dgp[r] = __builtin_fmaf(Sb[r][3], dSb[3], y);
+      float y = Sb[0] * dSb[0];
+      y = __builtin_fmaf(Sb[1], dSb[1], y);
+      y = __builtin_fmaf(Sb[2], dSb[2], y);
+      dgp[r] = __builtin_fmaf(Sb[3], dSb[3], y);
       dS[r] = dSb * a[r];
     }
     // dv: final, one lane per column quad
@@ -351,22 +354,31 @@ __global__ __launch_bounds__(Cfg::NT) void kda_bwd_kernel(
   for (int r = 0; r < RPT; ++r)
     S[r] = S0 ? *reinterpret_cast<const f32x4*>(S0 + sbase + (size_t)r * DV)
               : f32x4{0.f, 0.f, 0.f, 0.f};
+  // the inputs of two blocks ahead are in flight, in two register sets that
+  // alternate (the loop body is written out twice so that no set is copied)
+  Stage sa;
   if (nb > 0) {
     K::template stage_load<false>(st, q, k, v, g, beta, dout, vp, t0, blen(0), H, h);
     K::stage_store(st, in_buf(0));
   }
-  for (int m = 0; m < nb; ++m) {
+  if (nb > 1) K::template stage_load<false>(sa, q, k, v, g, beta, dout, vp, t0 + BK, blen(1), H, h);
+  auto fwd_block = [&](int m, Stage& next, Stage& later) {
     const int L = blen(m);
     const size_t tok0 = t0 + (size_t)m * BK;
     float* in = in_buf(m);
 #pragma unroll
     for (int r = 0; r < RPT; ++r) *ck_at(m, r) = S[r];
     __syncthreads();
-    if (m + 1 < nb)
-      K::template stage_load<false>(st, q, k, v, g, beta, dout, vp, tok0 + BK, blen(m + 1), H, h);
+    if (m + 2 < nb)
+      K::template stage_load<false>(later, q, k, v, g, beta, dout, vp, tok0 + 2 * BK, blen(m + 2),
+                                    H, h);
     for (int j = 0; j < L; ++j)
       K::fwd_step(S, in, j, vp + ((tok0 + j) * H + h) * (size_t)DV, ln);
-    if (m + 1 < nb) K::stage_store(st, in_buf(m + 1));
+    if (m + 1 < nb) K::stage_store(next, in_buf(m + 1));
+  };
+  for (int m = 0; m < nb; m += 2) {
+    fwd_block(m, sa, st);
+    if (m + 1 < nb) fwd_block(m + 1, st, sa);
   }
   __syncthreads();   // the forward sweep's staging reads and vp writes are done
 
@@ -383,44 +395,56 @@ __global__ __launch_bounds__(Cfg::NT) void kda_bwd_kernel(
     for (int r = 0; r < RPT; ++r) Sc[r] = *ck_at(nb - 1, r);
     K::stage_store(st, in_buf(nb - 1));
   }
+  float* red = lds + Cfg::OFF_RED;
+  float* rs = lds + Cfg::OFF_RS;
   for (int m = nb - 1; m >= 0; --m) {
-    const int p = m & 1;
     const int L = blen(m);
     const size_t tok0 = t0 + (size_t)m * BK;
     float* in = in_buf(m);
-    float* red = lds + Cfg::OFF_RED + p * Cfg::RED_SZ;
-    float* rs = lds + Cfg::OFF_RS + p * Cfg::RS_SZ;
-    __syncthreads();
-    if (m + 1 < nb)
-      K::write_out(lds + Cfg::OFF_RED + (p ^ 1) * Cfg::RED_SZ,
-                   lds + Cfg::OFF_RS + (p ^ 1) * Cfg::RS_SZ, tok0 + BK, blen(m + 1), H, h, dq, dk,
-                   dg, dbeta);
-    if (m > 0)
-      K::template stage_load<true>(st, q, k, v, g, beta, dout, vp, tok0 - BK, BK, H, h);
-    // states before tokens 0 and 1 of the block stay in registers (Sc, S1);
-    // later ones are recomputed from S1
-    f32x4 S1[RPT];
+    __syncthreads();   // this block's inputs are staged; the partials hold block m + 1's
+    if (m + 1 < nb) {
+      K::write_out(red, rs, tok0 + BK, blen(m + 1), H, h, dq, dk, dg, dbeta);
+      __syncthreads();   // the partials are free again
+    }
+    auto dvp = [&](int j) { return dv + ((tok0 + j) * H + h) * (size_t)DV; };
+    // States before tokens 0, 1 and 4 of the block stay in registers (Sc, S1,
+    // S4); the others are recomputed from the nearest one below: 13 steps for
+    // 8 tokens.
+    f32x4 S1[RPT], S4[RPT];
     if (L >= 2) {
 #pragma unroll
       for (int r = 0; r < RPT; ++r) S1[r] = Sc[r];
       K::re_step(S1, in, 0, ln);
     }
-    for (int j = L - 1; j >= 2; --j) {
+    if (L >= 5) {
+#pragma unroll
+      for (int r = 0; r < RPT; ++r) S4[r] = S1[r];
+      for (int t = 1; t < 4; ++t) K::re_step(S4, in, t, ln);
+      for (int j = L - 1; j >= 5; --j) {
+        f32x4 Sw[RPT];
+#pragma unroll
+        for (int r = 0; r < RPT; ++r) Sw[r] = S4[r];
+        for (int t = 4; t < j; ++t) K::re_step(Sw, in, t, ln);
+        K::bwd_step(Sw, dS, in, j, red, rs, dvp(j), scale, ln);
+      }
+      K::bwd_step(S4, dS, in, 4, red, rs, dvp(4), scale, ln);
+    }
+    for (int j = (L < 4 ? L : 4) - 1; j >= 2; --j) {
       f32x4 Sw[RPT];
 #pragma unroll
       for (int r = 0; r < RPT; ++r) Sw[r] = S1[r];
       for (int t = 1; t < j; ++t) K::re_step(Sw, in, t, ln);
-      K::bwd_step(Sw, dS, in, j, red, rs, dv + ((tok0 + j) * H + h) * (size_t)DV, scale, ln);
+      K::bwd_step(Sw, dS, in, j, red, rs, dvp(j), scale, ln);
     }
-    // the previous block's checkpoint loads during the last two tokens
+    // the previous block's inputs and checkpoint load during the last two tokens
     f32x4 Sn[RPT];
     if (m > 0) {
+      K::template stage_load<true>(st, q, k, v, g, beta, dout, vp, tok0 - BK, BK, H, h);
 #pragma unroll
       for (int r = 0; r < RPT; ++r) Sn[r] = *ck_at(m - 1, r);
     }
-    if (L >= 2)
-      K::bwd_step(S1, dS, in, 1, red, rs, dv + ((tok0 + 1) * H + h) * (size_t)DV, scale, ln);
-    K::bwd_step(Sc, dS, in, 0, red, rs, dv + (tok0 * H + h) * (size_t)DV, scale, ln);
+    if (L >= 2) K::bwd_step(S1, dS, in, 1, red, rs, dvp(1), scale, ln);
+    K::bwd_step(Sc, dS, in, 0, red, rs, dvp(0), scale, ln);
     if (m > 0) {
 #pragma unroll
       for (int r = 0; r < RPT; ++r) Sc[r] = Sn[r];
@@ -428,7 +452,7 @@ __global__ __launch_bounds__(Cfg::NT) void kda_bwd_kernel(
     }
   }
   __syncthreads();
-  if (nb > 0) K::write_out(lds + Cfg::OFF_RED, lds + Cfg::OFF_RS, t0, blen(0), H, h, dq, dk, dg, dbeta);
+  if (nb > 0) K::write_out(red, rs, t0, blen(0), H, h, dq, dk, dg, dbeta);
   if (dS0) {
 #pragma unroll
     for (int r = 0; r < RPT; ++r) *reinterpret_cast<f32x4*>(dS0 + sbase + (size_t)r * DV) = dS[r];

@@ -299,7 +299,7 @@ int kda_decode_step_fused(const void* q, const void* k, const void* v, const flo
  *  dS0        dL/dS0 [N, H, d_k, d_v] fp32, or NULL (not written)
  *  workspace  device memory of at least kda_backward_workspace_size() bytes,
  *             16-byte aligned, overlapping nothing else; it holds the state
- *             at the start of every 4-token block and is clobbered
+ *             at the start of every 8-token block and v - p of every token, and is clobbered
  *
  * Every gradient is written in full (rows of empty sequences have none).  No
  * output may overlap an input, another output or the workspace.  d_k and d_v
