@@ -10,8 +10,9 @@ kda_decode_step calls) and reports its steps/s, and the multi-token decode
 workload (the same states, 256 sequences of U{1..8} new tokens, one
 kda_recurrent_fwd_varlen call updating them in place) and the Gated DeltaNet
 prefill (the headline shapes with one gate per token and head,
-kda_gdn_chunk_fwd) and the prefill of raw layer inputs with the in-kernel
-input transforms (q/k L2 norm, beta sigmoid, the -5 sigmoid gate).
+kda_gdn_chunk_fwd), the prefill of raw layer inputs with the in-kernel
+input transforms (q/k L2 norm, beta sigmoid, the -5 sigmoid gate), and the
+backward (kda_backward: every input gradient) of the headline prefill.
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 
@@ -34,11 +35,28 @@ def log(*a):
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA, published
+FP32_VALU_PEAK_TFLOPS = 157.3  # fp32 vector, published (256 CUs x 2.4 GHz x 256 flop/clk)
 
 PREFILL = dict(B=8, T=8192, H=32, dk=128, dv=128, io="bf16", chunk=64)
 DECODE = dict(N=256, H=32, dk=128, dv=128, io="bf16", steps=128)
 # multi-token decode: 256 sequences of U{1..8} tokens (seed 0) on resident states
 RECURRENT = dict(n_seq=256, lo=1, hi=8, H=32, dk=128, dv=128, io="bf16", calls=20)
+BACKWARD_CALLS = 5
+
+
+def backward_alg_flops(B, T, H, dk, dv):
+    """fp32 flops per head-token of the recurrence's backward, per state
+    element: the forward's decay, predict and write (1 + 2 + 2) and the
+    backward's read (dS += q do^T, dq: 2 + 2), de (2), dk (two terms, 4),
+    dSbar (2), dg (2) and the decay of dS (1): 20 d_k d_v."""
+    return B * T * H * 20 * dk * dv
+
+
+def backward_alg_bytes(B, T, H, dk, dv, io):
+    """q, k, v, d_out in the I/O type, log_alpha and beta in fp32 read once;
+    dq, dk, dv, dlog_alpha and dbeta in fp32 written once."""
+    e = 2 if io == "bf16" else 4
+    return B * T * H * (e * (2 * dk + 2 * dv) + 4 * dk + 4 + 4 * (3 * dk + dv) + 4)
 
 
 def prefill_alg_bytes(B, T, H, dk, dv, io, with_S0=False, with_S_final=True, gate_dims=None):
@@ -62,13 +80,16 @@ TRAFFIC_FILE = os.path.join(HERE, "profiles",
 CSRC = os.path.join(HERE, "gated_delta_rule_06_amd", "csrc")
 
 
-def measured_traffic(kernel="chunk", source="chunk.hip"):
+BWD_TRAFFIC_FILE = os.path.join(HERE, "profiles", "traffic_backward_b8_h32_t8192.md")
+
+
+def measured_traffic(kernel="chunk", source="chunk.hip", path=TRAFFIC_FILE):
     """HBM bytes per launch of one kernel from the committed counter summary
     (FETCH_SIZE + WRITE_SIZE, calibrated on a plain copy), or None when the
     kernel's source has changed since the counters were taken."""
     import hashlib
     try:
-        txt = open(TRAFFIC_FILE).read()
+        txt = open(path).read()
         src = hashlib.sha256(open(os.path.join(CSRC, source), "rb").read()).hexdigest()
     except OSError:
         return None
@@ -343,6 +364,29 @@ def main():
     del dr, Sr, o_rec
     torch.cuda.empty_cache()
 
+    # ---------------------------------------------------------------- backward
+    log("generating backward inputs (the prefill workload plus dL/dout)")
+    dbw = inputs.prefill_inputs(P["B"], P["T"], P["H"], P["dk"], P["dv"], io=P["io"], seed=0,
+                                with_S0=False, device=dev)
+    inputs.grad_inputs(dbw, seed=0, with_dS_final=False, device=dev)
+    ws_bw = torch.empty(kda.backward_workspace_size(P["B"], P["T"], P["H"], P["dk"], P["dv"]),
+                        dtype=torch.uint8, device=dev)
+
+    def bwd_call():
+        kda.backward(dbw["q"], dbw["k"], dbw["v"], dbw["g"], dbw["beta"], dbw["d_out"],
+                     want_dS0=False, workspace=ws_bw)
+
+    bw_ms = timed_calls(bwd_call, BACKWARD_CALLS, warm=2)
+    bw_f = backward_alg_flops(P["B"], P["T"], P["H"], P["dk"], P["dv"])
+    bw_b = backward_alg_bytes(P["B"], P["T"], P["H"], P["dk"], P["dv"], P["io"])
+    bw_tf = bw_f / (bw_ms * 1e-3) / 1e12
+    log("backward: %.2f ms per launch, %.1f TFLOP/s fp32 (%.1f%% of %.1f), %.0f GB/s"
+        % (bw_ms, bw_tf, 100 * bw_tf / FP32_VALU_PEAK_TFLOPS, FP32_VALU_PEAK_TFLOPS,
+           bw_b / (bw_ms * 1e-3) / 1e9))
+    bw_ws_gb = ws_bw.numel() / 1e9
+    del dbw, ws_bw
+    torch.cuda.empty_cache()
+
     # ---------------------------------------------------------------- CPU baseline
     cpu = None
     parity = None
@@ -447,6 +491,18 @@ def main():
                                    "traffic": measured_traffic("recurrent", "recurrent.hip"),
                                    "kernel": "recurrent_fwd_kernel<128,128,bf16>",
                                    "alg_bytes_per_launch": rec_b, "avg_launch_ms": rec_ms}},
+        "backward": {"workload": "backward_b8_h32_t8192 (dq, dk, dv, dlog_alpha, dbeta)",
+                     "avg_launch_ms": bw_ms, "tokens_per_s": tokens / (bw_ms * 1e-3),
+                     "workspace_gb": bw_ws_gb,
+                     "roofline": {"bound": "alu", "achieved": bw_tf,
+                                  "peak": FP32_VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                  "frac": bw_tf / FP32_VALU_PEAK_TFLOPS,
+                                  "traffic": measured_traffic("backward", "backward.hip",
+                                                              BWD_TRAFFIC_FILE),
+                                  "kernel": "kda_bwd_kernel<128,128,bf16>",
+                                  "alg_flops_per_launch": bw_f, "alg_bytes_per_launch": bw_b,
+                                  "hbm_gbs": bw_b / (bw_ms * 1e-3) / 1e9,
+                                  "avg_launch_ms": bw_ms}},
         "parity_sample": parity,
     }
     print(json.dumps(rec), flush=True)

@@ -55,7 +55,8 @@ def test_gdn_chunk_strong_decay_matches_oracle(gate, io):
     chunk step scales its products by per-token ratios Gamma_i / Gamma_j <= 1, so
     it needs no guard; the results must still match."""
     note("gdn chunk strong decay gate=%s io=%s" % (gate, io))
-    d = inputs.prefill_inputs(1, 150, 2, 128, 128, io=io, seed=3, with_S0=True, device=DEV,
+    dim = 128 if io == "bf16" else 64      # fp32 I/O runs d_k = d_v = 64
+    d = inputs.prefill_inputs(1, 150, 2, dim, dim, io=io, seed=3, with_S0=True, device=DEV,
                               gate="gdn")
     if gate == "uniform":
         gen = torch.Generator().manual_seed(11)
