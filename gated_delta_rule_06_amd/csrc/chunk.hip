@@ -1103,11 +1103,13 @@ struct ChunkKernel {
     }
   }
 
+  // next_norms: also write the next chunk's norm partials from `nxt` (FU with
+  // the L2-norm transform), ahead of the barrier this step has anyway.
   static __device__ __forceinline__ void scan_step(LDS char* smem, f32x4 (&S)[MTK][NVT],
                                                    f32x4 (&Y)[4][NVT], f32x4 (&Ob)[4][NVT],
                                                    void* out,
                                                    size_t row_base, int H, int h, int clen,
-                                                   int lo = 0) {
+                                                   int lo, const Raw& nxt, bool next_norms) {
     const int w = threadIdx.x >> 6, l = lane_fresh();
     const LDS T* QG = (const LDS T*)(smem + Cfg::OFF_QG);
     const LDS T* KG = (const LDS T*)(smem + Cfg::OFF_KG);
@@ -1213,6 +1215,10 @@ struct ChunkKernel {
         }
       }
     }
+    // The next chunk's q and k have arrived by now (loaded before the last
+    // barrier); their norm partials go to LDS here, where no wave reads them
+    // any more, and are visible to the next prep after the barrier below.
+    if (Cfg::FU && next_norms) norm_partials(nxt, smem);
     // Once the staged tile is complete all of the chunk's LDS reads are done:
     // after this barrier only the copy below reads LDS, and the next chunk's
     // prep writes nothing it reads, so no barrier separates the two.
@@ -1416,6 +1422,8 @@ struct ChunkKernel {
     const Offsets offs = lane_offsets(H);
     Raw raw;
     if (len > 0) load_raw<LOAD_ALL>(raw, offs, q, k, v, g, beta, row_base, H, h, len < C ? len : C);
+    const bool l2n = Cfg::FU && (pro.flags & PRO_L2NORM);
+    bool norms_ready = false;   // this chunk's norm partials are in LDS already
     for (int c0 = 0; c0 < len; c0 += C) {
       const int clen = (len - c0) < C ? (len - c0) : C;
       // the next chunk's loads are issued on every step, with an empty range
@@ -1424,11 +1432,14 @@ struct ChunkKernel {
       const bool more = c0 + C < len;
       const int nlen = !more ? 0 : ((len - c0 - C) < C ? (len - c0 - C) : C);
       const size_t next = more ? row_base + c0 + C : row_base;
-      if (Cfg::FU && (pro.flags & PRO_L2NORM)) {
-        // the chunk's norms need every wave's channels: one more barrier
+      if (l2n && !norms_ready) {
+        // the chunk's norms need every wave's channels: one more barrier (the
+        // first chunk, and after a guard-path chunk; otherwise the previous
+        // chunk step wrote them)
         norm_partials(raw, smem);
         __syncthreads();
       }
+      norms_ready = false;
       const int bad = prep(raw, smem, scale, pro, ea, 0, clen);
       // the vote runs in every lane: inside the lane-0 branch it would only
       // see lane 0's flag (the scan path sets it in other lanes)
@@ -1452,7 +1463,8 @@ struct ChunkKernel {
         compiler_fence();
         load_raw<LOAD_Q | LOAD_K>(raw, offs, q, k, v, g, beta, next, H, h, nlen);
         __syncthreads();                                         // B2
-        scan_step(smem, S, Y, O, out, row_base + c0, H, h, clen);
+        scan_step(smem, S, Y, O, out, row_base + c0, H, h, clen, 0, raw, l2n);
+        norms_ready = l2n;
       } else {
         // Some channel decays by more than 2^100 over the chunk, beyond what
         // one reference point (the chunk start) can scale: redo the chunk as
@@ -1483,7 +1495,7 @@ struct ChunkKernel {
             f32x4 Y[4][NVT], O[4][NVT];
             middle(smem, S, Y, O);
             __syncthreads();
-            scan_step(smem, S, Y, O, out, row_base + c0, H, h, hi, lo);
+            scan_step(smem, S, Y, O, out, row_base + c0, H, h, hi, lo, rw, false);
           } else {
             recurrent_chunk(S, q, k, v, g, beta, out, row_base + c0 + lo, H, h, hi - lo, scale,
                             pro, ea);

@@ -104,6 +104,18 @@ def test_backward_without_dS0_output():
     compare(got, run_oracle(d), "backward no dS0")
 
 
+def test_backward_without_tokens_passes_dS_final_through():
+    """T = 0: no gradient rows, and dS0 = dS_final (zeros without one)."""
+    note("backward T=0")
+    for with_dSf in (True, False):
+        d = inputs.prefill_inputs(2, 0, 3, 64, 128, io="bf16", seed=1, with_S0=True, device=DEV)
+        inputs.grad_inputs(d, seed=1, with_dS_final=with_dSf, device=DEV)
+        got = run_gpu(d)
+        assert got["dq"].shape == (2, 0, 3, 64) and got["dbeta"].shape == (2, 0, 3)
+        want = d["dS_final"].cpu().numpy() if with_dSf else np.zeros((2, 3, 64, 128), np.float32)
+        np.testing.assert_array_equal(got["dS0"], want)
+
+
 def test_backward_strong_decay():
     """log alpha down to -20 per channel: no division by the decay anywhere,
     so gradients stay exact where the states vanish."""
