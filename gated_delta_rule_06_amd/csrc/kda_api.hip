@@ -249,6 +249,7 @@ int backward_impl(const void* q, const void* k, const void* v, const float* log_
   const bool packed = cu_seqlens != nullptr;
   const size_t rows = packed ? (size_t)T : (size_t)n_seq * T;
   if (rows > 0x7fffffffu) return KDA_ERR_DIM;
+  if ((size_t)n_seq * H > 0x7fffffffu) return KDA_ERR_DIM;   // one workgroup per chain
   if (rows > 0 && (!q || !k || !v || !log_alpha || !beta || !d_out || !dq || !dk || !dv || !dg ||
                    !dbeta))
     return KDA_ERR_NULL;
