@@ -18,6 +18,8 @@
 // Sums over key rows (p, de) stay inside a 16-lane DPP row; sums over value
 // columns (dq, dk, dg, dbeta) take two lane shuffles inside the wave and then
 // one LDS slot per wave, added over the waves once per block of BK tokens.
+// dq = scale S_t do_t needs only the forward state, so the forward sweep forms
+// it; the reverse sweep, which is short of registers, does the rest.
 //
 // The backward needs the forward states in reverse order.  A forward sweep
 // stores the state at the start of every block of BK = 8 tokens to the
@@ -80,7 +82,7 @@ struct Bwd {
   // registers, written to a staging buffer once the buffer is free.  Rows
   // past the block's length read as zeros.  Gated DeltaNet gates are copied to
   // every key row.  REV: the reverse sweep's set (q, k, g, v - p from the
-  // workspace, do, beta); otherwise the forward sweep's (k, g, v, beta).
+  // workspace, do, beta); otherwise the forward sweep's (k, g, v, do, beta).
   struct Stage {
     float q[NQ], k[NQ], g[NQ], v[NV], d[NV], b;
   };
@@ -107,7 +109,7 @@ struct Bwd {
       const size_t e = ((tok0 + j) * H + h) * (size_t)DV + c;
       const bool ok = i < BK * DV && j < L;
       st.v[s] = ok ? (REV ? vp[e] : Io::load(v, e)) : 0.f;
-      st.d[s] = (REV && ok) ? Io::load(dout, e) : 0.f;
+      st.d[s] = ok ? Io::load(dout, e) : 0.f;
     }
     st.b = (int)threadIdx.x < L ? beta[(tok0 + threadIdx.x) * H + h] : 0.f;
   }
@@ -141,10 +143,20 @@ struct Bwd {
     }
   }
 
-  // Forward sweep, token j of the staged block: the full step on S, and
-  // v - p of the lane's columns to `vp_out` (one lane per column quad).
+  // Sum over the four column quads of the wave (lanes l, l^16, l^32, l^48).
+  static __device__ __forceinline__ float quad_sum(float x) {
+    x += __shfl_xor(x, 16);
+    x += __shfl_xor(x, 32);
+    return x;
+  }
+
+  // Forward sweep, token j of the staged block: the full step on S; v - p of
+  // the lane's columns to `vp_out` (one lane per column quad); and the wave's
+  // part of dq_j = scale S_j do_j (S_j after the write: the read of the forward
+  // needs no backward quantity) to `red_j`.
   static __device__ __forceinline__ void fwd_step(f32x4 (&S)[RPT], const float* in, int j,
-                                                  float* vp_out, const Lane& ln) {
+                                                  float* vp_out, float* red_j, float scale,
+                                                  const Lane& ln) {
     float kr[RPT], gr[RPT];
     rows(in + Cfg::IN_K + j * DK + RPT * ln.rg, kr);
     rows(in + Cfg::IN_G + j * DK + RPT * ln.rg, gr);
@@ -163,6 +175,22 @@ struct Bwd {
     const f32x4 e = b * vp;
 #pragma unroll
     for (int r = 0; r < RPT; ++r) S[r] += kr[r] * e;
+    const f32x4 dov = *reinterpret_cast<const f32x4*>(in + Cfg::IN_DO + j * DV + ln.c0);
+    float dqp[RPT];
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) {
+      float t = S[r][0] * dov[0];
+      t = __builtin_fmaf(S[r][1], dov[1], t);
+      t = __builtin_fmaf(S[r][2], dov[2], t);
+      t = __builtin_fmaf(S[r][3], dov[3], t);
+      dqp[r] = scale * quad_sum(t);
+    }
+    if (ln.cq == 0) {
+      float* rj = red_j + ln.w * DK + RPT * ln.rg;
+#pragma unroll
+      for (int r = 0; r < RPT; r += 4)
+        *reinterpret_cast<f32x4*>(rj + r) = f32x4{dqp[r], dqp[r + 1], dqp[r + 2], dqp[r + 3]};
+    }
   }
 
   // Reverse sweep, recomputing: the step of token j from the stored v - p
@@ -177,16 +205,11 @@ struct Bwd {
     for (int r = 0; r < RPT; ++r) S[r] = S[r] * gr[r] + kr[r] * e;
   }
 
-  // Sum over the four column quads of the wave (lanes l, l^16, l^32, l^48).
-  static __device__ __forceinline__ float quad_sum(float x) {
-    x += __shfl_xor(x, 16);
-    x += __shfl_xor(x, 32);
-    return x;
-  }
 
   // Token j of the staged block, from its previous state Sp: the backward
-  // step on dS.  Per-wave partials of dq, dk, dg go to red[j], of dbeta (and
-  // the Gated DeltaNet dg) to rs[j]; dv is final and goes straight out.
+  // step on dS.  Per-wave partials of dk, dg go to red[j], of dbeta (and the
+  // Gated DeltaNet dg) to rs[j]; dv is final and goes straight out.  (dq came
+  // from the forward sweep.)
   static __device__ __forceinline__ void bwd_step(const f32x4 (&Sp)[RPT], f32x4 (&dS)[RPT],
                                                   const float* in, int j, float* red, float* rs,
                                                   float* dv_out, float scale, const Lane& ln) {
@@ -198,21 +221,11 @@ struct Bwd {
     const f32x4 dov = *reinterpret_cast<const f32x4*>(in + Cfg::IN_DO + j * DV + ln.c0);
     const float b = in[Cfg::IN_B + j];
     const f32x4 e = b * vp;
-    // the read o = scale S_j^T q with S_j = Sbar + k e^T: dq = scale (Sbar do +
-    // k (e . do)), and dS += scale q do^T
-    const float edo = e[0] * dov[0] + e[1] * dov[1] + e[2] * dov[2] + e[3] * dov[3];
-    // Sbar = Diag(alpha) Sp is formed where it is used (registers are short)
+    // the read o = scale S_j^T q: dS += scale q do^T
     const float (&a)[RPT] = gr;
-    float dqp[RPT];
     f32x4 de = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int r = 0; r < RPT; ++r) {
-      const f32x4 Sb = Sp[r] * a[r];
-      float x = kr[r] * edo;
-      x = __builtin_fmaf(Sb[0], dov[0], x);
-      x = __builtin_fmaf(Sb[1], dov[1], x);
-      x = __builtin_fmaf(Sb[2], dov[2], x);
-      dqp[r] = __builtin_fmaf(Sb[3], dov[3], x);
       dS[r] += (scale * qr[r]) * dov;
       de += dS[r] * kr[r];
     }
@@ -224,7 +237,7 @@ struct Bwd {
     float dkp[RPT], dgp[RPT];
 #pragma unroll
     for (int r = 0; r < RPT; ++r) {
-      const f32x4 Sb = Sp[r] * a[r];
+      const f32x4 Sb = Sp[r] * a[r];   // Sbar = Diag(alpha) Sp
       float x = dS[r][0] * e[0];
       x = __builtin_fmaf(dS[r][1], e[1], x);
       x = __builtin_fmaf(dS[r][2], e[2], x);
@@ -245,7 +258,6 @@ struct Bwd {
     // sums over the wave's 16 columns
 #pragma unroll
     for (int r = 0; r < RPT; ++r) {
-      dqp[r] = scale * quad_sum(dqp[r]);
       dkp[r] = quad_sum(dkp[r]);
       dgp[r] = quad_sum(dgp[r]);
     }
@@ -254,7 +266,6 @@ struct Bwd {
     if (ln.cq == 0) {
 #pragma unroll
       for (int r = 0; r < RPT; r += 4) {
-        *reinterpret_cast<f32x4*>(rj + r) = f32x4{dqp[r], dqp[r + 1], dqp[r + 2], dqp[r + 3]};
         *reinterpret_cast<f32x4*>(rj + NW * DK + r) =
             f32x4{dkp[r], dkp[r + 1], dkp[r + 2], dkp[r + 3]};
         if (!Cfg::SG)
@@ -274,18 +285,31 @@ struct Bwd {
     if (ln.l == 0) sj[0] = dbp;
   }
 
-  // Sums over the waves of one block's partials, to dq, dk, dg, dbeta.
+  // Sums over the waves of one block's dq partials (slot `slot` of red).
+  static __device__ void write_dq(const float* red, int slot, size_t tok0, int L, int H, int h,
+                                  float* dq) {
+    for (int i = threadIdx.x; i < L * DK; i += NT) {
+      const int j = i / DK, row = i - j * DK;
+      const float* src = red + (j * 3 + slot) * NW * DK + row;
+      float s = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) s += src[w * DK];
+      dq[((tok0 + j) * H + h) * (size_t)DK + row] = s;
+    }
+  }
+
+  // Sums over the waves of one block's partials, to dk, dg (slots 1, 2), dbeta.
   static __device__ void write_out(const float* red, const float* rs, size_t tok0, int L, int H,
-                                   int h, float* dq, float* dk, float* dg, float* dbeta) {
-    for (int i = threadIdx.x; i < L * 3 * DK; i += NT) {
-      const int j = i / (3 * DK), rem = i - j * 3 * DK;
-      const int qty = rem / DK, row = rem - qty * DK;
+                                   int h, float* dk, float* dg, float* dbeta) {
+    for (int i = threadIdx.x; i < L * 2 * DK; i += NT) {
+      const int j = i / (2 * DK), rem = i - j * 2 * DK;
+      const int qty = 1 + rem / DK, row = rem - (qty - 1) * DK;
       if (Cfg::SG && qty == 2) continue;
       const float* src = red + (j * 3 + qty) * NW * DK + row;
       float s = 0.f;
 #pragma unroll
       for (int w = 0; w < NW; ++w) s += src[w * DK];
-      float* dst = qty == 0 ? dq : (qty == 1 ? dk : dg);
+      float* dst = qty == 1 ? dk : dg;
       dst[((tok0 + j) * H + h) * (size_t)DK + row] = s;
     }
     if ((int)threadIdx.x < L) {
@@ -345,6 +369,8 @@ __global__ __launch_bounds__(Cfg::NT) void kda_bwd_kernel(
   };
   auto in_buf = [&](int m) { return lds + Cfg::OFF_IN + (m & 1) * Cfg::IN_SZ; };
   const size_t sbase = (size_t)nh * DK * DV + (size_t)(RPT * ln.rg) * DV + ln.c0;
+  float* red = lds + Cfg::OFF_RED;
+  float* rs = lds + Cfg::OFF_RS;
   Stage st;
 
   // forward sweep: checkpoint at the start of every block, v - p per token;
@@ -369,11 +395,15 @@ __global__ __launch_bounds__(Cfg::NT) void kda_bwd_kernel(
 #pragma unroll
     for (int r = 0; r < RPT; ++r) *ck_at(m, r) = S[r];
     __syncthreads();
+    // dq of the previous block (its partials in slot (m - 1) & 1; this block
+    // writes the other slot, and the next barrier separates the two uses)
+    if (m > 0) K::write_dq(red, (m - 1) & 1, tok0 - BK, BK, H, h, dq);
     if (m + 2 < nb)
       K::template stage_load<false>(later, q, k, v, g, beta, dout, vp, tok0 + 2 * BK, blen(m + 2),
                                     H, h);
     for (int j = 0; j < L; ++j)
-      K::fwd_step(S, in, j, vp + ((tok0 + j) * H + h) * (size_t)DV, ln);
+      K::fwd_step(S, in, j, vp + ((tok0 + j) * H + h) * (size_t)DV,
+                  red + (j * 3 + (m & 1)) * Cfg::NW * DK, scale, ln);
     if (m + 1 < nb) K::stage_store(next, in_buf(m + 1));
   };
   for (int m = 0; m < nb; m += 2) {
@@ -381,6 +411,7 @@ __global__ __launch_bounds__(Cfg::NT) void kda_bwd_kernel(
     if (m + 1 < nb) fwd_block(m + 1, st, sa);
   }
   __syncthreads();   // the forward sweep's staging reads and vp writes are done
+  if (nb > 0) K::write_dq(red, (nb - 1) & 1, t0 + (size_t)(nb - 1) * BK, blen(nb - 1), H, h, dq);
 
   // reverse sweep
   f32x4 dS[RPT], Sc[RPT];
@@ -395,15 +426,13 @@ __global__ __launch_bounds__(Cfg::NT) void kda_bwd_kernel(
     for (int r = 0; r < RPT; ++r) Sc[r] = *ck_at(nb - 1, r);
     K::stage_store(st, in_buf(nb - 1));
   }
-  float* red = lds + Cfg::OFF_RED;
-  float* rs = lds + Cfg::OFF_RS;
   for (int m = nb - 1; m >= 0; --m) {
     const int L = blen(m);
     const size_t tok0 = t0 + (size_t)m * BK;
     float* in = in_buf(m);
     __syncthreads();   // this block's inputs are staged; the partials hold block m + 1's
     if (m + 1 < nb) {
-      K::write_out(red, rs, tok0 + BK, blen(m + 1), H, h, dq, dk, dg, dbeta);
+      K::write_out(red, rs, tok0 + BK, blen(m + 1), H, h, dk, dg, dbeta);
       __syncthreads();   // the partials are free again
     }
     auto dvp = [&](int j) { return dv + ((tok0 + j) * H + h) * (size_t)DV; };
@@ -452,7 +481,7 @@ __global__ __launch_bounds__(Cfg::NT) void kda_bwd_kernel(
     }
   }
   __syncthreads();
-  if (nb > 0) K::write_out(red, rs, t0, blen(0), H, h, dq, dk, dg, dbeta);
+  if (nb > 0) K::write_out(red, rs, t0, blen(0), H, h, dk, dg, dbeta);
   if (dS0) {
 #pragma unroll
     for (int r = 0; r < RPT; ++r) *reinterpret_cast<f32x4*>(dS0 + sbase + (size_t)r * DV) = dS[r];
