@@ -393,7 +393,7 @@ __global__ __launch_bounds__(Cfg::NT) void kda_bwd_kernel(
     const size_t tok0 = t0 + (size_t)m * BK;
     float* in = in_buf(m);
 #pragma unroll
-    for (int r = 0; r < RPT; ++r) *ck_at(m, r) = S[r];
+    for (int r = 0; r < RPT; ++r) __builtin_nontemporal_store(S[r], ck_at(m, r));
     __syncthreads();
     // dq of the previous block (its partials in slot (m - 1) & 1; this block
     // writes the other slot, and the next barrier separates the two uses)
@@ -423,7 +423,7 @@ __global__ __launch_bounds__(Cfg::NT) void kda_bwd_kernel(
     K::template stage_load<true>(st, q, k, v, g, beta, dout, vp, t0 + (size_t)(nb - 1) * BK,
                                  blen(nb - 1), H, h);
 #pragma unroll
-    for (int r = 0; r < RPT; ++r) Sc[r] = *ck_at(nb - 1, r);
+    for (int r = 0; r < RPT; ++r) Sc[r] = __builtin_nontemporal_load(ck_at(nb - 1, r));
     K::stage_store(st, in_buf(nb - 1));
   }
   for (int m = nb - 1; m >= 0; --m) {
@@ -470,7 +470,7 @@ __global__ __launch_bounds__(Cfg::NT) void kda_bwd_kernel(
     if (m > 0) {
       K::template stage_load<true>(st, q, k, v, g, beta, dout, vp, tok0 - BK, BK, H, h);
 #pragma unroll
-      for (int r = 0; r < RPT; ++r) Sn[r] = *ck_at(m - 1, r);
+      for (int r = 0; r < RPT; ++r) Sn[r] = __builtin_nontemporal_load(ck_at(m - 1, r));
     }
     if (L >= 2) K::bwd_step(S1, dS, in, 1, red, rs, dvp(1), scale, ln);
     K::bwd_step(Sc, dS, in, 0, red, rs, dvp(0), scale, ln);
