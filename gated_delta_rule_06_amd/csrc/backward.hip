@@ -108,7 +108,7 @@ struct Bwd {
       const int j = i / DV, c = i - j * DV;
       const size_t e = ((tok0 + j) * H + h) * (size_t)DV + c;
       const bool ok = i < BK * DV && j < L;
-      st.v[s] = ok ? (REV ? vp[e] : Io::load(v, e)) : 0.f;
+      st.v[s] = ok ? (REV ? __builtin_nontemporal_load(vp + e) : Io::load(v, e)) : 0.f;
       st.d[s] = ok ? Io::load(dout, e) : 0.f;
     }
     st.b = (int)threadIdx.x < L ? beta[(tok0 + threadIdx.x) * H + h] : 0.f;
@@ -171,7 +171,7 @@ struct Bwd {
     f32x4 vp;
 #pragma unroll
     for (int c = 0; c < 4; ++c) vp[c] = vv[c] - row_sum16(p[c]);
-    if (ln.rg == 0) *reinterpret_cast<f32x4*>(vp_out + ln.c0) = vp;
+    if (ln.rg == 0) __builtin_nontemporal_store(vp, reinterpret_cast<f32x4*>(vp_out + ln.c0));
     const f32x4 e = b * vp;
 #pragma unroll
     for (int r = 0; r < RPT; ++r) S[r] += kr[r] * e;
@@ -254,7 +254,7 @@ struct Bwd {
       dS[r] = dSb * a[r];
     }
     // dv: final, one lane per column quad
-    if (ln.rg == 0) *reinterpret_cast<f32x4*>(dv_out + ln.c0) = b * de;
+    if (ln.rg == 0) __builtin_nontemporal_store(b * de, reinterpret_cast<f32x4*>(dv_out + ln.c0));
     // sums over the wave's 16 columns
 #pragma unroll
     for (int r = 0; r < RPT; ++r) {
@@ -294,7 +294,7 @@ struct Bwd {
       float s = 0.f;
 #pragma unroll
       for (int w = 0; w < NW; ++w) s += src[w * DK];
-      dq[((tok0 + j) * H + h) * (size_t)DK + row] = s;
+      __builtin_nontemporal_store(s, dq + ((tok0 + j) * H + h) * (size_t)DK + row);
     }
   }
 
@@ -310,7 +310,7 @@ struct Bwd {
 #pragma unroll
       for (int w = 0; w < NW; ++w) s += src[w * DK];
       float* dst = qty == 1 ? dk : dg;
-      dst[((tok0 + j) * H + h) * (size_t)DK + row] = s;
+      __builtin_nontemporal_store(s, dst + ((tok0 + j) * H + h) * (size_t)DK + row);
     }
     if ((int)threadIdx.x < L) {
       const int j = threadIdx.x;
