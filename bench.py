@@ -132,9 +132,8 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        msg = ("bench.py measures one GPU only: this build runs the KDA forward on a single "
-               "MI355X (how the path would shard is described in DESIGN.md); got --gpus %d, "
-               "WORLD_SIZE %d" % (args.gpus, world))
+        msg = ("bench.py measures one GPU only: the KDA library runs on a single MI355X, "
+               "and no multi-GPU path exists; got --gpus %d, WORLD_SIZE %d" % (args.gpus, world))
         print(msg, file=sys.stderr)
         sys.exit(2)
 

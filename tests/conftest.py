@@ -14,7 +14,7 @@ def pytest_configure(config):
 
 def pytest_collection_modifyitems(config, items):
     # GPU tests are skipped (not failed) when no GPU is visible, so that a plain
-    # `pytest` here still runs the CPU suite; `-m gpu` on the GPU machine runs them.
+    # `pytest` without a GPU still runs the CPU suite; `-m gpu` on an MI355X runs them.
     try:
         import torch
         have_gpu = torch.cuda.is_available()
