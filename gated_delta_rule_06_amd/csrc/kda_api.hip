@@ -105,7 +105,7 @@ int check_prologue(const kda_prologue* pro, int H, int d_k, bool sg, kda::Prolog
 }
 
 // Shared validation of the calls over token sequences (prefill and
-// recurrent); `supported` is the caller's verdict on d_k, d_v, chunk, io_dtype.
+// recurrent); `supported` is the caller's check of d_k, d_v, chunk and io_dtype.
 int check_tokens(const void* q, const void* k, const void* v, const float* log_alpha,
                  const float* beta, const float* S0, void* out, float* S_final,
                  const int32_t* cu, size_t rows, int n_seq, int H, int d_k, int d_v,
