@@ -401,9 +401,19 @@ __global__ __launch_bounds__(Cfg::NT) void kda_bwd_kernel(
     if (m + 2 < nb)
       K::template stage_load<false>(later, q, k, v, g, beta, dout, vp, tok0 + 2 * BK, blen(m + 2),
                                     H, h);
-    for (int j = 0; j < L; ++j)
+    auto step = [&](int j) {
       K::fwd_step(S, in, j, vp + ((tok0 + j) * H + h) * (size_t)DV,
                   red + (j * 3 + (m & 1)) * Cfg::NW * DK, scale, ln);
+    };
+    if (L == BK) {
+      // a full block, written out so that one token's dq tail (lane swaps
+      // and LDS writes, off the state's dependency chain) overlaps the next
+      // token's step
+#pragma unroll
+      for (int j = 0; j < BK; ++j) step(j);
+    } else {
+      for (int j = 0; j < L; ++j) step(j);
+    }
     if (m + 1 < nb) K::stage_store(next, in_buf(m + 1));
   };
   for (int m = 0; m < nb; m += 2) {
