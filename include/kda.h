@@ -1,5 +1,8 @@
 /*
- * kda.h -- C ABI of the MI355X (gfx950) Kimi Delta Attention forward library.
+ * kda.h -- C ABI of the MI355X (gfx950) Kimi Delta Attention library: the
+ * forward (prefill, packed prefill, decode, multi-token recurrence, each also
+ * for Gated DeltaNet gates and with optional in-kernel input transforms) and
+ * its backward (kda_backward).
  *
  * The operation (one head; S is d_k x d_v, row = key channel, column = value
  * channel; g = log alpha with natural log, g <= 0):
@@ -32,9 +35,9 @@
  *    overlap between an output and another argument is not.
  *  - Supported sizes: d_k and d_v in {64, 128}; chunk == 64.  The two
  *    prefill calls take KDA_IO_F32 only with d_k == d_v == 64 (their fp32
- *    operand tiles do not fit in LDS otherwise); decode and the recurrent
- *    calls take both types at every supported size.  Anything else returns
- *    KDA_ERR_UNSUPPORTED.
+ *    operand tiles do not fit in LDS otherwise); decode, the recurrent calls
+ *    and the backward take both types at every supported size.  Anything
+ *    else returns KDA_ERR_UNSUPPORTED.
  *  - Errors: every argument is validated before any work is enqueued; on a
  *    validation error nothing is enqueued and a negative KDA_ERR_* code is
  *    returned.  KDA_ERR_HIP reports a launch failure (hipGetLastError).
