@@ -64,6 +64,7 @@ struct BwdCfg {
   static constexpr int OFF_RS = OFF_RED + RED_SZ;
   static constexpr int LDS_FLOATS = OFF_RS + RS_SZ;
   static_assert(LDS_FLOATS * 4 <= 160 * 1024, "LDS budget");
+  static_assert(LDS_FLOATS >= KDA_LPT_MAX + 1, "LDS holds the length ranking");
 };
 
 // Lane coordinates: wave w, row group rg (rows RPT*rg + r), column quad cq
@@ -342,7 +343,28 @@ __global__ __launch_bounds__(Cfg::NT) void kda_bwd_kernel(
   typedef typename K::Stage Stage;
   constexpr int DK = Cfg::DK, DV = Cfg::DV, RPT = Cfg::RPT;
   extern __shared__ __attribute__((aligned(16))) float lds[];
-  const int nh = blockIdx.x, n = nh / H, h = nh - n * H;
+  // Packed sequences: workgroup b takes head b % H of the (b / H)-th longest
+  // sequence (ties by index; each workgroup ranks the lengths itself in LDS,
+  // up to KDA_LPT_MAX sequences), so that long chains start first.
+  const int h = blockIdx.x % H;
+  int n = blockIdx.x / H;
+  if (cu && (int)(gridDim.x / H) <= KDA_LPT_MAX) {
+    const int N = gridDim.x / H;
+    int* lens = reinterpret_cast<int*>(lds);
+    int* sel = lens + KDA_LPT_MAX;
+    for (int m = threadIdx.x; m < N; m += Cfg::NT) lens[m] = cu[m + 1] - cu[m];
+    __syncthreads();
+    for (int m = threadIdx.x; m < N; m += Cfg::NT) {
+      const int lm = lens[m];
+      int rank = 0;
+      for (int j = 0; j < N; ++j) rank += (lens[j] > lm) || (lens[j] == lm && j < m);
+      if (rank == n) *sel = m;
+    }
+    __syncthreads();
+    n = *sel;
+    __syncthreads();   // the LDS is the kernel's from here on
+  }
+  const int nh = n * H + h;
   Lane ln;
   ln.w = threadIdx.x >> 6;
   ln.l = threadIdx.x & 63;

@@ -48,9 +48,6 @@
 //    on the same on-chip state instead; outputs are identical up to rounding.
 #include "common.h"
 
-// Packed sequences up to this count are started longest first.
-#define KDA_LPT_MAX 256
-
 namespace kda {
 
 // ============================================================ lane shifts

@@ -4,6 +4,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+// Packed sequences up to this count are started longest first.
+#define KDA_LPT_MAX 256
+
 namespace kda {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
