@@ -95,7 +95,13 @@ __global__ __launch_bounds__(256) void recurrent_fwd_kernel(
   constexpr int CW = 64;                 // value columns per workgroup
   constexpr int NSL = DV / CW;
   constexpr int RPT = DK / 16;           // key rows per lane
-  constexpr int LDX = CW + 4;            // LDS row stride of the state slice (floats)
+  // LDS tile of the state slice: rows of CW floats with no padding (32 KB at
+  // d_k = 128, so five workgroups fit a CU); the 16-byte slots of a row are
+  // XOR-swizzled by the row's lane group (row / RPT), which keeps both the
+  // row-wise copies (16 threads per row) and the compute layout's reads (16
+  // lanes, one row group each) free of bank conflicts.
+  constexpr int LDX = CW;
+  constexpr int RSH = RPT == 8 ? 3 : 2;  // log2(RPT)
   static_assert(DV % CW == 0 && DK % 16 == 0, "shape");
 
   const int slice = blockIdx.x % NSL;
@@ -120,13 +126,14 @@ __global__ __launch_bounds__(256) void recurrent_fwd_kernel(
   __shared__ __attribute__((aligned(16))) float X[DK * LDX];
   const float* Sg0 = S0 + (size_t)nh * DK * DV + slice * CW;
   const int c4 = 4 * (threadIdx.x & 15), r16 = threadIdx.x >> 4;
-  float* xl = X + row0 * LDX + w * 16 + 4 * cg;     // this lane's rows in the compute layout
+  auto xs = [](int row, int col) { return row * LDX + (((col >> 2) ^ ((row >> RSH) & 15)) << 2); };
+  float* xl = X + xs(row0, w * 16 + 4 * cg);        // this lane's rows in the compute layout
   f32x4 st[RPT];
   if (S0) {
 #pragma unroll
     for (int j = 0; j < DK / 16; ++j) {
       const int row = r16 + 16 * j;
-      *reinterpret_cast<f32x4*>(X + row * LDX + c4) =
+      *reinterpret_cast<f32x4*>(X + xs(row, c4)) =
           __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Sg0 + (size_t)row * DV + c4));
     }
     __syncthreads();
@@ -232,7 +239,7 @@ __global__ __launch_bounds__(256) void recurrent_fwd_kernel(
 #pragma unroll
     for (int j = 0; j < DK / 16; ++j) {
       const int row = r16 + 16 * j;
-      __builtin_nontemporal_store(*reinterpret_cast<const f32x4*>(X + row * LDX + c4),
+      __builtin_nontemporal_store(*reinterpret_cast<const f32x4*>(X + xs(row, c4)),
                                   reinterpret_cast<f32x4*>(Sg1 + (size_t)row * DV + c4));
     }
   }
