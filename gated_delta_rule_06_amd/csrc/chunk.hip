@@ -391,9 +391,10 @@ struct ChunkCfg {
   // head's gate biases [DK]
   static constexpr int OFF_NM = OFF_FL + 64;
   static constexpr int SZ_NM = FU ? 2 * C * NW * 4 + DK * 4 : 0;
-  // SG only: per-token factors of the raw operands, C floats each (SV_*)
+  // SG only: per-token factors of the raw operands, C floats each (SV_*), and
+  // the log2 decay of each 16-token block (4 floats)
   static constexpr int OFF_SV = OFF_NM + SZ_NM;
-  static constexpr int SZ_SV = SG ? 7 * C * 4 : 0;
+  static constexpr int SZ_SV = SG ? (7 * C + 4) * 4 : 0;
   static constexpr int LDS_TOTAL = OFF_SV + SZ_SV;
   static_assert(LDS_TOTAL <= 160 * 1024, "LDS budget");
   static_assert(LDS_TOTAL >= (KDA_LPT_MAX + 1) * 4, "LDS holds the length ranking");
@@ -564,14 +565,19 @@ struct ChunkKernel {
   // factors of every product are per-token scalars, so the operands stay the
   // raw inputs: QG = q, KG = k, -KI = -k (and the key-major -k), -V, and the
   // scalars go to LDS, C floats each, for the epilogues of the products:
-  //   SV_G   gamma_i = log2 Gamma_i (prefix sum of log2 alpha over the chunk)
+  //   SV_G   gamma_i: prefix sum of log2 alpha from the start of token i's
+  //          16-token block (block-local, so differences of nearby tokens stay
+  //          exact to rounding however much the chunk decayed before them)
   //   SV_RQ  rq_i = scale / |q_i|      SV_RK  rk_i = 1 / |k_i|  (1 without the
   //                                    L2-norm transform)
   //   SV_BK  beta_i rk_i               SV_FY  beta_i Gamma_i rk_i   (Y)
   //   SV_FO  Gamma_i rq_i   (O)        SV_FS  rk_i Gamma_L / Gamma_i (S update)
+  //   SV_T   (4 floats) the total log2 decay of each 16-token block
   // Every factor is at most 1 in size (for log alpha <= 0): no decay is too
-  // strong for this form, so there is no guard.
-  enum { SV_G = 0, SV_RQ = 1, SV_RK = 2, SV_BK = 3, SV_FY = 4, SV_FO = 5, SV_FS = 6 };
+  // strong for this form, so there is no guard.  Each exponent is formed from
+  // block-local sums and block totals, never as a difference of two prefix
+  // sums over the whole chunk.
+  enum { SV_G = 0, SV_RQ = 1, SV_RK = 2, SV_BK = 3, SV_FY = 4, SV_FO = 5, SV_FS = 6, SV_T = 7 };
   static __device__ __forceinline__ void prep_sg(const Raw& r, LDS char* smem, float scale,
                                                  const Prologue& pro, float ea, int lo, int hi) {
     const int w = threadIdx.x >> 6, l = lane_fresh();
@@ -590,9 +596,10 @@ struct ChunkKernel {
     constexpr float LOG2E = 1.4426950408889634f;
 
     // gamma of the lane's tokens: a running sum over its TPL tokens, an
-    // inclusive scan of the group sums over the lanes cq + CQ tg, then one
-    // group back.  Rows outside [lo, hi) keep log alpha = 0 under the gate
-    // transform (identity tokens).
+    // inclusive scan of the group sums over the lanes cq + CQ tg within each
+    // 16-token block (segments of GPB groups), then one group back.  Rows
+    // outside [lo, hi) keep log alpha = 0 under the gate transform (identity
+    // tokens).
     const bool xg = Cfg::FU && (pro.flags & PRO_GATE);
     const float gb = xg ? ((const LDS float*)(smem + Cfg::OFF_NM + 2 * C * NW * 4))[0] : 0.f;
     float gam[TPL];
@@ -602,19 +609,31 @@ struct ChunkKernel {
       const float la = xg ? (real ? gate_logalpha(r.gs[t], ea, gb) : 0.f) : r.gs[t];
       gam[t] = (t == 0 ? 0.f : gam[t - 1]) + la * LOG2E;
     }
+    constexpr int GPB = 16 / TPL;               // token groups per 16-token block
+    static_assert(16 % TPL == 0, "a lane's tokens stay in one block");
     float x = gam[TPL - 1];
 #pragma unroll
-    for (int d = CQ; d < 64; d <<= 1) {
-      const float y = __shfl_up(x, d);
-      if (l >= d) x += y;
+    for (int d = 1; d < GPB; d <<= 1) {
+      const float y = __shfl_up(x, CQ * d);
+      if (tg % GPB >= d) x += y;
     }
-    const float gam_l = __shfl(x, 63);
-    const float y = __shfl_up(x, CQ);
-    const float e0 = (l >= CQ) ? y : 0.f;
+    float tb[4];                                // block totals, in every lane
 #pragma unroll
-    for (int t = 0; t < TPL; ++t) gam[t] += e0;
+    for (int b = 0; b < 4; ++b) tb[b] = __shfl(x, CQ * (GPB * b + GPB - 1));
+    const float y = __shfl_up(x, CQ);
+    const float e0 = (tg % GPB) ? y : 0.f;
+#pragma unroll
+    for (int t = 0; t < TPL; ++t) gam[t] += e0;  // block-local gamma
+    const int blk = TPL * tg / 16;
+    float before = 0.f, after = 0.f;            // the blocks before / after the lane's
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      if (b < blk) before += tb[b];
+      if (b > blk) after += tb[b];
+    }
+    if (w == 0 && l < 4) SV[SV_T * C + l] = l == 0 ? tb[0] : l == 1 ? tb[1] : l == 2 ? tb[2] : tb[3];
     if (tg == 0) {
-      const float gl = exp2f(gam_l);
+      const float gl = exp2f((tb[0] + tb[1]) + (tb[2] + tb[3]));
       *lds_ptr<f32x4>(GL + kc0) = f32x4{gl, gl, gl, gl};
       *lds_ptr<f32x4>(GL + kc0 + 4) = f32x4{gl, gl, gl, gl};
     }
@@ -646,14 +665,14 @@ struct ChunkKernel {
         }
         const float bi = __shfl(beta, i);
         if (cq == 0) {
-          const float G = exp2f(gam[t]);
+          const float G = exp2f(before + gam[t]);
           SV[SV_G * C + i] = gam[t];
           SV[SV_RQ * C + i] = rq;
           SV[SV_RK * C + i] = rk;
           SV[SV_BK * C + i] = bi * rk;
           SV[SV_FY * C + i] = bi * G * rk;
           SV[SV_FO * C + i] = G * rq;
-          SV[SV_FS * C + i] = exp2f(gam_l - gam[t]) * rk;
+          SV[SV_FS * C + i] = exp2f((tb[blk] - gam[t]) + after) * rk;
         }
       }
     }
@@ -959,14 +978,18 @@ struct ChunkKernel {
           accA[r] = (g4 + r <= n) ? accA[r] * fa : 0.f;   // lower with diagonal
         }
       } else {
-        // i = 16I + n, j = 16J + g4 + r for both
+        // i = 16I + n, j = 16J + g4 + r for both; gamma_i - gamma_j = gi +
+        // (rest of block J after j) + (whole blocks between), all block-local
         const f32x4 gj = *lds_ptr<const f32x4>(SV + SV_G * C + 16 * J + g4);
         const f32x4 kj = *lds_ptr<const f32x4>(SV + SV_RK * C + 16 * J + g4);
         const float gi = SV[SV_G * C + 16 * I + n], bi = SV[SV_BK * C + 16 * I + n];
         const float qi = SV[SV_RQ * C + 16 * I + n];
+        const float tj = SV[SV_T * C + J];
+        float mid = 0.f;
+        for (int b = J + 1; b < I; ++b) mid += SV[SV_T * C + b];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float e = __builtin_amdgcn_exp2f(gi - gj[r]) * kj[r];
+          const float e = __builtin_amdgcn_exp2f(gi + ((tj - gj[r]) + mid)) * kj[r];
           accR[r] *= e * bi;
           accA[r] *= e * qi;
         }

@@ -48,12 +48,15 @@ def test_gdn_chunk_fwd_matches_oracle(B, T, H, dk, dv, io, with_S0):
     assert_close(go, gs, ro, rs, tol_for(io), "gdn chunk")
 
 
-@pytest.mark.parametrize("gate,io", [("-3", "bf16"), ("-30", "f32"), ("uniform", "f32")])
+@pytest.mark.parametrize("gate,io", [("-3", "bf16"), ("-30", "f32"), ("uniform", "f32"),
+                                     ("strong_then_weak", "f32")])
 def test_gdn_chunk_strong_decay_matches_oracle(gate, io):
     """Decays far beyond one chunk's range: log alpha = -3 or -30 for every token
-    (a chunk decays by e^-192 or e^-1920), or uniform in [-8, 0].  The scalar-gate
-    chunk step scales its products by per-token ratios Gamma_i / Gamma_j <= 1, so
-    it needs no guard; the results must still match."""
+    (a chunk decays by e^-192 or e^-1920), or uniform in [-8, 0], or -100 for the
+    first 32 tokens of each chunk and -0.01 for the rest (the later tokens' decay
+    ratios must not inherit the rounding of the large early sums).  The
+    scalar-gate chunk step scales its products by per-token ratios
+    Gamma_i / Gamma_j <= 1, so it needs no guard; the results must still match."""
     note("gdn chunk strong decay gate=%s io=%s" % (gate, io))
     dim = 128 if io == "bf16" else 64      # fp32 I/O runs d_k = d_v = 64
     d = inputs.prefill_inputs(1, 150, 2, dim, dim, io=io, seed=3, with_S0=True, device=DEV,
@@ -61,6 +64,10 @@ def test_gdn_chunk_strong_decay_matches_oracle(gate, io):
     if gate == "uniform":
         gen = torch.Generator().manual_seed(11)
         d["g"] = (-8.0 * torch.rand(d["g"].shape, generator=gen)).to(DEV)
+    elif gate == "strong_then_weak":
+        g = torch.full_like(d["g"], -0.01)
+        g[:, (torch.arange(g.shape[1], device=g.device) % 64) < 32] = -100.0
+        d["g"] = g.contiguous()
     else:
         d["g"] = torch.full_like(d["g"], float(gate))
     o, S = kda().chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], S0=d["S0"])
