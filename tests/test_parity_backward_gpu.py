@@ -65,6 +65,8 @@ def compare(got, ref, what, tol=TOL):
     (2, 10, 2, 128, 128, "bf16", True, True, "gdn"),
     (1, 4, 1, 64, 64, "f32", False, True, "gdn"),
     (1, 1, 2, 128, 128, "bf16", True, True, "kda"),
+    (2, 8, 2, 128, 128, "f32", True, True, "kda"),    # exactly one checkpoint block
+    (1, 16, 3, 128, 128, "bf16", False, True, "gdn"), # two full blocks
 ])
 def test_backward_matches_oracle(B, T, H, dk, dv, io, with_S0, with_dSf, gate):
     what = "backward B=%d T=%d H=%d dk=%d dv=%d io=%s S0=%s dSf=%s gate=%s" % (
