@@ -2,7 +2,8 @@
 
     python -m gated_delta_rule_06_amd.build
 
-compiles every ``csrc/*.hip`` with hipcc into ``gated_delta_rule_06_amd/libkda.so``.
+compiles every ``csrc/*.hip`` with hipcc (one object per source under
+``_build/kda``, in parallel) and links them into ``gated_delta_rule_06_amd/libkda.so``.
 """
 from __future__ import annotations
 
@@ -35,23 +36,46 @@ def sources():
     return sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip")))
 
 
-def build(verbose: bool = False, extra_flags=None) -> str:
-    """Compile all HIP sources into libkda.so (always recompiles)."""
-    srcs = sources()
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc(), *HIPCC_FLAGS, *(extra_flags or []), "-I", os.path.join(ROOT, "include"),
-           "-I", os.path.join(PKG, "csrc"), "-o", tmp, *srcs]
-    if verbose:
-        print(" ".join(cmd), flush=True)
+def _run(cmd):
     res = subprocess.run(cmd, capture_output=True, text=True)
     # hipcc's host pass warns that it does not know the packed-fp32 feature
     err = "\n".join(x for x in res.stderr.splitlines() if "packed-fp32-ops" not in x)
-    if res.returncode != 0:
+    return res.returncode, err
+
+
+def build(verbose: bool = False, extra_flags=None) -> str:
+    """Compile all HIP sources into libkda.so (always recompiles): one object
+    per source, compiled in parallel, then one link."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    srcs = sources()
+    objdir = os.path.join(ROOT, "_build", "kda")
+    os.makedirs(objdir, exist_ok=True)
+    inc = ["-I", os.path.join(ROOT, "include"), "-I", os.path.join(PKG, "csrc")]
+    cflags = [f for f in HIPCC_FLAGS if f != "-shared"] + list(extra_flags or [])
+    objs = [os.path.join(objdir, os.path.basename(s)[:-4] + ".o") for s in srcs]
+    cmds = [[hipcc(), *cflags, *inc, "-c", "-o", o, s] for s, o in zip(srcs, objs)]
+    if verbose:
+        for c in cmds:
+            print(" ".join(c), flush=True)
+    jobs = max(1, min(len(cmds), int(os.environ.get("MAX_JOBS", "0") or 0) or (os.cpu_count() or 1)))
+    with ThreadPoolExecutor(jobs) as ex:
+        results = list(ex.map(_run, cmds))
+    errs = [e for rc, e in results if rc != 0]
+    if errs:
+        raise RuntimeError("hipcc failed:\n" + "\n".join(errs))
+    tmp = LIB + ".tmp%d" % os.getpid()
+    link = [hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp, *objs]
+    if verbose:
+        print(" ".join(link), flush=True)
+    rc, err = _run(link)
+    if rc != 0:
         if os.path.exists(tmp):
             os.remove(tmp)
-        raise RuntimeError("hipcc failed:\n" + err)
-    if verbose and err.strip():
-        print(err, file=sys.stderr)
+        raise RuntimeError("hipcc link failed:\n" + err)
+    for _, e in results:
+        if verbose and e.strip():
+            print(e, file=sys.stderr)
     os.replace(tmp, LIB)
     return LIB
 

@@ -97,6 +97,23 @@ def test_backward_varlen_matches_oracle(lens, io, gate):
             np.testing.assert_array_equal(got["dS0"][n], d["dS_final"][n].cpu().numpy())
 
 
+def test_backward_varlen_many_sequences_packed_order():
+    """More packed sequences than the length ranking covers (300 > 256): the
+    backward then takes them in packed order; every gradient of every chain
+    is checked, empty sequences included."""
+    rng = np.random.default_rng(301)
+    lens = rng.integers(0, 24, size=300)
+    lens[[0, 100, 299]] = [0, 1, 40]
+    what = "backward varlen 300 sequences total=%d" % int(lens.sum())
+    note(what)
+    d = inputs.varlen_inputs(lens, 2, 64, 64, io="bf16", seed=301, with_S0=True, device=DEV)
+    inputs.grad_inputs(d, seed=301, device=DEV)
+    got = run_gpu(d)
+    compare(got, run_oracle(d), what)
+    for n in np.flatnonzero(lens == 0):
+        np.testing.assert_array_equal(got["dS0"][n], d["dS_final"][n].cpu().numpy())
+
+
 def test_backward_without_dS0_output():
     note("backward want_dS0=False")
     d = inputs.prefill_inputs(1, 7, 2, 64, 64, io="f32", seed=2, with_S0=True, device=DEV)

@@ -51,6 +51,21 @@ def test_chunk_fwd_matches_oracle(B, T, H, dk, dv, io, with_S0):
     assert_close(go, gs, ro, rs, tol_for(io), "chunk")
 
 
+def test_single_head_f32_seed0():
+    """The single-head fp32 workload exactly as specified: B=1, H=1, T=256,
+    d_k=d_v=64, fp32 I/O, S0=0, scale d_k^-1/2, seed 0; bar 1e-4."""
+    cfg = inputs.CONFIGS["single_head_f32"]
+    note("single_head_f32 seed 0")
+    d = inputs.prefill_inputs(cfg["B"], cfg["T"], cfg["H"], cfg["dk"], cfg["dv"], io=cfg["io"],
+                              seed=0, with_S0=False, device=DEV)
+    o, S = kda().chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"])
+    torch.cuda.synchronize()
+    chains = [(0, 0)]
+    ro, rs = oracle_batched(d, chains)
+    go, gs = gpu_chains_batched(o, S, chains)
+    assert_close(go, gs, ro, rs, tol_for("f32"), "single_head_f32 seed 0")
+
+
 @pytest.mark.parametrize("dk,dv,io,strong_channels,gval", [(128, 128, "bf16", None, -3.0),
                                                            (128, 128, "bf16", 8, -3.0),
                                                            (128, 64, "bf16", 8, -3.0),
@@ -106,7 +121,9 @@ def test_headline_prefill_sampled_chains():
     o, S = kda().chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"])
     torch.cuda.synchronize()
     assert torch.isfinite(o.float()).all() and torch.isfinite(S).all()
-    chains = [(0, 0), (3, 17), (7, 31)]
+    # 16 chains: both heads of every sequence b, 16 distinct heads in all
+    chains = [(b, h) for b in range(8) for h in ((4 * b) % 32, (4 * b + 17) % 32)]
+    assert len({h for _, h in chains}) >= 4 and {b for b, _ in chains} == set(range(8))
     ro, rs = oracle_batched(d, chains)
     go, gs = gpu_chains_batched(o, S, chains)
     assert_close(go, gs, ro, rs, tol_for("bf16"), "headline sampled")
@@ -139,10 +156,30 @@ def test_varlen_matches_oracle(lens, H, dk, dv, io, with_S0):
         assert_close(go, gs, ro, rs, tol_for(io), "varlen")
 
 
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+def test_varlen_many_sequences_packed_order(io):
+    """More packed sequences than the length ranking covers (300 > 256): the
+    kernel then takes them in packed order.  Every chain is checked, with
+    empty, 1-token and multi-chunk sequences among them."""
+    rng = np.random.default_rng(300)
+    lens = rng.integers(0, 140, size=300)
+    lens[[3, 150, 299]] = [0, 1, 200]
+    dk = dv = 64
+    note("varlen 300 sequences io=%s total=%d" % (io, int(lens.sum())))
+    d = inputs.varlen_inputs(lens, 2, dk, dv, io=io, seed=300, with_S0=True, device=DEV)
+    o, S = kda().chunk_fwd_varlen(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"],
+                                  S0=d["S0"])
+    torch.cuda.synchronize()
+    chains = [(n, h) for n in range(300) for h in range(2)]
+    ro, rs = oracle_varlen(d, chains)
+    go, gs = gpu_chains_varlen(o, S, d["cu_seqlens"], chains)
+    assert_close(go, gs, ro, rs, tol_for(io), "varlen 300 sequences")
+
+
 def test_varlen_16seq_sampled_chains():
     """16 packed sequences of U{1024..65536} tokens (seed 0), H=32, with 8
-    long-horizon key channels per head; the oracle checks the shortest and the
-    longest sequence at two heads."""
+    long-horizon key channels per head; the oracle checks every sequence at two
+    heads."""
     cfg = inputs.CONFIGS["varlen_16seq_h32"]
     lens = inputs.varlen_lengths(cfg["n_seq"], cfg["lo"], cfg["hi"], seed=0)
     note("varlen_16seq_h32 total=%d" % int(lens.sum()))
@@ -151,10 +188,12 @@ def test_varlen_16seq_sampled_chains():
     o, S = kda().chunk_fwd_varlen(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"])
     torch.cuda.synchronize()
     assert torch.isfinite(S).all()
-    chains = [(int(np.argmin(lens)), 0), (int(np.argmax(lens)), 5)]
+    # every sequence at two heads (the packed kernel ranks sequences by length,
+    # so every rank of the schedule is checked)
+    chains = [(n, h) for n in range(cfg["n_seq"]) for h in (n % 32, (n + 13) % 32)]
     ro, rs = oracle_varlen(d, chains)
     go, gs = gpu_chains_varlen(o, S, d["cu_seqlens"], chains)
-    assert_close(go, gs, ro, rs, tol_for("bf16"), "varlen sampled")
+    assert_close(go, gs, ro, rs, tol_for("bf16"), "varlen 16 sequences")
 
 
 # ------------------------------------------------------------------ decode
