@@ -2,6 +2,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "common.h"
 #include "kda.h"
 
@@ -243,7 +245,8 @@ int backward_impl(const void* q, const void* k, const void* v, const float* log_
                   float* dq, float* dk, float* dv, float* dg, float* dbeta, float* dS0,
                   const int32_t* cu_seqlens, int n_seq, int T, int H, int d_k, int d_v,
                   float scale, int io_dtype, bool sg, void* workspace, size_t workspace_bytes,
-                  void* stream) {
+                  void* stream, bool check_only = false) {
+  // check_only: validate everything except the workspace and enqueue nothing
   if (n_seq < 0 || T < 0 || H <= 0) return KDA_ERR_DIM;
   if (!io_ok(io_dtype) || !shape_ok(d_k) || !shape_ok(d_v)) return KDA_ERR_UNSUPPORTED;
   const bool packed = cu_seqlens != nullptr;
@@ -260,7 +263,7 @@ int backward_impl(const void* q, const void* k, const void* v, const float* log_
   for (const void* p : a4)
     if (!aligned(p, 4)) return KDA_ERR_ALIGN;
   const size_t need = kda::backward_workspace_bytes(n_seq, rows, H, d_k, d_v);
-  if (n_seq > 0 && (!workspace || workspace_bytes < need)) return KDA_ERR_WORKSPACE;
+  if (!check_only && n_seq > 0 && (!workspace || workspace_bytes < need)) return KDA_ERR_WORKSPACE;
   const size_t e = io_bytes(io_dtype);
   const size_t state = (size_t)n_seq * H * d_k * d_v * 4;
   const size_t gk = rows * H * (sg ? 1 : d_k) * 4;
@@ -272,19 +275,48 @@ int backward_impl(const void* q, const void* k, const void* v, const float* log_
   const Range outs[] = {span(dq, rows * H * d_k * 4), span(dk, rows * H * d_k * 4),
                         span(dv, rows * H * d_v * 4), span(dg, gk),
                         span(dbeta, rows * H * 4),    span(dS0, dS0 ? state : 0),
-                        span(workspace, n_seq > 0 ? need : 0)};
+                        span(workspace, n_seq > 0 && !check_only ? need : 0)};
   for (size_t i = 0; i < sizeof(outs) / sizeof(outs[0]); ++i) {
     for (const Range& r : in)
       if (overlap(outs[i], r)) return KDA_ERR_ALIAS;
     for (size_t j = i + 1; j < sizeof(outs) / sizeof(outs[0]); ++j)
       if (overlap(outs[i], outs[j])) return KDA_ERR_ALIAS;
   }
-  if (n_seq == 0) return KDA_OK;
+  if (n_seq == 0 || check_only) return KDA_OK;
   return launch_status(kda::launch_backward(q, k, v, log_alpha, beta, S0, d_out, dS_final, dq, dk,
                                             dv, dg, dbeta, dS0, cu_seqlens, n_seq, T, H, d_k, d_v,
                                             scale, io_dtype == KDA_IO_BF16, sg,
                                             reinterpret_cast<float*>(workspace),
                                             reinterpret_cast<hipStream_t>(stream)));
+}
+
+// ------------------------------------------------------------ static scratch
+// The allocation-free backward (kda_backward_noalloc) keeps its workspace in
+// this array instead of caller memory.  Each device that loads the library
+// holds its own copy, at its own address, until the process ends.  In host
+// code `scratch` only names the symbol: its device address comes from
+// hipGetSymbolAddress with that device current, once per device, and is the
+// only form in which the array is handed to a kernel.
+constexpr size_t kScratchBytes = KDA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array (looked up on the
+// first call on that device).
+int current_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return KDA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return KDA_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return KDA_OK;
 }
 
 }  // namespace
@@ -303,6 +335,8 @@ const char* kda_status_string(int status) {
     case KDA_ERR_HIP: return "KDA_ERR_HIP: a HIP launch failed";
     case KDA_ERR_ALIAS: return "KDA_ERR_ALIAS: an output overlaps an input";
     case KDA_ERR_ALIGN: return "KDA_ERR_ALIGN: an array is not 16-byte aligned";
+    case KDA_ERR_SCRATCH:
+      return "KDA_ERR_SCRATCH: the problem needs more scratch than the static buffer holds";
     default: return "unknown KDA status";
   }
 }
@@ -448,6 +482,33 @@ int kda_backward(const void* q, const void* k, const void* v, const float* log_a
   return backward_impl(q, k, v, log_alpha, beta, S0, d_out, dS_final, dq, dk, dv, dlog_alpha,
                        dbeta, dS0, cu_seqlens, N, T, H, d_k, d_v, scale, io_dtype,
                        per_head_gate == 1, workspace, workspace_bytes, stream);
+}
+
+size_t kda_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+int kda_backward_noalloc(const void* q, const void* k, const void* v, const float* log_alpha,
+                         const float* beta, const float* S0, const void* d_out,
+                         const float* dS_final, float* dq, float* dk, float* dv,
+                         float* dlog_alpha, float* dbeta, float* dS0,
+                         const int32_t* cu_seqlens, int N, int T, int H, int d_k, int d_v,
+                         float scale, int io_dtype, int per_head_gate, void* stream) {
+  if (per_head_gate != 0 && per_head_gate != 1) return KDA_ERR_UNSUPPORTED;
+  // every argument first, with nothing enqueued and no HIP call
+  int st = backward_impl(q, k, v, log_alpha, beta, S0, d_out, dS_final, dq, dk, dv, dlog_alpha,
+                         dbeta, dS0, cu_seqlens, N, T, H, d_k, d_v, scale, io_dtype,
+                         per_head_gate == 1, nullptr, 0, stream, /*check_only=*/true);
+  if (st != KDA_OK) return st;
+  const size_t rows = cu_seqlens ? (size_t)T : (size_t)N * T;
+  if (kda::backward_workspace_bytes(N, rows, H, d_k, d_v) > kScratchBytes) return KDA_ERR_SCRATCH;
+  if (N == 0) return KDA_OK;
+  void* ws = nullptr;
+  st = current_scratch(&ws);
+  if (st != KDA_OK) return st;
+  // Every word of the workspace the kernel reads, it wrote earlier in the
+  // same call (checkpoints and v - p), so nothing needs clearing.
+  return backward_impl(q, k, v, log_alpha, beta, S0, d_out, dS_final, dq, dk, dv, dlog_alpha,
+                       dbeta, dS0, cu_seqlens, N, T, H, d_k, d_v, scale, io_dtype,
+                       per_head_gate == 1, ws, kScratchBytes, stream);
 }
 
 }  // extern "C"

@@ -76,6 +76,11 @@ def _load():
     lib.kda_backward.restype = i
     lib.kda_backward.argtypes = [vp, vp, vp, fp, fp, fp, vp, fp, fp, fp, fp, fp, fp, fp, vp, i, i, i,
                                  i, i, f, i, i, vp, sz, vp]
+    lib.kda_backward_noalloc.restype = i
+    lib.kda_backward_noalloc.argtypes = [vp, vp, vp, fp, fp, fp, vp, fp, fp, fp, fp, fp, fp, fp,
+                                         vp, i, i, i, i, i, f, i, i, vp]
+    lib.kda_noalloc_scratch_bytes.restype = sz
+    lib.kda_noalloc_scratch_bytes.argtypes = []
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_status_string.argtypes = [i]
     lib.kda_version.restype = i
@@ -426,6 +431,58 @@ def backward(q, k, v, log_alpha, beta, d_out, S0=None, dS_final=None, cu_seqlens
     if st != 0:
         raise KdaError(st, "kda_backward")
     return res
+
+
+def backward_noalloc(q, k, v, log_alpha, beta, d_out, out, S0=None, dS_final=None,
+                     cu_seqlens=None, scale=None):
+    """kda_backward_noalloc: the backward with the library's static scratch as
+    its workspace, for callers that cannot allocate.  ``out`` is a dict of
+    caller-allocated fp32 output tensors shaped as backward() returns them
+    (dq, dk, dv, dlog_alpha, dbeta; dS0 optional); neither this function nor
+    the library allocates anything.  Problems needing more than
+    noalloc_scratch_bytes() of workspace raise KdaError (KDA_ERR_SCRATCH)."""
+    packed = cu_seqlens is not None
+    lead = tuple(q.shape[:-2])
+    H, dk = q.shape[-2], q.shape[-1]
+    dv = v.shape[-1]
+    dev = q.device
+    if packed:
+        (Tt,) = lead
+        N, T = cu_seqlens.shape[0] - 1, Tt
+    else:
+        N, T = lead
+    if scale is None:
+        scale = dk ** -0.5
+    gshape, pre = _gate(log_alpha, lead + (H,), dk)
+    for name, t, shp, dt in (("q", q, lead + (H, dk), q.dtype), ("k", k, lead + (H, dk), q.dtype),
+                             ("v", v, lead + (H, dv), q.dtype),
+                             ("log_alpha", log_alpha, gshape, torch.float32),
+                             ("beta", beta, lead + (H,), torch.float32),
+                             ("d_out", d_out, lead + (H, dv), q.dtype),
+                             ("cu_seqlens", cu_seqlens, (N + 1,), torch.int32),
+                             ("S0", S0, (N, H, dk, dv), torch.float32),
+                             ("dS_final", dS_final, (N, H, dk, dv), torch.float32),
+                             ("dq", out["dq"], lead + (H, dk), torch.float32),
+                             ("dk", out["dk"], lead + (H, dk), torch.float32),
+                             ("dv", out["dv"], lead + (H, dv), torch.float32),
+                             ("dlog_alpha", out["dlog_alpha"], gshape, torch.float32),
+                             ("dbeta", out["dbeta"], lead + (H,), torch.float32),
+                             ("dS0", out.get("dS0"), (N, H, dk, dv), torch.float32)):
+        _check(t, name, shp, dt, dev)
+    st = lib.kda_backward_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                                  _ptr(S0), _ptr(d_out), _ptr(dS_final), _ptr(out["dq"]),
+                                  _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dlog_alpha"]),
+                                  _ptr(out["dbeta"]), _ptr(out.get("dS0")), _ptr(cu_seqlens), N, T,
+                                  H, dk, dv, float(scale), _io_code(q.dtype),
+                                  int(pre == "kda_gdn_"), _stream(dev))
+    if st != 0:
+        raise KdaError(st, "kda_backward_noalloc")
+    return out
+
+
+def noalloc_scratch_bytes():
+    """Size of the static scratch array behind backward_noalloc (bytes)."""
+    return int(lib.kda_noalloc_scratch_bytes())
 
 
 for _f in (chunk_fwd, chunk_fwd_varlen, decode_step, recurrent_fwd, recurrent_fwd_varlen):

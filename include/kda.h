@@ -28,7 +28,9 @@
  *  - The state is always fp32 and is kept fp32 on chip across a whole call.
  *  - Ownership: the caller allocates and frees every buffer, including the
  *    workspace.  The library allocates nothing, never frees, never
- *    synchronises the device and keeps no state between calls; work is
+ *    synchronises the device and keeps no state between calls (except the
+ *    static scratch array of kda_backward_noalloc and its per-device
+ *    address, below); work is
  *    enqueued on `stream` (a hipStream_t cast to void*, NULL = the default
  *    stream) and results are valid once that stream has reached them.
  *  - Aliasing: S0 == S_final is allowed (in-place state update); any other
@@ -68,7 +70,9 @@ enum kda_status {
   KDA_ERR_WORKSPACE = -4,   /* workspace missing or smaller than required */
   KDA_ERR_HIP = -5,         /* a HIP launch failed */
   KDA_ERR_ALIAS = -6,       /* an output overlaps an input (other than S0 == S_final) */
-  KDA_ERR_ALIGN = -7        /* an array is not aligned (16 bytes; beta and cu_seqlens 4) */
+  KDA_ERR_ALIGN = -7,       /* an array is not aligned (16 bytes; beta and cu_seqlens 4) */
+  KDA_ERR_SCRATCH = -8      /* kda_backward_noalloc: the problem needs more scratch than
+                               KDA_NOALLOC_SCRATCH_BYTES */
 };
 
 /*
@@ -315,6 +319,37 @@ int kda_backward(const void* q, const void* k, const void* v, const float* log_a
                  const int32_t* cu_seqlens, int N, int T, int H, int d_k, int d_v, float scale,
                  int io_dtype, int per_head_gate, void* workspace, size_t workspace_bytes,
                  void* stream);
+
+/*
+ * kda_backward_noalloc -- kda_backward for callers that cannot allocate
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same arguments, results and status codes as
+ * kda_backward, without the workspace: the library keeps it in a static
+ * device array of KDA_NOALLOC_SCRATCH_BYTES (64 MiB) on each device it runs
+ * on, held until the process ends.  The call allocates nothing (no hipMalloc,
+ * no allocating library routine); the caller still passes every input and
+ * output.
+ *
+ *  - A problem whose kda_backward_workspace_size() exceeds
+ *    KDA_NOALLOC_SCRATCH_BYTES returns KDA_ERR_SCRATCH (nothing enqueued).
+ *    At d_k = d_v = 128 that is about 7,700 head-tokens (rows x H).
+ *  - The first call on a device looks up that device's array address
+ *    (hipGetSymbolAddress, with the device current); later calls reuse it.
+ *  - Every call on one device shares that device's array, which keeps the
+ *    last call's contents.  Calls that overlap in time on one device (other
+ *    streams, other threads) race on it and give undefined results; order
+ *    them on one stream.
+ */
+#define KDA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int kda_backward_noalloc(const void* q, const void* k, const void* v, const float* log_alpha,
+                         const float* beta, const float* S0, const void* d_out,
+                         const float* dS_final, float* dq, float* dk, float* dv,
+                         float* dlog_alpha, float* dbeta, float* dS0,
+                         const int32_t* cu_seqlens, int N, int T, int H, int d_k, int d_v,
+                         float scale, int io_dtype, int per_head_gate, void* stream);
+
+/* KDA_NOALLOC_SCRATCH_BYTES, as the library was built. */
+size_t kda_noalloc_scratch_bytes(void);
 
 /* Workspace bytes kda_chunk_fwd needs for these sizes (0 if none; the
  * arguments are not validated here: unsupported sizes give 0). */

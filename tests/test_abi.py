@@ -33,6 +33,7 @@ def test_header_declares_the_entry_points():
                  "kda_gdn_chunk_fwd_varlen", "kda_gdn_decode_step", "kda_gdn_recurrent_fwd",
                  "kda_gdn_recurrent_fwd_varlen", "kda_chunk_fwd_fused", "kda_recurrent_fwd_fused",
                  "kda_decode_step_fused", "kda_backward", "kda_backward_workspace_size",
+                 "kda_backward_noalloc", "kda_noalloc_scratch_bytes",
                  "kda_chunk_fwd_workspace_size", "kda_chunk_fwd_varlen_workspace_size",
                  "kda_status_string", "kda_version"):
         assert want in names
@@ -46,7 +47,7 @@ def test_library_exports_every_declared_symbol(lib):
 def test_status_strings_and_version(lib):
     from gated_delta_rule_06_amd import kda
     assert kda.status_string(0) == "KDA_OK"
-    for code in range(-1, -8, -1):
+    for code in range(-1, -9, -1):
         assert kda.status_string(code).startswith("KDA_ERR_")
     assert "unknown" in kda.status_string(-99)
     assert lib.kda_version() >= 100
@@ -246,6 +247,26 @@ def test_backward_workspace_and_validation(lib):
     assert call(dk=P[6]) == -6                              # two outputs in one array
     assert call(ws=P[3]) == -6                              # workspace is log_alpha
     assert call(N=0) == 0
+
+
+def test_backward_noalloc_validation(lib):
+    """The allocation-free backward validates like kda_backward and rejects a
+    problem whose workspace exceeds its static scratch (KDA_ERR_SCRATCH)
+    before any HIP call."""
+    assert lib.kda_noalloc_scratch_bytes() == 64 << 20
+
+    def call(T=8, H=2, N=1, dk=128, dv=128, q=P[0], per_head=0, io=1):
+        return lib.kda_backward_noalloc(q, P[1], P[2], P[3], P[4], None, P[5], None, P[6], P[7],
+                                        P[8], P[9], P[10], None, None, N, T, H, dk, dv, 0.1, io,
+                                        per_head, None)
+    assert call(q=None) == -1
+    assert call(T=-1) == -2
+    assert call(dk=96) == -3
+    assert call(per_head=2) == -3
+    assert call(io=5) == -3
+    big_T = 4096
+    assert lib.kda_backward_workspace_size(1, big_T, 8, 128, 128, 0) > 64 << 20
+    assert call(T=big_T, H=8) == -8                        # KDA_ERR_SCRATCH
 
 
 def test_product_path_has_no_oracle_or_cpu_fallback():
