@@ -158,8 +158,11 @@ __device__ __forceinline__ void buf_store16(__amdgpu_buffer_rsrc_t r, uint32_t o
 // bf16 operands, fp32 accumulation: v_mfma_f32_16x16x32_bf16 / 16x16x16_bf16.
 struct OpBf16 {
   typedef uint16_t T;
-  static constexpr int PAD_RM = 8;    // row padding (elements) of buffers read row-wise
-  static constexpr int PAD_TR = 16;   // row padding of buffers read with the transpose read
+  static constexpr int PAD_RM = 8;    // row padding (elements) of buffers read as 8-byte rows
+  // Row padding of buffers read as 16-byte rows by 16 consecutive rows: a row
+  // stride of 8 (mod 16) dwords puts the 32 lanes of each half-wave on 32
+  // distinct 8-byte bank pairs in both passes of ds_read_b128.
+  static constexpr int PAD_B128 = 16;
   typedef i16x4 F16;                  // 16-deep operand fragment
   struct F32 { i16x4 lo, hi; };       // 32-deep operand fragment
 
@@ -239,7 +242,7 @@ struct OpBf16 {
 struct OpF32 {
   typedef float T;
   static constexpr int PAD_RM = 4;
-  static constexpr int PAD_TR = 4;
+  static constexpr int PAD_B128 = 4;   // (8 would avoid the conflicts but not fit in LDS)
   typedef f32x4 F16;
   struct F32 { f32x4 lo, hi; };
 
@@ -361,9 +364,13 @@ struct ChunkCfg {
   static_assert((NW == 4 || NW == 8) && CQ * TG == 64 && TPL * TG == C && VPL * CQ == VW,
                 "layout");
   // LDS leading dimensions (elements)
-  static constexpr int LD_K = DK + Op::PAD_RM;   // QG, KG, KIn [C][LD_K]
-  static constexpr int LD_V = DV + Op::PAD_TR;   // -V (buffer BV) [C][LD_V]
-  static constexpr int LD_64 = C + Op::PAD_RM;   // RR, AQ [C][LD_64] (row-wise reads)
+  // Row strides are chosen against LDS bank conflicts (gfx950: 64 dword banks per
+  // half-wave for 8-byte reads, ds_read_b128 in two 8-byte passes): buffers read
+  // as 16-byte row fragments take PAD_B128, the others PAD_RM.
+  static constexpr int LD_K = DK + Op::PAD_B128;  // QG, KG, KIn [C][LD_K]
+  static constexpr int LD_V = DV + Op::PAD_RM;    // -V (buffer BV) [C][LD_V]
+  static constexpr int LD_RR = C + Op::PAD_RM;    // RR [C][LD_RR] (8-byte row reads)
+  static constexpr int LD_AQ = C + Op::PAD_B128;  // AQ [C][LD_AQ] (16-byte row reads)
   static constexpr int SZ = sizeof(T);
   // LDS byte offsets.
   static constexpr int OFF_QG = 0;
@@ -375,9 +382,9 @@ struct ChunkCfg {
   static constexpr int OFF_OS = OFF_RD + NB * 16 * RD_LD * 4;
   static constexpr int OFF_BV = OFF_OS + C * LD_OS * SZ;
   static constexpr int OFF_AQ = OFF_BV + C * LD_V * SZ;
-  static constexpr int OFF_RT = OFF_AQ + C * LD_64 * SZ;
-  static constexpr int OFF_TD = OFF_RT + C * LD_64 * SZ;
-  static constexpr int LD_KT = C + Op::PAD_RM;  // KIT [DK][LD_KT]
+  static constexpr int OFF_RT = OFF_AQ + C * LD_AQ * SZ;
+  static constexpr int OFF_TD = OFF_RT + C * LD_RR * SZ;
+  static constexpr int LD_KT = C + Op::PAD_B128;  // KIT [DK][LD_KT]
   static constexpr int OFF_KT = OFF_TD + NB * 16 * 16 * SZ;
   // per-wave block for the decay scan (two lanes per token group, 16 key
   // channels per wave): 16 channel rows of 32 group totals (padded)
@@ -401,7 +408,8 @@ struct ChunkCfg {
   static_assert(OFF_KG % 16 == 0 && OFF_KI % 16 == 0 && OFF_RD % 16 == 0 && OFF_OS % 16 == 0 && OFF_FL % 16 == 0 &&
                 OFF_BV % 16 == 0 && OFF_AQ % 16 == 0 && OFF_RT % 16 == 0 && OFF_TD % 16 == 0 &&
                 OFF_GL % 16 == 0 && OFF_BT % 16 == 0 && OFF_KT % 16 == 0 && OFF_SC % 16 == 0 && (LD_K * SZ) % 16 == 0 &&
-                (LD_KT * SZ) % 16 == 0, "LDS alignment");
+                (LD_KT * SZ) % 16 == 0 && (LD_V * SZ) % 16 == 0 && (LD_AQ * SZ) % 16 == 0 &&
+                (LD_RR * SZ) % 8 == 0 && (LD_OS * SZ) % 16 == 0, "LDS alignment");
 };
 
 // Threshold below which a channel's chunk decay Gamma_L makes k / Gamma unsafe.
@@ -1011,9 +1019,9 @@ struct ChunkKernel {
       // RD[I][m][i] = R[16I + i][16I + m]  (column m of the block, contiguous over i)
       *lds_ptr<f32x4>(RD + I * 16 * Cfg::RD_LD + n * Cfg::RD_LD + g4) = -accR;
     } else {
-      *lds_ptr<typename Op::F16>(RR + (16 * I + n) * Cfg::LD_64 + 16 * J + g4) = Op::pack(accR);
+      *lds_ptr<typename Op::F16>(RR + (16 * I + n) * Cfg::LD_RR + 16 * J + g4) = Op::pack(accR);
     }
-    *lds_ptr<typename Op::F16>(AQ + (16 * I + n) * Cfg::LD_64 + Op::perm_pos(16 * J + g4)) =
+    *lds_ptr<typename Op::F16>(AQ + (16 * I + n) * Cfg::LD_AQ + Op::perm_pos(16 * J + g4)) =
         Op::pack(accA);
   }
 
@@ -1163,7 +1171,7 @@ struct ChunkKernel {
 #pragma unroll
         for (int J = 0; J < I; ++J) {
           // A[m = i][k = j] = -R[16I + m][16J + k] = RR[16I + m][16J + k]
-          const typename Op::F16 a = Op::ld16_rm(l, RR, Cfg::LD_64, 16 * I, 16 * J);
+          const typename Op::F16 a = Op::ld16_rm(l, RR, Cfg::LD_RR, 16 * I, 16 * J);
 #pragma unroll
           for (int nt = 0; nt < NVT; ++nt) Z[nt] = Op::mma16(a, XP[J][nt], Z[nt]);
         }
@@ -1202,7 +1210,7 @@ struct ChunkKernel {
       f32x4 (&O)[NVT] = Ob[I];
 #pragma unroll
       for (int kt = 0; kt <= I / 2; ++kt) {
-        const typename Op::F32 ba = Op::ld32_rmp(l, AQ, Cfg::LD_64, 16 * I, 32 * kt);
+        const typename Op::F32 ba = Op::ld32_rmp(l, AQ, Cfg::LD_AQ, 16 * I, 32 * kt);
 #pragma unroll
         for (int nt = 0; nt < NVT; ++nt) O[nt] = Op::mma32(EB[kt][nt], ba, O[nt]);
       }
@@ -1270,10 +1278,13 @@ struct ChunkKernel {
                                                          const float* g, const float* beta,
                                                          void* out, size_t row_base, int H,
                                                          int h, int clen, float scale,
-                                                         const Prologue& pro, float ea) {
+                                                         const Prologue& pro, float ea,
+                                                         int vw0 = -1) {
+    // vw0: the first value column of this wave's state tiles (default: the
+    // wave's own slice of the workgroup)
     const int w = threadIdx.x >> 6, l = lane_fresh();
     const int n = l & 15, g4 = 4 * (l >> 4);
-    const int vw0 = w * VW;
+    if (vw0 < 0) vw0 = w * VW;
     const bool xg = Cfg::FU && (pro.flags & PRO_GATE);
     const bool xn = Cfg::FU && (pro.flags & PRO_L2NORM);
     for (int t = 0; t < clen; ++t) {
@@ -1409,7 +1420,7 @@ struct ChunkKernel {
     // written: zero the buffer once.
     {
       LDS T* AQ = (LDS T*)(smem + Cfg::OFF_AQ);
-      for (int i = threadIdx.x; i < C * Cfg::LD_64; i += Cfg::NTHREADS) AQ[i] = Op::cvt(0.f);
+      for (int i = threadIdx.x; i < C * Cfg::LD_AQ; i += Cfg::NTHREADS) AQ[i] = Op::cvt(0.f);
     }
     // FU: the head's exp(A_log) and gate biases (LDS, read by prep)
     float ea = 1.f;
@@ -1607,6 +1618,401 @@ static hipError_t launch_chunk_t(const void* q, const void* k, const void* v, co
     hipLaunchKernelGGL(kern, dim3(n_seq * H), dim3(Cfg::NTHREADS), bytes, stream, q, k, v, g,
                        beta, S0, out, S_final, T, H, scale, pro);
   }
+  return hipGetLastError();
+}
+
+// ============================================================ chunk-parallel schedule
+// For few (sequence, head) chains the one-workgroup-per-chain kernel leaves
+// most CUs idle and its serial chunk chain sets the time.  This schedule
+// follows the three-stage structure of "Kimi Unveils Delta Attention and K3
+// Architecture Updates", section 6.6 (per-chunk WY factors, one inter-chunk
+// state scan, outputs of all chunks in parallel), with the factors of section
+// 6.3/6.4 written out in the key-by-value orientation:
+//
+//   W = (I + R)^{-1} Diag(beta) KG          U = (I + R)^{-1} Diag(beta) V
+//   E_c = U - W S_c                         (the resolved errors of 6.3)
+//   S_{c+1} = Diag(Gamma_L) S_c + K_end^T E_c,   K_end = Gamma_L * KI (6.4)
+//   O_c = QG S_c + Aqk E_c                  (6.5)
+//
+// Stage A (chunk_intra_kernel, one workgroup per (chunk, head), all chunks at
+// once) forms everything that does not depend on the state; stage B
+// (chunk_scan_kernel, one wave per (chain, 16 value columns)) is the only
+// serial loop, two 128-deep products per chunk; stage C (chunk_out_kernel,
+// all chunks at once) forms the outputs.  Every factor goes through the
+// workspace as bf16 MFMA fragments in the exact lane order its consumer
+// reads, one 16-byte load per lane per fragment.  A chunk whose decay leaves
+// the range of the single chunk-start reference (the fused kernel's guard)
+// is flagged by stage A and recomputed token by token by stage B.
+template <class Cfg>
+struct ParLayout {
+  static constexpr int DK = Cfg::DK, DV = Cfg::DV;
+  static constexpr int NKS = DK / 32, MTK = DK / 16, NVS = DV / 16;
+  static constexpr int FR = 64 * 16;                          // one fragment, 64 lanes
+  static constexpr int OFF_W = 0;                             // -W   [I 4][ks]
+  static constexpr int OFF_QG = OFF_W + 4 * NKS * FR;         // QG   [I 4][ks]
+  static constexpr int OFF_KE = OFF_QG + 4 * NKS * FR;        // -K_end^T [mt][kt 2]
+  static constexpr int OFF_AQ = OFF_KE + MTK * 2 * FR;        // -Aqk [I 4][kt 2]
+  static constexpr int OFF_U = OFF_AQ + 4 * 2 * FR;           // U    [vs][I 4][lane] 8 B
+  static constexpr int OFF_GL = OFF_U + NVS * 4 * 64 * 8;     // Gamma_L [DK] fp32
+  static constexpr int OFF_SB = OFF_GL + DK * 4;              // S_c  [vs][ks][lane] 16 B
+  static constexpr int OFF_EB = OFF_SB + NVS * NKS * FR;      // -E_c [vs][kt 2][lane] 16 B
+  static constexpr int PER_CHUNK = OFF_EB + NVS * 2 * FR;
+  static_assert(PER_CHUNK % 256 == 0, "chunk records stay 256-byte aligned");
+  // bytes of workspace for n chunk-heads: the records, then one int flag each
+  static size_t bytes(size_t n) { return n * PER_CHUNK + ((n * 4 + 255) / 256) * 256; }
+};
+
+template <class Cfg>
+struct ParKernel {
+  typedef ChunkKernel<Cfg> K;
+  typedef ParLayout<Cfg> L;
+  typedef typename Cfg::Op Op;
+  typedef typename Cfg::T T;
+  typedef typename Cfg::Io Io;
+  static constexpr int C = Cfg::C, DK = Cfg::DK, DV = Cfg::DV, NW = Cfg::NW;
+  static constexpr int NKS = Cfg::NKS, MTK = Cfg::MTK;
+  static_assert(NW == 8 && DK == 128 && DV == 128 && Op::PERMUTED, "bf16 128x128 only");
+
+  static __device__ __forceinline__ void st16(char* p, typename Op::F32 f) {
+    *reinterpret_cast<u32x4*>(p) = __builtin_bit_cast(u32x4, __builtin_shufflevector(f.lo, f.hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  }
+  static __device__ __forceinline__ typename Op::F32 ld16(const char* p) {
+    const u32x4 w = *reinterpret_cast<const u32x4*>(p);
+    const i16x8 v = __builtin_bit_cast(i16x8, w);
+    return typename Op::F32{__builtin_shufflevector(v, v, 0, 1, 2, 3), __builtin_shufflevector(v, v, 4, 5, 6, 7)};
+  }
+  static __device__ __forceinline__ typename Op::F16 neg16(typename Op::F16 f) {
+    return __builtin_bit_cast(typename Op::F16, __builtin_bit_cast(u32x2, f) ^ u32x2{0x80008000u, 0x80008000u});
+  }
+
+  // The state-independent tiles and inverses (the fused kernel's middle
+  // interval without its state products).
+  static __device__ __forceinline__ void tiles(LDS char* smem) {
+    switch (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) {
+      case 0: K::tile_qk(smem, 0, 0); K::template invert_diag<0>(smem); break;
+      case 1: K::tile_qk(smem, 1, 1); K::template invert_diag<1>(smem); break;
+      case 2: K::tile_qk(smem, 2, 2); K::template invert_diag<2>(smem); break;
+      case 3: K::tile_qk(smem, 3, 3); K::template invert_diag<3>(smem); break;
+      case 4: K::tile_qk(smem, 1, 0); K::tile_qk(smem, 3, 2); break;
+      case 5: K::tile_qk(smem, 2, 0); K::tile_qk(smem, 2, 1); break;
+      case 6: K::tile_qk(smem, 3, 0); break;
+      default: K::tile_qk(smem, 3, 1); break;
+    }
+  }
+
+  // X = (I + R)^{-1} Y by 16-token blocks for this wave's two 16-column tiles:
+  // waves 0-3 take Y = Diag(beta) KG (key columns 32w ..), so X = W; waves
+  // 4-7 take Y = Diag(beta) (-V) (value columns 32(w-4) ..), so X = -U.
+  // -W goes back into the KG buffer (the wave's own columns, which only it
+  // reads from here on); U goes straight to the workspace in the
+  // accumulator layout stage B starts E from.
+  static __device__ __forceinline__ void wy(LDS char* smem, char* rec) {
+    const int w = threadIdx.x >> 6, l = lane_fresh();
+    const int n = l & 15, g = l >> 4;
+    LDS T* KG = (LDS T*)(smem + Cfg::OFF_KG);
+    const LDS T* BV = (const LDS T*)(smem + Cfg::OFF_BV);
+    const LDS T* RR = (const LDS T*)(smem + Cfg::OFF_RT);
+    const LDS T* TD = (const LDS T*)(smem + Cfg::OFF_TD);
+    const LDS float* BT = (const LDS float*)(smem + Cfg::OFF_BT);
+    const bool keys = w < 4;
+    const int c0 = 32 * (w & 3);
+    f32x4 Y[4][2];
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+      const f32x4 b = *lds_ptr<const f32x4>(BT + 16 * I + 4 * g);
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const typename Op::F16 f = keys ? Op::ld16_trp(l, KG, Cfg::LD_K, 16 * I, Op::perm_pos(c0 + 16 * nt))
+                                        : Op::ld16_tr(l, BV, Cfg::LD_V, 16 * I, c0 + 16 * nt);
+        Y[I][nt] = Op::unpack(f) * b;
+      }
+    }
+    typename Op::F16 XP[4][2];
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+      if (I > 0) {
+        f32x4 Z[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int J = 0; J < I; ++J) {
+          const typename Op::F16 a = Op::ld16_rm(l, RR, Cfg::LD_RR, 16 * I, 16 * J);   // -R_IJ
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) Z[nt] = Op::mma16(a, XP[J][nt], Z[nt]);
+        }
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) Y[I][nt] += Z[nt];
+      }
+      const typename Op::F16 a = Op::ld16_tr(l, TD + I * 256, 16, 0, 0);   // T_II
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        XP[I][nt] = Op::pack(Op::mma16(a, Op::pack(Y[I][nt]), z));
+      }
+    }
+#pragma unroll
+    for (int I = 0; I < 4; ++I)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        if (keys) {
+          // -W[16I + 4g + r][c0 + 16nt + n] into the (permuted) KG rows
+          const u32x2 wv = __builtin_bit_cast(u32x2, neg16(XP[I][nt]));
+          const int col = Op::perm_pos(c0 + 16 * nt + n);
+          LDS uint16_t* p = (LDS uint16_t*)(KG) + (16 * I + 4 * g) * Cfg::LD_K + col;
+          p[0] = (uint16_t)(wv[0] & 0xffffu);
+          p[Cfg::LD_K] = (uint16_t)(wv[0] >> 16);
+          p[2 * Cfg::LD_K] = (uint16_t)(wv[1] & 0xffffu);
+          p[3 * Cfg::LD_K] = (uint16_t)(wv[1] >> 16);
+        } else {
+          // U = -X: value tile vs = (c0 + 16nt) / 16, token block I, this lane
+          const int vs = (c0 + 16 * nt) / 16;
+          *reinterpret_cast<u32x2*>(rec + L::OFF_U + ((vs * 4 + I) * 64 + l) * 8) =
+              __builtin_bit_cast(u32x2, neg16(XP[I][nt]));
+        }
+      }
+  }
+
+  // The remaining factors to the workspace, each as the fragments their
+  // consumers read: -W and QG (rows = tokens, k = keys), -K_end^T (rows =
+  // keys, k = tokens), -Aqk (rows = tokens, k = tokens), Gamma_L.
+  static __device__ __forceinline__ void write_factors(LDS char* smem, char* rec) {
+    const int w = threadIdx.x >> 6, l = lane_fresh();
+    const LDS T* KG = (const LDS T*)(smem + Cfg::OFF_KG);   // now -W
+    const LDS T* QG = (const LDS T*)(smem + Cfg::OFF_QG);
+    const LDS T* KIT = (const LDS T*)(smem + Cfg::OFF_KT);
+    const LDS T* AQ = (const LDS T*)(smem + Cfg::OFF_AQ);
+    const LDS float* GL = (const LDS float*)(smem + Cfg::OFF_GL);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int f = 2 * w + j;                  // 0 .. 15
+      const int I = f / NKS, ks = f % NKS;
+      st16(rec + L::OFF_W + f * L::FR + l * 16, Op::ld32_rmp(l, KG, Cfg::LD_K, 16 * I, 32 * ks));
+      st16(rec + L::OFF_QG + f * L::FR + l * 16, Op::ld32_rmp(l, QG, Cfg::LD_K, 16 * I, 32 * ks));
+      // KIT holds -KI key-major; -K_end = Gamma_L (-KI) row-wise (row = key)
+      const int mt = f / 2, kt = f % 2;
+      typename Op::F32 a = Op::ld32_rmp(l, KIT, Cfg::LD_KT, 16 * mt, 32 * kt);
+      const float gl = GL[16 * mt + (l & 15)];
+      a.lo = Op::pack(Op::unpack(a.lo) * gl);
+      a.hi = Op::pack(Op::unpack(a.hi) * gl);
+      st16(rec + L::OFF_KE + f * L::FR + l * 16, a);
+    }
+    st16(rec + L::OFF_AQ + w * L::FR + l * 16, Op::ld32_rmp(l, AQ, Cfg::LD_AQ, 16 * (w / 2), 32 * (w % 2)));
+    if (w == 0 && l < DK / 4)
+      *reinterpret_cast<f32x4*>(rec + L::OFF_GL + 16 * l) = *lds_ptr<const f32x4>(GL + 4 * l);
+  }
+};
+
+// Stage A: one workgroup per (chain, chunk); blockIdx.x = chain * NC + chunk.
+template <class Cfg>
+__global__ __launch_bounds__(Cfg::NTHREADS, 1) void chunk_intra_kernel(
+    const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
+    const float* __restrict__ g, const float* __restrict__ beta, char* __restrict__ ws, int T,
+    int H, int NC, float scale) {
+  typedef ChunkKernel<Cfg> K;
+  typedef ParLayout<Cfg> L;
+  typedef typename Cfg::Op Op;
+  typedef typename Cfg::T OpT;
+  extern __shared__ __attribute__((aligned(16))) char smem_[];
+  LDS char* smem = (LDS char*)smem_;
+  const int idx = blockIdx.x;
+  const int chain = idx / NC, c = idx % NC;
+  const int b = chain / H, h = chain % H;
+  const size_t row_base = (size_t)b * T + (size_t)c * Cfg::C;
+  const int clen = min(Cfg::C, T - c * Cfg::C);
+  char* rec = ws + (size_t)idx * L::PER_CHUNK;
+  int* flags = reinterpret_cast<int*>(ws + (size_t)gridDim.x * L::PER_CHUNK);
+  {
+    LDS OpT* AQ = (LDS OpT*)(smem + Cfg::OFF_AQ);   // tiles above the diagonal stay zero
+    for (int i = threadIdx.x; i < Cfg::C * Cfg::LD_AQ; i += Cfg::NTHREADS) AQ[i] = Op::cvt(0.f);
+  }
+  const typename K::Offsets offs = K::lane_offsets(H);
+  typename K::Raw raw;
+  K::template load_raw<K::LOAD_ALL>(raw, offs, q, k, v, g, beta, row_base, H, h, clen);
+  const Prologue pro{0u, nullptr, nullptr};
+  const int bad = K::prep(raw, smem, scale, pro, 1.f, 0, clen);
+  LDS int* FL = (LDS int*)(smem + Cfg::OFF_FL);
+  const int w = threadIdx.x >> 6;
+  const int wave_bad = __any(bad);
+  if (lane_fresh() == 0) FL[w] = wave_bad ? 1 : 0;
+  __syncthreads();
+  int any_bad = 0;
+#pragma unroll
+  for (int i = 0; i < Cfg::NW; ++i) any_bad |= FL[i];
+  if (threadIdx.x == 0) flags[idx] = any_bad;
+  if (any_bad) return;   // the whole workgroup: stage B redoes this chunk token by token
+  ParKernel<Cfg>::tiles(smem);
+  __syncthreads();
+  ParKernel<Cfg>::wy(smem, rec);
+  __syncthreads();
+  ParKernel<Cfg>::write_factors(smem, rec);
+}
+
+// Stage B: one wave per (chain, 16 value columns); blockIdx.x = chain * NVS + vs.
+// The fragments of chunk c + 1 are loaded while chunk c is computed: -W right
+// after its last use, -K_end, U and Gamma_L after the state update.
+template <class Cfg>
+__global__ __launch_bounds__(64, 1) void chunk_scan_kernel(
+    const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
+    const float* __restrict__ g, const float* __restrict__ beta, const float* S0, void* out,
+    float* S_final, char* __restrict__ ws, int T, int H, int NC, float scale) {
+  typedef ChunkKernel<Cfg> K;
+  typedef ParLayout<Cfg> L;
+  typedef ParKernel<Cfg> P;
+  typedef typename Cfg::Op Op;
+  constexpr int MTK = Cfg::MTK, NKS = Cfg::NKS, DK = Cfg::DK, DV = Cfg::DV;
+  const int chain = blockIdx.x / L::NVS, vs = blockIdx.x % L::NVS;
+  const int b = chain / H, h = chain % H;
+  const int l = lane_fresh();
+  const int n = l & 15, g4 = 4 * (l >> 4);
+  const int* flags = reinterpret_cast<const int*>(ws + (size_t)(gridDim.x / L::NVS) * NC * L::PER_CHUNK);
+  f32x4 S[MTK][1];
+#pragma unroll
+  for (int mt = 0; mt < MTK; ++mt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      S[mt][0][r] = S0 ? S0[((size_t)chain * DK + 16 * mt + g4 + r) * DV + 16 * vs + n] : 0.f;
+  typename Op::F32 Wf[4][NKS], Kf[MTK][2];
+  u32x2 Uf[4];
+  f32x4 Gf[MTK];
+  auto load_w = [&](const char* rec) {
+#pragma unroll
+    for (int f = 0; f < 4 * NKS; ++f) Wf[f / NKS][f % NKS] = P::ld16(rec + L::OFF_W + f * L::FR + l * 16);
+  };
+  auto load_rest = [&](const char* rec) {
+#pragma unroll
+    for (int f = 0; f < 2 * MTK; ++f) Kf[f / 2][f % 2] = P::ld16(rec + L::OFF_KE + f * L::FR + l * 16);
+#pragma unroll
+    for (int I = 0; I < 4; ++I) Uf[I] = *reinterpret_cast<const u32x2*>(rec + L::OFF_U + ((vs * 4 + I) * 64 + l) * 8);
+#pragma unroll
+    for (int mt = 0; mt < MTK; ++mt) Gf[mt] = *reinterpret_cast<const f32x4*>(rec + L::OFF_GL + (16 * mt + g4) * 4);
+  };
+  const char* rec0 = ws + (size_t)chain * NC * L::PER_CHUNK;
+  load_w(rec0);
+  load_rest(rec0);
+  for (int c = 0; c < NC; ++c) {
+    char* rec = ws + ((size_t)chain * NC + c) * L::PER_CHUNK;
+    const char* nrec = ws + ((size_t)chain * NC + (c + 1 < NC ? c + 1 : c)) * L::PER_CHUNK;
+    if (__builtin_amdgcn_readfirstlane(flags[chain * NC + c])) {
+      // outside the chunk-start reference's range: the recurrence token by token
+      const Prologue pro{0u, nullptr, nullptr};
+      K::recurrent_chunk(S, q, k, v, g, beta, out, (size_t)b * T + (size_t)c * Cfg::C, H, h,
+                         min(Cfg::C, T - c * Cfg::C), scale, pro, 1.f, 16 * vs);
+      load_w(nrec);
+      load_rest(nrec);
+      continue;
+    }
+    // S_c as 32-deep operands over keys (also stage C's A operand)
+    typename Op::F32 SB[NKS];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      SB[ks] = typename Op::F32{Op::pack(S[2 * ks][0]), Op::pack(S[2 * ks + 1][0])};
+      P::st16(rec + L::OFF_SB + (vs * NKS + ks) * L::FR + l * 16, SB[ks]);
+    }
+    // E = U + (-W) S_c
+    f32x4 E[4];
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+      E[I] = Op::unpack(__builtin_bit_cast(typename Op::F16, Uf[I]));
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) E[I] = Op::mma32(Wf[I][ks], SB[ks], E[I]);
+    }
+    load_w(nrec);
+    // -E as 32-deep operands over tokens
+    typename Op::F32 EB[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      EB[kt] = typename Op::F32{Op::pack(-E[2 * kt]), Op::pack(-E[2 * kt + 1])};
+      P::st16(rec + L::OFF_EB + (vs * 2 + kt) * L::FR + l * 16, EB[kt]);
+    }
+    // S <- Diag(Gamma_L) S + (-K_end)^T (-E)
+#pragma unroll
+    for (int mt = 0; mt < MTK; ++mt) {
+      f32x4 s = S[mt][0] * Gf[mt];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) s = Op::mma32(Kf[mt][kt], EB[kt], s);
+      S[mt][0] = s;
+    }
+    load_rest(nrec);
+  }
+  if (S_final) {
+#pragma unroll
+    for (int mt = 0; mt < MTK; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        S_final[((size_t)chain * DK + 16 * mt + g4 + r) * DV + 16 * vs + n] = S[mt][0][r];
+  }
+}
+
+// Stage C: one workgroup per (chain, chunk), wave vs = 16 value columns:
+// O^T = S_c^T QG^T + (-E)^T (-Aqk)^T, written as 4 consecutive values of a token.
+template <class Cfg>
+__global__ __launch_bounds__(Cfg::NTHREADS, 1) void chunk_out_kernel(void* out,
+                                                                     const char* __restrict__ ws,
+                                                                     int T, int H, int NC) {
+  typedef ParLayout<Cfg> L;
+  typedef ParKernel<Cfg> P;
+  typedef typename Cfg::Op Op;
+  typedef typename Cfg::Io Io;
+  constexpr int NKS = Cfg::NKS, DV = Cfg::DV;
+  const int idx = blockIdx.x;
+  const int* flags = reinterpret_cast<const int*>(ws + (size_t)gridDim.x * L::PER_CHUNK);
+  if (flags[idx]) return;   // written token by token by stage B
+  const int chain = idx / NC, c = idx % NC;
+  const int b = chain / H, h = chain % H;
+  const int clen = min(Cfg::C, T - c * Cfg::C);
+  const int vs = threadIdx.x >> 6, l = lane_fresh();
+  const char* rec = ws + (size_t)idx * L::PER_CHUNK;
+  typename Op::F32 SB[NKS], EB[2];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) SB[ks] = P::ld16(rec + L::OFF_SB + (vs * NKS + ks) * L::FR + l * 16);
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) EB[kt] = P::ld16(rec + L::OFF_EB + (vs * 2 + kt) * L::FR + l * 16);
+#pragma unroll
+  for (int I = 0; I < 4; ++I) {
+    f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+      o = Op::mma32(SB[ks], P::ld16(rec + L::OFF_QG + (I * NKS + ks) * L::FR + l * 16), o);
+#pragma unroll
+    for (int kt = 0; kt <= I / 2; ++kt)
+      o = Op::mma32(EB[kt], P::ld16(rec + L::OFF_AQ + (I * 2 + kt) * L::FR + l * 16), o);
+    const int t = 16 * I + (l & 15);
+    if (t < clen) {
+      const size_t row = ((size_t)b * T + (size_t)c * Cfg::C + t) * H + h;
+      Io::store4(out, row * DV + 16 * vs + 4 * (l >> 4), o);
+    }
+  }
+}
+
+// The schedule by shape: a bf16 128x128 batch of few, long chains takes the
+// chunk-parallel stages (the state chain of each sequence is then 128-deep
+// products only); everything else the one-workgroup-per-chain kernel.
+size_t chunk_par_workspace_bytes(int n_seq, int T, int H) {
+  typedef ChunkCfg<128, 128, IoBf16, OpBf16, 8, false, false> Cfg;
+  const size_t NC = (size_t)(T + Cfg::C - 1) / Cfg::C;
+  return ParLayout<Cfg>::bytes((size_t)n_seq * H * NC);
+}
+
+bool chunk_par_selected(int n_seq, int T, int H, int dk, int dv, bool bf16) {
+  return bf16 && dk == 128 && dv == 128 && n_seq > 0 && (long)n_seq * H <= KDA_PAR_MAX_CHAINS &&
+         T >= KDA_PAR_MIN_T && chunk_par_workspace_bytes(n_seq, T, H) <= KDA_PAR_MAX_WS;
+}
+
+hipError_t launch_chunk_par(const void* q, const void* k, const void* v, const float* g,
+                            const float* beta, const float* S0, void* out, float* S_final,
+                            int n_seq, int T, int H, float scale, void* ws, hipStream_t stream) {
+  typedef ChunkCfg<128, 128, IoBf16, OpBf16, 8, false, false> Cfg;
+  typedef ParLayout<Cfg> L;
+  const int NC = (T + Cfg::C - 1) / Cfg::C;
+  const int chains = n_seq * H;
+  const int bytes = Cfg::LDS_TOTAL;
+  auto ka = chunk_intra_kernel<Cfg>;
+  hipError_t e = hipFuncSetAttribute((const void*)ka, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(ka, dim3(chains * NC), dim3(Cfg::NTHREADS), bytes, stream, q, k, v, g, beta,
+                     (char*)ws, T, H, NC, scale);
+  hipLaunchKernelGGL(chunk_scan_kernel<Cfg>, dim3(chains * L::NVS), dim3(64), 0, stream, q, k, v,
+                     g, beta, S0, out, S_final, (char*)ws, T, H, NC, scale);
+  hipLaunchKernelGGL(chunk_out_kernel<Cfg>, dim3(chains * NC), dim3(Cfg::NTHREADS), 0, stream, out,
+                     (const char*)ws, T, H, NC);
   return hipGetLastError();
 }
 

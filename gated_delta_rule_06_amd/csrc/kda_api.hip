@@ -18,6 +18,11 @@ hipError_t launch_chunk(const void* q, const void* k, const void* v, const float
                         float scale, bool bf16, bool scalar_gate, const Prologue& pro,
                         hipStream_t stream);
 bool chunk_supported(int dk, int dv, bool bf16);
+bool chunk_par_selected(int n_seq, int T, int H, int dk, int dv, bool bf16);
+size_t chunk_par_workspace_bytes(int n_seq, int T, int H);
+hipError_t launch_chunk_par(const void* q, const void* k, const void* v, const float* g,
+                            const float* beta, const float* S0, void* out, float* S_final,
+                            int n_seq, int T, int H, float scale, void* ws, hipStream_t stream);
 hipError_t launch_recurrent(const void* q, const void* k, const void* v, const float* g,
                             const float* beta, const float* S0, void* out, float* S_final,
                             const int32_t* cu, int n_seq, int T, int H, int dk, int dv,
@@ -158,14 +163,23 @@ namespace {
 
 // One implementation per operation; cu_seqlens NULL means the batched
 // layout (n_seq sequences of T tokens), otherwise the packed one (T = T_total).
+// Workspace of the plain batched KDA prefill: the chunk-parallel schedule's
+// per-chunk factors when that schedule is selected for these sizes, else none.
+size_t chunk_ws_bytes(int B, int T, int H, int d_k, int d_v, int chunk, int io_dtype) {
+  if (B < 0 || T < 0 || H <= 0 || chunk != 64 || !io_ok(io_dtype)) return 0;
+  if (!kda::chunk_par_selected(B, T, H, d_k, d_v, io_dtype == KDA_IO_BF16)) return 0;
+  return kda::chunk_par_workspace_bytes(B, T, H);
+}
+
 int chunk_impl(const void* q, const void* k, const void* v, const float* log_alpha,
                const float* beta, const float* S0, void* out, float* S_final,
                const int32_t* cu_seqlens, bool packed, int n_seq, int T, int H, int d_k, int d_v,
                float scale, int chunk, int io_dtype, bool sg, const kda_prologue* pro,
-               void* stream) {
+               void* stream, void* workspace = nullptr, size_t workspace_bytes = 0) {
   if (n_seq < 0 || T < 0 || H <= 0) return KDA_ERR_DIM;
   if (packed && !cu_seqlens) return KDA_ERR_NULL;
   const size_t rows = packed ? (size_t)T : (size_t)n_seq * T;
+  if (rows > 0x7fffffffu) return KDA_ERR_DIM;   // token rows are 32-bit in the kernels
   int st = check_prefill(q, k, v, log_alpha, beta, S0, out, S_final, cu_seqlens, rows, n_seq, H,
                          d_k, d_v, chunk, io_dtype, sg);
   if (st != KDA_OK) return st;
@@ -174,8 +188,27 @@ int chunk_impl(const void* q, const void* k, const void* v, const float* log_alp
   st = check_prologue(pro, H, d_k, sg, &pr, span(out, rows * H * d_v * io_bytes(io_dtype)),
                       span(S_final, S_final ? state : 0));
   if (st != KDA_OK) return st;
+  // the chunk-parallel schedule (plain batched KDA calls of few long chains)
+  const bool par = !packed && !sg && pr.flags == 0 &&
+                   kda::chunk_par_selected(n_seq, T, H, d_k, d_v, io_dtype == KDA_IO_BF16);
+  if (par) {
+    const size_t need = kda::chunk_par_workspace_bytes(n_seq, T, H);
+    if (!workspace || workspace_bytes < need) return KDA_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return KDA_ERR_ALIGN;
+    const size_t e = io_bytes(io_dtype);
+    const Range rw = span(workspace, need);
+    const Range others[] = {span(q, rows * H * d_k * e), span(k, rows * H * d_k * e),
+                            span(v, rows * H * d_v * e), span(log_alpha, rows * H * d_k * 4),
+                            span(beta, rows * H * 4), span(S0, S0 ? state : 0),
+                            span(out, rows * H * d_v * e), span(S_final, S_final ? state : 0)};
+    for (const Range& r : others)
+      if (overlap(rw, r)) return KDA_ERR_ALIAS;
+  }
   if (n_seq == 0) return KDA_OK;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (par)
+    return launch_status(kda::launch_chunk_par(q, k, v, log_alpha, beta, S0, out, S_final, n_seq,
+                                               T, H, scale, workspace, s));
   if (!packed && T == 0) {
     if (!S_final || S0 == S_final) return KDA_OK;
     hipLaunchKernelGGL(copy_state_kernel, dim3(1024), dim3(256), 0, s, S0, S_final, state / 4);
@@ -341,7 +374,10 @@ const char* kda_status_string(int status) {
   }
 }
 
-size_t kda_chunk_fwd_workspace_size(int, int, int, int, int, int, int) { return 0; }
+size_t kda_chunk_fwd_workspace_size(int B, int T, int H, int d_k, int d_v, int chunk,
+                                    int io_dtype) {
+  return chunk_ws_bytes(B, T, H, d_k, d_v, chunk, io_dtype);
+}
 
 size_t kda_chunk_fwd_varlen_workspace_size(int, int, int, int, int, int, int) { return 0; }
 
@@ -349,10 +385,8 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const float* log_
                   const float* beta, const float* S0, void* out, float* S_final, int B, int T,
                   int H, int d_k, int d_v, float scale, int chunk, int io_dtype, void* workspace,
                   size_t workspace_bytes, void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   return chunk_impl(q, k, v, log_alpha, beta, S0, out, S_final, nullptr, false, B, T, H, d_k, d_v,
-                    scale, chunk, io_dtype, false, nullptr, stream);
+                    scale, chunk, io_dtype, false, nullptr, stream, workspace, workspace_bytes);
 }
 
 int kda_chunk_fwd_varlen(const void* q, const void* k, const void* v, const float* log_alpha,
@@ -439,11 +473,10 @@ int kda_chunk_fwd_fused(const void* q, const void* k, const void* v, const float
                         float scale, int chunk, int io_dtype, int per_head_gate,
                         const kda_prologue* pro, void* workspace, size_t workspace_bytes,
                         void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   if (per_head_gate != 0 && per_head_gate != 1) return KDA_ERR_UNSUPPORTED;
   return chunk_impl(q, k, v, log_alpha, beta, S0, out, S_final, cu_seqlens, cu_seqlens != nullptr,
-                    N, T, H, d_k, d_v, scale, chunk, io_dtype, per_head_gate == 1, pro, stream);
+                    N, T, H, d_k, d_v, scale, chunk, io_dtype, per_head_gate == 1, pro, stream,
+                    workspace, workspace_bytes);
 }
 
 int kda_recurrent_fwd_fused(const void* q, const void* k, const void* v, const float* log_alpha,

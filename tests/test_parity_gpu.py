@@ -111,6 +111,34 @@ def test_prefill_h16_t4096_with_S0():
     assert_close(go, gs, ro, rs, tol_for("bf16"), "prefill_h16_s0")
 
 
+@pytest.mark.parametrize("B,T,H,with_S0,strong", [(2, 1000, 3, True, False),
+                                                  (1, 512, 2, False, False),
+                                                  (1, 700, 2, True, True)])
+def test_chunk_parallel_schedule_matches_oracle(B, T, H, with_S0, strong):
+    """Few long chains take the chunk-parallel schedule (per-chunk WY factors,
+    one state scan, outputs of all chunks in parallel).  Every chain is checked,
+    with a ragged last chunk; with ``strong`` some chunks decay beyond the
+    chunk-start reference's range in 8 channels and are recomputed token by
+    token by the scan stage."""
+    K = kda()
+    assert K.chunk_fwd_workspace_size(B, T, H, 128, 128) > 0   # the schedule is taken
+    note("chunk-parallel B=%d T=%d H=%d S0=%s strong=%s" % (B, T, H, with_S0, strong))
+    d = inputs.prefill_inputs(B, T, H, 128, 128, io="bf16", seed=T + H, with_S0=with_S0,
+                              device=DEV)
+    if strong:
+        gen = torch.Generator(device=DEV)
+        gen.manual_seed(7)
+        idx = torch.randperm(128, generator=gen, device=DEV)[:8]
+        sl = d["g"][:, 128:300]
+        sl[..., idx] = -3.0
+    o, S = K.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], S0=d["S0"])
+    torch.cuda.synchronize()
+    chains = [(b, h) for b in range(B) for h in range(H)]
+    ro, rs = oracle_batched(d, chains)
+    go, gs = gpu_chains_batched(o, S, chains)
+    assert_close(go, gs, ro, rs, tol_for("bf16"), "chunk-parallel")
+
+
 def test_headline_prefill_sampled_chains():
     """B=8, H=32, T=8192, d=128 bf16 at full size in the benchmark's launch;
     the oracle recomputes a sample of chains one by one."""

@@ -76,6 +76,14 @@ def test_reruns_are_bit_identical():
     torch.cuda.synchronize()
     assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1]), "decode"
 
+    # the chunk-parallel schedule (few long chains)
+    dp = inputs.prefill_inputs(1, 1100, 4, 128, 128, io="bf16", seed=15, with_S0=True, device=DEV)
+    assert K.chunk_fwd_workspace_size(1, 1100, 4, 128, 128) > 0
+    runs = [K.chunk_fwd(dp["q"], dp["k"], dp["v"], dp["g"], dp["beta"], S0=dp["S0"])
+            for _ in range(2)]
+    torch.cuda.synchronize()
+    assert all(torch.equal(a, b) for a, b in zip(runs[0], runs[1])), "chunk-parallel"
+
     inputs.grad_inputs(d, seed=14, device=DEV)
     g1 = K.backward(d["q"], d["k"], d["v"], d["g"], d["beta"], d["d_out"], S0=d["S0"],
                     dS_final=d["dS_final"])
