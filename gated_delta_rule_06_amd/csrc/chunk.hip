@@ -1800,105 +1800,133 @@ struct ParKernel {
   }
 };
 
-// Stage A: one workgroup per (chain, chunk); blockIdx.x = chain * NC + chunk.
+// Stage A: persistent workgroups, each taking (chain, chunk) records idx =
+// chain * NC + chunk in steps of the grid size; the next record's raw inputs
+// are loaded in three batches while the current one is formed.
 template <class Cfg>
 __global__ __launch_bounds__(Cfg::NTHREADS, 1) void chunk_intra_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, char* __restrict__ ws, int T,
-    int H, int NC, float scale) {
+    int H, int NC, int total, float scale) {
   typedef ChunkKernel<Cfg> K;
   typedef ParLayout<Cfg> L;
+  typedef ParKernel<Cfg> P;
   typedef typename Cfg::Op Op;
   typedef typename Cfg::T OpT;
   extern __shared__ __attribute__((aligned(16))) char smem_[];
   LDS char* smem = (LDS char*)smem_;
-  const int idx = blockIdx.x;
-  const int chain = idx / NC, c = idx % NC;
-  const int b = chain / H, h = chain % H;
-  const size_t row_base = (size_t)b * T + (size_t)c * Cfg::C;
-  const int clen = min(Cfg::C, T - c * Cfg::C);
-  char* rec = ws + (size_t)idx * L::PER_CHUNK;
-  int* flags = reinterpret_cast<int*>(ws + (size_t)gridDim.x * L::PER_CHUNK);
+  int* flags = reinterpret_cast<int*>(ws + (size_t)total * L::PER_CHUNK);
   {
     LDS OpT* AQ = (LDS OpT*)(smem + Cfg::OFF_AQ);   // tiles above the diagonal stay zero
     for (int i = threadIdx.x; i < Cfg::C * Cfg::LD_AQ; i += Cfg::NTHREADS) AQ[i] = Op::cvt(0.f);
   }
+  // record idx -> first token row, head, tokens
+  auto where = [&](int idx, size_t& row0, int& h, int& clen) {
+    const int chain = idx / NC, c = idx % NC;
+    h = chain % H;
+    row0 = (size_t)(chain / H) * T + (size_t)c * Cfg::C;
+    clen = min(Cfg::C, T - c * Cfg::C);
+  };
   const typename K::Offsets offs = K::lane_offsets(H);
-  typename K::Raw raw;
-  K::template load_raw<K::LOAD_ALL>(raw, offs, q, k, v, g, beta, row_base, H, h, clen);
   const Prologue pro{0u, nullptr, nullptr};
-  const int bad = K::prep(raw, smem, scale, pro, 1.f, 0, clen);
   LDS int* FL = (LDS int*)(smem + Cfg::OFF_FL);
   const int w = threadIdx.x >> 6;
-  const int wave_bad = __any(bad);
-  if (lane_fresh() == 0) FL[w] = wave_bad ? 1 : 0;
-  __syncthreads();
-  int any_bad = 0;
+  typename K::Raw raw;
+  size_t row0;
+  int h, clen;
+  where(blockIdx.x, row0, h, clen);
+  K::template load_raw<K::LOAD_ALL>(raw, offs, q, k, v, g, beta, row0, H, h, clen);
+  for (int idx = blockIdx.x; idx < total; idx += gridDim.x) {
+    // the next record (an empty range after the last: nothing is read)
+    const int nidx = idx + gridDim.x;
+    size_t nrow0 = row0;
+    int nh = h, nlen = 0;
+    if (nidx < total) where(nidx, nrow0, nh, nlen);
+    const int bad = K::prep(raw, smem, scale, pro, 1.f, 0, clen);
+    const int wave_bad = __any(bad);
+    if (lane_fresh() == 0) FL[w] = wave_bad ? 1 : 0;
+    compiler_fence();
+    K::template load_raw<K::LOAD_G>(raw, offs, q, k, v, g, beta, nrow0, H, nh, nlen);
+    __syncthreads();
+    int any_bad = 0;
 #pragma unroll
-  for (int i = 0; i < Cfg::NW; ++i) any_bad |= FL[i];
-  if (threadIdx.x == 0) flags[idx] = any_bad;
-  if (any_bad) return;   // the whole workgroup: stage B redoes this chunk token by token
-  ParKernel<Cfg>::tiles(smem);
-  __syncthreads();
-  ParKernel<Cfg>::wy(smem, rec);
-  __syncthreads();
-  ParKernel<Cfg>::write_factors(smem, rec);
+    for (int i = 0; i < Cfg::NW; ++i) any_bad |= FL[i];
+    if (threadIdx.x == 0) flags[idx] = any_bad;
+    // a flagged chunk is redone token by token by stage B
+    K::template load_raw<K::LOAD_V>(raw, offs, q, k, v, g, beta, nrow0, H, nh, nlen);
+    compiler_fence();
+    if (!any_bad) P::tiles(smem);
+    compiler_fence();
+    __syncthreads();
+    K::template load_raw<K::LOAD_Q | K::LOAD_K>(raw, offs, q, k, v, g, beta, nrow0, H, nh, nlen);
+    char* rec = ws + (size_t)idx * L::PER_CHUNK;
+    if (!any_bad) P::wy(smem, rec);
+    __syncthreads();
+    if (!any_bad) P::write_factors(smem, rec);
+    __syncthreads();   // the LDS is free for the next record's prep
+    row0 = nrow0;
+    h = nh;
+    clen = nlen;
+  }
 }
 
-// Stage B: one wave per (chain, 16 value columns); blockIdx.x = chain * NVS + vs.
+// Stage B: one wave per (chain, 16 value columns).
 // The fragments of chunk c + 1 are loaded while chunk c is computed: -W right
 // after its last use, -K_end, U and Gamma_L after the state update.
 template <class Cfg>
 __global__ __launch_bounds__(64, 1) void chunk_scan_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, const float* S0, void* out,
-    float* S_final, char* __restrict__ ws, int T, int H, int NC, float scale) {
+    float* S_final, char* __restrict__ ws, const int* __restrict__ flags, int T, int H, int NC,
+    int n_chains, float scale) {
+  // flags: stage A's per-chunk flags, read-only here (scalar loads: a vector
+  // load would make each step wait for every prefetched factor)
   typedef ChunkKernel<Cfg> K;
   typedef ParLayout<Cfg> L;
   typedef ParKernel<Cfg> P;
   typedef typename Cfg::Op Op;
   constexpr int MTK = Cfg::MTK, NKS = Cfg::NKS, DK = Cfg::DK, DV = Cfg::DV;
-  const int chain = blockIdx.x / L::NVS, vs = blockIdx.x % L::NVS;
+  // Workgroups are dealt to the 8 XCDs round robin (block i on XCD i % 8):
+  // the NVS slices of one chain go to one XCD, so that they share its L2 for
+  // the chain's factors.  Blocks past the last chain have nothing to do.
+  static_assert(L::NVS == 8, "eight value slices per chain");
+  const int xcd = blockIdx.x % 8, r = blockIdx.x / 8;
+  const int chain = (r / L::NVS) * 8 + xcd, vs = r % L::NVS;
+  if (chain >= n_chains) return;
   const int b = chain / H, h = chain % H;
   const int l = lane_fresh();
   const int n = l & 15, g4 = 4 * (l >> 4);
-  const int* flags = reinterpret_cast<const int*>(ws + (size_t)(gridDim.x / L::NVS) * NC * L::PER_CHUNK);
   f32x4 S[MTK][1];
 #pragma unroll
   for (int mt = 0; mt < MTK; ++mt)
 #pragma unroll
     for (int r = 0; r < 4; ++r)
       S[mt][0][r] = S0 ? S0[((size_t)chain * DK + 16 * mt + g4 + r) * DV + 16 * vs + n] : 0.f;
-  typename Op::F32 Wf[4][NKS], Kf[MTK][2];
-  u32x2 Uf[4];
-  f32x4 Gf[MTK];
-  auto load_w = [&](const char* rec) {
-#pragma unroll
-    for (int f = 0; f < 4 * NKS; ++f) Wf[f / NKS][f % NKS] = P::ld16(rec + L::OFF_W + f * L::FR + l * 16);
+  // The factors of one chunk in registers.
+  struct Fac {
+    typename Op::F32 W[4][NKS], K[MTK][2];
+    u32x2 U[4];
+    f32x4 G[MTK];
   };
-  auto load_rest = [&](const char* rec) {
+  auto load_w = [&](Fac& f, const char* rec) {
 #pragma unroll
-    for (int f = 0; f < 2 * MTK; ++f) Kf[f / 2][f % 2] = P::ld16(rec + L::OFF_KE + f * L::FR + l * 16);
-#pragma unroll
-    for (int I = 0; I < 4; ++I) Uf[I] = *reinterpret_cast<const u32x2*>(rec + L::OFF_U + ((vs * 4 + I) * 64 + l) * 8);
-#pragma unroll
-    for (int mt = 0; mt < MTK; ++mt) Gf[mt] = *reinterpret_cast<const f32x4*>(rec + L::OFF_GL + (16 * mt + g4) * 4);
+    for (int i = 0; i < 4 * NKS; ++i) f.W[i / NKS][i % NKS] = P::ld16(rec + L::OFF_W + i * L::FR + l * 16);
   };
-  const char* rec0 = ws + (size_t)chain * NC * L::PER_CHUNK;
-  load_w(rec0);
-  load_rest(rec0);
-  for (int c = 0; c < NC; ++c) {
-    char* rec = ws + ((size_t)chain * NC + c) * L::PER_CHUNK;
-    const char* nrec = ws + ((size_t)chain * NC + (c + 1 < NC ? c + 1 : c)) * L::PER_CHUNK;
-    if (__builtin_amdgcn_readfirstlane(flags[chain * NC + c])) {
-      // outside the chunk-start reference's range: the recurrence token by token
-      const Prologue pro{0u, nullptr, nullptr};
-      K::recurrent_chunk(S, q, k, v, g, beta, out, (size_t)b * T + (size_t)c * Cfg::C, H, h,
-                         min(Cfg::C, T - c * Cfg::C), scale, pro, 1.f, 16 * vs);
-      load_w(nrec);
-      load_rest(nrec);
-      continue;
-    }
+  // in the order of use: U (end of the E products), Gamma_L, -K_end (state update)
+  auto load_rest = [&](Fac& f, const char* rec) {
+#pragma unroll
+    for (int I = 0; I < 4; ++I) f.U[I] = *reinterpret_cast<const u32x2*>(rec + L::OFF_U + ((vs * 4 + I) * 64 + l) * 8);
+#pragma unroll
+    for (int mt = 0; mt < MTK; ++mt) f.G[mt] = *reinterpret_cast<const f32x4*>(rec + L::OFF_GL + (16 * mt + g4) * 4);
+#pragma unroll
+    for (int i = 0; i < 2 * MTK; ++i) f.K[i / 2][i % 2] = P::ld16(rec + L::OFF_KE + i * L::FR + l * 16);
+  };
+  auto rec_of = [&](int c) { return ws + ((size_t)chain * NC + (c < NC ? c : NC - 1)) * L::PER_CHUNK; };
+  // One step of the scan on chunk c from the factors in f; with pf >= 0 the
+  // factors of chunk pf are loaded into f behind it (-W after its last use,
+  // the rest after the state update).
+  auto step = [&](int c, Fac& f, int pf) {
+    char* rec = rec_of(c);
     // S_c as 32-deep operands over keys (also stage C's A operand)
     typename Op::F32 SB[NKS];
 #pragma unroll
@@ -1910,11 +1938,12 @@ __global__ __launch_bounds__(64, 1) void chunk_scan_kernel(
     f32x4 E[4];
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
-      E[I] = Op::unpack(__builtin_bit_cast(typename Op::F16, Uf[I]));
+      E[I] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) E[I] = Op::mma32(Wf[I][ks], SB[ks], E[I]);
+      for (int ks = 0; ks < NKS; ++ks) E[I] = Op::mma32(f.W[I][ks], SB[ks], E[I]);
+      E[I] += Op::unpack(__builtin_bit_cast(typename Op::F16, f.U[I]));
     }
-    load_w(nrec);
+    if (pf >= 0) load_w(f, rec_of(pf));
     // -E as 32-deep operands over tokens
     typename Op::F32 EB[2];
 #pragma unroll
@@ -1925,12 +1954,45 @@ __global__ __launch_bounds__(64, 1) void chunk_scan_kernel(
     // S <- Diag(Gamma_L) S + (-K_end)^T (-E)
 #pragma unroll
     for (int mt = 0; mt < MTK; ++mt) {
-      f32x4 s = S[mt][0] * Gf[mt];
+      f32x4 s = S[mt][0] * f.G[mt];
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) s = Op::mma32(Kf[mt][kt], EB[kt], s);
+      for (int kt = 0; kt < 2; ++kt) s = Op::mma32(f.K[mt][kt], EB[kt], s);
       S[mt][0] = s;
     }
-    load_rest(nrec);
+    if (pf >= 0) load_rest(f, rec_of(pf));
+  };
+  // Chunks stage A flagged are redone token by token; a chain without any
+  // runs a loop with no branch inside, two chunks of factors in flight (so
+  // that the loads stay where they are issued, a chunk ahead of their use).
+  int any_flag = 0;
+  for (int c = 0; c < NC; ++c) any_flag |= flags[chain * NC + c];
+  if (!any_flag) {
+    Fac fa, fb;
+    load_w(fa, rec_of(0));
+    load_rest(fa, rec_of(0));
+    load_w(fb, rec_of(1));
+    load_rest(fb, rec_of(1));
+    int c = 0;
+    for (; c + 1 < NC; c += 2) {
+      step(c, fa, c + 2);
+      step(c + 1, fb, c + 3);
+    }
+    if (c < NC) step(c, fa, -1);
+  } else {
+    // (rare) without prefetching
+    Fac fa;
+    for (int c = 0; c < NC; ++c) {
+      if (flags[chain * NC + c]) {
+        // outside the chunk-start reference's range: the recurrence token by token
+        const Prologue pro{0u, nullptr, nullptr};
+        K::recurrent_chunk(S, q, k, v, g, beta, out, (size_t)b * T + (size_t)c * Cfg::C, H, h,
+                           min(Cfg::C, T - c * Cfg::C), scale, pro, 1.f, 16 * vs);
+      } else {
+        load_w(fa, rec_of(c));
+        load_rest(fa, rec_of(c));
+        step(c, fa, -1);
+      }
+    }
   }
   if (S_final) {
 #pragma unroll
@@ -2007,10 +2069,19 @@ hipError_t launch_chunk_par(const void* q, const void* k, const void* v, const f
   auto ka = chunk_intra_kernel<Cfg>;
   hipError_t e = hipFuncSetAttribute((const void*)ka, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(ka, dim3(chains * NC), dim3(Cfg::NTHREADS), bytes, stream, q, k, v, g, beta,
-                     (char*)ws, T, H, NC, scale);
-  hipLaunchKernelGGL(chunk_scan_kernel<Cfg>, dim3(chains * L::NVS), dim3(64), 0, stream, q, k, v,
-                     g, beta, S0, out, S_final, (char*)ws, T, H, NC, scale);
+  // one persistent workgroup per CU (the LDS holds one)
+  int dev = 0, cus = 0;
+  e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  const int total = chains * NC;
+  const int grid_a = total < cus ? total : cus;
+  hipLaunchKernelGGL(ka, dim3(grid_a), dim3(Cfg::NTHREADS), bytes, stream, q, k, v, g, beta,
+                     (char*)ws, T, H, NC, total, scale);
+  const int* flags = reinterpret_cast<const int*>((char*)ws + (size_t)chains * NC * L::PER_CHUNK);
+  const int grid_b = (chains + 7) / 8 * 8 * L::NVS;
+  hipLaunchKernelGGL(chunk_scan_kernel<Cfg>, dim3(grid_b), dim3(64), 0, stream, q, k, v, g, beta,
+                     S0, out, S_final, (char*)ws, flags, T, H, NC, chains, scale);
   hipLaunchKernelGGL(chunk_out_kernel<Cfg>, dim3(chains * NC), dim3(Cfg::NTHREADS), 0, stream, out,
                      (const char*)ws, T, H, NC);
   return hipGetLastError();

@@ -9,7 +9,7 @@
 // The chunk-parallel prefill schedule is taken for at most this many
 // (sequence, head) chains of at least KDA_PAR_MIN_T tokens each (bf16,
 // d_k = d_v = 128), while its workspace stays within KDA_PAR_MAX_WS bytes.
-#define KDA_PAR_MAX_CHAINS 128
+#define KDA_PAR_MAX_CHAINS 64
 #define KDA_PAR_MIN_T 512
 #define KDA_PAR_MAX_WS ((size_t)8 << 30)
 
