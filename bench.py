@@ -289,6 +289,24 @@ def main():
         % (ms_per_step, avg_kernel_ms, min(kern_ms), value, achieved))
     log("prefill launch ms, warm-up:", " ".join("%.3f" % a.elapsed_time(b) for a, b in warm_ev))
     log("prefill launch ms, timed:", " ".join("%.3f" % x for x in kern_ms))
+
+    # ---------------------------------------------------------------- fast-forgetting channels
+    # The same workload with 8 of the 128 key channels of every head redrawn
+    # at log alpha ~ U[-5, -2] per token (up to e^-320 over a chunk).
+    inputs.strong_gate_channels(d, 8, -5.0, -2.0, seed=0)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs_s = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(args.steps)]
+    for a, b in evs_s:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    sg_ms = float(np.mean([a.elapsed_time(b) for a, b in evs_s]))
+    log("prefill, 8 of 128 channels at log alpha ~ U[-5,-2]: kernel %.3f ms avg (%.3f x the "
+        "plain inputs)" % (sg_ms, sg_ms / avg_kernel_ms))
     del d
     torch.cuda.empty_cache()
 
@@ -490,6 +508,10 @@ def main():
                                 "traffic": measured_traffic("decode", "decode.hip"),
                                 "alg_bytes_per_launch": dec_b,
                                 "avg_launch_ms": dec_kernel_ms}},
+        "strong_gate_prefill": {"workload": "prefill_b8_h32_t8192, 8 of 128 key channels per "
+                                            "head at log_alpha ~ U[-5,-2]",
+                                "avg_launch_ms": sg_ms, "vs_plain": sg_ms / avg_kernel_ms,
+                                "tokens_per_s": tokens / (sg_ms * 1e-3)},
         "gdn_prefill": {"workload": "gated_deltanet_prefill_b8_h32_t8192",
                         "tokens_per_s": tokens / gdn_wall, "ms_per_step": gdn_wall * 1e3,
                         "roofline": {"bound": "hbm", "achieved": gdn_gbs, "peak": HBM_PEAK_GBS,

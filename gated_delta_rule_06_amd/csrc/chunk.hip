@@ -5,24 +5,33 @@
 // decay multiplies key rows).  For one chunk of C = 64 tokens with incoming
 // state S_c, let Gamma_i = prod_{m<=i} alpha_m (chunk-local cumulative decay,
 // section 6.1/6.6 -- kept as a running product instead of exp of a prefix
-// sum), Gamma_L the decay over the whole chunk, and
-//
-//   QG_i = s q_i * Gamma_i          KG_i = k_i * Gamma_i
-//   KI_i = k_i / Gamma_i
-//
-// (products per key channel).  Then (section 6.3) R = Diag(beta)
-// strict_tril(KG KI^T) holds rho_ij = beta_i <k_j, D_{j+1:i} k_i>, (section
-// 6.5) Aqk = tril(QG KI^T) holds chi_ij, the provisional errors of section 6.2
-// are Ebar = Diag(beta) (V - KG S_c), and the resolved errors are
+// sum) and Gamma_L the decay over the whole chunk.  Then (section 6.3)
+// R = Diag(beta) strict_tril(K_i Gamma_i / Gamma_j K_j^T) holds rho_ij =
+// beta_i <k_j, D_{j+1:i} k_i>, (section 6.5) Aqk = tril(s Q_i Gamma_i /
+// Gamma_j K_j^T) holds chi_ij, the provisional errors of section 6.2 are
+// Ebar = Diag(beta) (V - (K Gamma) S_c), and the resolved errors are
 // E = (I + R)^{-1} Ebar (the causal triangular solve of section 6.3).  beta
 // scales whole rows, so it is applied to the R tiles and to Y rather than to
 // the stored operands.  Finally (6.4, 6.5)
 //
-//   O_c     = QG S_c + Aqk E
-//   S_{c+1} = Diag(Gamma_L) (S_c + KI^T E)
+//   O_c     = (s Q Gamma) S_c + Aqk E
+//   S_{c+1} = Diag(Gamma_L) S_c + K_end^T E,   K_end_i = k_i Gamma_L / Gamma_i.
 //
-// (the second line is Diag(Gamma_L) S_c + K_end^T E with K_end = k Gamma_L /
-// Gamma row-wise, so K_end is never formed).
+// Decay references (KDA, one gate per key channel): every per-token factor
+// is taken relative to the start of its token's 16-token block b, Pi_i =
+// Gamma_i / Gamma_{16b-1}, and the chunk's stored operands are
+//
+//   QG_i = s q_i Pi_i      KG_i = k_i Pi_i      KI_i = k_i / Pi_i
+//   K_end_i = k_i TQ_b / Pi_i           (TQ_b = T_b T_{b+1} .. T_3)
+//
+// with T_b the decay over block b.  The rest of each ratio is a product over
+// whole blocks, per key channel: a tile across blocks I > J takes F_IJ =
+// T_J .. T_{I-1} on its KI fragments, and block I's state products take P_I =
+// T_0 .. T_{I-1} on the rows of S.  Inside one block Pi stays within
+// [T_b, 1], so the operands stay in range however much the chunk decays as a
+// whole; only a block decaying below 2^-120 in some channel (log alpha
+// averaging below about -5.2 over 16 tokens) is beyond this, and that chunk
+// runs the recurrence token by token on the same on-chip state instead.
 //
 // Design (one workgroup per (sequence, head) chain, all of d_v; 8 waves -- two
 // per SIMD -- for d_v = 128, 4 for d_v = 64):
@@ -42,10 +51,6 @@
 //    so that the solve yields -E directly and no extra negation is needed;
 //  * the next chunk's inputs are loaded into registers while this chunk is
 //    computed, in three batches spread over the phases.
-//  * Exactness guard: the single chunk-start reference of KI = k / Gamma needs
-//    Gamma_L >= 2^-100 in every key channel.  A chunk that decays more than
-//    that in any channel is processed token by token (the recurrence itself)
-//    on the same on-chip state instead; outputs are identical up to rounding.
 #include "common.h"
 
 namespace kda {
@@ -61,31 +66,6 @@ __device__ __forceinline__ float dpp1(float x) {
 // x of lane l - D inside the lane's 16-lane row (1 for the first D lanes)
 template <int D>
 __device__ __forceinline__ float dpp_row_shr(float x) { return dpp1<0x110 + D, 0xf>(x); }
-// x of lane l - 1 across the whole wave (1 for lane 0)
-__device__ __forceinline__ float dpp_wave_shr1(float x) { return dpp1<0x138, 0xf>(x); }
-// x of the last lane (15) of the previous row, into rows 1 and 3 (others 1)
-__device__ __forceinline__ float dpp_bcast15(float x) { return dpp1<0x142, 0xa>(x); }
-// x of lane 31, into rows 2 and 3 (others 1)
-__device__ __forceinline__ float dpp_bcast31(float x) { return dpp1<0x143, 0xc>(x); }
-
-// Inclusive product scan over the lanes of one parity (lane = 2 t + p,
-// p = this lane's parity): in-row shifts by 2, 4, 8, then the rows' totals
-// (lanes 16r + 14 + p) carried into the later rows -- lane 14 is first moved
-// to lane 15 for the even lanes, since the row broadcasts take lane 15/31.
-__device__ __forceinline__ float scan_stride2(float x, int p) {
-  x *= dpp_row_shr<2>(x);
-  x *= dpp_row_shr<4>(x);
-  x *= dpp_row_shr<8>(x);
-  {
-    const float odd = dpp_bcast15(x), even = dpp_bcast15(dpp_row_shr<1>(x));
-    x *= p ? odd : even;
-  }
-  {
-    const float odd = dpp_bcast31(x), even = dpp_bcast31(dpp_row_shr<1>(x));
-    x *= p ? odd : even;
-  }
-  return x;
-}
 
 // ============================================================ operand policies
 typedef short i16x8 __attribute__((ext_vector_type(8)));
@@ -155,6 +135,16 @@ __device__ __forceinline__ void buf_store16(__amdgpu_buffer_rsrc_t r, uint32_t o
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), r, off, 0, 0);
 }
 
+// The k order of a 32-deep operand fragment: inside every block of 32
+// indices, position 8g + e holds index 4g + e and position 8g + 4 + e holds
+// index 16 + 4g + e (g, e < 4).  Lane group g of a fragment over k0 .. k0+31
+// holds exactly the indices at positions k0 + 8g .. k0 + 8g + 7, and any four
+// consecutive indices starting at a multiple of 4 stay contiguous.
+__device__ __forceinline__ int frag_pos(int c) {
+  const int r = c & 31;
+  return (c & ~31) + 8 * ((r & 15) >> 2) + ((r & 16) >> 2) + (r & 3);
+}
+
 // bf16 operands, fp32 accumulation: v_mfma_f32_16x16x32_bf16 / 16x16x16_bf16.
 struct OpBf16 {
   typedef uint16_t T;
@@ -207,16 +197,11 @@ struct OpBf16 {
   static __device__ __forceinline__ F32 ld32_tr(int l, const LDS T* X, int ld, int k0, int m0) {
     return F32{ld16_tr(l, X, ld, k0, m0), ld16_tr(l, X, ld, k0 + 16, m0)};
   }
-  // Permuted buffers (QG, KG, -KI over key channels, the key-major -KI over
-  // tokens): inside every block of 32 indices, position 8g + e holds index
-  // 4g + e and position 8g + 4 + e holds index 16 + 4g + e (g, e < 4) -- the
-  // k order of a 32-deep operand -- so that one 16-byte read gives a lane both
-  // halves of its fragment.
+  // Permuted buffers (the operands over key channels, the key-major -K_end
+  // over tokens) are stored in fragment order (frag_pos), so that one 16-byte
+  // read gives a lane both halves of its fragment.
   static constexpr bool PERMUTED = true;
-  static __device__ __forceinline__ int perm_pos(int c) {
-    const int r = c & 31;
-    return (c & ~31) + 8 * ((r & 15) >> 2) + ((r & 16) >> 2) + (r & 3);
-  }
+  static __device__ __forceinline__ int perm_pos(int c) { return frag_pos(c); }
   static __device__ __forceinline__ F32 ld32_rmp(int l, const LDS T* X, int ld, int row0, int k0) {
     const i16x8 v = *lds_ptr<const i16x8>(X + (row0 + (l & 15)) * ld + k0 + 8 * (l >> 4));
     return F32{__builtin_shufflevector(v, v, 0, 1, 2, 3), __builtin_shufflevector(v, v, 4, 5, 6, 7)};
@@ -386,12 +371,17 @@ struct ChunkCfg {
   static constexpr int OFF_TD = OFF_RT + C * LD_RR * SZ;
   static constexpr int LD_KT = C + Op::PAD_B128;  // KIT [DK][LD_KT]
   static constexpr int OFF_KT = OFF_TD + NB * 16 * 16 * SZ;
-  // per-wave block for the decay scan (two lanes per token group, 16 key
-  // channels per wave): 16 channel rows of 32 group totals (padded)
-  static constexpr int SC_LD = 36;
-  static constexpr int OFF_SC = OFF_KT + DK * LD_KT * SZ;
-  static constexpr int SZ_SC = (CQ == 2 && DK / NW == 16) ? NW * 16 * SC_LD * 4 : 0;
-  static constexpr int OFF_GL = OFF_SC + SZ_SC;
+  // KDA decay factors per key channel, fp32 in fragment order (frag_pos):
+  // [4][DK] the block totals T_b (each wave's own channels, read back only by
+  // that wave); [4][DK] the state factors of the block-referenced channels
+  // (P_b = T_0 .. T_{b-1}, else 1); [6][DK] their tile factors F_IJ =
+  // T_J .. T_{I-1} (else 1) of the pairs I > J in the order (1,0) (2,0)
+  // (2,1) (3,0) (3,1) (3,2)
+  static constexpr int OFF_DT = OFF_KT + DK * LD_KT * SZ;
+  static constexpr int OFF_DP = OFF_DT + 4 * DK * 4;
+  static constexpr int OFF_DF = OFF_DP + 4 * DK * 4;
+  static constexpr int SZ_D = SG ? 0 : 14 * DK * 4;
+  static constexpr int OFF_GL = OFF_DT + SZ_D;
   static constexpr int OFF_BT = OFF_GL + DK * 4;          // beta of the chunk's tokens
   static constexpr int OFF_FL = OFF_BT + C * 4;
   // FU only: per-wave partial squared norms of q and k, [C][NW] each, and the
@@ -407,13 +397,15 @@ struct ChunkCfg {
   static_assert(LDS_TOTAL >= (KDA_LPT_MAX + 1) * 4, "LDS holds the length ranking");
   static_assert(OFF_KG % 16 == 0 && OFF_KI % 16 == 0 && OFF_RD % 16 == 0 && OFF_OS % 16 == 0 && OFF_FL % 16 == 0 &&
                 OFF_BV % 16 == 0 && OFF_AQ % 16 == 0 && OFF_RT % 16 == 0 && OFF_TD % 16 == 0 &&
-                OFF_GL % 16 == 0 && OFF_BT % 16 == 0 && OFF_KT % 16 == 0 && OFF_SC % 16 == 0 && (LD_K * SZ) % 16 == 0 &&
+                OFF_GL % 16 == 0 && OFF_BT % 16 == 0 && OFF_KT % 16 == 0 && OFF_DT % 16 == 0 && (LD_K * SZ) % 16 == 0 &&
                 (LD_KT * SZ) % 16 == 0 && (LD_V * SZ) % 16 == 0 && (LD_AQ * SZ) % 16 == 0 &&
                 (LD_RR * SZ) % 8 == 0 && (LD_OS * SZ) % 16 == 0, "LDS alignment");
 };
 
-// Threshold below which a channel's chunk decay Gamma_L makes k / Gamma unsafe.
-#define KDA_GAMMA_MIN 7.888609052210118e-31f /* 2^-100 */
+// Threshold below which a 16-token block's decay T_b makes k / Pi unsafe
+// (Pi >= T_b inside the block, so 1 / Pi stays below 2^120).  With the gate
+// transform, log alpha >= -5 per token keeps every block above 2^-115.5.
+#define KDA_BLOCK_DECAY_MIN 7.52316384526264e-37f /* 2^-120 */
 
 // ============================================================ the kernel
 template <class Cfg>
@@ -533,26 +525,6 @@ struct ChunkKernel {
     }
   }
 
-  // ---------------------------------------------------------------- windows
-  // Zero the raw inputs of the tokens outside [lo, hi): they become identity
-  // tokens (q = k = v = 0, alpha = 1, beta = 0).
-  static __device__ __forceinline__ void mask_window(Raw& r, int lo, int hi) {
-    const int l = lane_fresh();
-    const int tg = l / CQ;
-#pragma unroll
-    for (int t = 0; t < TPL; ++t) {
-      const int i = TPL * tg + t;
-      if (i < lo || i >= hi) {
-        r.q[t].w.zero();
-        r.k[t].w.zero();
-        r.v[t].w.zero();
-        r.g[t].zero();
-        r.gs[t] = 0.f;
-      }
-    }
-    if (l < lo || l >= hi) r.beta = 0.f;   // lane l holds beta of token l
-  }
-
   // ---------------------------------------------------------------- raw operands (SG)
   // 8 consecutive channels of one row straight from the raw words (the I/O
   // type is the operand type), sign bits XOR-ed with `sign`.
@@ -587,7 +559,7 @@ struct ChunkKernel {
   // sums over the whole chunk.
   enum { SV_G = 0, SV_RQ = 1, SV_RK = 2, SV_BK = 3, SV_FY = 4, SV_FO = 5, SV_FS = 6, SV_T = 7 };
   static __device__ __forceinline__ void prep_sg(const Raw& r, LDS char* smem, float scale,
-                                                 const Prologue& pro, float ea, int lo, int hi) {
+                                                 const Prologue& pro, float ea, int hi) {
     const int w = threadIdx.x >> 6, l = lane_fresh();
     const int tg = l / CQ, cq = l % CQ;
     const int kc0 = w * (DK / NW) + CPL * cq;
@@ -606,14 +578,13 @@ struct ChunkKernel {
     // gamma of the lane's tokens: a running sum over its TPL tokens, an
     // inclusive scan of the group sums over the lanes cq + CQ tg within each
     // 16-token block (segments of GPB groups), then one group back.  Rows
-    // outside [lo, hi) keep log alpha = 0 under the gate transform (identity
-    // tokens).
+    // past hi keep log alpha = 0 under the gate transform (identity tokens).
     const bool xg = Cfg::FU && (pro.flags & PRO_GATE);
     const float gb = xg ? ((const LDS float*)(smem + Cfg::OFF_NM + 2 * C * NW * 4))[0] : 0.f;
     float gam[TPL];
 #pragma unroll
     for (int t = 0; t < TPL; ++t) {
-      const bool real = TPL * tg + t >= lo && TPL * tg + t < hi;
+      const bool real = TPL * tg + t < hi;
       const float la = xg ? (real ? gate_logalpha(r.gs[t], ea, gb) : 0.f) : r.gs[t];
       gam[t] = (t == 0 ? 0.f : gam[t - 1]) + la * LOG2E;
     }
@@ -706,18 +677,47 @@ struct ChunkKernel {
   }
 
   // ---------------------------------------------------------------- prep
-  // Cumulative decay and the five gate-scaled operands; returns the chunk's
-  // guard flag (1 = some channel decays below KDA_GAMMA_MIN).
-  static __device__ __forceinline__ int prep(const Raw& r, LDS char* smem, float scale,
-                                             const Prologue& pro, float ea, int lo, int hi) {
-    if constexpr (Cfg::SG) {
-      prep_sg(r, smem, scale, pro, ea, lo, hi);
-      return 0;
+  // Inclusive product scan over the lanes of one cq inside a 16-lane DPP row
+  // (stride CQ): the token groups of one 16-token block.
+  template <int D>
+  static __device__ __forceinline__ float row_scan(float x) {
+    if constexpr (D < 16) {
+      x *= dpp_row_shr<D>(x);
+      return row_scan<2 * D>(x);
+    } else {
+      return x;
     }
+  }
+
+  // KDA: the decay factors and the gate-scaled operands of one chunk (tokens
+  // [0, hi) real, the rest identity tokens), "Kimi Unveils Delta Attention
+  // and K3 Architecture Updates", section 6.1 (cumulative decay) and 6.6.
+  // Each wave picks the reference point of its key channels' factors:
+  //  * chunk start (the common case): QG_i = s q_i Gamma_i, KG_i = k_i
+  //    Gamma_i, KI_i = -k_i / Gamma_i.  Safe while Gamma_L >= 2^-100, which
+  //    holds when every 16-token block decays by at most 2^-25;
+  //  * block start, when some block of some channel of the wave decays more:
+  //    Pi_i = Gamma_i / Gamma_{16b-1} (b the token's 16-token block) in place
+  //    of Gamma_i.  Pi stays within [T_b, 1] (T_b the block's decay), so the
+  //    operands stay in range however much the chunk decays as a whole; the
+  //    rest of each ratio is a product over whole blocks, which the tiles
+  //    (F_IJ) and the state products (P_b) apply per channel.
+  // KIT = -K_end^T, K_end_i = k_i Gamma_L / Gamma_i, in either form.  Returns
+  // (wave-uniform) bit 0: some block decays below KDA_BLOCK_DECAY_MIN, past
+  // what the block-start reference can scale; bit 1: block-start references.
+  static __device__ __forceinline__ int prep(const Raw& r, LDS char* smem, float scale,
+                                             const Prologue& pro, float ea, int hi) {
+    if constexpr (Cfg::SG) {
+      prep_sg(r, smem, scale, pro, ea, hi);
+      return 0;
+    } else {
     const int w = threadIdx.x >> 6, l = lane_fresh();
     const int tg = l / CQ, cq = l % CQ;
     const int kc0 = w * (DK / NW) + CPL * cq;
     const int vc0 = w * VW + VPL * cq;
+    constexpr int GPB = 16 / TPL;               // token groups per 16-token block
+    static_assert(CQ == TPL && CQ * GPB == 16, "a 16-token block is one 16-lane row");
+    const int blk = tg / GPB;
     LDS T* QG = (LDS T*)(smem + Cfg::OFF_QG);
     LDS T* KG = (LDS T*)(smem + Cfg::OFF_KG);
     LDS T* KI = (LDS T*)(smem + Cfg::OFF_KI);
@@ -725,16 +725,18 @@ struct ChunkKernel {
     LDS T* KIT = (LDS T*)(smem + Cfg::OFF_KT);
     LDS float* GL = (LDS float*)(smem + Cfg::OFF_GL);
     LDS float* BT = (LDS float*)(smem + Cfg::OFF_BT);
+    LDS float* DT = (LDS float*)(smem + Cfg::OFF_DT);
+    LDS float* DP = (LDS float*)(smem + Cfg::OFF_DP);
+    LDS float* DF = (LDS float*)(smem + Cfg::OFF_DF);
 
     // beta is applied to R and Y later, where it scales whole rows (R =
-    // Diag(beta) strict_tril((k Gamma) KI^T), Ebar = Diag(beta)(v - (k Gamma) S))
+    // Diag(beta) strict_tril(...), Ebar = Diag(beta)(v - (k Gamma) S))
     if (w == 0) {                               // lane l holds beta of token l
       BT[l] = (Cfg::FU && (pro.flags & PRO_BETA_SIGMOID)) ? sigmoid_f(r.beta) : r.beta;
     }
     // gate transform (FU): the raw gate through -5 sigmoid(exp(A_log) (g + bias)).
-    // Rows outside [lo, hi) (past the chunk's end, or outside a window) read
-    // as zeros and must stay identity tokens (alpha = 1), so the transform
-    // leaves their gate at 0.
+    // Rows past hi read as zeros and must stay identity tokens (alpha = 1),
+    // so the transform leaves their gate at 0.
     const bool xg = Cfg::FU && (pro.flags & PRO_GATE);
     float gbias[CPL];
     if (xg) {
@@ -744,88 +746,58 @@ struct ChunkKernel {
       gbias[4] = b1[0]; gbias[5] = b1[1]; gbias[6] = b1[2]; gbias[7] = b1[3];
     }
 
-    float cp[TPL][CPL];   // in-lane running products of alpha over the lane's tokens
-    float ex[CPL];        // product over the earlier token groups (exclusive prefix)
-    int bad = 0;
-    {
+    // Pi of the lane's tokens: running products over its TPL tokens, then a
+    // product scan over the block's token groups (one DPP row) and one group
+    // back; the block's last group holds T_b.
+    float cp[TPL][CPL];
 #pragma unroll
-      for (int t = 0; t < TPL; ++t)
+    for (int t = 0; t < TPL; ++t)
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-          const float gr = __uint_as_float(r.g[t].word(c));
-          const bool real = TPL * tg + t >= lo && TPL * tg + t < hi;
-          const float a = __expf(xg ? (real ? gate_logalpha(gr, ea, gbias[c]) : 0.f) : gr);
-          cp[t][c] = (t == 0) ? a : cp[t - 1][c] * a;
-        }
-      // product over the TG token groups: ex = exclusive prefix, Gamma_L -> GL
-      if (Cfg::SZ_SC > 0) {
-        // Two lanes per token group (lane = 2 tg + cq, 16 channels per wave).
-        // The group totals go through a wave-private LDS block, transposed to
-        // X[channel][group]; there lane 4 ch + qq takes groups 8 qq .. 8 qq + 7
-        // of channel ch: a running product over its eight groups, then an
-        // exclusive product scan over the four lanes of the quad (DPP quad
-        // permutations; the first lane of each quad holds 1, so lanes that
-        // read it are unaffected).  A wave's LDS accesses complete in order.
-        LDS float* X = (LDS float*)(smem + Cfg::OFF_SC) + w * 16 * Cfg::SC_LD;
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) X[(8 * cq + c) * Cfg::SC_LD + tg] = cp[TPL - 1][c];
-        __asm__ __volatile__("" ::: "memory");
-        const int ch = l >> 2, qq = l & 3;
-        LDS float* xr = X + ch * Cfg::SC_LD + 8 * qq;
-        const f32x4 v0 = *lds_ptr<const f32x4>(xr), v1 = *lds_ptr<const f32x4>(xr + 4);
-        const float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-        float e[8];
-        e[0] = 1.f;
-#pragma unroll
-        for (int m = 1; m < 8; ++m) e[m] = e[m - 1] * v[m - 1];
-        const float tq = e[7] * v[7];                       // this quarter's product
-        float z = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(tq), 0x90, 0xf, 0xf, false));
-        z = (qq == 0) ? 1.f : z;                            // quad_perm [0,0,1,2]: the previous lane
-        z *= __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(z), 0x90, 0xf, 0xf, false));
-        z *= __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(z), 0x40, 0xf, 0xf, false));
-        *lds_ptr<f32x4>(xr) = f32x4{z * e[0], z * e[1], z * e[2], z * e[3]};
-        *lds_ptr<f32x4>(xr + 4) = f32x4{z * e[4], z * e[5], z * e[6], z * e[7]};
-        if (qq == 3) {
-          const float gl = z * tq;                          // Gamma_L of channel ch
-          GL[w * 16 + ch] = gl;
-          bad = !(gl >= KDA_GAMMA_MIN);
-        }
-        __asm__ __volatile__("" ::: "memory");
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) ex[c] = X[(8 * cq + c) * Cfg::SC_LD + tg];
-      } else {
-        // inclusive scan over the lanes cq + CQ tg, then shift by one group
-        float tot[CPL];
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-          float x = cp[TPL - 1][c];
-#pragma unroll
-          for (int d = CQ; d < 64; d <<= 1) {
-            const float y = __shfl_up(x, d);
-            if (l >= d) x *= y;
-          }
-          tot[c] = __shfl(x, 64 - CQ + cq);     // Gamma_L
-          const float y = __shfl_up(x, CQ);
-          ex[c] = (l >= CQ) ? y : 1.f;
-        }
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) bad |= !(tot[c] >= KDA_GAMMA_MIN);
-        if (tg == 0) {
-          *lds_ptr<f32x4>(GL + kc0) = f32x4{tot[0], tot[1], tot[2], tot[3]};
-          *lds_ptr<f32x4>(GL + kc0 + 4) = f32x4{tot[4], tot[5], tot[6], tot[7]};
-        }
+      for (int c = 0; c < CPL; ++c) {
+        const float gr = __uint_as_float(r.g[t].word(c));
+        const bool real = TPL * tg + t < hi;
+        const float a = __expf(xg ? (real ? gate_logalpha(gr, ea, gbias[c]) : 0.f) : gr);
+        cp[t][c] = (t == 0) ? a : cp[t - 1][c] * a;
       }
+    float ex[CPL], tb[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      tb[c] = row_scan<CQ>(cp[TPL - 1][c]);
+      ex[c] = dpp_row_shr<CQ>(tb[c]);
     }
-    // -KI of the lane's tokens per key channel, for the key-major copy
-    constexpr bool KIT_PAIRS = Cfg::SZ == 2 && TPL == 2;
-    T kit[CPL][TPL];
-    float kif[CPL][TPL];
+    if (tg % GPB == GPB - 1) {
+      *lds_ptr<f32x4>(DT + blk * DK + frag_pos(kc0)) = f32x4{tb[0], tb[1], tb[2], tb[3]};
+      *lds_ptr<f32x4>(DT + blk * DK + frag_pos(kc0 + 4)) = f32x4{tb[4], tb[5], tb[6], tb[7]};
+    }
+    // Every partial product is at least its block's total, so the wave's
+    // minimum over them is its minimum over the T_b.
+    bool weak = false, gone = false;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      weak |= !(tb[c] >= 2.98023223876953125e-08f);       // 2^-25
+      gone |= !(tb[c] >= KDA_BLOCK_DECAY_MIN);
+    }
+    const bool blockref = __any(weak), bad = __any(gone);
+    __asm__ __volatile__("" ::: "memory");
+
+    // The four block totals of the lane's channels, read back while the work
+    // that needs no decay factor goes on (a wave's LDS accesses complete in
+    // order; each wave reads back only its own channels).
+    f32x4 tx[4], ty[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      tx[b] = *lds_ptr<const f32x4>(DT + b * DK + frag_pos(kc0));
+      ty[b] = *lds_ptr<const f32x4>(DT + b * DK + frag_pos(kc0 + 4));
+    }
+    __asm__ __volatile__("" ::: "memory");
+    // -v, and q and k unpacked (and L2-normalised)
+    float qv[TPL][CPL], kv[TPL][CPL];
 #pragma unroll
     for (int t = 0; t < TPL; ++t) {
       const int i = TPL * tg + t;
-      float qv[CPL], kv[CPL];
-      r.q[t].unpack(qv);
-      r.k[t].unpack(kv);
+      st_neg(BV + i * Cfg::LD_V + vc0, r.v[t]);     // -v, exactly: the sign bits flipped
+      r.q[t].unpack(qv[t]);
+      r.k[t].unpack(kv[t]);
       if (Cfg::FU && (pro.flags & PRO_L2NORM)) {
         // the token's squared norms: the sum of the waves' partials
         const LDS float* NQ = (const LDS float*)(smem + Cfg::OFF_NM) + i * NW;
@@ -841,24 +813,95 @@ struct ChunkKernel {
         const float rk = __builtin_amdgcn_rsqf(sk + PRO_NORM_EPS);
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
-          qv[c] *= rq;
-          kv[c] *= rk;
+          qv[t][c] *= rq;
+          kv[t][c] *= rk;
         }
       }
-      float qg[CPL], kg[CPL];
+    }
+    float tt[4][CPL];
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        tt[b][c] = tx[b][c];
+        tt[b][c + 4] = ty[b][c];
+      }
+    // Per channel: fa takes Pi to the operands' reference (P_b, or 1), fm
+    // takes -k / (that reference) to -K_end (Gamma_L, or TQ_b = T_b .. T_3).
+    // Lane-dependent choices are products of selects against 1.
+    const bool b1 = blk >= 1, b2 = blk >= 2, b3 = blk == 3;
+    float fa[CPL], fm[CPL], pb[CPL], gl[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      pb[c] = (b1 ? tt[0][c] : 1.f) * (b2 ? tt[1][c] : 1.f) * (b3 ? tt[2][c] : 1.f);
+      gl[c] = (tt[0][c] * tt[1][c]) * (tt[2][c] * tt[3][c]);
+    }
+    if (blockref) {
 #pragma unroll
       for (int c = 0; c < CPL; ++c) {
-        const float gam = ex[c] * cp[t][c];
+        fa[c] = 1.f;
+        fm[c] = (b1 ? 1.f : tt[0][c]) * (b2 ? 1.f : tt[1][c]) * (b3 ? 1.f : tt[2][c]) * tt[3][c];
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        fa[c] = pb[c];
+        fm[c] = gl[c];
+      }
+    }
+    // The first token group of each block writes the block's factors for the
+    // other waves: Gamma_L (block 0), and for block-referenced channels P_b
+    // and the F_IJ with I = b (1 for chunk-referenced channels).
+    if (tg % GPB == 0) {
+      auto st8 = [&](LDS float* row, const float (&x)[CPL]) {
+        *lds_ptr<f32x4>(row + frag_pos(kc0)) = f32x4{x[0], x[1], x[2], x[3]};
+        *lds_ptr<f32x4>(row + frag_pos(kc0 + 4)) = f32x4{x[4], x[5], x[6], x[7]};
+      };
+      if (blk == 0) {
+        *lds_ptr<f32x4>(GL + kc0) = f32x4{gl[0], gl[1], gl[2], gl[3]};
+        *lds_ptr<f32x4>(GL + kc0 + 4) = f32x4{gl[4], gl[5], gl[6], gl[7]};
+      } else {
+        // F_{b, b-1} = T_{b-1}, F_{b, b-2} = T_{b-2} T_{b-1}, F_{3,0} = T_0 T_1 T_2
+        float f1[CPL], f2[CPL], f3[CPL], p[CPL];
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+          const float bm1 = b3 ? tt[2][c] : (b2 ? tt[1][c] : tt[0][c]);
+          const float bm2 = b3 ? tt[1][c] : tt[0][c];
+          f1[c] = blockref ? bm1 : 1.f;
+          f2[c] = blockref ? bm2 * bm1 : 1.f;
+          f3[c] = blockref ? tt[0][c] * tt[1][c] * tt[2][c] : 1.f;
+          p[c] = blockref ? pb[c] : 1.f;
+        }
+        const int pbase = blk * (blk - 1) / 2;           // pair (b, 0)
+        st8(DP + blk * DK, p);
+        st8(DF + (pbase + blk - 1) * DK, f1);
+        if (b2) st8(DF + (pbase + blk - 2) * DK, f2);
+        if (b3) st8(DF + pbase * DK, f3);
+      }
+    }
+
+    // the operands; -K_end of the lane's tokens per key channel for the
+    // key-major copy
+    constexpr bool KIT_PAIRS = Cfg::SZ == 2 && TPL == 2;
+    T kit[CPL][TPL];
+    float kef[CPL][TPL];
+#pragma unroll
+    for (int t = 0; t < TPL; ++t) {
+      const int i = TPL * tg + t;
+      float qg[CPL], kg[CPL], ki[CPL];
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        const float gam = ex[c] * cp[t][c] * fa[c];
         const float inv = __builtin_amdgcn_rcpf(gam);
-        qg[c] = scale * qv[c] * gam;
-        kg[c] = kv[c] * gam;                    // k Gamma (beta comes later)
-        kif[c][t] = -kv[c] * inv;               // -KI
-        kit[c][t] = Op::cvt(kif[c][t]);
+        qg[c] = scale * qv[t][c] * gam;
+        kg[c] = kv[t][c] * gam;                 // beta comes later
+        ki[c] = -kv[t][c] * inv;
+        kef[c][t] = ki[c] * fm[c];              // -K_end
+        kit[c][t] = Op::cvt(kef[c][t]);
       }
       st_row8(QG + i * Cfg::LD_K, kc0, qg);
       st_row8(KG + i * Cfg::LD_K, kc0, kg);
-      st_row8(KI + i * Cfg::LD_K, kc0, kif, t);
-      st_neg(BV + i * Cfg::LD_V + vc0, r.v[t]);     // -v, exactly: the sign bits flipped
+      st_row8(KI + i * Cfg::LD_K, kc0, ki);
     }
     // key-major copy KIT[channel][token]: the lane's TPL tokens are
     // consecutive (and stay so under the token permutation)
@@ -866,11 +909,12 @@ struct ChunkKernel {
     for (int c = 0; c < CPL; ++c) {
       LDS T* p = KIT + (kc0 + c) * Cfg::LD_KT + Op::perm_pos(TPL * tg);
       if (KIT_PAIRS)
-        *lds_ptr<uint32_t>(p) = pack_bf16x2(kif[c][0], kif[c][TPL - 1]);
+        *lds_ptr<uint32_t>(p) = pack_bf16x2(kef[c][0], kef[c][TPL - 1]);
       else
         st_vec(p, kit[c]);
     }
-    return bad;
+    return (bad ? 1 : 0) | (blockref ? 2 : 0);
+    }
   }
 
   // N raw input elements to LDS with their sign bits flipped (exact negation;
@@ -908,11 +952,6 @@ struct ChunkKernel {
       st_chunk(row + c0, y);
     }
   }
-  template <int N>
-  static __device__ __forceinline__ void st_row8(LDS T* row, int c0, const float (&x)[8][N], int t) {
-    const float y[8] = {x[0][t], x[1][t], x[2][t], x[3][t], x[4][t], x[5][t], x[6][t], x[7][t]};
-    st_row8(row, c0, y);
-  }
 
   // 8 consecutive channels c0 .. c0+7 of one row of a channel-permuted
   // buffer: two 4-element pieces at their permuted positions
@@ -938,13 +977,17 @@ struct ChunkKernel {
 
   // ---------------------------------------------------------------- phase A
   // R = strict_tril(KG KI^T) and Aqk = tril(QG KI^T) by 16x16 tiles, from
-  // the stored -KI (so the products come out negated).  The tiles are formed
+  // the stored -KI (so the products come out negated).  KDA: the operands
+  // are referenced to their own block's start, so a tile across blocks (I >
+  // J) takes the decay of the whole blocks J .. I-1 between the two
+  // references (F_IJ, per key channel) on its -KI fragments.  The tiles are formed
   // as (KI QG^T)^T-style products so that a lane ends up with four
   // consecutive columns of one row: off-diagonal -R tiles go row-major to RR,
   // -Aqk row-major to AQ (columns permuted like the 32-deep operand that reads
   // them), and the diagonal R tiles (in the other orientation) to RD, fp32,
   // column-contiguous, for the inverse.
-  static __device__ __forceinline__ void tile_qk(LDS char* smem, int I, int J) {
+  // sc: some wave references its channels to block starts (F_IJ != 1).
+  static __device__ __forceinline__ void tile_qk(LDS char* smem, int I, int J, bool sc) {
     const int l = lane_fresh();
     const LDS T* QG = (const LDS T*)(smem + Cfg::OFF_QG);
     const LDS T* KG = (const LDS T*)(smem + Cfg::OFF_KG);
@@ -955,7 +998,15 @@ struct ChunkKernel {
     f32x4 accR = {0.f, 0.f, 0.f, 0.f}, accA = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      const typename Op::F32 b = Op::ld32_rmp(l, KI, Cfg::LD_K, 16 * J, 32 * ks);
+      typename Op::F32 b = Op::ld32_rmp(l, KI, Cfg::LD_K, 16 * J, 32 * ks);
+      if constexpr (!Cfg::SG) {
+        if (I != J && sc) {
+          const LDS float* F = (const LDS float*)(smem + Cfg::OFF_DF) +
+                               (I * (I - 1) / 2 + J) * DK + 32 * ks + 8 * (l >> 4);
+          b.lo = Op::pack(Op::unpack(b.lo) * *lds_ptr<const f32x4>(F));
+          b.hi = Op::pack(Op::unpack(b.hi) * *lds_ptr<const f32x4>(F + 4));
+        }
+      }
       const typename Op::F32 ak = Op::ld32_rmp(l, KG, Cfg::LD_K, 16 * I, 32 * ks);
       const typename Op::F32 aq = Op::ld32_rmp(l, QG, Cfg::LD_K, 16 * I, 32 * ks);
       accR = (I == J) ? Op::mma32(ak, b, accR) : Op::mma32(b, ak, accR);
@@ -963,7 +1014,7 @@ struct ChunkKernel {
     }
     // accA[r] = -Aqk[16I + n][16J + g4 + r]; accR[r] = -R[16I + g4 + r][16I + n]
     // on the diagonal, -R[16I + n][16J + g4 + r] off it, once the rows are
-    // scaled by beta (KG holds k Gamma)
+    // scaled by beta
     const int n = l & 15, g4 = 4 * (l >> 4);
     const LDS float* BT = (const LDS float*)(smem + Cfg::OFF_BT);
     if constexpr (Cfg::SG) {
@@ -1068,22 +1119,37 @@ struct ChunkKernel {
   // The parts that need no inverse: Y_I = Diag(beta_I) (KG_I S - V_I) and the S part of
   // the outputs, O_I^T = S^T QG_I^T, for the four token blocks, with S as
   // 32-deep operands over key channels (lane: value column, k: channels).
+  // KDA: the channels of a block-referenced wave take the state into block
+  // I's products as Diag(P_I) S (P_I = T_0 .. T_{I-1}; 1 for the others).
   static __device__ __forceinline__ void scan_y(LDS char* smem, const f32x4 (&S)[MTK][NVT],
-                                                f32x4 (&Y)[4][NVT], f32x4 (&O)[4][NVT]) {
+                                                f32x4 (&Y)[4][NVT], f32x4 (&O)[4][NVT],
+                                                bool sc) {
     const int w = threadIdx.x >> 6, l = lane_fresh();
     const LDS T* KG = (const LDS T*)(smem + Cfg::OFF_KG);
     const LDS T* QG = (const LDS T*)(smem + Cfg::OFF_QG);
     const LDS T* BV = (const LDS T*)(smem + Cfg::OFF_BV);
     const LDS float* BT = (const LDS float*)(smem + Cfg::OFF_BT);
+    const LDS float* DP = (const LDS float*)(smem + Cfg::OFF_DP);
     typename Op::F32 SB[NKS][NVT];
     const int vw0 = w * VW;
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
-#pragma unroll
-      for (int nt = 0; nt < NVT; ++nt)
-        SB[ks][nt] = typename Op::F32{Op::pack(S[2 * ks][nt]), Op::pack(S[2 * ks + 1][nt])};
-#pragma unroll
     for (int I = 0; I < 4; ++I) {
+      if (I == 0 || (!Cfg::SG && sc)) {
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+          for (int nt = 0; nt < NVT; ++nt) {
+            f32x4 lo = S[2 * ks][nt], hi = S[2 * ks + 1][nt];
+            if (!Cfg::SG && I > 0 && sc) {
+              // rows 32 ks + 4g + r and 32 ks + 16 + 4g + r: fragment positions
+              // 32 ks + 8g + r and 32 ks + 8g + 4 + r
+              const LDS float* P = DP + I * DK + 32 * ks + 8 * (l >> 4);
+              lo *= *lds_ptr<const f32x4>(P);
+              hi *= *lds_ptr<const f32x4>(P + 4);
+            }
+            SB[ks][nt] = typename Op::F32{Op::pack(lo), Op::pack(hi)};
+          }
+      }
 #pragma unroll
       for (int nt = 0; nt < NVT; ++nt)
         Y[I][nt] = Op::unpack(Op::ld16_tr(l, BV, Cfg::LD_V, 16 * I, vw0 + 16 * nt));   // -V
@@ -1110,7 +1176,7 @@ struct ChunkKernel {
 #pragma unroll
           for (int nt = 0; nt < NVT; ++nt) Y[I][nt] = Op::mma32(ak, SB[ks][nt], Y[I][nt]);
         }
-        // rows 16I + g4 + r scaled by beta: Y = Diag(beta)((k Gamma) S - v)
+        // rows 16I + g4 + r scaled by beta: Y = Diag(beta)((k Pi) (P_I S) - v)
 #pragma unroll
         for (int nt = 0; nt < NVT; ++nt) Y[I][nt] *= b;
       }
@@ -1137,7 +1203,7 @@ struct ChunkKernel {
                                                    f32x4 (&Y)[4][NVT], f32x4 (&Ob)[4][NVT],
                                                    void* out,
                                                    size_t row_base, int H, int h, int clen,
-                                                   int lo, const Raw& nxt, bool next_norms) {
+                                                   const Raw& nxt, bool next_norms) {
     const int w = threadIdx.x >> 6, l = lane_fresh();
     const LDS T* QG = (const LDS T*)(smem + Cfg::OFF_QG);
     const LDS T* KG = (const LDS T*)(smem + Cfg::OFF_KG);
@@ -1217,9 +1283,8 @@ struct ChunkKernel {
 #pragma unroll
       for (int nt = 0; nt < NVT; ++nt) Op::st_ct(l, OST, Cfg::LD_OS, 16 * I, vw0 + 16 * nt, O[nt]);
     }
-    // (4) state update, S <- Diag(Gamma_L) (S + KI^T E), from -KI and -E.
-    //     K_end = Diag(Gamma_L) KI row-wise, so this is Diag(Gamma_L) S +
-    //     K_end^T E without forming K_end (section 6.4).
+    // (4) state update, S <- Diag(Gamma_L) S + K_end^T E (section 6.4), from
+    //     the key-major -K_end (KDA) or -k (Gated DeltaNet) and -E.
 #pragma unroll
     for (int mt = 0; mt < MTK; ++mt) {
       const f32x4 gl = *lds_ptr<const f32x4>(GL + 16 * mt + g4);
@@ -1236,10 +1301,10 @@ struct ChunkKernel {
           for (int kt = 0; kt < 2; ++kt) s = Op::mma32(a[kt], ES[kt][nt], s);
           S[mt][nt] = s;
         } else {
-          f32x4 s = S[mt][nt];
+          f32x4 s = S[mt][nt] * gl;
 #pragma unroll
           for (int kt = 0; kt < 2; ++kt) s = Op::mma32(a[kt], EB[kt][nt], s);
-          S[mt][nt] = s * gl;
+          S[mt][nt] = s;
         }
       }
     }
@@ -1264,7 +1329,7 @@ struct ChunkKernel {
         const int p = p0 + threadIdx.x;
         const int i = p / PER_ROW, c = (p % PER_ROW) * PIECE;
         const u32x4 val = *lds_ptr<const u32x4>(OST + i * Cfg::LD_OS + c);
-        if (i >= lo) buf_store16(ro, i * srow + c * E, val);   // rows [lo, clen)
+        buf_store16(ro, i * srow + c * E, val);   // rows past clen are dropped
       }
     }
 
@@ -1377,29 +1442,30 @@ struct ChunkKernel {
   // off-diagonal pairs; each wave's case is one scheduling region, so VALU
   // (inverse) and MFMA (tiles, Y, S^T QG^T) interleave.
   static __device__ __forceinline__ void middle(LDS char* smem, f32x4 (&S)[MTK][NVT],
-                                                f32x4 (&Y)[4][NVT], f32x4 (&O)[4][NVT]) {
+                                                f32x4 (&Y)[4][NVT], f32x4 (&O)[4][NVT],
+                                                bool sc) {
     const int w = threadIdx.x >> 6;
     if (NW == 8) {
       switch (__builtin_amdgcn_readfirstlane(w)) {
-        case 0: tile_qk(smem, 0, 0); invert_diag<0>(smem); scan_y(smem, S, Y, O); break;
-        case 1: tile_qk(smem, 1, 1); invert_diag<1>(smem); scan_y(smem, S, Y, O); break;
-        case 2: tile_qk(smem, 2, 2); invert_diag<2>(smem); scan_y(smem, S, Y, O); break;
-        case 3: tile_qk(smem, 3, 3); invert_diag<3>(smem); scan_y(smem, S, Y, O); break;
-        case 4: tile_qk(smem, 1, 0); tile_qk(smem, 3, 2); scan_y(smem, S, Y, O); break;
-        case 5: tile_qk(smem, 2, 0); tile_qk(smem, 2, 1); scan_y(smem, S, Y, O); break;
-        case 6: tile_qk(smem, 3, 0); scan_y(smem, S, Y, O); break;
-        default: tile_qk(smem, 3, 1); scan_y(smem, S, Y, O); break;
+        case 0: tile_qk(smem, 0, 0, sc); invert_diag<0>(smem); scan_y(smem, S, Y, O, sc); break;
+        case 1: tile_qk(smem, 1, 1, sc); invert_diag<1>(smem); scan_y(smem, S, Y, O, sc); break;
+        case 2: tile_qk(smem, 2, 2, sc); invert_diag<2>(smem); scan_y(smem, S, Y, O, sc); break;
+        case 3: tile_qk(smem, 3, 3, sc); invert_diag<3>(smem); scan_y(smem, S, Y, O, sc); break;
+        case 4: tile_qk(smem, 1, 0, sc); tile_qk(smem, 3, 2, sc); scan_y(smem, S, Y, O, sc); break;
+        case 5: tile_qk(smem, 2, 0, sc); tile_qk(smem, 2, 1, sc); scan_y(smem, S, Y, O, sc); break;
+        case 6: tile_qk(smem, 3, 0, sc); scan_y(smem, S, Y, O, sc); break;
+        default: tile_qk(smem, 3, 1, sc); scan_y(smem, S, Y, O, sc); break;
       }
     } else {
       switch (__builtin_amdgcn_readfirstlane(w)) {
-        case 0: tile_qk(smem, 0, 0); invert_diag<0>(smem); tile_qk(smem, 1, 0);
-                tile_qk(smem, 2, 0); scan_y(smem, S, Y, O); break;
-        case 1: tile_qk(smem, 1, 1); invert_diag<1>(smem); tile_qk(smem, 2, 1);
-                tile_qk(smem, 3, 0); scan_y(smem, S, Y, O); break;
-        case 2: tile_qk(smem, 2, 2); invert_diag<2>(smem); tile_qk(smem, 3, 1);
-                scan_y(smem, S, Y, O); break;
-        default: tile_qk(smem, 3, 3); invert_diag<3>(smem); tile_qk(smem, 3, 2);
-                 scan_y(smem, S, Y, O); break;
+        case 0: tile_qk(smem, 0, 0, sc); invert_diag<0>(smem); tile_qk(smem, 1, 0, sc);
+                tile_qk(smem, 2, 0, sc); scan_y(smem, S, Y, O, sc); break;
+        case 1: tile_qk(smem, 1, 1, sc); invert_diag<1>(smem); tile_qk(smem, 2, 1, sc);
+                tile_qk(smem, 3, 0, sc); scan_y(smem, S, Y, O, sc); break;
+        case 2: tile_qk(smem, 2, 2, sc); invert_diag<2>(smem); tile_qk(smem, 3, 1, sc);
+                scan_y(smem, S, Y, O, sc); break;
+        default: tile_qk(smem, 3, 3, sc); invert_diag<3>(smem); tile_qk(smem, 3, 2, sc);
+                 scan_y(smem, S, Y, O, sc); break;
       }
     }
   }
@@ -1471,68 +1537,37 @@ struct ChunkKernel {
         __syncthreads();
       }
       norms_ready = false;
-      const int bad = prep(raw, smem, scale, pro, ea, 0, clen);
-      // the vote runs in every lane: inside the lane-0 branch it would only
-      // see lane 0's flag (the scan path sets it in other lanes)
+      const int fl = prep(raw, smem, scale, pro, ea, clen);   // wave-uniform flags
       if constexpr (!Cfg::SG) {   // the single-gate form has no guard
-        const int wave_bad = __any(bad);
-        if (lane_fresh() == 0) FL[w] = wave_bad ? 1 : 0;
+        if (lane_fresh() == 0) FL[w] = fl;
       }
       compiler_fence();
       load_raw<LOAD_G>(raw, offs, q, k, v, g, beta, next, H, h, nlen);
       __syncthreads();                                           // B1
-      int any_bad = 0;
+      int any = 0;
       if constexpr (!Cfg::SG) {
 #pragma unroll
-        for (int i = 0; i < NW; ++i) any_bad |= FL[i];
+        for (int i = 0; i < NW; ++i) any |= FL[i];
       }
-      if (!any_bad) {
+      if (!(any & 1)) {
         load_raw<LOAD_V>(raw, offs, q, k, v, g, beta, next, H, h, nlen);
         compiler_fence();
         f32x4 Y[4][NVT], O[4][NVT];
-        middle(smem, S, Y, O);
+        middle(smem, S, Y, O, (any & 2) != 0);
         compiler_fence();
         load_raw<LOAD_Q | LOAD_K>(raw, offs, q, k, v, g, beta, next, H, h, nlen);
         __syncthreads();                                         // B2
-        scan_step(smem, S, Y, O, out, row_base + c0, H, h, clen, 0, raw, l2n);
+        scan_step(smem, S, Y, O, out, row_base + c0, H, h, clen, raw, l2n);
         norms_ready = l2n;
       } else {
-        // Some channel decays by more than 2^100 over the chunk, beyond what
-        // one reference point (the chunk start) can scale: redo the chunk as
-        // 16-token windows, each a full chunk step with the other rows as
-        // identity tokens (a window stays in range unless log alpha averages
-        // below about -4.3 over it); a window that still decays too fast runs
-        // the recurrence token by token.  The windows use their own raw
-        // registers; the next chunk's gates are already on their way, and
-        // its q, k, v follow as on the guard path before, so the loads in
-        // flight at the top of the loop are the same on both paths.
-        for (int lo = 0; lo < clen; lo += 16) {
-          const int hi = (lo + 16) < clen ? (lo + 16) : clen;
-          Raw rw;
-          load_raw<LOAD_ALL>(rw, offs, q, k, v, g, beta, row_base + c0, H, h, clen);
-          mask_window(rw, lo, hi);
-          if (Cfg::FU && (pro.flags & PRO_L2NORM)) {
-            norm_partials(rw, smem);
-            __syncthreads();
-          }
-          const int wbad = prep(rw, smem, scale, pro, ea, lo, hi);
-          const int wave_wbad = __any(wbad);
-          if (lane_fresh() == 0) FL[w] = wave_wbad ? 1 : 0;
-          __syncthreads();
-          int any_wbad = 0;
-#pragma unroll
-          for (int i = 0; i < NW; ++i) any_wbad |= FL[i];
-          if (!any_wbad) {
-            f32x4 Y[4][NVT], O[4][NVT];
-            middle(smem, S, Y, O);
-            __syncthreads();
-            scan_step(smem, S, Y, O, out, row_base + c0, H, h, hi, lo, rw, false);
-          } else {
-            recurrent_chunk(S, q, k, v, g, beta, out, row_base + c0 + lo, H, h, hi - lo, scale,
-                            pro, ea);
-            __syncthreads();
-          }
-        }
+        // Some channel decays by more than 2^120 within one 16-token block
+        // (log alpha averaging below about -5.2 over it, beyond the gate
+        // transform's range), past what a block-start reference can scale:
+        // the chunk runs the recurrence token by token on the same on-chip
+        // state.  The next chunk's gates are already on their way; its q, k,
+        // v follow here, so the loads in flight at the top of the loop are the
+        // same on both paths.
+        recurrent_chunk(S, q, k, v, g, beta, out, row_base + c0, H, h, clen, scale, pro, ea);
         load_raw<LOAD_Q | LOAD_K | LOAD_V>(raw, offs, q, k, v, g, beta, next, H, h, nlen);
         __syncthreads();                                         // LDS reuse
       }
@@ -1640,9 +1675,10 @@ static hipError_t launch_chunk_t(const void* q, const void* k, const void* v, co
 // serial loop, two 128-deep products per chunk; stage C (chunk_out_kernel,
 // all chunks at once) forms the outputs.  Every factor goes through the
 // workspace as bf16 MFMA fragments in the exact lane order its consumer
-// reads, one 16-byte load per lane per fragment.  A chunk whose decay leaves
-// the range of the single chunk-start reference (the fused kernel's guard)
-// is flagged by stage A and recomputed token by token by stage B.
+// reads, one 16-byte load per lane per fragment.  A chunk with a 16-token
+// block that decays below KDA_BLOCK_DECAY_MIN in some channel (the fused
+// kernel's guard) is flagged by stage A and recomputed token by token by
+// stage B.
 template <class Cfg>
 struct ParLayout {
   static constexpr int DK = Cfg::DK, DV = Cfg::DV;
@@ -1687,22 +1723,24 @@ struct ParKernel {
 
   // The state-independent tiles and inverses (the fused kernel's middle
   // interval without its state products).
-  static __device__ __forceinline__ void tiles(LDS char* smem) {
+  static __device__ __forceinline__ void tiles(LDS char* smem, bool sc) {
     switch (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) {
-      case 0: K::tile_qk(smem, 0, 0); K::template invert_diag<0>(smem); break;
-      case 1: K::tile_qk(smem, 1, 1); K::template invert_diag<1>(smem); break;
-      case 2: K::tile_qk(smem, 2, 2); K::template invert_diag<2>(smem); break;
-      case 3: K::tile_qk(smem, 3, 3); K::template invert_diag<3>(smem); break;
-      case 4: K::tile_qk(smem, 1, 0); K::tile_qk(smem, 3, 2); break;
-      case 5: K::tile_qk(smem, 2, 0); K::tile_qk(smem, 2, 1); break;
-      case 6: K::tile_qk(smem, 3, 0); break;
-      default: K::tile_qk(smem, 3, 1); break;
+      case 0: K::tile_qk(smem, 0, 0, sc); K::template invert_diag<0>(smem); break;
+      case 1: K::tile_qk(smem, 1, 1, sc); K::template invert_diag<1>(smem); break;
+      case 2: K::tile_qk(smem, 2, 2, sc); K::template invert_diag<2>(smem); break;
+      case 3: K::tile_qk(smem, 3, 3, sc); K::template invert_diag<3>(smem); break;
+      case 4: K::tile_qk(smem, 1, 0, sc); K::tile_qk(smem, 3, 2, sc); break;
+      case 5: K::tile_qk(smem, 2, 0, sc); K::tile_qk(smem, 2, 1, sc); break;
+      case 6: K::tile_qk(smem, 3, 0, sc); break;
+      default: K::tile_qk(smem, 3, 1, sc); break;
     }
   }
 
   // X = (I + R)^{-1} Y by 16-token blocks for this wave's two 16-column tiles:
-  // waves 0-3 take Y = Diag(beta) KG (key columns 32w ..), so X = W; waves
-  // 4-7 take Y = Diag(beta) (-V) (value columns 32(w-4) ..), so X = -U.
+  // waves 0-3 take Y = Diag(beta) k Gamma (key columns 32w ..; for channels
+  // referenced to the block start the KG buffer holds k Pi, so block I takes
+  // P_I on each key column, 1 for the others), so X = W; waves 4-7 take
+  // Y = Diag(beta) (-V) (value columns 32(w-4) ..), so X = -U.
   // -W goes back into the KG buffer (the wave's own columns, which only it
   // reads from here on); U goes straight to the workspace in the
   // accumulator layout stage B starts E from.
@@ -1714,6 +1752,7 @@ struct ParKernel {
     const LDS T* RR = (const LDS T*)(smem + Cfg::OFF_RT);
     const LDS T* TD = (const LDS T*)(smem + Cfg::OFF_TD);
     const LDS float* BT = (const LDS float*)(smem + Cfg::OFF_BT);
+    const LDS float* DP = (const LDS float*)(smem + Cfg::OFF_DP);
     const bool keys = w < 4;
     const int c0 = 32 * (w & 3);
     f32x4 Y[4][2];
@@ -1724,7 +1763,8 @@ struct ParKernel {
       for (int nt = 0; nt < 2; ++nt) {
         const typename Op::F16 f = keys ? Op::ld16_trp(l, KG, Cfg::LD_K, 16 * I, Op::perm_pos(c0 + 16 * nt))
                                         : Op::ld16_tr(l, BV, Cfg::LD_V, 16 * I, c0 + 16 * nt);
-        Y[I][nt] = Op::unpack(f) * b;
+        const float pf = (keys && I > 0) ? DP[I * DK + frag_pos(c0 + 16 * nt + n)] : 1.f;
+        Y[I][nt] = Op::unpack(f) * (b * pf);
       }
     }
     typename Op::F16 XP[4][2];
@@ -1771,8 +1811,9 @@ struct ParKernel {
   }
 
   // The remaining factors to the workspace, each as the fragments their
-  // consumers read: -W and QG (rows = tokens, k = keys), -K_end^T (rows =
-  // keys, k = tokens), -Aqk (rows = tokens, k = tokens), Gamma_L.
+  // consumers read: -W and QG = s q Gamma (rows = tokens, k = keys; block I
+  // takes P_I on each block-referenced channel), -K_end^T
+  // (rows = keys, k = tokens), -Aqk (rows = tokens, k = tokens), Gamma_L.
   static __device__ __forceinline__ void write_factors(LDS char* smem, char* rec) {
     const int w = threadIdx.x >> 6, l = lane_fresh();
     const LDS T* KG = (const LDS T*)(smem + Cfg::OFF_KG);   // now -W
@@ -1780,19 +1821,21 @@ struct ParKernel {
     const LDS T* KIT = (const LDS T*)(smem + Cfg::OFF_KT);
     const LDS T* AQ = (const LDS T*)(smem + Cfg::OFF_AQ);
     const LDS float* GL = (const LDS float*)(smem + Cfg::OFF_GL);
+    const LDS float* DP = (const LDS float*)(smem + Cfg::OFF_DP);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int f = 2 * w + j;                  // 0 .. 15
       const int I = f / NKS, ks = f % NKS;
       st16(rec + L::OFF_W + f * L::FR + l * 16, Op::ld32_rmp(l, KG, Cfg::LD_K, 16 * I, 32 * ks));
-      st16(rec + L::OFF_QG + f * L::FR + l * 16, Op::ld32_rmp(l, QG, Cfg::LD_K, 16 * I, 32 * ks));
-      // KIT holds -KI key-major; -K_end = Gamma_L (-KI) row-wise (row = key)
-      const int mt = f / 2, kt = f % 2;
-      typename Op::F32 a = Op::ld32_rmp(l, KIT, Cfg::LD_KT, 16 * mt, 32 * kt);
-      const float gl = GL[16 * mt + (l & 15)];
-      a.lo = Op::pack(Op::unpack(a.lo) * gl);
-      a.hi = Op::pack(Op::unpack(a.hi) * gl);
-      st16(rec + L::OFF_KE + f * L::FR + l * 16, a);
+      typename Op::F32 qf = Op::ld32_rmp(l, QG, Cfg::LD_K, 16 * I, 32 * ks);
+      if (I > 0) {
+        const LDS float* P = DP + I * DK + 32 * ks + 8 * (l >> 4);
+        qf.lo = Op::pack(Op::unpack(qf.lo) * *lds_ptr<const f32x4>(P));
+        qf.hi = Op::pack(Op::unpack(qf.hi) * *lds_ptr<const f32x4>(P + 4));
+      }
+      st16(rec + L::OFF_QG + f * L::FR + l * 16, qf);
+      const int mt = f / 2, kt = f % 2;         // KIT holds -K_end key-major
+      st16(rec + L::OFF_KE + f * L::FR + l * 16, Op::ld32_rmp(l, KIT, Cfg::LD_KT, 16 * mt, 32 * kt));
     }
     st16(rec + L::OFF_AQ + w * L::FR + l * 16, Op::ld32_rmp(l, AQ, Cfg::LD_AQ, 16 * (w / 2), 32 * (w % 2)));
     if (w == 0 && l < DK / 4)
@@ -1842,20 +1885,20 @@ __global__ __launch_bounds__(Cfg::NTHREADS, 1) void chunk_intra_kernel(
     size_t nrow0 = row0;
     int nh = h, nlen = 0;
     if (nidx < total) where(nidx, nrow0, nh, nlen);
-    const int bad = K::prep(raw, smem, scale, pro, 1.f, 0, clen);
-    const int wave_bad = __any(bad);
-    if (lane_fresh() == 0) FL[w] = wave_bad ? 1 : 0;
+    const int fl = K::prep(raw, smem, scale, pro, 1.f, clen);   // wave-uniform flags
+    if (lane_fresh() == 0) FL[w] = fl;
     compiler_fence();
     K::template load_raw<K::LOAD_G>(raw, offs, q, k, v, g, beta, nrow0, H, nh, nlen);
     __syncthreads();
-    int any_bad = 0;
+    int any = 0;
 #pragma unroll
-    for (int i = 0; i < Cfg::NW; ++i) any_bad |= FL[i];
+    for (int i = 0; i < Cfg::NW; ++i) any |= FL[i];
+    const int any_bad = any & 1;
     if (threadIdx.x == 0) flags[idx] = any_bad;
     // a flagged chunk is redone token by token by stage B
     K::template load_raw<K::LOAD_V>(raw, offs, q, k, v, g, beta, nrow0, H, nh, nlen);
     compiler_fence();
-    if (!any_bad) P::tiles(smem);
+    if (!any_bad) P::tiles(smem, (any & 2) != 0);
     compiler_fence();
     __syncthreads();
     K::template load_raw<K::LOAD_Q | K::LOAD_K>(raw, offs, q, k, v, g, beta, nrow0, H, nh, nlen);

@@ -16,6 +16,10 @@ Recipe (the pages fix only shapes and distributions; the rest is chosen here):
   packed along the token axis with cu_seqlens; in each head a seeded choice of
   ``long_channels`` key channels draws log_alpha = -exp(N(-8, 0.5)) instead
   (a decay horizon of a few thousand tokens).
+* strong_gate_channels: in every head a seeded choice of n key channels
+  redraws log_alpha ~ U[lo, hi] (default [-5, -2]) per token: fast-forgetting
+  channels down to the gate transform's floor of -5 per token, up to e^-320
+  over a 64-token chunk.
 * gate="gdn" (Gated DeltaNet) draws one log_alpha per (token, head), shape
   [..., H], from the same -exp(N(-3, 1)); gate="kda" one per key channel.
 * Draw order: q, k, v, g, beta, S0 (lengths first for varlen).  Random numbers
@@ -32,7 +36,8 @@ import numpy as np
 import torch
 
 __all__ = ["prefill_inputs", "varlen_lengths", "varlen_inputs", "decode_inputs",
-           "raw_layer_inputs", "grad_inputs", "to_host", "bf16_bits_from_f32", "CONFIGS"]
+           "raw_layer_inputs", "strong_gate_channels", "grad_inputs", "to_host",
+           "bf16_bits_from_f32", "CONFIGS"]
 
 _IO = {"bf16": torch.bfloat16, "f32": torch.float32}
 
@@ -160,6 +165,26 @@ def raw_layer_inputs(d, H, dk, seed=0, gate="kda", strong_decay=False, device="c
     d["A_log"] = 0.3 * torch.randn((H,), generator=gen, device=device)
     bshape = (H,) if gate == "gdn" else (H, dk)
     d["gate_bias"] = 0.5 * torch.randn(bshape, generator=gen, device=device)
+    return d
+
+
+def strong_gate_channels(d, n_channels, lo=-5.0, hi=-2.0, seed=0):
+    """Per-channel KDA inputs (batched or packed): in every head a seeded
+    choice of ``n_channels`` key channels redraws log_alpha ~ U[lo, hi] per
+    token, from a generator of its own.  Modifies d["g"] in place and records
+    the choice as d["strong_idx"] ([H, n_channels] int64)."""
+    g = d["g"]
+    dev = g.device
+    gen = _gen(dev, seed + 15485863)
+    H, dk = g.shape[-2], g.shape[-1]
+    rows = g.shape[:-2]
+    chosen = []
+    for h in range(H):
+        idx = torch.randperm(dk, generator=gen, device=dev)[:n_channels]
+        u = torch.rand(rows + (n_channels,), generator=gen, device=dev, dtype=torch.float32)
+        g[..., h, idx] = lo + (hi - lo) * u
+        chosen.append(idx)
+    d["strong_idx"] = torch.stack(chosen) if chosen else None
     return d
 
 

@@ -44,7 +44,7 @@ CHUNK_CASES = [
     (1, 100, 2, 128, 128, "bf16", "kda", oracle.L2NORM, False),
     (1, 70, 2, 64, 128, "bf16", "kda", oracle.BETA_SIGMOID, False),
     (1, 80, 2, 64, 64, "f32", "gdn", oracle.GATE, False),
-    (1, 96, 2, 128, 128, "bf16", "kda", ALL, True),     # every chunk takes the guard path
+    (1, 96, 2, 128, 128, "bf16", "kda", ALL, True),     # log alpha near -5 in every channel
     (1, 65, 1, 64, 64, "f32", "gdn", ALL, True),
 ]
 
@@ -62,6 +62,30 @@ def test_fused_chunk_fwd_matches_oracle(B, T, H, dk, dv, io, gate, flags, strong
     ro, rs = oracle_batched(d, chains, flags=flags)
     go, gs = gpu_chains_batched(o, S, chains)
     assert_close(go, gs, ro, rs, tol_for(io), "fused chunk")
+
+
+def test_fused_guard_path_matches_oracle():
+    """The token-by-token guard path with the q/k norm and beta transforms:
+    raw log alpha (no gate transform) at -20 in 8 channels over tokens
+    40 .. 110, so the chunks holding them decay below 2^-120 within a
+    16-token block; the other chunks take the MFMA path."""
+    note("fused guard path")
+    flags = oracle.L2NORM | oracle.BETA_SIGMOID
+    d = inputs.prefill_inputs(2, 150, 2, 128, 128, io="bf16", seed=17, with_S0=True, device=DEV)
+    g = d["g"].clone()
+    d = inputs.raw_layer_inputs(d, 2, 128, seed=17, device=DEV)
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(9)
+    idx = torch.randperm(128, generator=gen, device=DEV)[:8]
+    sl = g[:, 40:110]
+    sl[..., idx] = -20.0
+    d["g"] = g
+    o, S = kda().chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], S0=d["S0"], **kw(d, flags))
+    torch.cuda.synchronize()
+    chains = [(b, h) for b in range(2) for h in range(2)]
+    ro, rs = oracle_batched(d, chains, flags=flags)
+    go, gs = gpu_chains_batched(o, S, chains)
+    assert_close(go, gs, ro, rs, tol_for("bf16"), "fused guard path")
 
 
 @pytest.mark.parametrize("lens,gate", [([70, 0, 1, 129], "kda"), ([33, 64, 0], "gdn")])

@@ -72,14 +72,18 @@ def test_single_head_f32_seed0():
                                                            (64, 128, "bf16", None, -3.0),
                                                            (64, 64, "f32", 4, -3.0),
                                                            (128, 128, "bf16", 8, -5.0),
-                                                           (64, 64, "f32", None, -5.0)])
-def test_strong_decay_takes_the_guard_path(dk, dv, io, strong_channels, gval):
-    """Chunks whose decay in some key channel falls below 2^-100 must leave the
-    one-reference fast path, also when only a few channels decay that fast
-    (the detection must see every lane's channels).  At log alpha = -3 per
-    token (e^-192 over a chunk) each 16-token window fits (e^-48); at -5
-    (e^-80 per window) the windows run token by token.  Results must match
-    the oracle."""
+                                                           (64, 64, "f32", None, -5.0),
+                                                           (128, 128, "bf16", 8, -8.0),
+                                                           (128, 64, "bf16", 1, -20.0),
+                                                           (64, 64, "f32", None, -8.0)])
+def test_strong_decay_matches_oracle(dk, dv, io, strong_channels, gval):
+    """Fast-decaying key channels.  At log alpha = -3 (e^-192 over a chunk) and
+    -5 per token (e^-80 over a 16-token block, 2^-115.4, the gate transform's
+    floor) the block-start references keep every operand in range and the
+    chunk takes the MFMA path; at -8 and -20 a 16-token block decays below
+    2^-120 and the chunk runs the recurrence token by token (also when a
+    single channel of one wave does so: the flag must see every lane's
+    channels).  Results must match the oracle."""
     note("strong decay dk=%d dv=%d io=%s channels=%s g=%.1f" % (dk, dv, io, strong_channels, gval))
     d = inputs.prefill_inputs(2, 150, 2, dk, dv, io=io, seed=dk + dv, with_S0=True, device=DEV)
     if strong_channels is None:
@@ -97,6 +101,24 @@ def test_strong_decay_takes_the_guard_path(dk, dv, io, strong_channels, gval):
     assert_close(go, gs, ro, rs, tol_for(io), "strong decay")
 
 
+@pytest.mark.parametrize("dk,dv,io", [(128, 128, "bf16"), (128, 64, "bf16"), (64, 128, "bf16"),
+                                      (64, 64, "bf16"), (64, 64, "f32")])
+def test_strong_gate_channels_match_oracle(dk, dv, io):
+    """8 of every 128 key channels (4 of 64) at log alpha ~ U[-5, -2] per token,
+    the rest as usual: whole chunks decay far beyond 2^-126 in those channels
+    while every 16-token block stays in range.  Every config of the fused
+    kernel, all chains checked, with a ragged last chunk."""
+    note("strong gate channels dk=%d dv=%d io=%s" % (dk, dv, io))
+    d = inputs.prefill_inputs(2, 333, 3, dk, dv, io=io, seed=dk * dv, with_S0=True, device=DEV)
+    inputs.strong_gate_channels(d, 8 if dk == 128 else 4, seed=dk + dv)
+    o, S = kda().chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], S0=d["S0"])
+    torch.cuda.synchronize()
+    chains = [(b, h) for b in range(2) for h in range(3)]
+    ro, rs = oracle_batched(d, chains)
+    go, gs = gpu_chains_batched(o, S, chains)
+    assert_close(go, gs, ro, rs, tol_for(io), "strong gate channels")
+
+
 def test_prefill_h16_t4096_with_S0():
     """The B=1, H=16, T=4096, d=128 bf16 workload with a random fp32 S0."""
     cfg = inputs.CONFIGS["prefill_h16_s0"]
@@ -111,26 +133,28 @@ def test_prefill_h16_t4096_with_S0():
     assert_close(go, gs, ro, rs, tol_for("bf16"), "prefill_h16_s0")
 
 
-@pytest.mark.parametrize("B,T,H,with_S0,strong", [(2, 1000, 3, True, False),
-                                                  (1, 512, 2, False, False),
-                                                  (1, 700, 2, True, True)])
+@pytest.mark.parametrize("B,T,H,with_S0,strong", [(2, 1000, 3, True, None),
+                                                  (1, 512, 2, False, None),
+                                                  (1, 700, 2, True, -3.0),
+                                                  (1, 700, 2, True, -20.0)])
 def test_chunk_parallel_schedule_matches_oracle(B, T, H, with_S0, strong):
     """Few long chains take the chunk-parallel schedule (per-chunk WY factors,
     one state scan, outputs of all chunks in parallel).  Every chain is checked,
-    with a ragged last chunk; with ``strong`` some chunks decay beyond the
-    chunk-start reference's range in 8 channels and are recomputed token by
-    token by the scan stage."""
+    with a ragged last chunk.  With ``strong`` = -3, 8 channels decay by e^-192
+    over the chunks of tokens 128 .. 300 (block-start references in stage A);
+    with -20 their blocks decay below 2^-120, stage A flags those chunks and
+    the scan stage recomputes them token by token."""
     K = kda()
     assert K.chunk_fwd_workspace_size(B, T, H, 128, 128) > 0   # the schedule is taken
     note("chunk-parallel B=%d T=%d H=%d S0=%s strong=%s" % (B, T, H, with_S0, strong))
     d = inputs.prefill_inputs(B, T, H, 128, 128, io="bf16", seed=T + H, with_S0=with_S0,
                               device=DEV)
-    if strong:
+    if strong is not None:
         gen = torch.Generator(device=DEV)
         gen.manual_seed(7)
         idx = torch.randperm(128, generator=gen, device=DEV)[:8]
         sl = d["g"][:, 128:300]
-        sl[..., idx] = -3.0
+        sl[..., idx] = strong
     o, S = K.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], S0=d["S0"])
     torch.cuda.synchronize()
     chains = [(b, h) for b in range(B) for h in range(H)]
