@@ -66,6 +66,12 @@ __device__ __forceinline__ float dpp1(float x) {
 // x of lane l - D inside the lane's 16-lane row (1 for the first D lanes)
 template <int D>
 __device__ __forceinline__ float dpp_row_shr(float x) { return dpp1<0x110 + D, 0xf>(x); }
+// x of lane l - D inside the lane's 16-lane row, 0 for the first D lanes (the
+// zero fill lets the compiler fuse the move into the consuming add)
+template <int D>
+__device__ __forceinline__ float dpp_row_shr0(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 + D, 0xf, 0xf, true));
+}
 
 // ============================================================ operand policies
 typedef short i16x8 __attribute__((ext_vector_type(8)));
@@ -371,16 +377,20 @@ struct ChunkCfg {
   static constexpr int OFF_TD = OFF_RT + C * LD_RR * SZ;
   static constexpr int LD_KT = C + Op::PAD_B128;  // KIT [DK][LD_KT]
   static constexpr int OFF_KT = OFF_TD + NB * 16 * 16 * SZ;
-  // KDA decay factors per key channel, fp32 in fragment order (frag_pos):
-  // [4][DK] the block totals T_b (each wave's own channels, read back only by
-  // that wave); [4][DK] the state factors of the block-referenced channels
-  // (P_b = T_0 .. T_{b-1}, else 1); [6][DK] their tile factors F_IJ =
-  // T_J .. T_{I-1} (else 1) of the pairs I > J in the order (1,0) (2,0)
-  // (2,1) (3,0) (3,1) (3,2)
+  // KDA decay factors per key channel, fp32 in fragment order (frag_pos).
+  // Each wave's own channels, read back only by that wave: [4][DK] the block
+  // totals T_b, and per block the factors that take the block-local decay
+  // to the operands' reference (FA) and -k / (that reference) to -K_end (FM).
+  // For the tiles and scan_y: [4][DK] the state factors of block-referenced
+  // channels (P_b = T_0 .. T_{b-1}, else 1) and [6][DK] their tile factors
+  // F_IJ = T_J .. T_{I-1} (else 1) of the pairs I > J in the order (1,0)
+  // (2,0) (2,1) (3,0) (3,1) (3,2).
   static constexpr int OFF_DT = OFF_KT + DK * LD_KT * SZ;
-  static constexpr int OFF_DP = OFF_DT + 4 * DK * 4;
+  static constexpr int OFF_FA = OFF_DT + 4 * DK * 4;
+  static constexpr int OFF_FM = OFF_FA + 4 * DK * 4;
+  static constexpr int OFF_DP = OFF_FM + 4 * DK * 4;
   static constexpr int OFF_DF = OFF_DP + 4 * DK * 4;
-  static constexpr int SZ_D = SG ? 0 : 14 * DK * 4;
+  static constexpr int SZ_D = SG ? 0 : 22 * DK * 4;
   static constexpr int OFF_GL = OFF_DT + SZ_D;
   static constexpr int OFF_BT = OFF_GL + DK * 4;          // beta of the chunk's tokens
   static constexpr int OFF_FL = OFF_BT + C * 4;
@@ -402,10 +412,14 @@ struct ChunkCfg {
                 (LD_RR * SZ) % 8 == 0 && (LD_OS * SZ) % 16 == 0, "LDS alignment");
 };
 
-// Threshold below which a 16-token block's decay T_b makes k / Pi unsafe
-// (Pi >= T_b inside the block, so 1 / Pi stays below 2^120).  With the gate
-// transform, log alpha >= -5 per token keeps every block above 2^-115.5.
-#define KDA_BLOCK_DECAY_MIN 7.52316384526264e-37f /* 2^-120 */
+// log2 of the threshold below which a 16-token block's decay T_b makes
+// k / Pi unsafe (Pi >= T_b inside the block, so 1 / Pi stays below 2^120).
+// With the gate transform, log alpha >= -5 per token keeps every block above
+// 2^-115.5.
+#define KDA_BLOCK_LOG2_MIN (-120.f)
+// log2 of the block decay down to which chunk-start references stay in use
+// (four blocks then decay by at most 2^-100)
+#define KDA_CHUNK_REF_LOG2_MIN (-25.f)
 
 // ============================================================ the kernel
 template <class Cfg>
@@ -677,12 +691,12 @@ struct ChunkKernel {
   }
 
   // ---------------------------------------------------------------- prep
-  // Inclusive product scan over the lanes of one cq inside a 16-lane DPP row
+  // Inclusive sum scan over the lanes of one cq inside a 16-lane DPP row
   // (stride CQ): the token groups of one 16-token block.
   template <int D>
   static __device__ __forceinline__ float row_scan(float x) {
     if constexpr (D < 16) {
-      x *= dpp_row_shr<D>(x);
+      x += dpp_row_shr0<D>(x);
       return row_scan<2 * D>(x);
     } else {
       return x;
@@ -703,7 +717,7 @@ struct ChunkKernel {
   //    rest of each ratio is a product over whole blocks, which the tiles
   //    (F_IJ) and the state products (P_b) apply per channel.
   // KIT = -K_end^T, K_end_i = k_i Gamma_L / Gamma_i, in either form.  Returns
-  // (wave-uniform) bit 0: some block decays below KDA_BLOCK_DECAY_MIN, past
+  // (wave-uniform) bit 0: some block decays below 2^KDA_BLOCK_LOG2_MIN, past
   // what the block-start reference can scale; bit 1: block-start references.
   static __device__ __forceinline__ int prep(const Raw& r, LDS char* smem, float scale,
                                              const Prologue& pro, float ea, int hi) {
@@ -726,6 +740,8 @@ struct ChunkKernel {
     LDS float* GL = (LDS float*)(smem + Cfg::OFF_GL);
     LDS float* BT = (LDS float*)(smem + Cfg::OFF_BT);
     LDS float* DT = (LDS float*)(smem + Cfg::OFF_DT);
+    LDS float* FA = (LDS float*)(smem + Cfg::OFF_FA);
+    LDS float* FM = (LDS float*)(smem + Cfg::OFF_FM);
     LDS float* DP = (LDS float*)(smem + Cfg::OFF_DP);
     LDS float* DF = (LDS float*)(smem + Cfg::OFF_DF);
 
@@ -746,57 +762,112 @@ struct ChunkKernel {
       gbias[4] = b1[0]; gbias[5] = b1[1]; gbias[6] = b1[2]; gbias[7] = b1[3];
     }
 
-    // Pi of the lane's tokens: running products over its TPL tokens, then a
-    // product scan over the block's token groups (one DPP row) and one group
-    // back; the block's last group holds T_b.
-    float cp[TPL][CPL];
+    // log2 Pi of the lane's tokens: running sums of log2 alpha over its TPL
+    // tokens, then a sum scan over the block's token groups (one DPP row) and
+    // one group back; the block's last group holds log2 T_b.
+    constexpr float LOG2E = 1.4426950408889634f;
+    float ls[TPL][CPL];
 #pragma unroll
     for (int t = 0; t < TPL; ++t)
 #pragma unroll
       for (int c = 0; c < CPL; ++c) {
         const float gr = __uint_as_float(r.g[t].word(c));
         const bool real = TPL * tg + t < hi;
-        const float a = __expf(xg ? (real ? gate_logalpha(gr, ea, gbias[c]) : 0.f) : gr);
-        cp[t][c] = (t == 0) ? a : cp[t - 1][c] * a;
+        const float la = (xg ? (real ? gate_logalpha(gr, ea, gbias[c]) : 0.f) : gr) * LOG2E;
+        ls[t][c] = (t == 0) ? la : ls[t - 1][c] + la;
       }
     float ex[CPL], tb[CPL];
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
-      tb[c] = row_scan<CQ>(cp[TPL - 1][c]);
-      ex[c] = dpp_row_shr<CQ>(tb[c]);
+      tb[c] = row_scan<CQ>(ls[TPL - 1][c]);
+      ex[c] = dpp_row_shr0<CQ>(tb[c]);
     }
     if (tg % GPB == GPB - 1) {
       *lds_ptr<f32x4>(DT + blk * DK + frag_pos(kc0)) = f32x4{tb[0], tb[1], tb[2], tb[3]};
       *lds_ptr<f32x4>(DT + blk * DK + frag_pos(kc0 + 4)) = f32x4{tb[4], tb[5], tb[6], tb[7]};
     }
-    // Every partial product is at least its block's total, so the wave's
-    // minimum over them is its minimum over the T_b.
-    bool weak = false, gone = false;
+    // -v and the unpacked q (work without decay factors, while the block
+    // totals reach LDS)
+    float qv[TPL][CPL];
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-      weak |= !(tb[c] >= 2.98023223876953125e-08f);       // 2^-25
-      gone |= !(tb[c] >= KDA_BLOCK_DECAY_MIN);
+    for (int t = 0; t < TPL; ++t) {
+      st_neg(BV + (TPL * tg + t) * Cfg::LD_V + vc0, r.v[t]);   // -v: the sign bits flipped
+      r.q[t].unpack(qv[t]);
     }
-    const bool blockref = __any(weak), bad = __any(gone);
     __asm__ __volatile__("" ::: "memory");
 
-    // The four block totals of the lane's channels, read back while the work
-    // that needs no decay factor goes on (a wave's LDS accesses complete in
-    // order; each wave reads back only its own channels).
-    f32x4 tx[4], ty[4];
+    // The block factors, one (block, channel) pair of the wave per lane (a
+    // wave's LDS accesses complete in order; each wave reads back only its
+    // own channels), from the log2 block totals l_0 .. l_3 of the channel:
+    //   chunk start: FA = P_b, FM = Gamma_L;  block start: FA = 1, FM = TQ_b
+    // with TQ_b = T_b .. T_3, and for the other waves Gamma_L, P_b and F_bJ.
+    // The wave takes block-start references if some block of some channel
+    // decays by more than 2^-25 (so chunk-start references stay above
+    // Gamma_L >= 2^-100), and flags the chunk for the token-by-token path if
+    // one decays below 2^KDA_BLOCK_LOG2_MIN.
+    constexpr int CW = DK / NW, NPASS = (4 * CW + 63) / 64;
+    float lt[NPASS][4];
+    bool weak = false, gone = false;
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      tx[b] = *lds_ptr<const f32x4>(DT + b * DK + frag_pos(kc0));
-      ty[b] = *lds_ptr<const f32x4>(DT + b * DK + frag_pos(kc0 + 4));
+    for (int ps = 0; ps < NPASS; ++ps) {
+      const int pp = 64 * ps + l;
+      const int pc = frag_pos(w * CW + (pp % CW));
+#pragma unroll
+      for (int b = 0; b < 4; ++b) lt[ps][b] = (pp < 4 * CW) ? DT[b * DK + pc] : 0.f;
+      const float mn = fminf(fminf(lt[ps][0], lt[ps][1]), fminf(lt[ps][2], lt[ps][3]));
+      weak |= !(mn >= KDA_CHUNK_REF_LOG2_MIN);
+      gone |= !(mn >= KDA_BLOCK_LOG2_MIN);
+    }
+    const bool blockref = __any(weak), bad = __any(gone);
+#pragma unroll
+    for (int ps = 0; ps < NPASS; ++ps) {
+      const int pp = 64 * ps + l;
+      if (pp < 4 * CW) {
+        const int b = pp / CW, c = w * CW + pp % CW, pc = frag_pos(c);
+        const float l0 = lt[ps][0], l1 = lt[ps][1], l2 = lt[ps][2], l3 = lt[ps][3];
+        const bool c1 = b >= 1, c2 = b >= 2, c3 = b == 3;
+        const float lp = (c1 ? l0 : 0.f) + (c2 ? l1 : 0.f) + (c3 ? l2 : 0.f);
+        const float lg = (l0 + l1) + (l2 + l3);
+        const float gf = __builtin_amdgcn_exp2f(lg);
+        if (!blockref) {
+          FA[b * DK + pc] = __builtin_amdgcn_exp2f(lp);
+          FM[b * DK + pc] = gf;
+          if (c1) {
+            DP[b * DK + pc] = 1.f;
+            const int pb0 = b * (b - 1) / 2;
+            DF[(pb0 + b - 1) * DK + pc] = 1.f;
+            if (c2) DF[(pb0 + b - 2) * DK + pc] = 1.f;
+            if (c3) DF[pb0 * DK + pc] = 1.f;
+          }
+        } else {
+          FA[b * DK + pc] = 1.f;
+          FM[b * DK + pc] = __builtin_amdgcn_exp2f(lg - lp);
+          if (c1) {
+            DP[b * DK + pc] = __builtin_amdgcn_exp2f(lp);
+            // F_{b,b-1} = T_{b-1}, F_{b,b-2} = T_{b-2} T_{b-1}, F_{3,0} = T_0 T_1 T_2
+            const float lm1 = c3 ? l2 : (c2 ? l1 : l0);
+            const float lm2 = c3 ? l1 : l0;
+            const int pb0 = b * (b - 1) / 2;
+            DF[(pb0 + b - 1) * DK + pc] = __builtin_amdgcn_exp2f(lm1);
+            if (c2) DF[(pb0 + b - 2) * DK + pc] = __builtin_amdgcn_exp2f(lm2 + lm1);
+            if (c3) DF[pb0 * DK + pc] = __builtin_amdgcn_exp2f(lp);
+          }
+        }
+        if (b == 0) GL[c] = gf;
+      }
     }
     __asm__ __volatile__("" ::: "memory");
-    // -v, and q and k unpacked (and L2-normalised)
-    float qv[TPL][CPL], kv[TPL][CPL];
+    // the lane's factors (issued now, used after the k work below)
+    const f32x4 fa0 = *lds_ptr<const f32x4>(FA + blk * DK + frag_pos(kc0));
+    const f32x4 fa1 = *lds_ptr<const f32x4>(FA + blk * DK + frag_pos(kc0 + 4));
+    const f32x4 fm0 = *lds_ptr<const f32x4>(FM + blk * DK + frag_pos(kc0));
+    const f32x4 fm1 = *lds_ptr<const f32x4>(FM + blk * DK + frag_pos(kc0 + 4));
+    __asm__ __volatile__("" ::: "memory");
+    // k unpacked, and the L2 norms (FU)
+    float kv[TPL][CPL];
 #pragma unroll
     for (int t = 0; t < TPL; ++t) {
       const int i = TPL * tg + t;
-      st_neg(BV + i * Cfg::LD_V + vc0, r.v[t]);     // -v, exactly: the sign bits flipped
-      r.q[t].unpack(qv[t]);
       r.k[t].unpack(kv[t]);
       if (Cfg::FU && (pro.flags & PRO_L2NORM)) {
         // the token's squared norms: the sum of the waves' partials
@@ -818,67 +889,8 @@ struct ChunkKernel {
         }
       }
     }
-    float tt[4][CPL];
-#pragma unroll
-    for (int b = 0; b < 4; ++b)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        tt[b][c] = tx[b][c];
-        tt[b][c + 4] = ty[b][c];
-      }
-    // Per channel: fa takes Pi to the operands' reference (P_b, or 1), fm
-    // takes -k / (that reference) to -K_end (Gamma_L, or TQ_b = T_b .. T_3).
-    // Lane-dependent choices are products of selects against 1.
-    const bool b1 = blk >= 1, b2 = blk >= 2, b3 = blk == 3;
-    float fa[CPL], fm[CPL], pb[CPL], gl[CPL];
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-      pb[c] = (b1 ? tt[0][c] : 1.f) * (b2 ? tt[1][c] : 1.f) * (b3 ? tt[2][c] : 1.f);
-      gl[c] = (tt[0][c] * tt[1][c]) * (tt[2][c] * tt[3][c]);
-    }
-    if (blockref) {
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) {
-        fa[c] = 1.f;
-        fm[c] = (b1 ? 1.f : tt[0][c]) * (b2 ? 1.f : tt[1][c]) * (b3 ? 1.f : tt[2][c]) * tt[3][c];
-      }
-    } else {
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) {
-        fa[c] = pb[c];
-        fm[c] = gl[c];
-      }
-    }
-    // The first token group of each block writes the block's factors for the
-    // other waves: Gamma_L (block 0), and for block-referenced channels P_b
-    // and the F_IJ with I = b (1 for chunk-referenced channels).
-    if (tg % GPB == 0) {
-      auto st8 = [&](LDS float* row, const float (&x)[CPL]) {
-        *lds_ptr<f32x4>(row + frag_pos(kc0)) = f32x4{x[0], x[1], x[2], x[3]};
-        *lds_ptr<f32x4>(row + frag_pos(kc0 + 4)) = f32x4{x[4], x[5], x[6], x[7]};
-      };
-      if (blk == 0) {
-        *lds_ptr<f32x4>(GL + kc0) = f32x4{gl[0], gl[1], gl[2], gl[3]};
-        *lds_ptr<f32x4>(GL + kc0 + 4) = f32x4{gl[4], gl[5], gl[6], gl[7]};
-      } else {
-        // F_{b, b-1} = T_{b-1}, F_{b, b-2} = T_{b-2} T_{b-1}, F_{3,0} = T_0 T_1 T_2
-        float f1[CPL], f2[CPL], f3[CPL], p[CPL];
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-          const float bm1 = b3 ? tt[2][c] : (b2 ? tt[1][c] : tt[0][c]);
-          const float bm2 = b3 ? tt[1][c] : tt[0][c];
-          f1[c] = blockref ? bm1 : 1.f;
-          f2[c] = blockref ? bm2 * bm1 : 1.f;
-          f3[c] = blockref ? tt[0][c] * tt[1][c] * tt[2][c] : 1.f;
-          p[c] = blockref ? pb[c] : 1.f;
-        }
-        const int pbase = blk * (blk - 1) / 2;           // pair (b, 0)
-        st8(DP + blk * DK, p);
-        st8(DF + (pbase + blk - 1) * DK, f1);
-        if (b2) st8(DF + (pbase + blk - 2) * DK, f2);
-        if (b3) st8(DF + pbase * DK, f3);
-      }
-    }
+    const float fa[CPL] = {fa0[0], fa0[1], fa0[2], fa0[3], fa1[0], fa1[1], fa1[2], fa1[3]};
+    const float fm[CPL] = {fm0[0], fm0[1], fm0[2], fm0[3], fm1[0], fm1[1], fm1[2], fm1[3]};
 
     // the operands; -K_end of the lane's tokens per key channel for the
     // key-major copy
@@ -891,7 +903,7 @@ struct ChunkKernel {
       float qg[CPL], kg[CPL], ki[CPL];
 #pragma unroll
       for (int c = 0; c < CPL; ++c) {
-        const float gam = ex[c] * cp[t][c] * fa[c];
+        const float gam = __builtin_amdgcn_exp2f(ex[c] + ls[t][c]) * fa[c];
         const float inv = __builtin_amdgcn_rcpf(gam);
         qg[c] = scale * qv[t][c] * gam;
         kg[c] = kv[t][c] * gam;                 // beta comes later
@@ -986,8 +998,9 @@ struct ChunkKernel {
   // -Aqk row-major to AQ (columns permuted like the 32-deep operand that reads
   // them), and the diagonal R tiles (in the other orientation) to RD, fp32,
   // column-contiguous, for the inverse.
-  // sc: some wave references its channels to block starts (F_IJ != 1).
-  static __device__ __forceinline__ void tile_qk(LDS char* smem, int I, int J, bool sc) {
+  // SC: some wave references its channels to block starts (F_IJ != 1).
+  template <bool SC>
+  static __device__ __forceinline__ void tile_qk(LDS char* smem, int I, int J) {
     const int l = lane_fresh();
     const LDS T* QG = (const LDS T*)(smem + Cfg::OFF_QG);
     const LDS T* KG = (const LDS T*)(smem + Cfg::OFF_KG);
@@ -1000,7 +1013,7 @@ struct ChunkKernel {
     for (int ks = 0; ks < NKS; ++ks) {
       typename Op::F32 b = Op::ld32_rmp(l, KI, Cfg::LD_K, 16 * J, 32 * ks);
       if constexpr (!Cfg::SG) {
-        if (I != J && sc) {
+        if (SC && I != J) {
           const LDS float* F = (const LDS float*)(smem + Cfg::OFF_DF) +
                                (I * (I - 1) / 2 + J) * DK + 32 * ks + 8 * (l >> 4);
           b.lo = Op::pack(Op::unpack(b.lo) * *lds_ptr<const f32x4>(F));
@@ -1121,9 +1134,9 @@ struct ChunkKernel {
   // 32-deep operands over key channels (lane: value column, k: channels).
   // KDA: the channels of a block-referenced wave take the state into block
   // I's products as Diag(P_I) S (P_I = T_0 .. T_{I-1}; 1 for the others).
+  template <bool SC>
   static __device__ __forceinline__ void scan_y(LDS char* smem, const f32x4 (&S)[MTK][NVT],
-                                                f32x4 (&Y)[4][NVT], f32x4 (&O)[4][NVT],
-                                                bool sc) {
+                                                f32x4 (&Y)[4][NVT], f32x4 (&O)[4][NVT]) {
     const int w = threadIdx.x >> 6, l = lane_fresh();
     const LDS T* KG = (const LDS T*)(smem + Cfg::OFF_KG);
     const LDS T* QG = (const LDS T*)(smem + Cfg::OFF_QG);
@@ -1134,13 +1147,13 @@ struct ChunkKernel {
     const int vw0 = w * VW;
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
-      if (I == 0 || (!Cfg::SG && sc)) {
+      if (I == 0 || (!Cfg::SG && SC)) {
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
           for (int nt = 0; nt < NVT; ++nt) {
             f32x4 lo = S[2 * ks][nt], hi = S[2 * ks + 1][nt];
-            if (!Cfg::SG && I > 0 && sc) {
+            if (!Cfg::SG && SC && I > 0) {
               // rows 32 ks + 4g + r and 32 ks + 16 + 4g + r: fragment positions
               // 32 ks + 8g + r and 32 ks + 8g + 4 + r
               const LDS float* P = DP + I * DK + 32 * ks + 8 * (l >> 4);
@@ -1441,31 +1454,31 @@ struct ChunkKernel {
   // wave's LDS accesses complete in order), waves 4-7 form the six
   // off-diagonal pairs; each wave's case is one scheduling region, so VALU
   // (inverse) and MFMA (tiles, Y, S^T QG^T) interleave.
+  template <bool SC>
   static __device__ __forceinline__ void middle(LDS char* smem, f32x4 (&S)[MTK][NVT],
-                                                f32x4 (&Y)[4][NVT], f32x4 (&O)[4][NVT],
-                                                bool sc) {
+                                                f32x4 (&Y)[4][NVT], f32x4 (&O)[4][NVT]) {
     const int w = threadIdx.x >> 6;
     if (NW == 8) {
       switch (__builtin_amdgcn_readfirstlane(w)) {
-        case 0: tile_qk(smem, 0, 0, sc); invert_diag<0>(smem); scan_y(smem, S, Y, O, sc); break;
-        case 1: tile_qk(smem, 1, 1, sc); invert_diag<1>(smem); scan_y(smem, S, Y, O, sc); break;
-        case 2: tile_qk(smem, 2, 2, sc); invert_diag<2>(smem); scan_y(smem, S, Y, O, sc); break;
-        case 3: tile_qk(smem, 3, 3, sc); invert_diag<3>(smem); scan_y(smem, S, Y, O, sc); break;
-        case 4: tile_qk(smem, 1, 0, sc); tile_qk(smem, 3, 2, sc); scan_y(smem, S, Y, O, sc); break;
-        case 5: tile_qk(smem, 2, 0, sc); tile_qk(smem, 2, 1, sc); scan_y(smem, S, Y, O, sc); break;
-        case 6: tile_qk(smem, 3, 0, sc); scan_y(smem, S, Y, O, sc); break;
-        default: tile_qk(smem, 3, 1, sc); scan_y(smem, S, Y, O, sc); break;
+        case 0: tile_qk<SC>(smem, 0, 0); invert_diag<0>(smem); scan_y<SC>(smem, S, Y, O); break;
+        case 1: tile_qk<SC>(smem, 1, 1); invert_diag<1>(smem); scan_y<SC>(smem, S, Y, O); break;
+        case 2: tile_qk<SC>(smem, 2, 2); invert_diag<2>(smem); scan_y<SC>(smem, S, Y, O); break;
+        case 3: tile_qk<SC>(smem, 3, 3); invert_diag<3>(smem); scan_y<SC>(smem, S, Y, O); break;
+        case 4: tile_qk<SC>(smem, 1, 0); tile_qk<SC>(smem, 3, 2); scan_y<SC>(smem, S, Y, O); break;
+        case 5: tile_qk<SC>(smem, 2, 0); tile_qk<SC>(smem, 2, 1); scan_y<SC>(smem, S, Y, O); break;
+        case 6: tile_qk<SC>(smem, 3, 0); scan_y<SC>(smem, S, Y, O); break;
+        default: tile_qk<SC>(smem, 3, 1); scan_y<SC>(smem, S, Y, O); break;
       }
     } else {
       switch (__builtin_amdgcn_readfirstlane(w)) {
-        case 0: tile_qk(smem, 0, 0, sc); invert_diag<0>(smem); tile_qk(smem, 1, 0, sc);
-                tile_qk(smem, 2, 0, sc); scan_y(smem, S, Y, O, sc); break;
-        case 1: tile_qk(smem, 1, 1, sc); invert_diag<1>(smem); tile_qk(smem, 2, 1, sc);
-                tile_qk(smem, 3, 0, sc); scan_y(smem, S, Y, O, sc); break;
-        case 2: tile_qk(smem, 2, 2, sc); invert_diag<2>(smem); tile_qk(smem, 3, 1, sc);
-                scan_y(smem, S, Y, O, sc); break;
-        default: tile_qk(smem, 3, 3, sc); invert_diag<3>(smem); tile_qk(smem, 3, 2, sc);
-                 scan_y(smem, S, Y, O, sc); break;
+        case 0: tile_qk<SC>(smem, 0, 0); invert_diag<0>(smem); tile_qk<SC>(smem, 1, 0);
+                tile_qk<SC>(smem, 2, 0); scan_y<SC>(smem, S, Y, O); break;
+        case 1: tile_qk<SC>(smem, 1, 1); invert_diag<1>(smem); tile_qk<SC>(smem, 2, 1);
+                tile_qk<SC>(smem, 3, 0); scan_y<SC>(smem, S, Y, O); break;
+        case 2: tile_qk<SC>(smem, 2, 2); invert_diag<2>(smem); tile_qk<SC>(smem, 3, 1);
+                scan_y<SC>(smem, S, Y, O); break;
+        default: tile_qk<SC>(smem, 3, 3); invert_diag<3>(smem); tile_qk<SC>(smem, 3, 2);
+                 scan_y<SC>(smem, S, Y, O); break;
       }
     }
   }
@@ -1553,7 +1566,12 @@ struct ChunkKernel {
         load_raw<LOAD_V>(raw, offs, q, k, v, g, beta, next, H, h, nlen);
         compiler_fence();
         f32x4 Y[4][NVT], O[4][NVT];
-        middle(smem, S, Y, O, (any & 2) != 0);
+        // one instance per reference mode: the common chunk-start case
+        // carries no block factors at all
+        if (any & 2)
+          middle<true>(smem, S, Y, O);
+        else
+          middle<false>(smem, S, Y, O);
         compiler_fence();
         load_raw<LOAD_Q | LOAD_K>(raw, offs, q, k, v, g, beta, next, H, h, nlen);
         __syncthreads();                                         // B2
@@ -1676,7 +1694,7 @@ static hipError_t launch_chunk_t(const void* q, const void* k, const void* v, co
 // all chunks at once) forms the outputs.  Every factor goes through the
 // workspace as bf16 MFMA fragments in the exact lane order its consumer
 // reads, one 16-byte load per lane per fragment.  A chunk with a 16-token
-// block that decays below KDA_BLOCK_DECAY_MIN in some channel (the fused
+// block that decays below 2^KDA_BLOCK_LOG2_MIN in some channel (the fused
 // kernel's guard) is flagged by stage A and recomputed token by token by
 // stage B.
 template <class Cfg>
@@ -1723,16 +1741,17 @@ struct ParKernel {
 
   // The state-independent tiles and inverses (the fused kernel's middle
   // interval without its state products).
-  static __device__ __forceinline__ void tiles(LDS char* smem, bool sc) {
+  template <bool SC>
+  static __device__ __forceinline__ void tiles(LDS char* smem) {
     switch (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) {
-      case 0: K::tile_qk(smem, 0, 0, sc); K::template invert_diag<0>(smem); break;
-      case 1: K::tile_qk(smem, 1, 1, sc); K::template invert_diag<1>(smem); break;
-      case 2: K::tile_qk(smem, 2, 2, sc); K::template invert_diag<2>(smem); break;
-      case 3: K::tile_qk(smem, 3, 3, sc); K::template invert_diag<3>(smem); break;
-      case 4: K::tile_qk(smem, 1, 0, sc); K::tile_qk(smem, 3, 2, sc); break;
-      case 5: K::tile_qk(smem, 2, 0, sc); K::tile_qk(smem, 2, 1, sc); break;
-      case 6: K::tile_qk(smem, 3, 0, sc); break;
-      default: K::tile_qk(smem, 3, 1, sc); break;
+      case 0: K::template tile_qk<SC>(smem, 0, 0); K::template invert_diag<0>(smem); break;
+      case 1: K::template tile_qk<SC>(smem, 1, 1); K::template invert_diag<1>(smem); break;
+      case 2: K::template tile_qk<SC>(smem, 2, 2); K::template invert_diag<2>(smem); break;
+      case 3: K::template tile_qk<SC>(smem, 3, 3); K::template invert_diag<3>(smem); break;
+      case 4: K::template tile_qk<SC>(smem, 1, 0); K::template tile_qk<SC>(smem, 3, 2); break;
+      case 5: K::template tile_qk<SC>(smem, 2, 0); K::template tile_qk<SC>(smem, 2, 1); break;
+      case 6: K::template tile_qk<SC>(smem, 3, 0); break;
+      default: K::template tile_qk<SC>(smem, 3, 1); break;
     }
   }
 
@@ -1898,7 +1917,12 @@ __global__ __launch_bounds__(Cfg::NTHREADS, 1) void chunk_intra_kernel(
     // a flagged chunk is redone token by token by stage B
     K::template load_raw<K::LOAD_V>(raw, offs, q, k, v, g, beta, nrow0, H, nh, nlen);
     compiler_fence();
-    if (!any_bad) P::tiles(smem, (any & 2) != 0);
+    if (!any_bad) {
+      if (any & 2)
+        P::template tiles<true>(smem);
+      else
+        P::template tiles<false>(smem);
+    }
     compiler_fence();
     __syncthreads();
     K::template load_raw<K::LOAD_Q | K::LOAD_K>(raw, offs, q, k, v, g, beta, nrow0, H, nh, nlen);
