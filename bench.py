@@ -253,13 +253,41 @@ def main():
     del dr, Sr, o_rec
     torch.cuda.empty_cache()
 
+    # ---------------------------------------------------------------- Gated DeltaNet prefill
+    log("generating Gated DeltaNet prefill inputs (one gate per token and head)")
+    dg = inputs.prefill_inputs(P["B"], P["T"], P["H"], P["dk"], P["dv"], io=P["io"], seed=0,
+                               with_S0=False, device=dev, gate="gdn")
+
+    def gdn_step():
+        kda.chunk_fwd(dg["q"], dg["k"], dg["v"], dg["g"], dg["beta"], S0=None, out=out, S_final=Sf)
+
+    for _ in range(args.warmup):
+        gdn_step()
+    torch.cuda.synchronize()
+    evg = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for a, b in evg:
+        a.record(stream)
+        gdn_step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    gdn_wall = (time.perf_counter() - t0) / args.steps
+    tokens = P["B"] * P["T"]
+    gdn_ms = float(np.mean([a.elapsed_time(b) for a, b in evg]))
+    gdn_b = prefill_alg_bytes(P["B"], P["T"], P["H"], P["dk"], P["dv"], P["io"], gate_dims=1)
+    gdn_gbs = gdn_b / (gdn_ms * 1e-3) / 1e9
+    log("gdn prefill: %.3f ms/step (wall), kernel %.3f ms avg, %.3e tokens/s, %.0f GB/s"
+        % (gdn_wall * 1e3, gdn_ms, tokens / gdn_wall, gdn_gbs))
+
     # ---------------------------------------------------------------- headline prefill
-    # Timed after the decode legs, whose ~100 ms of back-to-back launches bring
-    # the engine clock to the level it holds under sustained load: at the start
-    # of a burst after idle the clock drops to about 1.6 GHz and recovers to
-    # about 2.35 GHz over some 30 ms, while the kernel's cycle count per launch
-    # stays the same (GRBM_GUI_ACTIVE per dispatch, profiles/).  The launch
-    # times of the warm-up and timed steps are printed to stderr.
+    # Timed right after the Gated DeltaNet prefill (the same kernel family,
+    # about 17 ms of back-to-back launches): at the start of a burst after
+    # idle the engine clock drops to about 1.7 GHz and recovers to about
+    # 2.2 GHz over some 25 launches of this kernel, while the kernel's cycle
+    # count per launch stays the same (GRBM_GUI_ACTIVE per dispatch,
+    # profiles/).  The launch times of the warm-up and timed steps are printed
+    # to stderr.
     warm_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(args.warmup)]
     for a, b in warm_ev:
@@ -307,35 +335,7 @@ def main():
     sg_ms = float(np.mean([a.elapsed_time(b) for a, b in evs_s]))
     log("prefill, 8 of 128 channels at log alpha ~ U[-5,-2]: kernel %.3f ms avg (%.3f x the "
         "plain inputs)" % (sg_ms, sg_ms / avg_kernel_ms))
-    del d
-    torch.cuda.empty_cache()
-
-    # ---------------------------------------------------------------- Gated DeltaNet prefill
-    log("generating Gated DeltaNet prefill inputs (one gate per token and head)")
-    dg = inputs.prefill_inputs(P["B"], P["T"], P["H"], P["dk"], P["dv"], io=P["io"], seed=0,
-                               with_S0=False, device=dev, gate="gdn")
-
-    def gdn_step():
-        kda.chunk_fwd(dg["q"], dg["k"], dg["v"], dg["g"], dg["beta"], S0=None, out=out, S_final=Sf)
-
-    for _ in range(args.warmup):
-        gdn_step()
-    torch.cuda.synchronize()
-    evg = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    for a, b in evg:
-        a.record(stream)
-        gdn_step()
-        b.record(stream)
-    torch.cuda.synchronize()
-    gdn_wall = (time.perf_counter() - t0) / args.steps
-    gdn_ms = float(np.mean([a.elapsed_time(b) for a, b in evg]))
-    gdn_b = prefill_alg_bytes(P["B"], P["T"], P["H"], P["dk"], P["dv"], P["io"], gate_dims=1)
-    gdn_gbs = gdn_b / (gdn_ms * 1e-3) / 1e9
-    log("gdn prefill: %.3f ms/step (wall), kernel %.3f ms avg, %.3e tokens/s, %.0f GB/s"
-        % (gdn_wall * 1e3, gdn_ms, tokens / gdn_wall, gdn_gbs))
-    del dg
+    del d, dg
     torch.cuda.empty_cache()
 
     # ---------------------------------------------------------------- fused input transforms

@@ -382,16 +382,20 @@ struct ChunkCfg {
   // totals T_b, and per block the factors that take the block-local decay
   // to the operands' reference (FA) and -k / (that reference) to -K_end (FM).
   // For the tiles and scan_y: [4][DK] the state factors of block-referenced
-  // channels (P_b = T_0 .. T_{b-1}, else 1) and [6][DK] their tile factors
+  // channels (P_b = T_0 .. T_{b-1}, else 1), [6][DK] their tile factors
   // F_IJ = T_J .. T_{I-1} (else 1) of the pairs I > J in the order (1,0)
-  // (2,0) (2,1) (3,0) (3,1) (3,2).
+  // (2,0) (2,1) (3,0) (3,1) (3,2), and a mask of the chunk-referenced
+  // channels.
   static constexpr int OFF_DT = OFF_KT + DK * LD_KT * SZ;
   static constexpr int OFF_FA = OFF_DT + 4 * DK * 4;
   static constexpr int OFF_FM = OFF_FA + 4 * DK * 4;
   static constexpr int OFF_DP = OFF_FM + 4 * DK * 4;
   static constexpr int OFF_DF = OFF_DP + 4 * DK * 4;
-  static constexpr int SZ_D = SG ? 0 : 22 * DK * 4;
+  // [DK] uint16: 0xffff for chunk-referenced channels, 0 for block-referenced
+  static constexpr int OFF_MK = OFF_DF + 6 * DK * 4;
+  static constexpr int SZ_D = SG ? 0 : OFF_MK - OFF_DT + ((DK * 2 + 15) / 16) * 16;
   static constexpr int OFF_GL = OFF_DT + SZ_D;
+  static_assert(SG || OFF_GL >= OFF_MK + DK * 2, "the decay factors fit their region");
   static constexpr int OFF_BT = OFF_GL + DK * 4;          // beta of the chunk's tokens
   static constexpr int OFF_FL = OFF_BT + C * 4;
   // FU only: per-wave partial squared norms of q and k, [C][NW] each, and the
@@ -420,6 +424,19 @@ struct ChunkCfg {
 // log2 of the block decay down to which chunk-start references stay in use
 // (four blocks then decay by at most 2^-100)
 #define KDA_CHUNK_REF_LOG2_MIN (-25.f)
+// log2 of the bound below which the state factors of a block-referenced
+// channel (P_b for b >= 1, all at most T_0) are taken as 0: the operands they
+// multiply are bounded by |k| and |s q| (Pi <= 1), so the terms stay below
+// 2^-40 of |k| |S|, far under fp32 rounding of the sums they enter.  (The
+// tile factors F_IJ are always applied: the -k / Pi_j they multiply grows as
+// they shrink.)
+#define KDA_STATE_LOG2_NEGLIGIBLE (-40.f)
+
+// Reference modes of a chunk (wave-uniform after the flag vote): every key
+// channel chunk-referenced; some block-referenced, all with negligible state
+// factors (a channel mask replaces them in the state products); some with
+// state factors that must be applied.
+enum { KDA_MODE_CHUNK = 0, KDA_MODE_MASK = 1, KDA_MODE_SCALE = 2 };
 
 // ============================================================ the kernel
 template <class Cfg>
@@ -706,11 +723,11 @@ struct ChunkKernel {
   // KDA: the decay factors and the gate-scaled operands of one chunk (tokens
   // [0, hi) real, the rest identity tokens), "Kimi Unveils Delta Attention
   // and K3 Architecture Updates", section 6.1 (cumulative decay) and 6.6.
-  // Each wave picks the reference point of its key channels' factors:
+  // Each key channel picks the reference point of its factors:
   //  * chunk start (the common case): QG_i = s q_i Gamma_i, KG_i = k_i
   //    Gamma_i, KI_i = -k_i / Gamma_i.  Safe while Gamma_L >= 2^-100, which
   //    holds when every 16-token block decays by at most 2^-25;
-  //  * block start, when some block of some channel of the wave decays more:
+  //  * block start, when some block of the channel decays more:
   //    Pi_i = Gamma_i / Gamma_{16b-1} (b the token's 16-token block) in place
   //    of Gamma_i.  Pi stays within [T_b, 1] (T_b the block's decay), so the
   //    operands stay in range however much the chunk decays as a whole; the
@@ -718,7 +735,8 @@ struct ChunkKernel {
   //    (F_IJ) and the state products (P_b) apply per channel.
   // KIT = -K_end^T, K_end_i = k_i Gamma_L / Gamma_i, in either form.  Returns
   // (wave-uniform) bit 0: some block decays below 2^KDA_BLOCK_LOG2_MIN, past
-  // what the block-start reference can scale; bit 1: block-start references.
+  // what the block-start reference can scale; bits 1-2: the wave's reference
+  // mode (KDA_MODE_*).
   static __device__ __forceinline__ int prep(const Raw& r, LDS char* smem, float scale,
                                              const Prologue& pro, float ea, int hi) {
     if constexpr (Cfg::SG) {
@@ -744,6 +762,7 @@ struct ChunkKernel {
     LDS float* FM = (LDS float*)(smem + Cfg::OFF_FM);
     LDS float* DP = (LDS float*)(smem + Cfg::OFF_DP);
     LDS float* DF = (LDS float*)(smem + Cfg::OFF_DF);
+    LDS uint16_t* MK = (LDS uint16_t*)(smem + Cfg::OFF_MK);
 
     // beta is applied to R and Y later, where it scales whole rows (R =
     // Diag(beta) strict_tril(...), Ebar = Diag(beta)(v - (k Gamma) S))
@@ -798,16 +817,18 @@ struct ChunkKernel {
 
     // The block factors, one (block, channel) pair of the wave per lane (a
     // wave's LDS accesses complete in order; each wave reads back only its
-    // own channels), from the log2 block totals l_0 .. l_3 of the channel:
+    // own channels), from the log2 block totals l_0 .. l_3 of the channel.
+    // A channel takes block-start references if one of its blocks decays by
+    // more than 2^KDA_CHUNK_REF_LOG2_MIN (chunk-start references then stay
+    // above Gamma_L >= 2^-100):
     //   chunk start: FA = P_b, FM = Gamma_L;  block start: FA = 1, FM = TQ_b
-    // with TQ_b = T_b .. T_3, and for the other waves Gamma_L, P_b and F_bJ.
-    // The wave takes block-start references if some block of some channel
-    // decays by more than 2^-25 (so chunk-start references stay above
-    // Gamma_L >= 2^-100), and flags the chunk for the token-by-token path if
-    // one decays below 2^KDA_BLOCK_LOG2_MIN.
+    // with TQ_b = T_b .. T_3, and for the other waves Gamma_L, P_b and F_bJ
+    // (1 for chunk-referenced channels) and the channel mask.  A chunk with a
+    // block below 2^KDA_BLOCK_LOG2_MIN is flagged for the token-by-token path.
     constexpr int CW = DK / NW, NPASS = (4 * CW + 63) / 64;
     float lt[NPASS][4];
-    bool weak = false, gone = false;
+    bool bref[NPASS];
+    bool any_ref = false, any_scale = false, gone = false;
 #pragma unroll
     for (int ps = 0; ps < NPASS; ++ps) {
       const int pp = 64 * ps + l;
@@ -815,10 +836,14 @@ struct ChunkKernel {
 #pragma unroll
       for (int b = 0; b < 4; ++b) lt[ps][b] = (pp < 4 * CW) ? DT[b * DK + pc] : 0.f;
       const float mn = fminf(fminf(lt[ps][0], lt[ps][1]), fminf(lt[ps][2], lt[ps][3]));
-      weak |= !(mn >= KDA_CHUNK_REF_LOG2_MIN);
+      bref[ps] = !(mn >= KDA_CHUNK_REF_LOG2_MIN);
+      any_ref |= bref[ps];
+      any_scale |= bref[ps] && !(lt[ps][0] < KDA_STATE_LOG2_NEGLIGIBLE);
       gone |= !(mn >= KDA_BLOCK_LOG2_MIN);
     }
-    const bool blockref = __any(weak), bad = __any(gone);
+    const int mode = __any(any_scale) ? KDA_MODE_SCALE : __any(any_ref) ? KDA_MODE_MASK
+                                                                         : KDA_MODE_CHUNK;
+    const bool bad = __any(gone);
 #pragma unroll
     for (int ps = 0; ps < NPASS; ++ps) {
       const int pp = 64 * ps + l;
@@ -829,7 +854,7 @@ struct ChunkKernel {
         const float lp = (c1 ? l0 : 0.f) + (c2 ? l1 : 0.f) + (c3 ? l2 : 0.f);
         const float lg = (l0 + l1) + (l2 + l3);
         const float gf = __builtin_amdgcn_exp2f(lg);
-        if (!blockref) {
+        if (!bref[ps]) {
           FA[b * DK + pc] = __builtin_amdgcn_exp2f(lp);
           FM[b * DK + pc] = gf;
           if (c1) {
@@ -853,7 +878,10 @@ struct ChunkKernel {
             if (c3) DF[pb0 * DK + pc] = __builtin_amdgcn_exp2f(lp);
           }
         }
-        if (b == 0) GL[c] = gf;
+        if (b == 0) {
+          GL[c] = gf;
+          MK[pc] = bref[ps] ? (uint16_t)0 : (uint16_t)0xffff;
+        }
       }
     }
     __asm__ __volatile__("" ::: "memory");
@@ -925,7 +953,7 @@ struct ChunkKernel {
       else
         st_vec(p, kit[c]);
     }
-    return (bad ? 1 : 0) | (blockref ? 2 : 0);
+    return (bad ? 1 : 0) | (mode << 1);
     }
   }
 
@@ -987,6 +1015,31 @@ struct ChunkKernel {
     }
   }
 
+  // A 32-deep operand fragment over key channels 32 ks .. 32 ks + 31 with the
+  // lane's block-referenced channels zeroed (the channel mask holds 16-bit
+  // all-ones or zeros in fragment order, one 16-byte read per lane).
+  static __device__ __forceinline__ typename Op::F32 mask_frag(LDS char* smem, typename Op::F32 f,
+                                                                int ks, int l) {
+    const LDS uint16_t* MK = (const LDS uint16_t*)(smem + Cfg::OFF_MK) + 32 * ks + 8 * (l >> 4);
+    if constexpr (Cfg::SZ == 2) {
+      const u32x4 m = *lds_ptr<const u32x4>(MK);
+      const u32x2 a = __builtin_bit_cast(u32x2, f.lo), b = __builtin_bit_cast(u32x2, f.hi);
+      f.lo = __builtin_bit_cast(typename Op::F16, u32x2{a[0] & m[0], a[1] & m[1]});
+      f.hi = __builtin_bit_cast(typename Op::F16, u32x2{b[0] & m[2], b[1] & m[3]});
+    } else {
+      const u32x4 m = *lds_ptr<const u32x4>(MK);
+      f32x4 lo = f.lo, hi = f.hi;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        lo[e] = ((m[e >> 1] >> (16 * (e & 1))) & 0xffffu) ? lo[e] : 0.f;
+        hi[e] = ((m[2 + (e >> 1)] >> (16 * (e & 1))) & 0xffffu) ? hi[e] : 0.f;
+      }
+      f.lo = lo;
+      f.hi = hi;
+    }
+    return f;
+  }
+
   // ---------------------------------------------------------------- phase A
   // R = strict_tril(KG KI^T) and Aqk = tril(QG KI^T) by 16x16 tiles, from
   // the stored -KI (so the products come out negated).  KDA: the operands
@@ -998,8 +1051,9 @@ struct ChunkKernel {
   // -Aqk row-major to AQ (columns permuted like the 32-deep operand that reads
   // them), and the diagonal R tiles (in the other orientation) to RD, fp32,
   // column-contiguous, for the inverse.
-  // SC: some wave references its channels to block starts (F_IJ != 1).
-  template <bool SC>
+  // MODE (KDA_MODE_*): whether some channel is block-referenced, so that the
+  // cross-block tiles take F_IJ.
+  template <int MODE>
   static __device__ __forceinline__ void tile_qk(LDS char* smem, int I, int J) {
     const int l = lane_fresh();
     const LDS T* QG = (const LDS T*)(smem + Cfg::OFF_QG);
@@ -1013,7 +1067,7 @@ struct ChunkKernel {
     for (int ks = 0; ks < NKS; ++ks) {
       typename Op::F32 b = Op::ld32_rmp(l, KI, Cfg::LD_K, 16 * J, 32 * ks);
       if constexpr (!Cfg::SG) {
-        if (SC && I != J) {
+        if (MODE != KDA_MODE_CHUNK && I != J) {
           const LDS float* F = (const LDS float*)(smem + Cfg::OFF_DF) +
                                (I * (I - 1) / 2 + J) * DK + 32 * ks + 8 * (l >> 4);
           b.lo = Op::pack(Op::unpack(b.lo) * *lds_ptr<const f32x4>(F));
@@ -1132,9 +1186,10 @@ struct ChunkKernel {
   // The parts that need no inverse: Y_I = Diag(beta_I) (KG_I S - V_I) and the S part of
   // the outputs, O_I^T = S^T QG_I^T, for the four token blocks, with S as
   // 32-deep operands over key channels (lane: value column, k: channels).
-  // KDA: the channels of a block-referenced wave take the state into block
-  // I's products as Diag(P_I) S (P_I = T_0 .. T_{I-1}; 1 for the others).
-  template <bool SC>
+  // KDA: block-referenced channels take the state into block I's products as
+  // Diag(P_I) S (P_I = T_0 .. T_{I-1}; 1 for the others), or drop out of
+  // blocks 1 .. 3 when P_1 is negligible (MODE).
+  template <int MODE>
   static __device__ __forceinline__ void scan_y(LDS char* smem, const f32x4 (&S)[MTK][NVT],
                                                 f32x4 (&Y)[4][NVT], f32x4 (&O)[4][NVT]) {
     const int w = threadIdx.x >> 6, l = lane_fresh();
@@ -1147,13 +1202,13 @@ struct ChunkKernel {
     const int vw0 = w * VW;
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
-      if (I == 0 || (!Cfg::SG && SC)) {
+      if (I == 0 || (!Cfg::SG && MODE == KDA_MODE_SCALE)) {
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
           for (int nt = 0; nt < NVT; ++nt) {
             f32x4 lo = S[2 * ks][nt], hi = S[2 * ks + 1][nt];
-            if (!Cfg::SG && SC && I > 0) {
+            if (!Cfg::SG && MODE == KDA_MODE_SCALE && I > 0) {
               // rows 32 ks + 4g + r and 32 ks + 16 + 4g + r: fragment positions
               // 32 ks + 8g + r and 32 ks + 8g + 4 + r
               const LDS float* P = DP + I * DK + 32 * ks + 8 * (l >> 4);
@@ -1162,6 +1217,12 @@ struct ChunkKernel {
             }
             SB[ks][nt] = typename Op::F32{Op::pack(lo), Op::pack(hi)};
           }
+      } else if (!Cfg::SG && MODE == KDA_MODE_MASK && I == 1) {
+        // blocks 1 .. 3: the block-referenced rows of S drop out (P_I < 2^-40)
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+          for (int nt = 0; nt < NVT; ++nt) SB[ks][nt] = mask_frag(smem, SB[ks][nt], ks, l);
       }
 #pragma unroll
       for (int nt = 0; nt < NVT; ++nt)
@@ -1454,31 +1515,31 @@ struct ChunkKernel {
   // wave's LDS accesses complete in order), waves 4-7 form the six
   // off-diagonal pairs; each wave's case is one scheduling region, so VALU
   // (inverse) and MFMA (tiles, Y, S^T QG^T) interleave.
-  template <bool SC>
+  template <int MODE>
   static __device__ __forceinline__ void middle(LDS char* smem, f32x4 (&S)[MTK][NVT],
                                                 f32x4 (&Y)[4][NVT], f32x4 (&O)[4][NVT]) {
     const int w = threadIdx.x >> 6;
     if (NW == 8) {
       switch (__builtin_amdgcn_readfirstlane(w)) {
-        case 0: tile_qk<SC>(smem, 0, 0); invert_diag<0>(smem); scan_y<SC>(smem, S, Y, O); break;
-        case 1: tile_qk<SC>(smem, 1, 1); invert_diag<1>(smem); scan_y<SC>(smem, S, Y, O); break;
-        case 2: tile_qk<SC>(smem, 2, 2); invert_diag<2>(smem); scan_y<SC>(smem, S, Y, O); break;
-        case 3: tile_qk<SC>(smem, 3, 3); invert_diag<3>(smem); scan_y<SC>(smem, S, Y, O); break;
-        case 4: tile_qk<SC>(smem, 1, 0); tile_qk<SC>(smem, 3, 2); scan_y<SC>(smem, S, Y, O); break;
-        case 5: tile_qk<SC>(smem, 2, 0); tile_qk<SC>(smem, 2, 1); scan_y<SC>(smem, S, Y, O); break;
-        case 6: tile_qk<SC>(smem, 3, 0); scan_y<SC>(smem, S, Y, O); break;
-        default: tile_qk<SC>(smem, 3, 1); scan_y<SC>(smem, S, Y, O); break;
+        case 0: tile_qk<MODE>(smem, 0, 0); invert_diag<0>(smem); scan_y<MODE>(smem, S, Y, O); break;
+        case 1: tile_qk<MODE>(smem, 1, 1); invert_diag<1>(smem); scan_y<MODE>(smem, S, Y, O); break;
+        case 2: tile_qk<MODE>(smem, 2, 2); invert_diag<2>(smem); scan_y<MODE>(smem, S, Y, O); break;
+        case 3: tile_qk<MODE>(smem, 3, 3); invert_diag<3>(smem); scan_y<MODE>(smem, S, Y, O); break;
+        case 4: tile_qk<MODE>(smem, 1, 0); tile_qk<MODE>(smem, 3, 2); scan_y<MODE>(smem, S, Y, O); break;
+        case 5: tile_qk<MODE>(smem, 2, 0); tile_qk<MODE>(smem, 2, 1); scan_y<MODE>(smem, S, Y, O); break;
+        case 6: tile_qk<MODE>(smem, 3, 0); scan_y<MODE>(smem, S, Y, O); break;
+        default: tile_qk<MODE>(smem, 3, 1); scan_y<MODE>(smem, S, Y, O); break;
       }
     } else {
       switch (__builtin_amdgcn_readfirstlane(w)) {
-        case 0: tile_qk<SC>(smem, 0, 0); invert_diag<0>(smem); tile_qk<SC>(smem, 1, 0);
-                tile_qk<SC>(smem, 2, 0); scan_y<SC>(smem, S, Y, O); break;
-        case 1: tile_qk<SC>(smem, 1, 1); invert_diag<1>(smem); tile_qk<SC>(smem, 2, 1);
-                tile_qk<SC>(smem, 3, 0); scan_y<SC>(smem, S, Y, O); break;
-        case 2: tile_qk<SC>(smem, 2, 2); invert_diag<2>(smem); tile_qk<SC>(smem, 3, 1);
-                scan_y<SC>(smem, S, Y, O); break;
-        default: tile_qk<SC>(smem, 3, 3); invert_diag<3>(smem); tile_qk<SC>(smem, 3, 2);
-                 scan_y<SC>(smem, S, Y, O); break;
+        case 0: tile_qk<MODE>(smem, 0, 0); invert_diag<0>(smem); tile_qk<MODE>(smem, 1, 0);
+                tile_qk<MODE>(smem, 2, 0); scan_y<MODE>(smem, S, Y, O); break;
+        case 1: tile_qk<MODE>(smem, 1, 1); invert_diag<1>(smem); tile_qk<MODE>(smem, 2, 1);
+                tile_qk<MODE>(smem, 3, 0); scan_y<MODE>(smem, S, Y, O); break;
+        case 2: tile_qk<MODE>(smem, 2, 2); invert_diag<2>(smem); tile_qk<MODE>(smem, 3, 1);
+                scan_y<MODE>(smem, S, Y, O); break;
+        default: tile_qk<MODE>(smem, 3, 3); invert_diag<3>(smem); tile_qk<MODE>(smem, 3, 2);
+                 scan_y<MODE>(smem, S, Y, O); break;
       }
     }
   }
@@ -1568,10 +1629,13 @@ struct ChunkKernel {
         f32x4 Y[4][NVT], O[4][NVT];
         // one instance per reference mode: the common chunk-start case
         // carries no block factors at all
-        if (any & 2)
-          middle<true>(smem, S, Y, O);
+        // the waves' modes are OR-ed: the strongest one present wins
+        if (any & (KDA_MODE_SCALE << 1))
+          middle<KDA_MODE_SCALE>(smem, S, Y, O);
+        else if (any & (KDA_MODE_MASK << 1))
+          middle<KDA_MODE_MASK>(smem, S, Y, O);
         else
-          middle<false>(smem, S, Y, O);
+          middle<KDA_MODE_CHUNK>(smem, S, Y, O);
         compiler_fence();
         load_raw<LOAD_Q | LOAD_K>(raw, offs, q, k, v, g, beta, next, H, h, nlen);
         __syncthreads();                                         // B2
@@ -1741,17 +1805,17 @@ struct ParKernel {
 
   // The state-independent tiles and inverses (the fused kernel's middle
   // interval without its state products).
-  template <bool SC>
+  template <int MODE>
   static __device__ __forceinline__ void tiles(LDS char* smem) {
     switch (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) {
-      case 0: K::template tile_qk<SC>(smem, 0, 0); K::template invert_diag<0>(smem); break;
-      case 1: K::template tile_qk<SC>(smem, 1, 1); K::template invert_diag<1>(smem); break;
-      case 2: K::template tile_qk<SC>(smem, 2, 2); K::template invert_diag<2>(smem); break;
-      case 3: K::template tile_qk<SC>(smem, 3, 3); K::template invert_diag<3>(smem); break;
-      case 4: K::template tile_qk<SC>(smem, 1, 0); K::template tile_qk<SC>(smem, 3, 2); break;
-      case 5: K::template tile_qk<SC>(smem, 2, 0); K::template tile_qk<SC>(smem, 2, 1); break;
-      case 6: K::template tile_qk<SC>(smem, 3, 0); break;
-      default: K::template tile_qk<SC>(smem, 3, 1); break;
+      case 0: K::template tile_qk<MODE>(smem, 0, 0); K::template invert_diag<0>(smem); break;
+      case 1: K::template tile_qk<MODE>(smem, 1, 1); K::template invert_diag<1>(smem); break;
+      case 2: K::template tile_qk<MODE>(smem, 2, 2); K::template invert_diag<2>(smem); break;
+      case 3: K::template tile_qk<MODE>(smem, 3, 3); K::template invert_diag<3>(smem); break;
+      case 4: K::template tile_qk<MODE>(smem, 1, 0); K::template tile_qk<MODE>(smem, 3, 2); break;
+      case 5: K::template tile_qk<MODE>(smem, 2, 0); K::template tile_qk<MODE>(smem, 2, 1); break;
+      case 6: K::template tile_qk<MODE>(smem, 3, 0); break;
+      default: K::template tile_qk<MODE>(smem, 3, 1); break;
     }
   }
 
@@ -1918,10 +1982,13 @@ __global__ __launch_bounds__(Cfg::NTHREADS, 1) void chunk_intra_kernel(
     K::template load_raw<K::LOAD_V>(raw, offs, q, k, v, g, beta, nrow0, H, nh, nlen);
     compiler_fence();
     if (!any_bad) {
-      if (any & 2)
-        P::template tiles<true>(smem);
+      // the waves' modes are OR-ed: the strongest one present wins
+      if (any & (KDA_MODE_SCALE << 1))
+        P::template tiles<KDA_MODE_SCALE>(smem);
+      else if (any & (KDA_MODE_MASK << 1))
+        P::template tiles<KDA_MODE_MASK>(smem);
       else
-        P::template tiles<false>(smem);
+        P::template tiles<KDA_MODE_CHUNK>(smem);
     }
     compiler_fence();
     __syncthreads();

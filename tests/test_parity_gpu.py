@@ -75,15 +75,20 @@ def test_single_head_f32_seed0():
                                                            (64, 64, "f32", None, -5.0),
                                                            (128, 128, "bf16", 8, -8.0),
                                                            (128, 64, "bf16", 1, -20.0),
-                                                           (64, 64, "f32", None, -8.0)])
+                                                           (64, 64, "f32", None, -8.0),
+                                                           (128, 128, "bf16", 8, -1.2),
+                                                           (64, 128, "bf16", None, -1.2),
+                                                           (64, 64, "f32", 4, -1.2)])
 def test_strong_decay_matches_oracle(dk, dv, io, strong_channels, gval):
     """Fast-decaying key channels.  At log alpha = -3 (e^-192 over a chunk) and
     -5 per token (e^-80 over a 16-token block, 2^-115.4, the gate transform's
     floor) the block-start references keep every operand in range and the
-    chunk takes the MFMA path; at -8 and -20 a 16-token block decays below
-    2^-120 and the chunk runs the recurrence token by token (also when a
-    single channel of one wave does so: the flag must see every lane's
-    channels).  Results must match the oracle."""
+    chunk takes the MFMA path, with the cross-block factors (below 2^-40)
+    masked; at -1.2 (2^-27.7 per block) the channels are block-referenced
+    with cross-block factors that must be applied; at -8 and -20 a 16-token
+    block decays below 2^-120 and the chunk runs the recurrence token by
+    token (also when a single channel of one wave does so: the flag must see
+    every lane's channels).  Results must match the oracle."""
     note("strong decay dk=%d dv=%d io=%s channels=%s g=%.1f" % (dk, dv, io, strong_channels, gval))
     d = inputs.prefill_inputs(2, 150, 2, dk, dv, io=io, seed=dk + dv, with_S0=True, device=DEV)
     if strong_channels is None:
@@ -99,6 +104,26 @@ def test_strong_decay_matches_oracle(dk, dv, io, strong_channels, gval):
     ro, rs = oracle_batched(d, chains)
     go, gs = gpu_chains_batched(o, S, chains)
     assert_close(go, gs, ro, rs, tol_for(io), "strong decay")
+
+
+def test_mixed_reference_modes_match_oracle():
+    """One chunk stream holding every reference mode: 8 channels at log alpha
+    ~ U[-5, -2] (masked cross-block factors), 8 at -1.2 (applied factors) in
+    tokens 100 .. 260, and chunks with neither; ragged last chunk."""
+    note("mixed reference modes")
+    d = inputs.prefill_inputs(2, 333, 3, 128, 128, io="bf16", seed=77, with_S0=True, device=DEV)
+    inputs.strong_gate_channels(d, 8, seed=3)
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(11)
+    idx = torch.randperm(128, generator=gen, device=DEV)[:8]
+    sl = d["g"][:, 100:260]
+    sl[..., idx] = -1.2
+    o, S = kda().chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], S0=d["S0"])
+    torch.cuda.synchronize()
+    chains = [(b, h) for b in range(2) for h in range(3)]
+    ro, rs = oracle_batched(d, chains)
+    go, gs = gpu_chains_batched(o, S, chains)
+    assert_close(go, gs, ro, rs, tol_for("bf16"), "mixed modes")
 
 
 @pytest.mark.parametrize("dk,dv,io", [(128, 128, "bf16"), (128, 64, "bf16"), (64, 128, "bf16"),
@@ -136,14 +161,16 @@ def test_prefill_h16_t4096_with_S0():
 @pytest.mark.parametrize("B,T,H,with_S0,strong", [(2, 1000, 3, True, None),
                                                   (1, 512, 2, False, None),
                                                   (1, 700, 2, True, -3.0),
+                                                  (1, 700, 2, True, -1.2),
                                                   (1, 700, 2, True, -20.0)])
 def test_chunk_parallel_schedule_matches_oracle(B, T, H, with_S0, strong):
     """Few long chains take the chunk-parallel schedule (per-chunk WY factors,
     one state scan, outputs of all chunks in parallel).  Every chain is checked,
     with a ragged last chunk.  With ``strong`` = -3, 8 channels decay by e^-192
-    over the chunks of tokens 128 .. 300 (block-start references in stage A);
-    with -20 their blocks decay below 2^-120, stage A flags those chunks and
-    the scan stage recomputes them token by token."""
+    over the chunks of tokens 128 .. 300 (block-start references in stage A,
+    cross-block factors masked); with -1.2 the cross-block factors are
+    applied; with -20 their blocks decay below 2^-120, stage A flags those
+    chunks and the scan stage recomputes them token by token."""
     K = kda()
     assert K.chunk_fwd_workspace_size(B, T, H, 128, 128) > 0   # the schedule is taken
     note("chunk-parallel B=%d T=%d H=%d S0=%s strong=%s" % (B, T, H, with_S0, strong))
