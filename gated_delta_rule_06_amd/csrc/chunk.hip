@@ -720,6 +720,40 @@ struct ChunkKernel {
     }
   }
 
+  // Lane-dependent LDS byte offsets of prep's accesses, formed once per chain
+  // (they do not change from chunk to chunk), so that each access is a base
+  // register plus an immediate offset.
+  struct PrepAddr {
+    int rowk;   // row TPL tg, key channel kc0 of a [C][LD_K] operand buffer
+    int rowv;   // row TPL tg, value channel vc0 of the [C][LD_V] buffer
+    int kit;    // key row kc0, token TPL tg of the key-major [DK][LD_KT] buffer
+    int fac;    // block tg / GPB, key channel kc0 of a [4][DK] float factor array
+  };
+  static __device__ __forceinline__ PrepAddr prep_addr() {
+    const int w = threadIdx.x >> 6, l = lane_fresh();
+    const int tg = l / CQ, cq = l % CQ;
+    const int kc0 = w * (DK / NW) + CPL * cq;
+    const int vc0 = w * VW + VPL * cq;
+    PrepAddr a;
+    a.rowk = ((TPL * tg) * Cfg::LD_K + Op::perm_pos(kc0)) * Cfg::SZ;
+    a.rowv = ((TPL * tg) * Cfg::LD_V + vc0) * Cfg::SZ;
+    a.kit = (kc0 * Cfg::LD_KT + Op::perm_pos(TPL * tg)) * Cfg::SZ;
+    a.fac = ((TPL * tg / 16) * DK + frag_pos(kc0)) * 4;
+    return a;
+  }
+  // Channels c0 .. c0 + 7 of one operand row at p (the lane's position of c0):
+  // in the permuted bf16 order c0 + 4 .. c0 + 7 sit 8 elements on, in the fp32
+  // order 4.
+  static __device__ __forceinline__ void st8_at(LDS T* p, const float (&x)[8]) {
+    if constexpr (Op::PERMUTED) {
+      *lds_ptr<u32x2>(p) = u32x2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+      *lds_ptr<u32x2>(p + 8) = u32x2{pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7])};
+    } else {
+      *lds_ptr<f32x4>(p) = f32x4{x[0], x[1], x[2], x[3]};
+      *lds_ptr<f32x4>(p + 4) = f32x4{x[4], x[5], x[6], x[7]};
+    }
+  }
+
   // KDA: the decay factors and the gate-scaled operands of one chunk (tokens
   // [0, hi) real, the rest identity tokens), "Kimi Unveils Delta Attention
   // and K3 Architecture Updates", section 6.1 (cumulative decay) and 6.6.
@@ -738,7 +772,8 @@ struct ChunkKernel {
   // what the block-start reference can scale; bits 1-2: the wave's reference
   // mode (KDA_MODE_*).
   static __device__ __forceinline__ int prep(const Raw& r, LDS char* smem, float scale,
-                                             const Prologue& pro, float ea, int hi) {
+                                             const Prologue& pro, float ea, int hi,
+                                             const PrepAddr& pa) {
     if constexpr (Cfg::SG) {
       prep_sg(r, smem, scale, pro, ea, hi);
       return 0;
@@ -802,15 +837,16 @@ struct ChunkKernel {
       ex[c] = dpp_row_shr0<CQ>(tb[c]);
     }
     if (tg % GPB == GPB - 1) {
-      *lds_ptr<f32x4>(DT + blk * DK + frag_pos(kc0)) = f32x4{tb[0], tb[1], tb[2], tb[3]};
-      *lds_ptr<f32x4>(DT + blk * DK + frag_pos(kc0 + 4)) = f32x4{tb[4], tb[5], tb[6], tb[7]};
+      LDS float* dt = (LDS float*)(smem + Cfg::OFF_DT + pa.fac);
+      *lds_ptr<f32x4>(dt) = f32x4{tb[0], tb[1], tb[2], tb[3]};
+      *lds_ptr<f32x4>(dt + 8) = f32x4{tb[4], tb[5], tb[6], tb[7]};
     }
     // -v and the unpacked q (work without decay factors, while the block
     // totals reach LDS)
     float qv[TPL][CPL];
 #pragma unroll
     for (int t = 0; t < TPL; ++t) {
-      st_neg(BV + (TPL * tg + t) * Cfg::LD_V + vc0, r.v[t]);   // -v: the sign bits flipped
+      st_neg((LDS T*)(smem + Cfg::OFF_BV + pa.rowv) + t * Cfg::LD_V, r.v[t]);   // -v: sign bits flipped
       r.q[t].unpack(qv[t]);
     }
     __asm__ __volatile__("" ::: "memory");
@@ -886,10 +922,10 @@ struct ChunkKernel {
     }
     __asm__ __volatile__("" ::: "memory");
     // the lane's factors (issued now, used after the k work below)
-    const f32x4 fa0 = *lds_ptr<const f32x4>(FA + blk * DK + frag_pos(kc0));
-    const f32x4 fa1 = *lds_ptr<const f32x4>(FA + blk * DK + frag_pos(kc0 + 4));
-    const f32x4 fm0 = *lds_ptr<const f32x4>(FM + blk * DK + frag_pos(kc0));
-    const f32x4 fm1 = *lds_ptr<const f32x4>(FM + blk * DK + frag_pos(kc0 + 4));
+    const LDS float* fap = (const LDS float*)(smem + Cfg::OFF_FA + pa.fac);
+    const LDS float* fmp = (const LDS float*)(smem + Cfg::OFF_FM + pa.fac);
+    const f32x4 fa0 = *lds_ptr<const f32x4>(fap), fa1 = *lds_ptr<const f32x4>(fap + 8);
+    const f32x4 fm0 = *lds_ptr<const f32x4>(fmp), fm1 = *lds_ptr<const f32x4>(fmp + 8);
     __asm__ __volatile__("" ::: "memory");
     // k unpacked, and the L2 norms (FU)
     float kv[TPL][CPL];
@@ -939,15 +975,15 @@ struct ChunkKernel {
         kef[c][t] = ki[c] * fm[c];              // -K_end
         kit[c][t] = Op::cvt(kef[c][t]);
       }
-      st_row8(QG + i * Cfg::LD_K, kc0, qg);
-      st_row8(KG + i * Cfg::LD_K, kc0, kg);
-      st_row8(KI + i * Cfg::LD_K, kc0, ki);
+      st8_at((LDS T*)(smem + Cfg::OFF_QG + pa.rowk) + t * Cfg::LD_K, qg);
+      st8_at((LDS T*)(smem + Cfg::OFF_KG + pa.rowk) + t * Cfg::LD_K, kg);
+      st8_at((LDS T*)(smem + Cfg::OFF_KI + pa.rowk) + t * Cfg::LD_K, ki);
     }
     // key-major copy KIT[channel][token]: the lane's TPL tokens are
     // consecutive (and stay so under the token permutation)
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
-      LDS T* p = KIT + (kc0 + c) * Cfg::LD_KT + Op::perm_pos(TPL * tg);
+      LDS T* p = (LDS T*)(smem + Cfg::OFF_KT + pa.kit) + c * Cfg::LD_KT;
       if (KIT_PAIRS)
         *lds_ptr<uint32_t>(p) = pack_bf16x2(kef[c][0], kef[c][TPL - 1]);
       else
@@ -1591,6 +1627,7 @@ struct ChunkKernel {
     // beta after the inverse) so that the memory system sees a steady stream
     // instead of one burst per chunk that would stall the issuing waves.
     const Offsets offs = lane_offsets(H);
+    const PrepAddr pa = prep_addr();
     Raw raw;
     if (len > 0) load_raw<LOAD_ALL>(raw, offs, q, k, v, g, beta, row_base, H, h, len < C ? len : C);
     const bool l2n = Cfg::FU && (pro.flags & PRO_L2NORM);
@@ -1611,7 +1648,7 @@ struct ChunkKernel {
         __syncthreads();
       }
       norms_ready = false;
-      const int fl = prep(raw, smem, scale, pro, ea, clen);   // wave-uniform flags
+      const int fl = prep(raw, smem, scale, pro, ea, clen, pa);   // wave-uniform flags
       if constexpr (!Cfg::SG) {   // the single-gate form has no guard
         if (lane_fresh() == 0) FL[w] = fl;
       }
@@ -1954,6 +1991,7 @@ __global__ __launch_bounds__(Cfg::NTHREADS, 1) void chunk_intra_kernel(
     clen = min(Cfg::C, T - c * Cfg::C);
   };
   const typename K::Offsets offs = K::lane_offsets(H);
+  const typename K::PrepAddr pa = K::prep_addr();
   const Prologue pro{0u, nullptr, nullptr};
   LDS int* FL = (LDS int*)(smem + Cfg::OFF_FL);
   const int w = threadIdx.x >> 6;
@@ -1968,7 +2006,7 @@ __global__ __launch_bounds__(Cfg::NTHREADS, 1) void chunk_intra_kernel(
     size_t nrow0 = row0;
     int nh = h, nlen = 0;
     if (nidx < total) where(nidx, nrow0, nh, nlen);
-    const int fl = K::prep(raw, smem, scale, pro, 1.f, clen);   // wave-uniform flags
+    const int fl = K::prep(raw, smem, scale, pro, 1.f, clen, pa);   // wave-uniform flags
     if (lane_fresh() == 0) FL[w] = fl;
     compiler_fence();
     K::template load_raw<K::LOAD_G>(raw, offs, q, k, v, g, beta, nrow0, H, nh, nlen);
