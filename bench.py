@@ -331,24 +331,26 @@ def main():
         kda.chunk_fwd(d["q"], d["k"], d["v"], strong["g"], d["beta"], S0=None, out=out,
                       S_final=Sf)
 
-    # A longer warm-up than the headline's: a few launches into this leg the
-    # engine clock dips (launch times rise by up to 40% and recover over some
-    # 20 launches; the first launches run at 1.04x the plain kernel), so the
-    # timed launches start after 30 untimed ones.
-    for _ in range(max(args.warmup, 30)):
-        strong_step()
-    torch.cuda.synchronize()
+    # A longer warm-up than the headline's, in one burst with the timed
+    # launches: a few launches after an idle gap the engine clock dips under
+    # this heavier load (launch times rise by up to 40% and recover over some
+    # 20 launches, while the cycles per launch stay 1.06x the plain kernel's),
+    # so the leg runs 30 untimed launches and then the timed ones with no
+    # synchronisation in between, and averages the timed ones only.
+    n_warm_s = max(args.warmup, 30)
     evs_s = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-             for _ in range(args.steps)]
+             for _ in range(n_warm_s + args.steps)]
     for a, b in evs_s:
         a.record(stream)
         strong_step()
         b.record(stream)
     torch.cuda.synchronize()
-    sg_launch = [a.elapsed_time(b) for a, b in evs_s]
+    sg_all = [a.elapsed_time(b) for a, b in evs_s]
+    sg_launch = sg_all[n_warm_s:]
     sg_ms = float(np.mean(sg_launch))
     log("prefill, 8 of 128 channels at log alpha ~ U[-5,-2]: kernel %.3f ms avg (%.3f x the "
         "plain inputs)" % (sg_ms, sg_ms / avg_kernel_ms))
+    log("fast-forgetting launch ms, warm-up:", " ".join("%.3f" % x for x in sg_all[:n_warm_s]))
     log("fast-forgetting launch ms, timed:", " ".join("%.3f" % x for x in sg_launch))
     del strong
     del d, dg
@@ -415,14 +417,27 @@ def main():
     log("generating the 16-sequence packed prefill (%d tokens)" % int(lens5.sum()))
     d5 = inputs.varlen_inputs(lens5, c5["H"], c5["dk"], c5["dv"], io=c5["io"], seed=0,
                               long_channels=c5["long_channels"], device=dev)
-    c5_ms = timed_calls(lambda: kda.chunk_fwd_varlen(d5["q"], d5["k"], d5["v"], d5["g"], d5["beta"],
-                                                     d5["cu_seqlens"]), 5, warm=2)
     c5_tokens = int(lens5.sum())
+    ws5 = torch.empty(kda.lib.kda_chunk_fwd_varlen_workspace_size(
+        c5["n_seq"], c5_tokens, c5["H"], c5["dk"], c5["dv"], 64, 1), dtype=torch.uint8, device=dev)
+    c5_ms = timed_calls(lambda: kda.chunk_fwd_varlen(d5["q"], d5["k"], d5["v"], d5["g"], d5["beta"],
+                                                     d5["cu_seqlens"], workspace=ws5), 5, warm=2)
+    # the balanced schedule's plan, as the kernels left it in the workspace:
+    # workgroups launched, slice length and total in chunks
+    w5 = ws5[:24].cpu().numpy()
+    c5_wg = int(w5[:4].view(np.uint32)[0])
+    c5_slice, c5_total = (int(x) for x in w5[8:24].view(np.int64))
+    # the same call with one workgroup per (sequence, head) chain, for comparison
+    c5_chain_ms = timed_calls(lambda: kda.chunk_fwd_varlen(
+        d5["q"], d5["k"], d5["v"], d5["g"], d5["beta"], d5["cu_seqlens"], balanced=False), 5,
+        warm=2)
     c5_b = c5_tokens * c5["H"] * 1540 + c5["n_seq"] * c5["H"] * c5["dk"] * c5["dv"] * 4
     c5_longest = int(-(-int(lens5.max()) // 64))
-    log("varlen 16 sequences: %.2f ms per launch, %.0f GB/s; longest chain %d chunks"
-        % (c5_ms, c5_b / (c5_ms * 1e-3) / 1e9, c5_longest))
-    del d5
+    log("varlen 16 sequences: %.2f ms per launch, %.0f GB/s (%d workgroups, slices of %d of %d "
+        "chunks; longest chain %d); one workgroup per chain: %.2f ms"
+        % (c5_ms, c5_b / (c5_ms * 1e-3) / 1e9, c5_wg, c5_slice, c5_total, c5_longest,
+           c5_chain_ms))
+    del d5, ws5
     torch.cuda.empty_cache()
 
     # ---------------------------------------------------------------- backward
@@ -555,7 +570,11 @@ def main():
             "avg_launch_ms": c5_ms, "tokens_per_s": c5_tokens / (c5_ms * 1e-3),
             "achieved_gbs": c5_b / (c5_ms * 1e-3) / 1e9, "alg_bytes_per_launch": c5_b,
             "frac_hbm": c5_b / (c5_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "longest_chain_chunks": c5_longest},
+            "longest_chain_chunks": c5_longest,
+            "schedule": "balanced: %d workgroups, %d chunks laid end to end per head and cut "
+                        "into slices of %d" % (c5_wg, c5_total, c5_slice),
+            "us_per_slice_chunk": c5_ms * 1e3 / c5_slice,
+            "one_workgroup_per_chain_ms": c5_chain_ms},
         "recurrent": {"workload": "multi_token_decode_n256_h32_len1to8",
                       "tokens_per_call": rec_tokens, "calls": R["calls"],
                       "us_per_call": rec_wall * 1e6, "tokens_per_s": rec_tokens / rec_wall,

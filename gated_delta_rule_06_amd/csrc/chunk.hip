@@ -1751,12 +1751,235 @@ __global__ __launch_bounds__(Cfg::NTHREADS, 1) void chunk_fwd_varlen_kernel(
                         (size_t)chain, scale, pro);
 }
 
+// ============================================================ balanced packed schedule
+// With one workgroup per (sequence, head) chain, a CU that receives two chains
+// runs their sum: with skewed lengths the busiest CU can exceed the average by
+// most of a chain whatever the order (16 sequences of U{1024..65536} tokens at
+// 32 heads: 1,183 chunk steps on the busiest CU against 1,058 on average).
+// Packed calls with more chains than the GPU holds at once (up to four times
+// as many) therefore take McNaughton's wrap-around rule for preemptive
+// scheduling on identical machines (R. McNaughton, "Scheduling with deadlines
+// and loss functions", Management Science 6(1), 1959) when the caller gives a
+// workspace:
+//
+// - the resident workgroups form M machines of H workgroups, one per head, so
+//   that the heads of a sequence still read the same token rows side by side;
+// - the sequences, counted in chunks (an empty one counts one), are laid end
+//   to end and cut into M slices of T = max(ceil(total / M), longest) chunks;
+// - a sequence that crosses the boundary between slices m and m + 1 is split:
+//   machine m + 1 runs its first chunks as its first piece and hands the fp32
+//   state over through the workspace; machine m runs the rest as its last
+//   piece.  No sequence is longer than T, so the first piece ends no later
+//   than the last one starts: the makespan is T chunk steps, the bound for
+//   any division of the work.
+//
+// Chunks stay aligned to their sequence and the state crosses in fp32, so the
+// results are bit-identical to the one-workgroup-per-chain kernel.  Each
+// workgroup takes its place from a ticket counter, in the order workgroups
+// actually start; a machine's workgroups wait only on tickets taken earlier,
+// whose first piece waits on nothing, so every wait ends whatever order the
+// hardware starts workgroups in.  A wait is bounded all the same: past
+// KDA_SPLIT_SPIN polls the workgroup recomputes the first piece itself.
+struct SplitWs {
+  static constexpr size_t OFF_TICKET = 0;                             // u32
+  static constexpr size_t OFF_T = 8;                                  // i64 slice length
+  static constexpr size_t OFF_TOTAL = 16;                             // i64 total chunks
+  static constexpr size_t OFF_FLAGS = 256;                            // u32 per slot
+  static constexpr size_t OFF_PRE = OFF_FLAGS + KDA_SPLIT_MAX_WG * 4;  // i64 [N + 1]
+  __host__ __device__ static size_t off_state(int N) { return (OFF_PRE + (size_t)(N + 1) * 8 + 255) / 256 * 256; }
+  // handed-over states: slot m * H + h for the first piece on machine m >= 1;
+  // a full slice holds the start of a sequence of index >= m, so m < N
+  __host__ __device__ static int slots(int N, int H) {
+    const long s = (long)N * H;
+    return s < KDA_SPLIT_MAX_WG ? (int)s : KDA_SPLIT_MAX_WG;
+  }
+  __host__ __device__ static size_t bytes(int N, int H, int dk, int dv) {
+    return off_state(N) + (size_t)slots(N, H) * dk * dv * 4;
+  }
+};
+
+// Chunk counts per sequence -> prefix sums (i64), slice length and total; the
+// ticket and every hand-over flag start at zero on each call.
+__global__ __launch_bounds__(1024) void split_plan_kernel(const int32_t* __restrict__ cu, int N,
+                                                          int C, int M, int nslots, char* ws) {
+  __shared__ long long wsum[16];
+  __shared__ long long carry;
+  __shared__ int umax;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  unsigned* flags = reinterpret_cast<unsigned*>(ws + SplitWs::OFF_FLAGS);
+  long long* pre = reinterpret_cast<long long*>(ws + SplitWs::OFF_PRE);
+  for (int i = tid; i < nslots; i += 1024) flags[i] = 0u;
+  if (tid == 0) {
+    *reinterpret_cast<unsigned*>(ws + SplitWs::OFF_TICKET) = 0u;
+    pre[0] = 0;
+    carry = 0;
+    umax = 1;
+  }
+  __syncthreads();
+  for (int base = 0; base < N; base += 1024) {
+    const int n = base + tid;
+    long long u = 0;
+    if (n < N) {
+      const int len = cu[n + 1] - cu[n];
+      u = len > 0 ? (len + C - 1) / C : 1;
+      atomicMax(&umax, (int)u);
+    }
+    long long x = u;   // inclusive scan over the wave
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const long long y = __shfl_up(x, d, 64);
+      if (lane >= d) x += y;
+    }
+    if (lane == 63) wsum[wv] = x;
+    __syncthreads();
+    long long off = carry;
+    for (int i = 0; i < wv; ++i) off += wsum[i];
+    if (n < N) pre[n + 1] = off + x;
+    __syncthreads();
+    if (tid == 0) {
+      long long s = 0;
+      for (int i = 0; i < 16; ++i) s += wsum[i];
+      carry += s;
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    const long long total = carry;
+    long long T = (total + M - 1) / M;
+    if (T < umax) T = umax;
+    *reinterpret_cast<long long*>(ws + SplitWs::OFF_T) = T;
+    *reinterpret_cast<long long*>(ws + SplitWs::OFF_TOTAL) = total;
+  }
+}
+
+template <class Cfg>
+__global__ __launch_bounds__(Cfg::NTHREADS, 1) void chunk_fwd_split_kernel(
+    const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
+    const float* __restrict__ g, const float* __restrict__ beta, const float* S0, void* out,
+    float* S_final, const int32_t* __restrict__ cu, int N, int H, int M, int nslots, float scale,
+    Prologue pro, char* ws) {
+  extern __shared__ __attribute__((aligned(16))) char smem_[];
+  LDS volatile int* sh = (LDS volatile int*)smem_;
+  constexpr size_t SS = (size_t)Cfg::DK * Cfg::DV;
+  constexpr int C = Cfg::C;
+  if (threadIdx.x == 0)
+    sh[0] = (int)atomicAdd(reinterpret_cast<unsigned*>(ws + SplitWs::OFF_TICKET), 1u);
+  __syncthreads();
+  const int id = sh[0];
+  if (id >= M * H) return;
+  // machine m = M - 1 - id / H: the first piece of machine m + 1, which
+  // machine m's last piece waits for, belongs to a ticket H lower
+  const int m = M - 1 - id / H, h = id % H;
+  const long long T = *reinterpret_cast<const long long*>(ws + SplitWs::OFF_T);
+  const long long total = *reinterpret_cast<const long long*>(ws + SplitWs::OFF_TOTAL);
+  const long long* pre = reinterpret_cast<const long long*>(ws + SplitWs::OFF_PRE);
+  unsigned* flags = reinterpret_cast<unsigned*>(ws + SplitWs::OFF_FLAGS);
+  float* hand = reinterpret_cast<float*>(ws + SplitWs::off_state(N));
+  long long x = (long long)m * T;
+  const long long end = x + T < total ? x + T : total;
+  while (x < end) {
+    // the sequence holding chunk x of the concatenation: first n with pre[n + 1] > x
+    int lo = 0, hi = N - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (pre[mid + 1] > x) hi = mid;
+      else lo = mid + 1;
+    }
+    const int n = lo;
+    const long long s = pre[n], u = pre[n + 1] - s;
+    const int b0 = cu[n], len = cu[n + 1] - b0;
+    const size_t chain = (size_t)n * H + h;
+    const float* sin = S0 ? S0 + chain * SS : nullptr;
+    float* sout = S_final ? S_final + chain * SS : nullptr;
+    long long c0 = 0, c1 = u;
+    int post = -1, wait = -1;
+    if (x > s) {   // begun in slice m - 1: the first chunks here, state handed on
+      c1 = s + u - x;
+      post = m * H + h;
+      x = s + u;
+    } else if (s + u > end) {   // runs past the slice: the rest is machine m + 1's first piece
+      c0 = u - (end - s);
+      wait = (m + 1) * H + h;
+      x = end;
+    } else {
+      x = s + u;
+    }
+    if (post >= nslots || wait >= nslots) {   // outside the slots (excluded above): no split
+      c0 = 0;
+      c1 = u;
+      post = wait = -1;
+    }
+    if (post >= 0) sout = hand + (size_t)post * SS;
+    __syncthreads();   // the previous piece is done with the LDS
+    if (wait >= 0) {
+      if (threadIdx.x == 0) {
+        int got = 0;
+        for (int it = 0; it < KDA_SPLIT_SPIN && !got; ++it) {
+          got = __hip_atomic_load(flags + wait, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) != 0u;
+          if (!got) __builtin_amdgcn_s_sleep(8);
+        }
+        sh[1] = got;
+      }
+      // thread 0's device-scope acquire, then the barrier, orders every
+      // wave's reads of the handed-over state after the flag
+      __syncthreads();
+      const bool got = sh[1] != 0;
+      if (got) sin = hand + (size_t)wait * SS;
+      else c0 = 0;   // no hand-over in time: redo the first chunks here
+      __syncthreads();
+    }
+    const long long r0 = (long long)C * c0;
+    const long long r1 = (long long)C * c1 < len ? (long long)C * c1 : len;
+    ChunkKernel<Cfg>::run(q, k, v, g, beta, sin, out, sout, (size_t)b0 + (size_t)r0,
+                          (int)(r1 - r0), H, h, 0, scale, pro);
+    if (post >= 0) {
+      // the barrier orders every wave's state stores before thread 0's
+      // device-scope release (one write-back of this XCD's L2)
+      __syncthreads();
+      if (threadIdx.x == 0)
+        __hip_atomic_store(flags + post, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+size_t chunk_split_workspace_bytes(int n_seq, int H, int dk, int dv) {
+  return SplitWs::bytes(n_seq, H, dk, dv);
+}
+
 template <class Cfg>
 static hipError_t launch_chunk_t(const void* q, const void* k, const void* v, const float* g,
                                  const float* beta, const float* S0, void* out, float* S_final,
                                  const int32_t* cu, int n_seq, int T, int H, float scale,
-                                 const Prologue& pro, hipStream_t stream) {
+                                 const Prologue& pro, void* ws, hipStream_t stream) {
   const int bytes = Cfg::LDS_TOTAL;
+  if (cu && ws) {
+    // the balanced schedule when there are more chains than resident workgroups
+    auto kern = chunk_fwd_split_kernel<Cfg>;
+    hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e != hipSuccess) return e;
+    int dev = 0, cus = 0, occ = 0;
+    e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess)
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, (const void*)kern, Cfg::NTHREADS, bytes);
+    if (e != hipSuccess) return e;
+    long P = (long)cus * (occ > 0 ? occ : 1);
+    if (P > KDA_SPLIT_MAX_WG) P = KDA_SPLIT_MAX_WG;
+    const int M = (int)(P / H);
+    // up to 4 chains per workgroup: beyond that the hardware's dispatch of
+    // whole chains, longest first, already evens the load and also absorbs
+    // the CU-to-CU spread in speed, which a fixed split cannot
+    const long chains = (long)n_seq * H;
+    if (M >= 2 && chains > P && chains <= 4 * P) {
+      const int nslots = SplitWs::slots(n_seq, H);
+      hipLaunchKernelGGL(split_plan_kernel, dim3(1), dim3(1024), 0, stream, cu, n_seq, Cfg::C, M,
+                         nslots, (char*)ws);
+      hipLaunchKernelGGL(kern, dim3(M * H), dim3(Cfg::NTHREADS), bytes, stream, q, k, v, g, beta,
+                         S0, out, S_final, cu, n_seq, H, M, nslots, scale, pro, (char*)ws);
+      return hipGetLastError();
+    }
+  }
   if (cu) {
     auto kern = chunk_fwd_varlen_kernel<Cfg>;
     hipError_t e = hipFuncSetAttribute((const void*)kern,
@@ -2269,12 +2492,12 @@ bool chunk_supported(int dk, int dv, bool bf16) {
 hipError_t launch_chunk(const void* q, const void* k, const void* v, const float* g,
                         const float* beta, const float* S0, void* out, float* S_final,
                         const int32_t* cu_seqlens, int n_seq, int T, int H, int dk, int dv,
-                        float scale, bool bf16, bool scalar_gate, const Prologue& pro,
+                        float scale, bool bf16, bool scalar_gate, const Prologue& pro, void* ws,
                         hipStream_t stream) {
   const bool fu = pro.flags != 0;
 #define KDA_CH1(DK, DV, IO, OP, NWV, SG, FU)                                                 \
   return launch_chunk_t<ChunkCfg<DK, DV, IO, OP, NWV, SG, FU>>(                              \
-      q, k, v, g, beta, S0, out, S_final, cu_seqlens, n_seq, T, H, scale, pro, stream);
+      q, k, v, g, beta, S0, out, S_final, cu_seqlens, n_seq, T, H, scale, pro, ws, stream);
 #define KDA_CH(DK, DV, IO, OP, NWV)                                       \
   if (scalar_gate) {                                                      \
     if (fu) { KDA_CH1(DK, DV, IO, OP, NWV, true, true) }                  \

@@ -15,8 +15,9 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, const floa
 hipError_t launch_chunk(const void* q, const void* k, const void* v, const float* g,
                         const float* beta, const float* S0, void* out, float* S_final,
                         const int32_t* cu_seqlens, int n_seq, int T, int H, int dk, int dv,
-                        float scale, bool bf16, bool scalar_gate, const Prologue& pro,
+                        float scale, bool bf16, bool scalar_gate, const Prologue& pro, void* ws,
                         hipStream_t stream);
+size_t chunk_split_workspace_bytes(int n_seq, int H, int dk, int dv);
 bool chunk_supported(int dk, int dv, bool bf16);
 bool chunk_par_selected(int n_seq, int T, int H, int dk, int dv, bool bf16);
 size_t chunk_par_workspace_bytes(int n_seq, int T, int H);
@@ -204,6 +205,25 @@ int chunk_impl(const void* q, const void* k, const void* v, const float* log_alp
     for (const Range& r : others)
       if (overlap(rw, r)) return KDA_ERR_ALIAS;
   }
+  // packed calls: a workspace enables the balanced schedule (taken when there
+  // are more chains than resident workgroups)
+  void* split_ws = nullptr;
+  if (packed && workspace) {
+    const size_t need = kda::chunk_split_workspace_bytes(n_seq, H, d_k, d_v);
+    if (workspace_bytes < need) return KDA_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return KDA_ERR_ALIGN;
+    const size_t e = io_bytes(io_dtype);
+    const Range rw = span(workspace, need);
+    const Range others[] = {span(q, rows * H * d_k * e), span(k, rows * H * d_k * e),
+                            span(v, rows * H * d_v * e),
+                            span(log_alpha, rows * H * (sg ? 1 : d_k) * 4),
+                            span(beta, rows * H * 4), span(S0, S0 ? state : 0),
+                            span(out, rows * H * d_v * e), span(S_final, S_final ? state : 0),
+                            span(cu_seqlens, ((size_t)n_seq + 1) * 4)};
+    for (const Range& r : others)
+      if (overlap(rw, r)) return KDA_ERR_ALIAS;
+    split_ws = workspace;
+  }
   if (n_seq == 0) return KDA_OK;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (par)
@@ -216,7 +236,7 @@ int chunk_impl(const void* q, const void* k, const void* v, const float* log_alp
   }
   return launch_status(kda::launch_chunk(q, k, v, log_alpha, beta, S0, out, S_final,
                                          packed ? cu_seqlens : nullptr, n_seq, T, H, d_k, d_v,
-                                         scale, io_dtype == KDA_IO_BF16, sg, pr, s));
+                                         scale, io_dtype == KDA_IO_BF16, sg, pr, split_ws, s));
 }
 
 int decode_impl(const void* q, const void* k, const void* v, const float* log_alpha,
@@ -379,7 +399,13 @@ size_t kda_chunk_fwd_workspace_size(int B, int T, int H, int d_k, int d_v, int c
   return chunk_ws_bytes(B, T, H, d_k, d_v, chunk, io_dtype);
 }
 
-size_t kda_chunk_fwd_varlen_workspace_size(int, int, int, int, int, int, int) { return 0; }
+size_t kda_chunk_fwd_varlen_workspace_size(int N, int T_total, int H, int d_k, int d_v,
+                                           int chunk, int io_dtype) {
+  if (N <= 0 || T_total < 0 || H <= 0 || chunk != 64 || !io_ok(io_dtype) ||
+      !kda::chunk_supported(d_k, d_v, io_dtype == KDA_IO_BF16))
+    return 0;
+  return kda::chunk_split_workspace_bytes(N, H, d_k, d_v);
+}
 
 int kda_chunk_fwd(const void* q, const void* k, const void* v, const float* log_alpha,
                   const float* beta, const float* S0, void* out, float* S_final, int B, int T,
@@ -394,10 +420,9 @@ int kda_chunk_fwd_varlen(const void* q, const void* k, const void* v, const floa
                          const int32_t* cu_seqlens, int N, int T_total, int H, int d_k, int d_v,
                          float scale, int chunk, int io_dtype, void* workspace,
                          size_t workspace_bytes, void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   return chunk_impl(q, k, v, log_alpha, beta, S0, out, S_final, cu_seqlens, true, N, T_total, H,
-                    d_k, d_v, scale, chunk, io_dtype, false, nullptr, stream);
+                    d_k, d_v, scale, chunk, io_dtype, false, nullptr, stream,
+                    workspace, workspace_bytes);
 }
 
 int kda_decode_step(const void* q, const void* k, const void* v, const float* log_alpha,
@@ -437,10 +462,9 @@ int kda_gdn_chunk_fwd_varlen(const void* q, const void* k, const void* v, const 
                              const int32_t* cu_seqlens, int N, int T_total, int H, int d_k,
                              int d_v, float scale, int chunk, int io_dtype, void* workspace,
                              size_t workspace_bytes, void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   return chunk_impl(q, k, v, log_alpha, beta, S0, out, S_final, cu_seqlens, true, N, T_total, H,
-                    d_k, d_v, scale, chunk, io_dtype, true, nullptr, stream);
+                    d_k, d_v, scale, chunk, io_dtype, true, nullptr, stream,
+                    workspace, workspace_bytes);
 }
 
 int kda_gdn_decode_step(const void* q, const void* k, const void* v, const float* log_alpha,

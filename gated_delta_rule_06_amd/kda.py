@@ -224,11 +224,17 @@ def chunk_fwd_workspace_size(B, T, H, dk, dv, io="bf16", chunk=CHUNK):
 
 def chunk_fwd_varlen(q, k, v, log_alpha, beta, cu_seqlens, S0=None, scale=None, chunk=CHUNK,
                      out=None, S_final=None, output_final_state=True, qk_l2norm=False,
-                     beta_sigmoid=False, A_log=None, gate_bias=None):
+                     beta_sigmoid=False, A_log=None, gate_bias=None, balanced=True,
+                     workspace=None):
     """Packed variable-length prefill.  q, k: [T_total, H, d_k]; v: [T_total,
     H, d_v]; beta: [T_total, H]; log_alpha: [T_total, H, d_k] (KDA) or
     [T_total, H] (Gated DeltaNet); cu_seqlens: int32 [N+1] on the device; S0:
-    [N, H, d_k, d_v] fp32 or None.  Returns (o, S_final)."""
+    [N, H, d_k, d_v] fp32 or None.  balanced: give the library a workspace,
+    so that calls with more chains than resident workgroups split sequences
+    evenly over the workgroups (same bits); False keeps one workgroup per
+    chain.  workspace: a uint8 device tensor of at least
+    kda_chunk_fwd_varlen_workspace_size() bytes to use for that, or None
+    (allocated).  Returns (o, S_final)."""
     Tt, H, dk = q.shape
     dv = v.shape[-1]
     dev = q.device
@@ -250,7 +256,12 @@ def chunk_fwd_varlen(q, k, v, log_alpha, beta, cu_seqlens, S0=None, scale=None, 
     if S_final is None and output_final_state:
         S_final = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
     _check(S_final, "S_final", (N, H, dk, dv), torch.float32, dev)
-    ws, wsb = _workspace(lib.kda_chunk_fwd_varlen_workspace_size(N, Tt, H, dk, dv, chunk, io), dev)
+    ws, wsb = None, 0
+    if balanced and workspace is not None:
+        ws, wsb = workspace, workspace.numel()
+    elif balanced:
+        ws, wsb = _workspace(lib.kda_chunk_fwd_varlen_workspace_size(N, Tt, H, dk, dv, chunk, io),
+                             dev)
     pro = _prologue(H, dk, pre == "kda_gdn_", dev, qk_l2norm, beta_sigmoid, A_log, gate_bias)
     if pro is None:
         fn = pre + "chunk_fwd_varlen"

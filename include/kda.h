@@ -120,6 +120,19 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const float* log_
  *             non-decreasing, cu_seqlens[N] == T_total.  These preconditions
  *             are not checked on the device (the values are never read on the
  *             host); a violation gives undefined results.
+ *  workspace  NULL, or device memory of at least
+ *             kda_chunk_fwd_varlen_workspace_size(...) bytes, 256-byte
+ *             aligned, overlapping no other argument (else KDA_ERR_WORKSPACE,
+ *             KDA_ERR_ALIGN, KDA_ERR_ALIAS).  Its contents need no
+ *             initialisation.  With a workspace, a call of more (sequence,
+ *             head) chains than the GPU runs at once (and at most four times
+ *             as many) balances the chunks over the resident workgroups:
+ *             sequences are laid end to end and cut into equal slices
+ *             (McNaughton's wrap-around rule), a sequence that crosses a cut
+ *             continues on the next workgroup from the fp32 state handed over
+ *             in the workspace.  Chunks stay aligned to their sequence, so
+ *             the results are bit-identical to those without a workspace.
+ *             Calls that share a workspace must be ordered on one stream.
  * Returns KDA_OK or a KDA_ERR_* code.
  */
 int kda_chunk_fwd_varlen(const void* q, const void* k, const void* v, const float* log_alpha,
@@ -356,7 +369,11 @@ size_t kda_noalloc_scratch_bytes(void);
 size_t kda_chunk_fwd_workspace_size(int B, int T, int H, int d_k, int d_v, int chunk,
                                     int io_dtype);
 
-/* Workspace bytes kda_chunk_fwd_varlen needs for these sizes. */
+/* Workspace bytes kda_chunk_fwd_varlen (and kda_gdn_chunk_fwd_varlen,
+ * kda_chunk_fwd_fused with cu_seqlens) takes for the balanced schedule: the
+ * schedule's plan (per-sequence chunk prefix sums, hand-over flags) and one
+ * fp32 d_k x d_v state per hand-over slot, min(N * H, 1024) slots; 0 for
+ * unsupported sizes (the arguments are not otherwise validated here). */
 size_t kda_chunk_fwd_varlen_workspace_size(int N, int T_total, int H, int d_k, int d_v,
                                            int chunk, int io_dtype);
 

@@ -56,7 +56,13 @@ def test_status_strings_and_version(lib):
 def test_workspace_sizes(lib):
     # many chains: the one-workgroup-per-chain kernel, no workspace
     assert lib.kda_chunk_fwd_workspace_size(8, 8192, 32, 128, 128, 64, 1) == 0
-    assert lib.kda_chunk_fwd_varlen_workspace_size(16, 537014, 32, 128, 128, 64, 1) == 0
+    # packed calls: the balanced schedule's plan (flags, chunk prefix sums)
+    # and one hand-over state per slot, min(N * H, 1024) slots
+    assert lib.kda_chunk_fwd_varlen_workspace_size(16, 537014, 32, 128, 128, 64, 1) == \
+        4608 + 512 * 128 * 128 * 4
+    assert lib.kda_chunk_fwd_varlen_workspace_size(300, 9000, 8, 64, 64, 64, 0) == \
+        (4352 + 301 * 8 + 255) // 256 * 256 + 1024 * 64 * 64 * 4
+    assert lib.kda_chunk_fwd_varlen_workspace_size(4, 100, 2, 96, 128, 64, 1) == 0   # unsupported
     # few long bf16 128x128 chains: the chunk-parallel schedule's factors
     # (123,392 bytes per (chain, chunk) plus a flag each)
     assert lib.kda_chunk_fwd_workspace_size(1, 4096, 16, 128, 128, 64, 1) == 16 * 64 * 123392 + 4096
@@ -75,6 +81,20 @@ def test_chunk_parallel_needs_its_workspace(lib):
     assert call(ctypes.c_void_p(0x200000000), need - 1) == -4
     assert call(ctypes.c_void_p(0x200000000 + 16), need) == -7         # 256-byte alignment
     assert call(P_[5], need) == -6                                      # overlaps out
+
+
+def test_varlen_workspace_validation(lib):
+    """A packed call given a workspace checks its size, alignment and overlap
+    before any launch."""
+    P_ = [ctypes.c_void_p(0x100000000 + 0x10000000 * i) for i in range(8)]   # never dereferenced
+    need = lib.kda_chunk_fwd_varlen_workspace_size(40, 4000, 8, 128, 128, 64, 1)
+    call = lambda ws, n: lib.kda_chunk_fwd_varlen(P_[0], P_[1], P_[2], P_[3], P_[4], None, P_[5],
+                                                  P_[6], P_[7], 40, 4000, 8, 128, 128, 0.1, 64, 1,
+                                                  ws, n, None)
+    assert call(ctypes.c_void_p(0x200000000), need - 1) == -4          # KDA_ERR_WORKSPACE
+    assert call(ctypes.c_void_p(0x200000000 + 16), need) == -7         # 256-byte alignment
+    assert call(P_[5], need) == -6                                      # overlaps out
+    assert call(P_[7], need) == -6                                      # overlaps cu_seqlens
 
 
 P = [ctypes.c_void_p(0x10000000 + 0x1000000 * i) for i in range(12)]   # never dereferenced

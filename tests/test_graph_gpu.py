@@ -81,3 +81,38 @@ def test_prefill_replays_like_eager(B, T, H):
         assert torch.equal(out, o_ref) and torch.equal(Sf, S_ref), rep
         run()   # eager work between the replays
         torch.cuda.synchronize()
+
+
+def test_balanced_packed_prefill_replays_like_eager():
+    """The balanced schedule of a packed call (a plan kernel that clears the
+    hand-over flags, then the split kernel) under capture, replayed with eager
+    calls on the same workspace in between."""
+    import numpy as np
+    K = kda()
+    H = 8
+    lens = np.random.default_rng(43).integers(0, 2000, size=40)
+    d = inputs.varlen_inputs(lens, H, 128, 128, io="bf16", seed=43, with_S0=True, device=DEV)
+    out = torch.empty_like(d["v"])
+    Sf = torch.empty((40, H, 128, 128), dtype=torch.float32, device=DEV)
+    n = K.lib.kda_chunk_fwd_varlen_workspace_size(40, int(lens.sum()), H, 128, 128, 64, 1)
+    ws = torch.empty(n, dtype=torch.uint8, device=DEV)
+
+    def run():
+        K.chunk_fwd_varlen(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"],
+                           S0=d["S0"], out=out, S_final=Sf, workspace=ws)
+
+    run()
+    torch.cuda.synchronize()
+    o_ref, S_ref = out.clone(), Sf.clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    for rep in range(3):
+        out.zero_()
+        Sf.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, o_ref) and torch.equal(Sf, S_ref), rep
+        run()   # eager work between the replays
+        torch.cuda.synchronize()
