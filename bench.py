@@ -574,6 +574,7 @@ def main():
             "schedule": "balanced: %d workgroups, %d chunks laid end to end per head and cut "
                         "into slices of %d" % (c5_wg, c5_total, c5_slice),
             "us_per_slice_chunk": c5_ms * 1e3 / c5_slice,
+            "traffic": measured_traffic("varlen", "chunk.hip"),
             "one_workgroup_per_chain_ms": c5_chain_ms},
         "recurrent": {"workload": "multi_token_decode_n256_h32_len1to8",
                       "tokens_per_call": rec_tokens, "calls": R["calls"],
