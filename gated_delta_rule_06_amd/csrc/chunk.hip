@@ -2013,14 +2013,14 @@ static hipError_t launch_chunk_t(const void* q, const void* k, const void* v, co
 //
 // Stage A (chunk_intra_kernel, one workgroup per (chunk, head), all chunks at
 // once) forms everything that does not depend on the state; stage B
-// (chunk_scan_kernel, one wave per (chain, 16 value columns)) is the only
-// serial loop, two 128-deep products per chunk; stage C (chunk_out_kernel,
-// all chunks at once) forms the outputs.  Every factor goes through the
-// workspace as bf16 MFMA fragments in the exact lane order its consumer
-// reads, one 16-byte load per lane per fragment.  A chunk with a 16-token
-// block that decays below 2^KDA_BLOCK_LOG2_MIN in some channel (the fused
-// kernel's guard) is flagged by stage A and recomputed token by token by
-// stage B.
+// (chunk_scan_kernel, one workgroup per (chain, 16 value columns)) runs the
+// only serial loop, two 128-deep products per chunk, in one wave, while its
+// second wave forms each chunk's outputs from the state and errors the first
+// hands over through the LDS.  Every factor goes through the workspace as
+// bf16 MFMA fragments in the exact lane order its consumer reads, one 16-byte
+// load per lane per fragment.  A chunk with a 16-token block that decays
+// below 2^KDA_BLOCK_LOG2_MIN in some channel (the fused kernel's guard) is
+// flagged by stage A and recomputed token by token by stage B.
 template <class Cfg>
 struct ParLayout {
   static constexpr int DK = Cfg::DK, DV = Cfg::DV;
@@ -2032,9 +2032,7 @@ struct ParLayout {
   static constexpr int OFF_AQ = OFF_KE + MTK * 2 * FR;        // -Aqk [I 4][kt 2]
   static constexpr int OFF_U = OFF_AQ + 4 * 2 * FR;           // U    [vs][I 4][lane] 8 B
   static constexpr int OFF_GL = OFF_U + NVS * 4 * 64 * 8;     // Gamma_L [DK] fp32
-  static constexpr int OFF_SB = OFF_GL + DK * 4;              // S_c  [vs][ks][lane] 16 B
-  static constexpr int OFF_EB = OFF_SB + NVS * NKS * FR;      // -E_c [vs][kt 2][lane] 16 B
-  static constexpr int PER_CHUNK = OFF_EB + NVS * 2 * FR;
+  static constexpr int PER_CHUNK = OFF_GL + DK * 4;
   static_assert(PER_CHUNK % 256 == 0, "chunk records stay 256-byte aligned");
   // bytes of workspace for n chunk-heads: the records, then one int flag each
   static size_t bytes(size_t n) { return n * PER_CHUNK + ((n * 4 + 255) / 256) * 256; }
@@ -2265,11 +2263,17 @@ __global__ __launch_bounds__(Cfg::NTHREADS, 1) void chunk_intra_kernel(
   }
 }
 
-// Stage B: one wave per (chain, 16 value columns).
-// The fragments of chunk c + 1 are loaded while chunk c is computed: -W right
-// after its last use, -K_end, U and Gamma_L after the state update.
+// Stage B: one workgroup per (chain, 16 value columns), two waves.
+// Wave 0 scans the state: the fragments of chunk c + 1 are loaded while chunk
+// c is computed (-W right after its last use, -K_end, U and Gamma_L after the
+// state update).  It puts S_c and -E_c, as the bf16 fragments it multiplies
+// anyway, into one of two LDS slots and meets wave 1 at one barrier per chunk.
+// Wave 1 forms O_c^T = S_c^T QG^T + (-E_c)^T (-Aqk)^T from that slot, its
+// own factors a chunk ahead, and writes 4 consecutive values of a token per
+// lane.  Slot c & 1 is written again only for chunk c + 2, after the barrier
+// of chunk c + 1, which wave 1 reaches once it has read chunk c.
 template <class Cfg>
-__global__ __launch_bounds__(64, 1) void chunk_scan_kernel(
+__global__ __launch_bounds__(128, 1) void chunk_scan_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, const float* S0, void* out,
     float* S_final, char* __restrict__ ws, const int* __restrict__ flags, int T, int H, int NC,
@@ -2280,7 +2284,12 @@ __global__ __launch_bounds__(64, 1) void chunk_scan_kernel(
   typedef ParLayout<Cfg> L;
   typedef ParKernel<Cfg> P;
   typedef typename Cfg::Op Op;
+  typedef typename Cfg::Io Io;
+  typedef typename Op::F32 Frag;
   constexpr int MTK = Cfg::MTK, NKS = Cfg::NKS, DK = Cfg::DK, DV = Cfg::DV;
+  constexpr int SLOT = (NKS + 2) * L::FR;   // S_c [ks][lane], then -E_c [kt 2][lane]
+  __shared__ __attribute__((aligned(16))) char ring_[2 * SLOT];
+  LDS char* ring = (LDS char*)ring_;
   // Workgroups are dealt to the 8 XCDs round robin (block i on XCD i % 8):
   // the NVS slices of one chain go to one XCD, so that they share its L2 for
   // the chain's factors.  Blocks past the last chain have nothing to do.
@@ -2289,8 +2298,90 @@ __global__ __launch_bounds__(64, 1) void chunk_scan_kernel(
   const int chain = (r / L::NVS) * 8 + xcd, vs = r % L::NVS;
   if (chain >= n_chains) return;
   const int b = chain / H, h = chain % H;
+  const int w = threadIdx.x >> 6;
   const int l = lane_fresh();
   const int n = l & 15, g4 = 4 * (l >> 4);
+  auto rec_of = [&](int c) { return ws + ((size_t)chain * NC + (c < NC ? c : NC - 1)) * L::PER_CHUNK; };
+  auto st_slot = [&](int off, Frag f) {
+    *(LDS u32x4*)(ring + off + l * 16) =
+        __builtin_bit_cast(u32x4, __builtin_shufflevector(f.lo, f.hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  auto ld_slot = [&](int off) {
+    const u32x4 x = *(const LDS u32x4*)(ring + off + l * 16);
+    const i16x8 y = __builtin_bit_cast(i16x8, x);
+    return Frag{__builtin_shufflevector(y, y, 0, 1, 2, 3), __builtin_shufflevector(y, y, 4, 5, 6, 7)};
+  };
+  // Chunks stage A flagged are redone token by token by wave 0, which also
+  // writes their outputs; a chain without any runs loops with no branch inside.
+  int any_flag = 0;
+  for (int c = 0; c < NC; ++c) any_flag |= flags[chain * NC + c];
+
+  if (w == 1) {
+    // ---- wave 1: the outputs
+    struct OFac {
+      Frag Q[4][NKS], A[4][2];
+    };
+    auto load_o = [&](OFac& f, const char* rec) {
+#pragma unroll
+      for (int i = 0; i < 4 * NKS; ++i) f.Q[i / NKS][i % NKS] = P::ld16(rec + L::OFF_QG + i * L::FR + l * 16);
+#pragma unroll
+      for (int I = 0; I < 4; ++I)
+#pragma unroll
+        for (int kt = 0; kt <= I / 2; ++kt) f.A[I][kt] = P::ld16(rec + L::OFF_AQ + (I * 2 + kt) * L::FR + l * 16);
+    };
+    auto out_step = [&](int c, OFac& f, int pf) {
+      __syncthreads();   // chunk c's S_c and -E_c are in slot c & 1
+      const int so = (c & 1) * SLOT;
+      Frag SB[NKS], EB[2];
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) SB[ks] = ld_slot(so + ks * L::FR);
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) EB[kt] = ld_slot(so + (NKS + kt) * L::FR);
+      const int clen = min(Cfg::C, T - c * Cfg::C);
+      f32x4 o[4];
+#pragma unroll
+      for (int I = 0; I < 4; ++I) {
+        o[I] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) o[I] = Op::mma32(SB[ks], f.Q[I][ks], o[I]);
+#pragma unroll
+        for (int kt = 0; kt <= I / 2; ++kt) o[I] = Op::mma32(EB[kt], f.A[I][kt], o[I]);
+      }
+      if (pf >= 0) load_o(f, rec_of(pf));
+#pragma unroll
+      for (int I = 0; I < 4; ++I) {
+        const int t = 16 * I + (l & 15);
+        if (t < clen) {
+          const size_t row = ((size_t)b * T + (size_t)c * Cfg::C + t) * H + h;
+          Io::store4(out, row * DV + 16 * vs + 4 * (l >> 4), o[I]);
+        }
+      }
+    };
+    if (!any_flag) {
+      OFac fa, fb;
+      load_o(fa, rec_of(0));
+      load_o(fb, rec_of(1));
+      int c = 0;
+      for (; c + 1 < NC; c += 2) {
+        out_step(c, fa, c + 2);
+        out_step(c + 1, fb, c + 3);
+      }
+      if (c < NC) out_step(c, fa, -1);
+    } else {
+      OFac fa;
+      for (int c = 0; c < NC; ++c) {
+        if (flags[chain * NC + c]) {
+          __syncthreads();   // written token by token by wave 0
+        } else {
+          load_o(fa, rec_of(c));
+          out_step(c, fa, -1);
+        }
+      }
+    }
+    return;
+  }
+
+  // ---- wave 0: the state scan
   f32x4 S[MTK][1];
 #pragma unroll
   for (int mt = 0; mt < MTK; ++mt)
@@ -2299,7 +2390,7 @@ __global__ __launch_bounds__(64, 1) void chunk_scan_kernel(
       S[mt][0][r] = S0 ? S0[((size_t)chain * DK + 16 * mt + g4 + r) * DV + 16 * vs + n] : 0.f;
   // The factors of one chunk in registers.
   struct Fac {
-    typename Op::F32 W[4][NKS], K[MTK][2];
+    Frag W[4][NKS], K[MTK][2];
     u32x2 U[4];
     f32x4 G[MTK];
   };
@@ -2316,18 +2407,17 @@ __global__ __launch_bounds__(64, 1) void chunk_scan_kernel(
 #pragma unroll
     for (int i = 0; i < 2 * MTK; ++i) f.K[i / 2][i % 2] = P::ld16(rec + L::OFF_KE + i * L::FR + l * 16);
   };
-  auto rec_of = [&](int c) { return ws + ((size_t)chain * NC + (c < NC ? c : NC - 1)) * L::PER_CHUNK; };
   // One step of the scan on chunk c from the factors in f; with pf >= 0 the
   // factors of chunk pf are loaded into f behind it (-W after its last use,
   // the rest after the state update).
   auto step = [&](int c, Fac& f, int pf) {
-    char* rec = rec_of(c);
-    // S_c as 32-deep operands over keys (also stage C's A operand)
-    typename Op::F32 SB[NKS];
+    const int so = (c & 1) * SLOT;
+    // S_c as 32-deep operands over keys (also wave 1's A operand)
+    Frag SB[NKS];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      SB[ks] = typename Op::F32{Op::pack(S[2 * ks][0]), Op::pack(S[2 * ks + 1][0])};
-      P::st16(rec + L::OFF_SB + (vs * NKS + ks) * L::FR + l * 16, SB[ks]);
+      SB[ks] = Frag{Op::pack(S[2 * ks][0]), Op::pack(S[2 * ks + 1][0])};
+      st_slot(so + ks * L::FR, SB[ks]);
     }
     // E = U + (-W) S_c
     f32x4 E[4];
@@ -2340,12 +2430,13 @@ __global__ __launch_bounds__(64, 1) void chunk_scan_kernel(
     }
     if (pf >= 0) load_w(f, rec_of(pf));
     // -E as 32-deep operands over tokens
-    typename Op::F32 EB[2];
+    Frag EB[2];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-      EB[kt] = typename Op::F32{Op::pack(-E[2 * kt]), Op::pack(-E[2 * kt + 1])};
-      P::st16(rec + L::OFF_EB + (vs * 2 + kt) * L::FR + l * 16, EB[kt]);
+      EB[kt] = Frag{Op::pack(-E[2 * kt]), Op::pack(-E[2 * kt + 1])};
+      st_slot(so + (NKS + kt) * L::FR, EB[kt]);
     }
+    __syncthreads();   // slot c & 1 to wave 1
     // S <- Diag(Gamma_L) S + (-K_end)^T (-E)
 #pragma unroll
     for (int mt = 0; mt < MTK; ++mt) {
@@ -2356,12 +2447,9 @@ __global__ __launch_bounds__(64, 1) void chunk_scan_kernel(
     }
     if (pf >= 0) load_rest(f, rec_of(pf));
   };
-  // Chunks stage A flagged are redone token by token; a chain without any
-  // runs a loop with no branch inside, two chunks of factors in flight (so
-  // that the loads stay where they are issued, a chunk ahead of their use).
-  int any_flag = 0;
-  for (int c = 0; c < NC; ++c) any_flag |= flags[chain * NC + c];
   if (!any_flag) {
+    // two chunks of factors in flight (so that the loads stay where they are
+    // issued, a chunk ahead of their use)
     Fac fa, fb;
     load_w(fa, rec_of(0));
     load_rest(fa, rec_of(0));
@@ -2382,6 +2470,7 @@ __global__ __launch_bounds__(64, 1) void chunk_scan_kernel(
         const Prologue pro{0u, nullptr, nullptr};
         K::recurrent_chunk(S, q, k, v, g, beta, out, (size_t)b * T + (size_t)c * Cfg::C, H, h,
                            min(Cfg::C, T - c * Cfg::C), scale, pro, 1.f, 16 * vs);
+        __syncthreads();   // wave 1 skips this chunk
       } else {
         load_w(fa, rec_of(c));
         load_rest(fa, rec_of(c));
@@ -2395,47 +2484,6 @@ __global__ __launch_bounds__(64, 1) void chunk_scan_kernel(
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         S_final[((size_t)chain * DK + 16 * mt + g4 + r) * DV + 16 * vs + n] = S[mt][0][r];
-  }
-}
-
-// Stage C: one workgroup per (chain, chunk), wave vs = 16 value columns:
-// O^T = S_c^T QG^T + (-E)^T (-Aqk)^T, written as 4 consecutive values of a token.
-template <class Cfg>
-__global__ __launch_bounds__(Cfg::NTHREADS, 1) void chunk_out_kernel(void* out,
-                                                                     const char* __restrict__ ws,
-                                                                     int T, int H, int NC) {
-  typedef ParLayout<Cfg> L;
-  typedef ParKernel<Cfg> P;
-  typedef typename Cfg::Op Op;
-  typedef typename Cfg::Io Io;
-  constexpr int NKS = Cfg::NKS, DV = Cfg::DV;
-  const int idx = blockIdx.x;
-  const int* flags = reinterpret_cast<const int*>(ws + (size_t)gridDim.x * L::PER_CHUNK);
-  if (flags[idx]) return;   // written token by token by stage B
-  const int chain = idx / NC, c = idx % NC;
-  const int b = chain / H, h = chain % H;
-  const int clen = min(Cfg::C, T - c * Cfg::C);
-  const int vs = threadIdx.x >> 6, l = lane_fresh();
-  const char* rec = ws + (size_t)idx * L::PER_CHUNK;
-  typename Op::F32 SB[NKS], EB[2];
-#pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) SB[ks] = P::ld16(rec + L::OFF_SB + (vs * NKS + ks) * L::FR + l * 16);
-#pragma unroll
-  for (int kt = 0; kt < 2; ++kt) EB[kt] = P::ld16(rec + L::OFF_EB + (vs * 2 + kt) * L::FR + l * 16);
-#pragma unroll
-  for (int I = 0; I < 4; ++I) {
-    f32x4 o = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
-      o = Op::mma32(SB[ks], P::ld16(rec + L::OFF_QG + (I * NKS + ks) * L::FR + l * 16), o);
-#pragma unroll
-    for (int kt = 0; kt <= I / 2; ++kt)
-      o = Op::mma32(EB[kt], P::ld16(rec + L::OFF_AQ + (I * 2 + kt) * L::FR + l * 16), o);
-    const int t = 16 * I + (l & 15);
-    if (t < clen) {
-      const size_t row = ((size_t)b * T + (size_t)c * Cfg::C + t) * H + h;
-      Io::store4(out, row * DV + 16 * vs + 4 * (l >> 4), o);
-    }
   }
 }
 
@@ -2475,10 +2523,8 @@ hipError_t launch_chunk_par(const void* q, const void* k, const void* v, const f
                      (char*)ws, T, H, NC, total, scale);
   const int* flags = reinterpret_cast<const int*>((char*)ws + (size_t)chains * NC * L::PER_CHUNK);
   const int grid_b = (chains + 7) / 8 * 8 * L::NVS;
-  hipLaunchKernelGGL(chunk_scan_kernel<Cfg>, dim3(grid_b), dim3(64), 0, stream, q, k, v, g, beta,
+  hipLaunchKernelGGL(chunk_scan_kernel<Cfg>, dim3(grid_b), dim3(128), 0, stream, q, k, v, g, beta,
                      S0, out, S_final, (char*)ws, flags, T, H, NC, chains, scale);
-  hipLaunchKernelGGL(chunk_out_kernel<Cfg>, dim3(chains * NC), dim3(Cfg::NTHREADS), 0, stream, out,
-                     (const char*)ws, T, H, NC);
   return hipGetLastError();
 }
 

@@ -64,8 +64,8 @@ def test_workspace_sizes(lib):
         (4352 + 301 * 8 + 255) // 256 * 256 + 1024 * 64 * 64 * 4
     assert lib.kda_chunk_fwd_varlen_workspace_size(4, 100, 2, 96, 128, 64, 1) == 0   # unsupported
     # few long bf16 128x128 chains: the chunk-parallel schedule's factors
-    # (123,392 bytes per (chain, chunk) plus a flag each)
-    assert lib.kda_chunk_fwd_workspace_size(1, 4096, 16, 128, 128, 64, 1) == 16 * 64 * 123392 + 4096
+    # (74,240 bytes per (chain, chunk) plus a flag each)
+    assert lib.kda_chunk_fwd_workspace_size(1, 4096, 16, 128, 128, 64, 1) == 16 * 64 * 74240 + 4096
     assert lib.kda_chunk_fwd_workspace_size(1, 4096, 16, 128, 128, 64, 0) == 0   # fp32 I/O
     assert lib.kda_chunk_fwd_workspace_size(1, 4096, 16, 64, 64, 64, 1) == 0
     assert lib.kda_chunk_fwd_workspace_size(1, 511, 16, 128, 128, 64, 1) == 0   # short
