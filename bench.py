@@ -147,9 +147,14 @@ def main():
                               with_S0=False, device=dev)
     out = torch.empty((P["B"], P["T"], P["H"], P["dv"]), dtype=torch.bfloat16, device=dev)
     Sf = torch.empty((P["B"], P["H"], P["dk"], P["dv"]), dtype=torch.float32, device=dev)
+    # the call's workspace, allocated once as a serving loop would (256 chains
+    # on 256 CUs take one workgroup per chain; it is not read on this shape)
+    ws_pf = torch.empty(kda.chunk_fwd_workspace_size(P["B"], P["T"], P["H"], P["dk"], P["dv"]),
+                        dtype=torch.uint8, device=dev)
 
     def step():
-        kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], S0=None, out=out, S_final=Sf)
+        kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], S0=None, out=out, S_final=Sf,
+                      workspace=ws_pf)
 
     if args.calib_copy_mib:
         n = args.calib_copy_mib << 20
@@ -264,7 +269,8 @@ def main():
                                with_S0=False, device=dev, gate="gdn")
 
     def gdn_step():
-        kda.chunk_fwd(dg["q"], dg["k"], dg["v"], dg["g"], dg["beta"], S0=None, out=out, S_final=Sf)
+        kda.chunk_fwd(dg["q"], dg["k"], dg["v"], dg["g"], dg["beta"], S0=None, out=out, S_final=Sf,
+                      workspace=ws_pf)
 
     for _ in range(args.warmup):
         gdn_step()
@@ -329,7 +335,7 @@ def main():
     # gates were drawn before the headline, so the two legs run back to back.
     def strong_step():
         kda.chunk_fwd(d["q"], d["k"], d["v"], strong["g"], d["beta"], S0=None, out=out,
-                      S_final=Sf)
+                      S_final=Sf, workspace=ws_pf)
 
     # A longer warm-up than the headline's, in one burst with the timed
     # launches: a few launches after an idle gap the engine clock dips under
@@ -365,7 +371,7 @@ def main():
     def fused_step():
         kda.chunk_fwd(dr0["q"], dr0["k"], dr0["v"], dr0["g"], dr0["beta"], S0=None, out=out,
                       S_final=Sf, qk_l2norm=True, beta_sigmoid=True, A_log=dr0["A_log"],
-                      gate_bias=dr0["gate_bias"])
+                      gate_bias=dr0["gate_bias"], workspace=ws_pf)
 
     for _ in range(args.warmup):
         fused_step()

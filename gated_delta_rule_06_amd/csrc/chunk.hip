@@ -1756,11 +1756,11 @@ __global__ __launch_bounds__(Cfg::NTHREADS, 1) void chunk_fwd_varlen_kernel(
 // runs their sum: with skewed lengths the busiest CU can exceed the average by
 // most of a chain whatever the order (16 sequences of U{1024..65536} tokens at
 // 32 heads: 1,183 chunk steps on the busiest CU against 1,058 on average).
-// Packed calls with more chains than the GPU holds at once (up to four times
-// as many) therefore take McNaughton's wrap-around rule for preemptive
-// scheduling on identical machines (R. McNaughton, "Scheduling with deadlines
-// and loss functions", Management Science 6(1), 1959) when the caller gives a
-// workspace:
+// Calls with more chains than the GPU holds at once (up to four times as
+// many), packed or batched, therefore take McNaughton's wrap-around rule for
+// preemptive scheduling on identical machines (R. McNaughton, "Scheduling
+// with deadlines and loss functions", Management Science 6(1), 1959) when the
+// caller gives a workspace:
 //
 // - the resident workgroups form M machines of H workgroups, one per head, so
 //   that the heads of a sequence still read the same token rows side by side;
@@ -1799,9 +1799,11 @@ struct SplitWs {
 };
 
 // Chunk counts per sequence -> prefix sums (i64), slice length and total; the
-// ticket and every hand-over flag start at zero on each call.
+// ticket and every hand-over flag start at zero on each call.  cu == NULL: N
+// sequences of Tfix tokens each (the batched layout).
 __global__ __launch_bounds__(1024) void split_plan_kernel(const int32_t* __restrict__ cu, int N,
-                                                          int C, int M, int nslots, char* ws) {
+                                                          int Tfix, int C, int M, int nslots,
+                                                          char* ws) {
   __shared__ long long wsum[16];
   __shared__ long long carry;
   __shared__ int umax;
@@ -1820,7 +1822,7 @@ __global__ __launch_bounds__(1024) void split_plan_kernel(const int32_t* __restr
     const int n = base + tid;
     long long u = 0;
     if (n < N) {
-      const int len = cu[n + 1] - cu[n];
+      const int len = cu ? cu[n + 1] - cu[n] : Tfix;
       u = len > 0 ? (len + C - 1) / C : 1;
       atomicMax(&umax, (int)u);
     }
@@ -1856,8 +1858,8 @@ template <class Cfg>
 __global__ __launch_bounds__(Cfg::NTHREADS, 1) void chunk_fwd_split_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, const float* S0, void* out,
-    float* S_final, const int32_t* __restrict__ cu, int N, int H, int M, int nslots, float scale,
-    Prologue pro, char* ws) {
+    float* S_final, const int32_t* __restrict__ cu, int N, int Tfix, int H, int M, int nslots,
+    float scale, Prologue pro, char* ws) {
   extern __shared__ __attribute__((aligned(16))) char smem_[];
   LDS volatile int* sh = (LDS volatile int*)smem_;
   constexpr size_t SS = (size_t)Cfg::DK * Cfg::DV;
@@ -1887,7 +1889,9 @@ __global__ __launch_bounds__(Cfg::NTHREADS, 1) void chunk_fwd_split_kernel(
     }
     const int n = lo;
     const long long s = pre[n], u = pre[n + 1] - s;
-    const int b0 = cu[n], len = cu[n + 1] - b0;
+    // token rows of sequence n: packed from cu_seqlens, or n * Tfix batched
+    const size_t b0 = cu ? (size_t)cu[n] : (size_t)n * Tfix;
+    const int len = cu ? cu[n + 1] - cu[n] : Tfix;
     const size_t chain = (size_t)n * H + h;
     const float* sin = S0 ? S0 + chain * SS : nullptr;
     float* sout = S_final ? S_final + chain * SS : nullptr;
@@ -1930,8 +1934,8 @@ __global__ __launch_bounds__(Cfg::NTHREADS, 1) void chunk_fwd_split_kernel(
     }
     const long long r0 = (long long)C * c0;
     const long long r1 = (long long)C * c1 < len ? (long long)C * c1 : len;
-    ChunkKernel<Cfg>::run(q, k, v, g, beta, sin, out, sout, (size_t)b0 + (size_t)r0,
-                          (int)(r1 - r0), H, h, 0, scale, pro);
+    ChunkKernel<Cfg>::run(q, k, v, g, beta, sin, out, sout, b0 + (size_t)r0, (int)(r1 - r0), H,
+                          h, 0, scale, pro);
     if (post >= 0) {
       // the barrier orders every wave's state stores before thread 0's
       // device-scope release (one write-back of this XCD's L2)
@@ -1952,7 +1956,7 @@ static hipError_t launch_chunk_t(const void* q, const void* k, const void* v, co
                                  const int32_t* cu, int n_seq, int T, int H, float scale,
                                  const Prologue& pro, void* ws, hipStream_t stream) {
   const int bytes = Cfg::LDS_TOTAL;
-  if (cu && ws) {
+  if (ws) {
     // the balanced schedule when there are more chains than resident workgroups
     auto kern = chunk_fwd_split_kernel<Cfg>;
     hipError_t e = hipFuncSetAttribute((const void*)kern,
@@ -1973,10 +1977,10 @@ static hipError_t launch_chunk_t(const void* q, const void* k, const void* v, co
     const long chains = (long)n_seq * H;
     if (M >= 2 && chains > P && chains <= 4 * P) {
       const int nslots = SplitWs::slots(n_seq, H);
-      hipLaunchKernelGGL(split_plan_kernel, dim3(1), dim3(1024), 0, stream, cu, n_seq, Cfg::C, M,
-                         nslots, (char*)ws);
+      hipLaunchKernelGGL(split_plan_kernel, dim3(1), dim3(1024), 0, stream, cu, n_seq, T, Cfg::C,
+                         M, nslots, (char*)ws);
       hipLaunchKernelGGL(kern, dim3(M * H), dim3(Cfg::NTHREADS), bytes, stream, q, k, v, g, beta,
-                         S0, out, S_final, cu, n_seq, H, M, nslots, scale, pro, (char*)ws);
+                         S0, out, S_final, cu, n_seq, T, H, M, nslots, scale, pro, (char*)ws);
       return hipGetLastError();
     }
   }

@@ -166,10 +166,15 @@ namespace {
 // layout (n_seq sequences of T tokens), otherwise the packed one (T = T_total).
 // Workspace of the plain batched KDA prefill: the chunk-parallel schedule's
 // per-chunk factors when that schedule is selected for these sizes, else none.
+// The chunk-parallel schedule's factors for the shapes that take it (plain
+// KDA calls of few long chains), else the balanced schedule's plan and
+// hand-over states.
 size_t chunk_ws_bytes(int B, int T, int H, int d_k, int d_v, int chunk, int io_dtype) {
-  if (B < 0 || T < 0 || H <= 0 || chunk != 64 || !io_ok(io_dtype)) return 0;
-  if (!kda::chunk_par_selected(B, T, H, d_k, d_v, io_dtype == KDA_IO_BF16)) return 0;
-  return kda::chunk_par_workspace_bytes(B, T, H);
+  if (B <= 0 || T < 0 || H <= 0 || chunk != 64 || !io_ok(io_dtype)) return 0;
+  const bool bf16 = io_dtype == KDA_IO_BF16;
+  if (!kda::chunk_supported(d_k, d_v, bf16)) return 0;
+  if (kda::chunk_par_selected(B, T, H, d_k, d_v, bf16)) return kda::chunk_par_workspace_bytes(B, T, H);
+  return kda::chunk_split_workspace_bytes(B, H, d_k, d_v);
 }
 
 int chunk_impl(const void* q, const void* k, const void* v, const float* log_alpha,
@@ -205,10 +210,10 @@ int chunk_impl(const void* q, const void* k, const void* v, const float* log_alp
     for (const Range& r : others)
       if (overlap(rw, r)) return KDA_ERR_ALIAS;
   }
-  // packed calls: a workspace enables the balanced schedule (taken when there
-  // are more chains than resident workgroups)
+  // otherwise a workspace enables the balanced schedule (taken when there are
+  // more chains than resident workgroups)
   void* split_ws = nullptr;
-  if (packed && workspace) {
+  if (!par && workspace) {
     const size_t need = kda::chunk_split_workspace_bytes(n_seq, H, d_k, d_v);
     if (workspace_bytes < need) return KDA_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return KDA_ERR_ALIGN;
@@ -219,7 +224,7 @@ int chunk_impl(const void* q, const void* k, const void* v, const float* log_alp
                             span(log_alpha, rows * H * (sg ? 1 : d_k) * 4),
                             span(beta, rows * H * 4), span(S0, S0 ? state : 0),
                             span(out, rows * H * d_v * e), span(S_final, S_final ? state : 0),
-                            span(cu_seqlens, ((size_t)n_seq + 1) * 4)};
+                            span(cu_seqlens, cu_seqlens ? ((size_t)n_seq + 1) * 4 : 0)};
     for (const Range& r : others)
       if (overlap(rw, r)) return KDA_ERR_ALIAS;
     split_ws = workspace;
@@ -451,10 +456,8 @@ int kda_gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* 
                       const float* beta, const float* S0, void* out, float* S_final, int B, int T,
                       int H, int d_k, int d_v, float scale, int chunk, int io_dtype,
                       void* workspace, size_t workspace_bytes, void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   return chunk_impl(q, k, v, log_alpha, beta, S0, out, S_final, nullptr, false, B, T, H, d_k, d_v,
-                    scale, chunk, io_dtype, true, nullptr, stream);
+                    scale, chunk, io_dtype, true, nullptr, stream, workspace, workspace_bytes);
 }
 
 int kda_gdn_chunk_fwd_varlen(const void* q, const void* k, const void* v, const float* log_alpha,

@@ -165,12 +165,14 @@ _TRANSFORMS_DOC = """
 
 def chunk_fwd(q, k, v, log_alpha, beta, S0=None, scale=None, chunk=CHUNK, out=None,
               S_final=None, output_final_state=True, qk_l2norm=False, beta_sigmoid=False,
-              A_log=None, gate_bias=None, workspace=None):
+              A_log=None, gate_bias=None, workspace=None, balanced=True):
     """Chunkwise prefill.  q, k: [B, T, H, d_k]; v: [B, T, H, d_v]; beta:
     [B, T, H]; log_alpha: [B, T, H, d_k] (KDA) or [B, T, H] (Gated DeltaNet, one
     gate per token and head); S0: [B, H, d_k, d_v] fp32 or None.  workspace:
     a uint8 device tensor of at least chunk_fwd_workspace_size() bytes, or None
-    (allocated when the sizes need one).  Returns (o, S_final)."""
+    (allocated).  balanced=False with no workspace passes none (one workgroup
+    per chain; shapes that take the chunk-parallel schedule then fail, since
+    it needs one).  Returns (o, S_final)."""
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     dev = q.device
@@ -191,14 +193,13 @@ def chunk_fwd(q, k, v, log_alpha, beta, S0=None, scale=None, chunk=CHUNK, out=No
         S_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
     _check(S_final, "S_final", (B, H, dk, dv), torch.float32, dev)
     pro = _prologue(H, dk, pre == "kda_gdn_", dev, qk_l2norm, beta_sigmoid, A_log, gate_bias)
-    # only the plain KDA call can take the chunk-parallel schedule, which
-    # needs a workspace (kda_chunk_fwd_workspace_size gives its size)
+    # the chunk-parallel schedule (plain KDA calls of few long chains) needs a
+    # workspace; for other shapes it enables the balanced schedule
     ws, wsb = None, 0
-    if pro is None and pre == "kda_":
-        if workspace is None:
-            ws, wsb = _workspace(lib.kda_chunk_fwd_workspace_size(B, T, H, dk, dv, chunk, io), dev)
-        else:
-            ws, wsb = workspace, workspace.numel()
+    if workspace is not None:
+        ws, wsb = workspace, workspace.numel()
+    elif balanced:
+        ws, wsb = _workspace(lib.kda_chunk_fwd_workspace_size(B, T, H, dk, dv, chunk, io), dev)
     if pro is None:
         fn = pre + "chunk_fwd"
         st = getattr(lib, fn)(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S0),
@@ -216,8 +217,9 @@ def chunk_fwd(q, k, v, log_alpha, beta, S0=None, scale=None, chunk=CHUNK, out=No
 
 
 def chunk_fwd_workspace_size(B, T, H, dk, dv, io="bf16", chunk=CHUNK):
-    """Bytes of workspace kda_chunk_fwd needs for these sizes (0 when the
-    one-workgroup-per-chain kernel runs them)."""
+    """Bytes of workspace kda_chunk_fwd takes for these sizes: the
+    chunk-parallel schedule's factors where it runs, else the balanced
+    schedule's (0 for unsupported sizes)."""
     return int(lib.kda_chunk_fwd_workspace_size(B, T, H, dk, dv, chunk,
                                                 KDA_IO_BF16 if io == "bf16" else KDA_IO_F32))
 

@@ -95,7 +95,16 @@ enum kda_status {
  *  scale      multiplies q (the pages' default is d_k^-1/2)
  *  chunk      tokens per chunk; must be 64
  *  workspace  device scratch of at least kda_chunk_fwd_workspace_size(...)
- *             bytes (may be NULL when that size is 0)
+ *             bytes, 256-byte aligned, overlapping no other argument.  It is
+ *             required when the call takes the chunk-parallel schedule (bf16,
+ *             d_k = d_v = 128, plain KDA gates, at most 64 chains of at least
+ *             512 tokens: KDA_ERR_WORKSPACE without it).  Otherwise it may be
+ *             NULL; given, it enables the balanced schedule described under
+ *             kda_chunk_fwd_varlen (the B sequences of T tokens laid end to
+ *             end) for calls of one to four times as many chains as the GPU
+ *             runs at once, with bit-identical results.  Its contents need no
+ *             initialisation; calls that share it must be ordered on one
+ *             stream.
  * Returns KDA_OK or a KDA_ERR_* code.
  */
 int kda_chunk_fwd(const void* q, const void* k, const void* v, const float* log_alpha,
@@ -364,8 +373,11 @@ int kda_backward_noalloc(const void* q, const void* k, const void* v, const floa
 /* KDA_NOALLOC_SCRATCH_BYTES, as the library was built. */
 size_t kda_noalloc_scratch_bytes(void);
 
-/* Workspace bytes kda_chunk_fwd needs for these sizes (0 if none; the
- * arguments are not validated here: unsupported sizes give 0). */
+/* Workspace bytes kda_chunk_fwd (and kda_gdn_chunk_fwd, kda_chunk_fwd_fused
+ * without cu_seqlens) takes for these sizes: the chunk-parallel schedule's
+ * factors for the shapes that take it, else the balanced schedule's plan and
+ * hand-over states (as kda_chunk_fwd_varlen_workspace_size with N = B).  0 for
+ * unsupported sizes; the arguments are not otherwise validated here. */
 size_t kda_chunk_fwd_workspace_size(int B, int T, int H, int d_k, int d_v, int chunk,
                                     int io_dtype);
 

@@ -54,22 +54,24 @@ def test_status_strings_and_version(lib):
 
 
 def test_workspace_sizes(lib):
-    # many chains: the one-workgroup-per-chain kernel, no workspace
-    assert lib.kda_chunk_fwd_workspace_size(8, 8192, 32, 128, 128, 64, 1) == 0
-    # packed calls: the balanced schedule's plan (flags, chunk prefix sums)
-    # and one hand-over state per slot, min(N * H, 1024) slots
+    # the balanced schedule's plan (chunk prefix sums, flags) and one fp32
+    # hand-over state per slot, min(N * H, 1024) slots
+    split = lambda N, H, d: (4352 + (N + 1) * 8 + 255) // 256 * 256 + min(N * H, 1024) * d * d * 4
+    assert lib.kda_chunk_fwd_workspace_size(8, 8192, 32, 128, 128, 64, 1) == split(8, 32, 128)
     assert lib.kda_chunk_fwd_varlen_workspace_size(16, 537014, 32, 128, 128, 64, 1) == \
         4608 + 512 * 128 * 128 * 4
     assert lib.kda_chunk_fwd_varlen_workspace_size(300, 9000, 8, 64, 64, 64, 0) == \
         (4352 + 301 * 8 + 255) // 256 * 256 + 1024 * 64 * 64 * 4
-    assert lib.kda_chunk_fwd_varlen_workspace_size(4, 100, 2, 96, 128, 64, 1) == 0   # unsupported
     # few long bf16 128x128 chains: the chunk-parallel schedule's factors
     # (74,240 bytes per (chain, chunk) plus a flag each)
     assert lib.kda_chunk_fwd_workspace_size(1, 4096, 16, 128, 128, 64, 1) == 16 * 64 * 74240 + 4096
-    assert lib.kda_chunk_fwd_workspace_size(1, 4096, 16, 128, 128, 64, 0) == 0   # fp32 I/O
-    assert lib.kda_chunk_fwd_workspace_size(1, 4096, 16, 64, 64, 64, 1) == 0
-    assert lib.kda_chunk_fwd_workspace_size(1, 511, 16, 128, 128, 64, 1) == 0   # short
-    assert lib.kda_chunk_fwd_workspace_size(1, 4096, 16, 128, 128, 64, 1) > 0
+    assert lib.kda_chunk_fwd_workspace_size(1, 4096, 16, 64, 64, 64, 1) == split(1, 16, 64)
+    assert lib.kda_chunk_fwd_workspace_size(1, 511, 16, 128, 128, 64, 1) == split(1, 16, 128)
+    # unsupported sizes: none
+    assert lib.kda_chunk_fwd_workspace_size(1, 4096, 16, 128, 128, 64, 0) == 0   # fp32 I/O, d 128
+    assert lib.kda_chunk_fwd_workspace_size(4, 100, 2, 96, 128, 64, 1) == 0
+    assert lib.kda_chunk_fwd_workspace_size(0, 100, 2, 128, 128, 64, 1) == 0
+    assert lib.kda_chunk_fwd_varlen_workspace_size(4, 100, 2, 96, 128, 64, 1) == 0
 
 
 def test_chunk_parallel_needs_its_workspace(lib):

@@ -1,6 +1,6 @@
-"""GPU: the balanced schedule of packed prefill calls.  With a workspace and
-more (sequence, head) chains than resident workgroups (up to four times as
-many; every case here stays in that range), the library cuts the
+"""GPU: the balanced schedule of prefill calls, packed and batched.  With a
+workspace and more (sequence, head) chains than resident workgroups (up to
+four times as many; every case here stays in that range), the library cuts the
 concatenated sequences into equal slices (McNaughton's wrap-around rule) and
 hands the fp32 state of a split sequence from one workgroup to the next.
 Chunks stay aligned to their sequence, so the results must equal those of the
@@ -176,3 +176,66 @@ def test_balanced_calls_in_a_row():
         (oa, Sa), (ob, Sb) = both(d, ws)
         check_plan(ws, lens, H)
         assert torch.equal(oa, ob) and torch.equal(Sa, Sb), n_seq
+
+
+# ------------------------------------------------------------------ batched layout
+
+BATCHED = [
+    # (name, B, T, H, dk, dv, io, gate, with_S0)
+    ("kda 10 x 300 tokens", 10, 300, 32, 128, 128, "bf16", "kda", True),
+    ("gated deltanet 5 x 200", 5, 200, 64, 128, 128, "bf16", "gdn", False),
+    ("one token each", 300, 1, 1, 128, 128, "bf16", "kda", True),
+    ("fp32 64x64", 90, 130, 4, 64, 64, "f32", "kda", True),
+]
+
+
+def batched_both(d, ws, **kw):
+    K = kda()
+    args = (d["q"], d["k"], d["v"], d["g"], d["beta"])
+    a = K.chunk_fwd(*args, S0=d["S0"], workspace=ws, **kw)
+    b = K.chunk_fwd(*args, S0=d["S0"], balanced=False, **kw)
+    torch.cuda.synchronize()
+    return a, b
+
+
+def batched_workspace(B, T, H, dk, dv, io):
+    n = kda().chunk_fwd_workspace_size(B, T, H, dk, dv, io=io)
+    assert n > 0
+    return torch.empty(n, dtype=torch.uint8, device=DEV)
+
+
+@pytest.mark.parametrize("case", BATCHED, ids=[c[0] for c in BATCHED])
+def test_balanced_batched_equals_per_chain_kernel(case):
+    name, B, T, H, dk, dv, io, gate, with_S0 = case
+    note("balanced batched %s: B=%d T=%d H=%d" % (name, B, T, H))
+    d = inputs.prefill_inputs(B, T, H, dk, dv, io=io, seed=B + T, with_S0=with_S0, device=DEV,
+                              gate=gate)
+    ws = batched_workspace(B, T, H, dk, dv, io)
+    (oa, Sa), (ob, Sb) = batched_both(d, ws)
+    M, Ts = check_plan(ws, [T] * B, H)
+    note("  %d machines, slices of %d chunks, %d sequences split"
+         % (M, Ts, len(split_sequences([T] * B, Ts))))
+    assert torch.equal(oa, ob) and torch.equal(Sa, Sb)
+
+
+def test_balanced_batched_transforms_and_oracle():
+    """The input transforms through the balanced batched schedule, and the split
+    sequences against the oracle."""
+    from parity_util import gpu_chains_batched, oracle_batched
+    B, T, H = 10, 200, 32
+    d = inputs.prefill_inputs(B, T, H, 128, 128, io="bf16", seed=77, with_S0=True, device=DEV)
+    ws = batched_workspace(B, T, H, 128, 128, "bf16")
+    (oa, Sa), (ob, Sb) = batched_both(d, ws)
+    M, Ts = check_plan(ws, [T] * B, H)
+    assert torch.equal(oa, ob) and torch.equal(Sa, Sb)
+    split = split_sequences([T] * B, Ts)
+    assert split, "no sequence was split"
+    chains = [(b, h) for b in split for h in (b % H, (b + 7) % H)]
+    ro, rs = oracle_batched(d, chains)
+    go, gs = gpu_chains_batched(oa, Sa, chains)
+    assert_close(go, gs, ro, rs, tol_for("bf16"), "balanced batched split chains")
+    r = inputs.raw_layer_inputs(d, H, 128, seed=77, device=DEV)
+    kw = dict(qk_l2norm=True, beta_sigmoid=True, A_log=r["A_log"], gate_bias=r["gate_bias"])
+    (oa, Sa), (ob, Sb) = batched_both(r, ws, **kw)
+    check_plan(ws, [T] * B, H)
+    assert torch.equal(oa, ob) and torch.equal(Sa, Sb)
