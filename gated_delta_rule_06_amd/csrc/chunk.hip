@@ -51,6 +51,8 @@
 //    so that the solve yields -E directly and no extra negation is needed;
 //  * the next chunk's inputs are loaded into registers while this chunk is
 //    computed, in three batches spread over the phases.
+#include <stdlib.h>
+
 #include "common.h"
 
 namespace kda {
@@ -1779,7 +1781,9 @@ __global__ __launch_bounds__(Cfg::NTHREADS, 1) void chunk_fwd_varlen_kernel(
 // actually start; a machine's workgroups wait only on tickets taken earlier,
 // whose first piece waits on nothing, so every wait ends whatever order the
 // hardware starts workgroups in.  A wait is bounded all the same: past
-// KDA_SPLIT_SPIN polls the workgroup recomputes the first piece itself.
+// KDA_SPLIT_SPIN polls (or the count in the environment variable
+// KDA_SPLIT_SPIN_POLLS, which tests set to 0 to take this path) the workgroup
+// recomputes the first piece itself.
 struct SplitWs {
   static constexpr size_t OFF_TICKET = 0;                             // u32
   static constexpr size_t OFF_T = 8;                                  // i64 slice length
@@ -1859,7 +1863,7 @@ __global__ __launch_bounds__(Cfg::NTHREADS, 1) void chunk_fwd_split_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, const float* S0, void* out,
     float* S_final, const int32_t* __restrict__ cu, int N, int Tfix, int H, int M, int nslots,
-    float scale, Prologue pro, char* ws) {
+    int spin, float scale, Prologue pro, char* ws) {
   extern __shared__ __attribute__((aligned(16))) char smem_[];
   LDS volatile int* sh = (LDS volatile int*)smem_;
   constexpr size_t SS = (size_t)Cfg::DK * Cfg::DV;
@@ -1918,7 +1922,7 @@ __global__ __launch_bounds__(Cfg::NTHREADS, 1) void chunk_fwd_split_kernel(
     if (wait >= 0) {
       if (threadIdx.x == 0) {
         int got = 0;
-        for (int it = 0; it < KDA_SPLIT_SPIN && !got; ++it) {
+        for (int it = 0; it < spin && !got; ++it) {
           got = __hip_atomic_load(flags + wait, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) != 0u;
           if (!got) __builtin_amdgcn_s_sleep(8);
         }
@@ -1948,6 +1952,18 @@ __global__ __launch_bounds__(Cfg::NTHREADS, 1) void chunk_fwd_split_kernel(
 
 size_t chunk_split_workspace_bytes(int n_seq, int H, int dk, int dv) {
   return SplitWs::bytes(n_seq, H, dk, dv);
+}
+
+// The poll limit of a hand-over wait: KDA_SPLIT_SPIN, or a non-negative count
+// from the environment variable KDA_SPLIT_SPIN_POLLS (read on every call).
+static int split_spin_polls() {
+  const char* e = getenv("KDA_SPLIT_SPIN_POLLS");
+  if (e && *e) {
+    char* end = nullptr;
+    const long v = strtol(e, &end, 10);
+    if (end && *end == '\0' && v >= 0 && v <= KDA_SPLIT_SPIN) return (int)v;
+  }
+  return KDA_SPLIT_SPIN;
 }
 
 template <class Cfg>
@@ -1980,7 +1996,8 @@ static hipError_t launch_chunk_t(const void* q, const void* k, const void* v, co
       hipLaunchKernelGGL(split_plan_kernel, dim3(1), dim3(1024), 0, stream, cu, n_seq, T, Cfg::C,
                          M, nslots, (char*)ws);
       hipLaunchKernelGGL(kern, dim3(M * H), dim3(Cfg::NTHREADS), bytes, stream, q, k, v, g, beta,
-                         S0, out, S_final, cu, n_seq, T, H, M, nslots, scale, pro, (char*)ws);
+                         S0, out, S_final, cu, n_seq, T, H, M, nslots, split_spin_polls(), scale,
+                         pro, (char*)ws);
       return hipGetLastError();
     }
   }

@@ -12,9 +12,10 @@
 #define KDA_PAR_MAX_CHAINS 64
 #define KDA_PAR_MIN_T 512
 #define KDA_PAR_MAX_WS ((size_t)8 << 30)
-// The balanced schedule for packed calls uses at most this many resident
-// workgroups, and a workgroup polls a state hand-over at most KDA_SPLIT_SPIN
-// times (about 0.2 us apart) before it recomputes the first chunks itself.
+// The balanced prefill schedule uses at most this many resident workgroups,
+// and a workgroup polls a state hand-over at most KDA_SPLIT_SPIN times (about
+// 0.2 us apart; the environment variable KDA_SPLIT_SPIN_POLLS may set fewer)
+// before it recomputes the first chunks itself.
 #define KDA_SPLIT_MAX_WG 1024
 #define KDA_SPLIT_SPIN (1 << 22)
 

@@ -142,6 +142,11 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const float* log_
  *             in the workspace.  Chunks stay aligned to their sequence, so
  *             the results are bit-identical to those without a workspace.
  *             Calls that share a workspace must be ordered on one stream.
+ *             A workgroup waits for a handed-over state for a bounded number
+ *             of polls (2^22, or the count in the environment variable
+ *             KDA_SPLIT_SPIN_POLLS, read on every call) and past it
+ *             recomputes the sequence's first chunks itself: same results,
+ *             more work (tests set 0 to take that path).
  * Returns KDA_OK or a KDA_ERR_* code.
  */
 int kda_chunk_fwd_varlen(const void* q, const void* k, const void* v, const float* log_alpha,

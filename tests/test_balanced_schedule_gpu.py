@@ -239,3 +239,25 @@ def test_balanced_batched_transforms_and_oracle():
     (oa, Sa), (ob, Sb) = batched_both(r, ws, **kw)
     check_plan(ws, [T] * B, H)
     assert torch.equal(oa, ob) and torch.equal(Sa, Sb)
+
+
+def test_balanced_without_hand_over(monkeypatch):
+    """With no polls allowed (KDA_SPLIT_SPIN_POLLS=0) every workgroup that
+    would wait for a handed-over state recomputes the sequence from its start
+    instead: the bounded wait's other branch, same bits."""
+    monkeypatch.setenv("KDA_SPLIT_SPIN_POLLS", "0")
+    rng = np.random.default_rng(16)
+    lens = rng.integers(0, 3000, size=40)
+    H = 8
+    d = inputs.varlen_inputs(lens, H, 128, 128, io="bf16", seed=16, with_S0=True, device=DEV)
+    ws = workspace_for(d)
+    (oa, Sa), (ob, Sb) = both(d, ws)
+    M, T = check_plan(ws, lens, H)
+    assert split_sequences(lens, T), "no sequence was split"
+    assert torch.equal(oa, ob) and torch.equal(Sa, Sb)
+    B, Tb = 10, 300
+    db = inputs.prefill_inputs(B, Tb, 32, 128, 128, io="bf16", seed=16, with_S0=True, device=DEV)
+    wb = batched_workspace(B, Tb, 32, 128, 128, "bf16")
+    (oa, Sa), (ob, Sb) = batched_both(db, wb)
+    check_plan(wb, [Tb] * B, 32)
+    assert torch.equal(oa, ob) and torch.equal(Sa, Sb)
