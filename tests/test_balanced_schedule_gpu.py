@@ -81,6 +81,7 @@ CASES = [
     ("gated deltanet", 48, 1, 2000, 8, 128, 128, "bf16", "gdn", True, 3),
     ("fp32 64x64", 120, 0, 300, 4, 64, 64, "f32", "kda", True, 4),
     ("bf16 128x64", 70, 0, 1500, 8, 128, 64, "bf16", "kda", True, 5),
+    ("one head", 700, 0, 300, 1, 128, 128, "bf16", "kda", True, 6),
 ]
 
 
@@ -261,3 +262,38 @@ def test_balanced_without_hand_over(monkeypatch):
     (oa, Sa), (ob, Sb) = batched_both(db, wb)
     check_plan(wb, [Tb] * B, 32)
     assert torch.equal(oa, ob) and torch.equal(Sa, Sb)
+
+
+def test_balanced_random_mixes():
+    """Twelve seeded length mixes and head counts (1 to 32 heads; empty, short,
+    ragged and long sequences; with and without S0), each with 1 to 4 chains
+    per resident workgroup: every output and final state equal to one
+    workgroup per chain's."""
+    rng = np.random.default_rng(2024)
+    done = 0
+    while done < 12:
+        H = int(rng.choice([1, 2, 4, 8, 16, 32]))
+        kind = done % 4
+        n_lo, n_hi = -(-260 // H), 1024 // H
+        n_seq = int(rng.integers(n_lo, n_hi + 1))
+        if kind == 0:
+            lens = rng.integers(0, 400, size=n_seq)
+        elif kind == 1:
+            lens = rng.integers(1, 65, size=n_seq)
+        elif kind == 2:
+            lens = np.where(rng.random(n_seq) < 0.1, rng.integers(2000, 6000, size=n_seq),
+                            rng.integers(0, 200, size=n_seq))
+        else:
+            lens = rng.integers(500, 1500, size=n_seq)
+        if int(lens.sum()) * H > 4_000_000:
+            continue
+        with_S0 = bool(rng.integers(0, 2))
+        note("random mix %d: H=%d, %d sequences, %d tokens, S0=%s"
+             % (done, H, n_seq, int(lens.sum()), with_S0))
+        d = inputs.varlen_inputs(lens, H, 128, 128, io="bf16", seed=100 + done, with_S0=with_S0,
+                                 device=DEV)
+        ws = workspace_for(d)
+        (oa, Sa), (ob, Sb) = both(d, ws)
+        check_plan(ws, lens, H)
+        assert torch.equal(oa, ob) and torch.equal(Sa, Sb), done
+        done += 1
