@@ -2059,6 +2059,60 @@ struct ParLayout {
   static size_t bytes(size_t n) { return n * PER_CHUNK + ((n * 4 + 255) / 256) * 256; }
 };
 
+// Where the chunk-parallel records come from.  Batched (cu == NULL): chain
+// b * H + h has NC chunks of the sequence at rows b * T, records chain * NC +
+// c.  Packed: the chunk prefix sums pre[] of the balanced schedule's plan
+// (split_plan_kernel; an empty sequence counts one chunk, of no tokens, which
+// leaves its state as it is), the records of sequence n head-major from
+// H * pre[n].
+struct ParTable {
+  const int32_t* cu;
+  const long long* pre;
+  int T, H, NC, C;
+  // chain -> first record, chunks, first token row, tokens
+  __device__ __forceinline__ void chain(int ch, long long& rec0, int& nc, size_t& row0,
+                                        int& len) const {
+    const int n = ch / H, h = ch % H;
+    if (cu) {
+      const long long p0 = pre[n];
+      nc = (int)(pre[n + 1] - p0);
+      rec0 = (long long)H * p0 + (long long)h * nc;
+      row0 = (size_t)cu[n];
+      len = cu[n + 1] - cu[n];
+    } else {
+      nc = NC;
+      rec0 = (long long)ch * NC;
+      row0 = (size_t)n * T;
+      len = T;
+    }
+  }
+  // record -> first token row of its chunk, head, tokens (0 past the end)
+  __device__ __forceinline__ void record(long long idx, int N, size_t& row0, int& h,
+                                         int& clen) const {
+    if (cu) {
+      int lo = 0, hi = N - 1;   // the sequence: first n with H * pre[n + 1] > idx
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if ((long long)H * pre[mid + 1] > idx) hi = mid;
+        else lo = mid + 1;
+      }
+      const long long p0 = pre[lo];
+      const int nc = (int)(pre[lo + 1] - p0);
+      const long long r = idx - (long long)H * p0;
+      h = (int)(r / nc);
+      const int c = (int)(r % nc);
+      const int len = cu[lo + 1] - cu[lo];
+      row0 = (size_t)cu[lo] + (size_t)c * C;
+      clen = max(0, min(C, len - c * C));
+    } else {
+      const int chain = (int)(idx / NC), c = (int)(idx % NC);
+      h = chain % H;
+      row0 = (size_t)(chain / H) * T + (size_t)c * C;
+      clen = min(C, T - c * C);
+    }
+  }
+};
+
 template <class Cfg>
 struct ParKernel {
   typedef ChunkKernel<Cfg> K;
@@ -2211,8 +2265,9 @@ struct ParKernel {
 template <class Cfg>
 __global__ __launch_bounds__(Cfg::NTHREADS, 1) void chunk_intra_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
-    const float* __restrict__ g, const float* __restrict__ beta, char* __restrict__ ws, int T,
-    int H, int NC, int total, float scale) {
+    const float* __restrict__ g, const float* __restrict__ beta, char* __restrict__ ws,
+    int* __restrict__ flags, ParTable tab, int N, long long total_host,
+    const long long* __restrict__ total_dev, float scale) {
   typedef ChunkKernel<Cfg> K;
   typedef ParLayout<Cfg> L;
   typedef ParKernel<Cfg> P;
@@ -2220,17 +2275,16 @@ __global__ __launch_bounds__(Cfg::NTHREADS, 1) void chunk_intra_kernel(
   typedef typename Cfg::T OpT;
   extern __shared__ __attribute__((aligned(16))) char smem_[];
   LDS char* smem = (LDS char*)smem_;
-  int* flags = reinterpret_cast<int*>(ws + (size_t)total * L::PER_CHUNK);
+  const int H = tab.H;
+  // records: known on the host when batched, H times the plan's chunk total when packed
+  const long long total = total_dev ? (long long)H * *total_dev : total_host;
   {
     LDS OpT* AQ = (LDS OpT*)(smem + Cfg::OFF_AQ);   // tiles above the diagonal stay zero
     for (int i = threadIdx.x; i < Cfg::C * Cfg::LD_AQ; i += Cfg::NTHREADS) AQ[i] = Op::cvt(0.f);
   }
   // record idx -> first token row, head, tokens
-  auto where = [&](int idx, size_t& row0, int& h, int& clen) {
-    const int chain = idx / NC, c = idx % NC;
-    h = chain % H;
-    row0 = (size_t)(chain / H) * T + (size_t)c * Cfg::C;
-    clen = min(Cfg::C, T - c * Cfg::C);
+  auto where = [&](long long idx, size_t& row0, int& h, int& clen) {
+    tab.record(idx, N, row0, h, clen);
   };
   const typename K::Offsets offs = K::lane_offsets(H);
   const typename K::PrepAddr pa = K::prep_addr();
@@ -2238,13 +2292,13 @@ __global__ __launch_bounds__(Cfg::NTHREADS, 1) void chunk_intra_kernel(
   LDS int* FL = (LDS int*)(smem + Cfg::OFF_FL);
   const int w = threadIdx.x >> 6;
   typename K::Raw raw;
-  size_t row0;
-  int h, clen;
-  where(blockIdx.x, row0, h, clen);
+  size_t row0 = 0;
+  int h = 0, clen = 0;
+  if (blockIdx.x < total) where(blockIdx.x, row0, h, clen);
   K::template load_raw<K::LOAD_ALL>(raw, offs, q, k, v, g, beta, row0, H, h, clen);
-  for (int idx = blockIdx.x; idx < total; idx += gridDim.x) {
+  for (long long idx = blockIdx.x; idx < total; idx += gridDim.x) {
     // the next record (an empty range after the last: nothing is read)
-    const int nidx = idx + gridDim.x;
+    const long long nidx = idx + gridDim.x;
     size_t nrow0 = row0;
     int nh = h, nlen = 0;
     if (nidx < total) where(nidx, nrow0, nh, nlen);
@@ -2297,7 +2351,7 @@ template <class Cfg>
 __global__ __launch_bounds__(128, 1) void chunk_scan_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, const float* S0, void* out,
-    float* S_final, char* __restrict__ ws, const int* __restrict__ flags, int T, int H, int NC,
+    float* S_final, char* __restrict__ ws, const int* __restrict__ flags, ParTable tab,
     int n_chains, float scale) {
   // flags: stage A's per-chunk flags, read-only here (scalar loads: a vector
   // load would make each step wait for every prefetched factor)
@@ -2318,11 +2372,15 @@ __global__ __launch_bounds__(128, 1) void chunk_scan_kernel(
   const int xcd = blockIdx.x % 8, r = blockIdx.x / 8;
   const int chain = (r / L::NVS) * 8 + xcd, vs = r % L::NVS;
   if (chain >= n_chains) return;
-  const int b = chain / H, h = chain % H;
+  const int H = tab.H, h = chain % H;
+  long long rec0;
+  int NC, T;
+  size_t row_base;
+  tab.chain(chain, rec0, NC, row_base, T);   // the chain's records and token rows
   const int w = threadIdx.x >> 6;
   const int l = lane_fresh();
   const int n = l & 15, g4 = 4 * (l >> 4);
-  auto rec_of = [&](int c) { return ws + ((size_t)chain * NC + (c < NC ? c : NC - 1)) * L::PER_CHUNK; };
+  auto rec_of = [&](int c) { return ws + (size_t)(rec0 + (c < NC ? c : NC - 1)) * L::PER_CHUNK; };
   auto st_slot = [&](int off, Frag f) {
     *(LDS u32x4*)(ring + off + l * 16) =
         __builtin_bit_cast(u32x4, __builtin_shufflevector(f.lo, f.hi, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -2335,7 +2393,7 @@ __global__ __launch_bounds__(128, 1) void chunk_scan_kernel(
   // Chunks stage A flagged are redone token by token by wave 0, which also
   // writes their outputs; a chain without any runs loops with no branch inside.
   int any_flag = 0;
-  for (int c = 0; c < NC; ++c) any_flag |= flags[chain * NC + c];
+  for (int c = 0; c < NC; ++c) any_flag |= flags[rec0 + c];
 
   if (w == 1) {
     // ---- wave 1: the outputs
@@ -2373,7 +2431,7 @@ __global__ __launch_bounds__(128, 1) void chunk_scan_kernel(
       for (int I = 0; I < 4; ++I) {
         const int t = 16 * I + (l & 15);
         if (t < clen) {
-          const size_t row = ((size_t)b * T + (size_t)c * Cfg::C + t) * H + h;
+          const size_t row = (row_base + (size_t)c * Cfg::C + t) * H + h;
           Io::store4(out, row * DV + 16 * vs + 4 * (l >> 4), o[I]);
         }
       }
@@ -2391,7 +2449,7 @@ __global__ __launch_bounds__(128, 1) void chunk_scan_kernel(
     } else {
       OFac fa;
       for (int c = 0; c < NC; ++c) {
-        if (flags[chain * NC + c]) {
+        if (flags[rec0 + c]) {
           __syncthreads();   // written token by token by wave 0
         } else {
           load_o(fa, rec_of(c));
@@ -2486,10 +2544,10 @@ __global__ __launch_bounds__(128, 1) void chunk_scan_kernel(
     // (rare) without prefetching
     Fac fa;
     for (int c = 0; c < NC; ++c) {
-      if (flags[chain * NC + c]) {
+      if (flags[rec0 + c]) {
         // outside the chunk-start reference's range: the recurrence token by token
         const Prologue pro{0u, nullptr, nullptr};
-        K::recurrent_chunk(S, q, k, v, g, beta, out, (size_t)b * T + (size_t)c * Cfg::C, H, h,
+        K::recurrent_chunk(S, q, k, v, g, beta, out, row_base + (size_t)c * Cfg::C, H, h,
                            min(Cfg::C, T - c * Cfg::C), scale, pro, 1.f, 16 * vs);
         __syncthreads();   // wave 1 skips this chunk
       } else {
@@ -2508,7 +2566,7 @@ __global__ __launch_bounds__(128, 1) void chunk_scan_kernel(
   }
 }
 
-// The schedule by shape: a bf16 128x128 batch of few, long chains takes the
+// The schedule by shape: bf16 128x128 calls of few, long chains take the
 // chunk-parallel stages (the state chain of each sequence is then 128-deep
 // products only); everything else the one-workgroup-per-chain kernel.
 size_t chunk_par_workspace_bytes(int n_seq, int T, int H) {
@@ -2517,14 +2575,37 @@ size_t chunk_par_workspace_bytes(int n_seq, int T, int H) {
   return ParLayout<Cfg>::bytes((size_t)n_seq * H * NC);
 }
 
+// Packed: the chunk table (the balanced schedule's plan region), then records
+// for at most H * (ceil(T_total / C) + N) chunks (each sequence's last chunk
+// may be partial; an empty sequence takes one record).
+static size_t par_varlen_records(int N, int T_total, int H) {
+  const size_t C = 64;
+  return (size_t)H * (((size_t)T_total + C - 1) / C + (size_t)N);
+}
+
+size_t chunk_par_varlen_workspace_bytes(int N, int T_total, int H) {
+  typedef ChunkCfg<128, 128, IoBf16, OpBf16, 8, false, false> Cfg;
+  static_assert(Cfg::C == 64, "chunk");
+  return SplitWs::off_state(N) + ParLayout<Cfg>::bytes(par_varlen_records(N, T_total, H));
+}
+
 bool chunk_par_selected(int n_seq, int T, int H, int dk, int dv, bool bf16) {
   return bf16 && dk == 128 && dv == 128 && n_seq > 0 && (long)n_seq * H <= KDA_PAR_MAX_CHAINS &&
          T >= KDA_PAR_MIN_T && chunk_par_workspace_bytes(n_seq, T, H) <= KDA_PAR_MAX_WS;
 }
 
+// packed: the same few chains, at least KDA_PAR_MIN_T tokens per sequence on average
+bool chunk_par_varlen_selected(int N, int T_total, int H, int dk, int dv, bool bf16) {
+  return bf16 && dk == 128 && dv == 128 && N > 0 && (long)N * H <= KDA_PAR_MAX_CHAINS &&
+         (long)T_total >= (long)KDA_PAR_MIN_T * N &&
+         chunk_par_varlen_workspace_bytes(N, T_total, H) <= KDA_PAR_MAX_WS;
+}
+
+// cu == NULL: n_seq sequences of T tokens (batched); otherwise packed, T = T_total
 hipError_t launch_chunk_par(const void* q, const void* k, const void* v, const float* g,
                             const float* beta, const float* S0, void* out, float* S_final,
-                            int n_seq, int T, int H, float scale, void* ws, hipStream_t stream) {
+                            const int32_t* cu, int n_seq, int T, int H, float scale, void* ws,
+                            hipStream_t stream) {
   typedef ChunkCfg<128, 128, IoBf16, OpBf16, 8, false, false> Cfg;
   typedef ParLayout<Cfg> L;
   const int NC = (T + Cfg::C - 1) / Cfg::C;
@@ -2538,14 +2619,33 @@ hipError_t launch_chunk_par(const void* q, const void* k, const void* v, const f
   e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return e;
-  const int total = chains * NC;
-  const int grid_a = total < cus ? total : cus;
-  hipLaunchKernelGGL(ka, dim3(grid_a), dim3(Cfg::NTHREADS), bytes, stream, q, k, v, g, beta,
-                     (char*)ws, T, H, NC, total, scale);
-  const int* flags = reinterpret_cast<const int*>((char*)ws + (size_t)chains * NC * L::PER_CHUNK);
+  ParTable tab{cu, nullptr, T, H, NC, Cfg::C};
+  char* rec = (char*)ws;
+  size_t R;
+  long long total_host = 0;
+  const long long* total_dev = nullptr;
+  int grid_a;
+  if (cu) {
+    // the chunk table: chunks per sequence as prefix sums (the plan kernel,
+    // one machine; its slice length goes unused)
+    hipLaunchKernelGGL(split_plan_kernel, dim3(1), dim3(1024), 0, stream, cu, n_seq, T, Cfg::C, 1,
+                       0, (char*)ws);
+    tab.pre = reinterpret_cast<const long long*>((char*)ws + SplitWs::OFF_PRE);
+    total_dev = reinterpret_cast<const long long*>((char*)ws + SplitWs::OFF_TOTAL);
+    rec = (char*)ws + SplitWs::off_state(n_seq);
+    R = par_varlen_records(n_seq, T, H);
+    grid_a = cus;   // workgroups past the last record exit at once
+  } else {
+    R = (size_t)chains * NC;
+    total_host = (long long)R;
+    grid_a = total_host < cus ? (int)total_host : cus;
+  }
+  int* flags = reinterpret_cast<int*>(rec + R * L::PER_CHUNK);
+  hipLaunchKernelGGL(ka, dim3(grid_a), dim3(Cfg::NTHREADS), bytes, stream, q, k, v, g, beta, rec,
+                     flags, tab, n_seq, total_host, total_dev, scale);
   const int grid_b = (chains + 7) / 8 * 8 * L::NVS;
   hipLaunchKernelGGL(chunk_scan_kernel<Cfg>, dim3(grid_b), dim3(128), 0, stream, q, k, v, g, beta,
-                     S0, out, S_final, (char*)ws, flags, T, H, NC, chains, scale);
+                     S0, out, S_final, rec, flags, tab, chains, scale);
   return hipGetLastError();
 }
 

@@ -20,10 +20,13 @@ hipError_t launch_chunk(const void* q, const void* k, const void* v, const float
 size_t chunk_split_workspace_bytes(int n_seq, int H, int dk, int dv);
 bool chunk_supported(int dk, int dv, bool bf16);
 bool chunk_par_selected(int n_seq, int T, int H, int dk, int dv, bool bf16);
+bool chunk_par_varlen_selected(int N, int T_total, int H, int dk, int dv, bool bf16);
 size_t chunk_par_workspace_bytes(int n_seq, int T, int H);
+size_t chunk_par_varlen_workspace_bytes(int N, int T_total, int H);
 hipError_t launch_chunk_par(const void* q, const void* k, const void* v, const float* g,
                             const float* beta, const float* S0, void* out, float* S_final,
-                            int n_seq, int T, int H, float scale, void* ws, hipStream_t stream);
+                            const int32_t* cu, int n_seq, int T, int H, float scale, void* ws,
+                            hipStream_t stream);
 hipError_t launch_recurrent(const void* q, const void* k, const void* v, const float* g,
                             const float* beta, const float* S0, void* out, float* S_final,
                             const int32_t* cu, int n_seq, int T, int H, int dk, int dv,
@@ -194,11 +197,15 @@ int chunk_impl(const void* q, const void* k, const void* v, const float* log_alp
   st = check_prologue(pro, H, d_k, sg, &pr, span(out, rows * H * d_v * io_bytes(io_dtype)),
                       span(S_final, S_final ? state : 0));
   if (st != KDA_OK) return st;
-  // the chunk-parallel schedule (plain batched KDA calls of few long chains)
-  const bool par = !packed && !sg && pr.flags == 0 &&
-                   kda::chunk_par_selected(n_seq, T, H, d_k, d_v, io_dtype == KDA_IO_BF16);
+  // the chunk-parallel schedule (plain KDA calls of few long chains; packed
+  // calls take it when given a workspace, batched ones need one)
+  const bool bf16 = io_dtype == KDA_IO_BF16;
+  const bool par = !sg && pr.flags == 0 &&
+                   (packed ? workspace && kda::chunk_par_varlen_selected(n_seq, T, H, d_k, d_v, bf16)
+                           : kda::chunk_par_selected(n_seq, T, H, d_k, d_v, bf16));
   if (par) {
-    const size_t need = kda::chunk_par_workspace_bytes(n_seq, T, H);
+    const size_t need = packed ? kda::chunk_par_varlen_workspace_bytes(n_seq, T, H)
+                               : kda::chunk_par_workspace_bytes(n_seq, T, H);
     if (!workspace || workspace_bytes < need) return KDA_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return KDA_ERR_ALIGN;
     const size_t e = io_bytes(io_dtype);
@@ -206,7 +213,8 @@ int chunk_impl(const void* q, const void* k, const void* v, const float* log_alp
     const Range others[] = {span(q, rows * H * d_k * e), span(k, rows * H * d_k * e),
                             span(v, rows * H * d_v * e), span(log_alpha, rows * H * d_k * 4),
                             span(beta, rows * H * 4), span(S0, S0 ? state : 0),
-                            span(out, rows * H * d_v * e), span(S_final, S_final ? state : 0)};
+                            span(out, rows * H * d_v * e), span(S_final, S_final ? state : 0),
+                            span(cu_seqlens, cu_seqlens ? ((size_t)n_seq + 1) * 4 : 0)};
     for (const Range& r : others)
       if (overlap(rw, r)) return KDA_ERR_ALIAS;
   }
@@ -232,8 +240,9 @@ int chunk_impl(const void* q, const void* k, const void* v, const float* log_alp
   if (n_seq == 0) return KDA_OK;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (par)
-    return launch_status(kda::launch_chunk_par(q, k, v, log_alpha, beta, S0, out, S_final, n_seq,
-                                               T, H, scale, workspace, s));
+    return launch_status(kda::launch_chunk_par(q, k, v, log_alpha, beta, S0, out, S_final,
+                                               packed ? cu_seqlens : nullptr, n_seq, T, H, scale,
+                                               workspace, s));
   if (!packed && T == 0) {
     if (!S_final || S0 == S_final) return KDA_OK;
     hipLaunchKernelGGL(copy_state_kernel, dim3(1024), dim3(256), 0, s, S0, S_final, state / 4);
@@ -406,9 +415,12 @@ size_t kda_chunk_fwd_workspace_size(int B, int T, int H, int d_k, int d_v, int c
 
 size_t kda_chunk_fwd_varlen_workspace_size(int N, int T_total, int H, int d_k, int d_v,
                                            int chunk, int io_dtype) {
+  const bool bf16 = io_dtype == KDA_IO_BF16;
   if (N <= 0 || T_total < 0 || H <= 0 || chunk != 64 || !io_ok(io_dtype) ||
-      !kda::chunk_supported(d_k, d_v, io_dtype == KDA_IO_BF16))
+      !kda::chunk_supported(d_k, d_v, bf16))
     return 0;
+  if (kda::chunk_par_varlen_selected(N, T_total, H, d_k, d_v, bf16))
+    return kda::chunk_par_varlen_workspace_bytes(N, T_total, H);
   return kda::chunk_split_workspace_bytes(N, H, d_k, d_v);
 }
 

@@ -149,6 +149,12 @@ def _prologue(H, dk, per_head, device, qk_l2norm, beta_sigmoid, A_log, gate_bias
                      None if gate_bias is None else gate_bias.data_ptr())
 
 
+# The chunk-parallel schedule runs plain KDA calls of at most this many (sequence,
+# head) chains; other calls of so few chains use no workspace at all (the
+# balanced schedule needs more chains than resident workgroups).
+_PAR_MAX_CHAINS = 64
+
+
 def _workspace(nbytes, device):
     if nbytes == 0:
         return None, 0
@@ -198,7 +204,7 @@ def chunk_fwd(q, k, v, log_alpha, beta, S0=None, scale=None, chunk=CHUNK, out=No
     ws, wsb = None, 0
     if workspace is not None:
         ws, wsb = workspace, workspace.numel()
-    elif balanced:
+    elif balanced and (B * H > _PAR_MAX_CHAINS or (pro is None and pre == "kda_")):
         ws, wsb = _workspace(lib.kda_chunk_fwd_workspace_size(B, T, H, dk, dv, chunk, io), dev)
     if pro is None:
         fn = pre + "chunk_fwd"
@@ -258,13 +264,13 @@ def chunk_fwd_varlen(q, k, v, log_alpha, beta, cu_seqlens, S0=None, scale=None, 
     if S_final is None and output_final_state:
         S_final = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
     _check(S_final, "S_final", (N, H, dk, dv), torch.float32, dev)
+    pro = _prologue(H, dk, pre == "kda_gdn_", dev, qk_l2norm, beta_sigmoid, A_log, gate_bias)
     ws, wsb = None, 0
     if balanced and workspace is not None:
         ws, wsb = workspace, workspace.numel()
-    elif balanced:
+    elif balanced and (N * H > _PAR_MAX_CHAINS or (pro is None and pre == "kda_")):
         ws, wsb = _workspace(lib.kda_chunk_fwd_varlen_workspace_size(N, Tt, H, dk, dv, chunk, io),
                              dev)
-    pro = _prologue(H, dk, pre == "kda_gdn_", dev, qk_l2norm, beta_sigmoid, A_log, gate_bias)
     if pro is None:
         fn = pre + "chunk_fwd_varlen"
         st = getattr(lib, fn)(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S0),

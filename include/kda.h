@@ -98,7 +98,10 @@ enum kda_status {
  *             bytes, 256-byte aligned, overlapping no other argument.  It is
  *             required when the call takes the chunk-parallel schedule (bf16,
  *             d_k = d_v = 128, plain KDA gates, at most 64 chains of at least
- *             512 tokens: KDA_ERR_WORKSPACE without it).  Otherwise it may be
+ *             512 tokens: KDA_ERR_WORKSPACE without it), which forms the WY
+ *             factors of every chunk at once into the workspace and then scans
+ *             each chain's state over them ("Kimi Unveils Delta Attention and
+ *             K3 Architecture Updates", section 6.6).  Otherwise it may be
  *             NULL; given, it enables the balanced schedule described under
  *             kda_chunk_fwd_varlen (the B sequences of T tokens laid end to
  *             end) for calls of one to four times as many chains as the GPU
@@ -133,7 +136,12 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const float* log_
  *             kda_chunk_fwd_varlen_workspace_size(...) bytes, 256-byte
  *             aligned, overlapping no other argument (else KDA_ERR_WORKSPACE,
  *             KDA_ERR_ALIGN, KDA_ERR_ALIAS).  Its contents need no
- *             initialisation.  With a workspace, a call of more (sequence,
+ *             initialisation.  With a workspace, a call of few long sequences
+ *             (bf16, d_k = d_v = 128, plain KDA gates, at most 64 chains, at
+ *             least 512 tokens per sequence on average) takes the
+ *             chunk-parallel schedule described under kda_chunk_fwd, with
+ *             its records listed per sequence (results within rounding of
+ *             the schedule without a workspace); and a call of more (sequence,
  *             head) chains than the GPU runs at once (and at most four times
  *             as many) balances the chunks over the resident workgroups:
  *             sequences are laid end to end and cut into equal slices
@@ -387,10 +395,12 @@ size_t kda_chunk_fwd_workspace_size(int B, int T, int H, int d_k, int d_v, int c
                                     int io_dtype);
 
 /* Workspace bytes kda_chunk_fwd_varlen (and kda_gdn_chunk_fwd_varlen,
- * kda_chunk_fwd_fused with cu_seqlens) takes for the balanced schedule: the
- * schedule's plan (per-sequence chunk prefix sums, hand-over flags) and one
- * fp32 d_k x d_v state per hand-over slot, min(N * H, 1024) slots; 0 for
- * unsupported sizes (the arguments are not otherwise validated here). */
+ * kda_chunk_fwd_fused with cu_seqlens) takes: for plain KDA shapes that take
+ * the chunk-parallel schedule, its chunk table and the records of at most
+ * H * (ceil(T_total / 64) + N) chunks; otherwise the balanced schedule's plan
+ * (per-sequence chunk prefix sums, hand-over flags) and one fp32 d_k x d_v
+ * state per hand-over slot, min(N * H, 1024) slots; 0 for unsupported sizes
+ * (the arguments are not otherwise validated here). */
 size_t kda_chunk_fwd_varlen_workspace_size(int N, int T_total, int H, int d_k, int d_v,
                                            int chunk, int io_dtype);
 

@@ -67,6 +67,13 @@ def test_workspace_sizes(lib):
     assert lib.kda_chunk_fwd_workspace_size(1, 4096, 16, 128, 128, 64, 1) == 16 * 64 * 74240 + 4096
     assert lib.kda_chunk_fwd_workspace_size(1, 4096, 16, 64, 64, 64, 1) == split(1, 16, 64)
     assert lib.kda_chunk_fwd_workspace_size(1, 511, 16, 128, 128, 64, 1) == split(1, 16, 128)
+    # few long packed sequences (bf16 128x128, at most 64 chains, at least 512 tokens
+    # per sequence on average): the chunk table, then records for at most
+    # H * (ceil(T_total / 64) + N) chunks and a flag each
+    rec = 16 * (2048 + 2)
+    assert lib.kda_chunk_fwd_varlen_workspace_size(2, 131072, 16, 128, 128, 64, 1) == \
+        4608 + rec * 74240 + (rec * 4 + 255) // 256 * 256
+    assert lib.kda_chunk_fwd_varlen_workspace_size(4, 1000, 16, 128, 128, 64, 1) == split(4, 16, 128)
     # unsupported sizes: none
     assert lib.kda_chunk_fwd_workspace_size(1, 4096, 16, 128, 128, 64, 0) == 0   # fp32 I/O, d 128
     assert lib.kda_chunk_fwd_workspace_size(4, 100, 2, 96, 128, 64, 1) == 0

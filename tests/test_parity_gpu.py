@@ -190,6 +190,53 @@ def test_chunk_parallel_schedule_matches_oracle(B, T, H, with_S0, strong):
     assert_close(go, gs, ro, rs, tol_for("bf16"), "chunk-parallel")
 
 
+PACKED_PAR = [
+    # (lens, H, with_S0, strong)
+    ([700, 1300, 0, 2085], 8, True, None),
+    ([4096], 16, False, None),
+    ([3000, 65, 1, 2900], 16, True, -3.0),
+    ([1500, 2500], 4, True, -20.0),
+]
+
+
+@pytest.mark.parametrize("lens,H,with_S0,strong", PACKED_PAR)
+def test_chunk_parallel_packed_matches_oracle(lens, H, with_S0, strong):
+    """Few long packed sequences take the chunk-parallel schedule through the
+    chunk table of the packed call (empty, one-token and ragged sequences among
+    them); every chain against the oracle.  ``strong`` as in the batched test,
+    over packed rows 128 .. 300 (-20: flagged chunks redone token by token)."""
+    K = kda()
+    N = len(lens)
+    note("chunk-parallel packed lens=%s H=%d S0=%s strong=%s" % (lens, H, with_S0, strong))
+    d = inputs.varlen_inputs(lens, H, 128, 128, io="bf16", seed=sum(lens) + H, with_S0=with_S0,
+                             device=DEV)
+    if strong is not None:
+        gen = torch.Generator(device=DEV)
+        gen.manual_seed(7)
+        idx = torch.randperm(128, generator=gen, device=DEV)[:8]
+        sl = d["g"][128:300]
+        sl[..., idx] = strong
+    n = K.lib.kda_chunk_fwd_varlen_workspace_size(N, d["T_total"], H, 128, 128, 64, 1)
+    ws = torch.zeros(n, dtype=torch.uint8, device=DEV)
+    o, S = K.chunk_fwd_varlen(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"],
+                              S0=d["S0"], workspace=ws)
+    torch.cuda.synchronize()
+    # white-box: the chunk table's total (chunks, an empty sequence counting one)
+    # shows that the chunk-parallel stages ran
+    total = int(ws[16:24].cpu().numpy().view(np.int64)[0])
+    assert total == sum(max(1, -(-L // 64)) for L in lens)
+    chains = [(s, h) for s in range(N) for h in range(H)]
+    ro, rs = oracle_varlen(d, chains)
+    go, gs = gpu_chains_varlen(o, S, d["cu_seqlens"], chains)
+    assert_close(go, gs, ro, rs, tol_for("bf16"), "chunk-parallel packed")
+    # without a workspace: one workgroup per chain, the same results within the bar
+    o1, S1 = K.chunk_fwd_varlen(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"],
+                                S0=d["S0"], balanced=False)
+    torch.cuda.synchronize()
+    assert rel_l2(o.float().cpu().numpy(), o1.float().cpu().numpy()) < tol_for("bf16")
+    assert rel_l2(S.cpu().numpy(), S1.cpu().numpy()) < tol_for("bf16")
+
+
 def test_headline_prefill_sampled_chains():
     """B=8, H=32, T=8192, d=128 bf16 at full size in the benchmark's launch;
     the oracle recomputes a sample of chains one by one."""
