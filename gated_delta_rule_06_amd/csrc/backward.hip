@@ -338,7 +338,7 @@ __global__ __launch_bounds__(Cfg::NT) void kda_bwd_kernel(
     const void* __restrict__ dout, const float* __restrict__ dSf, float* __restrict__ dq,
     float* __restrict__ dk, float* __restrict__ dv, float* __restrict__ dg,
     float* __restrict__ dbeta, float* __restrict__ dS0, const int32_t* __restrict__ cu, int T,
-    int H, float scale, float* ws, float* vp) {
+    int H, float scale, float* ws, float* vp, const int* __restrict__ only) {
   typedef Bwd<Cfg> K;
   typedef typename K::Stage Stage;
   constexpr int DK = Cfg::DK, DV = Cfg::DV, RPT = Cfg::RPT;
@@ -365,6 +365,7 @@ __global__ __launch_bounds__(Cfg::NT) void kda_bwd_kernel(
     __syncthreads();   // the LDS is the kernel's from here on
   }
   const int nh = n * H + h;
+  if (only && only[nh] == 0) return;   // a chain the chunkwise backward has done
   Lane ln;
   ln.w = threadIdx.x >> 6;
   ln.l = threadIdx.x & 63;
@@ -525,7 +526,7 @@ hipError_t launch_bwd_t(const void* q, const void* k, const void* v, const float
                         const float* beta, const float* S0, const void* dout, const float* dSf,
                         float* dq, float* dk, float* dv, float* dg, float* dbeta, float* dS0,
                         const int32_t* cu, int n_seq, int T, int H, float scale, float* ws,
-                        hipStream_t stream) {
+                        const int* only, hipStream_t stream) {
   const int bytes = Cfg::LDS_FLOATS * 4;
   auto kern = kda_bwd_kernel<Cfg>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -535,18 +536,31 @@ hipError_t launch_bwd_t(const void* q, const void* k, const void* v, const float
   const size_t rows = cu ? (size_t)T : (size_t)n_seq * T;
   float* vp = ws + ((size_t)n_seq + rows / BK) * (size_t)H * Cfg::DK * Cfg::DV;
   hipLaunchKernelGGL(kern, dim3(n_seq * H), dim3(Cfg::NT), bytes, stream, q, k, v, g, beta, S0,
-                     dout, dSf, dq, dk, dv, dg, dbeta, dS0, cu, T, H, scale, ws, vp);
+                     dout, dSf, dq, dk, dv, dg, dbeta, dS0, cu, T, H, scale, ws, vp, only);
   return hipGetLastError();
 }
 
+// One int per chain at the front of the workspace: set by the chunkwise
+// backward for chains it leaves to the token loop.
+size_t flag_bytes(int n_seq, int H) { return ((size_t)n_seq * H * 4 + 255) / 256 * 256; }
+
 }  // namespace
 
-// Checkpoint slots the backward needs: n_seq + rows / BK per head.
-// Checkpoint slots (n_seq + rows / BK per head), then v - p of every token.
+// The chain flags, then checkpoint slots (n_seq + rows / BK per head) and v - p
+// of every token.  The chunkwise backward's states (one bf16 state per 32
+// tokens) fit in the space of the checkpoints.
 size_t backward_workspace_bytes(int n_seq, size_t rows, int H, int dk, int dv) {
-  return (((size_t)n_seq + rows / BK) * (size_t)H * dk * dv + rows * (size_t)H * dv) *
-         sizeof(float);
+  return flag_bytes(n_seq, H) +
+         (((size_t)n_seq + rows / BK) * (size_t)H * dk * dv + rows * (size_t)H * dv) *
+             sizeof(float);
 }
+
+hipError_t launch_backward_chunk(const void* q, const void* k, const void* v, const float* g,
+                                 const float* beta, const float* S0, const void* dout,
+                                 const float* dSf, float* dq, float* dk, float* dv, float* dg,
+                                 float* dbeta, float* dS0, const int32_t* cu, int n_seq, int T,
+                                 int H, float scale, bool scalar_gate, void* states, int* flags,
+                                 hipStream_t stream);
 
 hipError_t launch_backward(const void* q, const void* k, const void* v, const float* g,
                            const float* beta, const float* S0, const void* dout, const float* dSf,
@@ -554,9 +568,22 @@ hipError_t launch_backward(const void* q, const void* k, const void* v, const fl
                            const int32_t* cu, int n_seq, int T, int H, int d_k, int d_v,
                            float scale, bool bf16, bool scalar_gate, float* ws,
                            hipStream_t stream) {
+  // bf16 at d_k = d_v = 128: the chunkwise backward on MFMA, then the token
+  // loop for the chains it flagged (a chunk whose decay is beyond its range)
+  int* flags = reinterpret_cast<int*>(ws);
+  const int* only = nullptr;
+  ws = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + flag_bytes(n_seq, H));
+  if (bf16 && d_k == 128 && d_v == 128) {
+    const hipError_t e =
+        launch_backward_chunk(q, k, v, g, beta, S0, dout, dSf, dq, dk, dv, dg, dbeta, dS0, cu,
+                              n_seq, T, H, scale, scalar_gate, ws, flags, stream);
+    if (e != hipSuccess) return e;
+    only = flags;
+  }
 #define KDA_BW1(DK, DV, IO, SG)                                                                   \
   return launch_bwd_t<BwdCfg<DK, DV, IO, SG>>(q, k, v, g, beta, S0, dout, dSf, dq, dk, dv, dg,    \
-                                              dbeta, dS0, cu, n_seq, T, H, scale, ws, stream);
+                                              dbeta, dS0, cu, n_seq, T, H, scale, ws, only,       \
+                                              stream);
 #define KDA_BW(DK, DV)                                      \
   if (bf16) {                                               \
     if (scalar_gate) { KDA_BW1(DK, DV, IoBf16, true) }      \

@@ -1,0 +1,795 @@
+// backward_chunk.hip -- chunkwise backward on MFMA (bf16 I/O, d_k = d_v = 128).
+//
+// The gradients of the recurrence of "Kimi Unveils Delta Attention and K3
+// Architecture Updates", section 4, taken through its chunkwise form (section
+// 6, the training schedule): per chunk of C = 32 tokens with incoming state
+// S_c, cumulative log decay b_i (inclusive prefix sum of g inside the chunk)
+// and a per-channel reference r = b_15 (the chunk's middle),
+//
+//   QG = s Q e^{b-r}   KG = K e^{b-r}   KI = K e^{r-b}         (per element)
+//   A   = strict_tril(KG KI^T)          Aqk = tril(QG KI^T)     (sections 6.3, 6.5)
+//   T   = (I + Diag(beta) A)^{-1}       W = T Diag(beta) KG     U = T Diag(beta) V
+//   S_m = Diag(e^r) S_c                 E = U - W S_m           (section 6.4)
+//   O   = QG S_m + Aqk E                S_{c+1} = Diag(e^{b_L - r}) (S_m + KI^T E)
+//
+// Every product of a row factor and a column factor is e^{b_i - b_j}, so the
+// chunk's algebra is that of section 6 exactly; the reference only keeps the
+// stored factors within e^{+-76} when the chunk's two halves each decay by at
+// most that much in every channel (log alpha above about -4.7 on average over
+// 16 tokens, which covers the range (-5, 0) the pages give for K3's gates but
+// for saturated runs).  A chain with a chunk beyond that is flagged and left to
+// the token-by-token backward.
+//
+// Reverse mode, per chunk, given dS = dL/dS_{c+1} and dO (dS_m = Diag(e^{b_L-r}) dS):
+//   dE  = KI dS_m + Aqk^T dO                 dS_c = Diag(e^r)(dS_m + QG^T dO - W^T dE)
+//   dQG = dO S_m^T + dAqk KI,  dAqk = tril(dO E^T)
+//   dW  = -dE S_m^T,  dY = T^T [dE | dW],  dV = beta dY_v,  dKG = beta dY_k + dA KI
+//   dL  = -(dY_v U^T + dY_k W^T) (strict lower),  dA = Diag(beta) dL
+//   dbeta_i = sum_j dL_ij A_ij + dY_v,i . V_i + dY_k,i . KG_i
+//   dKI = dA^T KG + dAqk^T QG + E dS_m^T
+//   dq = s e^{b-r} dQG,  dk = e^{b-r} dKG + e^{r-b} dKI
+//   db = q dq + k (e^{b-r} dKG - e^{r-b} dKI),  plus sum_v dS S_{c+1} on the last token
+//   dlog_alpha_t = sum_{i >= t} db_i  (inside the chunk)
+// The loss does not depend on r (it cancels in every product), so r is held
+// constant in the derivative.
+//
+// Mapping (one workgroup of 8 waves per (sequence, head) chain):
+//  * a forward sweep carries S in fp32 registers and stores each chunk's S_c
+//    to the workspace as bf16 (the lanes' own order, 512 contiguous bytes per
+//    wave and tile); the reverse sweep reads S_c back and carries dS in fp32;
+//  * wave w owns value columns [16w, 16w+16) of S, dS, U, E, dE and dY_v, and
+//    key channels [16w, 16w+16) of dQG, dW, dY_k, dKG and dKI; a lane's prep
+//    elements (tokens 4g + r and 16 + 4g + r, channel 16w + l%16, g = lane/16)
+//    are exactly its accumulator elements of the latter, so the epilogue needs
+//    no exchange;
+//  * the in-chunk prefix sums (b) and suffix sums (dlog alpha) are fp32 MFMAs
+//    against triangular ones matrices built in registers;
+//  * operands go through LDS transposed ([channel][token]), the accumulator's
+//    natural 8-byte store; contractions over tokens read rows, contractions
+//    over channels use the gfx950 transpose read (ds_read_b64_tr_b16); S and
+//    dS in registers serve as 32-deep operands with the k index relabelled
+//    (two stacked 16-row accumulator tiles);
+//  * T is formed in fp32: the two 16x16 diagonal blocks by forward
+//    substitution (one wave each), then T_10 = -T_11 L_10 T_00.
+#include "common.h"
+
+namespace kda {
+
+namespace {
+
+#define LDS __attribute__((address_space(3)))
+
+constexpr int BC = 32;          // tokens per chunk
+constexpr int DD = 128;         // d_k = d_v
+constexpr int NW = 8;           // waves
+constexpr int NT = 64 * NW;     // threads
+constexpr int LT = BC + 8;      // row length (bf16) of [channel][token] buffers: 80 bytes
+constexpr int LR = DD + 8;      // row length (bf16) of the [value][channel] state buffer
+constexpr int LA = BC + 1;      // row length (fp32) of A and T
+constexpr float RANGE = 76.f;   // bound on |b_i - r| for the stored factors
+constexpr int SLOT_DW = DD * DD / 2;   // dwords of one bf16 state in the workspace
+
+// LDS layout (bytes)
+constexpr int SZ_T = DD * LT * 2;      // [128][40] bf16
+constexpr int SZ_S = BC * LT * 2;      // [32][40] bf16
+constexpr int SZ_F = BC * LA * 4;      // [32][33] fp32
+constexpr int O_QG = 0;
+constexpr int O_KG = O_QG + SZ_T;
+constexpr int O_KI = O_KG + SZ_T;
+constexpr int O_V = O_KI + SZ_T;       // V, then (own rows) dY_v
+constexpr int O_DO = O_V + SZ_T;
+constexpr int O_NW = O_DO + SZ_T;      // -W
+constexpr int O_NU = O_NW + SZ_T;      // -U
+constexpr int O_E = O_NU + SZ_T;
+constexpr int O_NDE = O_E + SZ_T;      // -dE, then dY_k
+constexpr int O_R = O_NDE + SZ_T;      // [value][channel]: S_m, then dS_m
+constexpr int O_A = O_R + DD * LR * 2; // fp32 A (strict lower)
+constexpr int O_T = O_A + SZ_F;        // fp32 T
+constexpr int O_AQ = O_T + SZ_F;       // Aqk^T  [j][i]
+constexpr int O_TT = O_AQ + SZ_S;      // T^T    [j][i]
+constexpr int O_TB = O_TT + SZ_S;      // (T Diag(beta))^T
+constexpr int O_DAQ = O_TB + SZ_S;     // dAqk^T
+constexpr int O_DA = O_DAQ + SZ_S;     // dA^T
+constexpr int O_BETA = O_DA + SZ_S;    // f32[32]
+constexpr int O_ER = O_BETA + 128;     // f32[128] e^r
+constexpr int O_DL = O_ER + 512;       // f32[128] e^{b_L - r}
+constexpr int O_RP = O_DL + 512;       // f32[8][128] per-wave partials of sum_v dS_m S_m
+constexpr int NDBP = 19;               // dbeta partial slots: 8 (dY_v), 8 (dY_k), 3 (dL)
+constexpr int O_DBP = O_RP + 4096;     // f32[19][32]
+constexpr int O_GP = O_DBP + NDBP * 128;   // f32[8][32] per-token dlog alpha partials (per-head gate)
+constexpr int O_FLAG = O_GP + 1024;
+constexpr int LDS_BYTES = O_FLAG + 16;
+static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef LDS uint16_t* lb;
+
+__device__ __forceinline__ f32x4 mma(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ bf16x8 cat(i16x4 lo, i16x4 hi) {
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+__device__ __forceinline__ i16x4 tr(const LDS uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS i16x4*)(p));
+}
+__device__ __forceinline__ bf16x8 pack8(f32x4 a, f32x4 b) {
+  u32x4 w{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(b[0], b[1]),
+          pack_bf16x2(b[2], b[3])};
+  return __builtin_bit_cast(bf16x8, w);
+}
+__device__ __forceinline__ f32x4 unpack4(u32x2 w) {
+  return f32x4{__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xffff0000u),
+               __uint_as_float(w[1] << 16), __uint_as_float(w[1] & 0xffff0000u)};
+}
+
+// Lane coordinates: n = lane % 16, g = lane / 16, wave w.
+struct Ln {
+  int n, g, w, l;
+};
+
+// The lane coordinates, re-materialised after every barrier: the volatile asm
+// keeps the compiler from hoisting lane-dependent LDS addresses out of the
+// chunk loops, where they would hold registers for the whole kernel.
+__device__ __forceinline__ Ln fresh() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return Ln{l & 15, l >> 4, __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6), l};
+}
+
+// Operand reads.  Natural k order: lane (n, g) holds k0 + 8g + e, e < 8.
+// X[row0 + n][k0 + 8g + e]
+__device__ __forceinline__ bf16x8 rd_row(const LDS uint16_t* X, int ld, int row0, int k0,
+                                         const Ln& L) {
+  return *(const LDS bf16x8*)(X + (row0 + L.n) * ld + k0 + 8 * L.g);
+}
+// X[k0 + 8g + e][col0 + n]
+__device__ __forceinline__ bf16x8 rd_tr(const LDS uint16_t* X, int ld, int k0, int col0,
+                                        const Ln& L) {
+  const LDS uint16_t* p = X + (k0 + 8 * L.g + (L.n >> 2)) * ld + col0 + 4 * (L.n & 3);
+  return cat(tr(p), tr(p + 4 * ld));
+}
+// Relabelled k order, to pair with two stacked accumulator tiles in registers:
+// position 8g + e holds k0 + 4g + e (e < 4) and k0 + 16 + 4g + e - 4 (e >= 4).
+__device__ __forceinline__ bf16x8 rd_rowp(const LDS uint16_t* X, int ld, int row0, int k0,
+                                          const Ln& L) {
+  const LDS uint16_t* p = X + (row0 + L.n) * ld + k0 + 4 * L.g;
+  return cat(*(const LDS i16x4*)p, *(const LDS i16x4*)(p + 16));
+}
+__device__ __forceinline__ bf16x8 rd_trp(const LDS uint16_t* X, int ld, int k0, int col0,
+                                         const Ln& L) {
+  const LDS uint16_t* p = X + (k0 + 4 * L.g + (L.n >> 2)) * ld + col0 + 4 * (L.n & 3);
+  return cat(tr(p), tr(p + 16 * ld));
+}
+// Accumulator tile (rows row0 + 4g + r, column col0 + n) stored transposed:
+// Xt[col0 + n][row0 + 4g + r], one 8-byte write.
+__device__ __forceinline__ void st_t(LDS uint16_t* Xt, int ld, int col0, int row0, f32x4 v,
+                                     const Ln& L) {
+  *(LDS u32x2*)(Xt + (col0 + L.n) * ld + row0 + 4 * L.g) =
+      u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+}
+__device__ __forceinline__ void st_raw(LDS uint16_t* Xt, int ld, int col0, int row0, u32x2 v,
+                                       const Ln& L) {
+  *(LDS u32x2*)(Xt + (col0 + L.n) * ld + row0 + 4 * L.g) = v;
+}
+__device__ __forceinline__ u32x2 ld_raw(const LDS uint16_t* Xt, int ld, int col0, int row0,
+                                        const Ln& L) {
+  return *(const LDS u32x2*)(Xt + (col0 + L.n) * ld + row0 + 4 * L.g);
+}
+__device__ __forceinline__ float shfl(float x, int src) {
+  return __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(x)));
+}
+
+// One chunk's per-lane inputs: tokens 16I + 4g + r (I < 2, r < 4) of channel or
+// value column 16w + n; bf16 as two packed words per I.
+struct In {
+  u32x2 q[2], k[2], v[2], o[2];
+  float gt[2][4];
+};
+
+template <bool SG>
+__device__ __forceinline__ void load_in(In& x, const uint16_t* q, const uint16_t* k,
+                                        const uint16_t* v, const uint16_t* dout, const float* g,
+                                        size_t tok0, int L, int H, int h, bool rev, const Ln& ln) {
+  const int c = 16 * ln.w + ln.n;
+#pragma unroll
+  for (int I = 0; I < 2; ++I) {
+    uint32_t wq[4], wk[4], wv[4], wo[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = 16 * I + 4 * ln.g + r;
+      const bool ok = i < L;
+      const size_t row = (tok0 + i) * H + h;
+      const size_t e = row * DD + c;
+      wq[r] = (ok && rev) ? q[e] : 0u;
+      wk[r] = ok ? k[e] : 0u;
+      wv[r] = ok ? v[e] : 0u;
+      wo[r] = (ok && rev) ? dout[e] : 0u;
+      x.gt[I][r] = ok ? (SG ? g[row] : g[e]) : 0.f;
+    }
+    x.q[I] = u32x2{wq[0] | (wq[1] << 16), wq[2] | (wq[3] << 16)};
+    x.k[I] = u32x2{wk[0] | (wk[1] << 16), wk[2] | (wk[3] << 16)};
+    x.v[I] = u32x2{wv[0] | (wv[1] << 16), wv[2] | (wv[3] << 16)};
+    x.o[I] = u32x2{wo[0] | (wo[1] << 16), wo[2] | (wo[3] << 16)};
+  }
+}
+
+// b - r for the lane's eight elements (prefix sums as MFMAs: lane group g
+// supplies token 4g + s at step s, the ones matrix is formed per lane), and
+// whether any lies beyond RANGE.  Also e^r and e^{b_L - r} of the lane's channel.
+__device__ __forceinline__ bool prefix(const In& x, f32x4 bm[2], float& er, float& dl,
+                                       const Ln& ln) {
+  f32x4 b0{0.f, 0.f, 0.f, 0.f}, b1{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const float a = (4 * ln.g + s <= ln.n) ? 1.f : 0.f;
+    b0 = mma4(a, x.gt[0][s], b0);
+    b1 = mma4(1.f, x.gt[0][s], b1);
+    b1 = mma4(a, x.gt[1][s], b1);
+  }
+  const float r = shfl(b0[3], 48 + ln.n);    // b_15 of the lane's channel
+  const float bl = shfl(b1[3], 48 + ln.n);   // b_31
+  bool bad = false;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    bm[0][e] = b0[e] - r;
+    bm[1][e] = b1[e] - r;
+    bad |= !(fabsf(bm[0][e]) <= RANGE) || !(fabsf(bm[1][e]) <= RANGE);
+  }
+  er = __expf(r);
+  dl = __expf(bl - r);
+  return bad;
+}
+
+// Forward substitution for the diagonal block bb of T = (I + Diag(beta) A)^{-1};
+// lane (n, g) forms column n, rows 4g + r.  Writes T (fp32), T^T and
+// (T Diag(beta))^T (bf16).
+__device__ __forceinline__ void solve_diag(LDS char* lds, int bb, const Ln& ln) {
+  const LDS float* A = (const LDS float*)(lds + O_A);
+  LDS float* Tf = (LDS float*)(lds + O_T);
+  const LDS float* beta = (const LDS float*)(lds + O_BETA);
+  const int off = 16 * bb;
+  float x[4], bet[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    x[r] = (4 * ln.g + r == ln.n) ? 1.f : 0.f;
+    bet[r] = beta[off + 4 * ln.g + r];
+  }
+#pragma unroll
+  for (int m = 0; m < 15; ++m) {
+    const float xm = shfl(x[m & 3], ln.n + 16 * (m >> 2));
+#pragma unroll
+    for (int r = 0; r < 4; ++r)   // A is zero on and above the diagonal
+      x[r] -= bet[r] * A[(off + 4 * ln.g + r) * LA + off + m] * xm;
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) Tf[(off + 4 * ln.g + r) * LA + off + ln.n] = x[r];
+  const f32x4 t{x[0], x[1], x[2], x[3]};
+  st_t((lb)(lds + O_TT), LT, off, off, t, ln);
+  st_t((lb)(lds + O_TB), LT, off, off, t * beta[off + ln.n], ln);
+}
+
+// T_10 = -T_11 (Diag(beta_1) A_10) T_00 (one wave).
+__device__ __forceinline__ void solve_off(LDS char* lds, const Ln& ln) {
+  const LDS float* A = (const LDS float*)(lds + O_A);
+  const LDS float* Tf = (const LDS float*)(lds + O_T);
+  const LDS float* beta = (const LDS float*)(lds + O_BETA);
+  float X[4] = {0.f, 0.f, 0.f, 0.f}, bet[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) bet[r] = beta[16 + 4 * ln.g + r];
+#pragma unroll
+  for (int m = 0; m < 16; ++m) {
+    const float t = Tf[m * LA + ln.n];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) X[r] += bet[r] * A[(16 + 4 * ln.g + r) * LA + m] * t;
+  }
+  float Y[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int m = 0; m < 16; ++m) {
+    const float xm = shfl(X[m & 3], ln.n + 16 * (m >> 2));
+#pragma unroll
+    for (int r = 0; r < 4; ++r) Y[r] -= Tf[(16 + 4 * ln.g + r) * LA + 16 + m] * xm;
+  }
+  const f32x4 t{Y[0], Y[1], Y[2], Y[3]};
+  st_t((lb)(lds + O_TT), LT, 0, 16, t, ln);
+  st_t((lb)(lds + O_TB), LT, 0, 16, t * beta[ln.n], ln);
+}
+
+// Lower-triangle 16x16 tiles of a 32x32 matrix: (0,0), (1,0), (1,1).
+__device__ __forceinline__ int tile_I(int t) { return t == 0 ? 0 : 1; }
+__device__ __forceinline__ int tile_J(int t) { return t == 2 ? 1 : 0; }
+
+// Writes every input prep product of one chunk: KG, KI, V (and, reverse sweep,
+// QG and dO) as [channel][token] bf16, e^r and e^{b_L - r} of the lane's channel.
+__device__ __forceinline__ void prep_store(LDS char* lds, const In& x, const f32x4 bm[2], float er,
+                                           float dl, float scale, bool rev, const Ln& ln) {
+#pragma unroll
+  for (int I = 0; I < 2; ++I) {
+    const f32x4 kf = unpack4(x.k[I]);
+    f32x4 p, pi;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      p[e] = __expf(bm[I][e]);
+      pi[e] = __expf(-bm[I][e]);
+    }
+    st_t((lb)(lds + O_KG), LT, 16 * ln.w, 16 * I, kf * p, ln);
+    st_t((lb)(lds + O_KI), LT, 16 * ln.w, 16 * I, kf * pi, ln);
+    st_raw((lb)(lds + O_V), LT, 16 * ln.w, 16 * I, x.v[I], ln);
+    if (rev) {
+      st_t((lb)(lds + O_QG), LT, 16 * ln.w, 16 * I, unpack4(x.q[I]) * p * scale, ln);
+      st_raw((lb)(lds + O_DO), LT, 16 * ln.w, 16 * I, x.o[I], ln);
+    }
+  }
+  if (ln.g == 0) {
+    ((LDS float*)(lds + O_ER))[16 * ln.w + ln.n] = er;
+    ((LDS float*)(lds + O_DL))[16 * ln.w + ln.n] = dl;
+  }
+}
+
+// A = strict_tril(KG KI^T) (fp32) and, reverse sweep, Aqk = tril(QG KI^T)
+// (bf16, transposed): six tiles on waves 0..5.
+__device__ __forceinline__ void tiles_a(LDS char* lds, bool rev, const Ln& ln) {
+  if (ln.w >= (rev ? 6 : 3)) return;
+  const bool qk = ln.w >= 3;
+  const int t = qk ? ln.w - 3 : ln.w;
+  const int I = tile_I(t), J = tile_J(t);
+  const lb X = (lb)(lds + (qk ? O_QG : O_KG));
+  f32x4 acc{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kc = 0; kc < 4; ++kc)
+    acc = mma(rd_tr(X, LT, 32 * kc, 16 * I, ln), rd_tr((lb)(lds + O_KI), LT, 32 * kc, 16 * J, ln),
+              acc);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int i = 16 * I + 4 * ln.g + r, j = 16 * J + ln.n;
+    acc[r] = (qk ? i >= j : i > j) ? acc[r] : 0.f;
+  }
+  if (qk) {
+    st_t((lb)(lds + O_AQ), LT, 16 * J, 16 * I, acc, ln);
+  } else {
+    LDS float* A = (LDS float*)(lds + O_A);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) A[(16 * I + 4 * ln.g + r) * LA + 16 * J + ln.n] = acc[r];
+  }
+}
+
+// U = T Diag(beta) V (own value columns, registers; -U also to LDS) and
+// W = T Diag(beta) KG (own key channels; -W to LDS).
+__device__ __forceinline__ void tiles_uw(LDS char* lds, f32x4 U[2], bool store_u, const Ln& ln) {
+#pragma unroll
+  for (int I = 0; I < 2; ++I) {
+    const bf16x8 tb = rd_tr((lb)(lds + O_TB), LT, 0, 16 * I, ln);
+    U[I] = mma(tb, rd_row((lb)(lds + O_V), LT, 16 * ln.w, 0, ln), f32x4{0.f, 0.f, 0.f, 0.f});
+    const f32x4 W = mma(tb, rd_row((lb)(lds + O_KG), LT, 16 * ln.w, 0, ln),
+                        f32x4{0.f, 0.f, 0.f, 0.f});
+    st_t((lb)(lds + O_NW), LT, 16 * ln.w, 16 * I, -W, ln);
+    if (store_u) st_t((lb)(lds + O_NU), LT, 16 * ln.w, 16 * I, -U[I], ln);
+  }
+}
+
+// y_t = sum_{i >= t} x_i + sum_{i < t} z_i over the chunk's tokens
+// (accumulator layout), as MFMAs against triangular ones matrices.
+__device__ __forceinline__ void suffix_prefix(const f32x4 x[2], const f32x4 z[2], f32x4 y[2],
+                                              const Ln& ln) {
+  y[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+  y[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const float a = (4 * ln.g + s >= ln.n) ? 1.f : 0.f;
+    const float c = 1.f - a;   // 4g + s < n
+    y[0] = mma4(a, x[0][s], y[0]);
+    y[0] = mma4(1.f, x[1][s], y[0]);
+    y[1] = mma4(a, x[1][s], y[1]);
+    y[0] = mma4(c, z[0][s], y[0]);
+    y[1] = mma4(1.f, z[0][s], y[1]);
+    y[1] = mma4(c, z[1][s], y[1]);
+  }
+}
+
+template <bool SG>
+__global__ __launch_bounds__(NT, 1) void bwd_chunk_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const float* __restrict__ g, const float* __restrict__ beta,
+    const float* __restrict__ S0, const uint16_t* __restrict__ dout,
+    const float* __restrict__ dSf, float* __restrict__ dq, float* __restrict__ dk,
+    float* __restrict__ dv, float* __restrict__ dg, float* __restrict__ dbeta,
+    float* __restrict__ dS0, const int32_t* __restrict__ cu, int T, int H, float scale,
+    uint32_t* __restrict__ states, int* __restrict__ flags) {
+  extern __shared__ __attribute__((aligned(16))) char lds_raw[];
+  LDS char* lds = (LDS char*)lds_raw;
+  Ln ln = fresh();
+  const int h = blockIdx.x % H, sq = blockIdx.x / H;
+  const int nh = sq * H + h;
+  size_t t0;
+  int len;
+  if (cu) {
+    t0 = (size_t)cu[sq];
+    len = cu[sq + 1] - cu[sq];
+  } else {
+    t0 = (size_t)sq * T;
+    len = T;
+  }
+  const int nc = (len + BC - 1) / BC;
+  uint32_t* slot0 = states + ((size_t)sq + t0 / BC) * H * SLOT_DW + (size_t)h * SLOT_DW;
+  auto slot = [&](int m, int cb) {
+    return (u32x2*)(slot0 + (size_t)m * H * SLOT_DW) + (ln.w * 8 + cb) * 64 + ln.l;
+  };
+  LDS float* ER = (LDS float*)(lds + O_ER);
+  LDS float* DL = (LDS float*)(lds + O_DL);
+  LDS float* BETA = (LDS float*)(lds + O_BETA);
+  LDS float* DBP = (LDS float*)(lds + O_DBP);
+  LDS float* RP = (LDS float*)(lds + O_RP);
+  LDS float* GP = (LDS float*)(lds + O_GP);
+  LDS int* FLAG = (LDS int*)(lds + O_FLAG);
+  // upper blocks of the [j][i] 32x32 buffers stay zero
+  for (int e = threadIdx.x; e < 5 * 256; e += NT) {
+    const int b = e >> 8, j = 16 + ((e >> 4) & 15), i = e & 15;
+    ((lb)(lds + O_AQ + b * SZ_S))[j * LT + i] = 0;
+  }
+  if (threadIdx.x == 0) *FLAG = 0;
+  const int col = 16 * ln.w + ln.n;   // the lane's value column / key channel
+  const size_t sbase = (size_t)nh * DD * DD;
+
+  // ------------------------------------------------------------ forward sweep
+  f32x4 S[8];
+#pragma unroll
+  for (int cb = 0; cb < 8; ++cb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      S[cb][r] = S0 ? S0[sbase + (size_t)(16 * cb + 4 * ln.g + r) * DD + col] : 0.f;
+  __syncthreads();
+    ln = fresh();
+  for (int m = 0; m < nc; ++m) {
+    const int L = len - BC * m < BC ? len - BC * m : BC;
+    const size_t tok0 = t0 + (size_t)BC * m;
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb)
+      *slot(m, cb) = u32x2{pack_bf16x2(S[cb][0], S[cb][1]), pack_bf16x2(S[cb][2], S[cb][3])};
+    In x;
+    load_in<SG>(x, q, k, v, dout, g, tok0, L, H, h, false, ln);
+    if (ln.w == 0 && ln.l < BC) BETA[ln.l] = ln.l < L ? beta[(tok0 + ln.l) * H + h] : 0.f;
+    f32x4 bm[2];
+    float er, dl;
+    if (prefix(x, bm, er, dl, ln)) *FLAG = 1;
+    prep_store(lds, x, bm, er, dl, scale, false, ln);
+    __syncthreads();
+    ln = fresh();
+    if (*FLAG) break;
+    tiles_a(lds, false, ln);
+    f32x4 Sm[8];
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb) Sm[cb] = S[cb] * *(const LDS f32x4*)(ER + 16 * cb + 4 * ln.g);
+    __syncthreads();
+    ln = fresh();
+    if (ln.w < 2) solve_diag(lds, ln.w, ln);
+    __syncthreads();
+    ln = fresh();
+    if (ln.w == 0) solve_off(lds, ln);
+    __syncthreads();
+    ln = fresh();
+    f32x4 U[2];
+    tiles_uw(lds, U, false, ln);
+    __syncthreads();
+    ln = fresh();
+    // E = U - W S_m (own value columns); S_{c+1} = Diag(e^{b_L - r}) (S_m + KI^T E)
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+      const bf16x8 sb = pack8(Sm[2 * kc], Sm[2 * kc + 1]);
+#pragma unroll
+      for (int I = 0; I < 2; ++I) U[I] = mma(rd_trp((lb)(lds + O_NW), LT, 32 * kc, 16 * I, ln), sb, U[I]);
+    }
+    const bf16x8 eb = pack8(U[0], U[1]);
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb)
+      S[cb] = mma(rd_rowp((lb)(lds + O_KI), LT, 16 * cb, 0, ln), eb, Sm[cb]) *
+              *(const LDS f32x4*)(DL + 16 * cb + 4 * ln.g);
+    __syncthreads();
+    ln = fresh();
+  }
+  if (*FLAG) {
+    if (threadIdx.x == 0) flags[nh] = 1;
+    return;
+  }
+  if (threadIdx.x == 0) flags[nh] = 0;
+
+  // ------------------------------------------------------------ reverse sweep
+  f32x4 dS[8];
+#pragma unroll
+  for (int cb = 0; cb < 8; ++cb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      dS[cb][r] = dSf ? dSf[sbase + (size_t)(16 * cb + 4 * ln.g + r) * DD + col] : 0.f;
+  // dbeta (and a per-head gate's dlog alpha) of chunk mm from the partials
+  auto finish_rows = [&](int mm) {
+    if (ln.w == 0 && ln.l < BC) {
+      const int L = len - BC * mm < BC ? len - BC * mm : BC;
+      if (ln.l < L) {
+        const size_t row = (t0 + (size_t)BC * mm + ln.l) * H + h;
+        float s = 0.f;
+        for (int p = 0; p < NDBP; ++p) s += DBP[p * BC + ln.l];
+        dbeta[row] = s;
+        if (SG) {
+          float t = 0.f;
+          for (int p = 0; p < NW; ++p) t += GP[p * BC + ln.l];
+          dg[row] = t;
+        }
+      }
+    }
+  };
+  for (int m = nc - 1; m >= 0; --m) {
+    const int L = len - BC * m < BC ? len - BC * m : BC;
+    const size_t tok0 = t0 + (size_t)BC * m;
+    In x;
+    load_in<SG>(x, q, k, v, dout, g, tok0, L, H, h, true, ln);
+    if (ln.w == 0 && ln.l < BC) BETA[ln.l] = ln.l < L ? beta[(tok0 + ln.l) * H + h] : 0.f;
+    u32x2 Sc[8];
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb) Sc[cb] = *slot(m, cb);
+    f32x4 bm[2];
+    float er, dl;
+    prefix(x, bm, er, dl, ln);
+    prep_store(lds, x, bm, er, dl, scale, true, ln);
+    __syncthreads();   // #1
+    ln = fresh();
+    if (m + 1 < nc) finish_rows(m + 1);
+    // dS_m = Diag(e^{b_L - r}) dS;  S_m = Diag(e^r) S_c to R ([value][channel]);
+    // sum_v dS_m S_m over the lane's columns into the partials (the decay of
+    // the incoming state over the chunk, part of every token's dlog alpha)
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb) {
+      dS[cb] *= *(const LDS f32x4*)(DL + 16 * cb + 4 * ln.g);
+      const f32x4 sm = unpack4(Sc[cb]) * *(const LDS f32x4*)(ER + 16 * cb + 4 * ln.g);
+      st_t((lb)(lds + O_R), LR, 16 * ln.w, 16 * cb, sm, ln);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float s = row_sum16(dS[cb][r] * sm[r]);
+        if (ln.n == 0) RP[ln.w * DD + 16 * cb + 4 * ln.g + r] = s;
+      }
+    }
+    tiles_a(lds, true, ln);
+    // dE = KI dS_m (+ Aqk^T dO below), own value columns
+    f32x4 dE[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+      const bf16x8 sb = pack8(dS[2 * kc], dS[2 * kc + 1]);
+#pragma unroll
+      for (int I = 0; I < 2; ++I) dE[I] = mma(rd_trp((lb)(lds + O_KI), LT, 32 * kc, 16 * I, ln), sb, dE[I]);
+    }
+    __syncthreads();   // #2: A, Aqk, R
+    ln = fresh();
+    if (ln.w < 2) solve_diag(lds, ln.w, ln);
+    {
+      const bf16x8 ob = rd_row((lb)(lds + O_DO), LT, 16 * ln.w, 0, ln);
+#pragma unroll
+      for (int I = 0; I < 2; ++I) dE[I] = mma(rd_row((lb)(lds + O_AQ), LT, 16 * I, 0, ln), ob, dE[I]);
+    }
+    __syncthreads();   // #3
+    ln = fresh();
+    if (ln.w == 0) solve_off(lds, ln);
+    __syncthreads();   // #4: T
+    ln = fresh();
+    f32x4 U[2];
+    tiles_uw(lds, U, true, ln);
+    {
+      // dY_v = T^T dE; dV = beta dY_v; dbeta += dY_v . V; dY_v over the own rows of V
+      const bf16x8 eb = pack8(dE[0], dE[1]);
+#pragma unroll
+      for (int I = 0; I < 2; ++I) {
+        const f32x4 y = mma(rd_rowp((lb)(lds + O_TT), LT, 16 * I, 0, ln), eb, f32x4{0.f, 0.f, 0.f, 0.f});
+        const f32x4 vv = unpack4(ld_raw((lb)(lds + O_V), LT, 16 * ln.w, 16 * I, ln));
+        const f32x4 bt = *(const LDS f32x4*)(BETA + 16 * I + 4 * ln.g);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = 16 * I + 4 * ln.g + r;
+          if (i < L) dv[(tok0 + i) * H * DD + (size_t)h * DD + col] = bt[r] * y[r];
+          const float s = row_sum16(y[r] * vv[r]);
+          if (ln.n == 0) DBP[ln.w * BC + i] = s;
+        }
+        st_t((lb)(lds + O_V), LT, 16 * ln.w, 16 * I, y, ln);
+        st_t((lb)(lds + O_NDE), LT, 16 * ln.w, 16 * I, -dE[I], ln);
+      }
+    }
+    __syncthreads();   // #5: -W, -U, -dE
+    ln = fresh();
+    // E = U - W S_m
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+      const bf16x8 sb = rd_row((lb)(lds + O_R), LR, 16 * ln.w, 32 * kc, ln);
+#pragma unroll
+      for (int I = 0; I < 2; ++I) U[I] = mma(rd_tr((lb)(lds + O_NW), LT, 32 * kc, 16 * I, ln), sb, U[I]);
+    }
+#pragma unroll
+    for (int I = 0; I < 2; ++I) st_t((lb)(lds + O_E), LT, 16 * ln.w, 16 * I, U[I], ln);
+    __syncthreads();   // #6: E
+    ln = fresh();
+    // own key channels: dQG = dO S_m^T, dW = -dE S_m^T; waves 0..2: dAqk = tril(dO E^T)
+    f32x4 dQG[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    f32x4 dW[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+      const bf16x8 sb = rd_tr((lb)(lds + O_R), LR, 32 * kc, 16 * ln.w, ln);
+#pragma unroll
+      for (int I = 0; I < 2; ++I) {
+        dQG[I] = mma(rd_tr((lb)(lds + O_DO), LT, 32 * kc, 16 * I, ln), sb, dQG[I]);
+        dW[I] = mma(rd_tr((lb)(lds + O_NDE), LT, 32 * kc, 16 * I, ln), sb, dW[I]);
+      }
+    }
+    if (ln.w < 3) {
+      const int I = tile_I(ln.w), J = tile_J(ln.w);
+      f32x4 acc{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc)
+        acc = mma(rd_tr((lb)(lds + O_DO), LT, 32 * kc, 16 * I, ln),
+                  rd_tr((lb)(lds + O_E), LT, 32 * kc, 16 * J, ln), acc);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[r] = (16 * I + 4 * ln.g + r >= 16 * J + ln.n) ? acc[r] : 0.f;
+      st_t((lb)(lds + O_DAQ), LT, 16 * J, 16 * I, acc, ln);
+    }
+    __syncthreads();   // #7: R, dO and -dE are free; dAqk
+    ln = fresh();
+    // dS_c = Diag(e^r) (dS_m + QG^T dO - W^T dE); dS_m to R for dKI
+    {
+      const bf16x8 ob = __builtin_bit_cast(bf16x8, u32x4{x.o[0][0], x.o[0][1], x.o[1][0], x.o[1][1]});
+      const bf16x8 eb = pack8(dE[0], dE[1]);
+#pragma unroll
+      for (int cb = 0; cb < 8; ++cb) {
+        st_t((lb)(lds + O_R), LR, 16 * ln.w, 16 * cb, dS[cb], ln);
+        dS[cb] = mma(rd_rowp((lb)(lds + O_QG), LT, 16 * cb, 0, ln), ob, dS[cb]);
+        dS[cb] = mma(rd_rowp((lb)(lds + O_NW), LT, 16 * cb, 0, ln), eb, dS[cb]);
+        dS[cb] *= *(const LDS f32x4*)(ER + 16 * cb + 4 * ln.g);
+      }
+    }
+    f32x4 dKG[2], dKI[2], dKIe[2];
+    {
+      // dY_k = T^T dW; dKG = beta dY_k; dbeta += dY_k . KG; dY_k to LDS
+      const bf16x8 wb = pack8(dW[0], dW[1]);
+#pragma unroll
+      for (int I = 0; I < 2; ++I) {
+        const f32x4 y = mma(rd_rowp((lb)(lds + O_TT), LT, 16 * I, 0, ln), wb, f32x4{0.f, 0.f, 0.f, 0.f});
+        const f32x4 bt = *(const LDS f32x4*)(BETA + 16 * I + 4 * ln.g);
+        const f32x4 kg = unpack4(ld_raw((lb)(lds + O_KG), LT, 16 * ln.w, 16 * I, ln));
+        dKG[I] = bt * y;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float s = row_sum16(y[r] * kg[r]);
+          if (ln.n == 0) DBP[(NW + ln.w) * BC + 16 * I + 4 * ln.g + r] = s;
+        }
+        st_t((lb)(lds + O_NDE), LT, 16 * ln.w, 16 * I, y, ln);
+      }
+      // dQG += dAqk KI; dKI = dAqk^T QG (+ E dS_m^T + dA^T KG below)
+      const bf16x8 kib = rd_row((lb)(lds + O_KI), LT, 16 * ln.w, 0, ln);
+      const bf16x8 qgb = rd_row((lb)(lds + O_QG), LT, 16 * ln.w, 0, ln);
+#pragma unroll
+      for (int I = 0; I < 2; ++I) {
+        dQG[I] = mma(rd_tr((lb)(lds + O_DAQ), LT, 0, 16 * I, ln), kib, dQG[I]);
+        dKI[I] = mma(rd_row((lb)(lds + O_DAQ), LT, 16 * I, 0, ln), qgb, f32x4{0.f, 0.f, 0.f, 0.f});
+      }
+    }
+    __syncthreads();   // #8: dY_v, dY_k, dS_m
+    ln = fresh();
+    if (ln.w < 3) {
+      // dL = -(dY_v U^T + dY_k W^T) (strict lower); dbeta += dL . A; dA = Diag(beta) dL
+      const int I = tile_I(ln.w), J = tile_J(ln.w);
+      f32x4 acc{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc) {
+        acc = mma(rd_tr((lb)(lds + O_V), LT, 32 * kc, 16 * I, ln),
+                  rd_tr((lb)(lds + O_NU), LT, 32 * kc, 16 * J, ln), acc);
+        acc = mma(rd_tr((lb)(lds + O_NDE), LT, 32 * kc, 16 * I, ln),
+                  rd_tr((lb)(lds + O_NW), LT, 32 * kc, 16 * J, ln), acc);
+      }
+      const LDS float* A = (const LDS float*)(lds + O_A);
+      const f32x4 bt = *(const LDS f32x4*)(BETA + 16 * I + 4 * ln.g);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * I + 4 * ln.g + r, j = 16 * J + ln.n;
+        acc[r] = i > j ? acc[r] : 0.f;
+        const float s = row_sum16(acc[r] * A[i * LA + j]);
+        if (ln.n == 0) {
+          DBP[(2 * NW + ln.w) * BC + i] = s;
+          DBP[(2 * NW + ln.w) * BC + (i ^ 16)] = 0.f;
+        }
+      }
+      st_t((lb)(lds + O_DA), LT, 16 * J, 16 * I, acc * bt, ln);
+    }
+    // dKIe = E dS_m^T (the K_end part of dKI, kept apart for dlog alpha)
+    dKIe[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+    dKIe[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+      const bf16x8 sb = rd_tr((lb)(lds + O_R), LR, 32 * kc, 16 * ln.w, ln);
+#pragma unroll
+      for (int I = 0; I < 2; ++I) dKIe[I] = mma(rd_tr((lb)(lds + O_E), LT, 32 * kc, 16 * I, ln), sb, dKIe[I]);
+    }
+    __syncthreads();   // #9: dA
+    ln = fresh();
+    {
+      const bf16x8 kib = rd_row((lb)(lds + O_KI), LT, 16 * ln.w, 0, ln);
+      const bf16x8 kgb = rd_row((lb)(lds + O_KG), LT, 16 * ln.w, 0, ln);
+#pragma unroll
+      for (int I = 0; I < 2; ++I) {
+        dKG[I] = mma(rd_tr((lb)(lds + O_DA), LT, 0, 16 * I, ln), kib, dKG[I]);
+        dKI[I] = mma(rd_row((lb)(lds + O_DA), LT, 16 * I, 0, ln), kgb, dKI[I]);
+      }
+    }
+    // epilogue: dq, dk and dlog alpha per element.  The in-chunk pair terms
+    // of dlog alpha enter token i (+) and token j (-) of every pair j < i, and
+    // the suffix sums cancel those with both tokens at or after t; both sides
+    // are formed from the same bf16 factors the products used, so that they
+    // cancel to fp32 rounding.  The K_end terms (E dS_m^T) enter as the sum
+    // over the tokens before t directly, and the incoming state's decay
+    // (sum_v dS_m S_m) enters every token.
+    {
+      f32x4 db[2], de[2];
+      float rs = 0.f;
+      for (int p = 0; p < NW; ++p) rs += RP[p * DD + col];
+#pragma unroll
+      for (int I = 0; I < 2; ++I) {
+        const f32x4 qg = unpack4(ld_raw((lb)(lds + O_QG), LT, 16 * ln.w, 16 * I, ln));
+        const f32x4 kg = unpack4(ld_raw((lb)(lds + O_KG), LT, 16 * ln.w, 16 * I, ln));
+        const f32x4 ki = unpack4(ld_raw((lb)(lds + O_KI), LT, 16 * ln.w, 16 * I, ln));
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float p = __expf(bm[I][r]), pi = __expf(-bm[I][r]);
+          db[I][r] = qg[r] * dQG[I][r] + kg[r] * dKG[I][r] - ki[r] * dKI[I][r];
+          de[I][r] = ki[r] * dKIe[I][r];
+          dQG[I][r] = scale * p * dQG[I][r];
+          dKG[I][r] = p * dKG[I][r] + pi * (dKI[I][r] + dKIe[I][r]);
+        }
+      }
+      f32x4 dgc[2];
+      suffix_prefix(db, de, dgc, ln);
+      dgc[0] += rs;
+      dgc[1] += rs;
+#pragma unroll
+      for (int I = 0; I < 2; ++I)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = 16 * I + 4 * ln.g + r;
+          const size_t row = (tok0 + i) * H + h;
+          if (i < L) {
+            dq[row * DD + col] = dQG[I][r];
+            dk[row * DD + col] = dKG[I][r];
+            if (!SG) dg[row * DD + col] = dgc[I][r];
+          }
+          if (SG) {
+            const float s = row_sum16(dgc[I][r]);
+            if (ln.n == 0) GP[ln.w * BC + i] = s;
+          }
+        }
+    }
+    __syncthreads();   // #10: the chunk's LDS may be rewritten
+    ln = fresh();
+  }
+  if (nc > 0) finish_rows(0);
+  if (dS0) {
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dS0[sbase + (size_t)(16 * cb + 4 * ln.g + r) * DD + col] = dS[cb][r];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_backward_chunk(const void* q, const void* k, const void* v, const float* g,
+                                 const float* beta, const float* S0, const void* dout,
+                                 const float* dSf, float* dq, float* dk, float* dv, float* dg,
+                                 float* dbeta, float* dS0, const int32_t* cu, int n_seq, int T,
+                                 int H, float scale, bool scalar_gate, void* states, int* flags,
+                                 hipStream_t stream) {
+  auto kern = scalar_gate ? bwd_chunk_kernel<true> : bwd_chunk_kernel<false>;
+  hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3(n_seq * H), dim3(NT), LDS_BYTES, stream,
+                     (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, g, beta, S0,
+                     (const uint16_t*)dout, dSf, dq, dk, dv, dg, dbeta, dS0, cu, T, H, scale,
+                     (uint32_t*)states, flags);
+  return hipGetLastError();
+}
+
+}  // namespace kda

@@ -266,11 +266,12 @@ def test_backward_workspace_and_validation(lib):
     """Sizes and error paths of kda_backward; every call here returns before
     any launch (fake pointers are never dereferenced)."""
     ws = lib.kda_backward_workspace_size
-    # one checkpoint slot (d_k x d_v fp32) per head for every 8 tokens, plus one per
-    # sequence, then d_v fp32 per head-token
-    assert ws(8, 8192, 32, 128, 128, 0) == ((8 + 8 * 8192 // 8) * 32 * 128 * 128
-                                            + 8 * 8192 * 32 * 128) * 4
-    assert ws(3, 10, 2, 64, 64, 1) == ((3 + 10 // 8) * 2 * 64 * 64 + 10 * 2 * 64) * 4
+    # one int per chain (256-byte aligned), then one checkpoint slot (d_k x d_v
+    # fp32) per head for every 8 tokens, plus one per sequence, then d_v fp32 per
+    # head-token
+    assert ws(8, 8192, 32, 128, 128, 0) == 1024 + ((8 + 8 * 8192 // 8) * 32 * 128 * 128
+                                                   + 8 * 8192 * 32 * 128) * 4
+    assert ws(3, 10, 2, 64, 64, 1) == 256 + ((3 + 10 // 8) * 2 * 64 * 64 + 10 * 2 * 64) * 4
     assert ws(1, 4, 2, 96, 64, 0) == 0
     need = ws(2, 4, 2, 64, 64, 0)
     f = lib.kda_backward
