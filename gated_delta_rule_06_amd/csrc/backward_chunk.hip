@@ -65,9 +65,10 @@ constexpr int NW = 8;           // waves
 constexpr int NT = 64 * NW;     // threads
 constexpr int LT = BC + 8;      // row length (bf16) of [channel][token] buffers: 80 bytes
 constexpr int LR = DD + 8;      // row length (bf16) of the [value][channel] state buffer
-constexpr int LA = BC + 1;      // row length (fp32) of A and T
+constexpr int LA = BC + 4;      // row length (fp32) of A and T (16-byte rows)
 constexpr float RANGE = 76.f;   // bound on |b_i - r| for the stored factors
-constexpr int SLOT_DW = DD * DD / 2;   // dwords of one bf16 state in the workspace
+constexpr int ST_DW = DD * DD / 2;     // dwords of one bf16 state
+constexpr int SLOT_DW = ST_DW + 2 * BC * BC / 2;   // a chunk's workspace slot: S_c, T^T, (T Diag(beta))^T
 
 // LDS layout (bytes)
 constexpr int SZ_T = DD * LT * 2;      // [128][40] bf16
@@ -190,25 +191,44 @@ struct In {
   float gt[2][4];
 };
 
+// Buffer views: a workgroup-uniform base and byte limit, a 32-bit lane offset
+// and a uniform offset per access; reads at or past the limit return zero and
+// writes there are dropped.  A chunk's view of a [rows, H, width] tensor starts
+// at its first row of head h and ends after its last valid row, so the
+// padding rows of a partial chunk need no test.
+constexpr int BUF_FLAGS = 0x00020000;
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+__device__ __forceinline__ Rsrc chunk_view(const void* p, size_t tok0, int L, int H, int h,
+                                           int width, int esz) {
+  const char* base = (const char*)p + (tok0 * H + h) * (size_t)width * esz;
+  const int bytes = L > 0 ? (int)(((size_t)(L - 1) * H * width + width) * esz) : 0;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, bytes, BUF_FLAGS);
+}
+__device__ __forceinline__ void st_f32(Rsrc r, uint32_t off, uint32_t soff, float x) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, off, soff, 0);
+}
+
 template <bool SG>
 __device__ __forceinline__ void load_in(In& x, const uint16_t* q, const uint16_t* k,
                                         const uint16_t* v, const uint16_t* dout, const float* g,
                                         size_t tok0, int L, int H, int h, bool rev, const Ln& ln) {
-  const int c = 16 * ln.w + ln.n;
+  const Rsrc rq = chunk_view(q, tok0, L, H, h, DD, 2), rk = chunk_view(k, tok0, L, H, h, DD, 2);
+  const Rsrc rv = chunk_view(v, tok0, L, H, h, DD, 2), ro = chunk_view(dout, tok0, L, H, h, DD, 2);
+  const Rsrc rg = chunk_view(g, tok0, L, H, h, SG ? 1 : DD, 4);
+  const uint32_t lo = (uint32_t)(4 * ln.g * H * DD + 16 * ln.w + ln.n);   // the lane's token 4g
+  const uint32_t lg = SG ? (uint32_t)(4 * ln.g * H) : lo;
 #pragma unroll
   for (int I = 0; I < 2; ++I) {
     uint32_t wq[4], wk[4], wv[4], wo[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int i = 16 * I + 4 * ln.g + r;
-      const bool ok = i < L;
-      const size_t row = (tok0 + i) * H + h;
-      const size_t e = row * DD + c;
-      wq[r] = (ok && rev) ? q[e] : 0u;
-      wk[r] = ok ? k[e] : 0u;
-      wv[r] = ok ? v[e] : 0u;
-      wo[r] = (ok && rev) ? dout[e] : 0u;
-      x.gt[I][r] = ok ? (SG ? g[row] : g[e]) : 0.f;
+      const uint32_t so = (uint32_t)((16 * I + r) * H * DD);
+      const uint32_t sg = SG ? (uint32_t)((16 * I + r) * H) : so;
+      wq[r] = rev ? __builtin_amdgcn_raw_buffer_load_b16(rq, 2 * lo, 2 * so, 0) : 0u;
+      wk[r] = __builtin_amdgcn_raw_buffer_load_b16(rk, 2 * lo, 2 * so, 0);
+      wv[r] = __builtin_amdgcn_raw_buffer_load_b16(rv, 2 * lo, 2 * so, 0);
+      wo[r] = rev ? __builtin_amdgcn_raw_buffer_load_b16(ro, 2 * lo, 2 * so, 0) : 0u;
+      x.gt[I][r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rg, 4 * lg, 4 * sg, 0));
     }
     x.q[I] = u32x2{wq[0] | (wq[1] << 16), wq[2] | (wq[3] << 16)};
     x.k[I] = u32x2{wk[0] | (wk[1] << 16), wk[2] | (wk[3] << 16)};
@@ -244,58 +264,65 @@ __device__ __forceinline__ bool prefix(const In& x, f32x4 bm[2], float& er, floa
   return bad;
 }
 
-// Forward substitution for the diagonal block bb of T = (I + Diag(beta) A)^{-1};
-// lane (n, g) forms column n, rows 4g + r.  Writes T (fp32), T^T and
-// (T Diag(beta))^T (bf16).
-__device__ __forceinline__ void solve_diag(LDS char* lds, int bb, const Ln& ln) {
+// T = (I + Diag(beta) A)^{-1} in fp32 by one wave, A strictly lower in LDS.
+// Lanes with g even take column n of T_00, lanes with g odd column n of T_11,
+// each with the whole column in registers (forward substitution with no lane
+// exchange; the second copy of every column costs nothing).  Then T_10 =
+// -T_11 X, X = Diag(beta_1) A_10 T_00: X by the T_00 lanes (eight rows each)
+// into the unused upper-right block of the fp32 buffer, T_10 by every lane
+// (rows 4g .. 4g+3 of column n); the exchange stays inside the wave.  Writes
+// T^T and (T Diag(beta))^T as bf16.
+__device__ __forceinline__ void solve_full(LDS char* lds, const Ln& ln) {
   const LDS float* A = (const LDS float*)(lds + O_A);
   LDS float* Tf = (LDS float*)(lds + O_T);
   const LDS float* beta = (const LDS float*)(lds + O_BETA);
-  const int off = 16 * bb;
-  float x[4], bet[4];
+  const int b = ln.g & 1, off = 16 * b, j = ln.n;
+  float x[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) x[i] = (i == j) ? 1.f : 0.f;
+#pragma unroll
+  for (int i = 1; i < 16; ++i) {
+    const LDS float* Ai = A + (off + i) * LA + off;
+    float acc = 0.f;
+#pragma unroll
+    for (int m = 0; m < i; ++m) acc += Ai[m] * x[m];
+    x[i] -= beta[off + i] * acc;
+  }
+  if (ln.g < 2) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) Tf[(off + i) * LA + off + j] = x[i];
+    const float bj = beta[off + j];
+    LDS uint16_t* tt = (lb)(lds + O_TT) + (off + j) * LT + off;
+    LDS uint16_t* tb = (lb)(lds + O_TB) + (off + j) * LT + off;
+#pragma unroll
+    for (int e = 0; e < 16; e += 4) {
+      *(LDS u32x2*)(tt + e) = u32x2{pack_bf16x2(x[e], x[e + 1]), pack_bf16x2(x[e + 2], x[e + 3])};
+      *(LDS u32x2*)(tb + e) = u32x2{pack_bf16x2(bj * x[e], bj * x[e + 1]),
+                                    pack_bf16x2(bj * x[e + 2], bj * x[e + 3])};
+    }
+  }
+  if (b == 0) {
+    const int i0 = 4 * ln.g;   // rows 0..7 (g = 0) or 8..15 (g = 2) of X
+#pragma unroll
+    for (int ii = 0; ii < 8; ++ii) {
+      const LDS float* Ai = A + (16 + i0 + ii) * LA;
+      float acc = 0.f;
+#pragma unroll
+      for (int m = 0; m < 16; ++m) acc += Ai[m] * x[m];
+      Tf[(i0 + ii) * LA + 16 + j] = beta[16 + i0 + ii] * acc;
+    }
+  }
+  f32x4 t;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    x[r] = (4 * ln.g + r == ln.n) ? 1.f : 0.f;
-    bet[r] = beta[off + 4 * ln.g + r];
+    const LDS float* Ti = Tf + (16 + 4 * ln.g + r) * LA + 16;
+    float acc = 0.f;
+#pragma unroll
+    for (int m = 0; m < 16; ++m) acc += Ti[m] * Tf[m * LA + 16 + j];
+    t[r] = -acc;
   }
-#pragma unroll
-  for (int m = 0; m < 15; ++m) {
-    const float xm = shfl(x[m & 3], ln.n + 16 * (m >> 2));
-#pragma unroll
-    for (int r = 0; r < 4; ++r)   // A is zero on and above the diagonal
-      x[r] -= bet[r] * A[(off + 4 * ln.g + r) * LA + off + m] * xm;
-  }
-#pragma unroll
-  for (int r = 0; r < 4; ++r) Tf[(off + 4 * ln.g + r) * LA + off + ln.n] = x[r];
-  const f32x4 t{x[0], x[1], x[2], x[3]};
-  st_t((lb)(lds + O_TT), LT, off, off, t, ln);
-  st_t((lb)(lds + O_TB), LT, off, off, t * beta[off + ln.n], ln);
-}
-
-// T_10 = -T_11 (Diag(beta_1) A_10) T_00 (one wave).
-__device__ __forceinline__ void solve_off(LDS char* lds, const Ln& ln) {
-  const LDS float* A = (const LDS float*)(lds + O_A);
-  const LDS float* Tf = (const LDS float*)(lds + O_T);
-  const LDS float* beta = (const LDS float*)(lds + O_BETA);
-  float X[4] = {0.f, 0.f, 0.f, 0.f}, bet[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) bet[r] = beta[16 + 4 * ln.g + r];
-#pragma unroll
-  for (int m = 0; m < 16; ++m) {
-    const float t = Tf[m * LA + ln.n];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) X[r] += bet[r] * A[(16 + 4 * ln.g + r) * LA + m] * t;
-  }
-  float Y[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int m = 0; m < 16; ++m) {
-    const float xm = shfl(X[m & 3], ln.n + 16 * (m >> 2));
-#pragma unroll
-    for (int r = 0; r < 4; ++r) Y[r] -= Tf[(16 + 4 * ln.g + r) * LA + 16 + m] * xm;
-  }
-  const f32x4 t{Y[0], Y[1], Y[2], Y[3]};
   st_t((lb)(lds + O_TT), LT, 0, 16, t, ln);
-  st_t((lb)(lds + O_TB), LT, 0, 16, t * beta[ln.n], ln);
+  st_t((lb)(lds + O_TB), LT, 0, 16, t * beta[j], ln);
 }
 
 // Lower-triangle 16x16 tiles of a 32x32 matrix: (0,0), (1,0), (1,1).
@@ -329,12 +356,9 @@ __device__ __forceinline__ void prep_store(LDS char* lds, const In& x, const f32
   }
 }
 
-// A = strict_tril(KG KI^T) (fp32) and, reverse sweep, Aqk = tril(QG KI^T)
-// (bf16, transposed): six tiles on waves 0..5.
-__device__ __forceinline__ void tiles_a(LDS char* lds, bool rev, const Ln& ln) {
-  if (ln.w >= (rev ? 6 : 3)) return;
-  const bool qk = ln.w >= 3;
-  const int t = qk ? ln.w - 3 : ln.w;
+// Tile t (0..2) of A = strict_tril(KG KI^T) (fp32) or, qk, of Aqk =
+// tril(QG KI^T) (bf16, transposed).
+__device__ __forceinline__ void tile_a(LDS char* lds, bool qk, int t, const Ln& ln) {
   const int I = tile_I(t), J = tile_J(t);
   const lb X = (lb)(lds + (qk ? O_QG : O_KG));
   f32x4 acc{0.f, 0.f, 0.f, 0.f};
@@ -354,6 +378,13 @@ __device__ __forceinline__ void tiles_a(LDS char* lds, bool rev, const Ln& ln) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) A[(16 * I + 4 * ln.g + r) * LA + 16 * J + ln.n] = acc[r];
   }
+}
+
+// Copies T^T and (T Diag(beta))^T between LDS and a workspace slot: thread
+// t moves four elements of row (t / 8) % 32 of buffer t / 256.
+__device__ __forceinline__ LDS u32x2* t_part(LDS char* lds) {
+  const int t = threadIdx.x;
+  return (LDS u32x2*)((lb)(lds + O_TT + (t >> 8) * SZ_S) + ((t >> 3) & 31) * LT + 4 * (t & 7));
 }
 
 // U = T Diag(beta) V (own value columns, registers; -U also to LDS) and
@@ -413,9 +444,13 @@ __global__ __launch_bounds__(NT, 1) void bwd_chunk_kernel(
     len = T;
   }
   const int nc = (len + BC - 1) / BC;
+  // chunk m's workspace slot: S_c in the lanes' own order, then T^T and (T Diag(beta))^T
   uint32_t* slot0 = states + ((size_t)sq + t0 / BC) * H * SLOT_DW + (size_t)h * SLOT_DW;
   auto slot = [&](int m, int cb) {
     return (u32x2*)(slot0 + (size_t)m * H * SLOT_DW) + (ln.w * 8 + cb) * 64 + ln.l;
+  };
+  auto tslot = [&](int m) {
+    return (u32x2*)(slot0 + (size_t)m * H * SLOT_DW + ST_DW) + threadIdx.x;
   };
   LDS float* ER = (LDS float*)(lds + O_ER);
   LDS float* DL = (LDS float*)(lds + O_DL);
@@ -441,38 +476,48 @@ __global__ __launch_bounds__(NT, 1) void bwd_chunk_kernel(
     for (int r = 0; r < 4; ++r)
       S[cb][r] = S0 ? S0[sbase + (size_t)(16 * cb + 4 * ln.g + r) * DD + col] : 0.f;
   __syncthreads();
-    ln = fresh();
+  ln = fresh();
+  // the next chunk's inputs (and, reverse sweep, its stored state and T) load
+  // while this one is computed
+  auto clen = [&](int mm) { return len - BC * mm < BC ? len - BC * mm : BC; };
+  In xn;
+  float bn = 0.f;
+  auto fetch = [&](int mm, bool rev) {
+    const int L = clen(mm);
+    const size_t tok0 = t0 + (size_t)BC * mm;
+    load_in<SG>(xn, q, k, v, dout, g, tok0, L, H, h, rev, ln);
+    bn = (ln.w == 0 && ln.l < L) ? beta[(tok0 + ln.l) * H + h] : 0.f;
+  };
+  if (nc > 0) fetch(0, false);
   for (int m = 0; m < nc; ++m) {
-    const int L = len - BC * m < BC ? len - BC * m : BC;
-    const size_t tok0 = t0 + (size_t)BC * m;
 #pragma unroll
     for (int cb = 0; cb < 8; ++cb)
       *slot(m, cb) = u32x2{pack_bf16x2(S[cb][0], S[cb][1]), pack_bf16x2(S[cb][2], S[cb][3])};
-    In x;
-    load_in<SG>(x, q, k, v, dout, g, tok0, L, H, h, false, ln);
-    if (ln.w == 0 && ln.l < BC) BETA[ln.l] = ln.l < L ? beta[(tok0 + ln.l) * H + h] : 0.f;
+    const In x = xn;
+    if (ln.w == 0 && ln.l < BC) BETA[ln.l] = bn;
     f32x4 bm[2];
     float er, dl;
     if (prefix(x, bm, er, dl, ln)) *FLAG = 1;
     prep_store(lds, x, bm, er, dl, scale, false, ln);
-    __syncthreads();
+    __syncthreads();   // #1
     ln = fresh();
     if (*FLAG) break;
-    tiles_a(lds, false, ln);
+    if (m + 1 < nc) fetch(m + 1, false);
+    if (ln.w == NW - 1) {
+      // A (all three tiles) and T on the last wave
+#pragma unroll
+      for (int t = 0; t < 3; ++t) tile_a(lds, false, t, ln);
+      solve_full(lds, ln);
+    }
     f32x4 Sm[8];
 #pragma unroll
     for (int cb = 0; cb < 8; ++cb) Sm[cb] = S[cb] * *(const LDS f32x4*)(ER + 16 * cb + 4 * ln.g);
-    __syncthreads();
+    __syncthreads();   // #2: T
     ln = fresh();
-    if (ln.w < 2) solve_diag(lds, ln.w, ln);
-    __syncthreads();
-    ln = fresh();
-    if (ln.w == 0) solve_off(lds, ln);
-    __syncthreads();
-    ln = fresh();
+    *tslot(m) = *t_part(lds);
     f32x4 U[2];
     tiles_uw(lds, U, false, ln);
-    __syncthreads();
+    __syncthreads();   // #3: -W
     ln = fresh();
     // E = U - W S_m (own value columns); S_{c+1} = Diag(e^{b_L - r}) (S_m + KI^T E)
 #pragma unroll
@@ -486,7 +531,7 @@ __global__ __launch_bounds__(NT, 1) void bwd_chunk_kernel(
     for (int cb = 0; cb < 8; ++cb)
       S[cb] = mma(rd_rowp((lb)(lds + O_KI), LT, 16 * cb, 0, ln), eb, Sm[cb]) *
               *(const LDS f32x4*)(DL + 16 * cb + 4 * ln.g);
-    __syncthreads();
+    __syncthreads();   // #4: the chunk's LDS may be rewritten
     ln = fresh();
   }
   if (*FLAG) {
@@ -505,7 +550,7 @@ __global__ __launch_bounds__(NT, 1) void bwd_chunk_kernel(
   // dbeta (and a per-head gate's dlog alpha) of chunk mm from the partials
   auto finish_rows = [&](int mm) {
     if (ln.w == 0 && ln.l < BC) {
-      const int L = len - BC * mm < BC ? len - BC * mm : BC;
+      const int L = clen(mm);
       if (ln.l < L) {
         const size_t row = (t0 + (size_t)BC * mm + ln.l) * H + h;
         float s = 0.f;
@@ -519,21 +564,30 @@ __global__ __launch_bounds__(NT, 1) void bwd_chunk_kernel(
       }
     }
   };
+  u32x2 Scn[8], Tn;
+  auto fetch2 = [&](int mm) {
+    fetch(mm, true);
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb) Scn[cb] = *slot(mm, cb);
+    Tn = *tslot(mm);
+  };
+  if (nc > 0) fetch2(nc - 1);
   for (int m = nc - 1; m >= 0; --m) {
-    const int L = len - BC * m < BC ? len - BC * m : BC;
+    const int L = clen(m);
     const size_t tok0 = t0 + (size_t)BC * m;
-    In x;
-    load_in<SG>(x, q, k, v, dout, g, tok0, L, H, h, true, ln);
-    if (ln.w == 0 && ln.l < BC) BETA[ln.l] = ln.l < L ? beta[(tok0 + ln.l) * H + h] : 0.f;
+    const In x = xn;
+    if (ln.w == 0 && ln.l < BC) BETA[ln.l] = bn;
     u32x2 Sc[8];
 #pragma unroll
-    for (int cb = 0; cb < 8; ++cb) Sc[cb] = *slot(m, cb);
+    for (int cb = 0; cb < 8; ++cb) Sc[cb] = Scn[cb];
+    *t_part(lds) = Tn;
     f32x4 bm[2];
     float er, dl;
     prefix(x, bm, er, dl, ln);
     prep_store(lds, x, bm, er, dl, scale, true, ln);
-    __syncthreads();   // #1
+    __syncthreads();   // #1: the chunk's operands, T
     ln = fresh();
+    if (m > 0) fetch2(m - 1);
     if (m + 1 < nc) finish_rows(m + 1);
     // dS_m = Diag(e^{b_L - r}) dS;  S_m = Diag(e^r) S_c to R ([value][channel]);
     // sum_v dS_m S_m over the lane's columns into the partials (the decay of
@@ -549,7 +603,7 @@ __global__ __launch_bounds__(NT, 1) void bwd_chunk_kernel(
         if (ln.n == 0) RP[ln.w * DD + 16 * cb + 4 * ln.g + r] = s;
       }
     }
-    tiles_a(lds, true, ln);
+    if (ln.w < 6) tile_a(lds, ln.w >= 3, ln.w % 3, ln);
     // dE = KI dS_m (+ Aqk^T dO below), own value columns
     f32x4 dE[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
@@ -558,24 +612,20 @@ __global__ __launch_bounds__(NT, 1) void bwd_chunk_kernel(
 #pragma unroll
       for (int I = 0; I < 2; ++I) dE[I] = mma(rd_trp((lb)(lds + O_KI), LT, 32 * kc, 16 * I, ln), sb, dE[I]);
     }
-    __syncthreads();   // #2: A, Aqk, R
+    f32x4 U[2];
+    tiles_uw(lds, U, true, ln);
+    __syncthreads();   // #2: A, Aqk, S_m, -W, -U
     ln = fresh();
-    if (ln.w < 2) solve_diag(lds, ln.w, ln);
     {
       const bf16x8 ob = rd_row((lb)(lds + O_DO), LT, 16 * ln.w, 0, ln);
 #pragma unroll
       for (int I = 0; I < 2; ++I) dE[I] = mma(rd_row((lb)(lds + O_AQ), LT, 16 * I, 0, ln), ob, dE[I]);
     }
-    __syncthreads();   // #3
-    ln = fresh();
-    if (ln.w == 0) solve_off(lds, ln);
-    __syncthreads();   // #4: T
-    ln = fresh();
-    f32x4 U[2];
-    tiles_uw(lds, U, true, ln);
     {
-      // dY_v = T^T dE; dV = beta dY_v; dbeta += dY_v . V; dY_v over the own rows of V
+      // dY_v = T^T dE; dV = beta dY_v; dbeta += dY_v . V; dY_v over the own rows of V; -dE
       const bf16x8 eb = pack8(dE[0], dE[1]);
+      const Rsrc rdv = chunk_view(dv, tok0, L, H, h, DD, 4);
+      const uint32_t lo = (uint32_t)(4 * ln.g * H * DD + col);
 #pragma unroll
       for (int I = 0; I < 2; ++I) {
         const f32x4 y = mma(rd_rowp((lb)(lds + O_TT), LT, 16 * I, 0, ln), eb, f32x4{0.f, 0.f, 0.f, 0.f});
@@ -583,18 +633,15 @@ __global__ __launch_bounds__(NT, 1) void bwd_chunk_kernel(
         const f32x4 bt = *(const LDS f32x4*)(BETA + 16 * I + 4 * ln.g);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int i = 16 * I + 4 * ln.g + r;
-          if (i < L) dv[(tok0 + i) * H * DD + (size_t)h * DD + col] = bt[r] * y[r];
+          st_f32(rdv, 4 * lo, 4 * (uint32_t)((16 * I + r) * H * DD), bt[r] * y[r]);
           const float s = row_sum16(y[r] * vv[r]);
-          if (ln.n == 0) DBP[ln.w * BC + i] = s;
+          if (ln.n == 0) DBP[ln.w * BC + 16 * I + 4 * ln.g + r] = s;
         }
         st_t((lb)(lds + O_V), LT, 16 * ln.w, 16 * I, y, ln);
         st_t((lb)(lds + O_NDE), LT, 16 * ln.w, 16 * I, -dE[I], ln);
       }
     }
-    __syncthreads();   // #5: -W, -U, -dE
-    ln = fresh();
-    // E = U - W S_m
+    // E = U - W S_m -> LDS
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
       const bf16x8 sb = rd_row((lb)(lds + O_R), LR, 16 * ln.w, 32 * kc, ln);
@@ -603,21 +650,42 @@ __global__ __launch_bounds__(NT, 1) void bwd_chunk_kernel(
     }
 #pragma unroll
     for (int I = 0; I < 2; ++I) st_t((lb)(lds + O_E), LT, 16 * ln.w, 16 * I, U[I], ln);
-    __syncthreads();   // #6: E
-    ln = fresh();
-    // own key channels: dQG = dO S_m^T, dW = -dE S_m^T; waves 0..2: dAqk = tril(dO E^T)
+    // own key channels: dQG = dO S_m^T
     f32x4 dQG[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-    f32x4 dW[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
       const bf16x8 sb = rd_tr((lb)(lds + O_R), LR, 32 * kc, 16 * ln.w, ln);
 #pragma unroll
+      for (int I = 0; I < 2; ++I) dQG[I] = mma(rd_tr((lb)(lds + O_DO), LT, 32 * kc, 16 * I, ln), sb, dQG[I]);
+    }
+    __syncthreads();   // #3: -dE, E
+    ln = fresh();
+    // own key channels: dW = -dE S_m^T, dY_k = T^T dW, dKG = beta dY_k, dbeta += dY_k . KG
+    f32x4 dKG[2], dYk[2];
+    {
+      f32x4 dW[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc) {
+        const bf16x8 sb = rd_tr((lb)(lds + O_R), LR, 32 * kc, 16 * ln.w, ln);
+#pragma unroll
+        for (int I = 0; I < 2; ++I) dW[I] = mma(rd_tr((lb)(lds + O_NDE), LT, 32 * kc, 16 * I, ln), sb, dW[I]);
+      }
+      const bf16x8 wb = pack8(dW[0], dW[1]);
+#pragma unroll
       for (int I = 0; I < 2; ++I) {
-        dQG[I] = mma(rd_tr((lb)(lds + O_DO), LT, 32 * kc, 16 * I, ln), sb, dQG[I]);
-        dW[I] = mma(rd_tr((lb)(lds + O_NDE), LT, 32 * kc, 16 * I, ln), sb, dW[I]);
+        dYk[I] = mma(rd_rowp((lb)(lds + O_TT), LT, 16 * I, 0, ln), wb, f32x4{0.f, 0.f, 0.f, 0.f});
+        const f32x4 bt = *(const LDS f32x4*)(BETA + 16 * I + 4 * ln.g);
+        const f32x4 kg = unpack4(ld_raw((lb)(lds + O_KG), LT, 16 * ln.w, 16 * I, ln));
+        dKG[I] = bt * dYk[I];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float s = row_sum16(dYk[I][r] * kg[r]);
+          if (ln.n == 0) DBP[(NW + ln.w) * BC + 16 * I + 4 * ln.g + r] = s;
+        }
       }
     }
     if (ln.w < 3) {
+      // dAqk = tril(dO E^T)
       const int I = tile_I(ln.w), J = tile_J(ln.w);
       f32x4 acc{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -628,8 +696,10 @@ __global__ __launch_bounds__(NT, 1) void bwd_chunk_kernel(
       for (int r = 0; r < 4; ++r) acc[r] = (16 * I + 4 * ln.g + r >= 16 * J + ln.n) ? acc[r] : 0.f;
       st_t((lb)(lds + O_DAQ), LT, 16 * J, 16 * I, acc, ln);
     }
-    __syncthreads();   // #7: R, dO and -dE are free; dAqk
+    __syncthreads();   // #4: S_m, -dE and dO are done with; dAqk
     ln = fresh();
+#pragma unroll
+    for (int I = 0; I < 2; ++I) st_t((lb)(lds + O_NDE), LT, 16 * ln.w, 16 * I, dYk[I], ln);
     // dS_c = Diag(e^r) (dS_m + QG^T dO - W^T dE); dS_m to R for dKI
     {
       const bf16x8 ob = __builtin_bit_cast(bf16x8, u32x4{x.o[0][0], x.o[0][1], x.o[1][0], x.o[1][1]});
@@ -642,24 +712,9 @@ __global__ __launch_bounds__(NT, 1) void bwd_chunk_kernel(
         dS[cb] *= *(const LDS f32x4*)(ER + 16 * cb + 4 * ln.g);
       }
     }
-    f32x4 dKG[2], dKI[2], dKIe[2];
+    // dQG += dAqk KI; dKI = dAqk^T QG (+ dA^T KG below)
+    f32x4 dKI[2];
     {
-      // dY_k = T^T dW; dKG = beta dY_k; dbeta += dY_k . KG; dY_k to LDS
-      const bf16x8 wb = pack8(dW[0], dW[1]);
-#pragma unroll
-      for (int I = 0; I < 2; ++I) {
-        const f32x4 y = mma(rd_rowp((lb)(lds + O_TT), LT, 16 * I, 0, ln), wb, f32x4{0.f, 0.f, 0.f, 0.f});
-        const f32x4 bt = *(const LDS f32x4*)(BETA + 16 * I + 4 * ln.g);
-        const f32x4 kg = unpack4(ld_raw((lb)(lds + O_KG), LT, 16 * ln.w, 16 * I, ln));
-        dKG[I] = bt * y;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float s = row_sum16(y[r] * kg[r]);
-          if (ln.n == 0) DBP[(NW + ln.w) * BC + 16 * I + 4 * ln.g + r] = s;
-        }
-        st_t((lb)(lds + O_NDE), LT, 16 * ln.w, 16 * I, y, ln);
-      }
-      // dQG += dAqk KI; dKI = dAqk^T QG (+ E dS_m^T + dA^T KG below)
       const bf16x8 kib = rd_row((lb)(lds + O_KI), LT, 16 * ln.w, 0, ln);
       const bf16x8 qgb = rd_row((lb)(lds + O_QG), LT, 16 * ln.w, 0, ln);
 #pragma unroll
@@ -668,7 +723,7 @@ __global__ __launch_bounds__(NT, 1) void bwd_chunk_kernel(
         dKI[I] = mma(rd_row((lb)(lds + O_DAQ), LT, 16 * I, 0, ln), qgb, f32x4{0.f, 0.f, 0.f, 0.f});
       }
     }
-    __syncthreads();   // #8: dY_v, dY_k, dS_m
+    __syncthreads();   // #5: dY_k, dS_m
     ln = fresh();
     if (ln.w < 3) {
       // dL = -(dY_v U^T + dY_k W^T) (strict lower); dbeta += dL . A; dA = Diag(beta) dL
@@ -696,15 +751,14 @@ __global__ __launch_bounds__(NT, 1) void bwd_chunk_kernel(
       st_t((lb)(lds + O_DA), LT, 16 * J, 16 * I, acc * bt, ln);
     }
     // dKIe = E dS_m^T (the K_end part of dKI, kept apart for dlog alpha)
-    dKIe[0] = f32x4{0.f, 0.f, 0.f, 0.f};
-    dKIe[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 dKIe[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
       const bf16x8 sb = rd_tr((lb)(lds + O_R), LR, 32 * kc, 16 * ln.w, ln);
 #pragma unroll
       for (int I = 0; I < 2; ++I) dKIe[I] = mma(rd_tr((lb)(lds + O_E), LT, 32 * kc, 16 * I, ln), sb, dKIe[I]);
     }
-    __syncthreads();   // #9: dA
+    __syncthreads();   // #6: dA
     ln = fresh();
     {
       const bf16x8 kib = rd_row((lb)(lds + O_KI), LT, 16 * ln.w, 0, ln);
@@ -744,24 +798,25 @@ __global__ __launch_bounds__(NT, 1) void bwd_chunk_kernel(
       suffix_prefix(db, de, dgc, ln);
       dgc[0] += rs;
       dgc[1] += rs;
+      const Rsrc rdq = chunk_view(dq, tok0, L, H, h, DD, 4);
+      const Rsrc rdk = chunk_view(dk, tok0, L, H, h, DD, 4);
+      const Rsrc rdg = chunk_view(dg, tok0, SG ? 0 : L, H, h, DD, 4);
+      const uint32_t lo = 4 * (uint32_t)(4 * ln.g * H * DD + col);
 #pragma unroll
       for (int I = 0; I < 2; ++I)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int i = 16 * I + 4 * ln.g + r;
-          const size_t row = (tok0 + i) * H + h;
-          if (i < L) {
-            dq[row * DD + col] = dQG[I][r];
-            dk[row * DD + col] = dKG[I][r];
-            if (!SG) dg[row * DD + col] = dgc[I][r];
-          }
+          const uint32_t so = 4 * (uint32_t)((16 * I + r) * H * DD);
+          st_f32(rdq, lo, so, dQG[I][r]);
+          st_f32(rdk, lo, so, dKG[I][r]);
+          if (!SG) st_f32(rdg, lo, so, dgc[I][r]);
           if (SG) {
             const float s = row_sum16(dgc[I][r]);
-            if (ln.n == 0) GP[ln.w * BC + i] = s;
+            if (ln.n == 0) GP[ln.w * BC + 16 * I + 4 * ln.g + r] = s;
           }
         }
     }
-    __syncthreads();   // #10: the chunk's LDS may be rewritten
+    __syncthreads();   // #7: the chunk's LDS may be rewritten
     ln = fresh();
   }
   if (nc > 0) finish_rows(0);
