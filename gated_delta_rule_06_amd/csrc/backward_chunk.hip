@@ -102,6 +102,17 @@ constexpr int O_FLAG = O_GP + 1024;
 constexpr int LDS_BYTES = O_FLAG + 16;
 static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 
+// One chunk's operand buffers.  The reverse sweep uses set 0; the forward
+// sweep alternates set 0 with buffers it has no other use for, so that the
+// next chunk's operands and T are formed while this chunk's state update runs.
+struct Set {
+  int kg, ki, v, beta, er, dl, tt;   // tb = tt + SZ_S
+};
+constexpr Set SET0{O_KG, O_KI, O_V, O_BETA, O_ER, O_DL, O_TT};
+constexpr Set SET1{O_QG, O_DO, O_NU, O_DBP, O_DBP + 128, O_DBP + 640, O_DAQ};
+static_assert(O_TB == O_TT + SZ_S && O_DA == O_DAQ + SZ_S, "T buffer pairs");
+static_assert(640 + 512 <= NDBP * 128, "second set's small buffers");
+
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef LDS uint16_t* lb;
 
@@ -185,11 +196,25 @@ __device__ __forceinline__ float shfl(float x, int src) {
 }
 
 // One chunk's per-lane inputs: tokens 16I + 4g + r (I < 2, r < 4) of channel or
-// value column 16w + n; bf16 as two packed words per I.
+// value column 16w + n.  A bf16 element comes in the aligned dword that holds
+// it and its neighbour channel (half n % 2); the lane's half is taken only
+// where it is used, so that a prefetch is never waited for where it is
+// issued (nothing packs or extends the loaded registers there).
 struct In {
-  u32x2 q[2], k[2], v[2], o[2];
+  uint32_t q[2][4], k[2][4], v[2][4], o[2][4];
   float gt[2][4];
 };
+// the lane's four bf16 as two packed dwords, and as fp32
+__device__ __forceinline__ u32x2 pack_raw(const uint32_t (&a)[4], uint32_t sel) {
+  return u32x2{__builtin_amdgcn_perm(a[1], a[0], sel), __builtin_amdgcn_perm(a[3], a[2], sel)};
+}
+__device__ __forceinline__ f32x4 unpack_raw(const uint32_t (&a)[4], uint32_t sh) {
+  return f32x4{__uint_as_float((a[0] << sh) & 0xffff0000u), __uint_as_float((a[1] << sh) & 0xffff0000u),
+               __uint_as_float((a[2] << sh) & 0xffff0000u), __uint_as_float((a[3] << sh) & 0xffff0000u)};
+}
+// byte selector and shift that pick the lane's half
+__device__ __forceinline__ uint32_t half_sel(int n) { return (n & 1) ? 0x07060302u : 0x05040100u; }
+__device__ __forceinline__ uint32_t half_sh(int n) { return (n & 1) ? 0u : 16u; }
 
 // Buffer views: a workgroup-uniform base and byte limit, a 32-bit lane offset
 // and a uniform offset per access; reads at or past the limit return zero and
@@ -217,24 +242,19 @@ __device__ __forceinline__ void load_in(In& x, const uint16_t* q, const uint16_t
   const Rsrc rg = chunk_view(g, tok0, L, H, h, SG ? 1 : DD, 4);
   const uint32_t lo = (uint32_t)(4 * ln.g * H * DD + 16 * ln.w + ln.n);   // the lane's token 4g
   const uint32_t lg = SG ? (uint32_t)(4 * ln.g * H) : lo;
+  const uint32_t lp = 2 * (lo & ~1u);   // byte offset of the dword holding the lane's element
 #pragma unroll
-  for (int I = 0; I < 2; ++I) {
-    uint32_t wq[4], wk[4], wv[4], wo[4];
+  for (int I = 0; I < 2; ++I)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const uint32_t so = (uint32_t)((16 * I + r) * H * DD);
       const uint32_t sg = SG ? (uint32_t)((16 * I + r) * H) : so;
-      wq[r] = rev ? __builtin_amdgcn_raw_buffer_load_b16(rq, 2 * lo, 2 * so, 0) : 0u;
-      wk[r] = __builtin_amdgcn_raw_buffer_load_b16(rk, 2 * lo, 2 * so, 0);
-      wv[r] = __builtin_amdgcn_raw_buffer_load_b16(rv, 2 * lo, 2 * so, 0);
-      wo[r] = rev ? __builtin_amdgcn_raw_buffer_load_b16(ro, 2 * lo, 2 * so, 0) : 0u;
+      x.q[I][r] = rev ? __builtin_amdgcn_raw_buffer_load_b32(rq, lp, 2 * so, 0) : 0u;
+      x.k[I][r] = __builtin_amdgcn_raw_buffer_load_b32(rk, lp, 2 * so, 0);
+      x.v[I][r] = __builtin_amdgcn_raw_buffer_load_b32(rv, lp, 2 * so, 0);
+      x.o[I][r] = rev ? __builtin_amdgcn_raw_buffer_load_b32(ro, lp, 2 * so, 0) : 0u;
       x.gt[I][r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rg, 4 * lg, 4 * sg, 0));
     }
-    x.q[I] = u32x2{wq[0] | (wq[1] << 16), wq[2] | (wq[3] << 16)};
-    x.k[I] = u32x2{wk[0] | (wk[1] << 16), wk[2] | (wk[3] << 16)};
-    x.v[I] = u32x2{wv[0] | (wv[1] << 16), wv[2] | (wv[3] << 16)};
-    x.o[I] = u32x2{wo[0] | (wo[1] << 16), wo[2] | (wo[3] << 16)};
-  }
 }
 
 // b - r for the lane's eight elements (prefix sums as MFMAs: lane group g
@@ -264,36 +284,35 @@ __device__ __forceinline__ bool prefix(const In& x, f32x4 bm[2], float& er, floa
   return bad;
 }
 
-// T = (I + Diag(beta) A)^{-1} in fp32 by one wave, A strictly lower in LDS.
-// Lanes with g even take column n of T_00, lanes with g odd column n of T_11,
-// each with the whole column in registers (forward substitution with no lane
-// exchange; the second copy of every column costs nothing).  Then T_10 =
-// -T_11 X, X = Diag(beta_1) A_10 T_00: X by the T_00 lanes (eight rows each)
+// T = (I + N)^{-1}, N = Diag(beta) A, in fp32 by one wave, from N^T (strictly
+// upper, [32][LA] fp32 in LDS).  Lanes with g even take column n of T_00,
+// lanes with g odd column n of T_11, each with the whole column in registers
+// (forward substitution with no lane exchange; the second copy of every
+// column costs nothing), updating every later row as soon as a row is final.
+// Then T_10 = -T_11 X, X = N_10 T_00: X by the T_00 lanes (eight rows each)
 // into the unused upper-right block of the fp32 buffer, T_10 by every lane
 // (rows 4g .. 4g+3 of column n); the exchange stays inside the wave.  Writes
-// T^T and (T Diag(beta))^T as bf16.
-__device__ __forceinline__ void solve_full(LDS char* lds, const Ln& ln) {
-  const LDS float* A = (const LDS float*)(lds + O_A);
+// T^T and (T Diag(beta))^T as bf16 into the set's buffers.
+__device__ __forceinline__ void solve_full(LDS char* lds, Set st, const Ln& ln) {
+  const LDS float* Nt = (const LDS float*)(lds + O_A);
   LDS float* Tf = (LDS float*)(lds + O_T);
-  const LDS float* beta = (const LDS float*)(lds + O_BETA);
+  const LDS float* beta = (const LDS float*)(lds + st.beta);
   const int b = ln.g & 1, off = 16 * b, j = ln.n;
   float x[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) x[i] = (i == j) ? 1.f : 0.f;
 #pragma unroll
-  for (int i = 1; i < 16; ++i) {
-    const LDS float* Ai = A + (off + i) * LA + off;
-    float acc = 0.f;
+  for (int m = 0; m < 15; ++m) {
+    const LDS float* Nm = Nt + (off + m) * LA + off;
 #pragma unroll
-    for (int m = 0; m < i; ++m) acc += Ai[m] * x[m];
-    x[i] -= beta[off + i] * acc;
+    for (int i = m + 1; i < 16; ++i) x[i] -= Nm[i] * x[m];
   }
   if (ln.g < 2) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) Tf[(off + i) * LA + off + j] = x[i];
     const float bj = beta[off + j];
-    LDS uint16_t* tt = (lb)(lds + O_TT) + (off + j) * LT + off;
-    LDS uint16_t* tb = (lb)(lds + O_TB) + (off + j) * LT + off;
+    LDS uint16_t* tt = (lb)(lds + st.tt) + (off + j) * LT + off;
+    LDS uint16_t* tb = (lb)(lds + st.tt + SZ_S) + (off + j) * LT + off;
 #pragma unroll
     for (int e = 0; e < 16; e += 4) {
       *(LDS u32x2*)(tt + e) = u32x2{pack_bf16x2(x[e], x[e + 1]), pack_bf16x2(x[e + 2], x[e + 3])};
@@ -303,26 +322,25 @@ __device__ __forceinline__ void solve_full(LDS char* lds, const Ln& ln) {
   }
   if (b == 0) {
     const int i0 = 4 * ln.g;   // rows 0..7 (g = 0) or 8..15 (g = 2) of X
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ii = 0; ii < 8; ++ii) {
-      const LDS float* Ai = A + (16 + i0 + ii) * LA;
-      float acc = 0.f;
+    for (int m = 0; m < 16; ++m) {
+      const LDS float* Nm = Nt + m * LA + 16 + i0;
 #pragma unroll
-      for (int m = 0; m < 16; ++m) acc += Ai[m] * x[m];
-      Tf[(i0 + ii) * LA + 16 + j] = beta[16 + i0 + ii] * acc;
+      for (int ii = 0; ii < 8; ++ii) acc[ii] += Nm[ii] * x[m];
     }
-  }
-  f32x4 t;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const LDS float* Ti = Tf + (16 + 4 * ln.g + r) * LA + 16;
-    float acc = 0.f;
-#pragma unroll
-    for (int m = 0; m < 16; ++m) acc += Ti[m] * Tf[m * LA + 16 + j];
-    t[r] = -acc;
+    for (int ii = 0; ii < 8; ++ii) Tf[(i0 + ii) * LA + 16 + j] = acc[ii];
   }
-  st_t((lb)(lds + O_TT), LT, 0, 16, t, ln);
-  st_t((lb)(lds + O_TB), LT, 0, 16, t * beta[j], ln);
+  f32x4 t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int m = 0; m < 16; ++m) {
+    const float xm = Tf[m * LA + 16 + j];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) t[r] -= Tf[(16 + 4 * ln.g + r) * LA + 16 + m] * xm;
+  }
+  st_t((lb)(lds + st.tt), LT, 0, 16, t, ln);
+  st_t((lb)(lds + st.tt + SZ_S), LT, 0, 16, t * beta[j], ln);
 }
 
 // Lower-triangle 16x16 tiles of a 32x32 matrix: (0,0), (1,0), (1,1).
@@ -331,40 +349,43 @@ __device__ __forceinline__ int tile_J(int t) { return t == 2 ? 1 : 0; }
 
 // Writes every input prep product of one chunk: KG, KI, V (and, reverse sweep,
 // QG and dO) as [channel][token] bf16, e^r and e^{b_L - r} of the lane's channel.
-__device__ __forceinline__ void prep_store(LDS char* lds, const In& x, const f32x4 bm[2], float er,
-                                           float dl, float scale, bool rev, const Ln& ln) {
+__device__ __forceinline__ void prep_store(LDS char* lds, Set st, const In& x,
+                                           const f32x4 bm[2], float er, float dl, float scale,
+                                           bool rev, const Ln& ln) {
 #pragma unroll
   for (int I = 0; I < 2; ++I) {
-    const f32x4 kf = unpack4(x.k[I]);
+    const f32x4 kf = unpack_raw(x.k[I], half_sh(ln.n));
     f32x4 p, pi;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       p[e] = __expf(bm[I][e]);
       pi[e] = __expf(-bm[I][e]);
     }
-    st_t((lb)(lds + O_KG), LT, 16 * ln.w, 16 * I, kf * p, ln);
-    st_t((lb)(lds + O_KI), LT, 16 * ln.w, 16 * I, kf * pi, ln);
-    st_raw((lb)(lds + O_V), LT, 16 * ln.w, 16 * I, x.v[I], ln);
+    st_t((lb)(lds + st.kg), LT, 16 * ln.w, 16 * I, kf * p, ln);
+    st_t((lb)(lds + st.ki), LT, 16 * ln.w, 16 * I, kf * pi, ln);
+    st_raw((lb)(lds + st.v), LT, 16 * ln.w, 16 * I, pack_raw(x.v[I], half_sel(ln.n)), ln);
     if (rev) {
-      st_t((lb)(lds + O_QG), LT, 16 * ln.w, 16 * I, unpack4(x.q[I]) * p * scale, ln);
-      st_raw((lb)(lds + O_DO), LT, 16 * ln.w, 16 * I, x.o[I], ln);
+      st_t((lb)(lds + O_QG), LT, 16 * ln.w, 16 * I, unpack_raw(x.q[I], half_sh(ln.n)) * p * scale, ln);
+      st_raw((lb)(lds + O_DO), LT, 16 * ln.w, 16 * I, pack_raw(x.o[I], half_sel(ln.n)), ln);
     }
   }
   if (ln.g == 0) {
-    ((LDS float*)(lds + O_ER))[16 * ln.w + ln.n] = er;
-    ((LDS float*)(lds + O_DL))[16 * ln.w + ln.n] = dl;
+    ((LDS float*)(lds + st.er))[16 * ln.w + ln.n] = er;
+    ((LDS float*)(lds + st.dl))[16 * ln.w + ln.n] = dl;
   }
 }
 
-// Tile t (0..2) of A = strict_tril(KG KI^T) (fp32) or, qk, of Aqk =
-// tril(QG KI^T) (bf16, transposed).
-__device__ __forceinline__ void tile_a(LDS char* lds, bool qk, int t, const Ln& ln) {
+// Tile t (0..2) of A = strict_tril(KG KI^T) or, qk, of Aqk = tril(QG KI^T)
+// (bf16, transposed).  A is stored fp32, row-major (reverse sweep, for dbeta)
+// or, nt, as N^T = (Diag(beta) A)^T for the solve.
+__device__ __forceinline__ void tile_a(LDS char* lds, Set st, bool qk, bool nt, int t,
+                                       const Ln& ln) {
   const int I = tile_I(t), J = tile_J(t);
-  const lb X = (lb)(lds + (qk ? O_QG : O_KG));
+  const lb X = (lb)(lds + (qk ? O_QG : st.kg));
   f32x4 acc{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kc = 0; kc < 4; ++kc)
-    acc = mma(rd_tr(X, LT, 32 * kc, 16 * I, ln), rd_tr((lb)(lds + O_KI), LT, 32 * kc, 16 * J, ln),
+    acc = mma(rd_tr(X, LT, 32 * kc, 16 * I, ln), rd_tr((lb)(lds + st.ki), LT, 32 * kc, 16 * J, ln),
               acc);
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
@@ -373,6 +394,9 @@ __device__ __forceinline__ void tile_a(LDS char* lds, bool qk, int t, const Ln& 
   }
   if (qk) {
     st_t((lb)(lds + O_AQ), LT, 16 * J, 16 * I, acc, ln);
+  } else if (nt) {
+    const f32x4 bt = *(const LDS f32x4*)((const LDS float*)(lds + st.beta) + 16 * I + 4 * ln.g);
+    *(LDS f32x4*)((LDS float*)(lds + O_A) + (16 * J + ln.n) * LA + 16 * I + 4 * ln.g) = acc * bt;
   } else {
     LDS float* A = (LDS float*)(lds + O_A);
 #pragma unroll
@@ -382,19 +406,20 @@ __device__ __forceinline__ void tile_a(LDS char* lds, bool qk, int t, const Ln& 
 
 // Copies T^T and (T Diag(beta))^T between LDS and a workspace slot: thread
 // t moves four elements of row (t / 8) % 32 of buffer t / 256.
-__device__ __forceinline__ LDS u32x2* t_part(LDS char* lds) {
+__device__ __forceinline__ LDS u32x2* t_part(LDS char* lds, Set st) {
   const int t = threadIdx.x;
-  return (LDS u32x2*)((lb)(lds + O_TT + (t >> 8) * SZ_S) + ((t >> 3) & 31) * LT + 4 * (t & 7));
+  return (LDS u32x2*)((lb)(lds + st.tt + (t >> 8) * SZ_S) + ((t >> 3) & 31) * LT + 4 * (t & 7));
 }
 
 // U = T Diag(beta) V (own value columns, registers; -U also to LDS) and
 // W = T Diag(beta) KG (own key channels; -W to LDS).
-__device__ __forceinline__ void tiles_uw(LDS char* lds, f32x4 U[2], bool store_u, const Ln& ln) {
+__device__ __forceinline__ void tiles_uw(LDS char* lds, Set st, f32x4 U[2], bool store_u,
+                                         const Ln& ln) {
 #pragma unroll
   for (int I = 0; I < 2; ++I) {
-    const bf16x8 tb = rd_tr((lb)(lds + O_TB), LT, 0, 16 * I, ln);
-    U[I] = mma(tb, rd_row((lb)(lds + O_V), LT, 16 * ln.w, 0, ln), f32x4{0.f, 0.f, 0.f, 0.f});
-    const f32x4 W = mma(tb, rd_row((lb)(lds + O_KG), LT, 16 * ln.w, 0, ln),
+    const bf16x8 tb = rd_tr((lb)(lds + st.tt + SZ_S), LT, 0, 16 * I, ln);
+    U[I] = mma(tb, rd_row((lb)(lds + st.v), LT, 16 * ln.w, 0, ln), f32x4{0.f, 0.f, 0.f, 0.f});
+    const f32x4 W = mma(tb, rd_row((lb)(lds + st.kg), LT, 16 * ln.w, 0, ln),
                         f32x4{0.f, 0.f, 0.f, 0.f});
     st_t((lb)(lds + O_NW), LT, 16 * ln.w, 16 * I, -W, ln);
     if (store_u) st_t((lb)(lds + O_NU), LT, 16 * ln.w, 16 * I, -U[I], ln);
@@ -446,8 +471,8 @@ __global__ __launch_bounds__(NT, 1) void bwd_chunk_kernel(
   const int nc = (len + BC - 1) / BC;
   // chunk m's workspace slot: S_c in the lanes' own order, then T^T and (T Diag(beta))^T
   uint32_t* slot0 = states + ((size_t)sq + t0 / BC) * H * SLOT_DW + (size_t)h * SLOT_DW;
-  auto slot = [&](int m, int cb) {
-    return (u32x2*)(slot0 + (size_t)m * H * SLOT_DW) + (ln.w * 8 + cb) * 64 + ln.l;
+  auto slot = [&](int m, int cb, const Ln& L) {
+    return (u32x2*)(slot0 + (size_t)m * H * SLOT_DW) + (L.w * 8 + cb) * 64 + L.l;
   };
   auto tslot = [&](int m) {
     return (u32x2*)(slot0 + (size_t)m * H * SLOT_DW + ST_DW) + threadIdx.x;
@@ -482,42 +507,52 @@ __global__ __launch_bounds__(NT, 1) void bwd_chunk_kernel(
   auto clen = [&](int mm) { return len - BC * mm < BC ? len - BC * mm : BC; };
   In xn;
   float bn = 0.f;
-  auto fetch = [&](int mm, bool rev) {
+  auto fetch = [&](int mm, bool rev, const Ln& ll) {
     const int L = clen(mm);
     const size_t tok0 = t0 + (size_t)BC * mm;
-    load_in<SG>(xn, q, k, v, dout, g, tok0, L, H, h, rev, ln);
-    bn = (ln.w == 0 && ln.l < L) ? beta[(tok0 + ln.l) * H + h] : 0.f;
+    load_in<SG>(xn, q, k, v, dout, g, tok0, L, H, h, rev, ll);
+    bn = (ll.w == 0 && ll.l < L) ? beta[(tok0 + ll.l) * H + h] : 0.f;
   };
-  if (nc > 0) fetch(0, false);
-  for (int m = 0; m < nc; ++m) {
-#pragma unroll
-    for (int cb = 0; cb < 8; ++cb)
-      *slot(m, cb) = u32x2{pack_bf16x2(S[cb][0], S[cb][1]), pack_bf16x2(S[cb][2], S[cb][3])};
+  if (nc > 0) fetch(0, false, ln);
+  // chunk mm's operands into set st from the prefetched inputs, then the next fetch
+  auto prep1 = [&](int mm, Set st, const Ln& ll) {
     const In x = xn;
-    if (ln.w == 0 && ln.l < BC) BETA[ln.l] = bn;
+    if (ll.w == 0 && ll.l < BC) ((LDS float*)(lds + st.beta))[ll.l] = bn;
+    if (mm + 1 < nc) fetch(mm + 1, false, ll);
     f32x4 bm[2];
     float er, dl;
-    if (prefix(x, bm, er, dl, ln)) *FLAG = 1;
-    prep_store(lds, x, bm, er, dl, scale, false, ln);
-    __syncthreads();   // #1
-    ln = fresh();
-    if (*FLAG) break;
-    if (m + 1 < nc) fetch(m + 1, false);
-    if (ln.w == NW - 1) {
-      // A (all three tiles) and T on the last wave
+    if (prefix(x, bm, er, dl, ll)) *FLAG = 1;
+    prep_store(lds, st, x, bm, er, dl, scale, false, ll);
+  };
+  // N^T and T of the chunk whose operands are in set st, on the last wave
+  auto solve1 = [&](Set st, const Ln& ll) {
 #pragma unroll
-      for (int t = 0; t < 3; ++t) tile_a(lds, false, t, ln);
-      solve_full(lds, ln);
-    }
+    for (int t = 0; t < 3; ++t) tile_a(lds, st, false, true, t, ll);
+    solve_full(lds, st, ll);
+  };
+  if (nc > 0) {
+    prep1(0, SET0, ln);
+    __syncthreads();
+    ln = fresh();
+    if (ln.w == NW - 1 && !*FLAG) solve1(SET0, ln);
+    __syncthreads();
+    ln = fresh();
+  }
+  for (int m = 0; m < nc; ++m) {
+    const Set cur = (m & 1) ? SET1 : SET0, nxt = (m & 1) ? SET0 : SET1;
+    if (*FLAG) break;
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb)
+      *slot(m, cb, ln) = u32x2{pack_bf16x2(S[cb][0], S[cb][1]), pack_bf16x2(S[cb][2], S[cb][3])};
+    *tslot(m) = *t_part(lds, cur);
     f32x4 Sm[8];
 #pragma unroll
-    for (int cb = 0; cb < 8; ++cb) Sm[cb] = S[cb] * *(const LDS f32x4*)(ER + 16 * cb + 4 * ln.g);
-    __syncthreads();   // #2: T
-    ln = fresh();
-    *tslot(m) = *t_part(lds);
+    for (int cb = 0; cb < 8; ++cb)
+      Sm[cb] = S[cb] * *(const LDS f32x4*)((const LDS float*)(lds + cur.er) + 16 * cb + 4 * ln.g);
     f32x4 U[2];
-    tiles_uw(lds, U, false, ln);
-    __syncthreads();   // #3: -W
+    tiles_uw(lds, cur, U, false, ln);
+    if (m + 1 < nc) prep1(m + 1, nxt, ln);
+    __syncthreads();   // #a: -W; the next chunk's operands
     ln = fresh();
     // E = U - W S_m (own value columns); S_{c+1} = Diag(e^{b_L - r}) (S_m + KI^T E)
 #pragma unroll
@@ -529,9 +564,10 @@ __global__ __launch_bounds__(NT, 1) void bwd_chunk_kernel(
     const bf16x8 eb = pack8(U[0], U[1]);
 #pragma unroll
     for (int cb = 0; cb < 8; ++cb)
-      S[cb] = mma(rd_rowp((lb)(lds + O_KI), LT, 16 * cb, 0, ln), eb, Sm[cb]) *
-              *(const LDS f32x4*)(DL + 16 * cb + 4 * ln.g);
-    __syncthreads();   // #4: the chunk's LDS may be rewritten
+      S[cb] = mma(rd_rowp((lb)(lds + cur.ki), LT, 16 * cb, 0, ln), eb, Sm[cb]) *
+              *(const LDS f32x4*)((const LDS float*)(lds + cur.dl) + 16 * cb + 4 * ln.g);
+    if (ln.w == NW - 1 && m + 1 < nc && !*FLAG) solve1(nxt, ln);
+    __syncthreads();   // #b: the next chunk's T; this chunk's buffers are free
     ln = fresh();
   }
   if (*FLAG) {
@@ -548,47 +584,48 @@ __global__ __launch_bounds__(NT, 1) void bwd_chunk_kernel(
     for (int r = 0; r < 4; ++r)
       dS[cb][r] = dSf ? dSf[sbase + (size_t)(16 * cb + 4 * ln.g + r) * DD + col] : 0.f;
   // dbeta (and a per-head gate's dlog alpha) of chunk mm from the partials
-  auto finish_rows = [&](int mm) {
-    if (ln.w == 0 && ln.l < BC) {
+  auto finish_rows = [&](int mm, const Ln& ll) {
+    if (ll.w == NW - 1 && ll.l < BC) {
       const int L = clen(mm);
-      if (ln.l < L) {
-        const size_t row = (t0 + (size_t)BC * mm + ln.l) * H + h;
+      if (ll.l < L) {
+        const size_t row = (t0 + (size_t)BC * mm + ll.l) * H + h;
         float s = 0.f;
-        for (int p = 0; p < NDBP; ++p) s += DBP[p * BC + ln.l];
+        for (int p = 0; p < NDBP; ++p) s += DBP[p * BC + ll.l];
         dbeta[row] = s;
         if (SG) {
           float t = 0.f;
-          for (int p = 0; p < NW; ++p) t += GP[p * BC + ln.l];
+          for (int p = 0; p < NW; ++p) t += GP[p * BC + ll.l];
           dg[row] = t;
         }
       }
     }
   };
   u32x2 Scn[8], Tn;
-  auto fetch2 = [&](int mm) {
-    fetch(mm, true);
+  auto fetch2 = [&](int mm, const Ln& L) {
+    fetch(mm, true, L);
 #pragma unroll
-    for (int cb = 0; cb < 8; ++cb) Scn[cb] = *slot(mm, cb);
+    for (int cb = 0; cb < 8; ++cb) Scn[cb] = *slot(mm, cb, L);
     Tn = *tslot(mm);
   };
-  if (nc > 0) fetch2(nc - 1);
+  if (nc > 0) fetch2(nc - 1, ln);
   for (int m = nc - 1; m >= 0; --m) {
     const int L = clen(m);
     const size_t tok0 = t0 + (size_t)BC * m;
     const In x = xn;
+    const u32x2 o0 = pack_raw(x.o[0], half_sel(ln.n)), o1 = pack_raw(x.o[1], half_sel(ln.n));
     if (ln.w == 0 && ln.l < BC) BETA[ln.l] = bn;
     u32x2 Sc[8];
 #pragma unroll
     for (int cb = 0; cb < 8; ++cb) Sc[cb] = Scn[cb];
-    *t_part(lds) = Tn;
+    *t_part(lds, SET0) = Tn;
     f32x4 bm[2];
     float er, dl;
     prefix(x, bm, er, dl, ln);
-    prep_store(lds, x, bm, er, dl, scale, true, ln);
+    prep_store(lds, SET0, x, bm, er, dl, scale, true, ln);
     __syncthreads();   // #1: the chunk's operands, T
     ln = fresh();
-    if (m > 0) fetch2(m - 1);
-    if (m + 1 < nc) finish_rows(m + 1);
+    if (m > 0) fetch2(m - 1, ln);
+    if (m + 1 < nc) finish_rows(m + 1, ln);
     // dS_m = Diag(e^{b_L - r}) dS;  S_m = Diag(e^r) S_c to R ([value][channel]);
     // sum_v dS_m S_m over the lane's columns into the partials (the decay of
     // the incoming state over the chunk, part of every token's dlog alpha)
@@ -603,7 +640,7 @@ __global__ __launch_bounds__(NT, 1) void bwd_chunk_kernel(
         if (ln.n == 0) RP[ln.w * DD + 16 * cb + 4 * ln.g + r] = s;
       }
     }
-    if (ln.w < 6) tile_a(lds, ln.w >= 3, ln.w % 3, ln);
+    if (ln.w < 6) tile_a(lds, SET0, ln.w >= 3, false, ln.w % 3, ln);
     // dE = KI dS_m (+ Aqk^T dO below), own value columns
     f32x4 dE[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
@@ -613,7 +650,7 @@ __global__ __launch_bounds__(NT, 1) void bwd_chunk_kernel(
       for (int I = 0; I < 2; ++I) dE[I] = mma(rd_trp((lb)(lds + O_KI), LT, 32 * kc, 16 * I, ln), sb, dE[I]);
     }
     f32x4 U[2];
-    tiles_uw(lds, U, true, ln);
+    tiles_uw(lds, SET0, U, true, ln);
     __syncthreads();   // #2: A, Aqk, S_m, -W, -U
     ln = fresh();
     {
@@ -702,7 +739,7 @@ __global__ __launch_bounds__(NT, 1) void bwd_chunk_kernel(
     for (int I = 0; I < 2; ++I) st_t((lb)(lds + O_NDE), LT, 16 * ln.w, 16 * I, dYk[I], ln);
     // dS_c = Diag(e^r) (dS_m + QG^T dO - W^T dE); dS_m to R for dKI
     {
-      const bf16x8 ob = __builtin_bit_cast(bf16x8, u32x4{x.o[0][0], x.o[0][1], x.o[1][0], x.o[1][1]});
+      const bf16x8 ob = __builtin_bit_cast(bf16x8, u32x4{o0[0], o0[1], o1[0], o1[1]});
       const bf16x8 eb = pack8(dE[0], dE[1]);
 #pragma unroll
       for (int cb = 0; cb < 8; ++cb) {
@@ -819,7 +856,7 @@ __global__ __launch_bounds__(NT, 1) void bwd_chunk_kernel(
     __syncthreads();   // #7: the chunk's LDS may be rewritten
     ln = fresh();
   }
-  if (nc > 0) finish_rows(0);
+  if (nc > 0) finish_rows(0, ln);
   if (dS0) {
 #pragma unroll
     for (int cb = 0; cb < 8; ++cb)
