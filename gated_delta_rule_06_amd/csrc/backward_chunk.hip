@@ -111,10 +111,18 @@ struct Set {
 constexpr Set SET0{O_KG, O_KI, O_V, O_BETA, O_ER, O_DL, O_TT};
 constexpr Set SET1{O_QG, O_DO, O_NU, O_DBP, O_DBP + 128, O_DBP + 640, O_DAQ};
 static_assert(O_TB == O_TT + SZ_S && O_DA == O_DAQ + SZ_S, "T buffer pairs");
+static_assert(O_NU == O_NW + SZ_T && NW * BC * 20 * 4 <= 2 * SZ_T, "store staging");
+// Per-wave staging of a chunk's loaded inputs (E, -dE and R are free whenever
+// a chunk's inputs are unpacked): four bf16 [32][16] tiles, then the fp32
+// gates as [32][20].
+constexpr int STG_BYTES = 4 * BC * 16 * 2 + BC * 20 * 4;
+static_assert(O_NDE == O_E + SZ_T && O_R == O_NDE + SZ_T &&
+              NW * STG_BYTES <= 2 * SZ_T + DD * LR * 2, "input staging");
 static_assert(640 + 512 <= NDBP * 128, "second set's small buffers");
 
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef LDS uint16_t* lb;
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ f32x4 mma(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -195,26 +203,22 @@ __device__ __forceinline__ float shfl(float x, int src) {
   return __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(x)));
 }
 
-// One chunk's per-lane inputs: tokens 16I + 4g + r (I < 2, r < 4) of channel or
-// value column 16w + n.  A bf16 element comes in the aligned dword that holds
-// it and its neighbour channel (half n % 2); the lane's half is taken only
-// where it is used, so that a prefetch is never waited for where it is
-// issued (nothing packs or extends the loaded registers there).
+// One chunk's inputs as loaded: each wave loads its own 32-token slice of its
+// 16 channels (value columns), 16 bytes per lane and tensor: bf16 tensors as
+// token L / 2, columns 8 (L % 2) .. +7; the gates as tokens L / 4 and 16 + L / 4,
+// columns 4 (L % 4) .. +3 (per-head gates: token L, L < 32).  Nothing touches
+// these registers until the chunk is unpacked, so the prefetch is never
+// waited for where it is issued.
 struct In {
-  uint32_t q[2][4], k[2][4], v[2][4], o[2][4];
+  u32x4 q, k, v, o;
+  f32x4 g0, g1;
+};
+// The lane's elements in the accumulator layout: tokens 16I + 4g + r of
+// column 16w + n, bf16 as two packed dwords per I.
+struct Ch {
+  u32x2 q[2], k[2], v[2], o[2];
   float gt[2][4];
 };
-// the lane's four bf16 as two packed dwords, and as fp32
-__device__ __forceinline__ u32x2 pack_raw(const uint32_t (&a)[4], uint32_t sel) {
-  return u32x2{__builtin_amdgcn_perm(a[1], a[0], sel), __builtin_amdgcn_perm(a[3], a[2], sel)};
-}
-__device__ __forceinline__ f32x4 unpack_raw(const uint32_t (&a)[4], uint32_t sh) {
-  return f32x4{__uint_as_float((a[0] << sh) & 0xffff0000u), __uint_as_float((a[1] << sh) & 0xffff0000u),
-               __uint_as_float((a[2] << sh) & 0xffff0000u), __uint_as_float((a[3] << sh) & 0xffff0000u)};
-}
-// byte selector and shift that pick the lane's half
-__device__ __forceinline__ uint32_t half_sel(int n) { return (n & 1) ? 0x07060302u : 0x05040100u; }
-__device__ __forceinline__ uint32_t half_sh(int n) { return (n & 1) ? 0u : 16u; }
 
 // Buffer views: a workgroup-uniform base and byte limit, a 32-bit lane offset
 // and a uniform offset per access; reads at or past the limit return zero and
@@ -240,27 +244,67 @@ __device__ __forceinline__ void load_in(In& x, const uint16_t* q, const uint16_t
   const Rsrc rq = chunk_view(q, tok0, L, H, h, DD, 2), rk = chunk_view(k, tok0, L, H, h, DD, 2);
   const Rsrc rv = chunk_view(v, tok0, L, H, h, DD, 2), ro = chunk_view(dout, tok0, L, H, h, DD, 2);
   const Rsrc rg = chunk_view(g, tok0, L, H, h, SG ? 1 : DD, 4);
-  const uint32_t lo = (uint32_t)(4 * ln.g * H * DD + 16 * ln.w + ln.n);   // the lane's token 4g
-  const uint32_t lg = SG ? (uint32_t)(4 * ln.g * H) : lo;
-  const uint32_t lp = 2 * (lo & ~1u);   // byte offset of the dword holding the lane's element
+  const uint32_t ob = 2 * (uint32_t)((ln.l >> 1) * H * DD + 16 * ln.w + 8 * (ln.l & 1));
+  const u32x4 z{0u, 0u, 0u, 0u};
+  x.q = rev ? __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, ob, 0, 0)) : z;
+  x.k = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, ob, 0, 0));
+  x.v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, ob, 0, 0));
+  x.o = rev ? __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ro, ob, 0, 0)) : z;
+  if (SG) {
+    x.g0 = f32x4{0.f, 0.f, 0.f, 0.f};
+    x.g0[0] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rg, 4 * (uint32_t)(ln.l * H), 0, 0));
+    x.g1 = f32x4{0.f, 0.f, 0.f, 0.f};
+  } else {
+    const uint32_t og = 4 * (uint32_t)((ln.l >> 2) * H * DD + 16 * ln.w + 4 * (ln.l & 3));
+    x.g0 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rg, og, 0, 0));
+    x.g1 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rg, og, 4 * (uint32_t)(16 * H * DD), 0));
+  }
+}
+
+// The loaded inputs into the accumulator layout through the wave's own
+// staging area (only this wave touches it, so no barrier): bf16 tiles as
+// [token][16] and read back with the transpose read (lane n of group g gets
+// tokens 4g .. 4g+3 of column n), gates as [token][20] fp32.
+template <bool SG>
+__device__ __forceinline__ Ch unstage(LDS char* lds, const In& x, bool rev, const Ln& ln) {
+  LDS char* stg = lds + O_E + ln.w * STG_BYTES;
+  const int tb = (ln.l >> 1) * 32 + (ln.l & 1) * 16;   // bytes
+  *(LDS u32x4*)(stg + 1024 + tb) = x.k;
+  *(LDS u32x4*)(stg + 2048 + tb) = x.v;
+  if (rev) {
+    *(LDS u32x4*)(stg + tb) = x.q;
+    *(LDS u32x4*)(stg + 3072 + tb) = x.o;
+  }
+  LDS float* sg = (LDS float*)(stg + 4096);
+  if (SG) {
+    if (ln.l < BC) sg[ln.l] = x.g0[0];
+  } else {
+    *(LDS f32x4*)(sg + (ln.l >> 2) * 20 + 4 * (ln.l & 3)) = x.g0;
+    *(LDS f32x4*)(sg + (16 + (ln.l >> 2)) * 20 + 4 * (ln.l & 3)) = x.g1;
+  }
+  Ch c;
 #pragma unroll
-  for (int I = 0; I < 2; ++I)
+  for (int I = 0; I < 2; ++I) {
+    const int e = (16 * I + 4 * ln.g + (ln.n >> 2)) * 16 + 4 * (ln.n & 3);   // elements
+    auto rd = [&](int base) {
+      return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                           (LDS i16x4*)((LDS uint16_t*)(stg + base) + e)));
+    };
+    c.k[I] = rd(1024);
+    c.v[I] = rd(2048);
+    c.q[I] = rev ? rd(0) : u32x2{0u, 0u};
+    c.o[I] = rev ? rd(3072) : u32x2{0u, 0u};
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const uint32_t so = (uint32_t)((16 * I + r) * H * DD);
-      const uint32_t sg = SG ? (uint32_t)((16 * I + r) * H) : so;
-      x.q[I][r] = rev ? __builtin_amdgcn_raw_buffer_load_b32(rq, lp, 2 * so, 0) : 0u;
-      x.k[I][r] = __builtin_amdgcn_raw_buffer_load_b32(rk, lp, 2 * so, 0);
-      x.v[I][r] = __builtin_amdgcn_raw_buffer_load_b32(rv, lp, 2 * so, 0);
-      x.o[I][r] = rev ? __builtin_amdgcn_raw_buffer_load_b32(ro, lp, 2 * so, 0) : 0u;
-      x.gt[I][r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rg, 4 * lg, 4 * sg, 0));
-    }
+    for (int r = 0; r < 4; ++r)
+      c.gt[I][r] = SG ? sg[16 * I + 4 * ln.g + r] : sg[(16 * I + 4 * ln.g + r) * 20 + ln.n];
+  }
+  return c;
 }
 
 // b - r for the lane's eight elements (prefix sums as MFMAs: lane group g
 // supplies token 4g + s at step s, the ones matrix is formed per lane), and
 // whether any lies beyond RANGE.  Also e^r and e^{b_L - r} of the lane's channel.
-__device__ __forceinline__ bool prefix(const In& x, f32x4 bm[2], float& er, float& dl,
+__device__ __forceinline__ bool prefix(const Ch& x, f32x4 bm[2], float& er, float& dl,
                                        const Ln& ln) {
   f32x4 b0{0.f, 0.f, 0.f, 0.f}, b1{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -343,18 +387,38 @@ __device__ __forceinline__ void solve_full(LDS char* lds, Set st, const Ln& ln) 
   st_t((lb)(lds + st.tt + SZ_S), LT, 0, 16, t * beta[j], ln);
 }
 
+// Stores a wave's 32 x 16 fp32 tile (accumulator layout: tokens 16I + 4g + r,
+// column 16w + n) to a chunk view of a [rows, H, 128] tensor, through the
+// wave's own LDS staging area (token rows of 20 dwords, no bank conflicts):
+// each lane then writes four columns of one token, 16 bytes.
+__device__ __forceinline__ void store_tile(Rsrc rv, LDS float* stg, const f32x4 x[2], int H,
+                                           const Ln& ln) {
+#pragma unroll
+  for (int I = 0; I < 2; ++I)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) stg[(16 * I + 4 * ln.g + r) * 20 + ln.n] = x[I][r];
+  const int t = ln.l >> 2, j = ln.l & 3;
+  const uint32_t off = 4 * (uint32_t)(t * H * DD + 16 * ln.w + 4 * j);
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    const f32x4 y = *(const LDS f32x4*)(stg + (16 * hh + t) * 20 + 4 * j);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, y), rv, off,
+                                           4 * (uint32_t)(16 * hh * H * DD), 0);
+  }
+}
+
 // Lower-triangle 16x16 tiles of a 32x32 matrix: (0,0), (1,0), (1,1).
 __device__ __forceinline__ int tile_I(int t) { return t == 0 ? 0 : 1; }
 __device__ __forceinline__ int tile_J(int t) { return t == 2 ? 1 : 0; }
 
 // Writes every input prep product of one chunk: KG, KI, V (and, reverse sweep,
 // QG and dO) as [channel][token] bf16, e^r and e^{b_L - r} of the lane's channel.
-__device__ __forceinline__ void prep_store(LDS char* lds, Set st, const In& x,
+__device__ __forceinline__ void prep_store(LDS char* lds, Set st, const Ch& x,
                                            const f32x4 bm[2], float er, float dl, float scale,
                                            bool rev, const Ln& ln) {
 #pragma unroll
   for (int I = 0; I < 2; ++I) {
-    const f32x4 kf = unpack_raw(x.k[I], half_sh(ln.n));
+    const f32x4 kf = unpack4(x.k[I]);
     f32x4 p, pi;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -363,10 +427,10 @@ __device__ __forceinline__ void prep_store(LDS char* lds, Set st, const In& x,
     }
     st_t((lb)(lds + st.kg), LT, 16 * ln.w, 16 * I, kf * p, ln);
     st_t((lb)(lds + st.ki), LT, 16 * ln.w, 16 * I, kf * pi, ln);
-    st_raw((lb)(lds + st.v), LT, 16 * ln.w, 16 * I, pack_raw(x.v[I], half_sel(ln.n)), ln);
+    st_raw((lb)(lds + st.v), LT, 16 * ln.w, 16 * I, x.v[I], ln);
     if (rev) {
-      st_t((lb)(lds + O_QG), LT, 16 * ln.w, 16 * I, unpack_raw(x.q[I], half_sh(ln.n)) * p * scale, ln);
-      st_raw((lb)(lds + O_DO), LT, 16 * ln.w, 16 * I, pack_raw(x.o[I], half_sel(ln.n)), ln);
+      st_t((lb)(lds + O_QG), LT, 16 * ln.w, 16 * I, unpack4(x.q[I]) * p * scale, ln);
+      st_raw((lb)(lds + O_DO), LT, 16 * ln.w, 16 * I, x.o[I], ln);
     }
   }
   if (ln.g == 0) {
@@ -516,7 +580,7 @@ __global__ __launch_bounds__(NT, 1) void bwd_chunk_kernel(
   if (nc > 0) fetch(0, false, ln);
   // chunk mm's operands into set st from the prefetched inputs, then the next fetch
   auto prep1 = [&](int mm, Set st, const Ln& ll) {
-    const In x = xn;
+    const Ch x = unstage<SG>(lds, xn, false, ll);
     if (ll.w == 0 && ll.l < BC) ((LDS float*)(lds + st.beta))[ll.l] = bn;
     if (mm + 1 < nc) fetch(mm + 1, false, ll);
     f32x4 bm[2];
@@ -611,8 +675,8 @@ __global__ __launch_bounds__(NT, 1) void bwd_chunk_kernel(
   for (int m = nc - 1; m >= 0; --m) {
     const int L = clen(m);
     const size_t tok0 = t0 + (size_t)BC * m;
-    const In x = xn;
-    const u32x2 o0 = pack_raw(x.o[0], half_sel(ln.n)), o1 = pack_raw(x.o[1], half_sel(ln.n));
+    const Ch x = unstage<SG>(lds, xn, true, ln);
+    const u32x2 o0 = x.o[0], o1 = x.o[1];
     if (ln.w == 0 && ln.l < BC) BETA[ln.l] = bn;
     u32x2 Sc[8];
 #pragma unroll
@@ -658,19 +722,18 @@ __global__ __launch_bounds__(NT, 1) void bwd_chunk_kernel(
 #pragma unroll
       for (int I = 0; I < 2; ++I) dE[I] = mma(rd_row((lb)(lds + O_AQ), LT, 16 * I, 0, ln), ob, dE[I]);
     }
+    f32x4 dvv[2];   // dV = beta dY_v, stored with the other gradients
     {
       // dY_v = T^T dE; dV = beta dY_v; dbeta += dY_v . V; dY_v over the own rows of V; -dE
       const bf16x8 eb = pack8(dE[0], dE[1]);
-      const Rsrc rdv = chunk_view(dv, tok0, L, H, h, DD, 4);
-      const uint32_t lo = (uint32_t)(4 * ln.g * H * DD + col);
 #pragma unroll
       for (int I = 0; I < 2; ++I) {
         const f32x4 y = mma(rd_rowp((lb)(lds + O_TT), LT, 16 * I, 0, ln), eb, f32x4{0.f, 0.f, 0.f, 0.f});
         const f32x4 vv = unpack4(ld_raw((lb)(lds + O_V), LT, 16 * ln.w, 16 * I, ln));
         const f32x4 bt = *(const LDS f32x4*)(BETA + 16 * I + 4 * ln.g);
+        dvv[I] = bt * y;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          st_f32(rdv, 4 * lo, 4 * (uint32_t)((16 * I + r) * H * DD), bt[r] * y[r]);
           const float s = row_sum16(y[r] * vv[r]);
           if (ln.n == 0) DBP[ln.w * BC + 16 * I + 4 * ln.g + r] = s;
         }
@@ -835,23 +898,21 @@ __global__ __launch_bounds__(NT, 1) void bwd_chunk_kernel(
       suffix_prefix(db, de, dgc, ln);
       dgc[0] += rs;
       dgc[1] += rs;
-      const Rsrc rdq = chunk_view(dq, tok0, L, H, h, DD, 4);
-      const Rsrc rdk = chunk_view(dk, tok0, L, H, h, DD, 4);
-      const Rsrc rdg = chunk_view(dg, tok0, SG ? 0 : L, H, h, DD, 4);
-      const uint32_t lo = 4 * (uint32_t)(4 * ln.g * H * DD + col);
+      // -W and -U are free: each wave stages its tiles in 2560 bytes of them
+      LDS float* stg = (LDS float*)(lds + O_NW) + ln.w * (BC * 20);
+      store_tile(chunk_view(dq, tok0, L, H, h, DD, 4), stg, dQG, H, ln);
+      store_tile(chunk_view(dk, tok0, L, H, h, DD, 4), stg, dKG, H, ln);
+      store_tile(chunk_view(dv, tok0, L, H, h, DD, 4), stg, dvv, H, ln);
+      if (!SG) store_tile(chunk_view(dg, tok0, L, H, h, DD, 4), stg, dgc, H, ln);
+      if (SG) {
 #pragma unroll
-      for (int I = 0; I < 2; ++I)
+        for (int I = 0; I < 2; ++I)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const uint32_t so = 4 * (uint32_t)((16 * I + r) * H * DD);
-          st_f32(rdq, lo, so, dQG[I][r]);
-          st_f32(rdk, lo, so, dKG[I][r]);
-          if (!SG) st_f32(rdg, lo, so, dgc[I][r]);
-          if (SG) {
+          for (int r = 0; r < 4; ++r) {
             const float s = row_sum16(dgc[I][r]);
             if (ln.n == 0) GP[ln.w * BC + 16 * I + 4 * ln.g + r] = s;
           }
-        }
+      }
     }
     __syncthreads();   // #7: the chunk's LDS may be rewritten
     ln = fresh();
