@@ -203,6 +203,35 @@ __device__ __forceinline__ float shfl(float x, int src) {
   return __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(x)));
 }
 
+// One reduce-scatter step inside 16-lane rows: lanes with `hi` keep b, the
+// others a, each adding the partner's copy (DPP pattern CTRL pairs every lane
+// with one of the other kind).
+template <int CTRL>
+__device__ __forceinline__ float rs_step(float a, float b, bool hi) {
+  const float keep = hi ? b : a, send = hi ? a : b;
+  return keep + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(send), CTRL, 0xf, 0xf, false));
+}
+
+// Sums over the 16 lanes of each DPP row of the 32 values x[cb][r] (rows
+// 16cb + 4g + r of a column-per-lane layout), scattered: lane n ends with the
+// sums of rows 16cb + 4g + 2(n % 2) + {0, 1}, cb = 4[n >= 8] + 2[n % 8 >= 4] +
+// [n % 4 >= 2].  Four butterfly steps (mirror, half mirror, quad reversal,
+// pair swap), 30 DPP adds in all instead of 128.
+__device__ __forceinline__ f32x2 row_sums_scatter(const f32x4 x[8], int n) {
+  float a[16], b[8], c[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) a[4 * k + r] = rs_step<0x140>(x[k][r], x[k + 4][r], n >= 8);
+#pragma unroll
+  for (int k = 0; k < 2; ++k)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) b[4 * k + r] = rs_step<0x141>(a[4 * k + r], a[4 * (k + 2) + r], (n & 7) >= 4);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) c[r] = rs_step<0x1B>(b[r], b[4 + r], (n & 3) >= 2);
+  return f32x2{rs_step<0xB1>(c[0], c[2], n & 1), rs_step<0xB1>(c[1], c[3], n & 1)};
+}
+
 // One chunk's inputs as loaded: each wave loads its own 32-token slice of its
 // 16 channels (value columns), 16 bytes per lane and tensor: bf16 tensors as
 // token L / 2, columns 8 (L % 2) .. +7; the gates as tokens L / 4 and 16 + L / 4,
@@ -665,13 +694,17 @@ __global__ __launch_bounds__(NT, 1) void bwd_chunk_kernel(
     }
   };
   u32x2 Scn[8], Tn;
-  auto fetch2 = [&](int mm, const Ln& L) {
-    fetch(mm, true, L);
+  // the next chunk's state and T, in two batches (the inputs come first)
+  auto fetch_s = [&](int mm, int c0, const Ln& L) {
 #pragma unroll
-    for (int cb = 0; cb < 8; ++cb) Scn[cb] = *slot(mm, cb, L);
-    Tn = *tslot(mm);
+    for (int cb = c0; cb < c0 + 4; ++cb) Scn[cb] = *slot(mm, cb, L);
+    if (c0) Tn = *tslot(mm);
   };
-  if (nc > 0) fetch2(nc - 1, ln);
+  if (nc > 0) {
+    fetch(nc - 1, true, ln);
+    fetch_s(nc - 1, 0, ln);
+    fetch_s(nc - 1, 4, ln);
+  }
   for (int m = nc - 1; m >= 0; --m) {
     const int L = clen(m);
     const size_t tok0 = t0 + (size_t)BC * m;
@@ -688,21 +721,23 @@ __global__ __launch_bounds__(NT, 1) void bwd_chunk_kernel(
     prep_store(lds, SET0, x, bm, er, dl, scale, true, ln);
     __syncthreads();   // #1: the chunk's operands, T
     ln = fresh();
-    if (m > 0) fetch2(m - 1, ln);
+    if (m > 0) fetch(m - 1, true, ln);
     if (m + 1 < nc) finish_rows(m + 1, ln);
     // dS_m = Diag(e^{b_L - r}) dS;  S_m = Diag(e^r) S_c to R ([value][channel]);
     // sum_v dS_m S_m over the lane's columns into the partials (the decay of
     // the incoming state over the chunk, part of every token's dlog alpha)
+    {
+      f32x4 pr[8];
 #pragma unroll
-    for (int cb = 0; cb < 8; ++cb) {
-      dS[cb] *= *(const LDS f32x4*)(DL + 16 * cb + 4 * ln.g);
-      const f32x4 sm = unpack4(Sc[cb]) * *(const LDS f32x4*)(ER + 16 * cb + 4 * ln.g);
-      st_t((lb)(lds + O_R), LR, 16 * ln.w, 16 * cb, sm, ln);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float s = row_sum16(dS[cb][r] * sm[r]);
-        if (ln.n == 0) RP[ln.w * DD + 16 * cb + 4 * ln.g + r] = s;
+      for (int cb = 0; cb < 8; ++cb) {
+        dS[cb] *= *(const LDS f32x4*)(DL + 16 * cb + 4 * ln.g);
+        const f32x4 sm = unpack4(Sc[cb]) * *(const LDS f32x4*)(ER + 16 * cb + 4 * ln.g);
+        st_t((lb)(lds + O_R), LR, 16 * ln.w, 16 * cb, sm, ln);
+        pr[cb] = dS[cb] * sm;
       }
+      const f32x2 rs = row_sums_scatter(pr, ln.n);
+      const int cb = 4 * (ln.n >= 8) + 2 * ((ln.n & 7) >= 4) + ((ln.n & 3) >= 2);
+      *(LDS f32x2*)(RP + ln.w * DD + 16 * cb + 4 * ln.g + 2 * (ln.n & 1)) = rs;
     }
     if (ln.w < 6) tile_a(lds, SET0, ln.w >= 3, false, ln.w % 3, ln);
     // dE = KI dS_m (+ Aqk^T dO below), own value columns
@@ -760,6 +795,7 @@ __global__ __launch_bounds__(NT, 1) void bwd_chunk_kernel(
     }
     __syncthreads();   // #3: -dE, E
     ln = fresh();
+    if (m > 0) fetch_s(m - 1, 0, ln);
     // own key channels: dW = -dE S_m^T, dY_k = T^T dW, dKG = beta dY_k, dbeta += dY_k . KG
     f32x4 dKG[2], dYk[2];
     {
@@ -825,6 +861,7 @@ __global__ __launch_bounds__(NT, 1) void bwd_chunk_kernel(
     }
     __syncthreads();   // #5: dY_k, dS_m
     ln = fresh();
+    if (m > 0) fetch_s(m - 1, 4, ln);
     if (ln.w < 3) {
       // dL = -(dY_v U^T + dY_k W^T) (strict lower); dbeta += dL . A; dA = Diag(beta) dL
       const int I = tile_I(ln.w), J = tile_J(ln.w);
