@@ -326,7 +326,15 @@ int kda_decode_step_fused(const void* q, const void* k, const void* v, const flo
  * backward; chunkwise KDA is the training form ("Kimi Unveils Delta Attention
  * and K3 Architecture Updates", section 6), so this is the reverse-mode
  * derivative of the recurrence of section 4 (forget, predict, correct, write,
- * read after the write) for L(out, S_final):
+ * read after the write) for L(out, S_final).
+ *
+ * bf16 I/O at d_k = d_v = 128 runs it in the chunkwise form of section 6 on
+ * MFMA (32-token chunks: a forward sweep stores each chunk's state, then a
+ * reverse sweep takes every gradient contraction as a matrix product; bf16
+ * operands, fp32 accumulation and fp32 state and gradient carries).  A chain
+ * with a chunk half whose log decay exceeds 76 in some key channel (log alpha
+ * below about -4.7 on average over 16 tokens) is redone by the token loop.
+ * Every other case runs the token loop, fp32 throughout.
  *
  *  inputs     q, k, v, log_alpha, beta, S0, cu_seqlens, N, T, H, d_k, d_v,
  *             scale, io_dtype, per_head_gate: exactly as given to the forward
@@ -340,8 +348,11 @@ int kda_decode_step_fused(const void* q, const void* k, const void* v, const flo
  *  dbeta      [rows, H] fp32
  *  dS0        dL/dS0 [N, H, d_k, d_v] fp32, or NULL (not written)
  *  workspace  device memory of at least kda_backward_workspace_size() bytes,
- *             16-byte aligned, overlapping nothing else; it holds the state
- *             at the start of every 8-token block and v - p of every token, and is clobbered
+ *             16-byte aligned, overlapping nothing else, clobbered.  It holds
+ *             one flag per chain, then either every 32-token chunk's state
+ *             and triangular-solve factors in bf16 (the chunkwise form) or,
+ *             for the token loop, the state at the start of every 8-token
+ *             block and v - p of every token
  *
  * Every gradient is written in full (rows of empty sequences have none).  No
  * output may overlap an input, another output or the workspace.  d_k and d_v
