@@ -101,6 +101,7 @@ constexpr int O_GP = O_DBP + NDBP * 128;   // f32[8][32] per-token dlog alpha pa
 constexpr int O_FLAG = O_GP + 1024;
 constexpr int LDS_BYTES = O_FLAG + 16;
 static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+static_assert((KDA_LPT_MAX + 1) * 4 <= SZ_T, "length ranking in the E buffer");
 
 // One chunk's operand buffers.  The reverse sweep uses set 0; the forward
 // sweep alternates set 0 with buffers it has no other use for, so that the
@@ -550,7 +551,27 @@ __global__ __launch_bounds__(NT, 1) void bwd_chunk_kernel(
   extern __shared__ __attribute__((aligned(16))) char lds_raw[];
   LDS char* lds = (LDS char*)lds_raw;
   Ln ln = fresh();
-  const int h = blockIdx.x % H, sq = blockIdx.x / H;
+  const int h = blockIdx.x % H;
+  int sq = blockIdx.x / H;
+  // Packed sequences: workgroup b takes head b % H of the (b / H)-th longest
+  // sequence (ties by index; ranked in LDS, up to KDA_LPT_MAX sequences), so
+  // that long chains start first.
+  if (cu && (int)(gridDim.x / H) <= KDA_LPT_MAX) {
+    const int N = gridDim.x / H;
+    LDS int* lens = (LDS int*)(lds + O_E);
+    LDS int* pick = lens + KDA_LPT_MAX;
+    for (int m = threadIdx.x; m < N; m += NT) lens[m] = cu[m + 1] - cu[m];
+    __syncthreads();
+    for (int m = threadIdx.x; m < N; m += NT) {
+      const int lm = lens[m];
+      int rank = 0;
+      for (int j = 0; j < N; ++j) rank += (lens[j] > lm) || (lens[j] == lm && j < m);
+      if (rank == sq) *pick = m;
+    }
+    __syncthreads();
+    sq = *pick;
+    __syncthreads();   // the LDS is the kernel's from here on
+  }
   const int nh = sq * H + h;
   size_t t0;
   int len;
