@@ -358,29 +358,72 @@ __device__ __forceinline__ bool prefix(const Ch& x, f32x4 bm[2], float& er, floa
   return bad;
 }
 
-// T = (I + N)^{-1}, N = Diag(beta) A, in fp32 by one wave, from N^T (strictly
-// upper, [32][LA] fp32 in LDS).  Lanes with g even take column n of T_00,
-// lanes with g odd column n of T_11, each with the whole column in registers
-// (forward substitution with no lane exchange; the second copy of every
-// column costs nothing), updating every later row as soon as a row is final.
-// Then T_10 = -T_11 X, X = N_10 T_00: X by the T_00 lanes (eight rows each)
-// into the unused upper-right block of the fp32 buffer, T_10 by every lane
-// (rows 4g .. 4g+3 of column n); the exchange stays inside the wave.  Writes
-// T^T and (T Diag(beta))^T as bf16 into the set's buffers.
-__device__ __forceinline__ void solve_full(LDS char* lds, Set st, const Ln& ln) {
-  const LDS float* Nt = (const LDS float*)(lds + O_A);
+// Lower-triangle 16x16 tiles of a 32x32 matrix: (0,0), (1,0), (1,1).
+__device__ __forceinline__ int tile_I(int t) { return t == 0 ? 0 : 1; }
+__device__ __forceinline__ int tile_J(int t) { return t == 2 ? 1 : 0; }
+
+// The WY inverse of one chunk on one wave, fp32: N = Diag(beta) A with
+// A = strict_tril(KG KI^T), T = (I + N)^{-1}.
+//  * The three lower 16x16 tiles of A share their operand reads; N^T goes to
+//    LDS ([j][i], fp32).
+//  * Diagonal blocks by forward substitution: lanes with g even take column n
+//    of T_00, lanes with g odd column n of T_11, the whole column in
+//    registers, every later row updated as soon as a row is final.  The rows
+//    of N^T are read three rows ahead of their use (the scheduling fences keep
+//    the compiler from sinking the reads back), so the LDS latency stays off
+//    the substitution's chain.
+//  * X = N_10 T_00 and T_10 = -T_11 X as fp32 MFMAs (16x16x4, k step r takes
+//    matrix index 4g + r): every operand is one LDS read or the lane's own
+//    accumulator register.
+// Writes T^T and (T Diag(beta))^T as bf16 into the set's buffers.
+__device__ __forceinline__ void solve_chunk(LDS char* lds, Set st, const Ln& ln) {
+  LDS float* Nt = (LDS float*)(lds + O_A);
   LDS float* Tf = (LDS float*)(lds + O_T);
   const LDS float* beta = (const LDS float*)(lds + st.beta);
+  {
+    f32x4 a[3] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f},
+                  f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+      const bf16x8 g0 = rd_tr((lb)(lds + st.kg), LT, 32 * kc, 0, ln);
+      const bf16x8 g1 = rd_tr((lb)(lds + st.kg), LT, 32 * kc, 16, ln);
+      const bf16x8 i0 = rd_tr((lb)(lds + st.ki), LT, 32 * kc, 0, ln);
+      const bf16x8 i1 = rd_tr((lb)(lds + st.ki), LT, 32 * kc, 16, ln);
+      a[0] = mma(g0, i0, a[0]);
+      a[1] = mma(g1, i0, a[1]);
+      a[2] = mma(g1, i1, a[2]);
+    }
+#pragma unroll
+    for (int t = 0; t < 3; ++t) {
+      const int I = tile_I(t), J = tile_J(t);
+      f32x4 acc = a[t];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[r] = (I > J || 4 * ln.g + r > ln.n) ? acc[r] : 0.f;
+      const f32x4 bt = *(const LDS f32x4*)(beta + 16 * I + 4 * ln.g);
+      *(LDS f32x4*)(Nt + (16 * J + ln.n) * LA + 16 * I + 4 * ln.g) = acc * bt;
+    }
+  }
   const int b = ln.g & 1, off = 16 * b, j = ln.n;
+  const LDS float* Nb = Nt + off * LA + off;   // row m: column m of N_bb
+  f32x4 R[15][4];
+  auto ldrow = [&](int m) {
+#pragma unroll
+    for (int q = (m + 1) >> 2; q < 4; ++q) R[m][q] = *(const LDS f32x4*)(Nb + m * LA + 4 * q);
+  };
   float x[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) x[i] = (i == j) ? 1.f : 0.f;
+  ldrow(0);
+  ldrow(1);
+  ldrow(2);
 #pragma unroll
   for (int m = 0; m < 15; ++m) {
-    const LDS float* Nm = Nt + (off + m) * LA + off;
+    if (m + 3 < 15) ldrow(m + 3);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = m + 1; i < 16; ++i) x[i] -= Nm[i] * x[m];
+    for (int i = m + 1; i < 16; ++i) x[i] -= R[m][i >> 2][i & 3] * x[m];
   }
+  __builtin_amdgcn_sched_barrier(0);
   if (ln.g < 2) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) Tf[(off + i) * LA + off + j] = x[i];
@@ -394,25 +437,14 @@ __device__ __forceinline__ void solve_full(LDS char* lds, Set st, const Ln& ln) 
                                     pack_bf16x2(bj * x[e + 2], bj * x[e + 3])};
     }
   }
-  if (b == 0) {
-    const int i0 = 4 * ln.g;   // rows 0..7 (g = 0) or 8..15 (g = 2) of X
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  f32x4 X{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int m = 0; m < 16; ++m) {
-      const LDS float* Nm = Nt + m * LA + 16 + i0;
-#pragma unroll
-      for (int ii = 0; ii < 8; ++ii) acc[ii] += Nm[ii] * x[m];
-    }
-#pragma unroll
-    for (int ii = 0; ii < 8; ++ii) Tf[(i0 + ii) * LA + 16 + j] = acc[ii];
-  }
+  for (int r = 0; r < 4; ++r)
+    X = mma4(Nt[(4 * ln.g + r) * LA + 16 + ln.n], Tf[(4 * ln.g + r) * LA + ln.n], X);
+  const f32x4 t11 = *(const LDS f32x4*)(Tf + (16 + ln.n) * LA + 16 + 4 * ln.g);
   f32x4 t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int m = 0; m < 16; ++m) {
-    const float xm = Tf[m * LA + 16 + j];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) t[r] -= Tf[(16 + 4 * ln.g + r) * LA + 16 + m] * xm;
-  }
+  for (int r = 0; r < 4; ++r) t = mma4(-t11[r], X[r], t);
   st_t((lb)(lds + st.tt), LT, 0, 16, t, ln);
   st_t((lb)(lds + st.tt + SZ_S), LT, 0, 16, t * beta[j], ln);
 }
@@ -436,10 +468,6 @@ __device__ __forceinline__ void store_tile(Rsrc rv, LDS float* stg, const f32x4 
                                            4 * (uint32_t)(16 * hh * H * DD), 0);
   }
 }
-
-// Lower-triangle 16x16 tiles of a 32x32 matrix: (0,0), (1,0), (1,1).
-__device__ __forceinline__ int tile_I(int t) { return t == 0 ? 0 : 1; }
-__device__ __forceinline__ int tile_J(int t) { return t == 2 ? 1 : 0; }
 
 // Writes every input prep product of one chunk: KG, KI, V (and, reverse sweep,
 // QG and dO) as [channel][token] bf16, e^r and e^{b_L - r} of the lane's channel.
@@ -470,10 +498,8 @@ __device__ __forceinline__ void prep_store(LDS char* lds, Set st, const Ch& x,
 }
 
 // Tile t (0..2) of A = strict_tril(KG KI^T) or, qk, of Aqk = tril(QG KI^T)
-// (bf16, transposed).  A is stored fp32, row-major (reverse sweep, for dbeta)
-// or, nt, as N^T = (Diag(beta) A)^T for the solve.
-__device__ __forceinline__ void tile_a(LDS char* lds, Set st, bool qk, bool nt, int t,
-                                       const Ln& ln) {
+// (bf16, transposed).  A is stored fp32, row-major, for dbeta.
+__device__ __forceinline__ void tile_a(LDS char* lds, Set st, bool qk, int t, const Ln& ln) {
   const int I = tile_I(t), J = tile_J(t);
   const lb X = (lb)(lds + (qk ? O_QG : st.kg));
   f32x4 acc{0.f, 0.f, 0.f, 0.f};
@@ -488,9 +514,6 @@ __device__ __forceinline__ void tile_a(LDS char* lds, Set st, bool qk, bool nt, 
   }
   if (qk) {
     st_t((lb)(lds + O_AQ), LT, 16 * J, 16 * I, acc, ln);
-  } else if (nt) {
-    const f32x4 bt = *(const LDS f32x4*)((const LDS float*)(lds + st.beta) + 16 * I + 4 * ln.g);
-    *(LDS f32x4*)((LDS float*)(lds + O_A) + (16 * J + ln.n) * LA + 16 * I + 4 * ln.g) = acc * bt;
   } else {
     LDS float* A = (LDS float*)(lds + O_A);
 #pragma unroll
@@ -638,12 +661,8 @@ __global__ __launch_bounds__(NT, 1) void bwd_chunk_kernel(
     if (prefix(x, bm, er, dl, ll)) *FLAG = 1;
     prep_store(lds, st, x, bm, er, dl, scale, false, ll);
   };
-  // N^T and T of the chunk whose operands are in set st, on the last wave
-  auto solve1 = [&](Set st, const Ln& ll) {
-#pragma unroll
-    for (int t = 0; t < 3; ++t) tile_a(lds, st, false, true, t, ll);
-    solve_full(lds, st, ll);
-  };
+  // T of the chunk whose operands are in set st, on the last wave
+  auto solve1 = [&](Set st, const Ln& ll) { solve_chunk(lds, st, ll); };
   if (nc > 0) {
     prep1(0, SET0, ln);
     __syncthreads();
@@ -760,7 +779,7 @@ __global__ __launch_bounds__(NT, 1) void bwd_chunk_kernel(
       const int cb = 4 * (ln.n >= 8) + 2 * ((ln.n & 7) >= 4) + ((ln.n & 3) >= 2);
       *(LDS f32x2*)(RP + ln.w * DD + 16 * cb + 4 * ln.g + 2 * (ln.n & 1)) = rs;
     }
-    if (ln.w < 6) tile_a(lds, SET0, ln.w >= 3, false, ln.w % 3, ln);
+    if (ln.w < 6) tile_a(lds, SET0, ln.w >= 3, ln.w % 3, ln);
     // dE = KI dS_m (+ Aqk^T dO below), own value columns
     f32x4 dE[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
