@@ -42,15 +42,16 @@
 //    elements (tokens 4g + r and 16 + 4g + r, channel 16w + l%16, g = lane/16)
 //    are exactly its accumulator elements of the latter, so the epilogue needs
 //    no exchange;
-//  * the in-chunk prefix sums (b) and suffix sums (dlog alpha) are fp32 MFMAs
-//    against triangular ones matrices built in registers;
+//  * the in-chunk prefix sums (b) are running sums in registers joined across
+//    lane groups by gfx950's permlane swaps; the suffix sums (dlog alpha) are
+//    fp32 MFMAs against triangular ones matrices built in registers;
 //  * operands go through LDS transposed ([channel][token]), the accumulator's
 //    natural 8-byte store; contractions over tokens read rows, contractions
 //    over channels use the gfx950 transpose read (ds_read_b64_tr_b16); S and
 //    dS in registers serve as 32-deep operands with the k index relabelled
 //    (two stacked 16-row accumulator tiles);
-//  * T is formed in fp32: the two 16x16 diagonal blocks by forward
-//    substitution (one wave each), then T_10 = -T_11 L_10 T_00.
+//  * T is formed in fp32 on one wave: the two 16x16 diagonal blocks by forward
+//    substitution (a lane group each), then T_10 = -T_11 N_10 T_00 as MFMAs.
 #include "common.h"
 
 namespace kda {
@@ -200,9 +201,6 @@ __device__ __forceinline__ u32x2 ld_raw(const LDS uint16_t* Xt, int ld, int col0
                                         const Ln& L) {
   return *(const LDS u32x2*)(Xt + (col0 + L.n) * ld + row0 + 4 * L.g);
 }
-__device__ __forceinline__ float shfl(float x, int src) {
-  return __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(x)));
-}
 
 // One reduce-scatter step inside 16-lane rows: lanes with `hi` keep b, the
 // others a, each adding the partner's copy (DPP pattern CTRL pairs every lane
@@ -331,26 +329,49 @@ __device__ __forceinline__ Ch unstage(LDS char* lds, const In& x, bool rev, cons
   return c;
 }
 
-// b - r for the lane's eight elements (prefix sums as MFMAs: lane group g
-// supplies token 4g + s at step s, the ones matrix is formed per lane), and
-// whether any lies beyond RANGE.  Also e^r and e^{b_L - r} of the lane's channel.
+// The value held by lane group g ^ 1 (g ^ 2) in the lane's column.  gfx950's
+// permlane16 (permlane32) swap, given one register as both operands, returns
+// it with rows 1 and 3 (lanes 32..63) taken from rows 0 and 2 (lanes 0..31)
+// as its first result and the converse as its second.
+__device__ __forceinline__ float from_g1(float x, const Ln& ln) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return __uint_as_float((ln.g & 1) ? r[0] : r[1]);
+}
+__device__ __forceinline__ float from_g2(float x, const Ln& ln) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float((ln.g & 2) ? r[0] : r[1]);
+}
+
+// b - r for the lane's eight elements and whether any lies beyond RANGE, with
+// r = b_15; also e^r and e^{b_L - r} of the lane's channel.  The in-chunk
+// prefix sums: running sums over the lane's four tokens, then over the four
+// lane groups by two swaps (a pair's sum, then the other pair's).
 __device__ __forceinline__ bool prefix(const Ch& x, f32x4 bm[2], float& er, float& dl,
                                        const Ln& ln) {
-  f32x4 b0{0.f, 0.f, 0.f, 0.f}, b1{0.f, 0.f, 0.f, 0.f};
+  f32x4 p[2];
+  float ex[2], all[2];
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    const float a = (4 * ln.g + s <= ln.n) ? 1.f : 0.f;
-    b0 = mma4(a, x.gt[0][s], b0);
-    b1 = mma4(1.f, x.gt[0][s], b1);
-    b1 = mma4(a, x.gt[1][s], b1);
+  for (int I = 0; I < 2; ++I) {
+    p[I][0] = x.gt[I][0];
+#pragma unroll
+    for (int s = 1; s < 4; ++s) p[I][s] = p[I][s - 1] + x.gt[I][s];
+    const float t = p[I][3];
+    const float o1 = from_g1(t, ln);
+    const float pair = t + o1;                  // groups 2h and 2h + 1
+    const float lo = (ln.g & 1) ? o1 : 0.f;     // group g - 1 of the pair
+    const float o2 = from_g2(pair, ln);
+    ex[I] = (ln.g & 2) ? o2 + lo : lo;          // groups before g
+    all[I] = pair + o2;                         // all sixteen tokens
   }
-  const float r = shfl(b0[3], 48 + ln.n);    // b_15 of the lane's channel
-  const float bl = shfl(b1[3], 48 + ln.n);   // b_31
+  const float r = all[0];                       // b_15
+  const float bl = all[0] + all[1];             // b_31
   bool bad = false;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    bm[0][e] = b0[e] - r;
-    bm[1][e] = b1[e] - r;
+    bm[0][e] = (p[0][e] + ex[0]) - r;
+    bm[1][e] = ((p[1][e] + ex[1]) + all[0]) - r;
     bad |= !(fabsf(bm[0][e]) <= RANGE) || !(fabsf(bm[1][e]) <= RANGE);
   }
   er = __expf(r);
