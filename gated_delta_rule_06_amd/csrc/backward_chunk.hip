@@ -42,9 +42,9 @@
 //    elements (tokens 4g + r and 16 + 4g + r, channel 16w + l%16, g = lane/16)
 //    are exactly its accumulator elements of the latter, so the epilogue needs
 //    no exchange;
-//  * the in-chunk prefix sums (b) are running sums in registers joined across
-//    lane groups by gfx950's permlane swaps; the suffix sums (dlog alpha) are
-//    fp32 MFMAs against triangular ones matrices built in registers;
+//  * the in-chunk prefix sums (b) and the suffix sums of dlog alpha are
+//    running sums in registers joined across lane groups by gfx950's permlane
+//    swaps;
 //  * operands go through LDS transposed ([channel][token]), the accumulator's
 //    natural 8-byte store; contractions over tokens read rows, contractions
 //    over channels use the gfx950 transpose read (ds_read_b64_tr_b16); S and
@@ -565,21 +565,36 @@ __device__ __forceinline__ void tiles_uw(LDS char* lds, Set st, f32x4 U[2], bool
 }
 
 // y_t = sum_{i >= t} x_i + sum_{i < t} z_i over the chunk's tokens
-// (accumulator layout), as MFMAs against triangular ones matrices.
+// (accumulator layout): running sums over the lane's four tokens (x from the
+// last, z exclusive from the first), joined across the four lane groups by two
+// swaps and across the chunk's halves by the half totals.
 __device__ __forceinline__ void suffix_prefix(const f32x4 x[2], const f32x4 z[2], f32x4 y[2],
                                               const Ln& ln) {
-  y[0] = f32x4{0.f, 0.f, 0.f, 0.f};
-  y[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 sx[2], pz[2];
+  float xa[2], zb[2], xall[2], zall[2];
+#pragma unroll
+  for (int I = 0; I < 2; ++I) {
+    sx[I][3] = x[I][3];
+#pragma unroll
+    for (int s = 2; s >= 0; --s) sx[I][s] = sx[I][s + 1] + x[I][s];
+    pz[I][0] = 0.f;
+#pragma unroll
+    for (int s = 1; s < 4; ++s) pz[I][s] = pz[I][s - 1] + z[I][s - 1];
+    const float tx = sx[I][0], tz = pz[I][3] + z[I][3];
+    const float ox = from_g1(tx, ln), oz = from_g1(tz, ln);
+    const float px = tx + ox, qz = tz + oz;          // pair sums
+    const float hx = (ln.g & 1) ? 0.f : ox;          // group g + 1 of the pair
+    const float lz = (ln.g & 1) ? oz : 0.f;          // group g - 1 of the pair
+    const float o2x = from_g2(px, ln), o2z = from_g2(qz, ln);
+    xa[I] = (ln.g & 2) ? hx : o2x + hx;              // x over the groups after g
+    zb[I] = (ln.g & 2) ? o2z + lz : lz;              // z over the groups before g
+    xall[I] = px + o2x;
+    zall[I] = qz + o2z;
+  }
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
-    const float a = (4 * ln.g + s >= ln.n) ? 1.f : 0.f;
-    const float c = 1.f - a;   // 4g + s < n
-    y[0] = mma4(a, x[0][s], y[0]);
-    y[0] = mma4(1.f, x[1][s], y[0]);
-    y[1] = mma4(a, x[1][s], y[1]);
-    y[0] = mma4(c, z[0][s], y[0]);
-    y[1] = mma4(1.f, z[0][s], y[1]);
-    y[1] = mma4(c, z[1][s], y[1]);
+    y[0][s] = ((sx[0][s] + xa[0]) + xall[1]) + (pz[0][s] + zb[0]);
+    y[1][s] = (sx[1][s] + xa[1]) + ((pz[1][s] + zb[1]) + zall[0]);
   }
 }
 
