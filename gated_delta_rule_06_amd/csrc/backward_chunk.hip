@@ -114,12 +114,17 @@ constexpr Set SET0{O_KG, O_KI, O_V, O_BETA, O_ER, O_DL, O_TT};
 constexpr Set SET1{O_QG, O_DO, O_NU, O_DBP, O_DBP + 128, O_DBP + 640, O_DAQ};
 static_assert(O_TB == O_TT + SZ_S && O_DA == O_DAQ + SZ_S, "T buffer pairs");
 static_assert(O_NU == O_NW + SZ_T && NW * BC * 20 * 4 <= 2 * SZ_T, "store staging");
-// Per-wave staging of a chunk's loaded inputs (E, -dE and R are free whenever
-// a chunk's inputs are unpacked): four bf16 [32][16] tiles, then the fp32
-// gates as [32][20].
-constexpr int STG_BYTES = 4 * BC * 16 * 2 + BC * 20 * 4;
+// Shared staging of a chunk's loaded inputs (E, -dE and R are free from the
+// time a chunk's inputs are staged until they are unpacked): q, k, v and dO as
+// bf16 [token][LS], then the gates as fp32 [token][LG] (a per-head gate:
+// f32[32]).  With 288-byte rows the four rows of a transpose read fall in
+// distinct banks.
+constexpr int LS = DD + 16;
+constexpr int LG = DD + 4;
+constexpr int STG_T = BC * LS * 2;
+constexpr int O_SG = O_E + 4 * STG_T;
 static_assert(O_NDE == O_E + SZ_T && O_R == O_NDE + SZ_T &&
-              NW * STG_BYTES <= 2 * SZ_T + DD * LR * 2, "input staging");
+              O_SG + BC * LG * 4 <= O_R + DD * LR * 2, "input staging");
 static_assert(640 + 512 <= NDBP * 128, "second set's small buffers");
 
 typedef short i16x8 __attribute__((ext_vector_type(8)));
@@ -265,6 +270,10 @@ __device__ __forceinline__ void st_f32(Rsrc r, uint32_t off, uint32_t soff, floa
   __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, off, soff, 0);
 }
 
+// A chunk's inputs, whole rows at a time: wave w loads tokens 4w .. 4w+3,
+// lane l 16 bytes of token 4w + l/16 (the fp32 gates in two loads, the row's
+// first and second halves), so that a load covers four whole rows.  A
+// per-head gate is loaded by wave 0 alone.
 template <bool SG>
 __device__ __forceinline__ void load_in(In& x, const uint16_t* q, const uint16_t* k,
                                         const uint16_t* v, const uint16_t* dout, const float* g,
@@ -272,59 +281,64 @@ __device__ __forceinline__ void load_in(In& x, const uint16_t* q, const uint16_t
   const Rsrc rq = chunk_view(q, tok0, L, H, h, DD, 2), rk = chunk_view(k, tok0, L, H, h, DD, 2);
   const Rsrc rv = chunk_view(v, tok0, L, H, h, DD, 2), ro = chunk_view(dout, tok0, L, H, h, DD, 2);
   const Rsrc rg = chunk_view(g, tok0, L, H, h, SG ? 1 : DD, 4);
-  const uint32_t ob = 2 * (uint32_t)((ln.l >> 1) * H * DD + 16 * ln.w + 8 * (ln.l & 1));
+  const uint32_t row = 4 * ln.w + (ln.l >> 4), c = ln.l & 15;
+  const uint32_t ob = 2 * (row * H * DD + 8 * c);
   const u32x4 z{0u, 0u, 0u, 0u};
   x.q = rev ? __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, ob, 0, 0)) : z;
   x.k = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, ob, 0, 0));
   x.v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, ob, 0, 0));
   x.o = rev ? __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ro, ob, 0, 0)) : z;
+  x.g0 = f32x4{0.f, 0.f, 0.f, 0.f};
+  x.g1 = f32x4{0.f, 0.f, 0.f, 0.f};
   if (SG) {
-    x.g0 = f32x4{0.f, 0.f, 0.f, 0.f};
-    x.g0[0] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rg, 4 * (uint32_t)(ln.l * H), 0, 0));
-    x.g1 = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (ln.w == 0)
+      x.g0[0] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rg, 4 * (uint32_t)(ln.l * H), 0, 0));
   } else {
-    const uint32_t og = 4 * (uint32_t)((ln.l >> 2) * H * DD + 16 * ln.w + 4 * (ln.l & 3));
+    const uint32_t og = 4 * (row * H * DD + 4 * c);
     x.g0 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rg, og, 0, 0));
-    x.g1 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rg, og, 4 * (uint32_t)(16 * H * DD), 0));
+    x.g1 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rg, og, 256, 0));
   }
 }
 
-// The loaded inputs into the accumulator layout through the wave's own
-// staging area (only this wave touches it, so no barrier): bf16 tiles as
-// [token][16] and read back with the transpose read (lane n of group g gets
-// tokens 4g .. 4g+3 of column n), gates as [token][20] fp32.
+// The loaded rows into the shared staging.  A barrier must separate this from
+// the unpacking reads, and those from the next staging.
 template <bool SG>
-__device__ __forceinline__ Ch unstage(LDS char* lds, const In& x, bool rev, const Ln& ln) {
-  LDS char* stg = lds + O_E + ln.w * STG_BYTES;
-  const int tb = (ln.l >> 1) * 32 + (ln.l & 1) * 16;   // bytes
-  *(LDS u32x4*)(stg + 1024 + tb) = x.k;
-  *(LDS u32x4*)(stg + 2048 + tb) = x.v;
-  if (rev) {
-    *(LDS u32x4*)(stg + tb) = x.q;
-    *(LDS u32x4*)(stg + 3072 + tb) = x.o;
-  }
-  LDS float* sg = (LDS float*)(stg + 4096);
+__device__ __forceinline__ void stage(LDS char* lds, const In& x, bool rev, const Ln& ln) {
+  const int row = 4 * ln.w + (ln.l >> 4), c = ln.l & 15;
+  LDS char* s = lds + O_E + (row * LS + 8 * c) * 2;
+  if (rev) *(LDS u32x4*)(s) = x.q;
+  *(LDS u32x4*)(s + STG_T) = x.k;
+  *(LDS u32x4*)(s + 2 * STG_T) = x.v;
+  if (rev) *(LDS u32x4*)(s + 3 * STG_T) = x.o;
+  LDS float* sg = (LDS float*)(lds + O_SG);
   if (SG) {
-    if (ln.l < BC) sg[ln.l] = x.g0[0];
+    if (ln.w == 0 && ln.l < BC) sg[ln.l] = x.g0[0];
   } else {
-    *(LDS f32x4*)(sg + (ln.l >> 2) * 20 + 4 * (ln.l & 3)) = x.g0;
-    *(LDS f32x4*)(sg + (16 + (ln.l >> 2)) * 20 + 4 * (ln.l & 3)) = x.g1;
+    *(LDS f32x4*)(sg + row * LG + 4 * c) = x.g0;
+    *(LDS f32x4*)(sg + row * LG + 64 + 4 * c) = x.g1;
   }
+}
+
+// The wave's columns of the staged chunk in the accumulator layout: the
+// transpose read gives lane n of group g tokens 4g .. 4g+3 of column 16w + n.
+template <bool SG>
+__device__ __forceinline__ Ch unstage(const LDS char* lds, bool rev, const Ln& ln) {
+  const LDS float* sg = (const LDS float*)(lds + O_SG);
   Ch c;
 #pragma unroll
   for (int I = 0; I < 2; ++I) {
-    const int e = (16 * I + 4 * ln.g + (ln.n >> 2)) * 16 + 4 * (ln.n & 3);   // elements
-    auto rd = [&](int base) {
+    const int e = (16 * I + 4 * ln.g + (ln.n >> 2)) * LS + 16 * ln.w + 4 * (ln.n & 3);
+    auto rd = [&](int t) {
       return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                                           (LDS i16x4*)((LDS uint16_t*)(stg + base) + e)));
+                                           (LDS i16x4*)((const LDS uint16_t*)(lds + O_E + t * STG_T) + e)));
     };
-    c.k[I] = rd(1024);
-    c.v[I] = rd(2048);
+    c.k[I] = rd(1);
+    c.v[I] = rd(2);
     c.q[I] = rev ? rd(0) : u32x2{0u, 0u};
-    c.o[I] = rev ? rd(3072) : u32x2{0u, 0u};
+    c.o[I] = rev ? rd(3) : u32x2{0u, 0u};
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      c.gt[I][r] = SG ? sg[16 * I + 4 * ln.g + r] : sg[(16 * I + 4 * ln.g + r) * 20 + ln.n];
+      c.gt[I][r] = SG ? sg[16 * I + 4 * ln.g + r] : sg[(16 * I + 4 * ln.g + r) * LG + 16 * ln.w + ln.n];
   }
   return c;
 }
@@ -689,7 +703,7 @@ __global__ __launch_bounds__(NT, 1) void bwd_chunk_kernel(
   if (nc > 0) fetch(0, false, ln);
   // chunk mm's operands into set st from the prefetched inputs, then the next fetch
   auto prep1 = [&](int mm, Set st, const Ln& ll) {
-    const Ch x = unstage<SG>(lds, xn, false, ll);
+    const Ch x = unstage<SG>(lds, false, ll);
     if (ll.w == 0 && ll.l < BC) ((LDS float*)(lds + st.beta))[ll.l] = bn;
     if (mm + 1 < nc) fetch(mm + 1, false, ll);
     f32x4 bm[2];
@@ -700,10 +714,14 @@ __global__ __launch_bounds__(NT, 1) void bwd_chunk_kernel(
   // T of the chunk whose operands are in set st, on the last wave
   auto solve1 = [&](Set st, const Ln& ll) { solve_chunk(lds, st, ll); };
   if (nc > 0) {
+    stage<SG>(lds, xn, false, ln);
+    __syncthreads();
+    ln = fresh();
     prep1(0, SET0, ln);
     __syncthreads();
     ln = fresh();
     if (ln.w == NW - 1 && !*FLAG) solve1(SET0, ln);
+    if (nc > 1) stage<SG>(lds, xn, false, ln);
     __syncthreads();
     ln = fresh();
   }
@@ -736,7 +754,8 @@ __global__ __launch_bounds__(NT, 1) void bwd_chunk_kernel(
       S[cb] = mma(rd_rowp((lb)(lds + cur.ki), LT, 16 * cb, 0, ln), eb, Sm[cb]) *
               *(const LDS f32x4*)((const LDS float*)(lds + cur.dl) + 16 * cb + 4 * ln.g);
     if (ln.w == NW - 1 && m + 1 < nc && !*FLAG) solve1(nxt, ln);
-    __syncthreads();   // #b: the next chunk's T; this chunk's buffers are free
+    if (m + 2 < nc) stage<SG>(lds, xn, false, ln);
+    __syncthreads();   // #b: the next chunk's T and staged inputs; this chunk's buffers are free
     ln = fresh();
   }
   if (*FLAG) {
@@ -780,11 +799,14 @@ __global__ __launch_bounds__(NT, 1) void bwd_chunk_kernel(
     fetch(nc - 1, true, ln);
     fetch_s(nc - 1, 0, ln);
     fetch_s(nc - 1, 4, ln);
+    stage<SG>(lds, xn, true, ln);
+    __syncthreads();
+    ln = fresh();
   }
   for (int m = nc - 1; m >= 0; --m) {
     const int L = clen(m);
     const size_t tok0 = t0 + (size_t)BC * m;
-    const Ch x = unstage<SG>(lds, xn, true, ln);
+    const Ch x = unstage<SG>(lds, true, ln);
     const u32x2 o0 = x.o[0], o1 = x.o[1];
     if (ln.w == 0 && ln.l < BC) BETA[ln.l] = bn;
     u32x2 Sc[8];
@@ -973,6 +995,7 @@ __global__ __launch_bounds__(NT, 1) void bwd_chunk_kernel(
     }
     __syncthreads();   // #6: dA
     ln = fresh();
+    if (m > 0) stage<SG>(lds, xn, true, ln);   // E, -dE and R are done with
     {
       const bf16x8 kib = rd_row((lb)(lds + O_KI), LT, 16 * ln.w, 0, ln);
       const bf16x8 kgb = rd_row((lb)(lds + O_KG), LT, 16 * ln.w, 0, ln);
