@@ -819,17 +819,23 @@ __global__ __launch_bounds__(NT, 1) void bwd_chunk_kernel(
     prep_store(lds, SET0, x, bm, er, dl, scale, true, ln);
     __syncthreads();   // #1: the chunk's operands, T
     ln = fresh();
-    if (m > 0) fetch(m - 1, true, ln);
     if (m + 1 < nc) finish_rows(m + 1, ln);
     // dS_m = Diag(e^{b_L - r}) dS;  S_m = Diag(e^r) S_c to R ([value][channel]);
     // sum_v dS_m S_m over the lane's columns into the partials (the decay of
     // the incoming state over the chunk, part of every token's dlog alpha)
     {
-      f32x4 pr[8];
+      // every factor is read before the first store (the compiler cannot
+      // tell the stores from the reads and would otherwise wait on each)
+      f32x4 pr[8], dlf[8], erf[8];
 #pragma unroll
       for (int cb = 0; cb < 8; ++cb) {
-        dS[cb] *= *(const LDS f32x4*)(DL + 16 * cb + 4 * ln.g);
-        const f32x4 sm = unpack4(Sc[cb]) * *(const LDS f32x4*)(ER + 16 * cb + 4 * ln.g);
+        dlf[cb] = *(const LDS f32x4*)(DL + 16 * cb + 4 * ln.g);
+        erf[cb] = *(const LDS f32x4*)(ER + 16 * cb + 4 * ln.g);
+      }
+#pragma unroll
+      for (int cb = 0; cb < 8; ++cb) {
+        dS[cb] *= dlf[cb];
+        const f32x4 sm = unpack4(Sc[cb]) * erf[cb];
         st_t((lb)(lds + O_R), LR, 16 * ln.w, 16 * cb, sm, ln);
         pr[cb] = dS[cb] * sm;
       }
@@ -932,18 +938,28 @@ __global__ __launch_bounds__(NT, 1) void bwd_chunk_kernel(
     }
     __syncthreads();   // #4: S_m, -dE and dO are done with; dAqk
     ln = fresh();
+    if (m > 0) fetch(m - 1, true, ln);
 #pragma unroll
     for (int I = 0; I < 2; ++I) st_t((lb)(lds + O_NDE), LT, 16 * ln.w, 16 * I, dYk[I], ln);
     // dS_c = Diag(e^r) (dS_m + QG^T dO - W^T dE); dS_m to R for dKI
     {
       const bf16x8 ob = __builtin_bit_cast(bf16x8, u32x4{o0[0], o0[1], o1[0], o1[1]});
       const bf16x8 eb = pack8(dE[0], dE[1]);
+      // the stores first: operand reads that follow no store need not wait on one
+#pragma unroll
+      for (int cb = 0; cb < 8; ++cb) st_t((lb)(lds + O_R), LR, 16 * ln.w, 16 * cb, dS[cb], ln);
 #pragma unroll
       for (int cb = 0; cb < 8; ++cb) {
-        st_t((lb)(lds + O_R), LR, 16 * ln.w, 16 * cb, dS[cb], ln);
         dS[cb] = mma(rd_rowp((lb)(lds + O_QG), LT, 16 * cb, 0, ln), ob, dS[cb]);
         dS[cb] = mma(rd_rowp((lb)(lds + O_NW), LT, 16 * cb, 0, ln), eb, dS[cb]);
         dS[cb] *= *(const LDS f32x4*)(ER + 16 * cb + 4 * ln.g);
+      }
+      // keep the operand reads a few products ahead
+      __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
     }
     // dQG += dAqk KI; dKI = dAqk^T QG (+ dA^T KG below)
@@ -995,7 +1011,6 @@ __global__ __launch_bounds__(NT, 1) void bwd_chunk_kernel(
     }
     __syncthreads();   // #6: dA
     ln = fresh();
-    if (m > 0) stage<SG>(lds, xn, true, ln);   // E, -dE and R are done with
     {
       const bf16x8 kib = rd_row((lb)(lds + O_KI), LT, 16 * ln.w, 0, ln);
       const bf16x8 kgb = rd_row((lb)(lds + O_KG), LT, 16 * ln.w, 0, ln);
@@ -1050,6 +1065,7 @@ __global__ __launch_bounds__(NT, 1) void bwd_chunk_kernel(
           }
       }
     }
+    if (m > 0) stage<SG>(lds, xn, true, ln);   // E, -dE and R are done with
     __syncthreads();   // #7: the chunk's LDS may be rewritten
     ln = fresh();
   }
