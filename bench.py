@@ -457,7 +457,9 @@ def main():
         kda.backward(dbw["q"], dbw["k"], dbw["v"], dbw["g"], dbw["beta"], dbw["d_out"],
                      want_dS0=False, workspace=ws_bw)
 
-    bw_ms = timed_calls(bwd_call, BACKWARD_CALLS, warm=2)
+    # the engine clock is still climbing over the first few calls of a burst
+    # after the lighter legs before it (launch times fall by some 10% over six)
+    bw_ms = timed_calls(bwd_call, BACKWARD_CALLS, warm=6)
     bw_f = backward_alg_flops(P["B"], P["T"], P["H"], P["dk"], P["dv"])
     bw_b = backward_alg_bytes(P["B"], P["T"], P["H"], P["dk"], P["dv"], P["io"])
     bw_tf = bw_f / (bw_ms * 1e-3) / 1e12
