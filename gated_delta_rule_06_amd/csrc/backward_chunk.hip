@@ -410,10 +410,11 @@ __device__ __forceinline__ int tile_J(int t) { return t == 2 ? 1 : 0; }
 //  * X = N_10 T_00 and T_10 = -T_11 X as fp32 MFMAs (16x16x4, k step r takes
 //    matrix index 4g + r): every operand is one LDS read or the lane's own
 //    accumulator register.
-// Writes T^T and (T Diag(beta))^T as bf16 into the set's buffers.
-__device__ __forceinline__ void solve_chunk(LDS char* lds, Set st, const Ln& ln) {
+// Writes T^T and (T Diag(beta))^T as bf16 into the set's buffers.  The tiles
+// and the rest are separate calls, so that the forward sweep can give the
+// tiles to another wave.
+__device__ __forceinline__ void tiles_nt(LDS char* lds, Set st, const Ln& ln) {
   LDS float* Nt = (LDS float*)(lds + O_A);
-  LDS float* Tf = (LDS float*)(lds + O_T);
   const LDS float* beta = (const LDS float*)(lds + st.beta);
   {
     f32x4 a[3] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f},
@@ -438,6 +439,11 @@ __device__ __forceinline__ void solve_chunk(LDS char* lds, Set st, const Ln& ln)
       *(LDS f32x4*)(Nt + (16 * J + ln.n) * LA + 16 * I + 4 * ln.g) = acc * bt;
     }
   }
+}
+__device__ __forceinline__ void invert_nt(LDS char* lds, Set st, const Ln& ln) {
+  const LDS float* Nt = (const LDS float*)(lds + O_A);
+  LDS float* Tf = (LDS float*)(lds + O_T);
+  const LDS float* beta = (const LDS float*)(lds + st.beta);
   const int b = ln.g & 1, off = 16 * b, j = ln.n;
   const LDS float* Nb = Nt + off * LA + off;   // row m: column m of N_bb
   f32x4 R[15][4];
@@ -671,12 +677,16 @@ __global__ __launch_bounds__(NT, 1) void bwd_chunk_kernel(
   LDS float* RP = (LDS float*)(lds + O_RP);
   LDS float* GP = (LDS float*)(lds + O_GP);
   LDS int* FLAG = (LDS int*)(lds + O_FLAG);
+  LDS int* TFLAG = FLAG + 1;   // forward sweep: index of the chunk whose A tiles are in O_A
   // upper blocks of the [j][i] 32x32 buffers stay zero
   for (int e = threadIdx.x; e < 5 * 256; e += NT) {
     const int b = e >> 8, j = 16 + ((e >> 4) & 15), i = e & 15;
     ((lb)(lds + O_AQ + b * SZ_S))[j * LT + i] = 0;
   }
-  if (threadIdx.x == 0) *FLAG = 0;
+  if (threadIdx.x == 0) {
+    *FLAG = 0;
+    *TFLAG = -1;
+  }
   const int col = 16 * ln.w + ln.n;   // the lane's value column / key channel
   const size_t sbase = (size_t)nh * DD * DD;
 
@@ -712,7 +722,10 @@ __global__ __launch_bounds__(NT, 1) void bwd_chunk_kernel(
     prep_store(lds, st, x, bm, er, dl, scale, false, ll);
   };
   // T of the chunk whose operands are in set st, on the last wave
-  auto solve1 = [&](Set st, const Ln& ll) { solve_chunk(lds, st, ll); };
+  auto solve1 = [&](Set st, const Ln& ll) {
+    tiles_nt(lds, st, ll);
+    invert_nt(lds, st, ll);
+  };
   if (nc > 0) {
     stage<SG>(lds, xn, false, ln);
     __syncthreads();
@@ -741,6 +754,13 @@ __global__ __launch_bounds__(NT, 1) void bwd_chunk_kernel(
     if (m + 1 < nc) prep1(m + 1, nxt, ln);
     __syncthreads();   // #a: -W; the next chunk's operands
     ln = fresh();
+    // the next chunk's A tiles on the second-to-last wave before its state update,
+    // published to the last wave, which inverts after its own update
+    const bool solve = m + 1 < nc && !*FLAG;
+    if (ln.w == NW - 2 && solve) {
+      tiles_nt(lds, nxt, ln);
+      __hip_atomic_store(TFLAG, m + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
     // E = U - W S_m (own value columns); S_{c+1} = Diag(e^{b_L - r}) (S_m + KI^T E)
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
@@ -753,7 +773,15 @@ __global__ __launch_bounds__(NT, 1) void bwd_chunk_kernel(
     for (int cb = 0; cb < 8; ++cb)
       S[cb] = mma(rd_rowp((lb)(lds + cur.ki), LT, 16 * cb, 0, ln), eb, Sm[cb]) *
               *(const LDS f32x4*)((const LDS float*)(lds + cur.dl) + 16 * cb + 4 * ln.g);
-    if (ln.w == NW - 1 && m + 1 < nc && !*FLAG) solve1(nxt, ln);
+    if (ln.w == NW - 1 && solve) {
+      // a bounded wait; past it the wave forms the tiles itself (the same values)
+      int tries = 0;
+      while (__hip_atomic_load(TFLAG, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) != m + 1 &&
+             ++tries < 512)
+        __builtin_amdgcn_s_sleep(1);
+      if (tries >= 512) tiles_nt(lds, nxt, ln);
+      invert_nt(lds, nxt, ln);
+    }
     if (m + 2 < nc) stage<SG>(lds, xn, false, ln);
     __syncthreads();   // #b: the next chunk's T and staged inputs; this chunk's buffers are free
     ln = fresh();
