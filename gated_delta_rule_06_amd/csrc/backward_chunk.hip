@@ -50,8 +50,11 @@
 //    over channels use the gfx950 transpose read (ds_read_b64_tr_b16); S and
 //    dS in registers serve as 32-deep operands with the k index relabelled
 //    (two stacked 16-row accumulator tiles);
-//  * T is formed in fp32 on one wave: the two 16x16 diagonal blocks by forward
+//  * T is formed in fp32: in the forward sweep the A tiles on one wave, handed
+//    to the last, which solves the two 16x16 diagonal blocks by forward
 //    substitution (a lane group each), then T_10 = -T_11 N_10 T_00 as MFMAs.
+#include <stdlib.h>
+
 #include "common.h"
 
 namespace kda {
@@ -626,7 +629,7 @@ __global__ __launch_bounds__(NT, 1) void bwd_chunk_kernel(
     const float* __restrict__ dSf, float* __restrict__ dq, float* __restrict__ dk,
     float* __restrict__ dv, float* __restrict__ dg, float* __restrict__ dbeta,
     float* __restrict__ dS0, const int32_t* __restrict__ cu, int T, int H, float scale,
-    uint32_t* __restrict__ states, int* __restrict__ flags) {
+    uint32_t* __restrict__ states, int* __restrict__ flags, int spin) {
   extern __shared__ __attribute__((aligned(16))) char lds_raw[];
   LDS char* lds = (LDS char*)lds_raw;
   Ln ln = fresh();
@@ -774,12 +777,15 @@ __global__ __launch_bounds__(NT, 1) void bwd_chunk_kernel(
       S[cb] = mma(rd_rowp((lb)(lds + cur.ki), LT, 16 * cb, 0, ln), eb, Sm[cb]) *
               *(const LDS f32x4*)((const LDS float*)(lds + cur.dl) + 16 * cb + 4 * ln.g);
     if (ln.w == NW - 1 && solve) {
-      // a bounded wait; past it the wave forms the tiles itself (the same values)
-      int tries = 0;
-      while (__hip_atomic_load(TFLAG, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) != m + 1 &&
-             ++tries < 512)
+      // a wait of at most `spin` polls; past it the wave forms the tiles itself
+      // (the same values, so a late second write changes nothing)
+      bool got = false;
+      for (int it = 0; it < spin; ++it) {
+        got = __hip_atomic_load(TFLAG, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == m + 1;
+        if (got) break;
         __builtin_amdgcn_s_sleep(1);
-      if (tries >= 512) tiles_nt(lds, nxt, ln);
+      }
+      if (!got) tiles_nt(lds, nxt, ln);
       invert_nt(lds, nxt, ln);
     }
     if (m + 2 < nc) stage<SG>(lds, xn, false, ln);
@@ -1108,6 +1114,20 @@ __global__ __launch_bounds__(NT, 1) void bwd_chunk_kernel(
 
 }  // namespace
 
+// The poll limit of the forward sweep's tile hand-over: BWD_SPIN, or a
+// non-negative count from the environment variable KDA_BWD_SPIN_POLLS (read on
+// every call; 0 makes the last wave form every chunk's tiles itself).
+constexpr int BWD_SPIN = 512;
+static int bwd_spin_polls() {
+  const char* e = getenv("KDA_BWD_SPIN_POLLS");
+  if (e && *e) {
+    char* end = nullptr;
+    const long v = strtol(e, &end, 10);
+    if (end && *end == '\0' && v >= 0 && v <= BWD_SPIN) return (int)v;
+  }
+  return BWD_SPIN;
+}
+
 hipError_t launch_backward_chunk(const void* q, const void* k, const void* v, const float* g,
                                  const float* beta, const float* S0, const void* dout,
                                  const float* dSf, float* dq, float* dk, float* dv, float* dg,
@@ -1121,7 +1141,7 @@ hipError_t launch_backward_chunk(const void* q, const void* k, const void* v, co
   hipLaunchKernelGGL(kern, dim3(n_seq * H), dim3(NT), LDS_BYTES, stream,
                      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, g, beta, S0,
                      (const uint16_t*)dout, dSf, dq, dk, dv, dg, dbeta, dS0, cu, T, H, scale,
-                     (uint32_t*)states, flags);
+                     (uint32_t*)states, flags, bwd_spin_polls());
   return hipGetLastError();
 }
 

@@ -334,7 +334,12 @@ int kda_decode_step_fused(const void* q, const void* k, const void* v, const flo
  * operands, fp32 accumulation and fp32 state and gradient carries).  A chain
  * with a chunk half whose log decay exceeds 76 in some key channel (log alpha
  * below about -4.7 on average over 16 tokens) is redone by the token loop.
- * Every other case runs the token loop, fp32 throughout.
+ * Every other case runs the token loop, fp32 throughout.  Inside a workgroup
+ * of the chunkwise form one wave hands each chunk's triangular-solve input to
+ * another and that wave waits for it a bounded number of polls (512, or the
+ * count in the environment variable KDA_BWD_SPIN_POLLS, read on every call);
+ * past the bound it forms the input itself: same results, more work (tests
+ * set 0 to take that path).
  *
  *  inputs     q, k, v, log_alpha, beta, S0, cu_seqlens, N, T, H, d_k, d_v,
  *             scale, io_dtype, per_head_gate: exactly as given to the forward

@@ -152,6 +152,24 @@ def test_chunkwise_backward_matches_oracle(B, T, H, with_S0, with_dSf, gate):
     compare(run_gpu(d), run_oracle(d), what, TOL_CHUNK, d)
 
 
+@pytest.mark.parametrize("gate", ["kda", "gdn"])
+def test_chunkwise_backward_without_tile_hand_over(monkeypatch, gate):
+    """With no polls allowed (KDA_BWD_SPIN_POLLS=0) the forward sweep's last
+    wave forms every chunk's A tiles itself instead of taking them from the
+    wave that forms them beside it: the bounded wait's other branch, the same
+    bits in every gradient."""
+    note("chunkwise backward without the tile hand-over, gate=%s" % gate)
+    d = inputs.prefill_inputs(2, 200, 3, 128, 128, io="bf16", seed=45, with_S0=True,
+                              device=DEV, gate=gate)
+    inputs.grad_inputs(d, seed=45, device=DEV)
+    ref = run_gpu(d)
+    monkeypatch.setenv("KDA_BWD_SPIN_POLLS", "0")
+    got = run_gpu(d)
+    for name in ref:
+        if ref[name] is not None:
+            assert np.array_equal(got[name], ref[name]), name
+
+
 def test_chunkwise_backward_near_the_edge_of_its_decay_range():
     """log alpha around -4.4 in every channel (each half chunk decays by about
     e^-70, inside the chunkwise form's e^+-76 factor range): still the MFMA
