@@ -31,7 +31,11 @@
 //   db = q dq + k (e^{b-r} dKG - e^{r-b} dKI),  plus sum_v dS S_{c+1} on the last token
 //   dlog_alpha_t = sum_{i >= t} db_i  (inside the chunk)
 // The loss does not depend on r (it cancels in every product), so r is held
-// constant in the derivative.
+// constant in the derivative.  The kernel forms dlog alpha in an equal order
+// that cancels in fp32: db from the same bf16 factors the products used
+// (QG dQG + KG dKG - KI dKI), the K_end part of dKI (E dS_m^T) as a sum over
+// the tokens before t, and the incoming state's decay (sum_v dS_m S_m) on
+// every token.
 //
 // Mapping (one workgroup of 8 waves per (sequence, head) chain):
 //  * a forward sweep carries S in fp32 registers and stores each chunk's S_c
@@ -42,6 +46,9 @@
 //    elements (tokens 4g + r and 16 + 4g + r, channel 16w + l%16, g = lane/16)
 //    are exactly its accumulator elements of the latter, so the epilogue needs
 //    no exchange;
+//  * the inputs load one chunk ahead as whole token rows (wave w takes tokens
+//    4w .. 4w+3) and go through a shared [token][channel] staging area in
+//    LDS, from which every wave takes its own columns with the transpose read;
 //  * the in-chunk prefix sums (b) and the suffix sums of dlog alpha are
 //    running sums in registers joined across lane groups by gfx950's permlane
 //    swaps;
