@@ -123,7 +123,6 @@ struct Set {
 constexpr Set SET0{O_KG, O_KI, O_V, O_BETA, O_ER, O_DL, O_TT};
 constexpr Set SET1{O_QG, O_DO, O_NU, O_DBP, O_DBP + 128, O_DBP + 640, O_DAQ};
 static_assert(O_TB == O_TT + SZ_S && O_DA == O_DAQ + SZ_S, "T buffer pairs");
-static_assert(O_NU == O_NW + SZ_T && NW * BC * 20 * 4 <= 2 * SZ_T, "store staging");
 // Shared staging of a chunk's loaded inputs (E, -dE and R are free from the
 // time a chunk's inputs are staged until they are unpacked): q, k, v and dO as
 // bf16 [token][LS], then the gates as fp32 [token][LG] (a per-head gate:
@@ -501,23 +500,17 @@ __device__ __forceinline__ void invert_nt(LDS char* lds, Set st, const Ln& ln) {
 }
 
 // Stores a wave's 32 x 16 fp32 tile (accumulator layout: tokens 16I + 4g + r,
-// column 16w + n) to a chunk view of a [rows, H, 128] tensor, through the
-// wave's own LDS staging area (token rows of 20 dwords, no bank conflicts):
-// each lane then writes four columns of one token, 16 bytes.
-__device__ __forceinline__ void store_tile(Rsrc rv, LDS float* stg, const f32x4 x[2], int H,
-                                           const Ln& ln) {
+// column 16w + n) to a chunk view of a [rows, H, 128] tensor: eight 4-byte
+// stores per lane, each instruction writing the wave's 64 bytes of four token
+// rows; the view drops the padding rows.  (Staging the tile through LDS into
+// 16-byte stores of the same rows measured slower: its LDS round trip sat in
+// the epilogue.)
+__device__ __forceinline__ void store_tile(Rsrc rv, const f32x4 x[2], int H, const Ln& ln) {
 #pragma unroll
   for (int I = 0; I < 2; ++I)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) stg[(16 * I + 4 * ln.g + r) * 20 + ln.n] = x[I][r];
-  const int t = ln.l >> 2, j = ln.l & 3;
-  const uint32_t off = 4 * (uint32_t)(t * H * DD + 16 * ln.w + 4 * j);
-#pragma unroll
-  for (int hh = 0; hh < 2; ++hh) {
-    const f32x4 y = *(const LDS f32x4*)(stg + (16 * hh + t) * 20 + 4 * j);
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, y), rv, off,
-                                           4 * (uint32_t)(16 * hh * H * DD), 0);
-  }
+    for (int r = 0; r < 4; ++r)
+      st_f32(rv, 4 * (uint32_t)((16 * I + 4 * ln.g + r) * H * DD + 16 * ln.w + ln.n), 0, x[I][r]);
 }
 
 // Writes every input prep product of one chunk: KG, KI, V (and, reverse sweep,
@@ -1090,12 +1083,10 @@ __global__ __launch_bounds__(NT, 1) void bwd_chunk_kernel(
       suffix_prefix(db, de, dgc, ln);
       dgc[0] += rs;
       dgc[1] += rs;
-      // -W and -U are free: each wave stages its tiles in 2560 bytes of them
-      LDS float* stg = (LDS float*)(lds + O_NW) + ln.w * (BC * 20);
-      store_tile(chunk_view(dq, tok0, L, H, h, DD, 4), stg, dQG, H, ln);
-      store_tile(chunk_view(dk, tok0, L, H, h, DD, 4), stg, dKG, H, ln);
-      store_tile(chunk_view(dv, tok0, L, H, h, DD, 4), stg, dvv, H, ln);
-      if (!SG) store_tile(chunk_view(dg, tok0, L, H, h, DD, 4), stg, dgc, H, ln);
+      store_tile(chunk_view(dq, tok0, L, H, h, DD, 4), dQG, H, ln);
+      store_tile(chunk_view(dk, tok0, L, H, h, DD, 4), dKG, H, ln);
+      store_tile(chunk_view(dv, tok0, L, H, h, DD, 4), dvv, H, ln);
+      if (!SG) store_tile(chunk_view(dg, tok0, L, H, h, DD, 4), dgc, H, ln);
       if (SG) {
 #pragma unroll
         for (int I = 0; I < 2; ++I)
